@@ -1,0 +1,1031 @@
+/*
+ * ckv_oracle.c -- CPU oracle for certified quantized-KV decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (see ckv_oracle.h).  Plain, slow and sequential
+ * on purpose: one head at a time, full sorts where the method says "order",
+ * FP64 for every value.  Built with -O2 -fno-fast-math -ffp-contract=off so
+ * that every FP32 operation is the single IEEE operation written here.
+ *
+ * Section tags ([Meth-1] ...) refer to the page "Runtime-Certified
+ * Bounded-Error Quantized Attention", technical summary; they are listed in
+ * ckv_oracle.h.  Where the page leaves a step open, the reading taken is
+ * stated at the step; the full list is in the design doc.
+ */
+#include "ckv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+int orc_mutation = 0;
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 helpers                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 -> binary32, exact (every half is a float). */
+float orc_h2f(uint16_t h)
+{
+    int sign = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(m | 1024), e - 25);
+    return sign ? -v : v;
+}
+
+/* Smallest non-negative binary16 that is >= x (x >= 0): rounding upward.
+ * Positive halves are ordered like their bit patterns, so a bisection over
+ * the patterns 0x0000..0x7C00 (the last is +inf) finds it. */
+uint16_t orc_f2h_up(float x)
+{
+    if (!(x > 0.0f))
+        return 0;
+    unsigned lo = 0, hi = 0x7C00; /* orc_h2f(hi) >= x always */
+    while (lo < hi) {
+        unsigned mid = (lo + hi) / 2;
+        if (orc_h2f((uint16_t)mid) >= x)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return (uint16_t)lo;
+}
+
+/* binary64 -> binary32 rounded upward. */
+float orc_ru32(double x)
+{
+    float f = (float)x;
+    if ((double)f < x)
+        f = nextafterf(f, INFINITY);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Canonical exponential used on every decision path.                       */
+/* exp(x) for x <= 0: k = rint(x * log2(e)), r = x - k*ln2 in two steps     */
+/* (Cody & Waite, "Software Manual for the Elementary Functions", 1980),    */
+/* e^r by its degree-7 Taylor polynomial in Horner form, result r * 2^k.    */
+/* Results below 2^-125 are flushed to 0 so that no subnormal is formed.    */
+/* ------------------------------------------------------------------------ */
+float orc_exp_c(float x)
+{
+    const float L2E = 0x1.715476p+0f;   /* log2(e) rounded to binary32 */
+    const float LN2A = 0x1.62e4p-1f;    /* leading bits of ln 2        */
+    const float LN2B = 0x1.7f7d1cp-20f; /* ln 2 - LN2A, rounded        */
+    float y = x * L2E;
+    float k = rintf(y);
+    if (k < -125.0f)
+        return 0.0f;
+    float r = fmaf(-k, LN2A, x);
+    r = fmaf(-k, LN2B, r);
+    /* 1/j! for j = 7..0, each rounded to binary32 */
+    float p = 0x1.a01a02p-13f;
+    p = fmaf(p, r, 0x1.6c16c2p-10f);
+    p = fmaf(p, r, 0x1.111112p-7f);
+    p = fmaf(p, r, 0x1.555556p-5f);
+    p = fmaf(p, r, 0x1.555556p-3f);
+    p = fmaf(p, r, 0x1.0p-1f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)k);
+}
+
+/* Halving-tree sum: for stride n/2, n/4, .., 1: a[i] += a[i + stride]. */
+static float tree_f32(float *a, int n)
+{
+    for (int s = n / 2; s >= 1; s /= 2)
+        for (int i = 0; i < s; i++)
+            a[i] = a[i] + a[i + s];
+    return a[0];
+}
+
+static double tree_f64(double *a, int n)
+{
+    for (int s = n / 2; s >= 1; s /= 2)
+        for (int i = 0; i < s; i++)
+            a[i] = a[i] + a[i + s];
+    return a[0];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Upper bounds of e^x, e^x - 1 and tanh(x/2) for x >= 0, from +,-,*,/ only */
+/* (so that every platform evaluates them to the same bits).                */
+/* ------------------------------------------------------------------------ */
+
+/* e^x <= expu(x).  x is halved j times (exactly) to r <= 1/16, e^r from its
+ * Taylor series to degree 12 (remainder < 2^-60 relative), squared j times;
+ * the factor (1 + 2^-36) covers the rounding of at most 10 squarings. */
+double orc_expu(double x)
+{
+    if (!(x <= 64.0))
+        return INFINITY;
+    if (x <= 0.0)
+        x = 0.0;
+    int j = 0;
+    double r = x;
+    while (r > 0.0625) {
+        r *= 0.5;
+        j++;
+    }
+    double p = 1.0 / 479001600.0; /* 1/12! */
+    double f = 479001600.0;
+    for (int i = 11; i >= 0; i--) {
+        f = f / (double)(i + 1); /* f = i! */
+        p = fma(p, r, 1.0 / f);
+    }
+    for (int i = 0; i < j; i++)
+        p = p * p;
+    return p * (1.0 + 0x1p-36);
+}
+
+/* e^x - 1 <= em1u(x).  Series to degree 16 below 1/2, else expu(x) - 1. */
+double orc_em1u(double x)
+{
+    if (!(x > 0.0))
+        return 0.0;
+    if (x > 64.0)
+        return INFINITY;
+    if (x <= 0.5) {
+        /* x * sum_{i=0..15} x^i / (i+1)! */
+        double c[16];
+        double f = 1.0;
+        for (int i = 0; i < 16; i++) {
+            f = f * (double)(i + 1);
+            c[i] = 1.0 / f;
+        }
+        double p = c[15];
+        for (int i = 14; i >= 0; i--)
+            p = fma(p, x, c[i]);
+        return x * p * (1.0 + 0x1p-48);
+    }
+    return (orc_expu(x) - 1.0) * (1.0 + 0x1p-50);
+}
+
+/* tanh(x/2) = m / (m + 2) with m = e^x - 1, increasing in m. */
+double orc_tanhu(double x)
+{
+    double m = orc_em1u(x);
+    if (isinf(m))
+        return 1.0;
+    double t = m / (m + 2.0) * (1.0 + 0x1p-48);
+    return t < 1.0 ? t : 1.0;
+}
+
+/* Bound terms in unsigned fixed point with 32 fraction bits, rounded up and
+ * capped; a capped term makes the sum it enters "unbounded". */
+#define FX_CAP ((uint64_t)1 << 46)
+uint64_t orc_fx(double t)
+{
+    if (!(t < 16384.0))
+        return FX_CAP;
+    if (t <= 0.0)
+        return 0;
+    double v = ceil(t * 4294967296.0);
+    uint64_t u = (uint64_t)v;
+    return u < FX_CAP ? u : FX_CAP;
+}
+
+static double fx_to_bound(uint64_t sum, int saturated)
+{
+    if (saturated)
+        return INFINITY;
+    return (double)sum * 0x1p-32 * (1.0 + 0x1p-50);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tier 1: quantization [Meth-1]                                            */
+/* Reading: INT8 key scale/offset per channel per 64-token block; INT4      */
+/* value scale/offset per token per 32-channel group; both affine with      */
+/* offset = min (exact in FP16) and scale = (max - min)/levels rounded up   */
+/* to FP16, so that no code is clamped and |x - x^| <= scale * (1/2 + eps). */
+/* ------------------------------------------------------------------------ */
+static uint16_t scale_for(float lo, float hi, float levels)
+{
+    float r = hi - lo;
+    if (r == 0.0f)
+        return 0;
+    return orc_f2h_up(r / levels);
+}
+
+static int code_for(float x, float lo, float s, int maxcode)
+{
+    if (s == 0.0f)
+        return 0;
+    float c = rintf((x - lo) / s);
+    if (c < 0.0f)
+        c = 0.0f;
+    if (c > (float)maxcode)
+        c = (float)maxcode;
+    return (int)c;
+}
+
+/* k: [64][d] FP16 of one block and one kv head. */
+void orc_quant_k_block(int d, const uint16_t *k, uint8_t *code, uint16_t *s, uint16_t *z)
+{
+    for (int c = 0; c < d; c++) {
+        float lo = orc_h2f(k[c]), hi = lo;
+        for (int t = 1; t < ORC_BT; t++) {
+            float x = orc_h2f(k[t * d + c]);
+            if (x < lo)
+                lo = x;
+            if (x > hi)
+                hi = x;
+        }
+        uint16_t sh = scale_for(lo, hi, 255.0f);
+        /* the minimum is itself an FP16 value: store its bits */
+        uint16_t zh = 0;
+        for (int t = 0; t < ORC_BT; t++)
+            if (orc_h2f(k[t * d + c]) == lo) {
+                zh = k[t * d + c];
+                break;
+            }
+        if (lo == 0.0f)
+            zh = 0; /* +0 and -0 compare equal; store +0 */
+        s[c] = sh;
+        z[c] = zh;
+        float sf = orc_h2f(sh);
+        for (int t = 0; t < ORC_BT; t++)
+            code[t * d + c] = (uint8_t)code_for(orc_h2f(k[t * d + c]), lo, sf, 255);
+    }
+}
+
+/* v: [64][d] FP16.  eta = max |v - (z + s*code)| over the block, exact in
+ * FP64 and rounded up to FP32 (reading of the per-block annotation). */
+void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z, float *eta)
+{
+    int ng = d / ORC_VG;
+    double emax = 0.0;
+    memset(code, 0, (size_t)ORC_BT * d / 2);
+    for (int t = 0; t < ORC_BT; t++) {
+        for (int g = 0; g < ng; g++) {
+            const uint16_t *row = v + (size_t)t * d + g * ORC_VG;
+            float lo = orc_h2f(row[0]), hi = lo;
+            uint16_t zh = row[0];
+            for (int c = 1; c < ORC_VG; c++) {
+                float x = orc_h2f(row[c]);
+                if (x < lo) {
+                    lo = x;
+                    zh = row[c];
+                }
+                if (x > hi)
+                    hi = x;
+            }
+            if (lo == 0.0f)
+                zh = 0;
+            uint16_t sh = scale_for(lo, hi, 15.0f);
+            s[t * ng + g] = sh;
+            z[t * ng + g] = zh;
+            float sf = orc_h2f(sh);
+            for (int c = 0; c < ORC_VG; c++) {
+                float x = orc_h2f(row[c]);
+                int q = code_for(x, lo, sf, 15);
+                int ch = g * ORC_VG + c;
+                code[(size_t)t * (d / 2) + ch / 2] |= (uint8_t)((ch & 1) ? (q << 4) : q);
+                double rec = (double)lo + (double)sf * (double)q;
+                double e = fabs((double)x - rec);
+                if (e > emax)
+                    emax = e;
+            }
+        }
+    }
+    *eta = orc_ru32(emax);
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8 scoring pass [Meth-3, adaptive top-K selection]                     */
+/* s^_t = fl(fl(a_t + C) * sm), a_t = fma chain over c of w_c * code_tc with */
+/* w_c = q_c * s_c, C = halving-tree sum of q_c * z_c.                      */
+/* ------------------------------------------------------------------------ */
+void orc_score_q8(int d, const uint16_t *q, const uint8_t *code, const uint16_t *s,
+                  const uint16_t *z, float sm, float *out)
+{
+    float w[256], cz[256];
+    for (int c = 0; c < d; c++) {
+        w[c] = orc_h2f(q[c]) * orc_h2f(s[c]);
+        cz[c] = orc_h2f(q[c]) * orc_h2f(z[c]);
+    }
+    float C = tree_f32(cz, d);
+    for (int t = 0; t < ORC_BT; t++) {
+        float a = 0.0f;
+        for (int c = 0; c < d; c++)
+            a = fmaf(w[c], (float)code[t * d + c], a);
+        out[t] = (a + C) * sm;
+    }
+}
+
+/* FP16-key score: an FP64 fma chain over c of q_c * k_c (each product is
+ * exact), times sm in FP64, rounded once to FP32. */
+void orc_score_f16(int d, const uint16_t *q, const uint16_t *k, int n, float sm, float *out)
+{
+    for (int t = 0; t < n; t++) {
+        double a = 0.0;
+        for (int c = 0; c < d; c++)
+            a = fma((double)orc_h2f(q[c]), (double)orc_h2f(k[t * d + c]), a);
+        out[t] = (float)(a * (double)sm);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-token score perturbation bound [Meth-2, E_key "bounded by Delta"]    */
+/* from the query and the quantization scales (tracked quantities only).    */
+/* With H = sum |q_c| s_c and A = sum |q_c| (|z_c| + 255 s_c):              */
+/*   |s^ - s| <= Delta = sm (kappa H + gamma(d+3) A)   (INT8 key score)      */
+/*   |s~ - s| <= rho   = sm 2^-23 A                   (FP16 key score)      */
+/* kappa = 1/2 + 2^-14 covers the code rounding, gamma(n) = n u/(1 - n u),   */
+/* u = 2^-24, the FP32 rounding of the INT8 fma chain; the FP16 chain runs   */
+/* in FP64 and is rounded once to FP32 (2^-24 + (d+3) 2^-53 < 2^-23).        */
+/* |k| <= |z| + 255 s for every key of the block, so A bounds sum |q_c k_c|. */
+/* Sums are FP64 halving trees; (1 + 2^-20) covers the FP64 rounding;       */
+/* results rounded up to FP32.                                              */
+/* ------------------------------------------------------------------------ */
+static double gamma_n(int n)
+{
+    double nu = (double)n * 0x1p-24;
+    return nu / (1.0 - nu);
+}
+
+void orc_delta_rho(int d, const uint16_t *q, const uint16_t *s, const uint16_t *z, float sm,
+                   float *delta, float *rho)
+{
+    double hv[256], av[256];
+    for (int c = 0; c < d; c++) {
+        double aq = fabs((double)orc_h2f(q[c]));
+        double sc = (double)orc_h2f(s[c]);
+        double zc = fabs((double)orc_h2f(z[c]));
+        hv[c] = aq * sc;
+        av[c] = aq * (zc + 255.0 * sc);
+    }
+    double H = tree_f64(hv, d);
+    double A = tree_f64(av, d);
+    double kappa = 0.5 + 0x1p-14;
+    double dl = kappa * H + gamma_n(d + 3) * A;
+    dl = dl * (double)sm;
+    dl = dl * (1.0 + 0x1p-20);
+    double rh = A * 0x1p-23;
+    rh = rh * (double)sm;
+    rh = rh * (1.0 + 0x1p-20);
+    if (orc_mutation & 2)
+        dl *= 0.5;
+    *delta = orc_ru32(dl);
+    *rho = orc_ru32(rh);
+}
+
+/* rho for the FP16 tokens of a partial block: A = sum |q_c| max_t |k_tc|. */
+static float rho_partial(int d, const uint16_t *q, const uint16_t *k, int n, float sm)
+{
+    double av[256];
+    for (int c = 0; c < d; c++) {
+        double m = 0.0;
+        for (int t = 0; t < n; t++) {
+            double x = fabs((double)orc_h2f(k[t * d + c]));
+            if (x > m)
+                m = x;
+        }
+        av[c] = fabs((double)orc_h2f(q[c])) * m;
+    }
+    double A = tree_f64(av, d);
+    double rh = A * 0x1p-23;
+    rh = rh * (double)sm;
+    rh = rh * (1.0 + 0x1p-20);
+    return orc_ru32(rh);
+}
+
+/* Block estimate: max score and l = halving-tree sum over 64 slots of
+ * exp_c(s_t - max); slots beyond n hold 0. */
+void orc_block_est(const float *sc, int n, float *mx, float *l)
+{
+    float m = sc[0];
+    for (int t = 1; t < n; t++)
+        if (sc[t] > m)
+            m = sc[t];
+    float e[ORC_BT];
+    for (int t = 0; t < ORC_BT; t++)
+        e[t] = t < n ? orc_exp_c(sc[t] - m) : 0.0f;
+    *mx = m;
+    *l = tree_f32(e, ORC_BT);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Selection by order (value desc, index asc)                               */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    uint64_t v;
+    int b;
+} vb_t;
+
+static int cmp_vb_desc(const void *x, const void *y)
+{
+    const vb_t *a = (const vb_t *)x, *b = (const vb_t *)y;
+    if (a->v != b->v)
+        return a->v > b->v ? -1 : 1;
+    return a->b < b->b ? -1 : (a->b > b->b);
+}
+
+int orc_select(int n, const uint64_t *m, uint64_t need, uint8_t *in_set)
+{
+    memset(in_set, 0, (size_t)n);
+    if (need == 0)
+        return 0;
+    vb_t *o = (vb_t *)malloc(sizeof(vb_t) * (size_t)(n > 0 ? n : 1));
+    for (int b = 0; b < n; b++) {
+        o[b].v = m[b];
+        o[b].b = b;
+    }
+    qsort(o, (size_t)n, sizeof(vb_t), cmp_vb_desc);
+    uint64_t acc = 0;
+    int k = 0;
+    while (k < n && acc < need) {
+        acc += o[k].v;
+        in_set[o[k].b] = 1;
+        k++;
+    }
+    free(o);
+    return k;
+}
+
+int64_t orc_discordant(int n, const uint64_t *key_a, const uint64_t *key_b)
+{
+    int64_t D = 0;
+    for (int i = 0; i < n; i++)
+        for (int j = i + 1; j < n; j++)
+            if ((key_a[i] > key_a[j]) != (key_b[i] > key_b[j]))
+                D++;
+    return D;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The plan of one q head: selection, the two-term bound and rungs 1-2,      */
+/* computed before paging from INT8-side quantities only [Contrib].          */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int N, has_part;
+    const float *bmax, *bl, *delta, *rho, *eta; /* [Np] (eta: [N]) */
+    double R;                                   /* range of V */
+    /* results */
+    float mref;
+    uint64_t *M; /* [Np] */
+    uint64_t S;
+    uint8_t *inP, *inVP; /* [N] */
+    int kstar, nvp, widened, cap_fail;
+    double tau, mu, tv, ekey, eval;
+} plan_t;
+
+static double phat_up(uint64_t Mb, uint64_t S)
+{
+    return ((double)(Mb + 1) / (double)S) * (1.0 + 0x1p-16);
+}
+
+/* Bound on the mass of block b under the certified scores relative to its
+ * INT8 estimate: p~_b <= phat_b * F * X_b, F = exp(max_{P} (Delta + rho)),
+ * X_b = exp(Delta_b + rho_b) on P, 1 on the tail. */
+static double factor_F(const plan_t *p)
+{
+    double mx = 0.0;
+    for (int b = 0; b < p->N; b++)
+        if (p->inP[b]) {
+            double f = (double)p->delta[b] + (double)p->rho[b];
+            if (f > mx)
+                mx = f;
+        }
+    return orc_expu(mx);
+}
+
+static double factor_X(const plan_t *p, int b)
+{
+    return p->inP[b] ? orc_expu((double)p->delta[b] + (double)p->rho[b]) : 1.0;
+}
+
+/* E_key [Meth-2]: TV(p~, p) <= mu / (1 - mu), mu = sum_b p~_b (e^delta_b - 1),
+ * and TV <= tanh(delta_max / 2); the output error is at most TV * range(V)
+ * because sum (p~ - p) = 0.  delta_b = rho on P (FP16 keys), Delta on the
+ * tail (INT8 keys). */
+static void key_bound(plan_t *p)
+{
+    double F = factor_F(p);
+    uint64_t sum = 0;
+    int sat = 0;
+    double dmax = 0.0;
+    for (int b = 0; b < p->N; b++) {
+        double dl = p->inP[b] ? (double)p->rho[b] : (double)p->delta[b];
+        double t = phat_up(p->M[b], p->S) * F * factor_X(p, b) * orc_em1u(dl) * (1.0 + 0x1p-48);
+        uint64_t u = orc_fx(t);
+        sat |= (u == FX_CAP);
+        sum += u;
+        if (dl > dmax)
+            dmax = dl;
+    }
+    if (p->has_part) {
+        double dl = (double)p->rho[p->N];
+        double t = phat_up(p->M[p->N], p->S) * F * 1.0 * orc_em1u(dl) * (1.0 + 0x1p-48);
+        uint64_t u = orc_fx(t);
+        sat |= (u == FX_CAP);
+        sum += u;
+        if (dl > dmax)
+            dmax = dl;
+    }
+    double mu = fx_to_bound(sum, sat);
+    double tv = 1.0;
+    if (mu < 1.0)
+        tv = mu / (1.0 - mu) * (1.0 + 0x1p-48);
+    double th = orc_tanhu(dmax);
+    if (th < tv)
+        tv = th;
+    if (tv > 1.0)
+        tv = 1.0;
+    p->mu = mu;
+    p->tv = tv;
+    p->ekey = tv * p->R * (1.0 + 0x1p-50);
+}
+
+/* E_val contribution of block b [Meth-2]: p~_b * eta_b, bounded by
+ * phat_b * F * X_b * eta_b. */
+static uint64_t val_term(const plan_t *p, double F, int b)
+{
+    double e = (double)p->eta[b];
+    if (orc_mutation & 1)
+        e = 0.0;
+    double t = phat_up(p->M[b], p->S) * F * factor_X(p, b) * e * (1.0 + 0x1p-48);
+    return orc_fx(t);
+}
+
+static void plan_head(plan_t *p, const orc_thresholds *th)
+{
+    int N = p->N, Np = N + p->has_part;
+    /* estimated masses */
+    float mref = p->bmax[0];
+    for (int b = 1; b < Np; b++)
+        if (p->bmax[b] > mref)
+            mref = p->bmax[b];
+    p->mref = mref;
+    uint64_t S = 0;
+    for (int b = 0; b < Np; b++) {
+        float mh = p->bl[b] * orc_exp_c(p->bmax[b] - mref);
+        p->M[b] = (uint64_t)((double)mh * 4294967296.0);
+        S += p->M[b];
+    }
+    p->S = S;
+    uint64_t Mpart = p->has_part ? p->M[N] : 0;
+
+    /* top-K* covering tau of the estimated mass, rung 1 widening [Meth-3].
+     * Reading: widen while E_key > k_tol by halving the uncovered target,
+     * at most n_widen times; still above k_tol escalates to rung 4. */
+    double tau = (double)th->tau_cov;
+    p->widened = 0;
+    p->cap_fail = 0;
+    for (int w = 0;; w++) {
+        uint64_t T = (uint64_t)ceil(tau * (double)S);
+        uint64_t need = T > Mpart ? T - Mpart : 0;
+        p->kstar = orc_select(N, p->M, need, p->inP);
+        key_bound(p);
+        if (!(p->ekey > (double)th->k_tol))
+            break;
+        if (w >= th->n_widen) {
+            p->cap_fail = 1;
+            break;
+        }
+        tau = 1.0 - (1.0 - tau) * 0.5;
+        p->widened = 1;
+    }
+    p->tau = tau;
+
+    /* E_val and rung 2: promote FP16 values of the blocks with the largest
+     * bounded contribution (order: contribution desc, index asc) until
+     * E_val <= v_tol.  Reading: no cap by default (promoting more values
+     * always pages less than a dense recompute); a caller-set cap that is
+     * too small escalates to rung 4. */
+    double F = factor_F(p);
+    uint64_t *cb = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(N > 0 ? N : 1));
+    for (int b = 0; b < N; b++)
+        cb[b] = val_term(p, F, b);
+    vb_t *o = (vb_t *)malloc(sizeof(vb_t) * (size_t)(N > 0 ? N : 1));
+    for (int b = 0; b < N; b++) {
+        o[b].v = cb[b];
+        o[b].b = b;
+    }
+    qsort(o, (size_t)N, sizeof(vb_t), cmp_vb_desc);
+    /* suffix sums: rest[k] = sum of o[k..N) */
+    memset(p->inVP, 0, (size_t)N);
+    int k = 0;
+    for (;; k++) {
+        uint64_t rest = 0;
+        int sat = 0;
+        for (int i = k; i < N; i++) {
+            rest += o[i].v;
+            sat |= (o[i].v == FX_CAP);
+        }
+        double ev = fx_to_bound(rest, sat);
+        if (!(ev > (double)th->v_tol) || k == N) {
+            p->eval = ev;
+            break;
+        }
+    }
+    for (int i = 0; i < k; i++)
+        p->inVP[o[i].b] = 1;
+    p->nvp = k;
+    int vcap = th->v_cap_blocks > 0 ? th->v_cap_blocks : N;
+    if (k > vcap || p->eval > (double)th->v_tol)
+        p->cap_fail = 1;
+    free(o);
+    free(cb);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact dense attention (FP64) [Signif: "FP16 reference"; Meth-1 fallback]  */
+/* ------------------------------------------------------------------------ */
+void orc_dense_head(int T, int Hkv, int d, int g, const uint16_t *k, const uint16_t *v,
+                    const uint16_t *q, double sm, double *out)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double mx = -INFINITY;
+    for (int t = 0; t < T; t++) {
+        const uint16_t *kt = k + ((size_t)t * Hkv + g) * d;
+        double a = 0.0;
+        for (int c = 0; c < d; c++)
+            a += (double)orc_h2f(q[c]) * (double)orc_h2f(kt[c]);
+        s[t] = sm * a;
+        if (s[t] > mx)
+            mx = s[t];
+    }
+    double den = 0.0;
+    for (int c = 0; c < d; c++)
+        out[c] = 0.0;
+    for (int t = 0; t < T; t++) {
+        double p = exp(s[t] - mx);
+        den += p;
+        const uint16_t *vt = v + ((size_t)t * Hkv + g) * d;
+        for (int c = 0; c < d; c++)
+            out[c] += p * (double)orc_h2f(vt[c]);
+    }
+    for (int c = 0; c < d; c++)
+        out[c] /= den;
+    free(s);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The decode step                                                          */
+/* ------------------------------------------------------------------------ */
+#define TRP(ptr, idx) ((ptr) ? &(ptr)[idx] : NULL)
+
+int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K,
+                         const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
+                         double *out, orc_report *rep, orc_trace *tr)
+{
+    if (B < 1 || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || (d != 64 && d != 128))
+        return -1;
+    const int G = Hq / Hkv, N = T / ORC_BT, np = T % ORC_BT, has_part = np > 0,
+              Np = N + has_part, ng = d / ORC_VG;
+    const double sm = (double)th->sm_scale;
+    orc_trace empty;
+    memset(&empty, 0, sizeof empty);
+    if (!tr)
+        tr = &empty;
+
+    /* per (sequence, kv head) tier-1 contents in the oracle's own layout */
+    size_t nb = (size_t)(N > 0 ? N : 1);
+    uint8_t *kc = (uint8_t *)malloc(nb * ORC_BT * d);
+    uint16_t *ks = (uint16_t *)malloc(nb * d * 2), *kz = (uint16_t *)malloc(nb * d * 2);
+    uint8_t *vc = (uint8_t *)malloc(nb * ORC_BT * d / 2);
+    uint16_t *vs = (uint16_t *)malloc(nb * ORC_BT * ng * 2), *vz = (uint16_t *)malloc(nb * ORC_BT * ng * 2);
+    float *eta = (float *)malloc(nb * sizeof(float));
+    uint16_t *blk = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
+    uint16_t *blv = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
+    /* per head work arrays */
+    float *sc = (float *)malloc((size_t)Np * ORC_BT * sizeof(float));
+    float *bmax = (float *)malloc((size_t)Np * sizeof(float)), *bl = (float *)malloc((size_t)Np * sizeof(float));
+    float *dl = (float *)malloc((size_t)Np * sizeof(float)), *rh = (float *)malloc((size_t)Np * sizeof(float));
+    uint64_t *M = (uint64_t *)malloc((size_t)Np * sizeof(uint64_t));
+    uint8_t *inP = (uint8_t *)malloc(nb), *inVP = (uint8_t *)malloc(nb);
+    double *odense = (double *)malloc((size_t)Hq * d * sizeof(double));
+    double *ocert = (double *)malloc((size_t)Hq * d * sizeof(double));
+    int *dense = (int *)malloc((size_t)Hq * sizeof(int));
+    /* per sequence: plans of all heads */
+    plan_t *plans = (plan_t *)calloc((size_t)Hq, sizeof(plan_t));
+    uint8_t *allP = (uint8_t *)malloc((size_t)Hq * nb), *allVP = (uint8_t *)malloc((size_t)Hq * nb);
+    uint64_t *allM = (uint64_t *)malloc((size_t)Hq * Np * sizeof(uint64_t));
+    float *allsc = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
+    double *ptil = (double *)malloc((size_t)Np * ORC_BT * sizeof(double));
+    double *pex = (double *)malloc((size_t)Np * ORC_BT * sizeof(double));
+    float *s16 = (float *)malloc((size_t)ORC_BT * sizeof(float));
+    float *b16max = (float *)malloc(nb * sizeof(float)), *b16l = (float *)malloc(nb * sizeof(float));
+    uint64_t *keyI = (uint64_t *)malloc(nb * sizeof(uint64_t)), *key16 = (uint64_t *)malloc(nb * sizeof(uint64_t));
+    int *plist = (int *)malloc(nb * sizeof(int));
+    float *vrange = (float *)malloc((size_t)Hkv * sizeof(float));
+    /* the certified scores of one head: FP16 on P and partial, INT8 on tail */
+    float *smix = (float *)malloc((size_t)Np * ORC_BT * sizeof(float));
+    float *allsmix = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
+    /* quantized tier 1 of all kv heads of the sequence (needed for outputs) */
+    uint8_t *all_vc = (uint8_t *)malloc((size_t)Hkv * nb * ORC_BT * d / 2);
+    uint16_t *all_vs = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * ng * 2);
+    uint16_t *all_vz = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * ng * 2);
+
+    for (int n = 0; n < B; n++) {
+        const uint16_t *Kn = K + (size_t)n * T * Hkv * d;
+        const uint16_t *Vn = V + (size_t)n * T * Hkv * d;
+        int rung4_pre = 0;
+        for (int g = 0; g < Hkv; g++) {
+            /* quantize every full block of this kv head [Meth-1] */
+            for (int b = 0; b < N; b++) {
+                for (int t = 0; t < ORC_BT; t++)
+                    for (int c = 0; c < d; c++) {
+                        size_t src = ((size_t)(b * ORC_BT + t) * Hkv + g) * d + c;
+                        blk[t * d + c] = Kn[src];
+                        blv[t * d + c] = Vn[src];
+                    }
+                orc_quant_k_block(d, blk, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d);
+                orc_quant_v_block(d, blv, vc + (size_t)b * ORC_BT * d / 2, vs + (size_t)b * ORC_BT * ng,
+                                  vz + (size_t)b * ORC_BT * ng, &eta[b]);
+            }
+            size_t gofs = ((size_t)n * Hkv + g) * N;
+            if (tr->k_code)
+                memcpy(tr->k_code + gofs * ORC_BT * d, kc, (size_t)N * ORC_BT * d);
+            if (tr->k_s)
+                memcpy(tr->k_s + gofs * d, ks, (size_t)N * d * 2);
+            if (tr->k_z)
+                memcpy(tr->k_z + gofs * d, kz, (size_t)N * d * 2);
+            if (tr->v_code)
+                memcpy(tr->v_code + gofs * ORC_BT * d / 2, vc, (size_t)N * ORC_BT * d / 2);
+            if (tr->v_s)
+                memcpy(tr->v_s + gofs * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
+            if (tr->v_z)
+                memcpy(tr->v_z + gofs * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
+            if (tr->eta)
+                memcpy(tr->eta + gofs, eta, (size_t)N * sizeof(float));
+            memcpy(all_vc + (size_t)g * nb * ORC_BT * d / 2, vc, (size_t)N * ORC_BT * d / 2);
+            memcpy(all_vs + (size_t)g * nb * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
+            memcpy(all_vz + (size_t)g * nb * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
+
+            /* value range R_g over all tokens, "value ranges" of [Meth-2] */
+            double rmax = 0.0;
+            for (int c = 0; c < d; c++) {
+                double lo = INFINITY, hi = -INFINITY;
+                for (int t = 0; t < T; t++) {
+                    double x = (double)orc_h2f(Vn[((size_t)t * Hkv + g) * d + c]);
+                    if (x < lo)
+                        lo = x;
+                    if (x > hi)
+                        hi = x;
+                }
+                if (hi - lo > rmax)
+                    rmax = hi - lo;
+            }
+            vrange[g] = orc_ru32(rmax);
+            if (tr->vrange)
+                tr->vrange[(size_t)n * Hkv + g] = vrange[g];
+
+            for (int j = 0; j < G; j++) {
+                int h = g * G + j;
+                const uint16_t *qh = q + ((size_t)n * Hq + h) * d;
+                /* scoring pass over tier 1; the partial block is scored
+                 * from its FP16 keys */
+                for (int b = 0; b < N; b++) {
+                    orc_score_q8(d, qh, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d,
+                                 th->sm_scale, sc + (size_t)b * ORC_BT);
+                    orc_block_est(sc + (size_t)b * ORC_BT, ORC_BT, &bmax[b], &bl[b]);
+                    orc_delta_rho(d, qh, ks + (size_t)b * d, kz + (size_t)b * d, th->sm_scale, &dl[b], &rh[b]);
+                }
+                if (has_part) {
+                    for (int t = 0; t < np; t++)
+                        for (int c = 0; c < d; c++)
+                            blk[t * d + c] = Kn[((size_t)(N * ORC_BT + t) * Hkv + g) * d + c];
+                    float *sp = sc + (size_t)N * ORC_BT;
+                    orc_score_f16(d, qh, blk, np, th->sm_scale, sp);
+                    for (int t = np; t < ORC_BT; t++)
+                        sp[t] = 0.0f;
+                    orc_block_est(sp, np, &bmax[N], &bl[N]);
+                    rh[N] = rho_partial(d, qh, blk, np, th->sm_scale);
+                    dl[N] = rh[N];
+                }
+                plan_t *p = &plans[h];
+                p->N = N;
+                p->has_part = has_part;
+                p->bmax = bmax;
+                p->bl = bl;
+                p->delta = dl;
+                p->rho = rh;
+                p->eta = eta;
+                p->R = (double)vrange[g];
+                p->M = allM + (size_t)h * Np;
+                p->inP = allP + (size_t)h * nb;
+                p->inVP = allVP + (size_t)h * nb;
+                plan_head(p, th);
+                if (p->cap_fail)
+                    rung4_pre = 1;
+
+                size_t ho = (size_t)n * Hq + h;
+                if (tr->score)
+                    memcpy(tr->score + ho * Np * ORC_BT, sc, (size_t)Np * ORC_BT * sizeof(float));
+                if (tr->bmax)
+                    memcpy(tr->bmax + ho * Np, bmax, (size_t)Np * sizeof(float));
+                if (tr->bl)
+                    memcpy(tr->bl + ho * Np, bl, (size_t)Np * sizeof(float));
+                if (tr->delta)
+                    memcpy(tr->delta + ho * Np, dl, (size_t)Np * sizeof(float));
+                if (tr->rho)
+                    memcpy(tr->rho + ho * Np, rh, (size_t)Np * sizeof(float));
+                if (tr->mref)
+                    tr->mref[ho] = p->mref;
+                if (tr->mfx)
+                    memcpy(tr->mfx + ho * Np, p->M, (size_t)Np * sizeof(uint64_t));
+                if (tr->sel)
+                    for (int b = 0; b < N; b++)
+                        tr->sel[ho * N + b] = (uint8_t)(p->inP[b] | (p->inVP[b] << 1));
+                if (tr->bounds) {
+                    tr->bounds[ho * 4 + 0] = p->mu;
+                    tr->bounds[ho * 4 + 1] = p->tv;
+                    tr->bounds[ho * 4 + 2] = p->ekey;
+                    tr->bounds[ho * 4 + 3] = p->eval;
+                }
+
+                /* certified scores: FP16 keys on P (paged from tier 2) and
+                 * on the partial block, INT8 scores on the tail [Meth-3] */
+                memcpy(smix, sc, (size_t)Np * ORC_BT * sizeof(float));
+                for (int b = 0; b < N; b++) {
+                    if (!p->inP[b])
+                        continue;
+                    for (int t = 0; t < ORC_BT; t++)
+                        for (int c = 0; c < d; c++)
+                            blk[t * d + c] = Kn[((size_t)(b * ORC_BT + t) * Hkv + g) * d + c];
+                    orc_score_f16(d, qh, blk, ORC_BT, th->sm_scale, smix + (size_t)b * ORC_BT);
+                }
+                memcpy(allsmix + (size_t)h * Np * ORC_BT, smix, (size_t)Np * ORC_BT * sizeof(float));
+                memcpy(allsc + (size_t)h * Np * ORC_BT, sc, (size_t)Np * ORC_BT * sizeof(float));
+                orc_dense_head(T, Hkv, d, g, Kn, Vn, qh, sm, odense + (size_t)h * d);
+            }
+        }
+
+        /* rank-consistency check on the promoted blocks [Meth-3]: order by
+         * INT8-estimated mass vs order by FP16-key mass; Kendall discordant
+         * pairs D; inconsistent iff D > floor(rank_tol * K*(K*-1)/2). */
+        int n_rung3 = 0;
+        int64_t *Dh = (int64_t *)calloc((size_t)Hq, sizeof(int64_t));
+        int *rank_ok = (int *)malloc((size_t)Hq * sizeof(int));
+        for (int h = 0; h < Hq; h++) {
+            plan_t *p = &plans[h];
+            const float *sm16 = allsmix + (size_t)h * Np * ORC_BT;
+            int kk = 0;
+            for (int b = 0; b < N; b++)
+                if (p->inP[b])
+                    plist[kk++] = b;
+            float mr16 = -INFINITY;
+            for (int i = 0; i < kk; i++) {
+                int b = plist[i];
+                orc_block_est(sm16 + (size_t)b * ORC_BT, ORC_BT, &b16max[i], &b16l[i]);
+                if (b16max[i] > mr16)
+                    mr16 = b16max[i];
+            }
+            size_t ho = (size_t)n * Hq + h;
+            if (tr->m16fx)
+                memset(tr->m16fx + ho * N, 0, (size_t)N * sizeof(uint64_t));
+            if (tr->score16) {
+                memset(tr->score16 + ho * N * ORC_BT, 0, (size_t)N * ORC_BT * sizeof(float));
+                for (int i = 0; i < kk; i++)
+                    memcpy(tr->score16 + ho * N * ORC_BT + (size_t)plist[i] * ORC_BT,
+                           sm16 + (size_t)plist[i] * ORC_BT, ORC_BT * sizeof(float));
+            }
+            for (int i = 0; i < kk; i++) {
+                int b = plist[i];
+                float m = b16l[i] * orc_exp_c(b16max[i] - mr16);
+                uint64_t M16 = (uint64_t)((double)m * 4294967296.0);
+                if (tr->m16fx)
+                    tr->m16fx[ho * N + b] = M16;
+                keyI[i] = (p->M[b] << 16) | (uint64_t)(0xFFFF - b);
+                key16[i] = (M16 << 16) | (uint64_t)(0xFFFF - b);
+            }
+            Dh[h] = orc_discordant(kk, keyI, key16);
+            double pairs = (double)kk * (double)(kk - 1) / 2.0;
+            double lim = floor((double)th->rank_tol * pairs);
+            rank_ok[h] = !((double)Dh[h] > lim);
+            if (!rank_ok[h])
+                n_rung3++;
+        }
+        int rung4_post = !rung4_pre && ((double)n_rung3 > (double)th->f_layer * (double)Hq);
+        if (tr->seq_flags)
+            tr->seq_flags[n] = rung4_pre | (rung4_post << 1);
+
+        /* outputs */
+        for (int h = 0; h < Hq; h++) {
+            plan_t *p = &plans[h];
+            int g = h / G;
+            const uint16_t *Vg = Vn;
+            const float *smh = allsmix + (size_t)h * Np * ORC_BT;
+            const uint8_t *vcg = all_vc + (size_t)g * nb * ORC_BT * d / 2;
+            const uint16_t *vsg = all_vs + (size_t)g * nb * ORC_BT * ng;
+            const uint16_t *vzg = all_vz + (size_t)g * nb * ORC_BT * ng;
+            double *oc = ocert + (size_t)h * d;
+            double *od = odense + (size_t)h * d;
+            /* p~ over all T tokens */
+            double mx = -INFINITY;
+            for (int t = 0; t < T; t++)
+                if ((double)smh[t] > mx)
+                    mx = (double)smh[t];
+            double den = 0.0;
+            for (int t = 0; t < T; t++) {
+                ptil[t] = exp((double)smh[t] - mx);
+                den += ptil[t];
+            }
+            for (int t = 0; t < T; t++)
+                ptil[t] /= den;
+            /* exact p */
+            {
+                const uint16_t *qh = q + ((size_t)n * Hq + h) * d;
+                double m2 = -INFINITY;
+                for (int t = 0; t < T; t++) {
+                    const uint16_t *kt = Kn + ((size_t)t * Hkv + g) * d;
+                    double a = 0.0;
+                    for (int c = 0; c < d; c++)
+                        a += (double)orc_h2f(qh[c]) * (double)orc_h2f(kt[c]);
+                    pex[t] = sm * a;
+                    if (pex[t] > m2)
+                        m2 = pex[t];
+                }
+                double dd = 0.0;
+                for (int t = 0; t < T; t++) {
+                    pex[t] = exp(pex[t] - m2);
+                    dd += pex[t];
+                }
+                for (int t = 0; t < T; t++)
+                    pex[t] /= dd;
+            }
+            double ek = 0.0, ev = 0.0;
+            for (int c = 0; c < d; c++) {
+                double acc = 0.0, akey = 0.0, aval = 0.0;
+                for (int t = 0; t < T; t++) {
+                    int b = t / ORC_BT, tt = t % ORC_BT;
+                    double v = (double)orc_h2f(Vg[((size_t)t * Hkv + g) * d + c]);
+                    double vu = v;
+                    if (b < N && !p->inVP[b]) {
+                        uint8_t byte = vcg[((size_t)b * ORC_BT + tt) * (d / 2) + c / 2];
+                        int code = (c & 1) ? (byte >> 4) : (byte & 15);
+                        size_t mi = ((size_t)b * ORC_BT + tt) * ng + c / ORC_VG;
+                        vu = (double)orc_h2f(vzg[mi]) + (double)orc_h2f(vsg[mi]) * (double)code;
+                    }
+                    acc += ptil[t] * vu;
+                    akey += (ptil[t] - pex[t]) * v;
+                    aval += ptil[t] * (vu - v);
+                }
+                oc[c] = acc;
+                if (fabs(akey) > ek)
+                    ek = fabs(akey);
+                if (fabs(aval) > ev)
+                    ev = fabs(aval);
+            }
+            size_t ho = (size_t)n * Hq + h;
+            if (tr->err_key)
+                tr->err_key[ho] = ek;
+            if (tr->err_val)
+                tr->err_val[ho] = ev;
+            if (tr->o_cert)
+                memcpy(tr->o_cert + ho * d, oc, (size_t)d * sizeof(double));
+            if (tr->o_dense)
+                memcpy(tr->o_dense + ho * d, od, (size_t)d * sizeof(double));
+
+            /* ladder outcome [Meth-3, four-rung fallback ladder] */
+            int mask = 0;
+            if (p->widened)
+                mask |= 2;
+            if (p->nvp > 0)
+                mask |= 4;
+            int is3 = !rung4_pre && !rank_ok[h];
+            if (is3)
+                mask |= 8;
+            int is4 = rung4_pre || rung4_post;
+            if (is4)
+                mask |= 16;
+            dense[h] = is3 || is4;
+            int rmax = 0;
+            for (int r = 1; r <= 4; r++)
+                if (mask & (1 << r))
+                    rmax = r;
+            orc_report *R = &rep[ho];
+            R->kstar = p->kstar;
+            R->n_v_promoted = p->nvp;
+            R->tau_final = (float)p->tau;
+            R->rank_ok = rung4_pre ? -1 : rank_ok[h];
+            R->n_discordant = rung4_pre ? 0 : (int)Dh[h];
+            R->rung_mask = mask;
+            R->rung_max = rmax;
+            if (dense[h]) {
+                R->e_key = R->e_val = R->tv_bound = 0.0f;
+                memcpy(out + ho * d, od, (size_t)d * sizeof(double));
+            } else {
+                R->e_key = orc_ru32(p->ekey);
+                R->e_val = orc_ru32(p->eval);
+                R->tv_bound = orc_ru32(p->tv);
+                memcpy(out + ho * d, oc, (size_t)d * sizeof(double));
+            }
+        }
+        free(Dh);
+        free(rank_ok);
+    }
+
+    free(kc); free(ks); free(kz); free(vc); free(vs); free(vz); free(eta); free(blk); free(blv);
+    free(sc); free(bmax); free(bl); free(dl); free(rh); free(M); free(inP); free(inVP);
+    free(odense); free(ocert); free(dense); free(plans); free(allP); free(allVP); free(allM);
+    free(allsc); free(ptil); free(pex); free(s16); free(b16max); free(b16l); free(keyI); free(key16);
+    free(plist); free(vrange); free(smix); free(allsmix); free(all_vc); free(all_vs); free(all_vz);
+    return 0;
+}
