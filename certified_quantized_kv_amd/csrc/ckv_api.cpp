@@ -1,0 +1,735 @@
+// ckv_api.cpp -- host runtime and C ABI of the certified quantized-KV
+// library: cache allocation (tier 1 in HBM, tier 2 FP16 originals in pinned
+// host memory, staging and scratch), the append path, and the orchestration
+// of a decode step with its host round trips (page lists after selection,
+// rank verdicts after the promoted pass).
+//
+// Section tags refer to the page "Runtime-Certified Bounded-Error Quantized
+// Attention" (technical summary): [Meth-1] tiered storage, [Meth-3] the
+// adaptive selection and the fallback ladder.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ckv.h"
+#include "ckv_internal.hpp"
+
+using namespace ckv;
+
+namespace {
+
+thread_local std::string g_err;
+
+ckv_status fail(ckv_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define HIPCHK(expr)                                                                        \
+    do {                                                                                    \
+        hipError_t e_ = (expr);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail(CKV_EHIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_),    \
+                        __FILE__, __LINE__);                                                \
+    } while (0)
+
+enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH_N = 8 };
+
+}  // namespace
+
+struct ckv_cache {
+    ckv_config cfg{};
+    Layout Ly{};
+    int G = 0, d = 0, Nmax = 0, NS = 0, nsplit_cap = 0;
+    size_t blk_fp16 = 0;  // elements of one FP16 block
+    std::vector<void *> dev_allocs;
+    size_t dev_bytes = 0, host_bytes = 0, tier1_bytes = 0;
+    // tier 2 (pinned host)
+    uint16_t *t2k = nullptr, *t2v = nullptr;
+    // staging and scratch (device)
+    uint16_t *stage_k = nullptr, *stage_v = nullptr;
+    float *score = nullptr, *part_tail = nullptr, *part_blk = nullptr;
+    float4 *bstat = nullptr;
+    uint64_t *mfx = nullptr, *cval = nullptr, *m16 = nullptr, *keys = nullptr;
+    uint32_t *sel = nullptr, *plist = nullptr, *dmask = nullptr;
+    HeadPlan *plan = nullptr;
+    float2 *st16 = nullptr;
+    int *dskip = nullptr, *dtmp_len = nullptr;
+    // pinned host mirrors
+    uint32_t *h_sel = nullptr, *h_mask = nullptr;
+    HeadPlan *h_plan = nullptr;
+    int *h_skip = nullptr, *h_len = nullptr, *h_tmp_len = nullptr;
+    std::vector<int> len;  // [L][B]
+    // append staging (device, grown on demand)
+    uint16_t *ain_k = nullptr, *ain_v = nullptr, *pk = nullptr, *pv = nullptr;
+    size_t ain_cap = 0, pk_cap = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
+    hipEvent_t pev[12] = {};
+    std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
+    std::vector<int> seq_flags;               // [B] of the last step
+    bool have_step = false;
+    int last_batch = 0, last_np = 0, last_nb = 0;
+    bool prof = false;
+    double ms[PH_N] = {};
+    int cnt[PH_N] = {};
+    size_t bytes_paged = 0;
+};
+
+namespace {
+
+template <class T>
+ckv_status dalloc(ckv_cache *c, T **p, size_t count) {
+    void *ptr = nullptr;
+    size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+    hipError_t e = hipMalloc(&ptr, bytes);
+    if (e != hipSuccess) return fail(CKV_ENOMEM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    c->dev_allocs.push_back(ptr);
+    c->dev_bytes += bytes;
+    *p = static_cast<T *>(ptr);
+    return CKV_OK;
+}
+
+template <class T>
+ckv_status halloc(ckv_cache *c, T **p, size_t count, bool tier2 = false) {
+    void *ptr = nullptr;
+    size_t bytes = std::max<size_t>(count * sizeof(T), 64);
+    hipError_t e = hipHostMalloc(&ptr, bytes, hipHostMallocDefault);
+    if (e != hipSuccess)
+        return fail(CKV_ENOMEM, "hipHostMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    if (tier2) c->host_bytes += bytes;
+    *p = static_cast<T *>(ptr);
+    return CKV_OK;
+}
+
+#define TRY(expr)                          \
+    do {                                   \
+        ckv_status s_ = (expr);            \
+        if (s_ != CKV_OK) return s_;       \
+    } while (0)
+
+ckv_status grow(ckv_cache *c, uint16_t **a, uint16_t **b, size_t *cap, size_t need) {
+    if (need <= *cap) return CKV_OK;
+    if (*a) (void)hipFree(*a);
+    if (*b) (void)hipFree(*b);
+    *a = *b = nullptr;
+    *cap = 0;
+    HIPCHK(hipMalloc((void **)a, need * 2));
+    HIPCHK(hipMalloc((void **)b, need * 2));
+    *cap = need;
+    return CKV_OK;
+}
+
+void fill_failed_reports(ckv_head_report *r, int n) {
+    if (!r) return;
+    for (int i = 0; i < n; ++i) {
+        std::memset(&r[i], 0, sizeof r[i]);
+        r[i].rung_max = -1;
+    }
+}
+
+float ru32h(double x) {
+    float f = (float)x;
+    if ((double)f < x) f = std::nextafter(f, INFINITY);
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ckv_last_error(void) { return g_err.c_str(); }
+
+void ckv_destroy(ckv_cache *c) {
+    if (!c) return;
+    (void)hipSetDevice(c->cfg.device);
+    (void)hipDeviceSynchronize();
+    for (void *p : c->dev_allocs) (void)hipFree(p);
+    for (void *p : {(void *)c->ain_k, (void *)c->ain_v, (void *)c->pk, (void *)c->pv})
+        if (p) (void)hipFree(p);
+    for (void *p : {(void *)c->t2k, (void *)c->t2v, (void *)c->h_sel, (void *)c->h_mask,
+                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_tmp_len})
+        if (p) (void)hipHostFree(p);
+    if (c->side) (void)hipStreamDestroy(c->side);
+    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done})
+        if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->pev)
+        if (e) (void)hipEventDestroy(e);
+    delete c;
+}
+
+ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
+    if (!cfg || !out) return fail(CKV_EINVAL, "null argument");
+    *out = nullptr;
+    const ckv_config &k = *cfg;
+    if (k.n_layers < 1 || k.max_batch < 1 || k.n_kv_heads < 1 || k.n_q_heads < k.n_kv_heads ||
+        k.n_q_heads % k.n_kv_heads || (k.head_dim != 64 && k.head_dim != 128) || k.max_context < 1)
+        return fail(CKV_EINVAL, "bad cache shape");
+    const int G = k.n_q_heads / k.n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(CKV_EINVAL, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+    const int Nmax = (k.max_context + 63) / 64;
+    if (Nmax > 65536) return fail(CKV_EINVAL, "max_context above 4M tokens");
+    HIPCHK(hipSetDevice(k.device));
+    ckv_cache *c = new ckv_cache();
+    c->cfg = k;
+    c->G = G;
+    c->d = k.head_dim;
+    c->Nmax = Nmax;
+    c->NS = Nmax + 1;
+    c->nsplit_cap = c->NS;
+    c->blk_fp16 = (size_t)64 * k.head_dim;
+    const int L = k.n_layers, B = k.max_batch, Hq = k.n_q_heads, Hkv = k.n_kv_heads, d = k.head_dim;
+    const size_t nblk = (size_t)L * B * Hkv * Nmax;
+    auto cleanup = [&](ckv_status s) {
+        std::string msg = g_err;
+        ckv_destroy(c);
+        g_err = msg;
+        return s;
+    };
+#define CTRY(expr)                     \
+    do {                               \
+        ckv_status s_ = (expr);        \
+        if (s_ != CKV_OK) return cleanup(s_); \
+    } while (0)
+    Layout &Ly = c->Ly;
+    Ly.L = L; Ly.B = B; Ly.Hq = Hq; Ly.Hkv = Hkv; Ly.d = d; Ly.G = G; Ly.Nmax = Nmax;
+    // tier 1 [Meth-1]
+    size_t before = c->dev_bytes;
+    CTRY(dalloc(c, &Ly.kq, nblk * 64 * d));
+    CTRY(dalloc(c, &Ly.kmeta, nblk * d));
+    CTRY(dalloc(c, &Ly.vq, nblk * 64 * (d / 2)));
+    CTRY(dalloc(c, &Ly.vmeta, nblk * 64 * (d / 32)));
+    CTRY(dalloc(c, &Ly.eta, nblk));
+    c->tier1_bytes = c->dev_bytes - before;
+    CTRY(dalloc(c, &Ly.vmin, (size_t)L * B * Hkv * d));
+    CTRY(dalloc(c, &Ly.vmax, (size_t)L * B * Hkv * d));
+    CTRY(dalloc(c, &Ly.kpart, (size_t)L * B * Hkv * 64 * d));
+    CTRY(dalloc(c, &Ly.vpart, (size_t)L * B * Hkv * 64 * d));
+    CTRY(dalloc(c, &Ly.len, (size_t)L * B));
+    HIPCHK(hipMemset(Ly.len, 0, sizeof(int) * L * B));
+    // tier 2: FP16 originals in pinned host memory [Meth-1]
+    CTRY(halloc(c, &c->t2k, nblk * 64 * d, true));
+    CTRY(halloc(c, &c->t2v, nblk * 64 * d, true));
+    // staging for one layer-step and scratch
+    const size_t sblk = (size_t)B * Hkv * Nmax;
+    CTRY(dalloc(c, &c->stage_k, sblk * 64 * d));
+    CTRY(dalloc(c, &c->stage_v, sblk * 64 * d));
+    const size_t hsl = (size_t)B * Hq * c->NS;
+    CTRY(dalloc(c, &c->score, hsl * 64));
+    CTRY(dalloc(c, &c->bstat, hsl));
+    CTRY(dalloc(c, &c->mfx, hsl));
+    CTRY(dalloc(c, &c->cval, hsl));
+    CTRY(dalloc(c, &c->sel, sblk));
+    CTRY(dalloc(c, &c->plan, (size_t)B * Hq));
+    CTRY(dalloc(c, &c->st16, (size_t)B * Hq * Nmax));
+    CTRY(dalloc(c, &c->m16, (size_t)B * Hq * Nmax));
+    CTRY(dalloc(c, &c->part_tail, (size_t)B * Hq * c->nsplit_cap * (d + 2)));
+    CTRY(dalloc(c, &c->part_blk, hsl * (d + 2)));
+    CTRY(dalloc(c, &c->plist, (size_t)B * Hq * Nmax));
+    CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
+    CTRY(dalloc(c, &c->dskip, (size_t)B));
+    CTRY(dalloc(c, &c->dtmp_len, (size_t)B));
+    CTRY(dalloc(c, &c->dmask, (size_t)B * Hkv));
+    CTRY(halloc(c, &c->h_sel, sblk));
+    CTRY(halloc(c, &c->h_mask, (size_t)B * Hkv));
+    CTRY(halloc(c, &c->h_plan, (size_t)B * Hq));
+    CTRY(halloc(c, &c->h_skip, (size_t)B));
+    CTRY(halloc(c, &c->h_len, (size_t)L * B));
+    CTRY(halloc(c, &c->h_tmp_len, (size_t)B));
+    c->len.assign((size_t)L * B, 0);
+    c->staged_k.assign(sblk, 0);
+    c->staged_v.assign(sblk, 0);
+    HIPCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_paged, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming));
+    for (auto &e : c->pev) HIPCHK(hipEventCreate(&e));
+    *out = c;
+    return CKV_OK;
+#undef CTRY
+}
+
+ckv_status ckv_reset_sequence(ckv_cache *c, int seq) {
+    if (!c || seq < 0 || seq >= c->cfg.max_batch) return fail(CKV_EINVAL, "bad sequence");
+    HIPCHK(hipSetDevice(c->cfg.device));
+    for (int l = 0; l < c->cfg.n_layers; ++l) {
+        c->len[(size_t)l * c->cfg.max_batch + seq] = 0;
+        c->h_len[(size_t)l * c->cfg.max_batch + seq] = 0;
+    }
+    HIPCHK(hipMemcpy(c->Ly.len, c->h_len, sizeof(int) * c->cfg.n_layers * c->cfg.max_batch,
+                     hipMemcpyHostToDevice));
+    return CKV_OK;
+}
+
+ckv_status ckv_seq_length(const ckv_cache *c, int layer, int seq, int *n) {
+    if (!c || !n || layer < 0 || layer >= c->cfg.n_layers || seq < 0 || seq >= c->cfg.max_batch)
+        return fail(CKV_EINVAL, "bad layer or sequence");
+    *n = c->len[(size_t)layer * c->cfg.max_batch + seq];
+    return CKV_OK;
+}
+
+ckv_status ckv_footprint(const ckv_cache *c, size_t *dev, size_t *host, size_t *tier1) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    if (dev) *dev = c->dev_bytes;
+    if (host) *host = c->host_bytes;
+    if (tier1) *tier1 = c->tier1_bytes;
+    return CKV_OK;
+}
+
+// Append [Meth-1]: pack the new tokens (with the unfinished block's earlier
+// tokens) into whole FP16 blocks, quantize the completed blocks, keep the
+// unfinished block FP16 on the device, update the value range, and copy
+// the FP16 blocks to tier 2.
+ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k, const void *v,
+                         int ntok, int src_on_device, void *stream) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    const ckv_config &cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || seq < 0 || seq >= cf.max_batch || ntok < 0)
+        return fail(CKV_EINVAL, "bad layer, sequence or token count");
+    if (ntok == 0) return CKV_OK;
+    if (!k || !v) return fail(CKV_EINVAL, "null K or V");
+    const size_t li = (size_t)layer * cf.max_batch + seq;
+    const int len0 = c->len[li];
+    if ((long)len0 + ntok > cf.max_context)
+        return fail(CKV_ERANGE, "append of %d tokens to %d exceeds max_context %d", ntok, len0,
+                    cf.max_context);
+    HIPCHK(hipSetDevice(cf.device));
+    hipStream_t s = (hipStream_t)stream;
+    const int d = c->d, Hkv = cf.n_kv_heads;
+    const size_t tokel = (size_t)Hkv * d;
+    const uint16_t *kin = (const uint16_t *)k, *vin = (const uint16_t *)v;
+    if (!src_on_device) {
+        TRY(grow(c, &c->ain_k, &c->ain_v, &c->ain_cap, (size_t)ntok * tokel));
+        HIPCHK(hipMemcpyAsync(c->ain_k, k, (size_t)ntok * tokel * 2, hipMemcpyHostToDevice, s));
+        HIPCHK(hipMemcpyAsync(c->ain_v, v, (size_t)ntok * tokel * 2, hipMemcpyHostToDevice, s));
+        kin = c->ain_k;
+        vin = c->ain_v;
+    }
+    const int b0 = len0 / 64;
+    const int new_len = len0 + ntok;
+    const int b_end = (new_len - 1) / 64;
+    const int nblk = b_end - b0 + 1;
+    TRY(grow(c, &c->pk, &c->pv, &c->pk_cap, (size_t)Hkv * nblk * c->blk_fp16));
+    const Layout &Ly = c->Ly;
+    HIPCHK(launch_pack(Ly, layer, seq, kin, vin, len0, ntok, b0, nblk, c->pk, c->pv, s));
+    const int nfull = new_len / 64 - b0;
+    HIPCHK(launch_quant(Ly, layer, seq, b0, nfull, nblk, c->pk, c->pv, s));
+    if (new_len % 64) HIPCHK(launch_set_partial(Ly, layer, seq, nblk - 1, nblk, c->pk, c->pv, s));
+    HIPCHK(launch_vrange(Ly, layer, seq, vin, ntok, len0 == 0, s));
+    for (int g = 0; g < Hkv; ++g) {
+        const size_t dst = Ly.blk(layer, seq, g, b0) * c->blk_fp16;
+        const size_t src = (size_t)g * nblk * c->blk_fp16;
+        HIPCHK(hipMemcpyAsync(c->t2k + dst, c->pk + src, (size_t)nblk * c->blk_fp16 * 2,
+                              hipMemcpyDeviceToHost, s));
+        HIPCHK(hipMemcpyAsync(c->t2v + dst, c->pv + src, (size_t)nblk * c->blk_fp16 * 2,
+                              hipMemcpyDeviceToHost, s));
+    }
+    c->h_len[li] = new_len;
+    HIPCHK(hipMemcpyAsync(c->Ly.len + li, c->h_len + li, sizeof(int), hipMemcpyHostToDevice, s));
+    HIPCHK(hipStreamSynchronize(s));
+    c->len[li] = new_len;
+    return CKV_OK;
+}
+
+namespace {
+
+// Page FP16 blocks of (seq n, kv head g) whose flag is set from tier 2 into
+// the staging area, one hipMemcpyAsync per run of consecutive blocks.
+ckv_status page_runs(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
+                     std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage,
+                     size_t *bytes) {
+    const Layout &Ly = c->Ly;
+    const size_t sb = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
+    int b = 0;
+    while (b < N) {
+        if (!want[b] || staged[sb + b]) {
+            ++b;
+            continue;
+        }
+        int e = b;
+        while (e < N && want[e] && !staged[sb + e]) ++e;
+        const size_t nbytes = (size_t)(e - b) * c->blk_fp16 * 2;
+        HIPCHK(hipMemcpyAsync(stage + (sb + b) * c->blk_fp16, t2 + Ly.blk(layer, n, g, b) * c->blk_fp16,
+                              nbytes, hipMemcpyHostToDevice, c->side));
+        for (int i = b; i < e; ++i) staged[sb + i] = 1;
+        *bytes += nbytes;
+        b = e;
+    }
+    return CKV_OK;
+}
+
+}  // namespace
+
+ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q, int batch,
+                                          const ckv_thresholds *th, float *out,
+                                          ckv_head_report *report, void *stream) {
+    auto t_start = std::chrono::steady_clock::now();
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    const ckv_config &cf = c->cfg;
+    const int Hq = cf.n_q_heads, Hkv = cf.n_kv_heads, G = c->G, d = c->d;
+    if (report && batch > 0 && batch <= cf.max_batch) fill_failed_reports(report, batch * Hq);
+    if (layer < 0 || layer >= cf.n_layers || batch < 1 || batch > cf.max_batch || !q || !th || !out ||
+        !report)
+        return fail(CKV_EINVAL, "bad layer, batch or null pointer");
+    if (!(th->tau_cov > 0.0f && th->tau_cov <= 1.0f) || !(th->sm_scale > 0.0f) ||
+        !std::isfinite(th->sm_scale) || th->n_widen < 0 || std::isnan(th->k_tol) ||
+        std::isnan(th->v_tol) || std::isnan(th->rank_tol) || std::isnan(th->f_layer))
+        return fail(CKV_EINVAL, "bad thresholds");
+    int nb = 0, np_any = 0;
+    for (int n = 0; n < batch; ++n) {
+        const int L_ = c->len[(size_t)layer * cf.max_batch + n];
+        if (L_ < 1) return fail(CKV_ESTATE, "sequence %d of layer %d is empty", n, layer);
+        nb = std::max(nb, L_ / 64);
+        np_any |= (L_ % 64) != 0;
+    }
+    HIPCHK(hipSetDevice(cf.device));
+    hipStream_t s = (hipStream_t)stream;
+    const Layout &Ly = c->Ly;
+
+    Step St{};
+    St.layer = layer;
+    St.batch = batch;
+    St.nb = nb;
+    St.NS = c->NS;
+    St.bps = std::max(1, std::min(64, (nb * Hkv * batch + 2047) / 2048));
+    St.nsplit = (nb + St.bps - 1) / St.bps;
+    St.nsplit_cap = c->nsplit_cap;
+    St.sm = th->sm_scale;
+    St.q = (const uint16_t *)q;
+    St.score = c->score;
+    St.bstat = c->bstat;
+    St.mfx = c->mfx;
+    St.cval = c->cval;
+    St.sel = c->sel;
+    St.plan = c->plan;
+    St.st16 = c->st16;
+    St.m16 = c->m16;
+    St.part_tail = c->part_tail;
+    St.part_blk = c->part_blk;
+    St.stage_k = c->stage_k;
+    St.stage_v = c->stage_v;
+    St.out = out;
+    Th T{};
+    T.tau = th->tau_cov;
+    T.k_tol = th->k_tol;
+    T.v_tol = th->v_tol;
+    T.rank_tol = th->rank_tol;
+    T.f_layer = th->f_layer;
+    T.n_widen = th->n_widen;
+    T.vcap = th->v_cap_blocks;
+
+    hipEvent_t *E = c->pev;
+    const bool prof = c->prof;
+    if (prof) HIPCHK(hipEventRecord(E[0], s));
+    // K1: INT8 scoring pass; K2: selection, bounds, rungs 1-2
+    HIPCHK(launch_score(Ly, St, s));
+    if (prof) HIPCHK(hipEventRecord(E[1], s));
+    HIPCHK(launch_select(Ly, St, T, s));
+    if (prof) HIPCHK(hipEventRecord(E[2], s));
+    // page lists and plans to the host (the round trip of the selection)
+    const size_t selbytes = (size_t)batch * Hkv * Ly.Nmax * sizeof(uint32_t);
+    HIPCHK(hipMemcpyAsync(c->h_sel, c->sel, selbytes, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipEventRecord(c->ev_sel, s));
+    // K3: tail blocks, overlapping the paging below
+    if (prof) HIPCHK(hipEventRecord(E[3], s));
+    if (St.nsplit > 0) HIPCHK(launch_tail(Ly, St, s));
+    if (prof) HIPCHK(hipEventRecord(E[4], s));
+    HIPCHK(hipEventSynchronize(c->ev_sel));
+
+    // rung 4 before paging: a cap exhausted on any head of the sequence
+    std::vector<uint8_t> wantk(Ly.Nmax), wantv(Ly.Nmax);
+    std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
+    std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
+    size_t paged = 0;
+    if (prof) HIPCHK(hipEventRecord(E[5], c->side));
+    for (int n = 0; n < batch; ++n) {
+        int skip = 0;
+        for (int h = 0; h < Hq; ++h) skip |= (c->h_plan[(size_t)n * Hq + h].flags >> 1) & 1;
+        c->h_skip[n] = skip;
+        const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
+        for (int g = 0; g < Hkv; ++g) {
+            const uint32_t *sl = c->h_sel + ((size_t)n * Hkv + g) * Ly.Nmax;
+            for (int b = 0; b < N; ++b) {
+                wantk[b] = skip || (sl[b] & 0xFFu);
+                wantv[b] = skip || ((sl[b] >> 8) & 0xFFu);
+            }
+            TRY(page_runs(c, layer, n, g, N, wantk.data(), c->staged_k, c->t2k, c->stage_k, &paged));
+            TRY(page_runs(c, layer, n, g, N, wantv.data(), c->staged_v, c->t2v, c->stage_v, &paged));
+        }
+    }
+    HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side));
+    if (prof) HIPCHK(hipEventRecord(E[6], c->side));
+    HIPCHK(hipEventRecord(c->ev_paged, c->side));
+    HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
+    // K4: promoted blocks, rank check, merge
+    if (prof) HIPCHK(hipEventRecord(E[7], s));
+    HIPCHK(launch_promoted(Ly, St, c->dskip, s));
+    HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, s));
+    if (prof) HIPCHK(hipEventRecord(E[8], s));
+    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipEventRecord(c->ev_done, s));
+    HIPCHK(hipEventSynchronize(c->ev_done));
+
+    // rungs 3 and 4 [Meth-3]: per-head dense on an inconsistent ranking;
+    // the whole layer (per sequence) when more than f_layer of the heads
+    // fell back, or when a cap was exhausted before paging.
+    std::vector<int> dense((size_t)batch * Hq, 0), r4post(batch, 0);
+    bool any_dense = false;
+    for (int n = 0; n < batch; ++n) {
+        int n3 = 0;
+        for (int h = 0; h < Hq; ++h) n3 += !c->h_skip[n] && c->h_plan[(size_t)n * Hq + h].rank_ok == 0;
+        r4post[n] = !c->h_skip[n] && ((double)n3 > (double)th->f_layer * (double)Hq);
+        for (int h = 0; h < Hq; ++h) {
+            const HeadPlan &P = c->h_plan[(size_t)n * Hq + h];
+            dense[(size_t)n * Hq + h] = c->h_skip[n] || r4post[n] || P.rank_ok == 0;
+            any_dense |= dense[(size_t)n * Hq + h] != 0;
+        }
+    }
+    if (any_dense) {
+        if (prof) HIPCHK(hipEventRecord(E[9], c->side));
+        std::vector<uint8_t> all(Ly.Nmax, 1);
+        for (int n = 0; n < batch; ++n) {
+            const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
+            for (int g = 0; g < Hkv; ++g) {
+                uint32_t m = 0;
+                for (int j = 0; j < G; ++j) m |= (uint32_t)dense[(size_t)n * Hq + g * G + j] << j;
+                c->h_mask[n * Hkv + g] = m;
+                if (m) {
+                    TRY(page_runs(c, layer, n, g, N, all.data(), c->staged_k, c->t2k, c->stage_k, &paged));
+                    TRY(page_runs(c, layer, n, g, N, all.data(), c->staged_v, c->t2v, c->stage_v, &paged));
+                }
+            }
+        }
+        HIPCHK(hipMemcpyAsync(c->dmask, c->h_mask, sizeof(uint32_t) * batch * Hkv, hipMemcpyHostToDevice,
+                              c->side));
+        HIPCHK(hipEventRecord(c->ev_paged, c->side));
+        HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
+        DenseSrc S{};
+        S.k = c->stage_k;
+        S.v = c->stage_v;
+        S.kp = Ly.kpart + Ly.seqg(layer, 0, 0) * c->blk_fp16;
+        S.vp = Ly.vpart + Ly.seqg(layer, 0, 0) * c->blk_fp16;
+        S.len = Ly.len + (size_t)layer * cf.max_batch;
+        S.nstride = Ly.Nmax;
+        S.mask = c->dmask;
+        S.q = (const uint16_t *)q;
+        S.sm = th->sm_scale;
+        S.part = c->part_tail;
+        S.nsplit_cap = c->nsplit_cap;
+        S.bps = St.bps;
+        S.Hq = Hq;
+        S.Hkv = Hkv;
+        S.out = out;
+        const int nsl = nb + np_any;
+        HIPCHK(launch_dense_src(d, G, S, (nsl + S.bps - 1) / S.bps, batch, s));
+        if (prof) HIPCHK(hipEventRecord(E[10], s));
+        HIPCHK(hipEventRecord(c->ev_done, s));
+        HIPCHK(hipEventSynchronize(c->ev_done));
+    }
+
+    // report [Meth-2 bounds per head and step; Meth-3 ladder]
+    for (int n = 0; n < batch; ++n)
+        for (int h = 0; h < Hq; ++h) {
+            const size_t i = (size_t)n * Hq + h;
+            const HeadPlan &P = c->h_plan[i];
+            ckv_head_report &R = report[i];
+            int mask = 0;
+            if (P.flags & 1) mask |= 2;
+            if (P.nvp > 0) mask |= 4;
+            const bool r3 = !c->h_skip[n] && P.rank_ok == 0;
+            if (r3) mask |= 8;
+            if (c->h_skip[n] || r4post[n]) mask |= 16;
+            int rmax = 0;
+            for (int r = 1; r <= 4; ++r)
+                if (mask & (1 << r)) rmax = r;
+            R.kstar = P.kstar;
+            R.n_v_promoted = P.nvp;
+            R.tau_final = (float)P.tau;
+            R.rank_ok = c->h_skip[n] ? -1 : P.rank_ok;
+            R.n_discordant = c->h_skip[n] ? 0 : P.ndisc;
+            R.rung_mask = mask;
+            R.rung_max = rmax;
+            if (dense[i]) {
+                R.e_key = R.e_val = R.tv_bound = 0.0f;
+            } else {
+                R.e_key = ru32h(P.ekey);
+                R.e_val = ru32h(P.eval);
+                R.tv_bound = ru32h(P.tv);
+            }
+        }
+    c->seq_flags.assign(batch, 0);
+    for (int n = 0; n < batch; ++n) c->seq_flags[n] = c->h_skip[n] | (r4post[n] << 1);
+    c->have_step = true;
+    c->last_batch = batch;
+    c->last_nb = nb;
+    c->last_np = nb + np_any;
+    c->bytes_paged += paged;
+    if (prof) {
+        float t;
+        auto acc = [&](int ph, int a, int b) -> ckv_status {
+            HIPCHK(hipEventElapsedTime(&t, E[a], E[b]));
+            c->ms[ph] += t;
+            c->cnt[ph] += 1;
+            return CKV_OK;
+        };
+        TRY(acc(PH_SCORE, 0, 1));
+        TRY(acc(PH_SELECT, 1, 2));
+        if (St.nsplit > 0) TRY(acc(PH_TAIL, 3, 4));
+        TRY(acc(PH_PAGE, 5, 6));
+        TRY(acc(PH_PROMO, 7, 8));
+        if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
+        c->ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+        c->cnt[PH_STEP] += 1;
+    }
+    return CKV_OK;
+}
+
+ckv_status ckv_dense_decode_attention(ckv_cache *c, const void *k, const void *v, int ntok,
+                                      const void *q, int batch, float sm, float *out, void *stream) {
+    if (!c || !k || !v || !q || !out) return fail(CKV_EINVAL, "null argument");
+    const ckv_config &cf = c->cfg;
+    if (batch < 1 || batch > cf.max_batch || ntok < 64 || ntok % 64 || ntok > c->Nmax * 64 || !(sm > 0))
+        return fail(CKV_EINVAL, "bad batch, token count (multiple of 64) or scale");
+    HIPCHK(hipSetDevice(cf.device));
+    hipStream_t s = (hipStream_t)stream;
+    for (int n = 0; n < batch; ++n) c->h_tmp_len[n] = ntok;
+    HIPCHK(hipMemcpyAsync(c->dtmp_len, c->h_tmp_len, sizeof(int) * batch, hipMemcpyHostToDevice, s));
+    DenseSrc S{};
+    S.k = (const uint16_t *)k;
+    S.v = (const uint16_t *)v;
+    S.kp = S.vp = nullptr;
+    S.len = c->dtmp_len;
+    S.nstride = (size_t)ntok / 64;
+    S.mask = nullptr;
+    S.q = (const uint16_t *)q;
+    S.sm = sm;
+    S.part = c->part_tail;
+    S.nsplit_cap = c->nsplit_cap;
+    const int nb = ntok / 64;
+    S.bps = std::max(1, std::min(64, (nb * cf.n_kv_heads * batch + 2047) / 2048));
+    S.Hq = cf.n_q_heads;
+    S.Hkv = cf.n_kv_heads;
+    S.out = out;
+    HIPCHK(launch_dense_src(c->d, c->G, S, (nb + S.bps - 1) / S.bps, batch, s));
+    return CKV_OK;
+}
+
+ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int g, int b, uint8_t *k_code,
+                            uint16_t *k_s, uint16_t *k_z, uint8_t *v_code, uint16_t *v_s,
+                            uint16_t *v_z, float *eta) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    const ckv_config &cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || seq < 0 || seq >= cf.max_batch || g < 0 ||
+        g >= cf.n_kv_heads || b < 0 || (long)(b + 1) * 64 > c->len[(size_t)layer * cf.max_batch + seq])
+        return fail(CKV_EINVAL, "block not complete or out of range");
+    HIPCHK(hipSetDevice(cf.device));
+    const Layout &Ly = c->Ly;
+    const int d = c->d;
+    const size_t bi = Ly.blk(layer, seq, g, b);
+    if (k_code) {
+        std::vector<uint8_t> raw((size_t)64 * d);
+        HIPCHK(hipMemcpy(raw.data(), Ly.kq + bi * 64 * d, raw.size(), hipMemcpyDeviceToHost));
+        for (int t = 0; t < 64; ++t)
+            for (int ch = 0; ch < d; ++ch) k_code[t * d + ch] = raw[(ch / 16) * 1024 + t * 16 + ch % 16];
+    }
+    if (k_s || k_z) {
+        std::vector<uint32_t> m(d);
+        HIPCHK(hipMemcpy(m.data(), Ly.kmeta + bi * d, d * 4, hipMemcpyDeviceToHost));
+        for (int ch = 0; ch < d; ++ch) {
+            if (k_s) k_s[ch] = (uint16_t)(m[ch] & 0xFFFFu);
+            if (k_z) k_z[ch] = (uint16_t)(m[ch] >> 16);
+        }
+    }
+    if (v_code) HIPCHK(hipMemcpy(v_code, Ly.vq + bi * 64 * (d / 2), 64 * (d / 2), hipMemcpyDeviceToHost));
+    if (v_s || v_z) {
+        std::vector<uint32_t> m(64 * (d / 32));
+        HIPCHK(hipMemcpy(m.data(), Ly.vmeta + bi * 64 * (d / 32), m.size() * 4, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < m.size(); ++i) {
+            if (v_s) v_s[i] = (uint16_t)(m[i] & 0xFFFFu);
+            if (v_z) v_z[i] = (uint16_t)(m[i] >> 16);
+        }
+    }
+    if (eta) HIPCHK(hipMemcpy(eta, Ly.eta + bi, 4, hipMemcpyDeviceToHost));
+    return CKV_OK;
+}
+
+ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, float *bstat,
+                           float *mref, uint64_t *mfx, uint32_t *sel, uint64_t *m16fx, double *bounds,
+                           int *seq_flags) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    if (!c->have_step) return fail(CKV_ESTATE, "no decode step yet");
+    if (batch < 1 || batch > c->last_batch) return fail(CKV_EINVAL, "bad batch");
+    HIPCHK(hipSetDevice(c->cfg.device));
+    const int Hq = c->cfg.n_q_heads, Hkv = c->cfg.n_kv_heads, NS = c->NS, Np = c->last_np,
+              N = c->last_nb, Nmax = c->Nmax;
+    if (np_out) *np_out = Np;
+    for (int n = 0; n < batch; ++n)
+        for (int h = 0; h < Hq; ++h) {
+            const size_t hs = (size_t)n * Hq + h, ho = hs;
+            if (score)
+                HIPCHK(hipMemcpy(score + ho * Np * 64, c->score + hs * NS * 64, (size_t)Np * 64 * 4,
+                                 hipMemcpyDeviceToHost));
+            if (bstat)
+                HIPCHK(hipMemcpy(bstat + ho * Np * 4, c->bstat + hs * NS, (size_t)Np * 16, hipMemcpyDeviceToHost));
+            if (mfx)
+                HIPCHK(hipMemcpy(mfx + ho * Np, c->mfx + hs * NS, (size_t)Np * 8, hipMemcpyDeviceToHost));
+            if (m16fx && N)
+                HIPCHK(hipMemcpy(m16fx + ho * Np, c->m16 + hs * Nmax, (size_t)N * 8, hipMemcpyDeviceToHost));
+        }
+    if (sel && N)
+        for (int n = 0; n < batch; ++n)
+            for (int g = 0; g < Hkv; ++g)
+                HIPCHK(hipMemcpy(sel + ((size_t)n * Hkv + g) * Np, c->sel + ((size_t)n * Hkv + g) * Nmax,
+                                 (size_t)N * 4, hipMemcpyDeviceToHost));
+    if (mref || bounds) {
+        std::vector<HeadPlan> P((size_t)batch * Hq);
+        HIPCHK(hipMemcpy(P.data(), c->plan, sizeof(HeadPlan) * P.size(), hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < P.size(); ++i) {
+            if (mref) mref[i] = P[i].mref;
+            if (bounds) {
+                bounds[i * 4 + 0] = P[i].mu;
+                bounds[i * 4 + 1] = P[i].tv;
+                bounds[i * 4 + 2] = P[i].ekey;
+                bounds[i * 4 + 3] = P[i].eval;
+            }
+        }
+    }
+    if (seq_flags)
+        for (int n = 0; n < batch; ++n) seq_flags[n] = c->seq_flags[n];
+    return CKV_OK;
+}
+
+ckv_status ckv_set_profiling(ckv_cache *c, int enable) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    c->prof = enable != 0;
+    std::memset(c->ms, 0, sizeof c->ms);
+    std::memset(c->cnt, 0, sizeof c->cnt);
+    c->bytes_paged = 0;
+    return CKV_OK;
+}
+
+ckv_status ckv_get_phase_times(ckv_cache *c, double *ms, int *counts, size_t *bytes_paged) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    for (int i = 0; i < PH_N; ++i) {
+        if (ms) ms[i] = c->ms[i];
+        if (counts) counts[i] = c->cnt[i];
+    }
+    if (bytes_paged) *bytes_paged = c->bytes_paged;
+    return CKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+// ckv_append.hip -- tier-1 construction [Meth-1 of the page "Runtime-
+// Certified Bounded-Error Quantized Attention": INT8 per-channel keys, INT4
+// per-group values, scales/offsets and per-block error annotations].
+//
+// Readings (where the page is silent): the key scale/offset is per channel
+// per 64-token block; the value scale/offset per token per 32-channel group;
+// both affine with offset = the exact FP16 minimum and scale = range /
+// levels rounded up to FP16, so no code is clamped; eta_b = the largest
+// absolute value-reconstruction error of the block, exact in FP64, rounded
+// up to FP32.
+#include "ckv_device.hpp"
+#include "ckv_internal.hpp"
+
+namespace ckv {
+
+// Pack tokens [len0, len0 + ntok) of (l, n), plus the unfinished block's
+// earlier tokens, into whole FP16 blocks b0 .. b0 + nblk - 1 in the tier-2
+// layout.  kin / vin: [ntok][Hkv][d].  Slots past the last token are 0.
+__global__ __launch_bounds__(256) void k_pack(Layout Ly, int l, int n, const uint16_t *kin,
+                                              const uint16_t *vin, int len0, int ntok, int b0,
+                                              int nblk, uint16_t *pk, uint16_t *pv) {
+    const int bi = blockIdx.x, g = blockIdx.y, d = Ly.d;
+    const size_t sg = Ly.seqg(l, n, g);
+    const uint16_t *kp = Ly.kpart + sg * 64 * d;
+    const uint16_t *vp = Ly.vpart + sg * 64 * d;
+    uint16_t *ok = pk + ((size_t)g * nblk + bi) * 64 * d;
+    uint16_t *ov = pv + ((size_t)g * nblk + bi) * 64 * d;
+    for (int e = threadIdx.x; e < 64 * d; e += blockDim.x) {
+        const int t = e / d, c = e % d;
+        const long i = (long)(b0 + bi) * 64 + t;
+        uint16_t kv = 0, vv = 0;
+        if (i < len0) {
+            kv = kp[(c / 8) * 512 + t * 8 + (c % 8)];
+            vv = vp[t * d + c];
+        } else if (i < (long)len0 + ntok) {
+            const size_t src = ((size_t)(i - len0) * Ly.Hkv + g) * d + c;
+            kv = kin[src];
+            vv = vin[src];
+        }
+        ok[(c / 8) * 512 + t * 8 + (c % 8)] = kv;
+        ov[t * d + c] = vv;
+    }
+}
+
+__device__ __forceinline__ int quant_code(float x, float lo, float s, float maxc) {
+    if (s == 0.0f) return 0;
+    float c = rintf((x - lo) / s);
+    c = c < 0.0f ? 0.0f : c;
+    c = c > maxc ? maxc : c;
+    return (int)c;
+}
+
+// Quantize full packed blocks 0 .. nfull-1 (block b0 + bi of the sequence).
+template <int D>
+__global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, int nblk,
+                                               const uint16_t *pk, const uint16_t *pv) {
+    const int bi = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    const size_t blk = Ly.blk(l, n, g, b0 + bi);
+    const uint16_t *kb = pk + ((size_t)g * nblk + bi) * 64 * D;
+    const uint16_t *vb = pv + ((size_t)g * nblk + bi) * 64 * D;
+    __shared__ double emax_s[128];
+
+    // keys: one thread per channel
+    if (tid < D) {
+        const int c = tid;
+        const uint16_t *col = kb + (c / 8) * 512 + (c % 8);
+        float lo = h2f(col[0]), hi = lo;
+        for (int t = 1; t < 64; ++t) {
+            float x = h2f(col[t * 8]);
+            lo = fminf(lo, x);
+            hi = fmaxf(hi, x);
+        }
+        const float r = hi - lo;
+        const uint16_t sb = r == 0.0f ? (uint16_t)0 : f2h_up(r / 255.0f);
+        const uint16_t zb = lo == 0.0f ? (uint16_t)0 : __half_as_ushort(__float2half_rn(lo));
+        const float sf = h2f(sb);
+        Ly.kmeta[blk * D + c] = (uint32_t)sb | ((uint32_t)zb << 16);
+        uint8_t *kq = Ly.kq + blk * 64 * D + (c / 16) * 1024 + (c % 16);
+        for (int t = 0; t < 64; ++t) kq[t * 16] = (uint8_t)quant_code(h2f(col[t * 8]), lo, sf, 255.0f);
+    }
+    // values: one thread per token
+    double emax = 0.0;
+    if (tid < 64) {
+        const int t = tid;
+        const uint16_t *row = vb + t * D;
+        uint8_t *vq = Ly.vq + blk * 64 * (D / 2) + t * (D / 2);
+        uint32_t *vm = Ly.vmeta + blk * 64 * (D / 32) + t * (D / 32);
+        for (int gr = 0; gr < D / 32; ++gr) {
+            float lo = h2f(row[gr * 32]), hi = lo;
+            for (int c = 1; c < 32; ++c) {
+                float x = h2f(row[gr * 32 + c]);
+                lo = fminf(lo, x);
+                hi = fmaxf(hi, x);
+            }
+            const float r = hi - lo;
+            const uint16_t sb = r == 0.0f ? (uint16_t)0 : f2h_up(r / 15.0f);
+            const uint16_t zb = lo == 0.0f ? (uint16_t)0 : __half_as_ushort(__float2half_rn(lo));
+            const float sf = h2f(sb);
+            vm[gr] = (uint32_t)sb | ((uint32_t)zb << 16);
+            for (int c = 0; c < 32; c += 2) {
+                const float x0 = h2f(row[gr * 32 + c]), x1 = h2f(row[gr * 32 + c + 1]);
+                const int q0 = quant_code(x0, lo, sf, 15.0f), q1 = quant_code(x1, lo, sf, 15.0f);
+                vq[(gr * 32 + c) / 2] = (uint8_t)(q0 | (q1 << 4));
+                const double r0 = (double)lo + (double)sf * (double)q0;
+                const double r1 = (double)lo + (double)sf * (double)q1;
+                emax = fmax(emax, fabs((double)x0 - r0));
+                emax = fmax(emax, fabs((double)x1 - r1));
+            }
+        }
+    }
+    emax_s[tid] = emax;
+    __syncthreads();
+    if (tid == 0) {
+        double m = 0.0;
+        for (int i = 0; i < 64; ++i) m = fmax(m, emax_s[i]);
+        Ly.eta[blk] = ru32(m);
+    }
+}
+
+// Copy packed block `bi` (the unfinished one) into the device FP16 slot.
+__global__ __launch_bounds__(256) void k_set_partial(Layout Ly, int l, int n, int bi, int nblk,
+                                                     const uint16_t *pk, const uint16_t *pv) {
+    const int g = blockIdx.x, d = Ly.d;
+    const size_t sg = Ly.seqg(l, n, g);
+    const uint16_t *sk = pk + ((size_t)g * nblk + bi) * 64 * d;
+    const uint16_t *sv = pv + ((size_t)g * nblk + bi) * 64 * d;
+    for (int e = threadIdx.x; e < 64 * d; e += blockDim.x) {
+        Ly.kpart[sg * 64 * d + e] = sk[e];
+        Ly.vpart[sg * 64 * d + e] = sv[e];
+    }
+}
+
+__global__ void k_vrange_init(Layout Ly, int l, int n) {
+    const int g = blockIdx.x, c = threadIdx.x;
+    if (c < Ly.d) {
+        Ly.vmin[Ly.seqg(l, n, g) * Ly.d + c] = 0xFFFFFFFFu;
+        Ly.vmax[Ly.seqg(l, n, g) * Ly.d + c] = 0u;
+    }
+}
+
+// Running per-channel min / max of V ("value ranges" of [Meth-2]).
+__global__ __launch_bounds__(128) void k_vrange(Layout Ly, int l, int n, const uint16_t *vin,
+                                                int ntok, int chunk) {
+    const int g = blockIdx.x, c = threadIdx.x, d = Ly.d;
+    if (c >= d) return;
+    const int t0 = blockIdx.y * chunk, t1 = min(ntok, t0 + chunk);
+    if (t0 >= t1) return;
+    float lo = h2f(vin[((size_t)t0 * Ly.Hkv + g) * d + c]), hi = lo;
+    for (int t = t0 + 1; t < t1; ++t) {
+        const float x = h2f(vin[((size_t)t * Ly.Hkv + g) * d + c]);
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+    }
+    atomicMin(&Ly.vmin[Ly.seqg(l, n, g) * d + c], f2ord(lo));
+    atomicMax(&Ly.vmax[Ly.seqg(l, n, g) * d + c], f2ord(hi));
+}
+
+hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,
+                       int len0, int ntok, int b0, int nblk, uint16_t *pk, uint16_t *pv,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(k_pack, dim3(nblk, Ly.Hkv), dim3(256), 0, s, Ly, l, n, kin, vin, len0, ntok,
+                       b0, nblk, pk, pv);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant(const Layout &Ly, int l, int n, int b0, int nfull, int nblk,
+                        const uint16_t *pk, const uint16_t *pv, hipStream_t s) {
+    if (nfull <= 0) return hipSuccess;
+    if (Ly.d == 64)
+        hipLaunchKernelGGL(k_quant<64>, dim3(nfull, Ly.Hkv), dim3(128), 0, s, Ly, l, n, b0, nblk, pk, pv);
+    else
+        hipLaunchKernelGGL(k_quant<128>, dim3(nfull, Ly.Hkv), dim3(128), 0, s, Ly, l, n, b0, nblk, pk, pv);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_partial(const Layout &Ly, int l, int n, int slot, int nblk,
+                              const uint16_t *pk, const uint16_t *pv, hipStream_t s) {
+    hipLaunchKernelGGL(k_set_partial, dim3(Ly.Hkv), dim3(256), 0, s, Ly, l, n, slot, nblk, pk, pv);
+    return hipGetLastError();
+}
+
+hipError_t launch_vrange(const Layout &Ly, int l, int n, const uint16_t *vin, int ntok, int reset,
+                         hipStream_t s) {
+    if (reset) hipLaunchKernelGGL(k_vrange_init, dim3(Ly.Hkv), dim3(128), 0, s, Ly, l, n);
+    const int chunk = 256;
+    const int nch = (ntok + chunk - 1) / chunk;
+    hipLaunchKernelGGL(k_vrange, dim3(Ly.Hkv, nch), dim3(128), 0, s, Ly, l, n, vin, ntok, chunk);
+    return hipGetLastError();
+}
+
+}  // namespace ckv

@@ -1,0 +1,1000 @@
+// ckv_decode.hip -- kernels of the certified decode step.
+//
+// Section tags refer to the page "Runtime-Certified Bounded-Error Quantized
+// Attention" (technical summary): [Meth-2] two-term error decomposition,
+// [Meth-3] adaptive top-K selection, rank-consistency check and the
+// four-rung fallback ladder, [Contrib] bounds computable without the FP16
+// originals during the main pass.
+//
+//   k_score     INT8 scoring pass: one wave per (seq, kv head, block); lane =
+//               token; 16-byte coalesced code loads; per-block weights
+//               w_c = q_c s_c staged in LDS.  Block max / mass / Delta / rho.
+//   k_select    per (seq, q head): estimated masses, top-K* by radix select,
+//               E_key / E_val, rung 1 (widen), rung 2 (FP16 values).
+//   k_tail      split-K flash decoding over blocks outside P and VP, INT4
+//               values unpacked in registers, online softmax partials.
+//   k_promoted  FP16-key scores of P blocks (from the staging area), FP16
+//               values of VP blocks, per-block partials and FP16 masses.
+//   k_merge     rank-consistency check + merge of all partials -> output.
+//   k_dense     exact attention on FP16 blocks (rungs 3 / 4, and the dense
+//               comparator), split-K partials; k_merge_dense -> output.
+#include <type_traits>
+
+#include "ckv_device.hpp"
+#include "ckv_internal.hpp"
+
+namespace ckv {
+
+template <class F>
+static hipError_t dispatch(int d, int G, F f) {
+#define CKV_CASE(DD, GG) \
+    if (d == DD && G == GG) return f(std::integral_constant<int, DD>{}, std::integral_constant<int, GG>{});
+    CKV_CASE(64, 1) CKV_CASE(64, 2) CKV_CASE(64, 4) CKV_CASE(64, 8)
+    CKV_CASE(128, 1) CKV_CASE(128, 2) CKV_CASE(128, 4) CKV_CASE(128, 8)
+#undef CKV_CASE
+    return hipErrorInvalidValue;
+}
+
+// ===========================================================================
+// K1: INT8 scoring pass [Meth-3 "lightweight scoring pass using INT8 keys to
+// estimate per-block attention masses"] and the per-token score
+// perturbation bound [Meth-2 "bounded by the per-token score perturbation"].
+//   s^_t = (a_t + C) * sm, a_t = fma chain over c of w_c * code_tc,
+//   w_c = q_c s_c, C = halving-tree sum of q_c z_c;
+//   Delta = sm (kappa H + gamma(d+3) A) (1 + 2^-20), rho = sm 2^-23 A (1 + 2^-20)
+//   with H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c), both FP64 trees.
+// ===========================================================================
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
+    constexpr int CPL = D / 64;  // channels per lane
+    const int slot = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+    const int l = St.layer;
+    const int len = Ly.len[l * Ly.B + n];
+    const int N = len / 64, np = len % 64;
+    if (slot > N || (slot == N && np == 0)) return;
+    __shared__ float qs[G][D];
+    __shared__ float w[G][D];
+    for (int i = lane; i < G * D; i += 64)
+        qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
+    __syncthreads();
+    const float sm = St.sm;
+    const size_t NS64 = (size_t)St.NS * 64;
+
+    if (slot == N) {
+        // unfinished block: FP16 keys on the device, FP64 chain, one rounding
+        const uint16_t *kp = Ly.kpart + Ly.seqg(l, n, g) * 64 * D;
+        const bool valid = lane < np;
+        double a[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) a[j] = 0.0;
+        for (int ch = 0; ch < D / 8; ++ch) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(kp + ch * 512 + lane * 8);
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double kc = (double)h2f((uint16_t)(wd[i / 2] >> (16 * (i & 1))));
+#pragma unroll
+                for (int j = 0; j < G; ++j) a[j] = fma((double)qs[j][ch * 8 + i], kc, a[j]);
+            }
+        }
+        // rho of the unfinished block: A = sum |q_c| max_t |k_tc|
+        double kmax[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const int c = lane + 64 * k;
+            double m = 0.0;
+            for (int t = 0; t < np; ++t) m = fmax(m, fabs((double)h2f(kp[(c / 8) * 512 + t * 8 + (c % 8)])));
+            kmax[k] = m;
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int h = g * G + j;
+            const float s = valid ? (float)(a[j] * (double)sm) : 0.0f;
+            St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane] = s;
+            const float mx = wave_max_f32(valid ? s : -INFINITY);
+            const float l_ = tree64_f32(valid ? exp_c(s - mx) : 0.0f);
+            double av = fabs((double)qs[j][lane]) * kmax[0];
+            if (CPL == 2) av = av + fabs((double)qs[j][lane + 64]) * kmax[CPL - 1];
+            const double A = tree64_f64(av);
+            if (lane == 0) {
+                double rh = A * 0x1p-23;
+                rh = rh * (double)sm;
+                rh = rh * (1.0 + 0x1p-20);
+                const float r = ru32(rh);
+                St.bstat[(size_t)(n * Ly.Hq + h) * St.NS + slot] = make_float4(mx, l_, r, r);
+            }
+        }
+        return;
+    }
+
+    // full block
+    const size_t bi = Ly.blk(l, n, g, slot);
+    if (lane == 0) St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot] = 0u;
+    float sc[CPL], zc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const uint32_t m = Ly.kmeta[bi * D + lane + 64 * k];
+        sc[k] = h2f((uint16_t)(m & 0xFFFFu));
+        zc[k] = h2f((uint16_t)(m >> 16));
+    }
+    float Cj[G], dj[G], rj[G];
+    const double kappa = 0.5 + 0x1p-14;
+    const double gam = gamma_n(D + 3);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float cz = qs[j][lane] * zc[0];
+        double hv = fabs((double)qs[j][lane]) * (double)sc[0];
+        double av = fabs((double)qs[j][lane]) * (fabs((double)zc[0]) + 255.0 * (double)sc[0]);
+        w[j][lane] = qs[j][lane] * sc[0];
+        if (CPL == 2) {
+            const float q1 = qs[j][lane + 64];
+            cz = cz + q1 * zc[CPL - 1];
+            hv = hv + fabs((double)q1) * (double)sc[CPL - 1];
+            av = av + fabs((double)q1) * (fabs((double)zc[CPL - 1]) + 255.0 * (double)sc[CPL - 1]);
+            w[j][lane + 64] = q1 * sc[CPL - 1];
+        }
+        const float C = tree64_f32(cz);
+        const double H = tree64_f64(hv);
+        const double A = tree64_f64(av);
+        Cj[j] = __shfl(C, 0, 64);
+        double dl = kappa * H + gam * A;
+        dl = dl * (double)sm;
+        dl = dl * (1.0 + 0x1p-20);
+        double rh = A * 0x1p-23;
+        rh = rh * (double)sm;
+        rh = rh * (1.0 + 0x1p-20);
+        dj[j] = ru32(dl);  // meaningful in lane 0
+        rj[j] = ru32(rh);
+    }
+    __syncthreads();
+
+    const uint8_t *kb = Ly.kq + bi * 64 * D;
+    float acc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j] = 0.0f;
+#pragma unroll 2
+    for (int ch = 0; ch < D / 16; ++ch) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(kb + ch * 1024 + lane * 16);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float cf = (float)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j] = fmaf(w[j][ch * 16 + i], cf, acc[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int h = g * G + j;
+        const float s = (acc[j] + Cj[j]) * sm;
+        St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane] = s;
+        const float mx = wave_max_f32(s);
+        const float l_ = tree64_f32(exp_c(s - mx));
+        if (lane == 0) St.bstat[(size_t)(n * Ly.Hq + h) * St.NS + slot] = make_float4(mx, l_, dj[j], rj[j]);
+    }
+}
+
+// ===========================================================================
+// K2: selection, bounds, rungs 1-2 [Meth-2, Meth-3, Contrib].
+// One 256-thread workgroup per (q head, sequence).
+// ===========================================================================
+constexpr int SEL_T = 256;
+
+struct SelShared {
+    uint64_t hsum[64];
+    uint32_t hsat[64];
+    uint64_t red_u[SEL_T / 64];
+    double red_d[SEL_T / 64];
+    float red_f[SEL_T / 64];
+    int red_i[SEL_T / 64];
+    uint64_t bc_u[4];
+    int bc_i[2];
+};
+
+__device__ __forceinline__ float block_max_f(float v, SelShared &sh) {
+    v = wave_max_f32(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh.red_f[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh.red_f[0];
+    for (int i = 1; i < SEL_T / 64; ++i) r = fmaxf(r, sh.red_f[i]);
+    return r;
+}
+__device__ __forceinline__ double block_max_d(double v, SelShared &sh) {
+    v = wave_max_f64(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh.red_d[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = sh.red_d[0];
+    for (int i = 1; i < SEL_T / 64; ++i) r = fmax(r, sh.red_d[i]);
+    return r;
+}
+__device__ __forceinline__ uint64_t block_sum_u(uint64_t v, SelShared &sh) {
+    v = wave_sum_u64(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh.red_u[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t r = 0;
+    for (int i = 0; i < SEL_T / 64; ++i) r += sh.red_u[i];
+    return r;
+}
+__device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
+    v = wave_sum_i32(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh.red_i[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = 0;
+    for (int i = 0; i < SEL_T / 64; ++i) r += sh.red_i[i];
+    return r;
+}
+
+// Radix select with 6-bit digits over 64-bit keys key(b) = (val_b << 16) |
+// (0xFFFF - b), unique per block, so "key desc" is the order (value desc,
+// index asc).  TOP: the largest threshold t with sum_{key >= t} val >= need
+// (the fewest blocks reaching `need`).  REST: the largest t whose rest
+// sum_{key < t} val satisfies E <= tol with no capped term left (the fewest
+// blocks to promote).  Returns t; the chosen set is {key >= t}.
+template <bool TOP>
+__device__ uint64_t radix_select(const uint64_t *val, int N, uint64_t need, double tol,
+                                 SelShared &sh) {
+    const int tid = threadIdx.x;
+    uint64_t prefix = 0, outside = 0;  // TOP: sum above the region; REST: sum below
+    uint32_t sat_out = 0;
+    for (int shift = 60; shift >= 0; shift -= 6) {
+        if (tid < 64) {
+            sh.hsum[tid] = 0;
+            sh.hsat[tid] = 0;
+        }
+        __syncthreads();
+        const uint64_t himask = (shift + 6 >= 64) ? 0ull : (~0ull << (shift + 6));
+        for (int b = tid; b < N; b += SEL_T) {
+            const uint64_t v = val[b];
+            const uint64_t key = (v << 16) | (uint64_t)(0xFFFF - b);
+            if ((key & himask) == (prefix & himask)) {
+                const int dg = (int)((key >> shift) & 63);
+                atomicAdd((unsigned long long *)&sh.hsum[dg], (unsigned long long)v);
+                if (!TOP && v >= FXCAP) atomicAdd(&sh.hsat[dg], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            const int dg = tid;
+            const uint64_t s = sh.hsum[dg];
+            const uint32_t cs = sh.hsat[dg];
+            bool pred;
+            uint64_t add = 0;
+            uint32_t addc = 0;
+            if (TOP) {
+                // suffix sum over digits >= dg
+                uint64_t suf = s;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint64_t x = __shfl_down(suf, o, 64);
+                    if (dg + o < 64) suf += x;
+                }
+                pred = (outside + suf >= need) || dg == 0;
+                add = suf - s;  // sum over digits > dg
+            } else {
+                // exclusive prefix over digits < dg
+                uint64_t pre = s;
+                uint32_t pc = cs;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint64_t x = __shfl_up(pre, o, 64);
+                    const uint32_t y = __shfl_up(pc, o, 64);
+                    if (dg >= o) { pre += x; pc += y; }
+                }
+                pre -= s;
+                pc -= cs;
+                const uint64_t rem = outside + pre;
+                const bool satr = (sat_out + pc) != 0;
+                pred = !(fx_bound(rem, satr) > tol) || dg == 0;
+                add = pre;
+                addc = pc;
+            }
+            const uint64_t bal = __ballot(pred);
+            const int best = 63 - __builtin_clzll(bal);  // largest digit with pred
+            if (dg == best) {
+                sh.bc_u[0] = prefix | ((uint64_t)best << shift);
+                sh.bc_u[1] = outside + add;
+                sh.bc_i[0] = (int)(sat_out + addc);
+            }
+        }
+        __syncthreads();
+        prefix = sh.bc_u[0];
+        outside = sh.bc_u[1];
+        sat_out = (uint32_t)sh.bc_i[0];
+        __syncthreads();
+    }
+    return prefix;
+}
+
+__device__ __forceinline__ bool in_set(const uint64_t *val, int b, uint64_t thr) {
+    return ((val[b] << 16) | (uint64_t)(0xFFFF - b)) >= thr;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
+    __shared__ SelShared sh;
+    const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
+    const int g = h / G, j = h % G, l = St.layer;
+    const int len = Ly.len[l * Ly.B + n];
+    const int N = len / 64, has_part = (len % 64) != 0, Np = N + has_part;
+    const size_t hs = (size_t)n * Ly.Hq + h;
+    const float4 *bs = St.bstat + hs * St.NS;
+    uint64_t *M = St.mfx + hs * St.NS;
+    uint64_t *cv = St.cval + hs * St.NS;
+
+    // estimated masses in fixed point
+    float m = -INFINITY;
+    for (int b = tid; b < Np; b += SEL_T) m = fmaxf(m, bs[b].x);
+    const float mref = block_max_f(m, sh);
+    uint64_t s = 0;
+    for (int b = tid; b < Np; b += SEL_T) {
+        const float4 st = bs[b];
+        const float mh = st.y * exp_c(st.x - mref);
+        const uint64_t Mb = (uint64_t)((double)mh * 4294967296.0);
+        M[b] = Mb;
+        s += Mb;
+    }
+    const uint64_t S = block_sum_u(s, sh);
+    const uint64_t Mpart = has_part ? M[N] : 0;
+
+    // range of V for this kv head: R = max_c (max - min), rounded up
+    double rr = 0.0;
+    for (int c = tid; c < D; c += SEL_T) {
+        const size_t vi = Ly.seqg(l, n, g) * D + c;
+        rr = fmax(rr, (double)ord2f(Ly.vmax[vi]) - (double)ord2f(Ly.vmin[vi]));
+    }
+    const double R = (double)ru32(block_max_d(rr, sh));
+
+    const double Sd = (double)S;
+    auto phat = [&](uint64_t Mb) { return ((double)(Mb + 1) / Sd) * (1.0 + 0x1p-16); };
+
+    double tau = (double)th.tau;
+    int widened = 0, cap_fail = 0;
+    uint64_t thrP = ~0ull;
+    double F = 1.0, mu = 0.0, tv = 1.0, ekey = 0.0;
+    for (int wv = 0;; ++wv) {
+        const uint64_t T = (uint64_t)ceil(tau * Sd);
+        const uint64_t need = T > Mpart ? T - Mpart : 0;
+        thrP = radix_select<true>(M, N, need, 0.0, sh);
+        // F = exp(max over P of (Delta + rho))
+        double fm = 0.0;
+        for (int b = tid; b < N; b += SEL_T)
+            if (in_set(M, b, thrP)) fm = fmax(fm, (double)bs[b].z + (double)bs[b].w);
+        F = expu(block_max_d(fm, sh));
+        uint64_t sum = 0;
+        int sat = 0;
+        double dmax = 0.0;
+        for (int b = tid; b < N; b += SEL_T) {
+            const float4 st = bs[b];
+            const bool p = in_set(M, b, thrP);
+            const double dl = p ? (double)st.w : (double)st.z;
+            const double X = p ? expu((double)st.z + (double)st.w) : 1.0;
+            const uint64_t u = fx(phat(M[b]) * F * X * em1u(dl) * (1.0 + 0x1p-48));
+            sat |= (u == FXCAP);
+            sum += u;
+            dmax = fmax(dmax, dl);
+        }
+        if (has_part && tid == 0) {
+            const double dl = (double)bs[N].w;
+            const uint64_t u = fx(phat(M[N]) * F * 1.0 * em1u(dl) * (1.0 + 0x1p-48));
+            sat |= (u == FXCAP);
+            sum += u;
+            dmax = fmax(dmax, dl);
+        }
+        sum = block_sum_u(sum, sh);
+        sat = block_sum_i(sat, sh);
+        dmax = block_max_d(dmax, sh);
+        mu = fx_bound(sum, sat != 0);
+        tv = 1.0;
+        if (mu < 1.0) tv = mu / (1.0 - mu) * (1.0 + 0x1p-48);
+        const double thb = tanhu(dmax);
+        if (thb < tv) tv = thb;
+        if (tv > 1.0) tv = 1.0;
+        ekey = tv * R * (1.0 + 0x1p-50);
+        if (!(ekey > (double)th.k_tol)) break;
+        if (wv >= th.n_widen) {
+            cap_fail = 1;
+            break;
+        }
+        tau = 1.0 - (1.0 - tau) * 0.5;
+        widened = 1;
+    }
+
+    // E_val contributions with the final P; rung 2 by radix select
+    uint64_t tot = 0;
+    int satv = 0;
+    for (int b = tid; b < N; b += SEL_T) {
+        const float4 st = bs[b];
+        const bool p = in_set(M, b, thrP);
+        const double X = p ? expu((double)st.z + (double)st.w) : 1.0;
+        const double e = (double)Ly.eta[Ly.blk(l, n, g, b)];
+        const uint64_t u = fx(phat(M[b]) * F * X * e * (1.0 + 0x1p-48));
+        cv[b] = u;
+        tot += u;
+        satv |= (u == FXCAP);
+    }
+    __syncthreads();
+    const uint64_t thrV = radix_select<false>(cv, N, 0, (double)th.v_tol, sh);
+    uint64_t rest = 0;
+    int nvp = 0, kst = 0, satr = 0;
+    for (int b = tid; b < N; b += SEL_T) {
+        const bool v = in_set(cv, b, thrV);
+        const bool p = in_set(M, b, thrP);
+        nvp += v;
+        kst += p;
+        if (!v) {
+            rest += cv[b];
+            satr |= (cv[b] == FXCAP);
+        }
+        const uint32_t bits = (p ? (1u << j) : 0u) | (v ? (1u << (8 + j)) : 0u);
+        if (bits) atomicOr(&St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b], bits);
+    }
+    rest = block_sum_u(rest, sh);
+    nvp = block_sum_i(nvp, sh);
+    kst = block_sum_i(kst, sh);
+    satr = block_sum_i(satr, sh);
+    const double eval = fx_bound(rest, satr != 0);
+    if ((th.vcap > 0 && nvp > th.vcap) || eval > (double)th.v_tol) cap_fail = 1;
+    (void)tot;
+    (void)satv;
+    if (tid == 0) {
+        HeadPlan P;
+        P.mu = mu;
+        P.tv = tv;
+        P.ekey = ekey;
+        P.eval = eval;
+        P.tau = tau;
+        P.mref = mref;
+        P.kstar = kst;
+        P.nvp = nvp;
+        P.flags = widened | (cap_fail << 1);
+        P.rank_ok = -1;
+        P.ndisc = 0;
+        P.S = S;
+        St.plan[hs] = P;
+    }
+}
+
+// ===========================================================================
+// K3: tail flash decoding over blocks outside P and VP [Meth-3: "remaining
+// tail blocks stay INT8"], values from INT4 codes.  One wave per (split,
+// kv head, sequence); lane owns D/64 channels; online softmax per q head.
+// Output path only: hardware exp and any summation order are allowed here.
+// ===========================================================================
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_tail(Layout Ly, Step St) {
+    constexpr int CPL = D / 64;
+    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+    const int l = St.layer;
+    const int len = Ly.len[l * Ly.B + n];
+    const int N = len / 64;
+    const int b0 = sp * St.bps, b1 = min(N, b0 + St.bps);
+    __shared__ uint8_t codes[64 * (D / 2)];
+    __shared__ float zs[64][D / 32], ss[64][D / 32];
+    __shared__ float pw[G][64];
+    float mrun[G], lrun[G], acc[G][CPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        mrun[j] = -INFINITY;
+        lrun[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[j][k] = 0.0f;
+    }
+    const size_t NS64 = (size_t)St.NS * 64;
+    for (int b = b0; b < b1; ++b) {
+        const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b];
+        const uint32_t use = ~(bits | (bits >> 8)) & ((1u << G) - 1u);
+        if (!use) continue;
+        const size_t bi = Ly.blk(l, n, g, b);
+        // stage INT4 codes + metadata
+        {
+            const uint4 *src = reinterpret_cast<const uint4 *>(Ly.vq + bi * 64 * (D / 2));
+            uint4 *dst = reinterpret_cast<uint4 *>(codes);
+            for (int i = lane; i < 64 * (D / 2) / 16; i += 64) dst[i] = src[i];
+            const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
+            for (int i = lane; i < 64 * (D / 32); i += 64) {
+                const uint32_t mm = vm[i];
+                ss[i / (D / 32)][i % (D / 32)] = h2f((uint16_t)(mm & 0xFFFFu));
+                zs[i / (D / 32)][i % (D / 32)] = h2f((uint16_t)(mm >> 16));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (!(use & (1u << j))) {
+                pw[j][lane] = 0.0f;
+                continue;
+            }
+            const int h = g * G + j;
+            const float s = St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane];
+            const float bm = St.bstat[(size_t)(n * Ly.Hq + h) * St.NS + b].x;
+            const float mn = fmaxf(mrun[j], bm);
+            const float sc = __expf(mrun[j] - mn);
+            mrun[j] = mn;
+            lrun[j] *= sc;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) acc[j][k] *= sc;
+            const float p = __expf(s - mn);
+            pw[j][lane] = p;
+            float ps = p;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
+            lrun[j] += ps;
+        }
+        __syncthreads();
+        for (int t = 0; t < 64; ++t) {
+            float v[CPL];
+            if (CPL == 2) {
+                const uint8_t byte = codes[t * (D / 2) + lane];
+                const int gr = (2 * lane) / 32;
+                v[0] = fmaf(ss[t][gr], (float)(byte & 15), zs[t][gr]);
+                v[CPL - 1] = fmaf(ss[t][gr], (float)(byte >> 4), zs[t][gr]);
+            } else {
+                const uint8_t byte = codes[t * (D / 2) + lane / 2];
+                const int gr = lane / 32;
+                v[0] = fmaf(ss[t][gr], (float)((lane & 1) ? (byte >> 4) : (byte & 15)), zs[t][gr]);
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float p = pw[j][t];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) acc[j][k] = fmaf(p, v[k], acc[j][k]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int h = g * G + j;
+        float *o = St.part_tail + ((size_t)(n * Ly.Hq + h) * St.nsplit_cap + sp) * (D + 2);
+        if (lane == 0) {
+            o[0] = mrun[j];
+            o[1] = lrun[j];
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) o[2 + lane * CPL + k] = acc[j][k];
+    }
+}
+
+// ===========================================================================
+// K4a: promoted blocks.  FP16-key scores of P blocks from the staging area
+// (FP64 chain, one rounding: the decision arithmetic of the rank check),
+// their FP16-side block estimate; values FP16 (VP) or INT4; partials.
+// One wave per (slot, kv head, sequence); the unfinished block is handled
+// here for every head.
+// ===========================================================================
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_promoted(Layout Ly, Step St, const int *skip_seq) {
+    constexpr int CPL = D / 64;
+    const int slot = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+    const int l = St.layer;
+    if (skip_seq[n]) return;
+    const int len = Ly.len[l * Ly.B + n];
+    const int N = len / 64, np = len % 64;
+    if (slot > N || (slot == N && np == 0)) return;
+    const bool part = slot == N;
+    uint32_t pm = 0, vm = 0;
+    if (!part) {
+        const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot];
+        pm = bits & 0xFFu;
+        vm = (bits >> 8) & 0xFFu;
+        if (!(pm | vm)) return;
+    }
+    __shared__ float qs[G][D];
+    __shared__ float pw[G][64];
+    __shared__ float vv[64][D + 1];
+    for (int i = lane; i < G * D; i += 64)
+        qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
+    const size_t NS64 = (size_t)St.NS * 64;
+    const size_t sblk = ((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot;
+    __syncthreads();
+
+    // FP16-key scores for the P heads
+    float s16[G];
+    if (!part && pm) {
+        const uint16_t *kb = St.stage_k + sblk * 64 * D;
+        double a[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) a[j] = 0.0;
+        for (int ch = 0; ch < D / 8; ++ch) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double kc = (double)h2f((uint16_t)(wd[i / 2] >> (16 * (i & 1))));
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    if (pm & (1u << j)) a[j] = fma((double)qs[j][ch * 8 + i], kc, a[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            s16[j] = (float)(a[j] * (double)St.sm);
+            if (pm & (1u << j)) {
+                const float mx = wave_max_f32(s16[j]);
+                const float l_ = tree64_f32(exp_c(s16[j] - mx));
+                if (lane == 0) St.st16[((size_t)n * Ly.Hq + g * G + j) * Ly.Nmax + slot] = make_float2(mx, l_);
+            }
+        }
+    }
+    // values of the block into LDS (FP32)
+    const bool any_fp16v = part || vm;
+    const bool any_int4 = !part && ((pm | vm) & ~vm);
+    // weights per head
+    float mloc[G], lsum[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int h = g * G + j;
+        const bool use = part || ((pm | vm) & (1u << j));
+        if (!use) {
+            pw[j][lane] = 0.0f;
+            mloc[j] = -INFINITY;
+            lsum[j] = 0.0f;
+            continue;
+        }
+        float s;
+        bool valid = true;
+        if (part) {
+            s = St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane];
+            valid = lane < np;
+        } else if (pm & (1u << j)) {
+            s = s16[j];
+        } else {
+            s = St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane];
+        }
+        const float mx = wave_max_f32(valid ? s : -INFINITY);
+        const float p = valid ? __expf(s - mx) : 0.0f;
+        pw[j][lane] = p;
+        float ps = p;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
+        mloc[j] = mx;
+        lsum[j] = ps;
+    }
+    // two passes over value sources: FP16 (for heads in VP / unfinished) and INT4
+    float acc[G][CPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[j][k] = 0.0f;
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 0 && !any_fp16v) continue;
+        if (pass == 1 && !any_int4) continue;
+        __syncthreads();
+        if (pass == 0) {
+            const uint16_t *vb = part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + sblk * 64 * D;
+            for (int e = lane; e < 64 * D; e += 64) vv[e / D][e % D] = h2f(vb[e]);
+        } else {
+            const size_t bi = Ly.blk(l, n, g, slot);
+            const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
+            const uint32_t *vmt = Ly.vmeta + bi * 64 * (D / 32);
+            for (int e = lane; e < 64 * (D / 2); e += 64) {
+                const int t = e / (D / 2), cb = e % (D / 2);
+                const uint8_t byte = vq[e];
+                const uint32_t mm = vmt[t * (D / 32) + (2 * cb) / 32];
+                const float sf = h2f((uint16_t)(mm & 0xFFFFu)), zf = h2f((uint16_t)(mm >> 16));
+                vv[t][2 * cb] = fmaf(sf, (float)(byte & 15), zf);
+                vv[t][2 * cb + 1] = fmaf(sf, (float)(byte >> 4), zf);
+            }
+        }
+        __syncthreads();
+        uint32_t heads = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const bool use = part || ((pm | vm) & (1u << j));
+            const bool fp16v = part || (vm & (1u << j));
+            if (use && (fp16v == (pass == 0))) heads |= 1u << j;
+        }
+        for (int t = 0; t < 64; ++t) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (!(heads & (1u << j))) continue;
+                const float p = pw[j][t];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) acc[j][k] = fmaf(p, vv[t][lane + 64 * k], acc[j][k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const bool use = part || ((pm | vm) & (1u << j));
+        if (!use) continue;
+        const int h = g * G + j;
+        float *o = St.part_blk + ((size_t)(n * Ly.Hq + h) * St.NS + slot) * (D + 2);
+        if (lane == 0) {
+            o[0] = mloc[j];
+            o[1] = lsum[j];
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) o[2 + lane + 64 * k] = acc[j][k];
+    }
+}
+
+// ===========================================================================
+// K4b: rank-consistency check [Meth-3] + merge of the partials -> output.
+// One wave per (q head, sequence).  Fixed-point FP16 masses M16 on P relative
+// to the largest FP16 block max of P; Kendall discordant pairs against the
+// INT8 order; inconsistent iff D > floor(rank_tol * K*(K*-1)/2).
+// ===========================================================================
+constexpr int RANK_LDS = 2048;
+
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const int *skip_seq,
+                                              uint32_t *plist_g, uint64_t *keys_g) {
+    constexpr int CPL = D / 64;
+    const int h = blockIdx.x, n = blockIdx.y, lane = threadIdx.x;
+    const int g = h / G, j = h % G, l = St.layer;
+    if (skip_seq[n]) return;
+    const int len = Ly.len[l * Ly.B + n];
+    const int N = len / 64, np = len % 64;
+    const size_t hs = (size_t)n * Ly.Hq + h;
+    const uint32_t *sel = St.sel + ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
+    __shared__ uint32_t lds_list[RANK_LDS];
+    __shared__ uint64_t lds_kI[RANK_LDS], lds_k16[RANK_LDS];
+    __shared__ int cnt_s;
+
+    // compact list of P blocks (ascending index)
+    const uint32_t bitP = 1u << j;
+    uint32_t *plist = plist_g + hs * Ly.Nmax;
+    int K = 0;
+    for (int b0 = 0; b0 < N; b0 += 64) {
+        const int b = b0 + lane;
+        const bool inP = b < N && (sel[b] & bitP);
+        const uint64_t bal = __ballot(inP);
+        const int pos = K + __popcll(bal & ((1ull << lane) - 1ull));
+        if (inP) {
+            plist[pos] = (uint32_t)b;
+            if (pos < RANK_LDS) lds_list[pos] = (uint32_t)b;
+        }
+        K += __popcll(bal);
+    }
+    __syncthreads();
+    const bool use_lds = K <= RANK_LDS;
+    const uint32_t *list = use_lds ? lds_list : plist;
+    uint64_t *kI = use_lds ? lds_kI : keys_g + hs * 2 * Ly.Nmax;
+    uint64_t *k16 = use_lds ? lds_k16 : keys_g + hs * 2 * Ly.Nmax + Ly.Nmax;
+    const float2 *st16 = St.st16 + hs * Ly.Nmax;
+    float mr = -INFINITY;
+    for (int i = lane; i < K; i += 64) mr = fmaxf(mr, st16[list[i]].x);
+    mr = wave_max_f32(mr);
+    const uint64_t *M = St.mfx + hs * St.NS;
+    for (int i = lane; i < K; i += 64) {
+        const uint32_t b = list[i];
+        const float2 s = st16[b];
+        const float m16 = s.y * exp_c(s.x - mr);
+        const uint64_t M16 = (uint64_t)((double)m16 * 4294967296.0);
+        St.m16[hs * Ly.Nmax + b] = M16;
+        kI[i] = (M[b] << 16) | (uint64_t)(0xFFFF - b);
+        k16[i] = (M16 << 16) | (uint64_t)(0xFFFF - b);
+    }
+    __syncthreads();
+    long long D_ = 0;
+    for (int i = lane; i < K; i += 64) {
+        const uint64_t a = kI[i], c = k16[i];
+        for (int q = i + 1; q < K; ++q) D_ += ((a > kI[q]) != (c > k16[q]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) D_ += __shfl_xor(D_, o, 64);
+    const double pairs = (double)K * (double)(K - 1) / 2.0;
+    const double lim = floor((double)th.rank_tol * pairs);
+    const int ok = !((double)D_ > lim);
+    if (lane == 0) {
+        St.plan[hs].rank_ok = ok;
+        St.plan[hs].ndisc = (int)D_;
+    }
+
+    // merge: tail splits, then used blocks in ascending order, then the
+    // unfinished block
+    float mx = -INFINITY;
+    const int nsp = (N + St.bps - 1) / St.bps;
+    const float *pt = St.part_tail + hs * St.nsplit_cap * (D + 2);
+    const float *pb = St.part_blk + hs * St.NS * (D + 2);
+    const uint32_t usebits = bitP | (bitP << 8);
+    for (int s = 0; s < nsp; ++s) mx = fmaxf(mx, pt[s * (D + 2)]);
+    for (int b = 0; b < N; ++b)
+        if (sel[b] & usebits) mx = fmaxf(mx, pb[(size_t)b * (D + 2)]);
+    if (np) mx = fmaxf(mx, pb[(size_t)N * (D + 2)]);
+    float den = 0.0f, num[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) num[k] = 0.0f;
+    auto add = [&](const float *p) {
+        const float m = p[0];
+        if (m == -INFINITY) return;
+        const float e = __expf(m - mx);
+        den = fmaf(e, p[1], den);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) num[k] = fmaf(e, p[2 + lane + 64 * k], num[k]);
+    };
+    for (int s = 0; s < nsp; ++s) add(pt + (size_t)s * (D + 2));
+    for (int b = 0; b < N; ++b)
+        if (sel[b] & usebits) add(pb + (size_t)b * (D + 2));
+    if (np) add(pb + (size_t)N * (D + 2));
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) St.out[hs * D + lane + 64 * k] = num[k] / den;
+}
+
+// ===========================================================================
+// K5: exact attention on FP16 blocks (rungs 3 / 4 [Meth-1 fallback, Meth-3]
+// and the dense comparator).  Blocks of (seq, kv head) are at
+// kbase + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
+// token-major); `nfull[n]` full blocks, then an optional unfinished block.
+// ===========================================================================
+
+
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_dense(DenseSrc S) {
+    constexpr int CPL = D / 64;
+    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+    const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
+    if (!mask) return;
+    const int len = S.len[n];
+    const int N = len / 64, np = len % 64;
+    const int nslot = N + (np ? 1 : 0);
+    const int b0 = sp * S.bps, b1 = min(nslot, b0 + S.bps);
+    __shared__ float qs[G][D];
+    __shared__ float pw[G][64];
+    __shared__ float vv[64][D + 1];
+    for (int i = lane; i < G * D; i += 64)
+        qs[i / D][i % D] = h2f(S.q[((size_t)n * S.Hq + g * G + i / D) * D + (i % D)]);
+    __syncthreads();
+    float mrun[G], lrun[G], acc[G][CPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        mrun[j] = -INFINITY;
+        lrun[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[j][k] = 0.0f;
+    }
+    for (int b = b0; b < b1; ++b) {
+        const bool part = b == N;
+        const uint16_t *kb, *vb;
+        if (part) {
+            kb = S.kp + ((size_t)n * S.Hkv + g) * 64 * D;
+            vb = S.vp + ((size_t)n * S.Hkv + g) * 64 * D;
+        } else {
+            kb = S.k + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
+            vb = S.v + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
+        }
+        const bool valid = !part || lane < np;
+        float a[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) a[j] = 0.0f;
+        for (int ch = 0; ch < D / 8; ++ch) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float kc = h2f((uint16_t)(wd[i / 2] >> (16 * (i & 1))));
+#pragma unroll
+                for (int j = 0; j < G; ++j) a[j] = fmaf(qs[j][ch * 8 + i], kc, a[j]);
+            }
+        }
+        __syncthreads();
+        for (int e = lane; e < 64 * D; e += 64) vv[e / D][e % D] = h2f(vb[e]);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float s = a[j] * S.sm;
+            const float bm = wave_max_f32(valid ? s : -INFINITY);
+            const float mn = fmaxf(mrun[j], bm);
+            const float sc = __expf(mrun[j] - mn);
+            mrun[j] = mn;
+            lrun[j] *= sc;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) acc[j][k] *= sc;
+            const float p = valid ? __expf(s - mn) : 0.0f;
+            pw[j][lane] = p;
+            float ps = p;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
+            lrun[j] += ps;
+        }
+        __syncthreads();
+        for (int t = 0; t < 64; ++t) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float p = pw[j][t];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) acc[j][k] = fmaf(p, vv[t][lane + 64 * k], acc[j][k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        if (!(mask & (1u << j))) continue;
+        const int h = g * G + j;
+        float *o = S.part + ((size_t)(n * S.Hq + h) * S.nsplit_cap + sp) * (D + 2);
+        if (lane == 0) {
+            o[0] = mrun[j];
+            o[1] = lrun[j];
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) o[2 + lane + 64 * k] = acc[j][k];
+    }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_merge_dense(DenseSrc S) {
+    constexpr int CPL = D / 64;
+    const int h = blockIdx.x, n = blockIdx.y, lane = threadIdx.x;
+    const int g = h / G, j = h % G;
+    const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
+    if (!(mask & (1u << j))) return;
+    const int len = S.len[n];
+    const int nslot = len / 64 + ((len % 64) ? 1 : 0);
+    const int nsp = (nslot + S.bps - 1) / S.bps;
+    const float *pt = S.part + (size_t)(n * S.Hq + h) * S.nsplit_cap * (D + 2);
+    float mx = -INFINITY;
+    for (int s = 0; s < nsp; ++s) mx = fmaxf(mx, pt[(size_t)s * (D + 2)]);
+    float den = 0.0f, num[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) num[k] = 0.0f;
+    for (int s = 0; s < nsp; ++s) {
+        const float *p = pt + (size_t)s * (D + 2);
+        if (p[0] == -INFINITY) continue;
+        const float e = __expf(p[0] - mx);
+        den = fmaf(e, p[1], den);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) num[k] = fmaf(e, p[2 + lane + 64 * k], num[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) S.out[((size_t)n * S.Hq + h) * D + lane + 64 * k] = num[k] / den;
+}
+
+// ---- launchers -------------------------------------------------------------
+
+hipError_t launch_score(const Layout &Ly, const Step &St, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        hipLaunchKernelGGL((k_score<decltype(D)::value, decltype(G)::value>),
+                           dim3(St.nb + 1, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        hipLaunchKernelGGL((k_select<decltype(D)::value, decltype(G)::value>),
+                           dim3(Ly.Hq, St.batch), dim3(SEL_T), 0, s, Ly, St, th);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        hipLaunchKernelGGL((k_tail<decltype(D)::value, decltype(G)::value>),
+                           dim3(St.nsplit, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        hipLaunchKernelGGL((k_promoted<decltype(D)::value, decltype(G)::value>),
+                           dim3(St.nb + 1, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St, skip_seq);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, const int *skip_seq,
+                             uint32_t *plist, uint64_t *keys, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        hipLaunchKernelGGL((k_merge<decltype(D)::value, decltype(G)::value>),
+                           dim3(Ly.Hq, St.batch), dim3(64), 0, s, Ly, St, th, skip_seq, plist, keys);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_dense_src(int d, int G, const DenseSrc &S, int nsplit, int batch, hipStream_t s) {
+    return dispatch(d, G, [&](auto D, auto GG) {
+        hipLaunchKernelGGL((k_dense<decltype(D)::value, decltype(GG)::value>),
+                           dim3(nsplit, S.Hkv, batch), dim3(64), 0, s, S);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_merge_dense<decltype(D)::value, decltype(GG)::value>),
+                           dim3(S.Hq, batch), dim3(64), 0, s, S);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace ckv

@@ -1,0 +1,159 @@
+// ckv_device.hpp -- device helpers of the certified quantized-KV library.
+//
+// Decision arithmetic (codes, scores, masses, bounds, verdicts) must give the
+// same bits on every run and every launch shape, so it is written here as a
+// fixed sequence of single IEEE operations: FP32 fma chains in one lane,
+// halving-tree sums whose pairing is fixed (lane i + lane i+stride), an
+// exponential built from fma/rint/ldexp only, FP64 upper bounds built from
+// + - * / only, and unsigned fixed-point sums (order-free).  The library is
+// compiled with -ffp-contract=off so no other fusion happens.
+#pragma once
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckv {
+
+constexpr int BT = 64;       // tokens per block
+constexpr int VG = 32;       // channels per INT4 value group
+constexpr uint64_t FXCAP = 1ull << 46;
+
+__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+// Smallest binary16 >= x, for x >= 0 (scale rounding upward).
+__device__ __forceinline__ uint16_t f2h_up(float x) {
+    if (!(x > 0.0f)) return 0;
+    uint16_t h = __half_as_ushort(__float2half_rn(x));
+    if (h < 0x7C00u && h2f(h) < x) h = (uint16_t)(h + 1);
+    return h;
+}
+
+// binary64 -> binary32 rounded upward, for x >= 0 (bounds and ranges).
+__device__ __forceinline__ float ru32(double x) {
+    float f = (float)x;
+    if ((double)f < x) f = __int_as_float(__float_as_int(f) + 1);
+    return f;
+}
+
+// exp(x) for x <= 0: k = rint(x log2 e); r = x - k ln2 with ln2 split in two
+// parts (Cody-Waite); e^r by the degree-7 Taylor polynomial (Horner, fma);
+// result r 2^k; 0 when k < -125 (no subnormal results).
+__device__ __forceinline__ float exp_c(float x) {
+    float y = x * 1.44269502f;           // log2(e) in binary32: 0x3FB8AA3B
+    float k = rintf(y);
+    if (k < -125.0f) return 0.0f;
+    float r = fmaf(-k, 0.693145751953125f, x);   // 0x3F317200
+    r = fmaf(-k, 1.42860677e-06f, r);            // 0x35BFBE8E
+    float p = 1.98412701e-04f;                   // 1/7!  0x39500D01
+    p = fmaf(p, r, 1.38888892e-03f);             // 1/6!  0x3AB60B61
+    p = fmaf(p, r, 8.33333377e-03f);             // 1/5!  0x3C088889
+    p = fmaf(p, r, 4.16666679e-02f);             // 1/4!  0x3D2AAAAB
+    p = fmaf(p, r, 1.66666672e-01f);             // 1/3!  0x3E2AAAAB
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)k);
+}
+
+// Upper bound of e^x, x >= 0: halve to r <= 1/16, Taylor to degree 12,
+// square back, times (1 + 2^-36).
+__device__ __forceinline__ double expu(double x) {
+    if (!(x <= 64.0)) return __longlong_as_double(0x7FF0000000000000ll);
+    if (x <= 0.0) x = 0.0;
+    int j = 0;
+    double r = x;
+    while (r > 0.0625) { r *= 0.5; ++j; }
+    double f = 479001600.0;              // 12!
+    double p = 1.0 / f;
+    for (int i = 11; i >= 0; --i) {
+        f = f / (double)(i + 1);         // i!
+        p = fma(p, r, 1.0 / f);
+    }
+    for (int i = 0; i < j; ++i) p = p * p;
+    return p * (1.0 + 0x1p-36);
+}
+
+// Upper bound of e^x - 1, x >= 0.
+__device__ __forceinline__ double em1u(double x) {
+    if (!(x > 0.0)) return 0.0;
+    if (x > 64.0) return __longlong_as_double(0x7FF0000000000000ll);
+    if (x <= 0.5) {
+        double c[16];
+        double f = 1.0;
+        for (int i = 0; i < 16; ++i) { f = f * (double)(i + 1); c[i] = 1.0 / f; }
+        double p = c[15];
+        for (int i = 14; i >= 0; --i) p = fma(p, x, c[i]);
+        return x * p * (1.0 + 0x1p-48);
+    }
+    return (expu(x) - 1.0) * (1.0 + 0x1p-50);
+}
+
+// Upper bound of tanh(x/2) = m / (m + 2), m = e^x - 1.
+__device__ __forceinline__ double tanhu(double x) {
+    double m = em1u(x);
+    if (__isinf(m)) return 1.0;
+    double t = m / (m + 2.0) * (1.0 + 0x1p-48);
+    return t < 1.0 ? t : 1.0;
+}
+
+// Bound term -> fixed point with 32 fraction bits, rounded up, capped.
+__device__ __forceinline__ uint64_t fx(double t) {
+    if (!(t < 16384.0)) return FXCAP;
+    if (t <= 0.0) return 0;
+    uint64_t u = (uint64_t)ceil(t * 4294967296.0);
+    return u < FXCAP ? u : FXCAP;
+}
+
+__device__ __forceinline__ double fx_bound(uint64_t sum, bool sat) {
+    if (sat) return __longlong_as_double(0x7FF0000000000000ll);
+    return (double)sum * 0x1p-32 * (1.0 + 0x1p-50);
+}
+
+__device__ __forceinline__ double gamma_n(int n) {
+    double nu = (double)n * 0x1p-24;
+    return nu / (1.0 - nu);
+}
+
+// ---- wave reductions (wave64) ---------------------------------------------
+
+// Halving-tree sum: lane i adds lane i + stride for stride 32..1; the result
+// is in lane 0 (other lanes hold partial sums).
+__device__ __forceinline__ float tree64_f32(float v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
+    return v;
+}
+__device__ __forceinline__ double tree64_f64(double v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
+    return v;
+}
+
+// Order-free reductions (every lane gets the result).
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = fmax(v, __shfl_xor(v, s, 64));
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_or_i32(int v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v |= __shfl_xor(v, s, 64);
+    return v;
+}
+
+}  // namespace ckv

@@ -1,0 +1,132 @@
+// ckv_internal.hpp -- layouts shared by the kernels and the host runtime.
+//
+// HBM layout of tier 1 (device), per (layer l, sequence n, kv head g,
+// block b), blocks of 64 tokens, d = head_dim:
+//   kq    u8  [d/16][64][16]   INT8 key codes, chunk-interleaved: one 16-byte
+//                              load per lane covers 16 channels of one token
+//                              and a wave's load covers 1 KiB contiguous
+//   kmeta u32 [d]              binary16 scale | binary16 offset << 16
+//   vq    u8  [64][d/2]        INT4 value codes, low nibble = even channel
+//   vmeta u32 [64][d/32]       binary16 scale | binary16 offset << 16
+//   eta   f32                  value-error annotation of the block
+// Unfinished block (device, FP16): kpart [d/8][64][8], vpart [64][d].
+// Tier 2 (pinned host) and the device staging area hold FP16 blocks in the
+// same per-block layout: K [d/8][64][8] (one 16-byte load = 8 channels of a
+// token), V [64][d].
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckv {
+
+struct Layout {
+    int L, B, Hq, Hkv, d, G, Nmax;  // Nmax: full-block capacity per sequence
+    uint8_t *kq;
+    uint32_t *kmeta;
+    uint8_t *vq;
+    uint32_t *vmeta;
+    float *eta;
+    uint32_t *vmin, *vmax;  // [L][B][Hkv][d] order-preserving encodings of FP32
+    uint16_t *kpart, *vpart;
+    int *len;               // [L][B] tokens per sequence (device mirror)
+
+    __host__ __device__ size_t blk(int l, int n, int g, int b) const {
+        return (((size_t)l * B + n) * Hkv + g) * Nmax + b;
+    }
+    __host__ __device__ size_t seqg(int l, int n, int g) const {
+        return ((size_t)l * B + n) * Hkv + g;
+    }
+};
+
+// Order-preserving u32 encoding of an FP32 value (for atomic min / max).
+__host__ __device__ inline uint32_t f2ord(float f) {
+    uint32_t u;
+    __builtin_memcpy(&u, &f, 4);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__host__ __device__ inline float ord2f(uint32_t u) {
+    uint32_t v = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    float f;
+    __builtin_memcpy(&f, &v, 4);
+    return f;
+}
+
+// Plan of one (sequence, q head), written by the selection kernel and
+// completed by the rank-check kernel.
+struct HeadPlan {
+    double mu, tv, ekey, eval, tau;
+    float mref;
+    int kstar, nvp, flags;  // flags: bit0 widened, bit1 a cap was exhausted
+    int rank_ok, ndisc;
+    uint64_t S;
+};
+
+// Scratch of one decode step; strides use the cache capacity so that any
+// batch size fits.  NS = Nmax + 1 slots per head (the extra one is the
+// unfinished block).
+struct Step {
+    int layer, batch, nb;   // nb: max full blocks over the batch
+    int NS;                 // slot stride
+    int nsplit, bps;        // tail splits per (seq, kv head), blocks per split
+    float sm;
+    const uint16_t *q;      // [batch][Hq][d]
+    float *score;           // [B][Hq][NS*64]
+    float4 *bstat;          // [B][Hq][NS]  max, l, Delta, rho
+    uint64_t *mfx;          // [B][Hq][NS]
+    uint64_t *cval;         // [B][Hq][NS]  E_val contribution per block
+    uint32_t *sel;          // [B][Hkv][Nmax]
+    HeadPlan *plan;         // [B][Hq]
+    float2 *st16;           // [B][Hq][Nmax] FP16-key block max, l on P
+    uint64_t *m16;          // [B][Hq][Nmax]
+    float *part_tail;       // [B][Hq][nsplit_cap][d+2]  m, l, acc
+    float *part_blk;        // [B][Hq][NS][d+2]
+    int nsplit_cap;
+    const uint16_t *stage_k, *stage_v;  // [B][Hkv][Nmax][64*d]
+    float *out;             // [batch][Hq][d]
+};
+
+// Source of an exact dense attention: FP16 blocks of (seq n, kv head g) at
+// k + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
+// token-major), len[n] tokens, the unfinished block (if any) at
+// kp / vp + (n * Hkv + g) * 64 * D.
+struct DenseSrc {
+    const uint16_t *k, *v;
+    const uint16_t *kp, *vp;
+    const int *len;
+    size_t nstride;
+    const uint32_t *mask;       // [B][Hkv] q heads of the group to compute (null: all)
+    const uint16_t *q;
+    float sm;
+    float *part;                // [B][Hq][nsplit_cap][D+2]
+    int nsplit_cap, bps, Hq, Hkv;
+    float *out;
+};
+
+// Decision thresholds as the kernels see them.
+struct Th {
+    float tau, k_tol, v_tol, rank_tol, f_layer;
+    int n_widen, vcap;  // vcap <= 0: no cap
+};
+
+// ---- launchers (defined in the .hip files) ---------------------------------
+hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,
+                       int len0, int ntok, int b0, int nblk, uint16_t *pk, uint16_t *pv,
+                       hipStream_t s);
+hipError_t launch_quant(const Layout &Ly, int l, int n, int b0, int nfull, int nblk,
+                        const uint16_t *pk, const uint16_t *pv, hipStream_t s);
+hipError_t launch_set_partial(const Layout &Ly, int l, int n, int slot, int nblk,
+                              const uint16_t *pk, const uint16_t *pv, hipStream_t s);
+hipError_t launch_vrange(const Layout &Ly, int l, int n, const uint16_t *vin, int ntok,
+                         int reset, hipStream_t s);
+
+hipError_t launch_score(const Layout &Ly, const Step &St, hipStream_t s);
+hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStream_t s);
+hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s);
+hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq,
+                           hipStream_t s);
+hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, const int *skip_seq,
+                             uint32_t *plist, uint64_t *keys, hipStream_t s);
+hipError_t launch_dense_src(int d, int G, const DenseSrc &S, int nsplit, int batch,
+                            hipStream_t s);
+
+}  // namespace ckv

@@ -1,0 +1,199 @@
+/*
+ * ckv.h -- C ABI of the certified quantized-KV decode attention library
+ * (HIP, gfx950 / MI355X).
+ *
+ * The method is the one described on the page "Runtime-Certified
+ * Bounded-Error Quantized Attention" (gist.science paper 2605.20868,
+ * technical summary).  Section tags used below:
+ *   [Meth-1]  Methodology 1, tiered storage with deterministic fallback
+ *   [Meth-2]  Methodology 2, two-term error decomposition
+ *   [Meth-3]  Methodology 3, adaptive precision and the fallback ladder
+ *   [Contrib] Key contributions
+ *   [Results] Experimental results
+ *
+ * Conventions for every entry point:
+ *   - Pointers are plain host or device addresses as stated per argument;
+ *     the library never takes ownership of caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *   - Errors are returned as ckv_status; nothing is thrown across the ABI.
+ *     On error a message is available from ckv_last_error() (per thread).
+ *     CKV_EHIP means a HIP runtime call failed; the HIP error text is in
+ *     the message.
+ *   - One cache must not be used from two host threads or two streams at
+ *     the same time.
+ *   - FP16 data is IEEE binary16, passed as 16-bit patterns.
+ */
+#ifndef CKV_H
+#define CKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CKV_OK = 0,
+    CKV_EINVAL = 1, /* bad argument (shape, pointer, layer/sequence index)   */
+    CKV_ENOMEM = 2, /* device or pinned host allocation failed               */
+    CKV_EHIP = 3,   /* a HIP runtime call failed                             */
+    CKV_ERANGE = 4, /* appending would exceed max_context                    */
+    CKV_ESTATE = 5  /* call not valid in the current state (e.g. empty seq)  */
+} ckv_status;
+
+typedef struct ckv_cache ckv_cache;
+
+/* Shape of a cache.  head_dim must be 64 or 128; n_q_heads a multiple of
+ * n_kv_heads with n_q_heads / n_kv_heads <= 8; max_context >= 1.  Blocks
+ * are 64 tokens; INT4 value groups are 32 channels. */
+typedef struct {
+    int n_layers;
+    int max_batch;    /* sequences per layer                               */
+    int n_q_heads;
+    int n_kv_heads;
+    int head_dim;
+    int max_context;  /* tokens per sequence                               */
+    int device;       /* HIP device ordinal                                */
+} ckv_config;
+
+/* Thresholds of the certified decode step [Meth-3, Results].
+ * tau_cov: coverage of the estimated attention mass by the blocks whose
+ *   FP16 keys are paged in (the page's example: 0.995).
+ * k_tol / v_tol: tolerances on E_key / E_val, in output units.
+ * rank_tol: the rank check fails when more than floor(rank_tol * K*(K*-1)/2)
+ *   pairs of promoted blocks are ordered differently by INT8 and FP16 keys.
+ * sm_scale: softmax scale applied to q.k.
+ * f_layer: a layer (per sequence) falls back whole when more than
+ *   f_layer * n_q_heads heads fell back on their own.
+ * n_widen: maximum number of rung-1 widenings (each halves 1 - tau).
+ * v_cap_blocks: maximum FP16-value blocks per head (<= 0: no cap). */
+typedef struct {
+    float tau_cov, k_tol, v_tol, rank_tol, sm_scale, f_layer;
+    int n_widen, v_cap_blocks;
+} ckv_thresholds;
+
+/* Per (sequence, q head) outcome of a decode step [Meth-2, Meth-3].
+ * e_key, e_val, tv_bound: certified bounds (0 for heads that fell back,
+ *   whose output is exact dense attention).
+ * tau_final: coverage after rung-1 widening.
+ * kstar: blocks with FP16 keys; n_v_promoted: blocks with FP16 values.
+ * rank_ok: 1 consistent, 0 inconsistent, -1 not run (layer fell back
+ *   before paging).  n_discordant: discordant pair count.
+ * rung_max: highest rung reached (0..4); rung_mask: bit r set for every
+ *   rung r reached. */
+typedef struct {
+    float e_key, e_val, tv_bound, tau_final;
+    int kstar, n_v_promoted, rank_ok, rung_max, rung_mask, n_discordant;
+} ckv_head_report;
+
+/* Create a cache: tier 1 (codes, metadata, annotations) in device memory,
+ * tier 2 (FP16 originals) in pinned host memory [Meth-1], plus staging and
+ * scratch.  *out receives the handle.  Errors: EINVAL, ENOMEM, EHIP. */
+ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out);
+
+/* Free everything the cache owns.  NULL is accepted. */
+void ckv_destroy(ckv_cache *c);
+
+/* Forget every token of sequence `seq` in all layers.  Errors: EINVAL. */
+ckv_status ckv_reset_sequence(ckv_cache *c, int seq);
+
+/* Append n_tokens tokens to (layer, seq) [Meth-1].
+ * k_fp16, v_fp16: [n_tokens][n_kv_heads][head_dim] binary16, in device
+ *   memory if src_on_device, else in host memory; read before return.
+ * Every completed 64-token block is quantized (INT8 keys with a per-channel
+ * scale/offset per block, INT4 values with a scale/offset per token and
+ * 32-channel group, the block's value-error annotation); tokens of an
+ * unfinished block stay FP16 on the device.  All tokens are copied to the
+ * FP16 tier in host memory.  The call synchronizes `stream`.
+ * Errors: EINVAL, ERANGE (would exceed max_context), EHIP. */
+ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k_fp16,
+                         const void *v_fp16, int n_tokens, int src_on_device, void *stream);
+
+/* Certified decode attention for sequences 0..batch-1 of `layer`
+ * [Meth-2, Meth-3, Contrib].
+ * q_fp16: device, [batch][n_q_heads][head_dim] binary16.
+ * th: host pointer to the thresholds.
+ * out: device, [batch][n_q_heads][head_dim] FP32 attention output.
+ * report: host, [batch][n_q_heads].
+ * Steps: INT8 scoring pass over tier 1; top-K* selection covering tau_cov
+ * of the estimated mass; E_key / E_val from quantities tracked on the
+ * device only; rungs 1-2; FP16 keys (and values of rung 2) paged from
+ * tier 2 with hipMemcpyAsync on a side stream while the tail is processed;
+ * rank-consistency check; rungs 3-4 page full FP16 KV and recompute dense.
+ * The call returns after the report is on the host (the ladder needs host
+ * round trips).  Every sequence must hold >= 1 token.
+ * Errors: EINVAL, ESTATE (empty sequence), EHIP.  On error `out` is
+ * unspecified and every report has rung_max = -1. */
+ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q_fp16, int batch,
+                                          const ckv_thresholds *th, float *out,
+                                          ckv_head_report *report, void *stream);
+
+/* Exact dense decode attention over caller-provided device FP16 K/V, the
+ * "fast dense path" the certified step is compared with [Results].
+ * k, v: device binary16 in the block layout
+ *   [batch][n_kv_heads][n_tokens/64][64 * head_dim], where a K block is
+ *   [head_dim/8][64 tokens][8 channels] and a V block [64 tokens][head_dim];
+ * n_tokens: a multiple of 64, at most the cache's max_context;
+ * q: device [batch][n_q_heads][head_dim] binary16; out: device FP32
+ * [batch][n_q_heads][head_dim].  Uses the cache's shape (heads, head_dim)
+ * and scratch; stream-ordered, returns without synchronizing.
+ * Errors: EINVAL, EHIP. */
+ckv_status ckv_dense_decode_attention(ckv_cache *c, const void *k, const void *v, int n_tokens,
+                                      const void *q_fp16, int batch, float sm_scale, float *out,
+                                      void *stream);
+
+/* Bytes held: tier 1 + partial blocks + staging + scratch on the device,
+ * tier 2 in pinned host memory. */
+ckv_status ckv_footprint(const ckv_cache *c, size_t *dev_bytes, size_t *host_bytes,
+                         size_t *tier1_bytes);
+
+/* Tokens currently held by (layer, seq). */
+ckv_status ckv_seq_length(const ckv_cache *c, int layer, int seq, int *n_tokens);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *ckv_last_error(void);
+
+/* ---- introspection (tests and benchmarks) ------------------------------ */
+
+/* Tier-1 contents of one block, in token-major layout:
+ * k_code [64][d] u8, k_s, k_z [d] binary16, v_code [64][d/2] u8 (low nibble
+ * = even channel), v_s, v_z [64][d/32] binary16, eta [1] FP32.  Host
+ * pointers; any may be NULL.  Errors: EINVAL (block not complete), EHIP. */
+ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int kv_head, int block,
+                            uint8_t *k_code, uint16_t *k_s, uint16_t *k_z, uint8_t *v_code,
+                            uint16_t *v_s, uint16_t *v_z, float *eta);
+
+/* Intermediates of the last decode step (host pointers, may be NULL), for
+ * batch rows 0..batch-1, with Np = N + (partial block ? 1 : 0) slots per
+ * head where N = full blocks of the longest sequence in the batch:
+ *   score  [batch][n_q_heads][Np*64] FP32  INT8 scores (partial: FP16)
+ *   bstat  [batch][n_q_heads][Np][4] FP32  block max, l, Delta, rho
+ *   mref   [batch][n_q_heads] FP32         largest estimated score
+ *   mfx    [batch][n_q_heads][Np] u64      fixed-point estimated masses
+ *   sel    [batch][n_kv_heads][Np] u32     bit j: P of head j of the
+ *                                          group, bit 8+j: VP of head j
+ *                                          (first N entries of each row)
+ *   m16fx  [batch][n_q_heads][Np] u64      fixed-point FP16 masses on P
+ *                                          (first N entries of each row)
+ *   bounds [batch][n_q_heads][4] FP64      mu, TV, E_key, E_val
+ *   seq_flags [batch] int                  bit0 rung 4 before paging,
+ *                                          bit1 rung 4 after the rank check
+ * np_out receives Np.  Errors: ESTATE (no step yet), EINVAL, EHIP. */
+ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, float *bstat,
+                           float *mref, uint64_t *mfx, uint32_t *sel, uint64_t *m16fx,
+                           double *bounds, int *seq_flags);
+
+/* Per-phase timing of decode steps, measured with HIP events on the
+ * streams the work runs on.  Phases: 0 score (K1), 1 select (K2),
+ * 2 tail (K3), 3 page-in wait (host round trip + H2D), 4 promoted + rank +
+ * merge (K4), 5 fallback (paging + dense), 6 whole step.  ms: [8]
+ * milliseconds accumulated since profiling was enabled; counts: [8]
+ * number of timed occurrences.  Enabling resets the sums. */
+ckv_status ckv_set_profiling(ckv_cache *c, int enable);
+ckv_status ckv_get_phase_times(ckv_cache *c, double *ms, int *counts, size_t *bytes_paged);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

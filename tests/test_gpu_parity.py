@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bit-exact: quantized codes, scales, offsets and eta_b; INT8 scores, block
+estimates, Delta, rho; fixed-point masses; selected sets P and VP; the FP64
+bounds; rank verdicts and discordant counts; rungs.  Outputs: within
+2e-3 absolute + 1e-2 relative of the oracle (FP32 accumulation on the GPU,
+FP64 in the oracle).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import certified_quantized_kv_amd as ckv  # noqa: F401  (raises if the library is missing)
+
+
+def f16(x):
+    return np.asarray(x, np.float16).view(np.uint16)
+
+
+def make_cache(B, Hq, Hkv, d, T):
+    import certified_quantized_kv_amd as ckv
+    return ckv.Cache(1, B, Hq, Hkv, d, T)
+
+
+def gpu_run(k, v, q, th, chunks=None, cache=None):
+    """Append k, v ([B][T][Hkv][d] uint16) and run one decode step."""
+    B, T, Hkv, d = k.shape
+    Hq = q.shape[1]
+    c = cache or make_cache(B, Hq, Hkv, d, T)
+    for n in range(B):
+        if chunks is None:
+            c.append_kv(0, n, k[n], v[n])
+        else:
+            t0 = 0
+            for i, ln in enumerate(chunks):
+                kk = k[n, t0:t0 + ln]
+                vv = v[n, t0:t0 + ln]
+                if i % 2:   # every other chunk from device memory
+                    c.append_kv(0, n, torch.from_numpy(kk.view(np.float16)).cuda(),
+                                torch.from_numpy(vv.view(np.float16)).cuda())
+                else:
+                    c.append_kv(0, n, kk, vv)
+                t0 += ln
+            assert t0 == T
+    qd = torch.from_numpy(q.view(np.float16)).cuda()
+    out, rep = c.certified_decode_attention(0, qd, th)
+    torch.cuda.synchronize()
+    step = c.export_step(B)
+    return c, out.cpu().numpy().astype(np.float64), rep, step
+
+
+def check_parity(k, v, q, th, res, c, out, rep, step, seqs=None, kv_heads=None):
+    """Compare the GPU step with the oracle result `res` (computed on the
+    sequences `seqs` and kv heads `kv_heads` of the GPU batch)."""
+    B, T, Hkv, d = k.shape
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    N = T // 64
+    tr = res.trace
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    kvh = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    heads = [g * G + j for g in kvh for j in range(G)]
+    for oi, n in enumerate(seqs):
+        # tier 1, bit-exact
+        for og, g in enumerate(kvh):
+            for b in sorted({0, N // 2, N - 1} if N else set()):
+                e = c.export_block(0, n, g, b)
+                assert np.array_equal(e["k_code"], tr["k_code"][oi, og, b]), (n, g, b)
+                assert np.array_equal(e["k_s"], tr["k_s"][oi, og, b])
+                assert np.array_equal(e["k_z"], tr["k_z"][oi, og, b])
+                assert np.array_equal(e["v_code"], tr["v_code"][oi, og, b])
+                assert np.array_equal(e["v_s"], tr["v_s"][oi, og, b])
+                assert np.array_equal(e["v_z"], tr["v_z"][oi, og, b])
+                assert e["eta"][0] == tr["eta"][oi, og, b]
+        Np = tr["score"].shape[-1] // 64
+        for oh, h in enumerate(heads):
+            g, j = h // G, h % G
+            ctx = (n, h)
+            assert np.array_equal(step["score"][n, h, :Np * 64], tr["score"][oi, oh]), ctx
+            bs = step["bstat"][n, h, :Np]
+            assert np.array_equal(bs[:, 0], tr["bmax"][oi, oh]), ctx
+            assert np.array_equal(bs[:, 1], tr["bl"][oi, oh]), ctx
+            assert np.array_equal(bs[:, 2], tr["delta"][oi, oh]), ctx
+            assert np.array_equal(bs[:, 3], tr["rho"][oi, oh]), ctx
+            assert step["mref"][n, h] == tr["mref"][oi, oh], ctx
+            assert np.array_equal(step["mfx"][n, h, :Np], tr["mfx"][oi, oh]), ctx
+            sel = step["sel"][n, g, :N]
+            assert np.array_equal((sel >> j) & 1, tr["sel"][oi, oh] & 1), ctx
+            assert np.array_equal((sel >> (8 + j)) & 1, (tr["sel"][oi, oh] >> 1) & 1), ctx
+            assert np.array_equal(step["bounds"][n, h], tr["bounds"][oi, oh]), ctx
+            ro, rg = res.report[oi, oh], rep[n, h]
+            for f in ("kstar", "n_v_promoted", "tau_final"):
+                assert ro[f] == rg[f], (ctx, f, ro[f], rg[f])
+        if kv_heads is None:
+            # ladder outcomes are per (sequence, layer): whole sequence needed
+            assert step["seq_flags"][n] == tr["seq_flags"][oi], n
+            for h in range(Hq):
+                ro, rg = res.report[oi, h], rep[n, h]
+                for f in ("rank_ok", "n_discordant", "rung_max", "rung_mask", "e_key", "e_val",
+                          "tv_bound"):
+                    assert ro[f] == rg[f], ((n, h), f, ro[f], rg[f])
+                if not (tr["seq_flags"][oi] & 1):
+                    inP = (tr["sel"][oi, h] & 1).astype(bool)
+                    assert np.array_equal(step["m16fx"][n, h, :N][inP], tr["m16fx"][oi, h][inP]), (n, h)
+            ref = res.out[oi]
+            assert np.all(np.abs(out[n] - ref) <= ATOL + RTOL * np.abs(ref)), \
+                (n, np.abs(out[n] - ref).max())
+        else:
+            # sampled kv heads: certified heads against the oracle's certified
+            # output, fallen-back heads against exact dense attention
+            for oh, h in enumerate(heads):
+                ref = tr["o_cert"][oi, oh] if rep[n, h]["rung_max"] < 3 else tr["o_dense"][oi, oh]
+                assert np.all(np.abs(out[n, h] - ref) <= ATOL + RTOL * np.abs(ref)), (n, h)
+
+
+def both(k, v, q, th, chunks=None):
+    print(f"case B={k.shape[0]} T={k.shape[1]} Hkv={k.shape[2]} d={k.shape[3]} Hq={q.shape[1]} "
+          f"th={th}", flush=True)
+    res = oracle.certified_decode(k, v, q, th)
+    c, out, rep, step = gpu_run(k, v, q, th, chunks=chunks)
+    check_parity(k, v, q, th, res, c, out, rep, step)
+    c.close()
+    return res, rep
+
+
+def micro(seed, T=512, Hq=4, Hkv=1, d=64, B=1, kind="normal"):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, Hkv, d))
+    v = rng.standard_normal((B, T, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    if kind == "outliers":
+        k[..., :4] *= 10
+    if kind == "peaked":
+        for n in range(B):
+            for g in range(Hkv):
+                b = int(rng.integers(0, max(T // 64, 1)))
+                u = q[n, g * (Hq // Hkv):(g + 1) * (Hq // Hkv)].mean(0)
+                k[n, b * 64:(b + 1) * 64, g] += 6.0 * u / np.linalg.norm(u)
+    if kind == "heavy":
+        v = rng.standard_t(3, v.shape)
+    if kind == "flat":
+        q *= 0.02
+    return f16(k), f16(v), f16(q), float(1 / np.sqrt(d))
+
+
+# -- small cases: every intermediate ------------------------------------------
+
+THRESHOLD_CASES = [
+    dict(),                                       # defaults
+    dict(v_cap_blocks=1),                         # rung 2 cap -> rung 4 before paging
+    dict(rank_tol=-1.0, f_layer=1.0),             # rung 3 on every head
+    dict(rank_tol=-1.0, f_layer=0.5),             # rung 4 after the rank check
+    dict(k_tol=2e-4),                             # rung 1 widening
+    dict(tau_cov=1.0, v_tol=0.0, k_tol=1.0),      # everything promoted
+]
+
+
+@pytest.mark.parametrize("case", range(len(THRESHOLD_CASES)))
+def test_tiny_config_all_rungs(case):
+    L = datagen.make_layer("tiny_1k", 0)
+    th = oracle.default_thresholds(L.sm, **THRESHOLD_CASES[case])
+    both(L.k, L.v, L.q, th)
+
+
+@pytest.mark.parametrize("chunks", [None, [1, 63, 100, 500, 336], [1000], [64, 64, 872]])
+def test_ragged_context_and_chunked_appends(chunks):
+    L = datagen.make_layer("tiny_1k", 0, T=1000)
+    th = oracle.default_thresholds(L.sm)
+    both(L.k, L.v, L.q, th, chunks=chunks)
+
+
+@pytest.mark.parametrize("shape", [(4, 1, 64), (8, 2, 64), (2, 2, 64), (16, 2, 128), (8, 1, 128),
+                                   (4, 4, 128)])
+@pytest.mark.parametrize("kind", ["normal", "peaked", "heavy", "flat", "outliers"])
+def test_head_shapes_and_distributions(shape, kind):
+    Hq, Hkv, d = shape
+    seed = zlib.crc32(repr((shape, kind)).encode()) % 1000
+    k, v, q, sm = micro(seed, T=[640, 1000, 130][seed % 3], Hq=Hq, Hkv=Hkv, d=d, B=2, kind=kind)
+    both(k, v, q, oracle.default_thresholds(sm))
+
+
+def test_single_token_and_single_block():
+    for T in [1, 63, 64, 65]:
+        k, v, q, sm = micro(T, T=T, Hq=8, Hkv=2, d=128)
+        both(k, v, q, oracle.default_thresholds(sm))
+
+
+def test_mixed_lengths_in_a_batch():
+    """Sequences of different lengths in one step (each compared alone)."""
+    import certified_quantized_kv_amd as ckv
+    Hq, Hkv, d = 8, 2, 128
+    lens = [1000, 256, 70]
+    c = ckv.Cache(1, 3, Hq, Hkv, d, 1024)
+    ks, vs = [], []
+    for n, T in enumerate(lens):
+        k, v, q, sm = micro(50 + n, T=T, Hq=Hq, Hkv=Hkv, d=d)
+        c.append_kv(0, n, k[0], v[0])
+        ks.append(k)
+        vs.append(v)
+    rng = np.random.default_rng(3)
+    q = f16(rng.standard_normal((3, Hq, d)))
+    th = oracle.default_thresholds(sm)
+    out, rep = c.certified_decode_attention(0, torch.from_numpy(q.view(np.float16)).cuda(), th)
+    out = out.cpu().numpy()
+    for n, T in enumerate(lens):
+        res = oracle.certified_decode(ks[n], vs[n], q[n:n + 1], th)
+        for f in ("kstar", "n_v_promoted", "rung_mask", "e_key", "e_val", "n_discordant"):
+            assert np.array_equal(rep[n][f], res.report[0][f]), (n, f)
+        ref = res.out[0]
+        assert np.all(np.abs(out[n] - ref) <= ATOL + RTOL * np.abs(ref))
+    c.close()
+
+
+def test_deterministic_across_runs():
+    L = datagen.make_layer("tiny_1k", 0, T=1000)
+    th = oracle.default_thresholds(L.sm)
+    c, out1, rep1, s1 = gpu_run(L.k, L.v, L.q, th)
+    qd = torch.from_numpy(L.q.view(np.float16)).cuda()
+    out2, rep2 = c.certified_decode_attention(0, qd, th)
+    s2 = c.export_step(1)
+    assert np.array_equal(out1, out2.cpu().numpy().astype(np.float64))
+    assert np.array_equal(rep1, rep2)
+    for key in s1:
+        assert np.array_equal(s1[key], s2[key]), key
+    c.close()
+
+
+# -- full-size workloads ---------------------------------------------------------
+
+def test_llama_8k_layer():
+    L = datagen.make_layer("llama_8k", 0)
+    both(L.k, L.v, L.q, oracle.default_thresholds(L.sm))
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_stress_32k_layers(layer):
+    L = datagen.make_layer("stress_32k", layer)
+    res, rep = both(L.k, L.v, L.q, oracle.default_thresholds(L.sm))
+
+
+def test_llama_32k_batch4_sampled_sequence():
+    """Full 4 x 32K layer on the GPU; the oracle recomputes sequence 2."""
+    L = datagen.make_layer("llama_32k", 0)
+    th = oracle.default_thresholds(L.sm)
+    c, out, rep, step = gpu_run(L.k, L.v, L.q, th)
+    res = oracle.certified_decode(L.k[2:3], L.v[2:3], L.q[2:3], th)
+    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step, seqs=[2])
+    c.close()
+
+
+def test_needle_128k_sampled_kv_head():
+    """Full 128K layer on the GPU; the oracle recomputes kv head 5's group."""
+    L = datagen.make_layer("needle_128k", 0)
+    th = oracle.default_thresholds(L.sm)
+    c, out, rep, step = gpu_run(L.k, L.v, L.q, th)
+    g = 5
+    res = oracle.certified_decode(L.k[:, :, g:g + 1], L.v[:, :, g:g + 1], L.q[:, 4 * g:4 * g + 4], th)
+    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step, kv_heads=[g])
+    c.close()
+
+
+# -- the dense comparator and error paths ---------------------------------------
+
+def to_blocks(k, v):
+    """[B][T][Hkv][d] -> block layout [B][Hkv][T/64][...] (K chunk-interleaved)."""
+    B, T, Hkv, d = k.shape
+    kb = k.reshape(B, T // 64, 64, Hkv, d // 8, 8).transpose(0, 3, 1, 4, 2, 5).copy()
+    vb = v.reshape(B, T // 64, 64, Hkv, d).transpose(0, 3, 1, 2, 4).copy()
+    return kb, vb
+
+
+def test_dense_comparator_matches_exact_attention():
+    import certified_quantized_kv_amd as ckv
+    k, v, q, sm = micro(77, T=2048, Hq=8, Hkv=2, d=128, B=2, kind="outliers")
+    kb, vb = to_blocks(k, v)
+    c = ckv.Cache(1, 2, 8, 2, 128, 2048)
+    kt = torch.from_numpy(kb.view(np.float16)).cuda()
+    vt = torch.from_numpy(vb.view(np.float16)).cuda()
+    qt = torch.from_numpy(q.view(np.float16)).cuda()
+    out = c.dense_decode_attention(kt, vt, 2048, qt, sm).cpu().numpy()
+    for n in range(2):
+        for h in range(8):
+            ref = oracle.dense_head(k[n], v[n], q[n, h], h // 4, sm)
+            assert np.all(np.abs(out[n, h] - ref) <= ATOL + RTOL * np.abs(ref))
+    c.close()
+
+
+def test_error_paths():
+    import certified_quantized_kv_amd as ckv
+    c = ckv.Cache(2, 2, 8, 2, 64, 256)
+    q = torch.zeros((1, 8, 64), dtype=torch.float16, device="cuda")
+    th = oracle.default_thresholds(0.125)
+    with pytest.raises(ckv.CkvError) as e:
+        c.certified_decode_attention(0, q, th)
+    assert e.value.name == "CKV_ESTATE"
+    k = np.zeros((200, 2, 64), np.uint16)
+    c.append_kv(0, 0, k, k)
+    with pytest.raises(ckv.CkvError) as e:
+        c.append_kv(0, 0, k, k)
+    assert e.value.name == "CKV_ERANGE"
+    assert c.seq_length(0, 0) == 200
+    with pytest.raises(ckv.CkvError) as e:
+        c.certified_decode_attention(5, q, th)
+    assert e.value.name == "CKV_EINVAL"
+    with pytest.raises(ckv.CkvError) as e:
+        c.certified_decode_attention(0, q, dict(th, tau_cov=0.0))
+    assert e.value.name == "CKV_EINVAL"
+    out, rep = c.certified_decode_attention(0, q, th)   # all-zero K, V, q: defined
+    assert np.all(out.cpu().numpy() == 0)
+    c.reset_sequence(0)
+    assert c.seq_length(0, 0) == 0
+    c.close()
