@@ -239,7 +239,9 @@ class Cache:
         paged = ctypes.c_size_t()
         _check(lib().ckv_get_phase_times(self._h, _np_ptr(ms), _np_ptr(cnt), ctypes.byref(paged)))
         names = ["score", "select", "tail", "page", "promoted", "fallback", "step"]
-        return {n: (float(ms[i]), int(cnt[i])) for i, n in enumerate(names)}, paged.value
+        ph = {n: (float(ms[i]), int(cnt[i])) for i, n in enumerate(names)}
+        ph["copies"] = (0.0, int(cnt[7]))
+        return ph, paged.value
 
 
 def _torch_cuda():

@@ -7,6 +7,7 @@
 // Section tags refer to the page "Runtime-Certified Bounded-Error Quantized
 // Attention" (technical summary): [Meth-1] tiered storage, [Meth-3] the
 // adaptive selection and the fallback ladder.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -86,6 +87,7 @@ struct ckv_cache {
     double ms[PH_N] = {};
     int cnt[PH_N] = {};
     size_t bytes_paged = 0;
+    size_t ncopies = 0;
 };
 
 namespace {
@@ -138,6 +140,15 @@ void fill_failed_reports(ckv_head_report *r, int n) {
         std::memset(&r[i], 0, sizeof r[i]);
         r[i].rung_max = -1;
     }
+}
+
+// Blocks per split of the value passes: a multiple of 4 (one block per wave
+// of a 256-thread workgroup), about 1024 workgroups per launch.
+int split_blocks(int nb, int Hkv, int batch) {
+    const long units = (long)nb * Hkv * batch;
+    int bps = (int)((units + 1023) / 1024);
+    bps = std::max(4, std::min(64, (bps + 3) / 4 * 4));
+    return bps;
 }
 
 float ru32h(double x) {
@@ -346,11 +357,27 @@ ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k, const 
 
 namespace {
 
-// Page FP16 blocks of (seq n, kv head g) whose flag is set from tier 2 into
-// the staging area, one hipMemcpyAsync per run of consecutive blocks.
-ckv_status page_runs(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
-                     std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage,
-                     size_t *bytes) {
+// Copies of one paging round: tier 2 -> staging.
+struct CopyList {
+    std::vector<void *> dst, src;
+    std::vector<size_t> size;
+    size_t bytes = 0;
+    void clear() {
+        dst.clear();
+        src.clear();
+        size.clear();
+        bytes = 0;
+    }
+};
+
+// Largest run of unwanted blocks that is copied anyway to join two runs:
+// a 16 KiB block costs ~0.3 us on the host link, a separate copy several us.
+constexpr int PAGE_GAP = 24;
+
+// Queue the FP16 blocks of (seq n, kv head g) whose flag is set (and not
+// already staged) as runs of consecutive blocks, small gaps filled.
+static void page_runs(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
+               std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage, CopyList &cl) {
     const Layout &Ly = c->Ly;
     const size_t sb = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
     int b = 0;
@@ -359,14 +386,44 @@ ckv_status page_runs(ckv_cache *c, int layer, int n, int g, int N, const uint8_t
             ++b;
             continue;
         }
-        int e = b;
-        while (e < N && want[e] && !staged[sb + e]) ++e;
+        int e = b + 1, last = b;
+        while (e < N && !staged[sb + e] && e - last <= PAGE_GAP) {
+            if (want[e]) last = e;
+            ++e;
+        }
+        e = last + 1;
         const size_t nbytes = (size_t)(e - b) * c->blk_fp16 * 2;
-        HIPCHK(hipMemcpyAsync(stage + (sb + b) * c->blk_fp16, t2 + Ly.blk(layer, n, g, b) * c->blk_fp16,
-                              nbytes, hipMemcpyHostToDevice, c->side));
+        cl.dst.push_back(stage + (sb + b) * c->blk_fp16);
+        cl.src.push_back((void *)(t2 + Ly.blk(layer, n, g, b) * c->blk_fp16));
+        cl.size.push_back(nbytes);
+        cl.bytes += nbytes;
         for (int i = b; i < e; ++i) staged[sb + i] = 1;
-        *bytes += nbytes;
         b = e;
+    }
+}
+
+// hipMemcpyBatchAsync exists from HIP 7.1 on; the HIP runtime loaded in the
+// process may be older, so it is looked up at run time.
+using batch_fn = hipError_t (*)(void **, void **, size_t *, size_t, hipMemcpyAttributes *, size_t *,
+                                size_t, size_t *, hipStream_t);
+static batch_fn batch_copy() {
+    static batch_fn f = (batch_fn)dlsym(RTLD_DEFAULT, "hipMemcpyBatchAsync");
+    return f;
+}
+
+// Issue a paging round on the side stream: one batched call when the
+// runtime has it, else one hipMemcpyAsync per run.
+static ckv_status issue_copies(ckv_cache *c, CopyList &cl) {
+    if (cl.size.empty()) return CKV_OK;
+    size_t fail_idx = 0;
+    hipError_t e = hipErrorNotSupported;
+    if (batch_fn f = batch_copy())
+        e = f(cl.dst.data(), cl.src.data(), cl.size.data(), cl.size.size(), nullptr, nullptr, 0,
+              &fail_idx, c->side);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        for (size_t i = 0; i < cl.size.size(); ++i)
+            HIPCHK(hipMemcpyAsync(cl.dst[i], cl.src[i], cl.size[i], hipMemcpyHostToDevice, c->side));
     }
     return CKV_OK;
 }
@@ -404,7 +461,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.batch = batch;
     St.nb = nb;
     St.NS = c->NS;
-    St.bps = std::max(1, std::min(64, (nb * Hkv * batch + 2047) / 2048));
+    St.bps = split_blocks(nb, Hkv, batch);
     St.nsplit = (nb + St.bps - 1) / St.bps;
     St.nsplit_cap = c->nsplit_cap;
     St.sm = th->sm_scale;
@@ -455,6 +512,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
     std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
     size_t paged = 0;
+    CopyList cl;
     if (prof) HIPCHK(hipEventRecord(E[5], c->side));
     for (int n = 0; n < batch; ++n) {
         int skip = 0;
@@ -467,10 +525,13 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 wantk[b] = skip || (sl[b] & 0xFFu);
                 wantv[b] = skip || ((sl[b] >> 8) & 0xFFu);
             }
-            TRY(page_runs(c, layer, n, g, N, wantk.data(), c->staged_k, c->t2k, c->stage_k, &paged));
-            TRY(page_runs(c, layer, n, g, N, wantv.data(), c->staged_v, c->t2v, c->stage_v, &paged));
+            page_runs(c, layer, n, g, N, wantk.data(), c->staged_k, c->t2k, c->stage_k, cl);
+            page_runs(c, layer, n, g, N, wantv.data(), c->staged_v, c->t2v, c->stage_v, cl);
         }
     }
+    TRY(issue_copies(c, cl));
+    paged += cl.bytes;
+    c->ncopies += cl.size.size();
     HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side));
     if (prof) HIPCHK(hipEventRecord(E[6], c->side));
     HIPCHK(hipEventRecord(c->ev_paged, c->side));
@@ -502,6 +563,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     if (any_dense) {
         if (prof) HIPCHK(hipEventRecord(E[9], c->side));
         std::vector<uint8_t> all(Ly.Nmax, 1);
+        cl.clear();
         for (int n = 0; n < batch; ++n) {
             const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
             for (int g = 0; g < Hkv; ++g) {
@@ -509,11 +571,14 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 for (int j = 0; j < G; ++j) m |= (uint32_t)dense[(size_t)n * Hq + g * G + j] << j;
                 c->h_mask[n * Hkv + g] = m;
                 if (m) {
-                    TRY(page_runs(c, layer, n, g, N, all.data(), c->staged_k, c->t2k, c->stage_k, &paged));
-                    TRY(page_runs(c, layer, n, g, N, all.data(), c->staged_v, c->t2v, c->stage_v, &paged));
+                    page_runs(c, layer, n, g, N, all.data(), c->staged_k, c->t2k, c->stage_k, cl);
+                    page_runs(c, layer, n, g, N, all.data(), c->staged_v, c->t2v, c->stage_v, cl);
                 }
             }
         }
+        TRY(issue_copies(c, cl));
+        paged += cl.bytes;
+        c->ncopies += cl.size.size();
         HIPCHK(hipMemcpyAsync(c->dmask, c->h_mask, sizeof(uint32_t) * batch * Hkv, hipMemcpyHostToDevice,
                               c->side));
         HIPCHK(hipEventRecord(c->ev_paged, c->side));
@@ -620,7 +685,7 @@ ckv_status ckv_dense_decode_attention(ckv_cache *c, const void *k, const void *v
     S.part = c->part_tail;
     S.nsplit_cap = c->nsplit_cap;
     const int nb = ntok / 64;
-    S.bps = std::max(1, std::min(64, (nb * cf.n_kv_heads * batch + 2047) / 2048));
+    S.bps = split_blocks(nb, cf.n_kv_heads, batch);
     S.Hq = cf.n_q_heads;
     S.Hkv = cf.n_kv_heads;
     S.out = out;
@@ -719,6 +784,7 @@ ckv_status ckv_set_profiling(ckv_cache *c, int enable) {
     std::memset(c->ms, 0, sizeof c->ms);
     std::memset(c->cnt, 0, sizeof c->cnt);
     c->bytes_paged = 0;
+    c->ncopies = 0;
     return CKV_OK;
 }
 
@@ -728,6 +794,7 @@ ckv_status ckv_get_phase_times(ckv_cache *c, double *ms, int *counts, size_t *by
         if (ms) ms[i] = c->ms[i];
         if (counts) counts[i] = c->cnt[i];
     }
+    if (counts) counts[PH_N - 1] = (int)std::min<size_t>(c->ncopies, 0x7FFFFFFF);
     if (bytes_paged) *bytes_paged = c->bytes_paged;
     return CKV_OK;
 }

@@ -459,257 +459,313 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
 }
 
 // ===========================================================================
-// K3: tail flash decoding over blocks outside P and VP [Meth-3: "remaining
-// tail blocks stay INT8"], values from INT4 codes.  One wave per (split,
-// kv head, sequence); lane owns D/64 channels; online softmax per q head.
-// Output path only: hardware exp and any summation order are allowed here.
+// Value passes (tail, promoted, dense) share one lane map: a wave covers one
+// 64-token block; lane owns 8 channels c0 = 8 (lane % (D/8)) and the tokens
+// t = i * RPI + lane / (D/8), i < TPL.  FP16 rows are read with 16-byte
+// loads, INT4 rows with 4-byte loads (8 nibbles); every load instruction of
+// a wave covers contiguous rows.  A workgroup has four waves on four blocks;
+// their online-softmax states are combined through LDS at the end.
 // ===========================================================================
-template <int D, int G>
-__global__ __launch_bounds__(64) void k_tail(Layout Ly, Step St) {
-    constexpr int CPL = D / 64;
-    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
-    const int l = St.layer;
-    const int len = Ly.len[l * Ly.B + n];
-    const int N = len / 64;
-    const int b0 = sp * St.bps, b1 = min(N, b0 + St.bps);
-    __shared__ uint8_t codes[64 * (D / 2)];
-    __shared__ float zs[64][D / 32], ss[64][D / 32];
-    __shared__ float pw[G][64];
-    float mrun[G], lrun[G], acc[G][CPL];
+template <int D>
+struct VMap {
+    static constexpr int LPR = D / 8;      // lanes per row
+    static constexpr int RPI = 64 / LPR;   // rows per load instruction
+    static constexpr int TPL = 64 / RPI;   // tokens per lane
+};
+
+// 8 FP16 values of row t at channel c0.
+__device__ __forceinline__ void unpack_fp16x8(const uint4 &u, float (&v)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        mrun[j] = -INFINITY;
-        lrun[j] = 0.0f;
+    for (int i = 0; i < 8; ++i) v[i] = h2f((uint16_t)(w[i / 2] >> (16 * (i & 1))));
+}
+// 8 INT4 codes (one 32-bit word) with the group's scale / offset.
+__device__ __forceinline__ void unpack_int4x8(uint32_t w, uint32_t meta, float (&v)[8]) {
+    const float sf = h2f((uint16_t)(meta & 0xFFFFu)), zf = h2f((uint16_t)(meta >> 16));
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) acc[j][k] = 0.0f;
-    }
-    const size_t NS64 = (size_t)St.NS * 64;
-    for (int b = b0; b < b1; ++b) {
-        const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b];
-        const uint32_t use = ~(bits | (bits >> 8)) & ((1u << G) - 1u);
-        if (!use) continue;
-        const size_t bi = Ly.blk(l, n, g, b);
-        // stage INT4 codes + metadata
-        {
-            const uint4 *src = reinterpret_cast<const uint4 *>(Ly.vq + bi * 64 * (D / 2));
-            uint4 *dst = reinterpret_cast<uint4 *>(codes);
-            for (int i = lane; i < 64 * (D / 2) / 16; i += 64) dst[i] = src[i];
-            const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
-            for (int i = lane; i < 64 * (D / 32); i += 64) {
-                const uint32_t mm = vm[i];
-                ss[i / (D / 32)][i % (D / 32)] = h2f((uint16_t)(mm & 0xFFFFu));
-                zs[i / (D / 32)][i % (D / 32)] = h2f((uint16_t)(mm >> 16));
-            }
-        }
+    for (int i = 0; i < 8; ++i) v[i] = fmaf(sf, (float)((w >> (4 * i)) & 15u), zf);
+}
+
+template <int G>
+struct OnlineState {
+    float m[G], l[G], acc[G][8];
+    __device__ __forceinline__ void init() {
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            if (!(use & (1u << j))) {
-                pw[j][lane] = 0.0f;
-                continue;
-            }
-            const int h = g * G + j;
-            const float s = St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane];
-            const float bm = St.bstat[(size_t)(n * Ly.Hq + h) * St.NS + b].x;
-            const float mn = fmaxf(mrun[j], bm);
-            const float sc = __expf(mrun[j] - mn);
-            mrun[j] = mn;
-            lrun[j] *= sc;
+            m[j] = -INFINITY;
+            l[j] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) acc[j][k] *= sc;
-            const float p = __expf(s - mn);
-            pw[j][lane] = p;
-            float ps = p;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
-            lrun[j] += ps;
+            for (int c = 0; c < 8; ++c) acc[j][c] = 0.0f;
         }
-        __syncthreads();
-        for (int t = 0; t < 64; ++t) {
-            float v[CPL];
-            if (CPL == 2) {
-                const uint8_t byte = codes[t * (D / 2) + lane];
-                const int gr = (2 * lane) / 32;
-                v[0] = fmaf(ss[t][gr], (float)(byte & 15), zs[t][gr]);
-                v[CPL - 1] = fmaf(ss[t][gr], (float)(byte >> 4), zs[t][gr]);
-            } else {
-                const uint8_t byte = codes[t * (D / 2) + lane / 2];
-                const int gr = lane / 32;
-                v[0] = fmaf(ss[t][gr], (float)((lane & 1) ? (byte >> 4) : (byte & 15)), zs[t][gr]);
-            }
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float p = pw[j][t];
-#pragma unroll
-                for (int k = 0; k < CPL; ++k) acc[j][k] = fmaf(p, v[k], acc[j][k]);
-            }
-        }
-        __syncthreads();
     }
+    // new block of head j: token score s (lane = token), valid lanes only;
+    // writes the token weights to pw[0..63].
+    __device__ __forceinline__ void weights(int j, float s, bool valid, float *pw, int lane) {
+        const float bm = wave_max_f32(valid ? s : -INFINITY);
+        const float mn = fmaxf(m[j], bm);
+        const float sc = __expf(m[j] - mn);
+        m[j] = mn;
+        l[j] *= sc;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const int h = g * G + j;
-        float *o = St.part_tail + ((size_t)(n * Ly.Hq + h) * St.nsplit_cap + sp) * (D + 2);
-        if (lane == 0) {
-            o[0] = mrun[j];
-            o[1] = lrun[j];
+        for (int c = 0; c < 8; ++c) acc[j][c] *= sc;
+        const float p = valid ? __expf(s - mn) : 0.0f;
+        pw[lane] = p;
+        float ps = p;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
+        l[j] += ps;
+    }
+};
+
+// Sum the partial accumulators of the lanes that share channels, combine the
+// four waves' states and write one partial (m, l, acc[D]) per head of the
+// group to part + (head * pstride + sp) * (D + 2).
+template <int D, int G>
+__device__ __forceinline__ void write_partials(OnlineState<G> &st, float *part, size_t hbase,
+                                               size_t pstride, int sp, uint32_t heads_mask) {
+    constexpr int LPR = VMap<D>::LPR;
+    __shared__ float sm_m[4][G], sm_l[4][G];
+    __shared__ float sm_acc[4][G][D];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int o = LPR; o < 64; o <<= 1) st.acc[j][c] += __shfl_xor(st.acc[j][c], o, 64);
+    if (lane < LPR) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sm_acc[wave][j][lane * 8 + c] = st.acc[j][c];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            sm_m[wave][j] = st.m[j];
+            sm_l[wave][j] = st.l[j];
         }
+    }
+    __syncthreads();
+    // all 256 threads: thread -> (head, channel) pairs
+    for (int e = threadIdx.x; e < G * (D + 2); e += 256) {
+        const int j = e / (D + 2), c = e % (D + 2);
+        if (!(heads_mask & (1u << j))) continue;
+        float M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) o[2 + lane * CPL + k] = acc[j][k];
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][j]);
+        float r;
+        if (c == 0) {
+            r = M;
+        } else {
+            r = 0.0f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if (sm_m[w][j] == -INFINITY) continue;
+                    const float e_ = __expf(sm_m[w][j] - M);
+                    r = fmaf(e_, c == 1 ? sm_l[w][j] : sm_acc[w][j][c - 2], r);
+                }
+            }
+        }
+        part[((hbase + j) * pstride + sp) * (D + 2) + c] = r;
     }
 }
 
 // ===========================================================================
-// K4a: promoted blocks.  FP16-key scores of P blocks from the staging area
-// (FP64 chain, one rounding: the decision arithmetic of the rank check),
-// their FP16-side block estimate; values FP16 (VP) or INT4; partials.
-// One wave per (slot, kv head, sequence); the unfinished block is handled
-// here for every head.
+// K3: tail flash decoding over blocks outside P and VP [Meth-3: "remaining
+// tail blocks stay INT8"], values from INT4 codes.  256 threads per (split,
+// kv head, sequence); output path only: hardware exp and any summation
+// order are allowed here.
 // ===========================================================================
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_promoted(Layout Ly, Step St, const int *skip_seq) {
-    constexpr int CPL = D / 64;
-    const int slot = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_tail(Layout Ly, Step St) {
+    using M = VMap<D>;
+    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l = St.layer;
+    const int len = Ly.len[l * Ly.B + n];
+    const int N = len / 64;
+    const int b0 = sp * St.bps, b1 = min(N, b0 + St.bps);
+    __shared__ float pw[4][G][64];
+    const int cg = lane % M::LPR, rs = lane / M::LPR, c0 = cg * 8;
+    const size_t NS64 = (size_t)St.NS * 64;
+    OnlineState<G> st;
+    st.init();
+    for (int b = b0 + wave; b < b1; b += 4) {
+        const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b];
+        const uint32_t use = ~(bits | (bits >> 8)) & ((1u << G) - 1u);
+        if (!use) continue;
+        const size_t bi = Ly.blk(l, n, g, b);
+        const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
+        const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
+        uint32_t code[M::TPL], meta[M::TPL];
+#pragma unroll
+        for (int i = 0; i < M::TPL; ++i) {
+            const int t = i * M::RPI + rs;
+            code[i] = *reinterpret_cast<const uint32_t *>(vq + t * (D / 2) + c0 / 2);
+            meta[i] = vm[t * (D / 32) + c0 / 32];
+        }
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) {
+            if (!(use & (1u << jj))) {
+                pw[wave][jj][lane] = 0.0f;
+                continue;
+            }
+            const float s = St.score[(size_t)(n * Ly.Hq + g * G + jj) * NS64 + (size_t)b * 64 + lane];
+            st.weights(jj, s, true, pw[wave][jj], lane);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < M::TPL; ++i) {
+            const int t = i * M::RPI + rs;
+            float v[8];
+            unpack_int4x8(code[i], meta[i], v);
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj) {
+                const float p = pw[wave][jj][t];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, v[c], st.acc[jj][c]);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    write_partials<D, G>(st, St.part_tail, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp,
+                         (1u << G) - 1u);
+}
+
+// ===========================================================================
+// K4a: promoted blocks.  256 threads per (split, kv head, sequence), one wave
+// per block of the split that any head of the group promoted (P: FP16 keys,
+// VP: FP16 values), plus the unfinished block.  FP16-key scores use the FP64
+// chain with one rounding (the decision arithmetic of the rank check) and
+// give the FP16-side block estimate; values come from the staging area
+// (FP16) or tier 1 (INT4).  Output: one online-softmax partial per q head.
+// ===========================================================================
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int *skip_seq) {
+    using M = VMap<D>;
+    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l = St.layer;
     if (skip_seq[n]) return;
     const int len = Ly.len[l * Ly.B + n];
     const int N = len / 64, np = len % 64;
-    if (slot > N || (slot == N && np == 0)) return;
-    const bool part = slot == N;
-    uint32_t pm = 0, vm = 0;
-    if (!part) {
-        const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot];
-        pm = bits & 0xFFu;
-        vm = (bits >> 8) & 0xFFu;
-        if (!(pm | vm)) return;
-    }
-    __shared__ float qs[G][D];
-    __shared__ float pw[G][64];
-    __shared__ float vv[64][D + 1];
-    for (int i = lane; i < G * D; i += 64)
-        qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
-    const size_t NS64 = (size_t)St.NS * 64;
-    const size_t sblk = ((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot;
+    const int nslot = N + (np ? 1 : 0);
+    const int b0 = sp * St.bps, b1 = min(nslot, b0 + St.bps);
+    __shared__ double qd[D][G];
+    __shared__ float pw[4][G][64];
+    for (int i = threadIdx.x; i < G * D; i += 256)
+        qd[i % D][i / D] = (double)h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
-
-    // FP16-key scores for the P heads
-    float s16[G];
-    if (!part && pm) {
-        const uint16_t *kb = St.stage_k + sblk * 64 * D;
-        double a[G];
+    const int cg = lane % M::LPR, rs = lane / M::LPR, c0 = cg * 8;
+    const size_t NS64 = (size_t)St.NS * 64;
+    OnlineState<G> st;
+    st.init();
+    for (int b = b0 + wave; b < b1; b += 4) {
+        const bool part = b == N;
+        uint32_t pm = 0, vm = 0;
+        if (!part) {
+            const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b];
+            pm = bits & ((1u << G) - 1u);
+            vm = (bits >> 8) & ((1u << G) - 1u);
+            if (!(pm | vm)) continue;
+        }
+        const uint32_t use = part ? ((1u << G) - 1u) : (pm | vm);
+        const uint32_t fp16v = part ? use : vm;
+        const size_t sblk = ((size_t)n * Ly.Hkv + g) * Ly.Nmax + b;
+        // FP16-key scores of the P heads (lane = token): FP64 fma chain over
+        // c = 0 .. D-1, one rounding to FP32 after the scale
+        float s16[G];
+        if (pm) {
+            const uint16_t *kb = St.stage_k + sblk * 64 * D;
+            double a[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) a[j] = 0.0;
-        for (int ch = 0; ch < D / 8; ++ch) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+            for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
+#pragma unroll 2
+            for (int ch = 0; ch < D / 8; ++ch) {
+                const uint4 kv = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
+                float kf[8];
+                unpack_fp16x8(kv, kf);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const double kc = (double)h2f((uint16_t)(wd[i / 2] >> (16 * (i & 1))));
+                for (int i = 0; i < 8; ++i) {
+                    const double kc = (double)kf[i];
 #pragma unroll
-                for (int j = 0; j < G; ++j)
-                    if (pm & (1u << j)) a[j] = fma((double)qs[j][ch * 8 + i], kc, a[j]);
+                    for (int jj = 0; jj < G; ++jj) a[jj] = fma(qd[ch * 8 + i][jj], kc, a[jj]);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj) {
+                s16[jj] = (float)(a[jj] * (double)St.sm);
+                if (pm & (1u << jj)) {
+                    const float mx = wave_max_f32(s16[jj]);
+                    const float l_ = tree64_f32(exp_c(s16[jj] - mx));
+                    if (lane == 0) St.st16[((size_t)n * Ly.Hq + g * G + jj) * Ly.Nmax + b] = make_float2(mx, l_);
+                }
             }
         }
+        const bool valid = !part || lane < np;
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            s16[j] = (float)(a[j] * (double)St.sm);
-            if (pm & (1u << j)) {
-                const float mx = wave_max_f32(s16[j]);
-                const float l_ = tree64_f32(exp_c(s16[j] - mx));
-                if (lane == 0) St.st16[((size_t)n * Ly.Hq + g * G + j) * Ly.Nmax + slot] = make_float2(mx, l_);
+        for (int jj = 0; jj < G; ++jj) {
+            if (!(use & (1u << jj))) {
+                pw[wave][jj][lane] = 0.0f;
+                continue;
+            }
+            const float s = (pm & (1u << jj)) ? s16[jj]
+                            : St.score[(size_t)(n * Ly.Hq + g * G + jj) * NS64 + (size_t)b * 64 + lane];
+            st.weights(jj, s, valid, pw[wave][jj], lane);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // FP16 values (VP heads, unfinished block)
+        if (fp16v) {
+            const uint16_t *vrow = part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + sblk * 64 * D;
+#pragma unroll 4
+            for (int i = 0; i < M::TPL; ++i) {
+                const int t = i * M::RPI + rs;
+                float vf[8];
+                unpack_fp16x8(*reinterpret_cast<const uint4 *>(vrow + t * D + c0), vf);
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) {
+                    if (!(fp16v & (1u << jj))) continue;
+                    const float p = pw[wave][jj][t];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, vf[c], st.acc[jj][c]);
+                }
             }
         }
-    }
-    // values of the block into LDS (FP32)
-    const bool any_fp16v = part || vm;
-    const bool any_int4 = !part && ((pm | vm) & ~vm);
-    // weights per head
-    float mloc[G], lsum[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const int h = g * G + j;
-        const bool use = part || ((pm | vm) & (1u << j));
-        if (!use) {
-            pw[j][lane] = 0.0f;
-            mloc[j] = -INFINITY;
-            lsum[j] = 0.0f;
-            continue;
-        }
-        float s;
-        bool valid = true;
-        if (part) {
-            s = St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane];
-            valid = lane < np;
-        } else if (pm & (1u << j)) {
-            s = s16[j];
-        } else {
-            s = St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane];
-        }
-        const float mx = wave_max_f32(valid ? s : -INFINITY);
-        const float p = valid ? __expf(s - mx) : 0.0f;
-        pw[j][lane] = p;
-        float ps = p;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
-        mloc[j] = mx;
-        lsum[j] = ps;
-    }
-    // two passes over value sources: FP16 (for heads in VP / unfinished) and INT4
-    float acc[G][CPL];
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) acc[j][k] = 0.0f;
-    for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 0 && !any_fp16v) continue;
-        if (pass == 1 && !any_int4) continue;
-        __syncthreads();
-        if (pass == 0) {
-            const uint16_t *vb = part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + sblk * 64 * D;
-            for (int e = lane; e < 64 * D; e += 64) vv[e / D][e % D] = h2f(vb[e]);
-        } else {
-            const size_t bi = Ly.blk(l, n, g, slot);
+        // INT4 values (P heads without FP16 values)
+        const uint32_t int4v = use & ~fp16v;
+        if (int4v) {
+            const size_t bi = Ly.blk(l, n, g, b);
             const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
             const uint32_t *vmt = Ly.vmeta + bi * 64 * (D / 32);
-            for (int e = lane; e < 64 * (D / 2); e += 64) {
-                const int t = e / (D / 2), cb = e % (D / 2);
-                const uint8_t byte = vq[e];
-                const uint32_t mm = vmt[t * (D / 32) + (2 * cb) / 32];
-                const float sf = h2f((uint16_t)(mm & 0xFFFFu)), zf = h2f((uint16_t)(mm >> 16));
-                vv[t][2 * cb] = fmaf(sf, (float)(byte & 15), zf);
-                vv[t][2 * cb + 1] = fmaf(sf, (float)(byte >> 4), zf);
+#pragma unroll 4
+            for (int i = 0; i < M::TPL; ++i) {
+                const int t = i * M::RPI + rs;
+                float vf[8];
+                unpack_int4x8(*reinterpret_cast<const uint32_t *>(vq + t * (D / 2) + c0 / 2),
+                              vmt[t * (D / 32) + c0 / 32], vf);
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) {
+                    if (!(int4v & (1u << jj))) continue;
+                    const float p = pw[wave][jj][t];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, vf[c], st.acc[jj][c]);
+                }
             }
         }
-        __syncthreads();
-        uint32_t heads = 0;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const bool use = part || ((pm | vm) & (1u << j));
-            const bool fp16v = part || (vm & (1u << j));
-            if (use && (fp16v == (pass == 0))) heads |= 1u << j;
-        }
-        for (int t = 0; t < 64; ++t) {
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                if (!(heads & (1u << j))) continue;
-                const float p = pw[j][t];
-#pragma unroll
-                for (int k = 0; k < CPL; ++k) acc[j][k] = fmaf(p, vv[t][lane + 64 * k], acc[j][k]);
-            }
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const bool use = part || ((pm | vm) & (1u << j));
-        if (!use) continue;
-        const int h = g * G + j;
-        float *o = St.part_blk + ((size_t)(n * Ly.Hq + h) * St.NS + slot) * (D + 2);
-        if (lane == 0) {
-            o[0] = mloc[j];
-            o[1] = lsum[j];
-        }
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) o[2 + lane + 64 * k] = acc[j][k];
-    }
+    write_partials<D, G>(st, St.part_blk, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp,
+                         (1u << G) - 1u);
 }
 
 // ===========================================================================
@@ -785,32 +841,49 @@ __global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const i
         St.plan[hs].ndisc = (int)D_;
     }
 
-    // merge: tail splits, then used blocks in ascending order, then the
-    // unfinished block
-    float mx = -INFINITY;
-    const int nsp = (N + St.bps - 1) / St.bps;
+    // merge the tail partials and the promoted partials (fixed order; eight
+    // loads in flight at a time)
+    const int nsp_t = (N + St.bps - 1) / St.bps;
+    const int nsp_p = (N + (np ? 1 : 0) + St.bps - 1) / St.bps;
     const float *pt = St.part_tail + hs * St.nsplit_cap * (D + 2);
-    const float *pb = St.part_blk + hs * St.NS * (D + 2);
-    const uint32_t usebits = bitP | (bitP << 8);
-    for (int s = 0; s < nsp; ++s) mx = fmaxf(mx, pt[s * (D + 2)]);
-    for (int b = 0; b < N; ++b)
-        if (sel[b] & usebits) mx = fmaxf(mx, pb[(size_t)b * (D + 2)]);
-    if (np) mx = fmaxf(mx, pb[(size_t)N * (D + 2)]);
+    const float *pp = St.part_blk + hs * St.nsplit_cap * (D + 2);
+    constexpr int BATCH = 8;
+    float mx = -INFINITY;
+    auto part_ptr = [&](int i) { return i < nsp_t ? pt + (size_t)i * (D + 2) : pp + (size_t)(i - nsp_t) * (D + 2); };
+    const int ntot = nsp_t + nsp_p;
+    for (int i0 = 0; i0 < ntot; i0 += BATCH) {
+        float m[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) m[i] = i0 + i < ntot ? part_ptr(i0 + i)[0] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) mx = fmaxf(mx, m[i]);
+    }
     float den = 0.0f, num[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) num[k] = 0.0f;
-    auto add = [&](const float *p) {
-        const float m = p[0];
-        if (m == -INFINITY) return;
-        const float e = __expf(m - mx);
-        den = fmaf(e, p[1], den);
+    for (int i0 = 0; i0 < ntot; i0 += BATCH) {
+        float m[BATCH], l_[BATCH], a[BATCH][CPL];
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) num[k] = fmaf(e, p[2 + lane + 64 * k], num[k]);
-    };
-    for (int s = 0; s < nsp; ++s) add(pt + (size_t)s * (D + 2));
-    for (int b = 0; b < N; ++b)
-        if (sel[b] & usebits) add(pb + (size_t)b * (D + 2));
-    if (np) add(pb + (size_t)N * (D + 2));
+        for (int i = 0; i < BATCH; ++i) {
+            m[i] = -INFINITY;
+            if (i0 + i < ntot) {
+                const float *p = part_ptr(i0 + i);
+                m[i] = p[0];
+                l_[i] = p[1];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) a[i][k] = p[2 + lane + 64 * k];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            if (m[i] != -INFINITY) {
+                const float e = __expf(m[i] - mx);
+                den = fmaf(e, l_[i], den);
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) num[k] = fmaf(e, a[i][k], num[k]);
+            }
+        }
+    }
 #pragma unroll
     for (int k = 0; k < CPL; ++k) St.out[hs * D + lane + 64 * k] = num[k] / den;
 }
@@ -824,9 +897,10 @@ __global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const i
 
 
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_dense(DenseSrc S) {
-    constexpr int CPL = D / 64;
-    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
+    using M = VMap<D>;
+    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
     if (!mask) return;
     const int len = S.len[n];
@@ -834,20 +908,14 @@ __global__ __launch_bounds__(64) void k_dense(DenseSrc S) {
     const int nslot = N + (np ? 1 : 0);
     const int b0 = sp * S.bps, b1 = min(nslot, b0 + S.bps);
     __shared__ float qs[G][D];
-    __shared__ float pw[G][64];
-    __shared__ float vv[64][D + 1];
-    for (int i = lane; i < G * D; i += 64)
+    __shared__ float pw[4][G][64];
+    for (int i = threadIdx.x; i < G * D; i += 256)
         qs[i / D][i % D] = h2f(S.q[((size_t)n * S.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
-    float mrun[G], lrun[G], acc[G][CPL];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        mrun[j] = -INFINITY;
-        lrun[j] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) acc[j][k] = 0.0f;
-    }
-    for (int b = b0; b < b1; ++b) {
+    const int cg = lane % M::LPR, rs = lane / M::LPR, c0 = cg * 8;
+    OnlineState<G> st;
+    st.init();
+    for (int b = b0 + wave; b < b1; b += 4) {
         const bool part = b == N;
         const uint16_t *kb, *vb;
         if (part) {
@@ -857,61 +925,46 @@ __global__ __launch_bounds__(64) void k_dense(DenseSrc S) {
             kb = S.k + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
             vb = S.v + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
         }
+        uint4 v16[M::TPL], kv[D / 8];
+#pragma unroll
+        for (int i = 0; i < M::TPL; ++i) v16[i] = *reinterpret_cast<const uint4 *>(vb + (i * M::RPI + rs) * D + c0);
+#pragma unroll
+        for (int ch = 0; ch < D / 8; ++ch) kv[ch] = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
         const bool valid = !part || lane < np;
         float a[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) a[j] = 0.0f;
+        for (int jj = 0; jj < G; ++jj) a[jj] = 0.0f;
+#pragma unroll
         for (int ch = 0; ch < D / 8; ++ch) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+            float kf[8];
+            unpack_fp16x8(kv[ch], kf);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float kc = h2f((uint16_t)(wd[i / 2] >> (16 * (i & 1))));
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < G; ++j) a[j] = fmaf(qs[j][ch * 8 + i], kc, a[j]);
+                for (int jj = 0; jj < G; ++jj) a[jj] = fmaf(qs[jj][ch * 8 + i], kf[i], a[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) st.weights(jj, a[jj] * S.sm, valid, pw[wave][jj], lane);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < M::TPL; ++i) {
+            const int t = i * M::RPI + rs;
+            float vf[8];
+            unpack_fp16x8(v16[i], vf);
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj) {
+                const float p = pw[wave][jj][t];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, vf[c], st.acc[jj][c]);
             }
         }
-        __syncthreads();
-        for (int e = lane; e < 64 * D; e += 64) vv[e / D][e % D] = h2f(vb[e]);
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float s = a[j] * S.sm;
-            const float bm = wave_max_f32(valid ? s : -INFINITY);
-            const float mn = fmaxf(mrun[j], bm);
-            const float sc = __expf(mrun[j] - mn);
-            mrun[j] = mn;
-            lrun[j] *= sc;
-#pragma unroll
-            for (int k = 0; k < CPL; ++k) acc[j][k] *= sc;
-            const float p = valid ? __expf(s - mn) : 0.0f;
-            pw[j][lane] = p;
-            float ps = p;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
-            lrun[j] += ps;
-        }
-        __syncthreads();
-        for (int t = 0; t < 64; ++t) {
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float p = pw[j][t];
-#pragma unroll
-                for (int k = 0; k < CPL; ++k) acc[j][k] = fmaf(p, vv[t][lane + 64 * k], acc[j][k]);
-            }
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        if (!(mask & (1u << j))) continue;
-        const int h = g * G + j;
-        float *o = S.part + ((size_t)(n * S.Hq + h) * S.nsplit_cap + sp) * (D + 2);
-        if (lane == 0) {
-            o[0] = mrun[j];
-            o[1] = lrun[j];
-        }
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) o[2 + lane + 64 * k] = acc[j][k];
-    }
+    write_partials<D, G>(st, S.part, (size_t)n * S.Hq + g * G, S.nsplit_cap, sp, mask);
 }
 
 template <int D, int G>
@@ -963,15 +1016,16 @@ hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStre
 hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         hipLaunchKernelGGL((k_tail<decltype(D)::value, decltype(G)::value>),
-                           dim3(St.nsplit, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St);
+                           dim3(St.nsplit, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
         return hipGetLastError();
     });
 }
 
 hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        const int nsp = (St.nb + 1 + St.bps - 1) / St.bps;
         hipLaunchKernelGGL((k_promoted<decltype(D)::value, decltype(G)::value>),
-                           dim3(St.nb + 1, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St, skip_seq);
+                           dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
         return hipGetLastError();
     });
 }
@@ -988,7 +1042,7 @@ hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, con
 hipError_t launch_dense_src(int d, int G, const DenseSrc &S, int nsplit, int batch, hipStream_t s) {
     return dispatch(d, G, [&](auto D, auto GG) {
         hipLaunchKernelGGL((k_dense<decltype(D)::value, decltype(GG)::value>),
-                           dim3(nsplit, S.Hkv, batch), dim3(64), 0, s, S);
+                           dim3(nsplit, S.Hkv, batch), dim3(256), 0, s, S);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((k_merge_dense<decltype(D)::value, decltype(GG)::value>),

@@ -85,6 +85,23 @@ static inline double uniform_at(uint64_t seed, uint32_t tag, uint64_t i)
     return u53(r.v[0], r.v[1]);
 }
 
+/* Both normals of pair j (numbers 2j and 2j + 1 of the stream). */
+static inline void normal_pair(uint64_t seed, uint32_t tag, uint64_t j, double *z0, double *z1)
+{
+    p4 c;
+    c.v[0] = (uint32_t)j;
+    c.v[1] = (uint32_t)(j >> 32);
+    c.v[2] = tag;
+    c.v[3] = 0x6b7a1d35u;
+    p4 r = dg_philox(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    double u1 = 1.0 - u53(r.v[0], r.v[1]);
+    double u2 = u53(r.v[2], r.v[3]);
+    double rad = sqrt(-2.0 * log(u1));
+    double ang = 6.283185307179586 * u2;
+    *z0 = rad * cos(ang);
+    *z1 = rad * sin(ang);
+}
+
 void dg_normal(uint64_t seed, uint32_t tag, int64_t start, int64_t n, double *out)
 {
 #pragma omp parallel for schedule(static)
@@ -172,13 +189,16 @@ void dg_keys(uint64_t seed, int B, int T, int Hkv, int d, const float *chan_scal
                 for (int r = 0; r < rank && r < 64; r++)
                     u[r] = normal_at(seed, 11u, (((uint64_t)n * T + src_t) * Hkv + g) * 64 + r);
                 int pblk = src_t / 64;
+                double zz[2] = {0.0, 0.0};
                 for (int c = 0; c < d; c++) {
                     uint64_t e = (((uint64_t)n * T + src_t) * Hkv + g) * d + c;
+                    if ((c & 1) == 0)
+                        normal_pair(seed, 10u, e >> 1, &zz[0], &zz[1]);
                     double lr = 0.0;
                     for (int r = 0; r < rank; r++)
                         lr += u[r] * (double)W[((size_t)g * rank + r) * d + c];
                     double o = (double)chan_scale[g * d + c];
-                    double x = o * (lr + noise_std * normal_at(seed, 10u, e));
+                    double x = o * (lr + noise_std * zz[c & 1]);
                     x += (double)amp[((size_t)n * Hkv + g) * NB + pblk] * (double)dir[((size_t)n * Hkv + g) * d + c];
                     if (tie) {
                         uint64_t e2 = (((uint64_t)n * T + t) * Hkv + g) * d + c;
@@ -197,18 +217,23 @@ void dg_keys(uint64_t seed, int B, int T, int Hkv, int d, const float *chan_scal
  * with nu degrees of freedom (integer nu: z / sqrt(chi2_nu / nu)). */
 void dg_values(uint64_t seed, int B, int T, int Hkv, int d, int nu, double scale, uint16_t *out)
 {
-    int64_t n_el = (int64_t)B * T * Hkv * d;
+    int64_t n_el = (int64_t)B * T * Hkv * d; /* even: d is */
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n_el; i++) {
-        double z = normal_at(seed, 20u, (uint64_t)i);
+    for (int64_t i = 0; i < n_el; i += 2) {
+        double z[2];
+        normal_pair(seed, 20u, (uint64_t)i >> 1, &z[0], &z[1]);
         if (nu > 0) {
-            double chi = 0.0;
+            double chi[2] = {0.0, 0.0};
             for (int j = 0; j < nu; j++) {
-                double w = normal_at(seed, 21u + (uint32_t)j, (uint64_t)i);
-                chi += w * w;
+                double w0, w1;
+                normal_pair(seed, 21u + (uint32_t)j, (uint64_t)i >> 1, &w0, &w1);
+                chi[0] += w0 * w0;
+                chi[1] += w1 * w1;
             }
-            z = z / sqrt(chi / nu);
+            z[0] = z[0] / sqrt(chi[0] / nu);
+            z[1] = z[1] / sqrt(chi[1] / nu);
         }
-        out[i] = f2h_rne(scale * z);
+        out[i] = f2h_rne(scale * z[0]);
+        out[i + 1] = f2h_rne(scale * z[1]);
     }
 }

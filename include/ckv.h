@@ -186,10 +186,12 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
 
 /* Per-phase timing of decode steps, measured with HIP events on the
  * streams the work runs on.  Phases: 0 score (K1), 1 select (K2),
- * 2 tail (K3), 3 page-in wait (host round trip + H2D), 4 promoted + rank +
- * merge (K4), 5 fallback (paging + dense), 6 whole step.  ms: [8]
- * milliseconds accumulated since profiling was enabled; counts: [8]
- * number of timed occurrences.  Enabling resets the sums. */
+ * 2 tail (K3), 3 page-in (the H2D copies on the side stream), 4 promoted
+ * + rank + merge (K4), 5 fallback (paging + dense), 6 whole step (host
+ * wall clock).  ms: [8] milliseconds accumulated since profiling was
+ * enabled; counts: [8] number of timed occurrences, except counts[7] =
+ * host-to-device copies issued.  bytes_paged: bytes copied from tier 2.
+ * Enabling resets the sums. */
 ckv_status ckv_set_profiling(ckv_cache *c, int enable);
 ckv_status ckv_get_phase_times(ckv_cache *c, double *ms, int *counts, size_t *bytes_paged);
 
