@@ -14,7 +14,7 @@ CKV_STATUS = {0: "CKV_OK", 1: "CKV_EINVAL", 2: "CKV_ENOMEM", 3: "CKV_EHIP", 4: "
 EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv",
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
-            "ckv_set_profiling", "ckv_get_phase_times"]
+            "ckv_set_profiling", "ckv_get_profile"]
 
 
 class CkvError(RuntimeError):
@@ -36,6 +36,17 @@ class Thresholds(ctypes.Structure):
                 ("v_tol", ctypes.c_float), ("rank_tol", ctypes.c_float),
                 ("sm_scale", ctypes.c_float), ("f_layer", ctypes.c_float),
                 ("n_widen", ctypes.c_int), ("v_cap_blocks", ctypes.c_int)]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 8), ("counts", ctypes.c_int * 8), ("steps", ctypes.c_int),
+                ("bytes_paged", ctypes.c_uint64), ("copies", ctypes.c_uint64),
+                ("q8_blocks", ctypes.c_uint64), ("tail_blocks", ctypes.c_uint64),
+                ("k16_blocks", ctypes.c_uint64), ("v16_blocks", ctypes.c_uint64),
+                ("int4p_blocks", ctypes.c_uint64), ("dense_blocks", ctypes.c_uint64)]
+
+
+PHASES = ["score", "select", "tail", "page", "promoted", "fallback", "step", "merge"]
 
 
 REPORT_DTYPE = np.dtype([("e_key", "<f4"), ("e_val", "<f4"), ("tv_bound", "<f4"),
@@ -77,7 +88,7 @@ def lib():
         L.ckv_export_step.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int), vp, vp, vp, vp, vp,
                                       vp, vp, vp]
         L.ckv_set_profiling.argtypes = [vp, i32]
-        L.ckv_get_phase_times.argtypes = [vp, vp, vp, szp]
+        L.ckv_get_profile.argtypes = [vp, ctypes.POINTER(Profile)]
         for name in EXPORTED:
             if name not in ("ckv_destroy", "ckv_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -233,15 +244,14 @@ class Cache:
     def set_profiling(self, enable=True):
         _check(lib().ckv_set_profiling(self._h, int(enable)))
 
-    def phase_times(self):
-        ms = np.zeros(8, np.float64)
-        cnt = np.zeros(8, np.int32)
-        paged = ctypes.c_size_t()
-        _check(lib().ckv_get_phase_times(self._h, _np_ptr(ms), _np_ptr(cnt), ctypes.byref(paged)))
-        names = ["score", "select", "tail", "page", "promoted", "fallback", "step"]
-        ph = {n: (float(ms[i]), int(cnt[i])) for i, n in enumerate(names)}
-        ph["copies"] = (0.0, int(cnt[7]))
-        return ph, paged.value
+    def profile(self):
+        """Profile since set_profiling(True): phase times {name: (ms, count)}
+        and the counters of ckv_profile."""
+        p = Profile()
+        _check(lib().ckv_get_profile(self._h, ctypes.byref(p)))
+        r = {f: getattr(p, f) for f, _ in Profile._fields_ if f not in ("ms", "counts")}
+        r["phases"] = {nm: (float(p.ms[i]), int(p.counts[i])) for i, nm in enumerate(PHASES)}
+        return r
 
 
 def _torch_cuda():

@@ -46,7 +46,7 @@ ckv_status fail(ckv_status st, const char *fmt, ...) {
                         __FILE__, __LINE__);                                                \
     } while (0)
 
-enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH_N = 8 };
+enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH_MERGE, PH_N = 8 };
 
 }  // namespace
 
@@ -84,10 +84,7 @@ struct ckv_cache {
     bool have_step = false;
     int last_batch = 0, last_np = 0, last_nb = 0;
     bool prof = false;
-    double ms[PH_N] = {};
-    int cnt[PH_N] = {};
-    size_t bytes_paged = 0;
-    size_t ncopies = 0;
+    ckv_profile pf{};
 };
 
 namespace {
@@ -514,6 +511,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     size_t paged = 0;
     CopyList cl;
     if (prof) HIPCHK(hipEventRecord(E[5], c->side));
+    const uint32_t allg = (1u << G) - 1u;
     for (int n = 0; n < batch; ++n) {
         int skip = 0;
         for (int h = 0; h < Hq; ++h) skip |= (c->h_plan[(size_t)n * Hq + h].flags >> 1) & 1;
@@ -522,16 +520,26 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         for (int g = 0; g < Hkv; ++g) {
             const uint32_t *sl = c->h_sel + ((size_t)n * Hkv + g) * Ly.Nmax;
             for (int b = 0; b < N; ++b) {
-                wantk[b] = skip || (sl[b] & 0xFFu);
-                wantv[b] = skip || ((sl[b] >> 8) & 0xFFu);
+                const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
+                wantk[b] = skip || pm;
+                wantv[b] = skip || vm;
+                if (prof) {
+                    c->pf.tail_blocks += ((pm | vm) != allg);
+                    if (!skip) {
+                        c->pf.k16_blocks += pm != 0;
+                        c->pf.v16_blocks += vm != 0;
+                        c->pf.int4p_blocks += (pm & ~vm) != 0;
+                    }
+                }
             }
+            if (prof) c->pf.q8_blocks += N;
             page_runs(c, layer, n, g, N, wantk.data(), c->staged_k, c->t2k, c->stage_k, cl);
             page_runs(c, layer, n, g, N, wantv.data(), c->staged_v, c->t2v, c->stage_v, cl);
         }
     }
     TRY(issue_copies(c, cl));
     paged += cl.bytes;
-    c->ncopies += cl.size.size();
+    if (prof) c->pf.copies += cl.size.size();
     HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side));
     if (prof) HIPCHK(hipEventRecord(E[6], c->side));
     HIPCHK(hipEventRecord(c->ev_paged, c->side));
@@ -539,6 +547,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     // K4: promoted blocks, rank check, merge
     if (prof) HIPCHK(hipEventRecord(E[7], s));
     HIPCHK(launch_promoted(Ly, St, c->dskip, s));
+    if (prof) HIPCHK(hipEventRecord(E[11], s));
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, s));
     if (prof) HIPCHK(hipEventRecord(E[8], s));
     HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
@@ -573,12 +582,13 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 if (m) {
                     page_runs(c, layer, n, g, N, all.data(), c->staged_k, c->t2k, c->stage_k, cl);
                     page_runs(c, layer, n, g, N, all.data(), c->staged_v, c->t2v, c->stage_v, cl);
+                    if (prof) c->pf.dense_blocks += N;
                 }
             }
         }
         TRY(issue_copies(c, cl));
         paged += cl.bytes;
-        c->ncopies += cl.size.size();
+        if (prof) c->pf.copies += cl.size.size();
         HIPCHK(hipMemcpyAsync(c->dmask, c->h_mask, sizeof(uint32_t) * batch * Hkv, hipMemcpyHostToDevice,
                               c->side));
         HIPCHK(hipEventRecord(c->ev_paged, c->side));
@@ -642,23 +652,25 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     c->last_batch = batch;
     c->last_nb = nb;
     c->last_np = nb + np_any;
-    c->bytes_paged += paged;
     if (prof) {
+        c->pf.bytes_paged += paged;
+        c->pf.steps += 1;
         float t;
         auto acc = [&](int ph, int a, int b) -> ckv_status {
             HIPCHK(hipEventElapsedTime(&t, E[a], E[b]));
-            c->ms[ph] += t;
-            c->cnt[ph] += 1;
+            c->pf.ms[ph] += t;
+            c->pf.counts[ph] += 1;
             return CKV_OK;
         };
         TRY(acc(PH_SCORE, 0, 1));
         TRY(acc(PH_SELECT, 1, 2));
         if (St.nsplit > 0) TRY(acc(PH_TAIL, 3, 4));
         TRY(acc(PH_PAGE, 5, 6));
-        TRY(acc(PH_PROMO, 7, 8));
+        TRY(acc(PH_PROMO, 7, 11));
+        TRY(acc(PH_MERGE, 11, 8));
         if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
-        c->ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
-        c->cnt[PH_STEP] += 1;
+        c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+        c->pf.counts[PH_STEP] += 1;
     }
     return CKV_OK;
 }
@@ -781,21 +793,13 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
 ckv_status ckv_set_profiling(ckv_cache *c, int enable) {
     if (!c) return fail(CKV_EINVAL, "null cache");
     c->prof = enable != 0;
-    std::memset(c->ms, 0, sizeof c->ms);
-    std::memset(c->cnt, 0, sizeof c->cnt);
-    c->bytes_paged = 0;
-    c->ncopies = 0;
+    c->pf = ckv_profile{};
     return CKV_OK;
 }
 
-ckv_status ckv_get_phase_times(ckv_cache *c, double *ms, int *counts, size_t *bytes_paged) {
-    if (!c) return fail(CKV_EINVAL, "null cache");
-    for (int i = 0; i < PH_N; ++i) {
-        if (ms) ms[i] = c->ms[i];
-        if (counts) counts[i] = c->cnt[i];
-    }
-    if (counts) counts[PH_N - 1] = (int)std::min<size_t>(c->ncopies, 0x7FFFFFFF);
-    if (bytes_paged) *bytes_paged = c->bytes_paged;
+ckv_status ckv_get_profile(const ckv_cache *c, ckv_profile *p) {
+    if (!c || !p) return fail(CKV_EINVAL, "null argument");
+    *p = c->pf;
     return CKV_OK;
 }
 

@@ -775,12 +775,14 @@ __global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int 
 // INT8 order; inconsistent iff D > floor(rank_tol * K*(K*-1)/2).
 // ===========================================================================
 constexpr int RANK_LDS = 2048;
+constexpr int MERGE_T = 256;
 
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const int *skip_seq,
-                                              uint32_t *plist_g, uint64_t *keys_g) {
+__global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, const int *skip_seq,
+                                                   uint32_t *plist_g, uint64_t *keys_g) {
     constexpr int CPL = D / 64;
-    const int h = blockIdx.x, n = blockIdx.y, lane = threadIdx.x;
+    const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int g = h / G, j = h % G, l = St.layer;
     if (skip_seq[n]) return;
     const int len = Ly.len[l * Ly.B + n];
@@ -789,34 +791,46 @@ __global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const i
     const uint32_t *sel = St.sel + ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
     __shared__ uint32_t lds_list[RANK_LDS];
     __shared__ uint64_t lds_kI[RANK_LDS], lds_k16[RANK_LDS];
+    __shared__ long long red_ll[MERGE_T / 64];
+    __shared__ float red_f[MERGE_T / 64];
+    __shared__ float w_m[MERGE_T / 64], w_l[MERGE_T / 64], w_acc[MERGE_T / 64][D];
     __shared__ int cnt_s;
 
-    // compact list of P blocks (ascending index)
+    // compact list of P blocks (ascending index), by wave 0
     const uint32_t bitP = 1u << j;
     uint32_t *plist = plist_g + hs * Ly.Nmax;
-    int K = 0;
-    for (int b0 = 0; b0 < N; b0 += 64) {
-        const int b = b0 + lane;
-        const bool inP = b < N && (sel[b] & bitP);
-        const uint64_t bal = __ballot(inP);
-        const int pos = K + __popcll(bal & ((1ull << lane) - 1ull));
-        if (inP) {
-            plist[pos] = (uint32_t)b;
-            if (pos < RANK_LDS) lds_list[pos] = (uint32_t)b;
+    if (wave == 0) {
+        int K = 0;
+        for (int b0 = 0; b0 < N; b0 += 64) {
+            const int b = b0 + lane;
+            const bool inP = b < N && (sel[b] & bitP);
+            const uint64_t bal = __ballot(inP);
+            const int pos = K + __popcll(bal & ((1ull << lane) - 1ull));
+            if (inP) {
+                plist[pos] = (uint32_t)b;
+                if (pos < RANK_LDS) lds_list[pos] = (uint32_t)b;
+            }
+            K += __popcll(bal);
         }
-        K += __popcll(bal);
+        if (lane == 0) cnt_s = K;
     }
     __syncthreads();
+    const int K = cnt_s;
     const bool use_lds = K <= RANK_LDS;
     const uint32_t *list = use_lds ? lds_list : plist;
     uint64_t *kI = use_lds ? lds_kI : keys_g + hs * 2 * Ly.Nmax;
     uint64_t *k16 = use_lds ? lds_k16 : keys_g + hs * 2 * Ly.Nmax + Ly.Nmax;
     const float2 *st16 = St.st16 + hs * Ly.Nmax;
+    // largest FP16 block max over P
     float mr = -INFINITY;
-    for (int i = lane; i < K; i += 64) mr = fmaxf(mr, st16[list[i]].x);
+    for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[list[i]].x);
     mr = wave_max_f32(mr);
+    if (lane == 0) red_f[wave] = mr;
+    __syncthreads();
+    mr = red_f[0];
+    for (int w = 1; w < MERGE_T / 64; ++w) mr = fmaxf(mr, red_f[w]);
     const uint64_t *M = St.mfx + hs * St.NS;
-    for (int i = lane; i < K; i += 64) {
+    for (int i = tid; i < K; i += MERGE_T) {
         const uint32_t b = list[i];
         const float2 s = st16[b];
         const float m16 = s.y * exp_c(s.x - mr);
@@ -826,47 +840,59 @@ __global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const i
         k16[i] = (M16 << 16) | (uint64_t)(0xFFFF - b);
     }
     __syncthreads();
+    // Kendall discordant pairs: rows i and K-1-i go to the same thread so
+    // that every thread gets about the same number of pairs
     long long D_ = 0;
-    for (int i = lane; i < K; i += 64) {
-        const uint64_t a = kI[i], c = k16[i];
-        for (int q = i + 1; q < K; ++q) D_ += ((a > kI[q]) != (c > k16[q]));
+    for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {
+        const int rows[2] = {i, K - 1 - i};
+        for (int r = 0; r < (rows[0] == rows[1] ? 1 : 2); ++r) {
+            const int a_ = rows[r];
+            const uint64_t a = kI[a_], c = k16[a_];
+            for (int q = a_ + 1; q < K; ++q) D_ += ((a > kI[q]) != (c > k16[q]));
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) D_ += __shfl_xor(D_, o, 64);
-    const double pairs = (double)K * (double)(K - 1) / 2.0;
-    const double lim = floor((double)th.rank_tol * pairs);
-    const int ok = !((double)D_ > lim);
-    if (lane == 0) {
-        St.plan[hs].rank_ok = ok;
-        St.plan[hs].ndisc = (int)D_;
+    if (lane == 0) red_ll[wave] = D_;
+    __syncthreads();
+    if (tid == 0) {
+        long long Dt = 0;
+        for (int w = 0; w < MERGE_T / 64; ++w) Dt += red_ll[w];
+        const double pairs = (double)K * (double)(K - 1) / 2.0;
+        const double lim = floor((double)th.rank_tol * pairs);
+        St.plan[hs].rank_ok = !((double)Dt > lim);
+        St.plan[hs].ndisc = (int)Dt;
     }
 
-    // merge the tail partials and the promoted partials (fixed order; eight
-    // loads in flight at a time)
+    // merge: tail partials then promoted partials; each wave merges a
+    // contiguous quarter (eight loads in flight), the quarters are combined
+    // in wave order
     const int nsp_t = (N + St.bps - 1) / St.bps;
     const int nsp_p = (N + (np ? 1 : 0) + St.bps - 1) / St.bps;
     const float *pt = St.part_tail + hs * St.nsplit_cap * (D + 2);
     const float *pp = St.part_blk + hs * St.nsplit_cap * (D + 2);
-    constexpr int BATCH = 8;
-    float mx = -INFINITY;
     auto part_ptr = [&](int i) { return i < nsp_t ? pt + (size_t)i * (D + 2) : pp + (size_t)(i - nsp_t) * (D + 2); };
     const int ntot = nsp_t + nsp_p;
-    for (int i0 = 0; i0 < ntot; i0 += BATCH) {
+    const int per = (ntot + MERGE_T / 64 - 1) / (MERGE_T / 64);
+    const int i_lo = wave * per, i_hi = min(ntot, i_lo + per);
+    constexpr int BATCH = 8;
+    float mx = -INFINITY;
+    for (int i0 = i_lo; i0 < i_hi; i0 += BATCH) {
         float m[BATCH];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) m[i] = i0 + i < ntot ? part_ptr(i0 + i)[0] : -INFINITY;
+        for (int i = 0; i < BATCH; ++i) m[i] = i0 + i < i_hi ? part_ptr(i0 + i)[0] : -INFINITY;
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) mx = fmaxf(mx, m[i]);
     }
     float den = 0.0f, num[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) num[k] = 0.0f;
-    for (int i0 = 0; i0 < ntot; i0 += BATCH) {
+    for (int i0 = i_lo; i0 < i_hi; i0 += BATCH) {
         float m[BATCH], l_[BATCH], a[BATCH][CPL];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             m[i] = -INFINITY;
-            if (i0 + i < ntot) {
+            if (i0 + i < i_hi) {
                 const float *p = part_ptr(i0 + i);
                 m[i] = p[0];
                 l_[i] = p[1];
@@ -884,8 +910,29 @@ __global__ __launch_bounds__(64) void k_merge(Layout Ly, Step St, Th th, const i
             }
         }
     }
+    if (lane == 0) {
+        w_m[wave] = mx;
+        w_l[wave] = den;
+    }
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) St.out[hs * D + lane + 64 * k] = num[k] / den;
+    for (int k = 0; k < CPL; ++k) w_acc[wave][lane + 64 * k] = num[k];
+    __syncthreads();
+    if (wave == 0) {
+        float Mx = -INFINITY;
+        for (int w = 0; w < MERGE_T / 64; ++w) Mx = fmaxf(Mx, w_m[w]);
+        float dd = 0.0f, nn[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) nn[k] = 0.0f;
+        for (int w = 0; w < MERGE_T / 64; ++w) {
+            if (w_m[w] == -INFINITY) continue;
+            const float e = __expf(w_m[w] - Mx);
+            dd = fmaf(e, w_l[w], dd);
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) nn[k] = fmaf(e, w_acc[w][lane + 64 * k], nn[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) St.out[hs * D + lane + 64 * k] = nn[k] / dd;
+    }
 }
 
 // ===========================================================================
@@ -1034,7 +1081,7 @@ hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, con
                              uint32_t *plist, uint64_t *keys, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         hipLaunchKernelGGL((k_merge<decltype(D)::value, decltype(G)::value>),
-                           dim3(Ly.Hq, St.batch), dim3(64), 0, s, Ly, St, th, skip_seq, plist, keys);
+                           dim3(Ly.Hq, St.batch), dim3(MERGE_T), 0, s, Ly, St, th, skip_seq, plist, keys);
         return hipGetLastError();
     });
 }

@@ -184,16 +184,30 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
                            float *mref, uint64_t *mfx, uint32_t *sel, uint64_t *m16fx,
                            double *bounds, int *seq_flags);
 
-/* Per-phase timing of decode steps, measured with HIP events on the
- * streams the work runs on.  Phases: 0 score (K1), 1 select (K2),
- * 2 tail (K3), 3 page-in (the H2D copies on the side stream), 4 promoted
- * + rank + merge (K4), 5 fallback (paging + dense), 6 whole step (host
- * wall clock).  ms: [8] milliseconds accumulated since profiling was
- * enabled; counts: [8] number of timed occurrences, except counts[7] =
- * host-to-device copies issued.  bytes_paged: bytes copied from tier 2.
- * Enabling resets the sums. */
+/* Profile of the decode steps since profiling was enabled (enabling resets
+ * it).  Phase times are measured with HIP events on the streams the work
+ * runs on: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
+ * 3 page-in (the host-to-device copies on the side stream), 4 promoted
+ * pass (K4a), 5 fallback (paging + dense recompute), 6 the whole step on
+ * the host wall clock, 7 rank check + merge (K4b).  Block counts are what the
+ * passes read, summed over steps: a block is one (sequence, kv head, 64
+ * tokens).  Profiling adds a few event records per step. */
+typedef struct {
+    double ms[8];           /* accumulated milliseconds per phase            */
+    int counts[8];          /* timed occurrences per phase                   */
+    int steps;              /* decode steps profiled                         */
+    uint64_t bytes_paged;   /* tier 2 -> staging bytes (with filled gaps)    */
+    uint64_t copies;        /* host-to-device copies issued                  */
+    uint64_t q8_blocks;     /* blocks read by the scoring pass               */
+    uint64_t tail_blocks;   /* blocks read by the tail pass (INT4 values)    */
+    uint64_t k16_blocks;    /* FP16 key blocks read by the promoted pass     */
+    uint64_t v16_blocks;    /* FP16 value blocks read by the promoted pass   */
+    uint64_t int4p_blocks;  /* INT4 value blocks read by the promoted pass   */
+    uint64_t dense_blocks;  /* FP16 K+V blocks read by the dense fallback    */
+} ckv_profile;
+
 ckv_status ckv_set_profiling(ckv_cache *c, int enable);
-ckv_status ckv_get_phase_times(ckv_cache *c, double *ms, int *counts, size_t *bytes_paged);
+ckv_status ckv_get_profile(const ckv_cache *c, ckv_profile *p);
 
 #ifdef __cplusplus
 }
