@@ -297,23 +297,47 @@ void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uin
 
 /* ------------------------------------------------------------------------ */
 /* INT8 scoring pass [Meth-3, adaptive top-K selection]                     */
-/* s^_t = fl(fl(a_t + C) * sm), a_t = fma chain over c of w_c * code_tc with */
-/* w_c = q_c * s_c, C = halving-tree sum of q_c * z_c.                      */
+/* Reading (the page fixes no arithmetic for the "lightweight" INT8 pass):  */
+/* an exact integer dot product of rounded weights.  w_c = q_c s_c is exact */
+/* in FP32; with e = floor(log2 max_c |w_c|) the weights are rounded to     */
+/* integers w~_c = rint(w_c 2^(20-e)), |w~_c| <= 2^21; S_t = sum_c w~_c     */
+/* code_tc exactly; s^_t = fl32(fl64(C + S_t 2^(e-20)) * sm) with C the      */
+/* halving-tree FP32 sum of q_c z_c.  No summation order enters S_t.        */
 /* ------------------------------------------------------------------------ */
+
+/* e = floor(log2 max_c |w_c|); returns 0 when every w_c is 0. */
+static int weight_exponent(int d, const float *w, int *e)
+{
+    float W = 0.0f;
+    for (int c = 0; c < d; c++)
+        if (fabsf(w[c]) > W)
+            W = fabsf(w[c]);
+    if (W == 0.0f)
+        return 0;
+    *e = ilogbf(W);
+    return 1;
+}
+
 void orc_score_q8(int d, const uint16_t *q, const uint8_t *code, const uint16_t *s,
                   const uint16_t *z, float sm, float *out)
 {
     float w[256], cz[256];
+    int64_t wt[256];
     for (int c = 0; c < d; c++) {
         w[c] = orc_h2f(q[c]) * orc_h2f(s[c]);
         cz[c] = orc_h2f(q[c]) * orc_h2f(z[c]);
     }
     float C = tree_f32(cz, d);
+    int e = 0;
+    int nz = weight_exponent(d, w, &e);
+    for (int c = 0; c < d; c++)
+        wt[c] = nz ? (int64_t)rintf(ldexpf(w[c], 20 - e)) : 0;
     for (int t = 0; t < ORC_BT; t++) {
-        float a = 0.0f;
+        int64_t S = 0;
         for (int c = 0; c < d; c++)
-            a = fmaf(w[c], (float)code[t * d + c], a);
-        out[t] = (a + C) * sm;
+            S += wt[c] * (int64_t)code[t * d + c];
+        double x = (double)C + ldexp((double)S, e - 20);
+        out[t] = (float)(x * (double)sm);
     }
 }
 
@@ -332,37 +356,40 @@ void orc_score_f16(int d, const uint16_t *q, const uint16_t *k, int n, float sm,
 /* ------------------------------------------------------------------------ */
 /* Per-token score perturbation bound [Meth-2, E_key "bounded by Delta"]    */
 /* from the query and the quantization scales (tracked quantities only).    */
-/* With H = sum |q_c| s_c and A = sum |q_c| (|z_c| + 255 s_c):              */
-/*   |s^ - s| <= Delta = sm (kappa H + gamma(d+3) A)   (INT8 key score)      */
+/* With H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c) and              */
+/* E_w = 2^(e-21) 255 d (the weight rounding: at most half a unit of         */
+/* 2^(e-20) per channel, times codes <= 255; 0 when every w_c is 0):         */
+/*   |s^ - s| <= Delta = sm (kappa H + E_w + (2^-20 + 2^-23) A + 2^-23 E_w)  */
 /*   |s~ - s| <= rho   = sm 2^-23 A                   (FP16 key score)      */
-/* kappa = 1/2 + 2^-14 covers the code rounding, gamma(n) = n u/(1 - n u),   */
-/* u = 2^-24, the FP32 rounding of the INT8 fma chain; the FP16 chain runs   */
+/* kappa = 1/2 + 2^-14 covers the code rounding; 2^-20 A covers the tree    */
+/* sum of C (depth <= 7, < 2^-20 relative); 2^-23 (A + E_w) the roundings    */
+/* of the final FP64 sum, scale and FP32 conversion.  The FP16 chain runs   */
 /* in FP64 and is rounded once to FP32 (2^-24 + (d+3) 2^-53 < 2^-23).        */
 /* |k| <= |z| + 255 s for every key of the block, so A bounds sum |q_c k_c|. */
 /* Sums are FP64 halving trees; (1 + 2^-20) covers the FP64 rounding;       */
 /* results rounded up to FP32.                                              */
 /* ------------------------------------------------------------------------ */
-static double gamma_n(int n)
-{
-    double nu = (double)n * 0x1p-24;
-    return nu / (1.0 - nu);
-}
-
 void orc_delta_rho(int d, const uint16_t *q, const uint16_t *s, const uint16_t *z, float sm,
                    float *delta, float *rho)
 {
     double hv[256], av[256];
+    float w[256];
     for (int c = 0; c < d; c++) {
         double aq = fabs((double)orc_h2f(q[c]));
         double sc = (double)orc_h2f(s[c]);
         double zc = fabs((double)orc_h2f(z[c]));
         hv[c] = aq * sc;
         av[c] = aq * (zc + 255.0 * sc);
+        w[c] = orc_h2f(q[c]) * orc_h2f(s[c]);
     }
     double H = tree_f64(hv, d);
     double A = tree_f64(av, d);
+    int e = 0;
+    double Ew = weight_exponent(d, w, &e) ? ldexp(255.0 * (double)d, e - 21) : 0.0;
     double kappa = 0.5 + 0x1p-14;
-    double dl = kappa * H + gamma_n(d + 3) * A;
+    double dl = kappa * H + Ew;
+    dl = dl + A * (0x1p-20 + 0x1p-23);
+    dl = dl + Ew * 0x1p-23;
     dl = dl * (double)sm;
     dl = dl * (1.0 + 0x1p-20);
     double rh = A * 0x1p-23;

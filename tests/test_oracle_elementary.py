@@ -236,6 +236,32 @@ def test_delta_dominates_int8_score_error_and_is_tight(d):
     assert worst > 0.7
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_score_matches_dequantized_dot_product(d):
+    """The INT8 score against the exact dot product with the dequantized keys
+    z + s code (FP64): the difference is only the weight and FP rounding,
+    E_w + (2^-20 + 2^-23) A + 2^-23 E_w (all of Delta except kappa H)."""
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        q = f16(rng.standard_normal(d) * 10.0 ** rng.uniform(-3, 1))
+        kb = _k_blocks(rng, d)[trial % 6]
+        sm = [1.0, 0.125, 0.0883883][trial % 3]
+        code, s, z = oracle.quant_k_block(kb)
+        sc = oracle.score_q8(q, code, s, z, sm).astype(np.float64)
+        qf, sf, zf = h2f(q), h2f(s), h2f(z)
+        deq = zf[None, :] + sf[None, :] * code.astype(np.float64)
+        exact = sm * (deq @ qf)
+        w = (qf * sf).astype(np.float32).astype(np.float64)
+        W = np.abs(w).max()
+        Ew = 0.0 if W == 0 else 2.0 ** (np.floor(np.log2(W)) - 21) * 255 * d
+        A = np.sum(np.abs(qf) * (np.abs(zf) + 255 * sf))
+        tol = sm * (Ew + (2.0 ** -20 + 2.0 ** -23) * A + 2.0 ** -23 * Ew) * (1 + 1e-6)
+        assert np.abs(sc - exact).max() <= tol, trial
+        if W > 0:
+            # and the rounding really is small next to the quantization term
+            assert tol < 0.05 * sm * 0.5 * np.sum(np.abs(w)) + 1e-30
+
+
 def test_halving_delta_breaks_dominance():
     """Mutation: with Delta halved in the oracle, the adversarial block's
     INT8 score error exceeds the bound (the dominance check has teeth)."""
