@@ -39,21 +39,38 @@ static hipError_t dispatch(int d, int G, F f) {
 // K1: INT8 scoring pass [Meth-3 "lightweight scoring pass using INT8 keys to
 // estimate per-block attention masses"] and the per-token score
 // perturbation bound [Meth-2 "bounded by the per-token score perturbation"].
-//   s^_t = (a_t + C) * sm, a_t = fma chain over c of w_c * code_tc,
-//   w_c = q_c s_c, C = halving-tree sum of q_c z_c;
-//   Delta = sm (kappa H + gamma(d+3) A) (1 + 2^-20), rho = sm 2^-23 A (1 + 2^-20)
-//   with H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c), both FP64 trees.
+//
+// Score of token t for q head h in block b, as an exact integer dot product:
+//   w_c = q_c s_c (exact in FP32), e = floor(log2 max_c |w_c|),
+//   w~_c = rint(w_c 2^(20-e)) in [-2^21, 2^21],
+//   S_t = sum_c w~_c code_tc (exact), s^_t = fl32(fl64(C + S_t 2^(e-20)) sm),
+//   C = halving-tree FP32 sum of q_c z_c.
+// S_t is formed on the matrix cores: w~ = 2^16 d2 + 2^8 d1 + d0 with signed
+// byte digits, codes shifted to code - 128, one v_mfma_i32_16x16x64_i8 per
+// (16 tokens, 64 channels) with rows = (head, digit); int32 accumulation is
+// exact, so the result does not depend on the order of the sums.
+//   Delta = sm (kappa H + E_w + (2^-20 + 2^-23) A + 2^-23 E_w) (1 + 2^-20),
+//   rho = sm 2^-23 A (1 + 2^-20), E_w = 2^(e-21) 255 d,
+// with H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c) as FP64 trees.
+// One wave per (slot, kv head, sequence).
 // ===========================================================================
+typedef int v4i __attribute__((ext_vector_type(4)));
+
 template <int D, int G>
 __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
-    constexpr int CPL = D / 64;  // channels per lane
+    constexpr int CPL = D / 64;           // channels per lane (meta, trees)
+    constexpr int KS = D / 64;            // MFMA k-steps of 64 channels
+    constexpr int RT = (4 * G + 15) / 16; // MFMA row tiles of 4 heads x 4 digits
     const int slot = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
     const int l = St.layer;
     const int len = Ly.len[l * Ly.B + n];
     const int N = len / 64, np = len % 64;
     if (slot > N || (slot == N && np == 0)) return;
     __shared__ float qs[G][D];
-    __shared__ float w[G][D];
+    __shared__ __attribute__((aligned(16))) int8_t dig[G][4][D];
+    __shared__ double hd_C[G];
+    __shared__ int hd_e[G], hd_W[G];
+    __shared__ float hd_dl[G], hd_rh[G];
     for (int i = lane; i < G * D; i += 64)
         qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
@@ -107,70 +124,144 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
         return;
     }
 
-    // full block
+    // full block: code loads first, they are in flight during the set-up
     const size_t bi = Ly.blk(l, n, g, slot);
-    if (lane == 0) St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot] = 0u;
-    float sc[CPL], zc[CPL];
+    const uint8_t *kb = Ly.kq + bi * 64 * D;
+    v4i bq[4][KS];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        const uint32_t m = Ly.kmeta[bi * D + lane + 64 * k];
+    for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bq[tile][ks] = *reinterpret_cast<const v4i *>(kb + (ks * 4 + lane / 16) * 1024 +
+                                                          (tile * 16 + lane % 16) * 16);
+    if (lane == 0) St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot] = 0u;
+    // set-up per head: row r of the wave takes head r (+4 on a second pass);
+    // lane i of the row holds channels c = i + 16 k, k < D/16, so the
+    // halving tree over the channels runs in-lane for strides >= 16 and
+    // across the row (DPP) for strides 8..1.
+    constexpr int CPR = D / 16;
+    const int r = lane / 16, i16 = lane % 16;
+    float sc[CPR], zc[CPR];
+#pragma unroll
+    for (int k = 0; k < CPR; ++k) {
+        const uint32_t m = Ly.kmeta[bi * D + i16 + 16 * k];
         sc[k] = h2f((uint16_t)(m & 0xFFFFu));
         zc[k] = h2f((uint16_t)(m >> 16));
     }
-    float Cj[G], dj[G], rj[G];
     const double kappa = 0.5 + 0x1p-14;
-    const double gam = gamma_n(D + 3);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        float cz = qs[j][lane] * zc[0];
-        double hv = fabs((double)qs[j][lane]) * (double)sc[0];
-        double av = fabs((double)qs[j][lane]) * (fabs((double)zc[0]) + 255.0 * (double)sc[0]);
-        w[j][lane] = qs[j][lane] * sc[0];
-        if (CPL == 2) {
-            const float q1 = qs[j][lane + 64];
-            cz = cz + q1 * zc[CPL - 1];
-            hv = hv + fabs((double)q1) * (double)sc[CPL - 1];
-            av = av + fabs((double)q1) * (fabs((double)zc[CPL - 1]) + 255.0 * (double)sc[CPL - 1]);
-            w[j][lane + 64] = q1 * sc[CPL - 1];
+    for (int pass = 0; pass < (G + 3) / 4; ++pass) {
+        const int j = pass * 4 + r;
+        if (j < G) {
+            float w[CPR], cz[CPR];
+            double hv[CPR], av[CPR];
+            float wm = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CPR; ++k) {
+                const float q = qs[j][i16 + 16 * k];
+                w[k] = q * sc[k];
+                cz[k] = q * zc[k];
+                hv[k] = fabs((double)q) * (double)sc[k];
+                av[k] = fabs((double)q) * (fabs((double)zc[k]) + 255.0 * (double)sc[k]);
+                wm = fmaxf(wm, fabsf(w[k]));
+            }
+            // in-lane tree levels (channel strides D/2 .. 16)
+#pragma unroll
+            for (int st = CPR / 2; st >= 1; st >>= 1)
+#pragma unroll
+                for (int k = 0; k < st; ++k) {
+                    cz[k] = cz[k] + cz[k + st];
+                    hv[k] = hv[k] + hv[k + st];
+                    av[k] = av[k] + av[k + st];
+                }
+            const float C = row_tree_f32(cz[0]);
+            const double H = row_tree_f64(hv[0]);
+            const double A = row_tree_f64(av[0]);
+            wm = row_max_f32(wm);
+            const bool nz = wm > 0.0f;
+            const int e = nz ? (int)((__float_as_uint(wm) >> 23) & 0xFFu) - 127 : 0;
+            int wsum = 0;
+#pragma unroll
+            for (int k = 0; k < CPR; ++k) {
+                const int wt = nz ? (int)rintf(ldexpf(w[k], 20 - e)) : 0;
+                wsum += wt;
+                const int d0 = ((wt + 128) & 255) - 128;
+                const int r1 = (wt - d0) >> 8;
+                const int d1 = ((r1 + 128) & 255) - 128;
+                const int d2 = (r1 - d1) >> 8;
+                const int c = i16 + 16 * k;
+                dig[j][0][c] = (int8_t)d0;
+                dig[j][1][c] = (int8_t)d1;
+                dig[j][2][c] = (int8_t)d2;
+                dig[j][3][c] = 0;
+            }
+            wsum = row_sum_i32(wsum);
+            if (i16 == 0) {
+                const double Ew = nz ? ldexp(255.0 * (double)D, e - 21) : 0.0;
+                double dl = kappa * H + Ew;
+                dl = dl + A * (0x1p-20 + 0x1p-23);
+                dl = dl + Ew * 0x1p-23;
+                dl = dl * (double)sm;
+                dl = dl * (1.0 + 0x1p-20);
+                double rh = A * 0x1p-23;
+                rh = rh * (double)sm;
+                rh = rh * (1.0 + 0x1p-20);
+                hd_C[j] = (double)C;
+                hd_e[j] = e;
+                hd_W[j] = wsum;
+                hd_dl[j] = ru32(dl);
+                hd_rh[j] = ru32(rh);
+            }
         }
-        const float C = tree64_f32(cz);
-        const double H = tree64_f64(hv);
-        const double A = tree64_f64(av);
-        Cj[j] = __shfl(C, 0, 64);
-        double dl = kappa * H + gam * A;
-        dl = dl * (double)sm;
-        dl = dl * (1.0 + 0x1p-20);
-        double rh = A * 0x1p-23;
-        rh = rh * (double)sm;
-        rh = rh * (1.0 + 0x1p-20);
-        dj[j] = ru32(dl);  // meaningful in lane 0
-        rj[j] = ru32(rh);
     }
     __syncthreads();
 
-    const uint8_t *kb = Ly.kq + bi * 64 * D;
-    float acc[G];
+    // matrix cores: rows = (head, digit), columns = tokens, k = channels
+    const int row = lane % 16, hrow = row / 4, drow = row % 4;
 #pragma unroll
-    for (int j = 0; j < G; ++j) acc[j] = 0.0f;
-#pragma unroll 2
-    for (int ch = 0; ch < D / 16; ++ch) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(kb + ch * 1024 + lane * 16);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    for (int rt = 0; rt < RT; ++rt) {
+        const int ha = rt * 4 + hrow;  // head of this lane's A row
+        v4i a[KS];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float cf = (float)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-#pragma unroll
-            for (int j = 0; j < G; ++j) acc[j] = fmaf(w[j][ch * 16 + i], cf, acc[j]);
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ha < G)
+                a[ks] = *reinterpret_cast<const v4i *>(&dig[ha][drow][ks * 64 + (lane / 16) * 16]);
+            else
+                a[ks] = v4i{0, 0, 0, 0};
         }
-    }
+        const int hh = rt * 4 + lane / 16;  // head of this lane's output rows
+        float sv[4];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const int h = g * G + j;
-        const float s = (acc[j] + Cj[j]) * sm;
-        St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane] = s;
-        const float mx = wave_max_f32(s);
-        const float l_ = tree64_f32(exp_c(s - mx));
-        if (lane == 0) St.bstat[(size_t)(n * Ly.Hq + h) * St.NS + slot] = make_float4(mx, l_, dj[j], rj[j]);
+        for (int tile = 0; tile < 4; ++tile) {
+            v4i acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const v4i b = bq[tile][ks] ^ v4i{(int)0x80808080, (int)0x80808080, (int)0x80808080,
+                                                  (int)0x80808080};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], b, acc, 0, 0, 0);
+            }
+            sv[tile] = 0.0f;
+            if (hh < G) {
+                const long long S = ((long long)acc[2] << 16) + ((long long)acc[1] << 8) + (long long)acc[0] +
+                                    128ll * (long long)hd_W[hh];
+                const double x = hd_C[hh] + ldexp((double)S, hd_e[hh] - 20);
+                sv[tile] = (float)(x * (double)sm);
+                St.score[(size_t)(n * Ly.Hq + g * G + hh) * NS64 + (size_t)slot * 64 + tile * 16 + row] =
+                    sv[tile];
+            }
+        }
+        // block estimate of head hh: tokens tile*16 + row live in the 16
+        // lanes of the group; the halving tree over the 64 tokens is the
+        // in-lane steps of stride 32 and 16, then strides 8..1 across lanes
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = row_max_f32(mx);
+        float e4[4];
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) e4[tile] = exp_c(sv[tile] - mx);
+        const float u0 = e4[0] + e4[2], u1 = e4[1] + e4[3];
+        const float v = row_tree_f32(u0 + u1);
+        if (hh < G && row == 0)
+            St.bstat[(size_t)(n * Ly.Hq + g * G + hh) * St.NS + slot] = make_float4(mx, v, hd_dl[hh], hd_rh[hh]);
     }
 }
 

@@ -156,4 +156,67 @@ __device__ __forceinline__ int wave_or_i32(int v) {
     return v;
 }
 
+// ---- DPP row operations (16-lane rows of a wave64) --------------------------
+// row_shl:n gives lane i the value of lane i + n of its row; lanes past the
+// end of the row keep their own value.  quad_perm / mirrors permute inside
+// a row.  These run on the VALU without going through LDS.
+enum : int {
+    DPP_QP_1032 = 0xB1,        // quad_perm [1,0,3,2]
+    DPP_QP_2301 = 0x4E,        // quad_perm [2,3,0,1]
+    DPP_ROW_SL1 = 0x101,
+    DPP_ROW_SL2 = 0x102,
+    DPP_ROW_SL4 = 0x104,
+    DPP_ROW_SL8 = 0x108,
+    DPP_ROW_MIRROR = 0x140,
+    DPP_ROW_HALF_MIRROR = 0x141,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp((int)b, (int)b, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(b >> 32), (int)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Halving tree over the 16 lanes of a row (strides 8, 4, 2, 1: lane i adds
+// lane i + stride); the row's sum ends in its lane 0.
+__device__ __forceinline__ float row_tree_f32(float v) {
+    v = v + dpp_f32<DPP_ROW_SL8>(v);
+    v = v + dpp_f32<DPP_ROW_SL4>(v);
+    v = v + dpp_f32<DPP_ROW_SL2>(v);
+    v = v + dpp_f32<DPP_ROW_SL1>(v);
+    return v;
+}
+__device__ __forceinline__ double row_tree_f64(double v) {
+    v = v + dpp_f64<DPP_ROW_SL8>(v);
+    v = v + dpp_f64<DPP_ROW_SL4>(v);
+    v = v + dpp_f64<DPP_ROW_SL2>(v);
+    v = v + dpp_f64<DPP_ROW_SL1>(v);
+    return v;
+}
+// Order-free reductions over a row; every lane of the row gets the result.
+__device__ __forceinline__ float row_max_f32(float v) {
+    v = fmaxf(v, dpp_f32<DPP_QP_1032>(v));
+    v = fmaxf(v, dpp_f32<DPP_QP_2301>(v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_MIRROR>(v));
+    return v;
+}
+__device__ __forceinline__ int row_sum_i32(int v) {
+    v = v + dpp_i32<DPP_QP_1032>(v);
+    v = v + dpp_i32<DPP_QP_2301>(v);
+    v = v + dpp_i32<DPP_ROW_HALF_MIRROR>(v);
+    v = v + dpp_i32<DPP_ROW_MIRROR>(v);
+    return v;
+}
+
 }  // namespace ckv
