@@ -868,6 +868,72 @@ __global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int 
 constexpr int RANK_LDS = 2048;
 constexpr int MERGE_T = 256;
 
+// Number of elements of the descending run r[0..n) greater than x
+// (keys are unique).
+__device__ __forceinline__ int count_greater(const uint64_t *r, int n, uint64_t x) {
+    int lo = 0, hi = n;  // r[0..lo) > x, r[hi..n) < x
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (r[mid] > x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// Kendall discordant pairs between two orders of the same K <= RANK_LDS items
+// given as unique keys (kI[i], k16[i]): sort by kI descending (bitonic, in
+// LDS), then merge-sort the k16 sequence descending, counting for every
+// element of a right run the elements of the left run smaller than it.
+// Exact integer result, independent of the thread count.  Uses and
+// overwrites kI, k16; tmp holds RANK_LDS entries.  All threads call it.
+__device__ long long discordant_sorted(uint64_t *kI, uint64_t *k16, uint64_t *tmp, int K) {
+    const int tid = threadIdx.x;
+    int Kp = 1;
+    while (Kp < K) Kp <<= 1;
+    for (int i = K + tid; i < Kp; i += MERGE_T) {
+        kI[i] = 0;   // real keys are >= 1 after the shift below: padding sorts last
+        k16[i] = 0;
+    }
+    for (int i = tid; i < K; i += MERGE_T) kI[i] += 1;
+    __syncthreads();
+    for (int size = 2; size <= Kp; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < Kp / 2; t += MERGE_T) {
+                const int i = 2 * stride * (t / stride) + (t % stride);
+                const int jx = i + stride;
+                const bool desc = ((i & size) == 0);
+                const uint64_t a = kI[i], b = kI[jx];
+                if ((a < b) == desc) {
+                    kI[i] = b; kI[jx] = a;
+                    const uint64_t c = k16[i]; k16[i] = k16[jx]; k16[jx] = c;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    long long D = 0;
+    uint64_t *src = k16, *dst = tmp;
+    for (int w = 1; w < K; w <<= 1) {
+        for (int e = tid; e < K; e += MERGE_T) {
+            const int s0 = (e / (2 * w)) * (2 * w);
+            const int lw = min(w, K - s0);
+            const int rw = max(0, min(w, K - s0 - w));
+            const uint64_t x = src[e];
+            int pos;
+            if (e < s0 + lw) {
+                pos = (e - s0) + count_greater(src + s0 + lw, rw, x);
+            } else {
+                const int g = count_greater(src + s0, lw, x);
+                D += lw - g;   // left elements smaller than x: discordant
+                pos = (e - s0 - lw) + g;
+            }
+            dst[s0 + pos] = x;
+        }
+        __syncthreads();
+        uint64_t *t_ = src; src = dst; dst = t_;
+    }
+    return D;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, const int *skip_seq,
                                                    uint32_t *plist_g, uint64_t *keys_g) {
@@ -881,7 +947,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     const size_t hs = (size_t)n * Ly.Hq + h;
     const uint32_t *sel = St.sel + ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
     __shared__ uint32_t lds_list[RANK_LDS];
-    __shared__ uint64_t lds_kI[RANK_LDS], lds_k16[RANK_LDS];
+    __shared__ uint64_t lds_kI[RANK_LDS], lds_k16[RANK_LDS], lds_tmp[RANK_LDS];
     __shared__ long long red_ll[MERGE_T / 64];
     __shared__ float red_f[MERGE_T / 64];
     __shared__ float w_m[MERGE_T / 64], w_l[MERGE_T / 64], w_acc[MERGE_T / 64][D];
@@ -931,15 +997,19 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         k16[i] = (M16 << 16) | (uint64_t)(0xFFFF - b);
     }
     __syncthreads();
-    // Kendall discordant pairs: rows i and K-1-i go to the same thread so
-    // that every thread gets about the same number of pairs
+    // Kendall discordant pairs
     long long D_ = 0;
-    for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {
-        const int rows[2] = {i, K - 1 - i};
-        for (int r = 0; r < (rows[0] == rows[1] ? 1 : 2); ++r) {
-            const int a_ = rows[r];
-            const uint64_t a = kI[a_], c = k16[a_];
-            for (int q = a_ + 1; q < K; ++q) D_ += ((a > kI[q]) != (c > k16[q]));
+    if (use_lds) {
+        D_ = discordant_sorted(kI, k16, lds_tmp, K);
+    } else {
+        // rows i and K-1-i go to the same thread (equal work per thread)
+        for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {
+            const int rows[2] = {i, K - 1 - i};
+            for (int r = 0; r < (rows[0] == rows[1] ? 1 : 2); ++r) {
+                const int a_ = rows[r];
+                const uint64_t a = kI[a_], c = k16[a_];
+                for (int q = a_ + 1; q < K; ++q) D_ += ((a > kI[q]) != (c > k16[q]));
+            }
         }
     }
 #pragma unroll
