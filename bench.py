@@ -53,7 +53,7 @@ def block_layout(k, v):
     import numpy as np
     B, T, Hkv, d = k.shape
     kb = k.reshape(B, T // 64, 64, Hkv, d // 8, 8).transpose(0, 3, 1, 4, 2, 5)
-    vb = v.reshape(B, T // 64, 64, Hkv, d).transpose(0, 3, 1, 2, 4)
+    vb = v.reshape(B, T // 64, 64, Hkv, d).transpose(0, 3, 1, 4, 2)
     return np.ascontiguousarray(kb), np.ascontiguousarray(vb)
 
 
@@ -153,9 +153,9 @@ def run_workload(name, args, cpu_baseline):
 
     kern = {
         "k_score": ("score", prof["q8_blocks"] * q8_blk),
-        "k_tail": ("tail", prof["tail_blocks"] * i4_blk),
-        "k_promoted": ("promoted", (prof["k16_blocks"] + prof["v16_blocks"]) * f16_blk
-                       + prof["int4p_blocks"] * i4_blk),
+        "k_values_tail": ("tail", prof["tail_blocks"] * i4_blk),
+        "k_keys16": ("keys16", prof["k16_blocks"] * f16_blk),
+        "k_values_promoted": ("promoted", prof["v16_blocks"] * f16_blk + prof["int4p_blocks"] * i4_blk),
     }
     table = {}
     for kname, (phase, total_bytes) in kern.items():

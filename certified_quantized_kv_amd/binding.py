@@ -39,14 +39,14 @@ class Thresholds(ctypes.Structure):
 
 
 class Profile(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 8), ("counts", ctypes.c_int * 8), ("steps", ctypes.c_int),
+    _fields_ = [("ms", ctypes.c_double * 9), ("counts", ctypes.c_int * 9), ("steps", ctypes.c_int),
                 ("bytes_paged", ctypes.c_uint64), ("copies", ctypes.c_uint64),
                 ("q8_blocks", ctypes.c_uint64), ("tail_blocks", ctypes.c_uint64),
                 ("k16_blocks", ctypes.c_uint64), ("v16_blocks", ctypes.c_uint64),
                 ("int4p_blocks", ctypes.c_uint64), ("dense_blocks", ctypes.c_uint64)]
 
 
-PHASES = ["score", "select", "tail", "page", "promoted", "fallback", "step", "merge"]
+PHASES = ["score", "select", "tail", "page", "promoted", "fallback", "step", "merge", "keys16"]
 
 
 REPORT_DTYPE = np.dtype([("e_key", "<f4"), ("e_val", "<f4"), ("tv_bound", "<f4"),
@@ -195,7 +195,7 @@ class Cache:
                                stream=None):
         """Exact dense attention on device FP16 K/V in the block layout
         [batch][n_kv_heads][n_tokens/64][64*head_dim] (K chunk-interleaved
-        [head_dim/8][64][8], V token-major)."""
+        [head_dim/8][64][8], V channel-major [head_dim][64])."""
         import torch
         B = q.shape[0]
         if out is None:

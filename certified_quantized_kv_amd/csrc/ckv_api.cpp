@@ -46,7 +46,7 @@ ckv_status fail(ckv_status st, const char *fmt, ...) {
                         __FILE__, __LINE__);                                                \
     } while (0)
 
-enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH_MERGE, PH_N = 8 };
+enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH_MERGE, PH_KEYS, PH_N = 9 };
 
 }  // namespace
 
@@ -61,7 +61,8 @@ struct ckv_cache {
     uint16_t *t2k = nullptr, *t2v = nullptr;
     // staging and scratch (device)
     uint16_t *stage_k = nullptr, *stage_v = nullptr;
-    float *score = nullptr, *part_tail = nullptr, *part_blk = nullptr;
+    float *score = nullptr, *score16 = nullptr, *part_tail = nullptr, *part_blk = nullptr;
+    double *qd = nullptr;
     float4 *bstat = nullptr;
     uint64_t *mfx = nullptr, *cval = nullptr, *m16 = nullptr, *keys = nullptr;
     uint32_t *sel = nullptr, *plist = nullptr, *dmask = nullptr;
@@ -78,7 +79,7 @@ struct ckv_cache {
     size_t ain_cap = 0, pk_cap = 0;
     hipStream_t side = nullptr;
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
-    hipEvent_t pev[12] = {};
+    hipEvent_t pev[13] = {};
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
     std::vector<int> seq_flags;               // [B] of the last step
     bool have_step = false;
@@ -224,6 +225,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     c->tier1_bytes = c->dev_bytes - before;
     CTRY(dalloc(c, &Ly.vmin, (size_t)L * B * Hkv * d));
     CTRY(dalloc(c, &Ly.vmax, (size_t)L * B * Hkv * d));
+    CTRY(dalloc(c, &Ly.vscale, (size_t)L * B * Hkv * (d / 32)));
     CTRY(dalloc(c, &Ly.kpart, (size_t)L * B * Hkv * 64 * d));
     CTRY(dalloc(c, &Ly.vpart, (size_t)L * B * Hkv * 64 * d));
     CTRY(dalloc(c, &Ly.len, (size_t)L * B));
@@ -237,6 +239,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->stage_v, sblk * 64 * d));
     const size_t hsl = (size_t)B * Hq * c->NS;
     CTRY(dalloc(c, &c->score, hsl * 64));
+    CTRY(dalloc(c, &c->score16, hsl * 64));
     CTRY(dalloc(c, &c->bstat, hsl));
     CTRY(dalloc(c, &c->mfx, hsl));
     CTRY(dalloc(c, &c->cval, hsl));
@@ -246,6 +249,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->m16, (size_t)B * Hq * Nmax));
     CTRY(dalloc(c, &c->part_tail, (size_t)B * Hq * c->nsplit_cap * (d + 2)));
     CTRY(dalloc(c, &c->part_blk, hsl * (d + 2)));
+    CTRY(dalloc(c, &c->qd, (size_t)B * Hq * d));
     CTRY(dalloc(c, &c->plist, (size_t)B * Hq * Nmax));
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
     CTRY(dalloc(c, &c->dskip, (size_t)B));
@@ -464,6 +468,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.sm = th->sm_scale;
     St.q = (const uint16_t *)q;
     St.score = c->score;
+    St.score16 = c->score16;
     St.bstat = c->bstat;
     St.mfx = c->mfx;
     St.cval = c->cval;
@@ -475,6 +480,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.part_blk = c->part_blk;
     St.stage_k = c->stage_k;
     St.stage_v = c->stage_v;
+    St.qd = c->qd;
     St.out = out;
     Th T{};
     T.tau = th->tau_cov;
@@ -546,6 +552,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
     // K4: promoted blocks, rank check, merge
     if (prof) HIPCHK(hipEventRecord(E[7], s));
+    HIPCHK(launch_keys16(Ly, St, c->dskip, s));
+    if (prof) HIPCHK(hipEventRecord(E[12], s));
     HIPCHK(launch_promoted(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[11], s));
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, s));
@@ -666,7 +674,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         TRY(acc(PH_SELECT, 1, 2));
         if (St.nsplit > 0) TRY(acc(PH_TAIL, 3, 4));
         TRY(acc(PH_PAGE, 5, 6));
-        TRY(acc(PH_PROMO, 7, 11));
+        TRY(acc(PH_KEYS, 7, 12));
+        TRY(acc(PH_PROMO, 12, 11));
         TRY(acc(PH_MERGE, 11, 8));
         if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
         c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
@@ -731,14 +740,28 @@ ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int g, int b, uint
             if (k_z) k_z[ch] = (uint16_t)(m[ch] >> 16);
         }
     }
-    if (v_code) HIPCHK(hipMemcpy(v_code, Ly.vq + bi * 64 * (d / 2), 64 * (d / 2), hipMemcpyDeviceToHost));
+    if (v_code) {
+        // stored channel-major (byte c * 32 + t / 2, low nibble = even t)
+        std::vector<uint8_t> raw((size_t)64 * (d / 2));
+        HIPCHK(hipMemcpy(raw.data(), Ly.vq + bi * 64 * (d / 2), raw.size(), hipMemcpyDeviceToHost));
+        for (int t = 0; t < 64; ++t)
+            for (int ch = 0; ch < d; ch += 2) {
+                const int c0 = (raw[ch * 32 + t / 2] >> (4 * (t & 1))) & 15;
+                const int c1 = (raw[(ch + 1) * 32 + t / 2] >> (4 * (t & 1))) & 15;
+                v_code[t * (d / 2) + ch / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+    }
     if (v_s || v_z) {
-        std::vector<uint32_t> m(64 * (d / 32));
-        HIPCHK(hipMemcpy(m.data(), Ly.vmeta + bi * 64 * (d / 32), m.size() * 4, hipMemcpyDeviceToHost));
-        for (size_t i = 0; i < m.size(); ++i) {
-            if (v_s) v_s[i] = (uint16_t)(m[i] & 0xFFFFu);
-            if (v_z) v_z[i] = (uint16_t)(m[i] >> 16);
-        }
+        // stored group-major [d/32][64]
+        const int ng = d / 32;
+        std::vector<uint32_t> m((size_t)64 * ng);
+        HIPCHK(hipMemcpy(m.data(), Ly.vmeta + bi * 64 * ng, m.size() * 4, hipMemcpyDeviceToHost));
+        for (int t = 0; t < 64; ++t)
+            for (int gr = 0; gr < ng; ++gr) {
+                const uint32_t w = m[(size_t)gr * 64 + t];
+                if (v_s) v_s[t * ng + gr] = (uint16_t)(w & 0xFFFFu);
+                if (v_z) v_z[t * ng + gr] = (uint16_t)(w >> 16);
+            }
     }
     if (eta) HIPCHK(hipMemcpy(eta, Ly.eta + bi, 4, hipMemcpyDeviceToHost));
     return CKV_OK;

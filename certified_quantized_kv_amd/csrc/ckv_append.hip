@@ -31,14 +31,14 @@ __global__ __launch_bounds__(256) void k_pack(Layout Ly, int l, int n, const uin
         uint16_t kv = 0, vv = 0;
         if (i < len0) {
             kv = kp[(c / 8) * 512 + t * 8 + (c % 8)];
-            vv = vp[t * d + c];
+            vv = vp[c * 64 + t];
         } else if (i < (long)len0 + ntok) {
             const size_t src = ((size_t)(i - len0) * Ly.Hkv + g) * d + c;
             kv = kin[src];
             vv = vin[src];
         }
         ok[(c / 8) * 512 + t * 8 + (c % 8)] = kv;
-        ov[t * d + c] = vv;
+        ov[c * 64 + t] = vv;
     }
 }
 
@@ -78,17 +78,18 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
         uint8_t *kq = Ly.kq + blk * 64 * D + (c / 16) * 1024 + (c % 16);
         for (int t = 0; t < 64; ++t) kq[t * 16] = (uint8_t)quant_code(h2f(col[t * 8]), lo, sf, 255.0f);
     }
-    // values: one thread per token
+    // values: one thread per token; the codes are staged in LDS and packed
+    // channel-major, two tokens per byte
+    __shared__ uint8_t cq[D][64];
     double emax = 0.0;
     if (tid < 64) {
         const int t = tid;
-        const uint16_t *row = vb + t * D;
-        uint8_t *vq = Ly.vq + blk * 64 * (D / 2) + t * (D / 2);
-        uint32_t *vm = Ly.vmeta + blk * 64 * (D / 32) + t * (D / 32);
+        uint32_t *vm = Ly.vmeta + blk * 64 * (D / 32);
         for (int gr = 0; gr < D / 32; ++gr) {
-            float lo = h2f(row[gr * 32]), hi = lo;
+            const uint16_t *col = vb + (size_t)gr * 32 * 64 + t;  // channel gr*32 + c at col[c * 64]
+            float lo = h2f(col[0]), hi = lo;
             for (int c = 1; c < 32; ++c) {
-                float x = h2f(row[gr * 32 + c]);
+                const float x = h2f(col[c * 64]);
                 lo = fminf(lo, x);
                 hi = fmaxf(hi, x);
             }
@@ -96,20 +97,23 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
             const uint16_t sb = r == 0.0f ? (uint16_t)0 : f2h_up(r / 15.0f);
             const uint16_t zb = lo == 0.0f ? (uint16_t)0 : __half_as_ushort(__float2half_rn(lo));
             const float sf = h2f(sb);
-            vm[gr] = (uint32_t)sb | ((uint32_t)zb << 16);
-            for (int c = 0; c < 32; c += 2) {
-                const float x0 = h2f(row[gr * 32 + c]), x1 = h2f(row[gr * 32 + c + 1]);
-                const int q0 = quant_code(x0, lo, sf, 15.0f), q1 = quant_code(x1, lo, sf, 15.0f);
-                vq[(gr * 32 + c) / 2] = (uint8_t)(q0 | (q1 << 4));
-                const double r0 = (double)lo + (double)sf * (double)q0;
-                const double r1 = (double)lo + (double)sf * (double)q1;
-                emax = fmax(emax, fabs((double)x0 - r0));
-                emax = fmax(emax, fabs((double)x1 - r1));
+            vm[gr * 64 + t] = (uint32_t)sb | ((uint32_t)zb << 16);
+            for (int c = 0; c < 32; ++c) {
+                const float x = h2f(col[c * 64]);
+                const int q = quant_code(x, lo, sf, 15.0f);
+                cq[gr * 32 + c][t] = (uint8_t)q;
+                const double rec = (double)lo + (double)sf * (double)q;
+                emax = fmax(emax, fabs((double)x - rec));
             }
         }
     }
     emax_s[tid] = emax;
     __syncthreads();
+    uint8_t *vq = Ly.vq + blk * 64 * (D / 2);
+    for (int e = tid; e < D * 32; e += 128) {
+        const int c = e / 32, j = e % 32;
+        vq[c * 32 + j] = (uint8_t)(cq[c][2 * j] | (cq[c][2 * j + 1] << 4));
+    }
     if (tid == 0) {
         double m = 0.0;
         for (int i = 0; i < 64; ++i) m = fmax(m, emax_s[i]);
@@ -155,6 +159,35 @@ __global__ __launch_bounds__(128) void k_vrange(Layout Ly, int l, int n, const u
     atomicMax(&Ly.vmax[Ly.seqg(l, n, g) * d + c], f2ord(hi));
 }
 
+// K of a value group from its range R (largest max minus smallest min over
+// the group's channels): the smallest power of two P >= R / 15 (1 + 2^-8)
+// bounds every INT4 scale of the group (scale = range / 15 rounded up to
+// FP16, so scale <= R / 15 (1 + 2^-10)(1 + 2^-23)), and K = 2^14 / P, kept
+// in [1, 2^15].  The value passes weight INT4 codes by p s K and FP16 values
+// by p K, both below 2^15, before splitting the weights into FP16 parts.
+__device__ __forceinline__ float value_scale(double R) {
+    const double x = R / 15.0 * (1.0 + 0x1p-8);
+    if (!(x > 0.0)) return 0x1p15f;
+    int e;
+    (void)frexp(x, &e);  // x < 2^e
+    const int k = min(15, max(0, 14 - e));
+    return ldexpf(1.0f, k);
+}
+
+// One thread per (kv head, value group) of (l, n), after the range update.
+__global__ void k_vscale(Layout Ly, int l, int n) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x, ng = Ly.d / 32;
+    if (t >= Ly.Hkv * ng) return;
+    const int g = t / ng, gr = t % ng;
+    const size_t base = Ly.seqg(l, n, g) * Ly.d + gr * 32;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int c = 0; c < 32; ++c) {
+        lo = fminf(lo, ord2f(Ly.vmin[base + c]));
+        hi = fmaxf(hi, ord2f(Ly.vmax[base + c]));
+    }
+    Ly.vscale[Ly.seqg(l, n, g) * ng + gr] = value_scale((double)hi - (double)lo);
+}
+
 hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,
                        int len0, int ntok, int b0, int nblk, uint16_t *pk, uint16_t *pv,
                        hipStream_t s) {
@@ -185,6 +218,7 @@ hipError_t launch_vrange(const Layout &Ly, int l, int n, const uint16_t *vin, in
     const int chunk = 256;
     const int nch = (ntok + chunk - 1) / chunk;
     hipLaunchKernelGGL(k_vrange, dim3(Ly.Hkv, nch), dim3(128), 0, s, Ly, l, n, vin, ntok, chunk);
+    hipLaunchKernelGGL(k_vscale, dim3((Ly.Hkv * (Ly.d / 32) + 255) / 256), dim3(256), 0, s, Ly, l, n);
     return hipGetLastError();
 }
 

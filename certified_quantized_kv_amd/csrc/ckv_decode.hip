@@ -11,10 +11,12 @@
 //               w_c = q_c s_c staged in LDS.  Block max / mass / Delta / rho.
 //   k_select    per (seq, q head): estimated masses, top-K* by radix select,
 //               E_key / E_val, rung 1 (widen), rung 2 (FP16 values).
-//   k_tail      split-K flash decoding over blocks outside P and VP, INT4
-//               values unpacked in registers, online softmax partials.
-//   k_promoted  FP16-key scores of P blocks (from the staging area), FP16
-//               values of VP blocks, per-block partials and FP16 masses.
+//   k_tail      split-K flash decoding over the blocks outside P and VP:
+//   k_promoted  INT4 values (tail), and over the promoted blocks: FP16-key
+//               scores on P, FP16 values on VP; values unpacked in registers
+//               and contracted with the softmax weights on the matrix cores.
+//   k_keys16    FP16-key scores of the P blocks (staging area), FP64 chain;
+//               FP16-side block max / mass for the rank check.
 //   k_merge     rank-consistency check + merge of all partials -> output.
 //   k_dense     exact attention on FP16 blocks (rungs 3 / 4, and the dense
 //               comparator), split-K partials; k_merge_dense -> output.
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
     constexpr int RT = (4 * G + 15) / 16; // MFMA row tiles of 4 heads x 4 digits
     const int slot = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
     const int l = St.layer;
-    const int len = Ly.len[l * Ly.B + n];
+    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, np = len % 64;
     if (slot > N || (slot == N && np == 0)) return;
     __shared__ float qs[G][D];
@@ -74,6 +76,9 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
     for (int i = lane; i < G * D; i += 64)
         qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
+    if (slot == 0)  // q in FP64, [D][G] per (seq, kv head), for the promoted pass
+        for (int i = lane; i < G * D; i += 64)
+            St.qd[((size_t)n * Ly.Hkv + g) * D * G + i] = (double)qs[i % G][i / G];
     const float sm = St.sm;
     const size_t NS64 = (size_t)St.NS * 64;
 
@@ -108,8 +113,8 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
             const int h = g * G + j;
             const float s = valid ? (float)(a[j] * (double)sm) : 0.0f;
             St.score[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)slot * 64 + lane] = s;
-            const float mx = wave_max_f32(valid ? s : -INFINITY);
-            const float l_ = tree64_f32(valid ? exp_c(s - mx) : 0.0f);
+            const float mx = wave_max_dpp(valid ? s : -INFINITY);
+            const float l_ = tree64_f32_dpp(valid ? exp_c(s - mx) : 0.0f);
             double av = fabs((double)qs[j][lane]) * kmax[0];
             if (CPL == 2) av = av + fabs((double)qs[j][lane + 64]) * kmax[CPL - 1];
             const double A = tree64_f64(av);
@@ -267,9 +272,10 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
 
 // ===========================================================================
 // K2: selection, bounds, rungs 1-2 [Meth-2, Meth-3, Contrib].
-// One 256-thread workgroup per (q head, sequence).
+// One SEL_T-thread workgroup per (q head, sequence).
 // ===========================================================================
-constexpr int SEL_T = 256;
+constexpr int SEL_T = 512;
+constexpr int MAX_BPS = 64;  // blocks per split, at most (the host keeps bps in [4, 64])
 
 struct SelShared {
     uint64_t hsum[64];
@@ -409,7 +415,7 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int g = h / G, j = h % G, l = St.layer;
-    const int len = Ly.len[l * Ly.B + n];
+    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, has_part = (len % 64) != 0, Np = N + has_part;
     const size_t hs = (size_t)n * Ly.Hq + h;
     const float4 *bs = St.bstat + hs * St.NS;
@@ -550,95 +556,313 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
 }
 
 // ===========================================================================
-// Value passes (tail, promoted, dense) share one lane map: a wave covers one
-// 64-token block; lane owns 8 channels c0 = 8 (lane % (D/8)) and the tokens
-// t = i * RPI + lane / (D/8), i < TPL.  FP16 rows are read with 16-byte
-// loads, INT4 rows with 4-byte loads (8 nibbles); every load instruction of
-// a wave covers contiguous rows.  A workgroup has four waves on four blocks;
-// their online-softmax states are combined through LDS at the end.
+// Value passes (tail, promoted, dense): a wave covers one 64-token block and
+// contracts the softmax weights with the values on the matrix cores
+// (v_mfma_f32_16x16x32_f16; output path only, FP32 accumulation).
+//
+// Rows r = gv * G + h (value group gv of 32 channels, q head h), columns =
+// channels, k = tokens.  A row's weight for token t is a = p_t s_t K (INT4
+// codes; s_t the token's group scale) or a = p_t K (FP16 values), split into
+// FP16 hi + lo parts; K = 2^k is a per-group power of two that keeps every
+// a below 2^15 (from the running value range, which bounds every INT4 scale
+// of the group).  Lane l holds, for k-step ks, the tokens
+// 16 (l / 16) + 8 ks + (0 .. 7) of A row / B column l % 16; accumulator
+// tile (rt, nt) holds rows 16 rt + 4 (l / 16) + i, i < 4, of column
+// 16 nt + l % 16.  Only rows whose group is the column's group are kept;
+// the INT4 offsets enter through z-sums sum_t p_t z_t kept per A row.
+// A workgroup has four waves on four blocks; their states are combined
+// through LDS at the end.
 // ===========================================================================
-template <int D>
-struct VMap {
-    static constexpr int LPR = D / 8;      // lanes per row
-    static constexpr int RPI = 64 / LPR;   // rows per load instruction
-    static constexpr int TPL = 64 / RPI;   // tokens per lane
-};
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// 8 FP16 values of row t at channel c0.
+// 8 FP16 values (one 16-byte load) as FP32.
 __device__ __forceinline__ void unpack_fp16x8(const uint4 &u, float (&v)[8]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = h2f((uint16_t)(w[i / 2] >> (16 * (i & 1))));
 }
-// 8 INT4 codes (one 32-bit word) with the group's scale / offset.
-__device__ __forceinline__ void unpack_int4x8(uint32_t w, uint32_t meta, float (&v)[8]) {
-    const float sf = h2f((uint16_t)(meta & 0xFFFFu)), zf = h2f((uint16_t)(meta >> 16));
+
+// Eight INT4 codes of one word (token i at bits 4i) as an FP16 operand with
+// element 2i = token i and element 2i + 1 = token i + 4: 0x6400 | code is
+// 1024 + code exactly, and the packed subtraction of 1024 is exact.
+__device__ __forceinline__ v8h int4_operand(uint32_t w) {
+    const v2h off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    v4u r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = fmaf(sf, (float)((w >> (4 * i)) & 15u), zf);
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, x) + off);
+    }
+    return __builtin_bit_cast(v8h, r);
 }
 
-template <int G>
-struct OnlineState {
-    float m[G], l[G], acc[G][8];
+// x = hi + lo + err with FP16 hi, lo (round toward zero);
+// |err| <= max(2^-20 |x|, 2^-24).
+__device__ __forceinline__ void split_pair(float x, float y, uint32_t &hi, uint32_t &lo) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x, y);
+    const auto w = __builtin_amdgcn_cvt_pkrtz(x - (float)h[0], y - (float)h[1]);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, w);
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int G>
+struct VAcc {
+    static constexpr int NG = D / 32;         // value groups
+    static constexpr int R = NG * G;          // rows (group, head)
+    static constexpr int RT = (R + 15) / 16;  // row tiles
+    static constexpr int NT = D / 16;         // column tiles
+    v4f acc[RT][NT];
+    float zacc[RT];
+    float m[G], l[G];
+
     __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            zacc[rt] = 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             m[j] = -INFINITY;
             l[j] = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[j][c] = 0.0f;
         }
     }
-    // new block of head j: token score s (lane = token), valid lanes only;
-    // writes the token weights to pw[0..63].
-    __device__ __forceinline__ void weights(int j, float s, bool valid, float *pw, int lane) {
-        const float bm = wave_max_f32(valid ? s : -INFINITY);
-        const float mn = fmaxf(m[j], bm);
-        const float sc = __expf(m[j] - mn);
-        m[j] = mn;
-        l[j] *= sc;
+    // head of accumulator row 16 rt + 4 (lane / 16) + i
+    static __device__ __forceinline__ int drow_head(int lane, int i) {
+        return G <= 4 ? i % G : 4 * ((lane >> 4) & 1) + i;
+    }
+    // Online softmax over one block (lane = token): heads in `use` take the
+    // scores s[j]; the weights go to pw[j][lane] and the state is rescaled
+    // (per-head factors passed to the lanes through scl[0..G-1], LDS).
+    __device__ __forceinline__ void softmax(uint32_t use, const float (&s)[G], bool valid, float *pw,
+                                            float *scl, int lane) {
+        float sc[G];
+        bool any = false;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[j][c] *= sc;
-        const float p = valid ? __expf(s - mn) : 0.0f;
-        pw[lane] = p;
-        float ps = p;
+        for (int j = 0; j < G; ++j) {
+            sc[j] = 1.0f;
+            if (!(use & (1u << j))) continue;
+            const float bm = wave_max_dpp(valid ? s[j] : -INFINITY);
+            const float mn = fmaxf(m[j], bm);
+            if (mn != m[j]) {
+                sc[j] = __expf(m[j] - mn);
+                any = true;
+            }
+            m[j] = mn;
+            const float p = valid ? __expf(s[j] - mn) : 0.0f;
+            pw[j * 64 + lane] = p;
+            l[j] = fmaf(l[j], sc[j], wave_sum_dpp(p));
+        }
+        if (any) {
+            if (lane == 0)
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
-        l[j] += ps;
+                for (int j = 0; j < G; ++j) scl[j] = sc[j];
+            wave_sync();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float f = G <= 4 ? sc[i % G] : scl[drow_head(lane, i)];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[rt][nt][i] *= f;
+            }
+            const float fz = scl[(lane & 15) % G];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) zacc[rt] *= fz;
+        }
+    }
+    // Weights of A row 16 rt + lane % 16 for its 16 tokens; false if the row
+    // is unused (its operand is zero).
+    __device__ __forceinline__ bool arow(int rt, uint32_t mask, const float *pw, int lane, int &gv,
+                                         float (&p)[16]) const {
+        const int r = 16 * rt + (lane & 15);
+        const int h = r % G;
+        gv = min(r / G, NG - 1);
+        const float4 *src = reinterpret_cast<const float4 *>(pw + h * 64 + 16 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 x = src[i];
+            p[4 * i] = x.x;
+            p[4 * i + 1] = x.y;
+            p[4 * i + 2] = x.z;
+            p[4 * i + 3] = x.w;
+        }
+        return r < R && (mask & (1u << h));
+    }
+    // INT4 values for the heads in `mask`.  cw[nt]: the 16 tokens' codes of
+    // channel 16 nt + lane % 16; mt[rt]: the 16 tokens' scale | offset of the
+    // A row's group.
+    __device__ __forceinline__ void int4_block(uint32_t mask, const float *pw, const v4u (&mt)[RT][4],
+                                               const uint2 (&cw)[NT], const float *ksg, int lane) {
+        v8h ahi[RT][2], alo[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            int gv;
+            float p[16];
+            const bool on = arow(rt, mask, pw, lane, gv, p);
+            const float K = ksg[gv];
+            float a[16];
+            float z = zacc[rt];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t mw = mt[rt][i / 4][i % 4];
+                const float s = h2f((uint16_t)(mw & 0xFFFFu)), zz = h2f((uint16_t)(mw >> 16));
+                a[i] = on ? (p[i] * s) * K : 0.0f;
+                z = on ? fmaf(p[i], zz, z) : z;
+            }
+            zacc[rt] = z;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                v4u hi, lo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t x, y;
+                    split_pair(a[8 * ks + i], a[8 * ks + i + 4], x, y);
+                    hi[i] = x;
+                    lo[i] = y;
+                }
+                ahi[rt][ks] = __builtin_bit_cast(v8h, hi);
+                alo[rt][ks] = __builtin_bit_cast(v8h, lo);
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const v8h b0 = int4_operand(cw[nt].x), b1 = int4_operand(cw[nt].y);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                v4f c = acc[rt][nt];
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[rt][0], b0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[rt][0], b0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[rt][1], b1, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[rt][1], b1, c, 0, 0, 0);
+                acc[rt][nt] = c;
+            }
+        }
+    }
+    // FP16 values for the heads in `mask`.  vv[nt][ks]: tokens
+    // 16 (lane / 16) + 8 ks + (0 .. 7) of channel 16 nt + lane % 16.
+    __device__ __forceinline__ void fp16_block(uint32_t mask, const float *pw, const uint4 (&vv)[NT][2],
+                                               const float *ksg, int lane) {
+        v8h ahi[RT][2], alo[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            int gv;
+            float p[16];
+            const bool on = arow(rt, mask, pw, lane, gv, p);
+            const float K = ksg[gv];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                v4u hi, lo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t x, y;
+                    split_pair(on ? p[8 * ks + 2 * i] * K : 0.0f, on ? p[8 * ks + 2 * i + 1] * K : 0.0f, x, y);
+                    hi[i] = x;
+                    lo[i] = y;
+                }
+                ahi[rt][ks] = __builtin_bit_cast(v8h, hi);
+                alo[rt][ks] = __builtin_bit_cast(v8h, lo);
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const v8h b0 = __builtin_bit_cast(v8h, vv[nt][0]), b1 = __builtin_bit_cast(v8h, vv[nt][1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                v4f c = acc[rt][nt];
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[rt][0], b0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[rt][0], b0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[rt][1], b1, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[rt][1], b1, c, 0, 0, 0);
+                acc[rt][nt] = c;
+            }
+        }
     }
 };
 
-// Sum the partial accumulators of the lanes that share channels, combine the
-// four waves' states and write one partial (m, l, acc[D]) per head of the
-// group to part + (head * pstride + sp) * (D + 2).
+// Tier-1 value operands of block `bi` for this lane: INT4 codes (channel-
+// major, 32 bytes per channel) and the scale | offset words of the A rows'
+// groups (group-major, 64 words per group).
 template <int D, int G>
-__device__ __forceinline__ void write_partials(OnlineState<G> &st, float *part, size_t hbase,
-                                               size_t pstride, int sp, uint32_t heads_mask) {
-    constexpr int LPR = VMap<D>::LPR;
+__device__ __forceinline__ void load_int4(const Layout &Ly, size_t bi, int lane, uint2 (&cw)[D / 16],
+                                          v4u (&mt)[VAcc<D, G>::RT][4]) {
+    using VA = VAcc<D, G>;
+    const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
+    const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
+#pragma unroll
+    for (int nt = 0; nt < VA::NT; ++nt)
+        cw[nt] = *reinterpret_cast<const uint2 *>(vq + (16 * nt + (lane & 15)) * 32 + 8 * (lane >> 4));
+#pragma unroll
+    for (int rt = 0; rt < VA::RT; ++rt) {
+        const int gv = min((16 * rt + (lane & 15)) / G, VA::NG - 1);
+        const v4u *src = reinterpret_cast<const v4u *>(vm + gv * 64 + 16 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mt[rt][i] = src[i];
+    }
+}
+
+// FP16 value operands of a channel-major block [D][64].
+template <int D>
+__device__ __forceinline__ void load_fp16v(const uint16_t *vb, int lane, uint4 (&vv)[D / 16][2]) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            vv[nt][ks] = *reinterpret_cast<const uint4 *>(vb + (16 * nt + (lane & 15)) * 64 +
+                                                          16 * (lane >> 4) + 8 * ks);
+}
+
+// Write one partial (m, l, acc[D]) per head of the group to
+// part + (head * pstride + sp) * (D + 2), combining the four waves.
+template <int D, int G>
+__device__ __forceinline__ void write_partials(VAcc<D, G> &va, const float *ksg, float *part,
+                                               size_t hbase, size_t pstride, int sp,
+                                               uint32_t heads_mask) {
+    using VA = VAcc<D, G>;
     __shared__ float sm_m[4][G], sm_l[4][G];
     __shared__ float sm_acc[4][G][D];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ float sm_z[4][VA::RT * 16];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kg = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+    for (int rt = 0; rt < VA::RT; ++rt) {
+        float z = va.zacc[rt];
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        if (lane < 16) sm_z[wave][16 * rt + lane] = z;
+    }
+    wave_sync();
+    // column tile nt belongs to value group nt / 2; the rows of that group
+    // hold its heads (accumulator indices stay compile-time constants)
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+    for (int nt = 0; nt < VA::NT; ++nt) {
+        const float inv = 1.0f / ksg[nt / 2];
 #pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) st.acc[j][c] += __shfl_xor(st.acc[j][c], o, 64);
-    if (lane < LPR) {
+        for (int rt = 0; rt < VA::RT; ++rt)
 #pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) sm_acc[wave][j][lane * 8 + c] = st.acc[j][c];
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rt + 4 * kg + i;
+                if (r < VA::R && r / G == nt / 2)
+                    sm_acc[wave][r % G][16 * nt + (lane & 15)] = fmaf(va.acc[rt][nt][i], inv, sm_z[wave][r]);
+            }
     }
     if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            sm_m[wave][j] = st.m[j];
-            sm_l[wave][j] = st.l[j];
+            sm_m[wave][j] = va.m[j];
+            sm_l[wave][j] = va.l[j];
         }
     }
     __syncthreads();
-    // all 256 threads: thread -> (head, channel) pairs
     for (int e = threadIdx.x; e < G * (D + 2); e += 256) {
         const int j = e / (D + 2), c = e % (D + 2);
         if (!(heads_mask & (1u << j))) continue;
@@ -664,199 +888,228 @@ __device__ __forceinline__ void write_partials(OnlineState<G> &st, float *part, 
 }
 
 // ===========================================================================
-// K3: tail flash decoding over blocks outside P and VP [Meth-3: "remaining
-// tail blocks stay INT8"], values from INT4 codes.  256 threads per (split,
-// kv head, sequence); output path only: hardware exp and any summation
-// order are allowed here.
+// K3 (k_tail) / K4a values (k_promoted): split-K flash decoding over one
+// split of blocks of a (kv head, sequence); 256 threads, one wave per block.
+//   tail (PROM = false)  blocks and heads outside P and VP [Meth-3: "remaining
+//                        tail blocks stay INT8"]: INT8 scores, INT4 values.
+//   promoted (PROM)      heads of P or VP, plus the unfinished block: FP16-key
+//                        scores on P (from k_keys16) else INT8 scores; FP16
+//                        values on VP (staging area) and the unfinished block
+//                        (device), INT4 values otherwise.
+// Output path only: hardware exp and any summation order are allowed here.
 // ===========================================================================
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_tail(Layout Ly, Step St) {
-    using M = VMap<D>;
+template <int D, int G, bool PROM>
+__device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, const int *skip_seq) {
+    using VA = VAcc<D, G>;
     const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave index as a uniform value: the block loop below branches uniformly
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l = St.layer;
-    const int len = Ly.len[l * Ly.B + n];
-    const int N = len / 64;
-    const int b0 = sp * St.bps, b1 = min(N, b0 + St.bps);
-    __shared__ float pw[4][G][64];
-    const int cg = lane % M::LPR, rs = lane / M::LPR, c0 = cg * 8;
+    if (PROM && skip_seq[n]) return;
+    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
+    const int N = len / 64, np = len % 64;
+    const int nslot = PROM ? N + (np ? 1 : 0) : N;
+    const int b0 = sp * St.bps, b1 = min(nslot, b0 + St.bps);
+    constexpr uint32_t ALL = (1u << G) - 1u;
+    __shared__ __attribute__((aligned(16))) float pw[4][G][64];
+    __shared__ float scl[4][G];
+    __shared__ float ksg[VA::NG];
+    __shared__ uint32_t sbits[MAX_BPS];
+    // selection bits of the split and the value-group scales: one round trip
+    const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
+    for (int i = threadIdx.x; i < b1 - b0; i += 256) sbits[i] = b0 + i < N ? St.sel[selbase + b0 + i] : 0u;
+    if (threadIdx.x < VA::NG) ksg[threadIdx.x] = Ly.vscale[Ly.seqg(l, n, g) * VA::NG + threadIdx.x];
+    __syncthreads();
     const size_t NS64 = (size_t)St.NS * 64;
-    OnlineState<G> st;
-    st.init();
-    for (int b = b0 + wave; b < b1; b += 4) {
-        const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b];
-        const uint32_t use = ~(bits | (bits >> 8)) & ((1u << G) - 1u);
-        if (!use) continue;
-        const size_t bi = Ly.blk(l, n, g, b);
-        const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
-        const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
-        uint32_t code[M::TPL], meta[M::TPL];
-#pragma unroll
-        for (int i = 0; i < M::TPL; ++i) {
-            const int t = i * M::RPI + rs;
-            code[i] = *reinterpret_cast<const uint32_t *>(vq + t * (D / 2) + c0 / 2);
-            meta[i] = vm[t * (D / 32) + c0 / 32];
+    VA va;
+    va.init();
+    struct Blk {
+        uint32_t pm, use, fp16v, int4v;
+        bool part;
+    };
+    struct Opd {
+        uint4 vv[VA::NT][2];
+        uint2 cw[VA::NT];
+        v4u mt[VA::RT][4];
+        float s[G];
+    };
+    auto plan = [&](int b) {
+        Blk k;
+        k.part = PROM && b == N;
+        k.pm = 0;
+        if (k.part) {
+            k.use = ALL;
+            k.fp16v = ALL;
+        } else {
+            const uint32_t bits = __builtin_amdgcn_readfirstlane(sbits[b - b0]);
+            k.pm = bits & ALL;
+            const uint32_t vm = (bits >> 8) & ALL;
+            k.use = PROM ? (k.pm | vm) : (~(k.pm | vm) & ALL);
+            k.fp16v = PROM ? vm : 0u;
         }
+        k.int4v = k.use & ~k.fp16v;
+        return k;
+    };
+    auto issue = [&](int b, const Blk &k, Opd &o) {
+        if (!k.use) return;
+        const size_t sblk = selbase + b;
+        if (PROM && k.fp16v)
+            load_fp16v<D>(k.part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + sblk * 64 * D, lane, o.vv);
+        if (k.int4v) load_int4<D, G>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
 #pragma unroll
-        for (int jj = 0; jj < G; ++jj) {
-            if (!(use & (1u << jj))) {
-                pw[wave][jj][lane] = 0.0f;
-                continue;
+        for (int j = 0; j < G; ++j) {
+            const size_t si = (size_t)(n * Ly.Hq + g * G + j) * NS64 + (size_t)b * 64 + lane;
+            o.s[j] = !(k.use & (1u << j)) ? 0.0f : (PROM && (k.pm & (1u << j))) ? St.score16[si] : St.score[si];
+        }
+    };
+    auto consume = [&](const Blk &k, const Opd &o) {
+        if (!k.use) return;
+        va.softmax(k.use, o.s, !k.part || lane < np, &pw[wave][0][0], scl[wave], lane);
+        wave_sync();
+        if (PROM && k.fp16v) va.fp16_block(k.fp16v, &pw[wave][0][0], o.vv, ksg, lane);
+        if (k.int4v) va.int4_block(k.int4v, &pw[wave][0][0], o.mt, o.cw, ksg, lane);
+        wave_sync();
+    };
+    if constexpr (!PROM) {
+        // two blocks in flight per wave: the next block's operands are
+        // requested before the current one is consumed
+        Opd o0, o1;
+        Blk k0{}, k1{};
+        int b = b0 + wave;
+        if (b < b1) {
+            k0 = plan(b);
+            issue(b, k0, o0);
+        }
+        for (; b < b1; b += 8) {
+            const bool more = b + 4 < b1;
+            if (more) {
+                k1 = plan(b + 4);
+                issue(b + 4, k1, o1);
             }
-            const float s = St.score[(size_t)(n * Ly.Hq + g * G + jj) * NS64 + (size_t)b * 64 + lane];
-            st.weights(jj, s, true, pw[wave][jj], lane);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int i = 0; i < M::TPL; ++i) {
-            const int t = i * M::RPI + rs;
-            float v[8];
-            unpack_int4x8(code[i], meta[i], v);
-#pragma unroll
-            for (int jj = 0; jj < G; ++jj) {
-                const float p = pw[wave][jj][t];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, v[c], st.acc[jj][c]);
+            consume(k0, o0);
+            if (!more) break;
+            if (b + 8 < b1) {
+                k0 = plan(b + 8);
+                issue(b + 8, k0, o0);
             }
+            consume(k1, o1);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        for (int b = b0 + wave; b < b1; b += 4) {
+            const Blk k = plan(b);
+            if (!k.use) continue;
+            Opd o;
+            issue(b, k, o);
+            consume(k, o);
+        }
     }
-    write_partials<D, G>(st, St.part_tail, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp,
-                         (1u << G) - 1u);
+    write_partials<D, G>(va, ksg, PROM ? St.part_blk : St.part_tail, (size_t)n * Ly.Hq + g * G,
+                         St.nsplit_cap, sp, ALL);
+}
+
+// Tail: three waves per SIMD where the registers allow (two blocks in flight
+// per wave).
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G * D <= 512 ? 3 : 2))) void k_tail(Layout Ly, Step St) {
+    values_pass<D, G, false>(Ly, St, nullptr);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int *skip_seq) {
+    values_pass<D, G, true>(Ly, St, skip_seq);
 }
 
 // ===========================================================================
-// K4a: promoted blocks.  256 threads per (split, kv head, sequence), one wave
-// per block of the split that any head of the group promoted (P: FP16 keys,
-// VP: FP16 values), plus the unfinished block.  FP16-key scores use the FP64
-// chain with one rounding (the decision arithmetic of the rank check) and
-// give the FP16-side block estimate; values come from the staging area
-// (FP16) or tier 1 (INT4).  Output: one online-softmax partial per q head.
+// K4a (keys): FP16-key scores of the P blocks from the staging area [Meth-3
+// rank-consistency check], one wave per block, lane = token: FP64 fma chain
+// over c = 0 .. D-1 with one rounding to FP32 after the scale (the decision
+// arithmetic of the rank check), the block's FP16-side max and mass (64-leaf
+// tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
+// through uniform scalar loads.
 // ===========================================================================
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int *skip_seq) {
-    using M = VMap<D>;
+__global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
+                                                const double *qd) {
     const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l = St.layer;
     if (skip_seq[n]) return;
-    const int len = Ly.len[l * Ly.B + n];
-    const int N = len / 64, np = len % 64;
-    const int nslot = N + (np ? 1 : 0);
-    const int b0 = sp * St.bps, b1 = min(nslot, b0 + St.bps);
-    __shared__ double qd[D][G];
-    __shared__ float pw[4][G][64];
-    for (int i = threadIdx.x; i < G * D; i += 256)
-        qd[i % D][i / D] = (double)h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
+    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
+    const int N = len / 64;
+    const int b0 = sp * St.bps, b1 = min(N, b0 + St.bps);
+    constexpr uint32_t ALL = (1u << G) - 1u;
+    __shared__ uint32_t sbits[MAX_BPS];
+    const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
+    for (int i = threadIdx.x; i < b1 - b0; i += 256) sbits[i] = St.sel[selbase + b0 + i];
     __syncthreads();
-    const int cg = lane % M::LPR, rs = lane / M::LPR, c0 = cg * 8;
+    // q as [D][G] FP64, read through the constant address space (qd is not
+    // written during this kernel): the loads are scalar
+    typedef const __attribute__((address_space(4))) double cdouble;
+    const int qbase = __builtin_amdgcn_readfirstlane((n * Ly.Hkv + g) * D * G);
     const size_t NS64 = (size_t)St.NS * 64;
-    OnlineState<G> st;
-    st.init();
-    for (int b = b0 + wave; b < b1; b += 4) {
-        const bool part = b == N;
-        uint32_t pm = 0, vm = 0;
-        if (!part) {
-            const uint32_t bits = St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b];
-            pm = bits & ((1u << G) - 1u);
-            vm = (bits >> 8) & ((1u << G) - 1u);
-            if (!(pm | vm)) continue;
-        }
-        const uint32_t use = part ? ((1u << G) - 1u) : (pm | vm);
-        const uint32_t fp16v = part ? use : vm;
-        const size_t sblk = ((size_t)n * Ly.Hkv + g) * Ly.Nmax + b;
-        // FP16-key scores of the P heads (lane = token): FP64 fma chain over
-        // c = 0 .. D-1, one rounding to FP32 after the scale
-        float s16[G];
-        if (pm) {
-            const uint16_t *kb = St.stage_k + sblk * 64 * D;
-            double a[G];
+    auto pmask = [&](int b) { return __builtin_amdgcn_readfirstlane(sbits[b - b0]) & ALL; };
+    auto issue = [&](int b, uint32_t pm, uint4 (&kr)[D / 8]) {
+        if (!pm) return;
+        const uint16_t *kb = St.stage_k + (selbase + b) * 64 * D;
 #pragma unroll
-            for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
-#pragma unroll 2
-            for (int ch = 0; ch < D / 8; ++ch) {
-                const uint4 kv = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
-                float kf[8];
-                unpack_fp16x8(kv, kf);
+        for (int ch = 0; ch < D / 8; ++ch) kr[ch] = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
+    };
+    auto consume = [&](int b, uint32_t pm, const uint4 (&kr)[D / 8]) {
+        if (!pm) return;
+        int qoff = 0;
+        asm volatile("" : "+s"(qoff));  // opaque zero: keeps the q loads in the loop
+        cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(qbase + qoff);
+        double a[G];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const double kc = (double)kf[i];
+        for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
 #pragma unroll
-                    for (int jj = 0; jj < G; ++jj) a[jj] = fma(qd[ch * 8 + i][jj], kc, a[jj]);
-                }
+        for (int ch = 0; ch < D / 8; ++ch) {
+            float kf[8];
+            unpack_fp16x8(kr[ch], kf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double kc = (double)kf[i];
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) a[jj] = fma(qb[(ch * 8 + i) * G + jj], kc, a[jj]);
             }
+            // finish this chunk before the next chunk's q loads are issued
+            // (bounds the scalar registers holding q)
 #pragma unroll
-            for (int jj = 0; jj < G; ++jj) {
-                s16[jj] = (float)(a[jj] * (double)St.sm);
-                if (pm & (1u << jj)) {
-                    const float mx = wave_max_f32(s16[jj]);
-                    const float l_ = tree64_f32(exp_c(s16[jj] - mx));
-                    if (lane == 0) St.st16[((size_t)n * Ly.Hq + g * G + jj) * Ly.Nmax + b] = make_float2(mx, l_);
-                }
-            }
+            for (int jj = 0; jj < G; ++jj) asm volatile("" : "+v"(a[jj])::"memory");
         }
-        const bool valid = !part || lane < np;
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
-            if (!(use & (1u << jj))) {
-                pw[wave][jj][lane] = 0.0f;
-                continue;
-            }
-            const float s = (pm & (1u << jj)) ? s16[jj]
-                            : St.score[(size_t)(n * Ly.Hq + g * G + jj) * NS64 + (size_t)b * 64 + lane];
-            st.weights(jj, s, valid, pw[wave][jj], lane);
+            if (!(pm & (1u << jj))) continue;
+            const int h = g * G + jj;
+            const float s = (float)(a[jj] * (double)St.sm);
+            St.score16[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane] = s;
+            const float mx = wave_max_dpp(s);
+            const float l_ = tree64_f32_dpp(exp_c(s - mx));
+            if (lane == 0) St.st16[((size_t)n * Ly.Hq + h) * Ly.Nmax + b] = make_float2(mx, l_);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // FP16 values (VP heads, unfinished block)
-        if (fp16v) {
-            const uint16_t *vrow = part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + sblk * 64 * D;
-#pragma unroll 4
-            for (int i = 0; i < M::TPL; ++i) {
-                const int t = i * M::RPI + rs;
-                float vf[8];
-                unpack_fp16x8(*reinterpret_cast<const uint4 *>(vrow + t * D + c0), vf);
-#pragma unroll
-                for (int jj = 0; jj < G; ++jj) {
-                    if (!(fp16v & (1u << jj))) continue;
-                    const float p = pw[wave][jj][t];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, vf[c], st.acc[jj][c]);
-                }
-            }
-        }
-        // INT4 values (P heads without FP16 values)
-        const uint32_t int4v = use & ~fp16v;
-        if (int4v) {
-            const size_t bi = Ly.blk(l, n, g, b);
-            const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
-            const uint32_t *vmt = Ly.vmeta + bi * 64 * (D / 32);
-#pragma unroll 4
-            for (int i = 0; i < M::TPL; ++i) {
-                const int t = i * M::RPI + rs;
-                float vf[8];
-                unpack_int4x8(*reinterpret_cast<const uint32_t *>(vq + t * (D / 2) + c0 / 2),
-                              vmt[t * (D / 32) + c0 / 32], vf);
-#pragma unroll
-                for (int jj = 0; jj < G; ++jj) {
-                    if (!(int4v & (1u << jj))) continue;
-                    const float p = pw[wave][jj][t];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, vf[c], st.acc[jj][c]);
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // two blocks in flight per wave
+    uint4 k0[D / 8], k1[D / 8];
+    uint32_t p0 = 0, p1 = 0;
+    int b = b0 + wave;
+    if (b < b1) {
+        p0 = pmask(b);
+        issue(b, p0, k0);
     }
-    write_partials<D, G>(st, St.part_blk, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp,
-                         (1u << G) - 1u);
+    for (; b < b1; b += 8) {
+        const bool more = b + 4 < b1;
+        if (more) {
+            p1 = pmask(b + 4);
+            issue(b + 4, p1, k1);
+        }
+        consume(b, p0, k0);
+        if (!more) break;
+        if (b + 8 < b1) {
+            p0 = pmask(b + 8);
+            issue(b + 8, p0, k0);
+        }
+        consume(b + 4, p1, k1);
+    }
 }
 
 // ===========================================================================
@@ -866,7 +1119,7 @@ __global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int 
 // INT8 order; inconsistent iff D > floor(rank_tol * K*(K*-1)/2).
 // ===========================================================================
 constexpr int RANK_LDS = 2048;
-constexpr int MERGE_T = 256;
+constexpr int MERGE_T = 1024;
 
 // Number of elements of the descending run r[0..n) greater than x
 // (keys are unique).
@@ -942,7 +1195,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     const int wave = tid >> 6, lane = tid & 63;
     const int g = h / G, j = h % G, l = St.layer;
     if (skip_seq[n]) return;
-    const int len = Ly.len[l * Ly.B + n];
+    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, np = len % 64;
     const size_t hs = (size_t)n * Ly.Hq + h;
     const uint32_t *sel = St.sel + ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
@@ -1100,29 +1353,31 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
 // K5: exact attention on FP16 blocks (rungs 3 / 4 [Meth-1 fallback, Meth-3]
 // and the dense comparator).  Blocks of (seq, kv head) are at
 // kbase + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
-// token-major); `nfull[n]` full blocks, then an optional unfinished block.
+// channel-major); `nfull[n]` full blocks, then an optional unfinished block.
+// Scores in FP32 on the vector units, values on the matrix cores.
 // ===========================================================================
-
-
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
-    using M = VMap<D>;
+    using VA = VAcc<D, G>;
     const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave index as a uniform value: the block loops below branch uniformly
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
     if (!mask) return;
-    const int len = S.len[n];
+    const int len = __builtin_amdgcn_readfirstlane(S.len[n]);
     const int N = len / 64, np = len % 64;
     const int nslot = N + (np ? 1 : 0);
     const int b0 = sp * S.bps, b1 = min(nslot, b0 + S.bps);
     __shared__ float qs[G][D];
-    __shared__ float pw[4][G][64];
+    __shared__ __attribute__((aligned(16))) float pw[4][G][64];
+    __shared__ float scl[4][G];
+    __shared__ float ksg[VA::NG];
     for (int i = threadIdx.x; i < G * D; i += 256)
         qs[i / D][i % D] = h2f(S.q[((size_t)n * S.Hq + g * G + i / D) * D + (i % D)]);
+    if (threadIdx.x < VA::NG) ksg[threadIdx.x] = 0x1p14f;  // FP16 values only: p K <= 2^14
     __syncthreads();
-    const int cg = lane % M::LPR, rs = lane / M::LPR, c0 = cg * 8;
-    OnlineState<G> st;
-    st.init();
+    VA va;
+    va.init();
     for (int b = b0 + wave; b < b1; b += 4) {
         const bool part = b == N;
         const uint16_t *kb, *vb;
@@ -1133,46 +1388,38 @@ __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
             kb = S.k + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
             vb = S.v + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
         }
-        uint4 v16[M::TPL], kv[D / 8];
-#pragma unroll
-        for (int i = 0; i < M::TPL; ++i) v16[i] = *reinterpret_cast<const uint4 *>(vb + (i * M::RPI + rs) * D + c0);
+        uint4 kv[D / 8];
 #pragma unroll
         for (int ch = 0; ch < D / 8; ++ch) kv[ch] = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
+        uint4 vv[VA::NT][2];
         const bool valid = !part || lane < np;
+        // opaque zero offset: keeps the q reads inside the loop
+        int qoff = 0;
+        asm volatile("" : "+s"(qoff));
+        const float *qsp = &qs[0][0] + qoff;
         float a[G];
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) a[jj] = 0.0f;
 #pragma unroll
         for (int ch = 0; ch < D / 8; ++ch) {
+            if (ch == D / 16) load_fp16v<D>(vb, lane, vv);  // values halfway through the keys
             float kf[8];
             unpack_fp16x8(kv[ch], kf);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int jj = 0; jj < G; ++jj) a[jj] = fmaf(qs[jj][ch * 8 + i], kf[i], a[jj]);
+                for (int jj = 0; jj < G; ++jj) a[jj] = fmaf(qsp[jj * D + ch * 8 + i], kf[i], a[jj]);
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj) asm volatile("" : "+v"(a[jj])::"memory");
         }
 #pragma unroll
-        for (int jj = 0; jj < G; ++jj) st.weights(jj, a[jj] * S.sm, valid, pw[wave][jj], lane);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int i = 0; i < M::TPL; ++i) {
-            const int t = i * M::RPI + rs;
-            float vf[8];
-            unpack_fp16x8(v16[i], vf);
-#pragma unroll
-            for (int jj = 0; jj < G; ++jj) {
-                const float p = pw[wave][jj][t];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) st.acc[jj][c] = fmaf(p, vf[c], st.acc[jj][c]);
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int jj = 0; jj < G; ++jj) a[jj] *= S.sm;
+        va.softmax(mask, a, valid, &pw[wave][0][0], scl[wave], lane);
+        wave_sync();
+        va.fp16_block(mask, &pw[wave][0][0], vv, ksg, lane);
+        wave_sync();
     }
-    write_partials<D, G>(st, S.part, (size_t)n * S.Hq + g * G, S.nsplit_cap, sp, mask);
+    write_partials<D, G>(va, ksg, S.part, (size_t)n * S.Hq + g * G, S.nsplit_cap, sp, mask);
 }
 
 template <int D, int G>
@@ -1182,7 +1429,7 @@ __global__ __launch_bounds__(64) void k_merge_dense(DenseSrc S) {
     const int g = h / G, j = h % G;
     const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
     if (!(mask & (1u << j))) return;
-    const int len = S.len[n];
+    const int len = __builtin_amdgcn_readfirstlane(S.len[n]);
     const int nslot = len / 64 + ((len % 64) ? 1 : 0);
     const int nsp = (nslot + S.bps - 1) / S.bps;
     const float *pt = S.part + (size_t)(n * S.Hq + h) * S.nsplit_cap * (D + 2);
@@ -1225,6 +1472,17 @@ hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         hipLaunchKernelGGL((k_tail<decltype(D)::value, decltype(G)::value>),
                            dim3(St.nsplit, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        const int nsp = (St.nb + St.bps - 1) / St.bps;
+        if (nsp == 0) return hipSuccess;
+        hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>),
+                           dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq,
+                           (const double *)St.qd);
         return hipGetLastError();
     });
 }

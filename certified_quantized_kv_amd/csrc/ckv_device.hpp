@@ -219,4 +219,39 @@ __device__ __forceinline__ int row_sum_i32(int v) {
     return v;
 }
 
+__device__ __forceinline__ float row_sum_f32(float v) {
+    v = v + dpp_f32<DPP_QP_1032>(v);
+    v = v + dpp_f32<DPP_QP_2301>(v);
+    v = v + dpp_f32<DPP_ROW_HALF_MIRROR>(v);
+    v = v + dpp_f32<DPP_ROW_MIRROR>(v);
+    return v;
+}
+
+// Wave-wide max / sum: DPP inside the rows, then the four row results read
+// as scalars.  Every lane gets the result.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = row_max_f32(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = row_sum_f32(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// The halving tree over 64 lanes (strides 32, 16 across rows, then 8..1
+// inside row 0); the result is in lane 0.  Same pairing as tree64_f32.
+__device__ __forceinline__ float tree64_f32_dpp(float v) {
+    v = v + __shfl_down(v, 32, 64);
+    v = v + __shfl_down(v, 16, 64);
+    return row_tree_f32(v);
+}
+
 }  // namespace ckv

@@ -6,13 +6,16 @@
 //                              load per lane covers 16 channels of one token
 //                              and a wave's load covers 1 KiB contiguous
 //   kmeta u32 [d]              binary16 scale | binary16 offset << 16
-//   vq    u8  [64][d/2]        INT4 value codes, low nibble = even channel
-//   vmeta u32 [64][d/32]       binary16 scale | binary16 offset << 16
+//   vq    u8  [d][32]          INT4 value codes, channel-major: byte
+//                              c * 32 + t / 2, low nibble = even token t
+//   vmeta u32 [d/32][64]       per (group, token): binary16 scale |
+//                              binary16 offset << 16
 //   eta   f32                  value-error annotation of the block
-// Unfinished block (device, FP16): kpart [d/8][64][8], vpart [64][d].
+// Unfinished block (device, FP16): kpart [d/8][64][8], vpart [d][64].
 // Tier 2 (pinned host) and the device staging area hold FP16 blocks in the
 // same per-block layout: K [d/8][64][8] (one 16-byte load = 8 channels of a
-// token), V [64][d].
+// token), V [d][64] (channel-major: a 16-byte load = 8 tokens of a channel,
+// the k-operand order of the value contraction).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,6 +30,7 @@ struct Layout {
     uint32_t *vmeta;
     float *eta;
     uint32_t *vmin, *vmax;  // [L][B][Hkv][d] order-preserving encodings of FP32
+    float *vscale;          // [L][B][Hkv][d/32] power-of-two weight scale per value group
     uint16_t *kpart, *vpart;
     int *len;               // [L][B] tokens per sequence (device mirror)
 
@@ -70,7 +74,8 @@ struct Step {
     int nsplit, bps;        // tail splits per (seq, kv head), blocks per split
     float sm;
     const uint16_t *q;      // [batch][Hq][d]
-    float *score;           // [B][Hq][NS*64]
+    float *score;           // [B][Hq][NS*64]  INT8 scores (unfinished block: FP16)
+    float *score16;         // [B][Hq][NS*64]  FP16-key scores on P
     float4 *bstat;          // [B][Hq][NS]  max, l, Delta, rho
     uint64_t *mfx;          // [B][Hq][NS]
     uint64_t *cval;         // [B][Hq][NS]  E_val contribution per block
@@ -82,12 +87,13 @@ struct Step {
     float *part_blk;        // [B][Hq][NS][d+2]
     int nsplit_cap;
     const uint16_t *stage_k, *stage_v;  // [B][Hkv][Nmax][64*d]
+    double *qd;             // [B][Hkv][d][G] q in FP64 (written by the scoring pass)
     float *out;             // [batch][Hq][d]
 };
 
 // Source of an exact dense attention: FP16 blocks of (seq n, kv head g) at
 // k + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
-// token-major), len[n] tokens, the unfinished block (if any) at
+// channel-major), len[n] tokens, the unfinished block (if any) at
 // kp / vp + (n * Hkv + g) * 64 * D.
 struct DenseSrc {
     const uint16_t *k, *v;
@@ -122,6 +128,7 @@ hipError_t launch_vrange(const Layout &Ly, int l, int n, const uint16_t *vin, in
 hipError_t launch_score(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStream_t s);
 hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s);
+hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq,
                            hipStream_t s);
 hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, const int *skip_seq,

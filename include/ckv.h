@@ -133,7 +133,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
  * "fast dense path" the certified step is compared with [Results].
  * k, v: device binary16 in the block layout
  *   [batch][n_kv_heads][n_tokens/64][64 * head_dim], where a K block is
- *   [head_dim/8][64 tokens][8 channels] and a V block [64 tokens][head_dim];
+ *   [head_dim/8][64 tokens][8 channels] and a V block [head_dim][64 tokens];
  * n_tokens: a multiple of 64, at most the cache's max_context;
  * q: device [batch][n_q_heads][head_dim] binary16; out: device FP32
  * [batch][n_q_heads][head_dim].  Uses the cache's shape (heads, head_dim)
@@ -188,13 +188,14 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
  * it).  Phase times are measured with HIP events on the streams the work
  * runs on: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
  * 3 page-in (the host-to-device copies on the side stream), 4 promoted
- * pass (K4a), 5 fallback (paging + dense recompute), 6 the whole step on
- * the host wall clock, 7 rank check + merge (K4b).  Block counts are what the
+ * value pass (K4a), 5 fallback (paging + dense recompute), 6 the whole step
+ * on the host wall clock, 7 rank check + merge (K4b), 8 FP16-key scoring of
+ * the promoted blocks (K4a keys).  Block counts are what the
  * passes read, summed over steps: a block is one (sequence, kv head, 64
  * tokens).  Profiling adds a few event records per step. */
 typedef struct {
-    double ms[8];           /* accumulated milliseconds per phase            */
-    int counts[8];          /* timed occurrences per phase                   */
+    double ms[9];           /* accumulated milliseconds per phase            */
+    int counts[9];          /* timed occurrences per phase                   */
     int steps;              /* decode steps profiled                         */
     uint64_t bytes_paged;   /* tier 2 -> staging bytes (with filled gaps)    */
     uint64_t copies;        /* host-to-device copies issued                  */

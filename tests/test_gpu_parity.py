@@ -277,10 +277,11 @@ def test_needle_128k_sampled_kv_head():
 # -- the dense comparator and error paths ---------------------------------------
 
 def to_blocks(k, v):
-    """[B][T][Hkv][d] -> block layout [B][Hkv][T/64][...] (K chunk-interleaved)."""
+    """[B][T][Hkv][d] -> block layout [B][Hkv][T/64][...] (K chunk-interleaved,
+    V channel-major)."""
     B, T, Hkv, d = k.shape
     kb = k.reshape(B, T // 64, 64, Hkv, d // 8, 8).transpose(0, 3, 1, 4, 2, 5).copy()
-    vb = v.reshape(B, T // 64, 64, Hkv, d).transpose(0, 3, 1, 2, 4).copy()
+    vb = v.reshape(B, T // 64, 64, Hkv, d).transpose(0, 3, 1, 4, 2).copy()
     return kb, vb
 
 
