@@ -142,11 +142,21 @@ void fill_failed_reports(ckv_head_report *r, int n) {
 
 // Blocks per split of the value passes: a multiple of 4 (one block per wave
 // of a 256-thread workgroup), about 1024 workgroups per launch.
+// Blocks per split of the value passes: about 704 four-wave workgroups, so
+// that the grid is resident in one round at three waves per SIMD (256 CUs x
+// 4 SIMDs x 3 = 3072 waves); a multiple of 4 in [4, 64].
 int split_blocks(int nb, int Hkv, int batch) {
     const long units = (long)nb * Hkv * batch;
-    int bps = (int)((units + 1023) / 1024);
+    int bps = (int)((units + 703) / 704);
     bps = std::max(4, std::min(64, (bps + 3) / 4 * 4));
     return bps;
+}
+
+// Block slots per wave of the scoring pass (one-wave workgroups): about
+// 2816 waves, at least 2 slots so that one block's loads overlap the other.
+int score_slots(int nb, int Hkv, int batch) {
+    const long units = (long)(nb + 1) * Hkv * batch;
+    return (int)std::max(2L, std::min(64L, (units + 2815) / 2816));
 }
 
 float ru32h(double x) {
@@ -463,6 +473,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.nb = nb;
     St.NS = c->NS;
     St.bps = split_blocks(nb, Hkv, batch);
+    St.spw = score_slots(nb, Hkv, batch);
     St.nsplit = (nb + St.bps - 1) / St.bps;
     St.nsplit_cap = c->nsplit_cap;
     St.sm = th->sm_scale;

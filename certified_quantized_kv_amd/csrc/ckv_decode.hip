@@ -54,7 +54,7 @@ static hipError_t dispatch(int d, int G, F f) {
 //   Delta = sm (kappa H + E_w + (2^-20 + 2^-23) A + 2^-23 E_w) (1 + 2^-20),
 //   rho = sm 2^-23 A (1 + 2^-20), E_w = 2^(e-21) 255 d,
 // with H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c) as FP64 trees.
-// One wave per (slot, kv head, sequence).
+// One wave per St.spw consecutive block slots of a (kv head, sequence).
 // ===========================================================================
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -63,26 +63,48 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
     constexpr int CPL = D / 64;           // channels per lane (meta, trees)
     constexpr int KS = D / 64;            // MFMA k-steps of 64 channels
     constexpr int RT = (4 * G + 15) / 16; // MFMA row tiles of 4 heads x 4 digits
-    const int slot = blockIdx.x, g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+    constexpr int CPR = D / 16;           // channels per lane in the set-up rows
+    const int g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
     const int l = St.layer;
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, np = len % 64;
-    if (slot > N || (slot == N && np == 0)) return;
+    const int nslot = N + (np ? 1 : 0);
+    const int s0 = blockIdx.x * St.spw, s1 = min(nslot, s0 + St.spw);
+    if (s0 >= s1) return;
     __shared__ float qs[G][D];
     __shared__ __attribute__((aligned(16))) int8_t dig[G][4][D];
     __shared__ double hd_C[G];
     __shared__ int hd_e[G], hd_W[G];
     __shared__ float hd_dl[G], hd_rh[G];
+    const int i16 = lane % 16;
+    // operands of a full block: codes (MFMA B operands) and this lane's
+    // scale / offset words; requested one block ahead
+    auto issue = [&](int slot, v4i (&bq)[4][KS], uint32_t (&km)[CPR]) {
+        if (slot >= N) return;
+        const size_t bi = Ly.blk(l, n, g, slot);
+        const uint8_t *kb = Ly.kq + bi * 64 * D;
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                bq[tile][ks] = *reinterpret_cast<const v4i *>(kb + (ks * 4 + lane / 16) * 1024 +
+                                                              (tile * 16 + lane % 16) * 16);
+#pragma unroll
+        for (int k = 0; k < CPR; ++k) km[k] = Ly.kmeta[bi * D + i16 + 16 * k];
+    };
+    v4i bq0[4][KS], bq1[4][KS];
+    uint32_t km0[CPR], km1[CPR];
+    issue(s0, bq0, km0);
     for (int i = lane; i < G * D; i += 64)
         qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
-    if (slot == 0)  // q in FP64, [D][G] per (seq, kv head), for the promoted pass
+    if (s0 == 0)  // q in FP64, [D][G] per (seq, kv head), for the FP16-key pass
         for (int i = lane; i < G * D; i += 64)
             St.qd[((size_t)n * Ly.Hkv + g) * D * G + i] = (double)qs[i % G][i / G];
     const float sm = St.sm;
     const size_t NS64 = (size_t)St.NS * 64;
 
-    if (slot == N) {
+    auto partial = [&](int slot) {
         // unfinished block: FP16 keys on the device, FP64 chain, one rounding
         const uint16_t *kp = Ly.kpart + Ly.seqg(l, n, g) * 64 * D;
         const bool valid = lane < np;
@@ -98,6 +120,9 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
 #pragma unroll
                 for (int j = 0; j < G; ++j) a[j] = fma((double)qs[j][ch * 8 + i], kc, a[j]);
             }
+            // one chunk at a time (bounds the registers holding q)
+#pragma unroll
+            for (int j = 0; j < G; ++j) asm volatile("" : "+v"(a[j])::"memory");
         }
         // rho of the unfinished block: A = sum |q_c| max_t |k_tc|
         double kmax[CPL];
@@ -126,148 +151,150 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                 St.bstat[(size_t)(n * Ly.Hq + h) * St.NS + slot] = make_float4(mx, l_, r, r);
             }
         }
-        return;
-    }
+    };
 
-    // full block: code loads first, they are in flight during the set-up
-    const size_t bi = Ly.blk(l, n, g, slot);
-    const uint8_t *kb = Ly.kq + bi * 64 * D;
-    v4i bq[4][KS];
-#pragma unroll
-    for (int tile = 0; tile < 4; ++tile)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            bq[tile][ks] = *reinterpret_cast<const v4i *>(kb + (ks * 4 + lane / 16) * 1024 +
-                                                          (tile * 16 + lane % 16) * 16);
-    if (lane == 0) St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot] = 0u;
-    // set-up per head: row r of the wave takes head r (+4 on a second pass);
-    // lane i of the row holds channels c = i + 16 k, k < D/16, so the
-    // halving tree over the channels runs in-lane for strides >= 16 and
-    // across the row (DPP) for strides 8..1.
-    constexpr int CPR = D / 16;
-    const int r = lane / 16, i16 = lane % 16;
-    float sc[CPR], zc[CPR];
-#pragma unroll
-    for (int k = 0; k < CPR; ++k) {
-        const uint32_t m = Ly.kmeta[bi * D + i16 + 16 * k];
-        sc[k] = h2f((uint16_t)(m & 0xFFFFu));
-        zc[k] = h2f((uint16_t)(m >> 16));
-    }
-    const double kappa = 0.5 + 0x1p-14;
-#pragma unroll
-    for (int pass = 0; pass < (G + 3) / 4; ++pass) {
-        const int j = pass * 4 + r;
-        if (j < G) {
-            float w[CPR], cz[CPR];
-            double hv[CPR], av[CPR];
-            float wm = 0.0f;
-#pragma unroll
-            for (int k = 0; k < CPR; ++k) {
-                const float q = qs[j][i16 + 16 * k];
-                w[k] = q * sc[k];
-                cz[k] = q * zc[k];
-                hv[k] = fabs((double)q) * (double)sc[k];
-                av[k] = fabs((double)q) * (fabs((double)zc[k]) + 255.0 * (double)sc[k]);
-                wm = fmaxf(wm, fabsf(w[k]));
-            }
-            // in-lane tree levels (channel strides D/2 .. 16)
-#pragma unroll
-            for (int st = CPR / 2; st >= 1; st >>= 1)
-#pragma unroll
-                for (int k = 0; k < st; ++k) {
-                    cz[k] = cz[k] + cz[k + st];
-                    hv[k] = hv[k] + hv[k + st];
-                    av[k] = av[k] + av[k + st];
+    auto full = [&](int slot, const v4i (&bq)[4][KS], const uint32_t (&km)[CPR]) {
+        // the previous block's reads of dig / hd_* are complete
+        __syncthreads();
+        if (lane == 0) St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot] = 0u;
+        // set-up per head: row r of the wave takes head r (+4 on a second pass);
+        // lane i of the row holds channels c = i + 16 k, k < D/16, so the
+        // halving tree over the channels runs in-lane for strides >= 16 and
+        // across the row (DPP) for strides 8..1.
+        const int r = lane / 16;
+        float sc[CPR], zc[CPR];
+    #pragma unroll
+        for (int k = 0; k < CPR; ++k) {
+            sc[k] = h2f((uint16_t)(km[k] & 0xFFFFu));
+            zc[k] = h2f((uint16_t)(km[k] >> 16));
+        }
+        const double kappa = 0.5 + 0x1p-14;
+    #pragma unroll
+        for (int pass = 0; pass < (G + 3) / 4; ++pass) {
+            const int j = pass * 4 + r;
+            if (j < G) {
+                float w[CPR], cz[CPR];
+                double hv[CPR], av[CPR];
+                float wm = 0.0f;
+    #pragma unroll
+                for (int k = 0; k < CPR; ++k) {
+                    const float q = qs[j][i16 + 16 * k];
+                    w[k] = q * sc[k];
+                    cz[k] = q * zc[k];
+                    hv[k] = fabs((double)q) * (double)sc[k];
+                    av[k] = fabs((double)q) * (fabs((double)zc[k]) + 255.0 * (double)sc[k]);
+                    wm = fmaxf(wm, fabsf(w[k]));
                 }
-            const float C = row_tree_f32(cz[0]);
-            const double H = row_tree_f64(hv[0]);
-            const double A = row_tree_f64(av[0]);
-            wm = row_max_f32(wm);
-            const bool nz = wm > 0.0f;
-            const int e = nz ? (int)((__float_as_uint(wm) >> 23) & 0xFFu) - 127 : 0;
-            int wsum = 0;
-#pragma unroll
-            for (int k = 0; k < CPR; ++k) {
-                const int wt = nz ? (int)rintf(ldexpf(w[k], 20 - e)) : 0;
-                wsum += wt;
-                const int d0 = ((wt + 128) & 255) - 128;
-                const int r1 = (wt - d0) >> 8;
-                const int d1 = ((r1 + 128) & 255) - 128;
-                const int d2 = (r1 - d1) >> 8;
-                const int c = i16 + 16 * k;
-                dig[j][0][c] = (int8_t)d0;
-                dig[j][1][c] = (int8_t)d1;
-                dig[j][2][c] = (int8_t)d2;
-                dig[j][3][c] = 0;
-            }
-            wsum = row_sum_i32(wsum);
-            if (i16 == 0) {
-                const double Ew = nz ? ldexp(255.0 * (double)D, e - 21) : 0.0;
-                double dl = kappa * H + Ew;
-                dl = dl + A * (0x1p-20 + 0x1p-23);
-                dl = dl + Ew * 0x1p-23;
-                dl = dl * (double)sm;
-                dl = dl * (1.0 + 0x1p-20);
-                double rh = A * 0x1p-23;
-                rh = rh * (double)sm;
-                rh = rh * (1.0 + 0x1p-20);
-                hd_C[j] = (double)C;
-                hd_e[j] = e;
-                hd_W[j] = wsum;
-                hd_dl[j] = ru32(dl);
-                hd_rh[j] = ru32(rh);
+                // in-lane tree levels (channel strides D/2 .. 16)
+    #pragma unroll
+                for (int st = CPR / 2; st >= 1; st >>= 1)
+    #pragma unroll
+                    for (int k = 0; k < st; ++k) {
+                        cz[k] = cz[k] + cz[k + st];
+                        hv[k] = hv[k] + hv[k + st];
+                        av[k] = av[k] + av[k + st];
+                    }
+                const float C = row_tree_f32(cz[0]);
+                const double H = row_tree_f64(hv[0]);
+                const double A = row_tree_f64(av[0]);
+                wm = row_max_f32(wm);
+                const bool nz = wm > 0.0f;
+                const int e = nz ? (int)((__float_as_uint(wm) >> 23) & 0xFFu) - 127 : 0;
+                int wsum = 0;
+    #pragma unroll
+                for (int k = 0; k < CPR; ++k) {
+                    const int wt = nz ? (int)rintf(ldexpf(w[k], 20 - e)) : 0;
+                    wsum += wt;
+                    const int d0 = ((wt + 128) & 255) - 128;
+                    const int r1 = (wt - d0) >> 8;
+                    const int d1 = ((r1 + 128) & 255) - 128;
+                    const int d2 = (r1 - d1) >> 8;
+                    const int c = i16 + 16 * k;
+                    dig[j][0][c] = (int8_t)d0;
+                    dig[j][1][c] = (int8_t)d1;
+                    dig[j][2][c] = (int8_t)d2;
+                    dig[j][3][c] = 0;
+                }
+                wsum = row_sum_i32(wsum);
+                if (i16 == 0) {
+                    const double Ew = nz ? ldexp(255.0 * (double)D, e - 21) : 0.0;
+                    double dl = kappa * H + Ew;
+                    dl = dl + A * (0x1p-20 + 0x1p-23);
+                    dl = dl + Ew * 0x1p-23;
+                    dl = dl * (double)sm;
+                    dl = dl * (1.0 + 0x1p-20);
+                    double rh = A * 0x1p-23;
+                    rh = rh * (double)sm;
+                    rh = rh * (1.0 + 0x1p-20);
+                    hd_C[j] = (double)C;
+                    hd_e[j] = e;
+                    hd_W[j] = wsum;
+                    hd_dl[j] = ru32(dl);
+                    hd_rh[j] = ru32(rh);
+                }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // matrix cores: rows = (head, digit), columns = tokens, k = channels
-    const int row = lane % 16, hrow = row / 4, drow = row % 4;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int ha = rt * 4 + hrow;  // head of this lane's A row
-        v4i a[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ha < G)
-                a[ks] = *reinterpret_cast<const v4i *>(&dig[ha][drow][ks * 64 + (lane / 16) * 16]);
-            else
-                a[ks] = v4i{0, 0, 0, 0};
-        }
-        const int hh = rt * 4 + lane / 16;  // head of this lane's output rows
-        float sv[4];
-#pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            v4i acc = {0, 0, 0, 0};
-#pragma unroll
+        // matrix cores: rows = (head, digit), columns = tokens, k = channels
+        const int row = lane % 16, hrow = row / 4, drow = row % 4;
+    #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int ha = rt * 4 + hrow;  // head of this lane's A row
+            v4i a[KS];
+    #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const v4i b = bq[tile][ks] ^ v4i{(int)0x80808080, (int)0x80808080, (int)0x80808080,
-                                                  (int)0x80808080};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], b, acc, 0, 0, 0);
+                if (ha < G)
+                    a[ks] = *reinterpret_cast<const v4i *>(&dig[ha][drow][ks * 64 + (lane / 16) * 16]);
+                else
+                    a[ks] = v4i{0, 0, 0, 0};
             }
-            sv[tile] = 0.0f;
-            if (hh < G) {
-                const long long S = ((long long)acc[2] << 16) + ((long long)acc[1] << 8) + (long long)acc[0] +
-                                    128ll * (long long)hd_W[hh];
-                const double x = hd_C[hh] + ldexp((double)S, hd_e[hh] - 20);
-                sv[tile] = (float)(x * (double)sm);
-                St.score[(size_t)(n * Ly.Hq + g * G + hh) * NS64 + (size_t)slot * 64 + tile * 16 + row] =
-                    sv[tile];
+            const int hh = rt * 4 + lane / 16;  // head of this lane's output rows
+            float sv[4];
+    #pragma unroll
+            for (int tile = 0; tile < 4; ++tile) {
+                v4i acc = {0, 0, 0, 0};
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const v4i b = bq[tile][ks] ^ v4i{(int)0x80808080, (int)0x80808080, (int)0x80808080,
+                                                      (int)0x80808080};
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], b, acc, 0, 0, 0);
+                }
+                sv[tile] = 0.0f;
+                if (hh < G) {
+                    const long long S = ((long long)acc[2] << 16) + ((long long)acc[1] << 8) + (long long)acc[0] +
+                                        128ll * (long long)hd_W[hh];
+                    const double x = hd_C[hh] + ldexp((double)S, hd_e[hh] - 20);
+                    sv[tile] = (float)(x * (double)sm);
+                    St.score[(size_t)(n * Ly.Hq + g * G + hh) * NS64 + (size_t)slot * 64 + tile * 16 + row] =
+                        sv[tile];
+                }
             }
+            // block estimate of head hh: tokens tile*16 + row live in the 16
+            // lanes of the group; the halving tree over the 64 tokens is the
+            // in-lane steps of stride 32 and 16, then strides 8..1 across lanes
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = row_max_f32(mx);
+            float e4[4];
+    #pragma unroll
+            for (int tile = 0; tile < 4; ++tile) e4[tile] = exp_c(sv[tile] - mx);
+            const float u0 = e4[0] + e4[2], u1 = e4[1] + e4[3];
+            const float v = row_tree_f32(u0 + u1);
+            if (hh < G && row == 0)
+                St.bstat[(size_t)(n * Ly.Hq + g * G + hh) * St.NS + slot] = make_float4(mx, v, hd_dl[hh], hd_rh[hh]);
         }
-        // block estimate of head hh: tokens tile*16 + row live in the 16
-        // lanes of the group; the halving tree over the 64 tokens is the
-        // in-lane steps of stride 32 and 16, then strides 8..1 across lanes
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mx = row_max_f32(mx);
-        float e4[4];
-#pragma unroll
-        for (int tile = 0; tile < 4; ++tile) e4[tile] = exp_c(sv[tile] - mx);
-        const float u0 = e4[0] + e4[2], u1 = e4[1] + e4[3];
-        const float v = row_tree_f32(u0 + u1);
-        if (hh < G && row == 0)
-            St.bstat[(size_t)(n * Ly.Hq + g * G + hh) * St.NS + slot] = make_float4(mx, v, hd_dl[hh], hd_rh[hh]);
+    };
+    // full blocks s0 .. f1-1, the next block's operands in flight during the
+    // current one; then the unfinished block, if it is in this range
+    const int f1 = min(s1, N);
+    for (int slot = s0; slot < f1; slot += 2) {
+        if (slot + 1 < f1) issue(slot + 1, bq1, km1);
+        full(slot, bq0, km0);
+        if (slot + 1 >= f1) break;
+        if (slot + 2 < f1) issue(slot + 2, bq0, km0);
+        full(slot + 1, bq1, km1);
     }
+    if (s1 > N) partial(N);
 }
 
 // ===========================================================================
@@ -1059,23 +1086,38 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
         int qoff = 0;
         asm volatile("" : "+s"(qoff));  // opaque zero: keeps the q loads in the loop
         cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(qbase + qoff);
+        // q in groups of 16 doubles (CS channels x G heads, two scalar loads);
+        // the next group is requested before the current one is used
+        constexpr int QN = 16, CS = QN / G, NQ = D / CS;
+        double qc[QN], qn[QN];
+#pragma unroll
+        for (int i = 0; i < QN; ++i) qc[i] = qb[i];
         double a[G];
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
+        float kf[8];
 #pragma unroll
-        for (int ch = 0; ch < D / 8; ++ch) {
-            float kf[8];
-            unpack_fp16x8(kr[ch], kf);
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (qi + 1 < NQ)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const double kc = (double)kf[i];
-#pragma unroll
-                for (int jj = 0; jj < G; ++jj) a[jj] = fma(qb[(ch * 8 + i) * G + jj], kc, a[jj]);
-            }
-            // finish this chunk before the next chunk's q loads are issued
-            // (bounds the scalar registers holding q)
+                for (int i = 0; i < QN; ++i) qn[i] = qb[(qi + 1) * QN + i];
+            // the next group's loads are issued here, before this group's FMAs
 #pragma unroll
             for (int jj = 0; jj < G; ++jj) asm volatile("" : "+v"(a[jj])::"memory");
+#pragma unroll
+            for (int cc = 0; cc < CS; ++cc) {
+                const int c = qi * CS + cc;
+                if (c % 8 == 0) unpack_fp16x8(kr[c / 8], kf);
+                const double kc = (double)kf[c % 8];
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) a[jj] = fma(qc[cc * G + jj], kc, a[jj]);
+            }
+            // and the loads after them wait for these FMAs (bounds the
+            // scalar registers holding q)
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj) asm volatile("" : "+v"(a[jj])::"memory");
+#pragma unroll
+            for (int i = 0; i < QN; ++i) qc[i] = qn[i];
         }
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
@@ -1114,7 +1156,7 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
 
 // ===========================================================================
 // K4b: rank-consistency check [Meth-3] + merge of the partials -> output.
-// One wave per (q head, sequence).  Fixed-point FP16 masses M16 on P relative
+// One MERGE_T-thread workgroup per (q head, sequence).  Fixed-point FP16 masses M16 on P relative
 // to the largest FP16 block max of P; Kendall discordant pairs against the
 // INT8 order; inconsistent iff D > floor(rank_tol * K*(K*-1)/2).
 // ===========================================================================
@@ -1204,28 +1246,32 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     __shared__ long long red_ll[MERGE_T / 64];
     __shared__ float red_f[MERGE_T / 64];
     __shared__ float w_m[MERGE_T / 64], w_l[MERGE_T / 64], w_acc[MERGE_T / 64][D];
-    __shared__ int cnt_s;
 
-    // compact list of P blocks (ascending index), by wave 0
+    // compact list of P blocks (ascending index): one block per thread and
+    // round, per-wave counts combined through LDS
     const uint32_t bitP = 1u << j;
     uint32_t *plist = plist_g + hs * Ly.Nmax;
-    if (wave == 0) {
-        int K = 0;
-        for (int b0 = 0; b0 < N; b0 += 64) {
-            const int b = b0 + lane;
-            const bool inP = b < N && (sel[b] & bitP);
-            const uint64_t bal = __ballot(inP);
-            const int pos = K + __popcll(bal & ((1ull << lane) - 1ull));
-            if (inP) {
-                plist[pos] = (uint32_t)b;
-                if (pos < RANK_LDS) lds_list[pos] = (uint32_t)b;
-            }
-            K += __popcll(bal);
+    __shared__ int wcnt[MERGE_T / 64];
+    int K = 0;
+    for (int r0 = 0; r0 < N; r0 += MERGE_T) {
+        const int b = r0 + tid;
+        const bool inP = b < N && (sel[b] & bitP);
+        const uint64_t bal = __ballot(inP);
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = K, tot = 0;
+        for (int w = 0; w < MERGE_T / 64; ++w) {
+            off += w < wave ? wcnt[w] : 0;
+            tot += wcnt[w];
         }
-        if (lane == 0) cnt_s = K;
+        const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
+        if (inP) {
+            plist[pos] = (uint32_t)b;
+            if (pos < RANK_LDS) lds_list[pos] = (uint32_t)b;
+        }
+        K += tot;
+        __syncthreads();
     }
-    __syncthreads();
-    const int K = cnt_s;
     const bool use_lds = K <= RANK_LDS;
     const uint32_t *list = use_lds ? lds_list : plist;
     uint64_t *kI = use_lds ? lds_kI : keys_g + hs * 2 * Ly.Nmax;
@@ -1455,7 +1501,7 @@ __global__ __launch_bounds__(64) void k_merge_dense(DenseSrc S) {
 hipError_t launch_score(const Layout &Ly, const Step &St, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         hipLaunchKernelGGL((k_score<decltype(D)::value, decltype(G)::value>),
-                           dim3(St.nb + 1, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St);
+                           dim3((St.nb + 1 + St.spw - 1) / St.spw, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St);
         return hipGetLastError();
     });
 }
