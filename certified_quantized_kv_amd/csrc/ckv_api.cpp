@@ -61,7 +61,7 @@ struct ckv_cache {
     uint16_t *t2k = nullptr, *t2v = nullptr;
     // staging and scratch (device)
     uint16_t *stage_k = nullptr, *stage_v = nullptr;
-    float *score = nullptr, *score16 = nullptr, *part_tail = nullptr, *part_blk = nullptr;
+    float *score = nullptr, *score16 = nullptr, *part_tail = nullptr, *part_blk = nullptr, *part_blk16 = nullptr;
     double *qd = nullptr;
     float4 *bstat = nullptr;
     uint64_t *mfx = nullptr, *cval = nullptr, *m16 = nullptr, *keys = nullptr;
@@ -259,6 +259,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->m16, (size_t)B * Hq * Nmax));
     CTRY(dalloc(c, &c->part_tail, (size_t)B * Hq * c->nsplit_cap * (d + 2)));
     CTRY(dalloc(c, &c->part_blk, hsl * (d + 2)));
+    CTRY(dalloc(c, &c->part_blk16, hsl * (d + 2)));
     CTRY(dalloc(c, &c->qd, (size_t)B * Hq * d));
     CTRY(dalloc(c, &c->plist, (size_t)B * Hq * Nmax));
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
@@ -489,6 +490,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.m16 = c->m16;
     St.part_tail = c->part_tail;
     St.part_blk = c->part_blk;
+    St.part_blk16 = c->part_blk16;
     St.stage_k = c->stage_k;
     St.stage_v = c->stage_v;
     St.qd = c->qd;
@@ -741,7 +743,7 @@ ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int g, int b, uint
         std::vector<uint8_t> raw((size_t)64 * d);
         HIPCHK(hipMemcpy(raw.data(), Ly.kq + bi * 64 * d, raw.size(), hipMemcpyDeviceToHost));
         for (int t = 0; t < 64; ++t)
-            for (int ch = 0; ch < d; ++ch) k_code[t * d + ch] = raw[(ch / 16) * 1024 + t * 16 + ch % 16];
+            for (int ch = 0; ch < d; ++ch) k_code[t * d + ch] = raw[(ch / 16) * 1024 + t * 16 + ch % 16] ^ 0x80;
     }
     if (k_s || k_z) {
         std::vector<uint32_t> m(d);

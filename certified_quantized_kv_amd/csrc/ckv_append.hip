@@ -76,7 +76,9 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
         const float sf = h2f(sb);
         Ly.kmeta[blk * D + c] = (uint32_t)sb | ((uint32_t)zb << 16);
         uint8_t *kq = Ly.kq + blk * 64 * D + (c / 16) * 1024 + (c % 16);
-        for (int t = 0; t < 64; ++t) kq[t * 16] = (uint8_t)quant_code(h2f(col[t * 8]), lo, sf, 255.0f);
+        // stored as code - 128 (two's complement byte): the signed operand
+        // of the scoring pass's integer matrix product
+        for (int t = 0; t < 64; ++t) kq[t * 16] = (uint8_t)(quant_code(h2f(col[t * 8]), lo, sf, 255.0f) ^ 0x80);
     }
     // values: one thread per token; the codes are staged in LDS and packed
     // channel-major, two tokens per byte

@@ -48,7 +48,7 @@ static hipError_t dispatch(int d, int G, F f) {
 //   S_t = sum_c w~_c code_tc (exact), s^_t = fl32(fl64(C + S_t 2^(e-20)) sm),
 //   C = halving-tree FP32 sum of q_c z_c.
 // S_t is formed on the matrix cores: w~ = 2^16 d2 + 2^8 d1 + d0 with signed
-// byte digits, codes shifted to code - 128, one v_mfma_i32_16x16x64_i8 per
+// byte digits, codes stored as code - 128, one v_mfma_i32_16x16x64_i8 per
 // (16 tokens, 64 channels) with rows = (head, digit); int32 accumulation is
 // exact, so the result does not depend on the order of the sums.
 //   Delta = sm (kappa H + E_w + (2^-20 + 2^-23) A + 2^-23 E_w) (1 + 2^-20),
@@ -95,6 +95,7 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
     v4i bq0[4][KS], bq1[4][KS];
     uint32_t km0[CPR], km1[CPR];
     issue(s0, bq0, km0);
+    for (int i = lane; i < G * D; i += 64) dig[i / D][3][i % D] = 0;  // the unused digit row
     for (int i = lane; i < G * D; i += 64)
         qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
@@ -205,15 +206,14 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                 for (int k = 0; k < CPR; ++k) {
                     const int wt = nz ? (int)rintf(ldexpf(w[k], 20 - e)) : 0;
                     wsum += wt;
-                    const int d0 = ((wt + 128) & 255) - 128;
+                    const int d0 = (int8_t)wt;  // balanced base-256 digits
                     const int r1 = (wt - d0) >> 8;
-                    const int d1 = ((r1 + 128) & 255) - 128;
+                    const int d1 = (int8_t)r1;
                     const int d2 = (r1 - d1) >> 8;
                     const int c = i16 + 16 * k;
                     dig[j][0][c] = (int8_t)d0;
                     dig[j][1][c] = (int8_t)d1;
                     dig[j][2][c] = (int8_t)d2;
-                    dig[j][3][c] = 0;
                 }
                 wsum = row_sum_i32(wsum);
                 if (i16 == 0) {
@@ -256,15 +256,15 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                 v4i acc = {0, 0, 0, 0};
     #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const v4i b = bq[tile][ks] ^ v4i{(int)0x80808080, (int)0x80808080, (int)0x80808080,
-                                                      (int)0x80808080};
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], b, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], bq[tile][ks], acc, 0, 0, 0);
                 }
                 sv[tile] = 0.0f;
                 if (hh < G) {
-                    const long long S = ((long long)acc[2] << 16) + ((long long)acc[1] << 8) + (long long)acc[0] +
-                                        128ll * (long long)hd_W[hh];
-                    const double x = hd_C[hh] + ldexp((double)S, hd_e[hh] - 20);
+                    // S = 2^16 acc2 + 2^8 acc1 + acc0 + 128 W: an integer below 2^53
+                    // in magnitude, formed exactly in FP64
+                    const double S = fma((double)acc[2], 65536.0,
+                                         fma((double)acc[1], 256.0, (double)acc[0] + 128.0 * (double)hd_W[hh]));
+                    const double x = hd_C[hh] + ldexp(S, hd_e[hh] - 20);
                     sv[tile] = (float)(x * (double)sm);
                     St.score[(size_t)(n * Ly.Hq + g * G + hh) * NS64 + (size_t)slot * 64 + tile * 16 + row] =
                         sv[tile];
@@ -588,20 +588,29 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
 // (v_mfma_f32_16x16x32_f16; output path only, FP32 accumulation).
 //
 // Rows r = gv * G + h (value group gv of 32 channels, q head h), columns =
-// channels, k = tokens.  A row's weight for token t is a = p_t s_t K (INT4
-// codes; s_t the token's group scale) or a = p_t K (FP16 values), split into
-// FP16 hi + lo parts; K = 2^k is a per-group power of two that keeps every
-// a below 2^15 (from the running value range, which bounds every INT4 scale
-// of the group).  Lane l holds, for k-step ks, the tokens
+// channels, k = tokens.  Lane l holds, for k-step ks, 8 tokens of
 // 16 (l / 16) + 8 ks + (0 .. 7) of A row / B column l % 16; accumulator
 // tile (rt, nt) holds rows 16 rt + 4 (l / 16) + i, i < 4, of column
-// 16 nt + l % 16.  Only rows whose group is the column's group are kept;
-// the INT4 offsets enter through z-sums sum_t p_t z_t kept per A row.
+// 16 nt + l % 16.  Only rows whose group is the column's group are kept.
+//
+// The online softmax runs in the A layout: lane l holds the scores of the
+// row's head for its 16 tokens, so the weights never leave the registers.
+//
+// INT4 values: an INT4 code n taken as FP16 bits is the subnormal n 2^-24,
+// exact; masking a word of eight codes (token i at bits 4i) with 0x000F000F
+// gives tokens (0, 4), with 0x00F000F0 tokens (1, 5) as 16 n 2^-24, and the
+// same on the word shifted by 8 gives (2, 6), (3, 7).  The A weight is
+// a = p s K (the odd registers a / 16), K = 2^k a per-group power of two
+// that keeps a below 2^15 (from the running value range, which bounds every
+// INT4 scale of the group); acc then holds sum p s n K 2^-24, and the
+// offsets enter through z-sums sum_t p_t z_t kept per A row.
+// FP16 values: B is the value itself and a = p K16, K16 = 2^14, in acc16.
+// Weights are split into FP16 hi + lo parts (relative error <= 2^-20 above
+// 2^-14, absolute <= 2^-24 below).
 // A workgroup has four waves on four blocks; their states are combined
 // through LDS at the end.
 // ===========================================================================
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -612,17 +621,11 @@ __device__ __forceinline__ void unpack_fp16x8(const uint4 &u, float (&v)[8]) {
     for (int i = 0; i < 8; ++i) v[i] = h2f((uint16_t)(w[i / 2] >> (16 * (i & 1))));
 }
 
-// Eight INT4 codes of one word (token i at bits 4i) as an FP16 operand with
-// element 2i = token i and element 2i + 1 = token i + 4: 0x6400 | code is
-// 1024 + code exactly, and the packed subtraction of 1024 is exact.
+// Eight INT4 codes of one word as an FP16 operand of subnormals: register r
+// holds tokens (r, r + 4), scaled by 16 for odd r.
 __device__ __forceinline__ v8h int4_operand(uint32_t w) {
-    const v2h off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    v4u r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t x = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-        r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, x) + off);
-    }
+    const uint32_t w8 = w >> 8;
+    const v4u r = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
     return __builtin_bit_cast(v8h, r);
 }
 
@@ -630,7 +633,7 @@ __device__ __forceinline__ v8h int4_operand(uint32_t w) {
 // |err| <= max(2^-20 |x|, 2^-24).
 __device__ __forceinline__ void split_pair(float x, float y, uint32_t &hi, uint32_t &lo) {
     const auto h = __builtin_amdgcn_cvt_pkrtz(x, y);
-    const auto w = __builtin_amdgcn_cvt_pkrtz(x - (float)h[0], y - (float)h[1]);
+    const auto w = __builtin_amdgcn_cvt_pkrtz(fmaf((float)h[0], -1.0f, x), fmaf((float)h[1], -1.0f, y));
     hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, w);
 }
@@ -641,122 +644,121 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int G>
+constexpr float K16 = 0x1p14f;  // weight scale of FP16 values
+
+template <int D, int G, bool F16ACC>
 struct VAcc {
     static constexpr int NG = D / 32;         // value groups
     static constexpr int R = NG * G;          // rows (group, head)
     static constexpr int RT = (R + 15) / 16;  // row tiles
     static constexpr int NT = D / 16;         // column tiles
-    v4f acc[RT][NT];
-    float zacc[RT];
-    float m[G], l[G];
+    static constexpr int RT16 = F16ACC ? RT : 1;
+    v4f acc[RT][NT];      // INT4 values (FP16 values when !F16ACC)
+    v4f acc16[RT16][NT];  // FP16 values (F16ACC)
+    float zacc[RT];       // sum p z of the A row
+    float mrow[RT], lrow[RT];  // online softmax of the A row's head
 
     __device__ __forceinline__ void init() {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             zacc[rt] = 0.0f;
+            mrow[rt] = -INFINITY;
+            lrow[rt] = 0.0f;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         }
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            m[j] = -INFINITY;
-            l[j] = 0.0f;
-        }
-    }
-    // head of accumulator row 16 rt + 4 (lane / 16) + i
-    static __device__ __forceinline__ int drow_head(int lane, int i) {
-        return G <= 4 ? i % G : 4 * ((lane >> 4) & 1) + i;
-    }
-    // Online softmax over one block (lane = token): heads in `use` take the
-    // scores s[j]; the weights go to pw[j][lane] and the state is rescaled
-    // (per-head factors passed to the lanes through scl[0..G-1], LDS).
-    __device__ __forceinline__ void softmax(uint32_t use, const float (&s)[G], bool valid, float *pw,
-                                            float *scl, int lane) {
-        float sc[G];
-        bool any = false;
+        for (int rt = 0; rt < RT16; ++rt)
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            sc[j] = 1.0f;
-            if (!(use & (1u << j))) continue;
-            const float bm = wave_max_dpp(valid ? s[j] : -INFINITY);
-            const float mn = fmaxf(m[j], bm);
-            if (mn != m[j]) {
-                sc[j] = __expf(m[j] - mn);
-                any = true;
+            for (int nt = 0; nt < NT; ++nt) acc16[rt][nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    static __device__ __forceinline__ int arow(int rt, int lane) { return 16 * rt + (lane & 15); }
+    static __device__ __forceinline__ int ahead(int rt, int lane) { return arow(rt, lane) % G; }
+    static __device__ __forceinline__ int agroup(int rt, int lane) { return min(arow(rt, lane) / G, NG - 1); }
+
+    // Online softmax over one block.  sv[rt][i]: score of the A row's head
+    // for token 16 (lane / 16) + i, -inf where the token is invalid or the
+    // head takes no part; replaced by the weights.  Rescales the state.
+    __device__ __forceinline__ void softmax(float (&sv)[RT][16], int lane) {
+        float sc[RT];
+        bool resc = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float bm = sv[rt][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) bm = fmaxf(bm, sv[rt][i]);
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float mn = fmaxf(mrow[rt], bm);
+            sc[rt] = mn == mrow[rt] ? 1.0f : __expf(mrow[rt] - mn);
+            resc |= sc[rt] != 1.0f;
+            // p = 2^(s log2e - mn log2e); a row with no part has mn = -inf and
+            // only -inf scores, which give 0 against a finite offset
+            const float off = mn == -INFINITY ? 0.0f : -mn * 1.44269504088896341f;
+            float ls = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sv[rt][i], 1.44269504088896341f, off));
+                sv[rt][i] = p;
+                ls += p;
             }
-            m[j] = mn;
-            const float p = valid ? __expf(s[j] - mn) : 0.0f;
-            pw[j * 64 + lane] = p;
-            l[j] = fmaf(l[j], sc[j], wave_sum_dpp(p));
+            ls += __shfl_xor(ls, 16, 64);
+            ls += __shfl_xor(ls, 32, 64);
+            lrow[rt] = fmaf(lrow[rt], sc[rt], ls);
+            mrow[rt] = mn;
+            zacc[rt] *= sc[rt];
         }
-        if (any) {
-            if (lane == 0)
+        if (__builtin_amdgcn_ballot_w64(resc)) {
+            // factor of head h: lane h (row h of the first tile) holds it
+            float scH[G];
 #pragma unroll
-                for (int j = 0; j < G; ++j) scl[j] = sc[j];
-            wave_sync();
+            for (int h = 0; h < G; ++h) scH[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[0]), h));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float f = G <= 4 ? sc[i % G] : scl[drow_head(lane, i)];
+                const float f = G <= 4 ? scH[i % G] : ((lane >> 4) & 1 ? scH[(4 + i) % G] : scH[i % G]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) acc[rt][nt][i] *= f;
+#pragma unroll
+                for (int rt = 0; rt < RT16; ++rt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        if (F16ACC) acc16[rt][nt][i] *= f;
             }
-            const float fz = scl[(lane & 15) % G];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) zacc[rt] *= fz;
         }
     }
-    // Weights of A row 16 rt + lane % 16 for its 16 tokens; false if the row
-    // is unused (its operand is zero).
-    __device__ __forceinline__ bool arow(int rt, uint32_t mask, const float *pw, int lane, int &gv,
-                                         float (&p)[16]) const {
-        const int r = 16 * rt + (lane & 15);
-        const int h = r % G;
-        gv = min(r / G, NG - 1);
-        const float4 *src = reinterpret_cast<const float4 *>(pw + h * 64 + 16 * (lane >> 4));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 x = src[i];
-            p[4 * i] = x.x;
-            p[4 * i + 1] = x.y;
-            p[4 * i + 2] = x.z;
-            p[4 * i + 3] = x.w;
-        }
-        return r < R && (mask & (1u << h));
-    }
-    // INT4 values for the heads in `mask`.  cw[nt]: the 16 tokens' codes of
-    // channel 16 nt + lane % 16; mt[rt]: the 16 tokens' scale | offset of the
-    // A row's group.
-    __device__ __forceinline__ void int4_block(uint32_t mask, const float *pw, const v4u (&mt)[RT][4],
+    // INT4 values for the heads in `mask`.  p: weights (A layout); cw[nt]:
+    // the codes of channel 16 nt + lane % 16 for tokens 16 (lane / 16) + 0..15;
+    // mt[rt]: scale | offset words of the A row's group for the same tokens.
+    __device__ __forceinline__ void int4_block(uint32_t mask, const float (&p)[RT][16], const v4u (&mt)[RT][4],
                                                const uint2 (&cw)[NT], const float *ksg, int lane) {
         v8h ahi[RT][2], alo[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            int gv;
-            float p[16];
-            const bool on = arow(rt, mask, pw, lane, gv, p);
-            const float K = ksg[gv];
+            const bool on = arow(rt, lane) < R && (mask & (1u << ahead(rt, lane)));
+            const float K = on ? ksg[agroup(rt, lane)] : 0.0f;
             float a[16];
-            float z = zacc[rt];
+            float z = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const uint32_t mw = mt[rt][i / 4][i % 4];
                 const float s = h2f((uint16_t)(mw & 0xFFFFu)), zz = h2f((uint16_t)(mw >> 16));
-                a[i] = on ? (p[i] * s) * K : 0.0f;
-                z = on ? fmaf(p[i], zz, z) : z;
+                // odd registers of the operand (tokens 1, 3, 5, 7 of each
+                // 8) carry codes scaled by 16
+                a[i] = (p[rt][i] * s) * ((i & 1) ? K * 0.0625f : K);
+                z = fmaf(p[rt][i], zz, z);
             }
-            zacc[rt] = z;
+            zacc[rt] += on ? z : 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 v4u hi, lo;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int r = 0; r < 4; ++r) {
                     uint32_t x, y;
-                    split_pair(a[8 * ks + i], a[8 * ks + i + 4], x, y);
-                    hi[i] = x;
-                    lo[i] = y;
+                    split_pair(a[8 * ks + r], a[8 * ks + r + 4], x, y);
+                    hi[r] = x;
+                    lo[r] = y;
                 }
                 ahi[rt][ks] = __builtin_bit_cast(v8h, hi);
                 alo[rt][ks] = __builtin_bit_cast(v8h, lo);
@@ -778,24 +780,22 @@ struct VAcc {
     }
     // FP16 values for the heads in `mask`.  vv[nt][ks]: tokens
     // 16 (lane / 16) + 8 ks + (0 .. 7) of channel 16 nt + lane % 16.
-    __device__ __forceinline__ void fp16_block(uint32_t mask, const float *pw, const uint4 (&vv)[NT][2],
-                                               const float *ksg, int lane) {
+    __device__ __forceinline__ void fp16_block(uint32_t mask, const float (&p)[RT][16], const uint4 (&vv)[NT][2],
+                                               int lane) {
         v8h ahi[RT][2], alo[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            int gv;
-            float p[16];
-            const bool on = arow(rt, mask, pw, lane, gv, p);
-            const float K = ksg[gv];
+            const bool on = arow(rt, lane) < R && (mask & (1u << ahead(rt, lane)));
+            const float K = on ? K16 : 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 v4u hi, lo;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int r = 0; r < 4; ++r) {
                     uint32_t x, y;
-                    split_pair(on ? p[8 * ks + 2 * i] * K : 0.0f, on ? p[8 * ks + 2 * i + 1] * K : 0.0f, x, y);
-                    hi[i] = x;
-                    lo[i] = y;
+                    split_pair(p[rt][8 * ks + 2 * r] * K, p[rt][8 * ks + 2 * r + 1] * K, x, y);
+                    hi[r] = x;
+                    lo[r] = y;
                 }
                 ahi[rt][ks] = __builtin_bit_cast(v8h, hi);
                 alo[rt][ks] = __builtin_bit_cast(v8h, lo);
@@ -806,12 +806,12 @@ struct VAcc {
             const v8h b0 = __builtin_bit_cast(v8h, vv[nt][0]), b1 = __builtin_bit_cast(v8h, vv[nt][1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                v4f c = acc[rt][nt];
+                v4f c = F16ACC ? acc16[F16ACC ? rt : 0][nt] : acc[rt][nt];
                 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[rt][0], b0, c, 0, 0, 0);
                 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[rt][0], b0, c, 0, 0, 0);
                 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[rt][1], b1, c, 0, 0, 0);
                 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[rt][1], b1, c, 0, 0, 0);
-                acc[rt][nt] = c;
+                if (F16ACC) acc16[F16ACC ? rt : 0][nt] = c; else acc[rt][nt] = c;
             }
         }
     }
@@ -820,10 +820,10 @@ struct VAcc {
 // Tier-1 value operands of block `bi` for this lane: INT4 codes (channel-
 // major, 32 bytes per channel) and the scale | offset words of the A rows'
 // groups (group-major, 64 words per group).
-template <int D, int G>
+template <int D, int G, bool F>
 __device__ __forceinline__ void load_int4(const Layout &Ly, size_t bi, int lane, uint2 (&cw)[D / 16],
-                                          v4u (&mt)[VAcc<D, G>::RT][4]) {
-    using VA = VAcc<D, G>;
+                                          v4u (&mt)[VAcc<D, G, F>::RT][4]) {
+    using VA = VAcc<D, G, F>;
     const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
     const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
 #pragma unroll
@@ -831,8 +831,7 @@ __device__ __forceinline__ void load_int4(const Layout &Ly, size_t bi, int lane,
         cw[nt] = *reinterpret_cast<const uint2 *>(vq + (16 * nt + (lane & 15)) * 32 + 8 * (lane >> 4));
 #pragma unroll
     for (int rt = 0; rt < VA::RT; ++rt) {
-        const int gv = min((16 * rt + (lane & 15)) / G, VA::NG - 1);
-        const v4u *src = reinterpret_cast<const v4u *>(vm + gv * 64 + 16 * (lane >> 4));
+        const v4u *src = reinterpret_cast<const v4u *>(vm + VA::agroup(rt, lane) * 64 + 16 * (lane >> 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) mt[rt][i] = src[i];
     }
@@ -849,13 +848,49 @@ __device__ __forceinline__ void load_fp16v(const uint16_t *vb, int lane, uint4 (
                                                           16 * (lane >> 4) + 8 * ks);
 }
 
+// Scores of the A rows' heads for this lane's 16 tokens (four 16-byte reads
+// per row tile) from a per-head array with stride hstride floats (base1 for
+// the heads in sel1, base0 for the others).
+template <int D, int G, bool F>
+__device__ __forceinline__ void load_scores(const float *base0, const float *base1, uint32_t sel1,
+                                            size_t hstride, int lane, float (&sv)[VAcc<D, G, F>::RT][16]) {
+    using VA = VAcc<D, G, F>;
+#pragma unroll
+    for (int rt = 0; rt < VA::RT; ++rt) {
+        const int h = VA::ahead(rt, lane);
+        const float *src = ((sel1 >> h) & 1 ? base1 : base0) + h * hstride + 16 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 x = reinterpret_cast<const float4 *>(src)[i];
+            sv[rt][4 * i] = x.x;
+            sv[rt][4 * i + 1] = x.y;
+            sv[rt][4 * i + 2] = x.z;
+            sv[rt][4 * i + 3] = x.w;
+        }
+    }
+}
+
+// Marks the tokens >= np (an unfinished block) and the rows whose head is
+// not in `use` as taking no part.
+template <int D, int G, bool F>
+__device__ __forceinline__ void mask_scores(uint32_t use, int np, int lane, float (&sv)[VAcc<D, G, F>::RT][16]) {
+    using VA = VAcc<D, G, F>;
+#pragma unroll
+    for (int rt = 0; rt < VA::RT; ++rt) {
+        const bool on = VA::arow(rt, lane) < VA::R && (use & (1u << VA::ahead(rt, lane)));
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (!on || 16 * (lane >> 4) + i >= np) sv[rt][i] = -INFINITY;
+    }
+}
+
 // Write one partial (m, l, acc[D]) per head of the group to
 // part + (head * pstride + sp) * (D + 2), combining the four waves.
-template <int D, int G>
-__device__ __forceinline__ void write_partials(VAcc<D, G> &va, const float *ksg, float *part,
+template <int D, int G, bool F>
+__device__ __forceinline__ void write_partials(VAcc<D, G, F> &va, const float *ksg, float *part,
                                                size_t hbase, size_t pstride, int sp,
-                                               uint32_t heads_mask) {
-    using VA = VAcc<D, G>;
+                                               uint32_t heads_mask, bool int4) {
+    using VA = VAcc<D, G, F>;
     __shared__ float sm_m[4][G], sm_l[4][G];
     __shared__ float sm_acc[4][G][D];
     __shared__ float sm_z[4][VA::RT * 16];
@@ -872,21 +907,28 @@ __device__ __forceinline__ void write_partials(VAcc<D, G> &va, const float *ksg,
     // hold its heads (accumulator indices stay compile-time constants)
 #pragma unroll
     for (int nt = 0; nt < VA::NT; ++nt) {
-        const float inv = 1.0f / ksg[nt / 2];
+        // INT4 values are in units of 2^-24 / K, FP16 values in units of 1 / K16
+        const float inv = int4 ? 0x1p24f / ksg[nt / 2] : 1.0f / ksg[nt / 2];
 #pragma unroll
         for (int rt = 0; rt < VA::RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * rt + 4 * kg + i;
-                if (r < VA::R && r / G == nt / 2)
-                    sm_acc[wave][r % G][16 * nt + (lane & 15)] = fmaf(va.acc[rt][nt][i], inv, sm_z[wave][r]);
+                if (r < VA::R && r / G == nt / 2) {
+                    float v = fmaf(va.acc[rt][nt][i], inv, sm_z[wave][r]);
+                    if (F) v = fmaf(va.acc16[F ? rt : 0][nt][i], 1.0f / K16, v);
+                    sm_acc[wave][r % G][16 * nt + (lane & 15)] = v;
+                }
             }
     }
-    if (lane == 0) {
+    // the softmax state of head h sits in lane h (row h of the first tile)
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            sm_m[wave][j] = va.m[j];
-            sm_l[wave][j] = va.l[j];
+    for (int h = 0; h < G; ++h) {
+        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va.mrow[0]), h));
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va.lrow[0]), h));
+        if (lane == 0) {
+            sm_m[wave][h] = m;
+            sm_l[wave][h] = l;
         }
     }
     __syncthreads();
@@ -915,135 +957,136 @@ __device__ __forceinline__ void write_partials(VAcc<D, G> &va, const float *ksg,
 }
 
 // ===========================================================================
-// K3 (k_tail) / K4a values (k_promoted): split-K flash decoding over one
-// split of blocks of a (kv head, sequence); 256 threads, one wave per block.
-//   tail (PROM = false)  blocks and heads outside P and VP [Meth-3: "remaining
-//                        tail blocks stay INT8"]: INT8 scores, INT4 values.
-//   promoted (PROM)      heads of P or VP, plus the unfinished block: FP16-key
-//                        scores on P (from k_keys16) else INT8 scores; FP16
-//                        values on VP (staging area) and the unfinished block
-//                        (device), INT4 values otherwise.
+// K3 (k_tail) / K4a values (k_promoted4, k_promoted16): split-K flash
+// decoding over one split of blocks of a (kv head, sequence); 256 threads,
+// one wave per block, two blocks in flight per wave.
+//   VP_TAIL   heads outside P and VP [Meth-3: "remaining tail blocks stay
+//             INT8"]: INT8 scores, INT4 values.
+//   VP_INT4   heads of P without FP16 values: FP16-key scores (k_keys16),
+//             INT4 values.
+//   VP_FP16   heads of VP (FP16-key scores on P, else INT8 scores) and every
+//             head of the unfinished block (FP16 scores from the scoring
+//             pass): FP16 values from the staging area / the device.
 // Output path only: hardware exp and any summation order are allowed here.
 // ===========================================================================
-template <int D, int G, bool PROM>
+enum { VP_TAIL = 0, VP_INT4 = 1, VP_FP16 = 2 };
+
+template <int D, int G, int MODE>
 __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, const int *skip_seq) {
-    using VA = VAcc<D, G>;
+    constexpr bool F16 = MODE == VP_FP16;
+    using VA = VAcc<D, G, false>;
     const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
     // wave index as a uniform value: the block loop below branches uniformly
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l = St.layer;
-    if (PROM && skip_seq[n]) return;
+    if (MODE != VP_TAIL && skip_seq[n]) return;
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, np = len % 64;
-    const int nslot = PROM ? N + (np ? 1 : 0) : N;
+    const int nslot = F16 ? N + (np ? 1 : 0) : N;
     const int b0 = sp * St.bps, b1 = min(nslot, b0 + St.bps);
     constexpr uint32_t ALL = (1u << G) - 1u;
-    __shared__ __attribute__((aligned(16))) float pw[4][G][64];
-    __shared__ float scl[4][G];
     __shared__ float ksg[VA::NG];
     __shared__ uint32_t sbits[MAX_BPS];
+    __shared__ __attribute__((aligned(16))) float st[4][G][64];
     // selection bits of the split and the value-group scales: one round trip
     const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
     for (int i = threadIdx.x; i < b1 - b0; i += 256) sbits[i] = b0 + i < N ? St.sel[selbase + b0 + i] : 0u;
-    if (threadIdx.x < VA::NG) ksg[threadIdx.x] = Ly.vscale[Ly.seqg(l, n, g) * VA::NG + threadIdx.x];
+    if (threadIdx.x < VA::NG) ksg[threadIdx.x] = F16 ? K16 : Ly.vscale[Ly.seqg(l, n, g) * VA::NG + threadIdx.x];
     __syncthreads();
     const size_t NS64 = (size_t)St.NS * 64;
     VA va;
     va.init();
     struct Blk {
-        uint32_t pm, use, fp16v, int4v;
+        uint32_t pm, use;
         bool part;
     };
     struct Opd {
-        uint4 vv[VA::NT][2];
-        uint2 cw[VA::NT];
-        v4u mt[VA::RT][4];
-        float s[G];
+        uint4 vv[F16 ? VA::NT : 1][2];
+        uint2 cw[F16 ? 1 : VA::NT];
+        v4u mt[F16 ? 1 : VA::RT][4];
+        float s[G];  // scores, lane = token
     };
     auto plan = [&](int b) {
         Blk k;
-        k.part = PROM && b == N;
+        k.part = F16 && b == N;
         k.pm = 0;
-        if (k.part) {
-            k.use = ALL;
-            k.fp16v = ALL;
-        } else {
+        k.use = ALL;
+        if (!k.part) {
             const uint32_t bits = __builtin_amdgcn_readfirstlane(sbits[b - b0]);
             k.pm = bits & ALL;
             const uint32_t vm = (bits >> 8) & ALL;
-            k.use = PROM ? (k.pm | vm) : (~(k.pm | vm) & ALL);
-            k.fp16v = PROM ? vm : 0u;
+            k.use = MODE == VP_TAIL ? (~(k.pm | vm) & ALL) : MODE == VP_INT4 ? (k.pm & ~vm) : vm;
         }
-        k.int4v = k.use & ~k.fp16v;
         return k;
     };
     auto issue = [&](int b, const Blk &k, Opd &o) {
         if (!k.use) return;
-        const size_t sblk = selbase + b;
-        if (PROM && k.fp16v)
-            load_fp16v<D>(k.part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + sblk * 64 * D, lane, o.vv);
-        if (k.int4v) load_int4<D, G>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
+        if constexpr (F16)
+            load_fp16v<D>(k.part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + (selbase + b) * 64 * D, lane,
+                          o.vv);
+        else
+            load_int4<D, G, false>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const size_t si = (size_t)(n * Ly.Hq + g * G + j) * NS64 + (size_t)b * 64 + lane;
-            o.s[j] = !(k.use & (1u << j)) ? 0.0f : (PROM && (k.pm & (1u << j))) ? St.score16[si] : St.score[si];
+            o.s[j] = !(k.use & (1u << j)) ? 0.0f : (MODE != VP_TAIL && (k.pm & (1u << j))) ? St.score16[si] : St.score[si];
         }
     };
-    auto consume = [&](const Blk &k, const Opd &o) {
+    auto consume = [&](const Blk &k, Opd &o) {
         if (!k.use) return;
-        va.softmax(k.use, o.s, !k.part || lane < np, &pw[wave][0][0], scl[wave], lane);
+        // scores to the A layout through LDS
+#pragma unroll
+        for (int j = 0; j < G; ++j) st[wave][j][lane] = o.s[j];
         wave_sync();
-        if (PROM && k.fp16v) va.fp16_block(k.fp16v, &pw[wave][0][0], o.vv, ksg, lane);
-        if (k.int4v) va.int4_block(k.int4v, &pw[wave][0][0], o.mt, o.cw, ksg, lane);
+        float sv[VA::RT][16];
+        load_scores<D, G, false>(&st[wave][0][0], &st[wave][0][0], 0u, 64, lane, sv);
         wave_sync();
+        mask_scores<D, G, false>(k.use, k.part ? np : 64, lane, sv);
+        va.softmax(sv, lane);
+        if constexpr (F16)
+            va.fp16_block(k.use, sv, o.vv, lane);
+        else
+            va.int4_block(k.use, sv, o.mt, o.cw, ksg, lane);
     };
-    if constexpr (!PROM) {
-        // two blocks in flight per wave: the next block's operands are
-        // requested before the current one is consumed
-        Opd o0, o1;
-        Blk k0{}, k1{};
-        int b = b0 + wave;
-        if (b < b1) {
-            k0 = plan(b);
-            issue(b, k0, o0);
-        }
-        for (; b < b1; b += 8) {
-            const bool more = b + 4 < b1;
-            if (more) {
-                k1 = plan(b + 4);
-                issue(b + 4, k1, o1);
-            }
-            consume(k0, o0);
-            if (!more) break;
-            if (b + 8 < b1) {
-                k0 = plan(b + 8);
-                issue(b + 8, k0, o0);
-            }
-            consume(k1, o1);
-        }
-    } else {
-        for (int b = b0 + wave; b < b1; b += 4) {
-            const Blk k = plan(b);
-            if (!k.use) continue;
-            Opd o;
-            issue(b, k, o);
-            consume(k, o);
-        }
+    Opd o0, o1;
+    Blk k0{}, k1{};
+    int b = b0 + wave;
+    if (b < b1) {
+        k0 = plan(b);
+        issue(b, k0, o0);
     }
-    write_partials<D, G>(va, ksg, PROM ? St.part_blk : St.part_tail, (size_t)n * Ly.Hq + g * G,
-                         St.nsplit_cap, sp, ALL);
+    for (; b < b1; b += 8) {
+        const bool more = b + 4 < b1;
+        if (more) {
+            k1 = plan(b + 4);
+            issue(b + 4, k1, o1);
+        }
+        consume(k0, o0);
+        if (!more) break;
+        if (b + 8 < b1) {
+            k0 = plan(b + 8);
+            issue(b + 8, k0, o0);
+        }
+        consume(k1, o1);
+    }
+    float *part = MODE == VP_TAIL ? St.part_tail : MODE == VP_INT4 ? St.part_blk : St.part_blk16;
+    write_partials<D, G, false>(va, ksg, part, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp, ALL, !F16);
 }
 
-// Tail: three waves per SIMD where the registers allow (two blocks in flight
-// per wave).
+// Three waves per SIMD where the registers allow.
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G * D <= 512 ? 3 : 2))) void k_tail(Layout Ly, Step St) {
-    values_pass<D, G, false>(Ly, St, nullptr);
+    values_pass<D, G, VP_TAIL>(Ly, St, nullptr);
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_promoted(Layout Ly, Step St, const int *skip_seq) {
-    values_pass<D, G, true>(Ly, St, skip_seq);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G * D <= 512 ? 3 : 2))) void k_promoted4(Layout Ly, Step St, const int *skip_seq) {
+    values_pass<D, G, VP_INT4>(Ly, St, skip_seq);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_promoted16(Layout Ly, Step St, const int *skip_seq) {
+    values_pass<D, G, VP_FP16>(Ly, St, skip_seq);
 }
 
 // ===========================================================================
@@ -1327,12 +1370,16 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     // merge: tail partials then promoted partials; each wave merges a
     // contiguous quarter (eight loads in flight), the quarters are combined
     // in wave order
-    const int nsp_t = (N + St.bps - 1) / St.bps;
-    const int nsp_p = (N + (np ? 1 : 0) + St.bps - 1) / St.bps;
+    const int nsp_t = (N + St.bps - 1) / St.bps;            // tail, and promoted INT4 values
+    const int nsp_f = (N + (np ? 1 : 0) + St.bps - 1) / St.bps;  // promoted FP16 values
     const float *pt = St.part_tail + hs * St.nsplit_cap * (D + 2);
-    const float *pp = St.part_blk + hs * St.nsplit_cap * (D + 2);
-    auto part_ptr = [&](int i) { return i < nsp_t ? pt + (size_t)i * (D + 2) : pp + (size_t)(i - nsp_t) * (D + 2); };
-    const int ntot = nsp_t + nsp_p;
+    const float *p4 = St.part_blk + hs * St.nsplit_cap * (D + 2);
+    const float *pf = St.part_blk16 + hs * St.nsplit_cap * (D + 2);
+    auto part_ptr = [&](int i) {
+        return i < nsp_t ? pt + (size_t)i * (D + 2)
+             : i < 2 * nsp_t ? p4 + (size_t)(i - nsp_t) * (D + 2) : pf + (size_t)(i - 2 * nsp_t) * (D + 2);
+    };
+    const int ntot = 2 * nsp_t + nsp_f;
     const int per = (ntot + MERGE_T / 64 - 1) / (MERGE_T / 64);
     const int i_lo = wave * per, i_hi = min(ntot, i_lo + per);
     constexpr int BATCH = 8;
@@ -1400,11 +1447,12 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
 // and the dense comparator).  Blocks of (seq, kv head) are at
 // kbase + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
 // channel-major); `nfull[n]` full blocks, then an optional unfinished block.
-// Scores in FP32 on the vector units, values on the matrix cores.
+// Scores in FP32 on the vector units (lane = token), moved to the A layout
+// through LDS; values on the matrix cores.
 // ===========================================================================
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
-    using VA = VAcc<D, G>;
+    using VA = VAcc<D, G, false>;
     const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
     // wave index as a uniform value: the block loops below branch uniformly
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1415,12 +1463,11 @@ __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
     const int nslot = N + (np ? 1 : 0);
     const int b0 = sp * S.bps, b1 = min(nslot, b0 + S.bps);
     __shared__ float qs[G][D];
-    __shared__ __attribute__((aligned(16))) float pw[4][G][64];
-    __shared__ float scl[4][G];
+    __shared__ __attribute__((aligned(16))) float st[4][G][64];  // scores, lane = token -> A layout
     __shared__ float ksg[VA::NG];
     for (int i = threadIdx.x; i < G * D; i += 256)
         qs[i / D][i % D] = h2f(S.q[((size_t)n * S.Hq + g * G + i / D) * D + (i % D)]);
-    if (threadIdx.x < VA::NG) ksg[threadIdx.x] = 0x1p14f;  // FP16 values only: p K <= 2^14
+    if (threadIdx.x < VA::NG) ksg[threadIdx.x] = K16;  // FP16 values only
     __syncthreads();
     VA va;
     va.init();
@@ -1438,7 +1485,6 @@ __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
 #pragma unroll
         for (int ch = 0; ch < D / 8; ++ch) kv[ch] = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
         uint4 vv[VA::NT][2];
-        const bool valid = !part || lane < np;
         // opaque zero offset: keeps the q reads inside the loop
         int qoff = 0;
         asm volatile("" : "+s"(qoff));
@@ -1459,13 +1505,27 @@ __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
             for (int jj = 0; jj < G; ++jj) asm volatile("" : "+v"(a[jj])::"memory");
         }
 #pragma unroll
-        for (int jj = 0; jj < G; ++jj) a[jj] *= S.sm;
-        va.softmax(mask, a, valid, &pw[wave][0][0], scl[wave], lane);
+        for (int jj = 0; jj < G; ++jj) st[wave][jj][lane] = a[jj] * S.sm;
         wave_sync();
-        va.fp16_block(mask, &pw[wave][0][0], vv, ksg, lane);
+        float sv[VA::RT][16];
+#pragma unroll
+        for (int rt = 0; rt < VA::RT; ++rt) {
+            const float4 *src = reinterpret_cast<const float4 *>(&st[wave][VA::ahead(rt, lane)][16 * (lane >> 4)]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 x = src[i];
+                sv[rt][4 * i] = x.x;
+                sv[rt][4 * i + 1] = x.y;
+                sv[rt][4 * i + 2] = x.z;
+                sv[rt][4 * i + 3] = x.w;
+            }
+        }
         wave_sync();
+        mask_scores<D, G, false>(mask, part ? np : 64, lane, sv);
+        va.softmax(sv, lane);
+        va.fp16_block(mask, sv, vv, lane);
     }
-    write_partials<D, G>(va, ksg, S.part, (size_t)n * S.Hq + g * G, S.nsplit_cap, sp, mask);
+    write_partials<D, G, false>(va, ksg, S.part, (size_t)n * S.Hq + g * G, S.nsplit_cap, sp, mask, false);
 }
 
 template <int D, int G>
@@ -1535,8 +1595,12 @@ hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, 
 
 hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        const int nsp4 = (St.nb + St.bps - 1) / St.bps;
+        if (nsp4 > 0)
+            hipLaunchKernelGGL((k_promoted4<decltype(D)::value, decltype(G)::value>),
+                               dim3(nsp4, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
         const int nsp = (St.nb + 1 + St.bps - 1) / St.bps;
-        hipLaunchKernelGGL((k_promoted<decltype(D)::value, decltype(G)::value>),
+        hipLaunchKernelGGL((k_promoted16<decltype(D)::value, decltype(G)::value>),
                            dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
         return hipGetLastError();
     });

@@ -2,7 +2,8 @@
 //
 // HBM layout of tier 1 (device), per (layer l, sequence n, kv head g,
 // block b), blocks of 64 tokens, d = head_dim:
-//   kq    u8  [d/16][64][16]   INT8 key codes, chunk-interleaved: one 16-byte
+//   kq    u8  [d/16][64][16]   INT8 key codes stored as code ^ 0x80 (= code -
+//                              128 as a signed byte), chunk-interleaved: one 16-byte
 //                              load per lane covers 16 channels of one token
 //                              and a wave's load covers 1 KiB contiguous
 //   kmeta u32 [d]              binary16 scale | binary16 offset << 16
@@ -85,7 +86,8 @@ struct Step {
     float2 *st16;           // [B][Hq][Nmax] FP16-key block max, l on P
     uint64_t *m16;          // [B][Hq][Nmax]
     float *part_tail;       // [B][Hq][nsplit_cap][d+2]  m, l, acc
-    float *part_blk;        // [B][Hq][NS][d+2]
+    float *part_blk;        // [B][Hq][NS][d+2]  promoted blocks, INT4 values
+    float *part_blk16;      // [B][Hq][NS][d+2]  promoted blocks, FP16 values
     int nsplit_cap;
     const uint16_t *stage_k, *stage_v;  // [B][Hkv][Nmax][64*d]
     double *qd;             // [B][Hkv][d][G] q in FP64 (written by the scoring pass)
