@@ -179,6 +179,9 @@ def run_workload(name, args, cpu_baseline):
         "roofline": roofline, "kernels": table,
         "hbm_algorithmic_GBps_end_to_end": round((tier1_step + paged_step) / (elapsed / K) / 1e9, 1),
         "paged_MiB_per_step": round(paged_step / 2 ** 20, 2),
+        "blocks_per_step": {k: round(prof[k] / K, 1) for k in
+                            ("q8_blocks", "tail_blocks", "k16_blocks", "v16_blocks", "int4p_blocks",
+                             "dense_blocks")},
         "h2d_copies_per_step": round(prof["copies"] / K, 1),
         "phases_ms_per_step": {k: round(v[0] / K, 4) for k, v in ph.items()},
         "rungs_max_hist": rungs.tolist(), "kstar_mean": round(kstar, 2),

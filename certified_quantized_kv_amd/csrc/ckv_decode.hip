@@ -302,17 +302,20 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
 // One SEL_T-thread workgroup per (q head, sequence).
 // ===========================================================================
 constexpr int SEL_T = 512;
-constexpr int MAX_BPS = 64;  // blocks per split, at most (the host keeps bps in [4, 64])
+constexpr int MAX_BPS = 64;
+constexpr int SEL_LDS = 2048;  // blocks per head whose selection keys stay in LDS  // blocks per split, at most (the host keeps bps in [4, 64])
 
 struct SelShared {
     uint64_t hsum[64];
+    uint64_t hkey[64];
     uint32_t hsat[64];
+    uint32_t hcnt[64];
     uint64_t red_u[SEL_T / 64];
     double red_d[SEL_T / 64];
     float red_f[SEL_T / 64];
     int red_i[SEL_T / 64];
     uint64_t bc_u[4];
-    int bc_i[2];
+    int bc_i[4];
 };
 
 __device__ __forceinline__ float block_max_f(float v, SelShared &sh) {
@@ -342,6 +345,16 @@ __device__ __forceinline__ uint64_t block_sum_u(uint64_t v, SelShared &sh) {
     for (int i = 0; i < SEL_T / 64; ++i) r += sh.red_u[i];
     return r;
 }
+__device__ __forceinline__ uint64_t block_or_u(uint64_t v, SelShared &sh) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh.red_u[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t r = 0;
+    for (int i = 0; i < SEL_T / 64; ++i) r |= sh.red_u[i];
+    return r;
+}
 __device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
     v = wave_sum_i32(v);
     __syncthreads();
@@ -358,16 +371,24 @@ __device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
 // (the fewest blocks reaching `need`).  REST: the largest t whose rest
 // sum_{key < t} val satisfies E <= tol with no capped term left (the fewest
 // blocks to promote).  Returns t; the chosen set is {key >= t}.
-template <bool TOP>
-__device__ uint64_t radix_select(const uint64_t *val, int N, uint64_t need, double tol,
-                                 SelShared &sh) {
+template <bool TOP, class P>
+__device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, double tol, SelShared &sh) {
     const int tid = threadIdx.x;
+    // the passes start at the digit of the highest set bit of any key, and
+    // stop once the chosen bucket holds a single key whose exclusion was
+    // tested (that key is then the threshold: it belongs to the set)
+    uint64_t orv = 0;
+    for (int b = tid; b < N; b += SEL_T) orv |= (val[b] << 16) | (uint64_t)(0xFFFF - b);
+    orv = block_or_u(orv, sh);
+    const int top = orv ? 63 - __builtin_clzll(orv) : 0;
     uint64_t prefix = 0, outside = 0;  // TOP: sum above the region; REST: sum below
     uint32_t sat_out = 0;
-    for (int shift = 60; shift >= 0; shift -= 6) {
+    for (int shift = (top / 6) * 6; shift >= 0; shift -= 6) {
         if (tid < 64) {
             sh.hsum[tid] = 0;
+            sh.hkey[tid] = 0;
             sh.hsat[tid] = 0;
+            sh.hcnt[tid] = 0;
         }
         __syncthreads();
         const uint64_t himask = (shift + 6 >= 64) ? 0ull : (~0ull << (shift + 6));
@@ -377,6 +398,8 @@ __device__ uint64_t radix_select(const uint64_t *val, int N, uint64_t need, doub
             if ((key & himask) == (prefix & himask)) {
                 const int dg = (int)((key >> shift) & 63);
                 atomicAdd((unsigned long long *)&sh.hsum[dg], (unsigned long long)v);
+                atomicMax((unsigned long long *)&sh.hkey[dg], (unsigned long long)key);
+                atomicAdd(&sh.hcnt[dg], 1u);
                 if (!TOP && v >= FXCAP) atomicAdd(&sh.hsat[dg], 1u);
             }
         }
@@ -421,19 +444,35 @@ __device__ uint64_t radix_select(const uint64_t *val, int N, uint64_t need, doub
             if (dg == best) {
                 sh.bc_u[0] = prefix | ((uint64_t)best << shift);
                 sh.bc_u[1] = outside + add;
+                sh.bc_u[2] = sh.hkey[best];
                 sh.bc_i[0] = (int)(sat_out + addc);
+                sh.bc_i[1] = (int)sh.hcnt[best];
+                sh.bc_i[2] = best;
             }
         }
         __syncthreads();
         prefix = sh.bc_u[0];
         outside = sh.bc_u[1];
         sat_out = (uint32_t)sh.bc_i[0];
+        const int cnt = sh.bc_i[1], best = sh.bc_i[2];
+        const uint64_t kk = sh.bc_u[2];
         __syncthreads();
+        // a single key in the chosen bucket, with the next digit tested and
+        // failing (best < 63): that key is the threshold
+        if (cnt == 1 && best < 63) return kk;
     }
     return prefix;
 }
 
-__device__ __forceinline__ bool in_set(const uint64_t *val, int b, uint64_t thr) {
+// Delta and rho of a block from its statistics (max, l, Delta, rho) or from
+// the LDS copy (Delta, rho).
+__device__ __forceinline__ float sel_delta(const float4 &v) { return v.z; }
+__device__ __forceinline__ float sel_rho(const float4 &v) { return v.w; }
+__device__ __forceinline__ float sel_delta(const float2 &v) { return v.x; }
+__device__ __forceinline__ float sel_rho(const float2 &v) { return v.y; }
+
+template <class P>
+__device__ __forceinline__ bool in_set(P val, int b, uint64_t thr) {
     return ((val[b] << 16) | (uint64_t)(0xFFFF - b)) >= thr;
 }
 
@@ -448,18 +487,58 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
     const float4 *bs = St.bstat + hs * St.NS;
     uint64_t *M = St.mfx + hs * St.NS;
     uint64_t *cv = St.cval + hs * St.NS;
+    // the block statistics, annotations, fixed-point masses and E_val
+    // contributions stay in LDS while the selections read them (global
+    // memory beyond SEL_LDS blocks); their loads are issued together
+    __shared__ uint64_t sM[SEL_LDS], sC[SEL_LDS];
+    __shared__ float2 sDR[SEL_LDS];  // Delta, rho
+    __shared__ float sEta[SEL_LDS];
+    const bool in_lds = Np <= SEL_LDS;
+    const float *etag = Ly.eta + Ly.blk(l, n, g, 0);
+    constexpr int SPT = SEL_LDS / SEL_T;
+    float4 stv[SPT];
+    float etv[SPT];
 
     // estimated masses in fixed point
     float m = -INFINITY;
-    for (int b = tid; b < Np; b += SEL_T) m = fmaxf(m, bs[b].x);
+    if (in_lds) {
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int b = tid + k * SEL_T;
+            if (b < Np) stv[k] = bs[b];
+            if (b < N) etv[k] = etag[b];
+        }
+#pragma unroll
+        for (int k = 0; k < SPT; ++k)
+            if (tid + k * SEL_T < Np) m = fmaxf(m, stv[k].x);
+    } else {
+        for (int b = tid; b < Np; b += SEL_T) m = fmaxf(m, bs[b].x);
+    }
     const float mref = block_max_f(m, sh);
     uint64_t s = 0;
-    for (int b = tid; b < Np; b += SEL_T) {
-        const float4 st = bs[b];
+    auto mass = [&](const float4 &st) {
         const float mh = st.y * exp_c(st.x - mref);
-        const uint64_t Mb = (uint64_t)((double)mh * 4294967296.0);
-        M[b] = Mb;
-        s += Mb;
+        return (uint64_t)((double)mh * 4294967296.0);
+    };
+    if (in_lds) {
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int b = tid + k * SEL_T;
+            if (b < Np) {
+                const uint64_t Mb = mass(stv[k]);
+                M[b] = Mb;
+                sM[b] = Mb;
+                sDR[b] = make_float2(stv[k].z, stv[k].w);
+                s += Mb;
+            }
+            if (b < N) sEta[b] = etv[k];
+        }
+    } else {
+        for (int b = tid; b < Np; b += SEL_T) {
+            const uint64_t Mb = mass(bs[b]);
+            M[b] = Mb;
+            s += Mb;
+        }
     }
     const uint64_t S = block_sum_u(s, sh);
     const uint64_t Mpart = has_part ? M[N] : 0;
@@ -475,111 +554,114 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
     const double Sd = (double)S;
     auto phat = [&](uint64_t Mb) { return ((double)(Mb + 1) / Sd) * (1.0 + 0x1p-16); };
 
-    double tau = (double)th.tau;
-    int widened = 0, cap_fail = 0;
-    uint64_t thrP = ~0ull;
-    double F = 1.0, mu = 0.0, tv = 1.0, ekey = 0.0;
-    for (int wv = 0;; ++wv) {
-        const uint64_t T = (uint64_t)ceil(tau * Sd);
-        const uint64_t need = T > Mpart ? T - Mpart : 0;
-        thrP = radix_select<true>(M, N, need, 0.0, sh);
-        // F = exp(max over P of (Delta + rho))
-        double fm = 0.0;
-        for (int b = tid; b < N; b += SEL_T)
-            if (in_set(M, b, thrP)) fm = fmax(fm, (double)bs[b].z + (double)bs[b].w);
-        F = expu(block_max_d(fm, sh));
-        uint64_t sum = 0;
-        int sat = 0;
-        double dmax = 0.0;
-        for (int b = tid; b < N; b += SEL_T) {
-            const float4 st = bs[b];
-            const bool p = in_set(M, b, thrP);
-            const double dl = p ? (double)st.w : (double)st.z;
-            const double X = p ? expu((double)st.z + (double)st.w) : 1.0;
-            const uint64_t u = fx(phat(M[b]) * F * X * em1u(dl) * (1.0 + 0x1p-48));
-            sat |= (u == FXCAP);
-            sum += u;
-            dmax = fmax(dmax, dl);
+    auto body = [&](auto *Mv, auto *Cv, auto *DRv, auto *Ev) {
+        double tau = (double)th.tau;
+        int widened = 0, cap_fail = 0;
+        uint64_t thrP = ~0ull;
+        double F = 1.0, mu = 0.0, tv = 1.0, ekey = 0.0;
+        for (int wv = 0;; ++wv) {
+            const uint64_t T = (uint64_t)ceil(tau * Sd);
+            const uint64_t need = T > Mpart ? T - Mpart : 0;
+            thrP = radix_select<true>(Mv, N, need, 0.0, sh);
+            // F = exp(max over P of (Delta + rho))
+            double fm = 0.0;
+            for (int b = tid; b < N; b += SEL_T)
+                if (in_set(Mv, b, thrP)) fm = fmax(fm, (double)sel_delta(DRv[b]) + (double)sel_rho(DRv[b]));
+            F = expu(block_max_d(fm, sh));
+            uint64_t sum = 0;
+            int sat = 0;
+            double dmax = 0.0;
+            for (int b = tid; b < N; b += SEL_T) {
+                const double dz = (double)sel_delta(DRv[b]), rh = (double)sel_rho(DRv[b]);
+                const bool p = in_set(Mv, b, thrP);
+                const double dl = p ? rh : dz;
+                const double X = p ? expu(dz + rh) : 1.0;
+                const uint64_t u = fx(phat(Mv[b]) * F * X * em1u(dl) * (1.0 + 0x1p-48));
+                sat |= (u == FXCAP);
+                sum += u;
+                dmax = fmax(dmax, dl);
+            }
+            if (has_part && tid == 0) {
+                const double dl = (double)bs[N].w;
+                const uint64_t u = fx(phat(M[N]) * F * 1.0 * em1u(dl) * (1.0 + 0x1p-48));
+                sat |= (u == FXCAP);
+                sum += u;
+                dmax = fmax(dmax, dl);
+            }
+            sum = block_sum_u(sum, sh);
+            sat = block_sum_i(sat, sh);
+            dmax = block_max_d(dmax, sh);
+            mu = fx_bound(sum, sat != 0);
+            tv = 1.0;
+            if (mu < 1.0) tv = mu / (1.0 - mu) * (1.0 + 0x1p-48);
+            const double thb = tanhu(dmax);
+            if (thb < tv) tv = thb;
+            if (tv > 1.0) tv = 1.0;
+            ekey = tv * R * (1.0 + 0x1p-50);
+            if (!(ekey > (double)th.k_tol)) break;
+            if (wv >= th.n_widen) {
+                cap_fail = 1;
+                break;
+            }
+            tau = 1.0 - (1.0 - tau) * 0.5;
+            widened = 1;
         }
-        if (has_part && tid == 0) {
-            const double dl = (double)bs[N].w;
-            const uint64_t u = fx(phat(M[N]) * F * 1.0 * em1u(dl) * (1.0 + 0x1p-48));
-            sat |= (u == FXCAP);
-            sum += u;
-            dmax = fmax(dmax, dl);
-        }
-        sum = block_sum_u(sum, sh);
-        sat = block_sum_i(sat, sh);
-        dmax = block_max_d(dmax, sh);
-        mu = fx_bound(sum, sat != 0);
-        tv = 1.0;
-        if (mu < 1.0) tv = mu / (1.0 - mu) * (1.0 + 0x1p-48);
-        const double thb = tanhu(dmax);
-        if (thb < tv) tv = thb;
-        if (tv > 1.0) tv = 1.0;
-        ekey = tv * R * (1.0 + 0x1p-50);
-        if (!(ekey > (double)th.k_tol)) break;
-        if (wv >= th.n_widen) {
-            cap_fail = 1;
-            break;
-        }
-        tau = 1.0 - (1.0 - tau) * 0.5;
-        widened = 1;
-    }
 
-    // E_val contributions with the final P; rung 2 by radix select
-    uint64_t tot = 0;
-    int satv = 0;
-    for (int b = tid; b < N; b += SEL_T) {
-        const float4 st = bs[b];
-        const bool p = in_set(M, b, thrP);
-        const double X = p ? expu((double)st.z + (double)st.w) : 1.0;
-        const double e = (double)Ly.eta[Ly.blk(l, n, g, b)];
-        const uint64_t u = fx(phat(M[b]) * F * X * e * (1.0 + 0x1p-48));
-        cv[b] = u;
-        tot += u;
-        satv |= (u == FXCAP);
-    }
-    __syncthreads();
-    const uint64_t thrV = radix_select<false>(cv, N, 0, (double)th.v_tol, sh);
-    uint64_t rest = 0;
-    int nvp = 0, kst = 0, satr = 0;
-    for (int b = tid; b < N; b += SEL_T) {
-        const bool v = in_set(cv, b, thrV);
-        const bool p = in_set(M, b, thrP);
-        nvp += v;
-        kst += p;
-        if (!v) {
-            rest += cv[b];
-            satr |= (cv[b] == FXCAP);
+        // E_val contributions with the final P; rung 2 by radix select
+        uint64_t tot = 0;
+        int satv = 0;
+        for (int b = tid; b < N; b += SEL_T) {
+            const bool p = in_set(Mv, b, thrP);
+            const double X = p ? expu((double)sel_delta(DRv[b]) + (double)sel_rho(DRv[b])) : 1.0;
+            const double e = (double)Ev[b];
+            const uint64_t u = fx(phat(Mv[b]) * F * X * e * (1.0 + 0x1p-48));
+            Cv[b] = u;
+            tot += u;
+            satv |= (u == FXCAP);
         }
-        const uint32_t bits = (p ? (1u << j) : 0u) | (v ? (1u << (8 + j)) : 0u);
-        if (bits) atomicOr(&St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b], bits);
-    }
-    rest = block_sum_u(rest, sh);
-    nvp = block_sum_i(nvp, sh);
-    kst = block_sum_i(kst, sh);
-    satr = block_sum_i(satr, sh);
-    const double eval = fx_bound(rest, satr != 0);
-    if ((th.vcap > 0 && nvp > th.vcap) || eval > (double)th.v_tol) cap_fail = 1;
-    (void)tot;
-    (void)satv;
-    if (tid == 0) {
-        HeadPlan P;
-        P.mu = mu;
-        P.tv = tv;
-        P.ekey = ekey;
-        P.eval = eval;
-        P.tau = tau;
-        P.mref = mref;
-        P.kstar = kst;
-        P.nvp = nvp;
-        P.flags = widened | (cap_fail << 1);
-        P.rank_ok = -1;
-        P.ndisc = 0;
-        P.S = S;
-        St.plan[hs] = P;
-    }
+        __syncthreads();
+        const uint64_t thrV = radix_select<false>(Cv, N, 0, (double)th.v_tol, sh);
+        uint64_t rest = 0;
+        int nvp = 0, kst = 0, satr = 0;
+        for (int b = tid; b < N; b += SEL_T) {
+            const bool v = in_set(Cv, b, thrV);
+            const bool p = in_set(Mv, b, thrP);
+            nvp += v;
+            kst += p;
+            if (!v) {
+                rest += Cv[b];
+                satr |= (Cv[b] == FXCAP);
+            }
+            const uint32_t bits = (p ? (1u << j) : 0u) | (v ? (1u << (8 + j)) : 0u);
+            if (bits) atomicOr(&St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + b], bits);
+        }
+        rest = block_sum_u(rest, sh);
+        nvp = block_sum_i(nvp, sh);
+        kst = block_sum_i(kst, sh);
+        satr = block_sum_i(satr, sh);
+        const double eval = fx_bound(rest, satr != 0);
+        if ((th.vcap > 0 && nvp > th.vcap) || eval > (double)th.v_tol) cap_fail = 1;
+        (void)tot;
+        (void)satv;
+        if (tid == 0) {
+            HeadPlan P;
+            P.mu = mu;
+            P.tv = tv;
+            P.ekey = ekey;
+            P.eval = eval;
+            P.tau = tau;
+            P.mref = mref;
+            P.kstar = kst;
+            P.nvp = nvp;
+            P.flags = widened | (cap_fail << 1);
+            P.rank_ok = -1;
+            P.ndisc = 0;
+            P.S = S;
+            St.plan[hs] = P;
+        }
+    };
+    __syncthreads();
+    if (in_lds) body(sM, sC, sDR, sEta); else body(M, cv, bs, etag);
 }
 
 // ===========================================================================
@@ -1204,6 +1286,7 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
 // INT8 order; inconsistent iff D > floor(rank_tol * K*(K*-1)/2).
 // ===========================================================================
 constexpr int RANK_LDS = 2048;
+constexpr int RANK_PAIRS = 512;  // up to this K the pairs are counted directly
 constexpr int MERGE_T = 1024;
 
 // Number of elements of the descending run r[0..n) greater than x
@@ -1223,7 +1306,7 @@ __device__ __forceinline__ int count_greater(const uint64_t *r, int n, uint64_t 
 // element of a right run the elements of the left run smaller than it.
 // Exact integer result, independent of the thread count.  Uses and
 // overwrites kI, k16; tmp holds RANK_LDS entries.  All threads call it.
-__device__ long long discordant_sorted(uint64_t *kI, uint64_t *k16, uint64_t *tmp, int K) {
+__device__ __forceinline__ long long discordant_sorted(uint64_t *kI, uint64_t *k16, uint64_t *tmp, int K) {
     const int tid = threadIdx.x;
     int Kp = 1;
     while (Kp < K) Kp <<= 1;
@@ -1316,34 +1399,58 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         __syncthreads();
     }
     const bool use_lds = K <= RANK_LDS;
-    const uint32_t *list = use_lds ? lds_list : plist;
-    uint64_t *kI = use_lds ? lds_kI : keys_g + hs * 2 * Ly.Nmax;
-    uint64_t *k16 = use_lds ? lds_k16 : keys_g + hs * 2 * Ly.Nmax + Ly.Nmax;
     const float2 *st16 = St.st16 + hs * Ly.Nmax;
-    // largest FP16 block max over P
-    float mr = -INFINITY;
-    for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[list[i]].x);
-    mr = wave_max_f32(mr);
-    if (lane == 0) red_f[wave] = mr;
-    __syncthreads();
-    mr = red_f[0];
-    for (int w = 1; w < MERGE_T / 64; ++w) mr = fmaxf(mr, red_f[w]);
     const uint64_t *M = St.mfx + hs * St.NS;
-    for (int i = tid; i < K; i += MERGE_T) {
-        const uint32_t b = list[i];
+    // block b's fixed-point FP16 mass M16 (relative to the largest FP16 block
+    // max mr over P) and the two keys (mass desc, index asc)
+    auto keys = [&](uint32_t b, float mr, uint64_t &ki, uint64_t &k16) {
         const float2 s = st16[b];
         const float m16 = s.y * exp_c(s.x - mr);
         const uint64_t M16 = (uint64_t)((double)m16 * 4294967296.0);
         St.m16[hs * Ly.Nmax + b] = M16;
-        kI[i] = (M[b] << 16) | (uint64_t)(0xFFFF - b);
-        k16[i] = (M16 << 16) | (uint64_t)(0xFFFF - b);
-    }
-    __syncthreads();
-    // Kendall discordant pairs
+        ki = (M[b] << 16) | (uint64_t)(0xFFFF - b);
+        k16 = (M16 << 16) | (uint64_t)(0xFFFF - b);
+    };
+    auto block_max = [&](float v) {
+        v = wave_max_f32(v);
+        if (lane == 0) red_f[wave] = v;
+        __syncthreads();
+        float r = red_f[0];
+        for (int w = 1; w < MERGE_T / 64; ++w) r = fmaxf(r, red_f[w]);
+        return r;
+    };
+    // Kendall discordant pairs; the LDS path names the shared arrays
+    // directly (LDS instructions, not generic addresses)
     long long D_ = 0;
     if (use_lds) {
-        D_ = discordant_sorted(kI, k16, lds_tmp, K);
+        float mr = -INFINITY;
+        for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[lds_list[i]].x);
+        mr = block_max(mr);
+        for (int i = tid; i < K; i += MERGE_T) keys(lds_list[i], mr, lds_kI[i], lds_k16[i]);
+        __syncthreads();
+        if (K <= RANK_PAIRS) {
+            // all pairs from LDS: rows i and K-1-i go to the same thread
+            for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {
+                const int rows[2] = {i, K - 1 - i};
+                for (int r = 0; r < (rows[0] == rows[1] ? 1 : 2); ++r) {
+                    const int a_ = rows[r];
+                    const uint64_t a = lds_kI[a_], c = lds_k16[a_];
+                    int d = 0;
+                    for (int q = a_ + 1; q < K; ++q) d += ((a > lds_kI[q]) != (c > lds_k16[q]));
+                    D_ += d;
+                }
+            }
+        } else {
+            D_ = discordant_sorted(lds_kI, lds_k16, lds_tmp, K);
+        }
     } else {
+        uint64_t *kI = keys_g + hs * 2 * Ly.Nmax;
+        uint64_t *k16 = kI + Ly.Nmax;
+        float mr = -INFINITY;
+        for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[plist[i]].x);
+        mr = block_max(mr);
+        for (int i = tid; i < K; i += MERGE_T) keys(plist[i], mr, kI[i], k16[i]);
+        __syncthreads();
         // rows i and K-1-i go to the same thread (equal work per thread)
         for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {
             const int rows[2] = {i, K - 1 - i};
