@@ -371,19 +371,66 @@ __device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
 // (the fewest blocks reaching `need`).  REST: the largest t whose rest
 // sum_{key < t} val satisfies E <= tol with no capped term left (the fewest
 // blocks to promote).  Returns t; the chosen set is {key >= t}.
+// Threshold selection over the keys key(b) = (val_b << 16) | (0xFFFF - b),
+// unique per block, so "key desc" is the order (value desc, index asc).
+// TOP: the largest threshold t with sum_{key >= t} val >= need (the fewest
+// blocks reaching `need`).  REST: the largest t whose rest sum_{key < t} val
+// satisfies E <= tol with no capped term left (the fewest blocks to
+// promote).  Returns t; the chosen set is {key >= t}.
+// Bucket passes over the current key range [lo, hi]: 64 buckets of width
+// 2^shift spanning the range, per-bucket value sums, counts and largest key
+// by LDS atomics; the bucket holding the threshold becomes the next range.
+// A bucket with a single key whose exclusion was tested (not the last
+// bucket) ends the search: that key is the threshold.
 template <bool TOP, class P>
 __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, double tol, SelShared &sh) {
-    const int tid = threadIdx.x;
-    // the passes start at the digit of the highest set bit of any key, and
-    // stop once the chosen bucket holds a single key whose exclusion was
-    // tested (that key is then the threshold: it belongs to the set)
-    uint64_t orv = 0;
-    for (int b = tid; b < N; b += SEL_T) orv |= (val[b] << 16) | (uint64_t)(0xFFFF - b);
-    orv = block_or_u(orv, sh);
-    const int top = orv ? 63 - __builtin_clzll(orv) : 0;
-    uint64_t prefix = 0, outside = 0;  // TOP: sum above the region; REST: sum below
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // key range and total (REST: the empty set may already satisfy)
+    uint64_t kmin = ~0ull, kmax = 0, tot = 0;
+    uint32_t tsat = 0;
+    for (int b = tid; b < N; b += SEL_T) {
+        const uint64_t v = val[b];
+        const uint64_t key = (v << 16) | (uint64_t)(0xFFFF - b);
+        kmin = key < kmin ? key : kmin;
+        kmax = key > kmax ? key : kmax;
+        tot += v;
+        tsat += (!TOP && v >= FXCAP);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t a = __shfl_xor(kmin, o, 64), c = __shfl_xor(kmax, o, 64);
+        kmin = a < kmin ? a : kmin;
+        kmax = c > kmax ? c : kmax;
+        tot += __shfl_xor(tot, o, 64);
+        tsat += __shfl_xor(tsat, o, 64);
+    }
+    __syncthreads();
+    if (lane == 0) {
+        sh.red_u[wave] = kmin;
+        sh.hkey[wave] = kmax;
+        sh.hsum[wave] = tot;
+        sh.hsat[wave] = tsat;
+    }
+    __syncthreads();
+    kmin = ~0ull;
+    kmax = 0;
+    tot = 0;
+    tsat = 0;
+    for (int w = 0; w < SEL_T / 64; ++w) {
+        kmin = sh.red_u[w] < kmin ? sh.red_u[w] : kmin;
+        kmax = sh.hkey[w] > kmax ? sh.hkey[w] : kmax;
+        tot += sh.hsum[w];
+        tsat += sh.hsat[w];
+    }
+    // the empty set already satisfies: threshold above every key
+    if (N == 0 || (TOP ? need == 0 : !(fx_bound(tot, tsat != 0) > tol))) return ~0ull;
+    uint64_t lo = kmin, hi = kmax;
+    uint64_t outside = 0;  // TOP: sum above [lo, hi]; REST: sum below
     uint32_t sat_out = 0;
-    for (int shift = (top / 6) * 6; shift >= 0; shift -= 6) {
+    for (;;) {
+        const uint64_t span = hi - lo;  // >= 0
+        const int shift = span >> 6 ? 58 - __builtin_clzll(span) : 0;  // (span >> shift) < 64
+        __syncthreads();
         if (tid < 64) {
             sh.hsum[tid] = 0;
             sh.hkey[tid] = 0;
@@ -391,12 +438,11 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
             sh.hcnt[tid] = 0;
         }
         __syncthreads();
-        const uint64_t himask = (shift + 6 >= 64) ? 0ull : (~0ull << (shift + 6));
         for (int b = tid; b < N; b += SEL_T) {
             const uint64_t v = val[b];
             const uint64_t key = (v << 16) | (uint64_t)(0xFFFF - b);
-            if ((key & himask) == (prefix & himask)) {
-                const int dg = (int)((key >> shift) & 63);
+            if (key >= lo && key <= hi) {
+                const int dg = (int)((key - lo) >> shift);
                 atomicAdd((unsigned long long *)&sh.hsum[dg], (unsigned long long)v);
                 atomicMax((unsigned long long *)&sh.hkey[dg], (unsigned long long)key);
                 atomicAdd(&sh.hcnt[dg], 1u);
@@ -412,7 +458,7 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
             uint64_t add = 0;
             uint32_t addc = 0;
             if (TOP) {
-                // suffix sum over digits >= dg
+                // suffix sum over buckets >= dg
                 uint64_t suf = s;
 #pragma unroll
                 for (int o = 1; o < 64; o <<= 1) {
@@ -420,9 +466,9 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
                     if (dg + o < 64) suf += x;
                 }
                 pred = (outside + suf >= need) || dg == 0;
-                add = suf - s;  // sum over digits > dg
+                add = suf - s;  // sum over buckets > dg
             } else {
-                // exclusive prefix over digits < dg
+                // exclusive prefix over buckets < dg
                 uint64_t pre = s;
                 uint32_t pc = cs;
 #pragma unroll
@@ -440,10 +486,9 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
                 addc = pc;
             }
             const uint64_t bal = __ballot(pred);
-            const int best = 63 - __builtin_clzll(bal);  // largest digit with pred
+            const int best = 63 - __builtin_clzll(bal);  // largest bucket with pred
             if (dg == best) {
-                sh.bc_u[0] = prefix | ((uint64_t)best << shift);
-                sh.bc_u[1] = outside + add;
+                sh.bc_u[0] = outside + add;
                 sh.bc_u[2] = sh.hkey[best];
                 sh.bc_i[0] = (int)(sat_out + addc);
                 sh.bc_i[1] = (int)sh.hcnt[best];
@@ -451,17 +496,18 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
             }
         }
         __syncthreads();
-        prefix = sh.bc_u[0];
-        outside = sh.bc_u[1];
+        outside = sh.bc_u[0];
         sat_out = (uint32_t)sh.bc_i[0];
         const int cnt = sh.bc_i[1], best = sh.bc_i[2];
         const uint64_t kk = sh.bc_u[2];
-        __syncthreads();
-        // a single key in the chosen bucket, with the next digit tested and
-        // failing (best < 63): that key is the threshold
-        if (cnt == 1 && best < 63) return kk;
+        // the threshold: a single key in the chosen bucket whose exclusion was
+        // tested, or the key value itself once buckets are single values
+        if ((cnt == 1 && best < 63) || shift == 0) return shift == 0 ? lo + (uint64_t)best : kk;
+        const uint64_t nlo = lo + ((uint64_t)best << shift);
+        const uint64_t nhi = nlo + ((1ull << shift) - 1);
+        lo = nlo;
+        hi = nhi < hi ? nhi : hi;
     }
-    return prefix;
 }
 
 // Delta and rho of a block from its statistics (max, l, Delta, rho) or from
@@ -1429,17 +1475,21 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         for (int i = tid; i < K; i += MERGE_T) keys(lds_list[i], mr, lds_kI[i], lds_k16[i]);
         __syncthreads();
         if (K <= RANK_PAIRS) {
-            // all pairs from LDS: rows i and K-1-i go to the same thread
-            for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {
+            // all pairs (i, q > i) from LDS: RANK_SUB threads per row, rows
+            // i and K-1-i on the same thread group (equal work)
+            constexpr int RANK_SUB = 8;
+            const int sub = tid % RANK_SUB;
+            int d = 0;
+            for (int i = tid / RANK_SUB; i < (K + 1) / 2; i += MERGE_T / RANK_SUB) {
                 const int rows[2] = {i, K - 1 - i};
                 for (int r = 0; r < (rows[0] == rows[1] ? 1 : 2); ++r) {
                     const int a_ = rows[r];
                     const uint64_t a = lds_kI[a_], c = lds_k16[a_];
-                    int d = 0;
-                    for (int q = a_ + 1; q < K; ++q) d += ((a > lds_kI[q]) != (c > lds_k16[q]));
-                    D_ += d;
+#pragma unroll 4
+                    for (int q = a_ + 1 + sub; q < K; q += RANK_SUB) d += ((a > lds_kI[q]) != (c > lds_k16[q]));
                 }
             }
+            D_ = d;
         } else {
             D_ = discordant_sorted(lds_kI, lds_k16, lds_tmp, K);
         }
