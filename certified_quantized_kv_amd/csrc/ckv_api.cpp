@@ -50,6 +50,12 @@ enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH
 
 }  // namespace
 
+// Paging streams.  A host-to-device copy costs about 10 us of its stream's
+// time beyond the bytes on the link; copies on two streams overlap that
+// latency (measured: 2 streams beat 1 by 11-16% per layer-step, 4 streams
+// share hardware queues with the compute stream and do slightly worse).
+constexpr int NSIDE = 2;
+
 struct ckv_cache {
     ckv_config cfg{};
     Layout Ly{};
@@ -65,7 +71,8 @@ struct ckv_cache {
     double *qd = nullptr;
     float4 *bstat = nullptr;
     uint64_t *mfx = nullptr, *cval = nullptr, *m16 = nullptr, *keys = nullptr;
-    uint32_t *sel = nullptr, *plist = nullptr, *dmask = nullptr;
+    uint32_t *sel = nullptr, *plist = nullptr, *dmask = nullptr, *wl = nullptr;
+    int *wcnt = nullptr;
     HeadPlan *plan = nullptr;
     float2 *st16 = nullptr;
     int *dskip = nullptr, *dtmp_len = nullptr;
@@ -77,7 +84,10 @@ struct ckv_cache {
     // append staging (device, grown on demand)
     uint16_t *ain_k = nullptr, *ain_v = nullptr, *pk = nullptr, *pv = nullptr;
     size_t ain_cap = 0, pk_cap = 0;
-    hipStream_t side = nullptr;
+    // paging streams: host-issued copies spread over several streams so that
+    // the per-copy latency of one stream overlaps the others'
+    hipStream_t side[NSIDE] = {};
+    hipEvent_t ev_side[NSIDE] = {};
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
     hipEvent_t pev[13] = {};
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
@@ -181,7 +191,10 @@ void ckv_destroy(ckv_cache *c) {
     for (void *p : {(void *)c->t2k, (void *)c->t2v, (void *)c->h_sel, (void *)c->h_mask,
                     (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_tmp_len})
         if (p) (void)hipHostFree(p);
-    if (c->side) (void)hipStreamDestroy(c->side);
+    for (hipStream_t st : c->side)
+        if (st) (void)hipStreamDestroy(st);
+    for (hipEvent_t e : c->ev_side)
+        if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done})
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->pev)
@@ -200,6 +213,10 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(CKV_EINVAL, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
     const int Nmax = (k.max_context + 63) / 64;
+    // the FP16 staging area of one (sequence, kv head) is addressed with
+    // 32-bit byte offsets (up to 1 GiB: 4M tokens at head_dim 128)
+    if ((size_t)Nmax * 64 * k.head_dim * 2 > ((size_t)1 << 30))
+        return fail(CKV_EINVAL, "max_context %d too large for head_dim %d", k.max_context, k.head_dim);
     if (Nmax > 65536) return fail(CKV_EINVAL, "max_context above 4M tokens");
     HIPCHK(hipSetDevice(k.device));
     ckv_cache *c = new ckv_cache();
@@ -262,6 +279,8 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->part_blk16, hsl * (d + 2)));
     CTRY(dalloc(c, &c->qd, (size_t)B * Hq * d));
     CTRY(dalloc(c, &c->plist, (size_t)B * Hq * Nmax));
+    CTRY(dalloc(c, &c->wl, (size_t)WL_KINDS * B * Hkv * (Nmax + 1)));
+    CTRY(dalloc(c, &c->wcnt, (size_t)WL_KINDS * B * Hkv));
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
     CTRY(dalloc(c, &c->dskip, (size_t)B));
     CTRY(dalloc(c, &c->dtmp_len, (size_t)B));
@@ -275,7 +294,10 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     c->len.assign((size_t)L * B, 0);
     c->staged_k.assign(sblk, 0);
     c->staged_v.assign(sblk, 0);
-    HIPCHK(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+    for (int k = 0; k < NSIDE; ++k) {
+        HIPCHK(hipStreamCreateWithFlags(&c->side[k], hipStreamNonBlocking));
+        HIPCHK(hipEventCreateWithFlags(&c->ev_side[k], hipEventDisableTiming));
+    }
     HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_paged, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming));
@@ -383,8 +405,12 @@ struct CopyList {
 };
 
 // Largest run of unwanted blocks that is copied anyway to join two runs:
-// a 16 KiB block costs ~0.3 us on the host link, a separate copy several us.
-constexpr int PAGE_GAP = 24;
+// a 16 KiB block costs ~0.3 us on the host link, a separate copy ~10 us of
+// one stream's time, shared by the paging streams (12 was the best of
+// 3, 6, 12, 24 at 32K and 128K contexts with two streams).
+constexpr int PAGE_GAP = 12;
+// per-copy cost, in bytes of link time, when spreading runs over the streams
+constexpr size_t COPY_COST_BYTES = (size_t)512 << 10;
 
 // Queue the FP16 blocks of (seq n, kv head g) whose flag is set (and not
 // already staged) as runs of consecutive blocks, small gaps filled.
@@ -423,19 +449,39 @@ static batch_fn batch_copy() {
     return f;
 }
 
-// Issue a paging round on the side stream: one batched call when the
-// runtime has it, else one hipMemcpyAsync per run.
+// Issue a paging round over the paging streams (each run to the stream with
+// the fewest bytes so far; per stream one batched call when the runtime has
+// it, else one hipMemcpyAsync per run), then join them on side[0].
 static ckv_status issue_copies(ckv_cache *c, CopyList &cl) {
     if (cl.size.empty()) return CKV_OK;
-    size_t fail_idx = 0;
-    hipError_t e = hipErrorNotSupported;
-    if (batch_fn f = batch_copy())
-        e = f(cl.dst.data(), cl.src.data(), cl.size.data(), cl.size.size(), nullptr, nullptr, 0,
-              &fail_idx, c->side);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        for (size_t i = 0; i < cl.size.size(); ++i)
-            HIPCHK(hipMemcpyAsync(cl.dst[i], cl.src[i], cl.size[i], hipMemcpyHostToDevice, c->side));
+    CopyList per[NSIDE];
+    size_t load[NSIDE] = {};
+    for (size_t i = 0; i < cl.size.size(); ++i) {
+        int k = 0;
+        for (int j = 1; j < NSIDE; ++j)
+            if (load[j] < load[k]) k = j;
+        load[k] += cl.size[i] + COPY_COST_BYTES;
+        per[k].dst.push_back(cl.dst[i]);
+        per[k].src.push_back(cl.src[i]);
+        per[k].size.push_back(cl.size[i]);
+    }
+    for (int k = 0; k < NSIDE; ++k) {
+        CopyList &q = per[k];
+        if (q.size.empty()) continue;
+        size_t fail_idx = 0;
+        hipError_t e = hipErrorNotSupported;
+        if (batch_fn f = batch_copy())
+            e = f(q.dst.data(), q.src.data(), q.size.data(), q.size.size(), nullptr, nullptr, 0,
+                  &fail_idx, c->side[k]);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            for (size_t i = 0; i < q.size.size(); ++i)
+                HIPCHK(hipMemcpyAsync(q.dst[i], q.src[i], q.size[i], hipMemcpyHostToDevice, c->side[k]));
+        }
+        if (k > 0) {
+            HIPCHK(hipEventRecord(c->ev_side[k], c->side[k]));
+            HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_side[k], 0));
+        }
     }
     return CKV_OK;
 }
@@ -494,6 +540,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.stage_k = c->stage_k;
     St.stage_v = c->stage_v;
     St.qd = c->qd;
+    St.wl = c->wl;
+    St.wcnt = c->wcnt;
     St.out = out;
     Th T{};
     T.tau = th->tau_cov;
@@ -517,7 +565,9 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     HIPCHK(hipMemcpyAsync(c->h_sel, c->sel, selbytes, hipMemcpyDeviceToHost, s));
     HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(c->ev_sel, s));
-    // K3: tail blocks, overlapping the paging below
+    // block lists of the value passes; K3: tail blocks; both overlap the
+    // host's page lists and the paging below
+    HIPCHK(launch_worklist(Ly, St, s));
     if (prof) HIPCHK(hipEventRecord(E[3], s));
     if (St.nsplit > 0) HIPCHK(launch_tail(Ly, St, s));
     if (prof) HIPCHK(hipEventRecord(E[4], s));
@@ -529,7 +579,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
     size_t paged = 0;
     CopyList cl;
-    if (prof) HIPCHK(hipEventRecord(E[5], c->side));
+    if (prof) HIPCHK(hipEventRecord(E[5], c->side[0]));
     const uint32_t allg = (1u << G) - 1u;
     for (int n = 0; n < batch; ++n) {
         int skip = 0;
@@ -559,9 +609,9 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     TRY(issue_copies(c, cl));
     paged += cl.bytes;
     if (prof) c->pf.copies += cl.size.size();
-    HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side));
-    if (prof) HIPCHK(hipEventRecord(E[6], c->side));
-    HIPCHK(hipEventRecord(c->ev_paged, c->side));
+    HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
+    if (prof) HIPCHK(hipEventRecord(E[6], c->side[0]));
+    HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
     // K4: promoted blocks, rank check, merge
     if (prof) HIPCHK(hipEventRecord(E[7], s));
@@ -591,7 +641,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         }
     }
     if (any_dense) {
-        if (prof) HIPCHK(hipEventRecord(E[9], c->side));
+        if (prof) HIPCHK(hipEventRecord(E[9], c->side[0]));
         std::vector<uint8_t> all(Ly.Nmax, 1);
         cl.clear();
         for (int n = 0; n < batch; ++n) {
@@ -611,8 +661,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         paged += cl.bytes;
         if (prof) c->pf.copies += cl.size.size();
         HIPCHK(hipMemcpyAsync(c->dmask, c->h_mask, sizeof(uint32_t) * batch * Hkv, hipMemcpyHostToDevice,
-                              c->side));
-        HIPCHK(hipEventRecord(c->ev_paged, c->side));
+                              c->side[0]));
+        HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
         HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
         DenseSrc S{};
         S.k = c->stage_k;

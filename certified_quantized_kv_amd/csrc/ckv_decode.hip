@@ -80,7 +80,6 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
     // operands of a full block: codes (MFMA B operands) and this lane's
     // scale / offset words; requested one block ahead
     auto issue = [&](int slot, v4i (&bq)[4][KS], uint32_t (&km)[CPR]) {
-        if (slot >= N) return;
         const size_t bi = Ly.blk(l, n, g, slot);
         const uint8_t *kb = Ly.kq + bi * 64 * D;
 #pragma unroll
@@ -94,7 +93,7 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
     };
     v4i bq0[4][KS], bq1[4][KS];
     uint32_t km0[CPR], km1[CPR];
-    issue(s0, bq0, km0);
+    if (s0 < N) issue(s0, bq0, km0);
     for (int i = lane; i < G * D; i += 64) dig[i / D][3][i % D] = 0;  // the unused digit row
     for (int i = lane; i < G * D; i += 64)
         qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
@@ -284,15 +283,26 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                 St.bstat[(size_t)(n * Ly.Hq + g * G + hh) * St.NS + slot] = make_float4(mx, v, hd_dl[hh], hd_rh[hh]);
         }
     };
-    // full blocks s0 .. f1-1, the next block's operands in flight during the
-    // current one; then the unfinished block, if it is in this range
+    // full blocks s0 .. f1-1, the next block's operands requested before the
+    // current block is used, on every path (a request made on some paths
+    // only would make the waits before each use drain it); then the
+    // unfinished block, if it is in this range
     const int f1 = min(s1, N);
-    for (int slot = s0; slot < f1; slot += 2) {
-        if (slot + 1 < f1) issue(slot + 1, bq1, km1);
-        full(slot, bq0, km0);
-        if (slot + 1 >= f1) break;
-        if (slot + 2 < f1) issue(slot + 2, bq0, km0);
-        full(slot + 1, bq1, km1);
+    if (s0 < f1) {
+        int slot = s0;
+        for (; slot + 2 < f1; slot += 2) {
+            issue(slot + 1, bq1, km1);
+            full(slot, bq0, km0);
+            issue(slot + 2, bq0, km0);
+            full(slot + 1, bq1, km1);
+        }
+        if (slot + 1 < f1) {
+            issue(slot + 1, bq1, km1);
+            full(slot, bq0, km0);
+            full(slot + 1, bq1, km1);
+        } else {
+            full(slot, bq0, km0);
+        }
     }
     if (s1 > N) partial(N);
 }
@@ -319,7 +329,7 @@ struct SelShared {
 };
 
 __device__ __forceinline__ float block_max_f(float v, SelShared &sh) {
-    v = wave_max_f32(v);
+    v = wave_max_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.red_f[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -328,7 +338,7 @@ __device__ __forceinline__ float block_max_f(float v, SelShared &sh) {
     return r;
 }
 __device__ __forceinline__ double block_max_d(double v, SelShared &sh) {
-    v = wave_max_f64(v);
+    v = wave_max_f64_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.red_d[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -337,7 +347,7 @@ __device__ __forceinline__ double block_max_d(double v, SelShared &sh) {
     return r;
 }
 __device__ __forceinline__ uint64_t block_sum_u(uint64_t v, SelShared &sh) {
-    v = wave_sum_u64(v);
+    v = wave_sum_u64_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.red_u[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -346,8 +356,7 @@ __device__ __forceinline__ uint64_t block_sum_u(uint64_t v, SelShared &sh) {
     return r;
 }
 __device__ __forceinline__ uint64_t block_or_u(uint64_t v, SelShared &sh) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
+    v = wave_or_u64_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.red_u[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -356,7 +365,7 @@ __device__ __forceinline__ uint64_t block_or_u(uint64_t v, SelShared &sh) {
     return r;
 }
 __device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
-    v = wave_sum_i32(v);
+    v = wave_sum_i32_dpp(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.red_i[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -365,12 +374,6 @@ __device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
     return r;
 }
 
-// Radix select with 6-bit digits over 64-bit keys key(b) = (val_b << 16) |
-// (0xFFFF - b), unique per block, so "key desc" is the order (value desc,
-// index asc).  TOP: the largest threshold t with sum_{key >= t} val >= need
-// (the fewest blocks reaching `need`).  REST: the largest t whose rest
-// sum_{key < t} val satisfies E <= tol with no capped term left (the fewest
-// blocks to promote).  Returns t; the chosen set is {key >= t}.
 // Threshold selection over the keys key(b) = (val_b << 16) | (0xFFFF - b),
 // unique per block, so "key desc" is the order (value desc, index asc).
 // TOP: the largest threshold t with sum_{key >= t} val >= need (the fewest
@@ -396,14 +399,10 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
         tot += v;
         tsat += (!TOP && v >= FXCAP);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t a = __shfl_xor(kmin, o, 64), c = __shfl_xor(kmax, o, 64);
-        kmin = a < kmin ? a : kmin;
-        kmax = c > kmax ? c : kmax;
-        tot += __shfl_xor(tot, o, 64);
-        tsat += __shfl_xor(tsat, o, 64);
-    }
+    kmin = wave_min_u64_dpp(kmin);
+    kmax = wave_max_u64_dpp(kmax);
+    tot = wave_sum_u64_dpp(tot);
+    tsat = (uint32_t)wave_sum_i32_dpp((int)tsat);
     __syncthreads();
     if (lane == 0) {
         sh.red_u[wave] = kmin;
@@ -459,26 +458,13 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
             uint32_t addc = 0;
             if (TOP) {
                 // suffix sum over buckets >= dg
-                uint64_t suf = s;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint64_t x = __shfl_down(suf, o, 64);
-                    if (dg + o < 64) suf += x;
-                }
+                const uint64_t suf = wave_suffix_u64(s, dg);
                 pred = (outside + suf >= need) || dg == 0;
                 add = suf - s;  // sum over buckets > dg
             } else {
                 // exclusive prefix over buckets < dg
-                uint64_t pre = s;
-                uint32_t pc = cs;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint64_t x = __shfl_up(pre, o, 64);
-                    const uint32_t y = __shfl_up(pc, o, 64);
-                    if (dg >= o) { pre += x; pc += y; }
-                }
-                pre -= s;
-                pc -= cs;
+                const uint64_t pre = wave_prefix_excl_u64(s, dg);
+                const uint32_t pc = wave_prefix_excl_u32(cs, dg);
                 const uint64_t rem = outside + pre;
                 const bool satr = (sat_out + pc) != 0;
                 pred = !(fx_bound(rem, satr) > tol) || dg == 0;
@@ -1111,14 +1097,31 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, np = len % 64;
     const int nslot = F16 ? N + (np ? 1 : 0) : N;
-    const int b0 = sp * St.bps, b1 = min(nslot, b0 + St.bps);
     constexpr uint32_t ALL = (1u << G) - 1u;
     __shared__ float ksg[VA::NG];
-    __shared__ uint32_t sbits[MAX_BPS];
+    __shared__ uint32_t sbits[MAX_BPS], sblk[MAX_BPS];
     __shared__ __attribute__((aligned(16))) float st[4][G][64];
-    // selection bits of the split and the value-group scales: one round trip
     const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
-    for (int i = threadIdx.x; i < b1 - b0; i += 256) sbits[i] = b0 + i < N ? St.sel[selbase + b0 + i] : 0u;
+    // The blocks of this split: an equal share of the pass's block list, over
+    // as many splits as the block range [0, nslot) has of bps blocks (the
+    // partials the merge reads); every listed block serves some head here.
+    int ne;
+    {
+        const int nsp = (nslot + St.bps - 1) / St.bps;
+        const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
+        const int kind = MODE == VP_TAIL ? WL_TAIL : F16 ? WL_FP16 : WL_INT4;
+        const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[kind * nk + ng]);
+        const int e0 = sp < nsp ? (int)((long long)sp * cnt / nsp) : cnt;
+        const int e1 = sp < nsp ? (int)((long long)(sp + 1) * cnt / nsp) : cnt;
+        ne = min(e1 - e0, MAX_BPS);
+        const uint32_t *lst = St.wl + (kind * nk + ng) * (size_t)(Ly.Nmax + 1);
+        // block indices and selection bits of the split: one round trip
+        for (int i = threadIdx.x; i < ne; i += 256) {
+            const uint32_t b = lst[e0 + i];
+            sblk[i] = b;
+            sbits[i] = (int)b < N ? St.sel[selbase + b] : 0u;
+        }
+    }
     if (threadIdx.x < VA::NG) ksg[threadIdx.x] = F16 ? K16 : Ly.vscale[Ly.seqg(l, n, g) * VA::NG + threadIdx.x];
     __syncthreads();
     const size_t NS64 = (size_t)St.NS * 64;
@@ -1126,6 +1129,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     va.init();
     struct Blk {
         uint32_t pm, use;
+        int b;
         bool part;
     };
     struct Opd {
@@ -1134,34 +1138,45 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
         v4u mt[F16 ? 1 : VA::RT][4];
         float s[G];  // scores, lane = token
     };
-    auto plan = [&](int b) {
+    // entry i of the split: block, heads of P, heads whose values it serves
+    auto plan = [&](int i) {
         Blk k;
-        k.part = F16 && b == N;
+        k.b = (int)__builtin_amdgcn_readfirstlane(sblk[i]);
+        k.part = F16 && k.b == N;
         k.pm = 0;
         k.use = ALL;
         if (!k.part) {
-            const uint32_t bits = __builtin_amdgcn_readfirstlane(sbits[b - b0]);
+            const uint32_t bits = __builtin_amdgcn_readfirstlane(sbits[i]);
             k.pm = bits & ALL;
             const uint32_t vm = (bits >> 8) & ALL;
             k.use = MODE == VP_TAIL ? (~(k.pm | vm) & ALL) : MODE == VP_INT4 ? (k.pm & ~vm) : vm;
         }
         return k;
     };
-    auto issue = [&](int b, const Blk &k, Opd &o) {
-        if (!k.use) return;
+    // the scores of the group's heads as buffer resources (uniform bases, a
+    // 32-bit offset per lane)
+    const size_t srow = (size_t)(n * Ly.Hq + g * G) * NS64;
+    const uint32_t sbytes = (uint32_t)(G * NS64 * 4);
+    const __amdgpu_buffer_rsrc_t rs8 = make_rsrc(St.score + srow, sbytes);
+    const __amdgpu_buffer_rsrc_t rs16 = make_rsrc(St.score16 + srow, sbytes);
+    auto issue = [&](const Blk &k, Opd &o) {
+        const int b = k.b;
         if constexpr (F16)
             load_fp16v<D>(k.part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + (selbase + b) * 64 * D, lane,
                           o.vv);
         else
             load_int4<D, G, false>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
+        // scores of the group's heads: the FP16-key ones on P (promoted
+        // passes), the INT8 ones elsewhere, zero for heads not served here
+        // (an offset past the range: no memory access)
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            const size_t si = (size_t)(n * Ly.Hq + g * G + j) * NS64 + (size_t)b * 64 + lane;
-            o.s[j] = !(k.use & (1u << j)) ? 0.0f : (MODE != VP_TAIL && (k.pm & (1u << j))) ? St.score16[si] : St.score[si];
+            const bool f16 = MODE != VP_TAIL && (k.pm & (1u << j));
+            const uint32_t off = (k.use & (1u << j)) ? (uint32_t)j * (uint32_t)(NS64 * 4) + (uint32_t)b * 256u : RSRC_OOB;
+            o.s[j] = rsrc_load_f32(f16 ? rs16 : rs8, off + lane * 4);
         }
     };
     auto consume = [&](const Blk &k, Opd &o) {
-        if (!k.use) return;
         // scores to the A layout through LDS
 #pragma unroll
         for (int j = 0; j < G; ++j) st[wave][j][lane] = o.s[j];
@@ -1176,24 +1191,26 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
         else
             va.int4_block(k.use, sv, o.mt, o.cw, ksg, lane);
     };
+    // entries wave, wave + 4, ...: the next entry's operands in flight
+    // while the current one is used
     Opd o0, o1;
     Blk k0{}, k1{};
-    int b = b0 + wave;
-    if (b < b1) {
-        k0 = plan(b);
-        issue(b, k0, o0);
+    int i = wave;
+    if (i < ne) {
+        k0 = plan(i);
+        issue(k0, o0);
     }
-    for (; b < b1; b += 8) {
-        const bool more = b + 4 < b1;
+    for (; i < ne; i += 8) {
+        const bool more = i + 4 < ne;
         if (more) {
-            k1 = plan(b + 4);
-            issue(b + 4, k1, o1);
+            k1 = plan(i + 4);
+            issue(k1, o1);
         }
         consume(k0, o0);
         if (!more) break;
-        if (b + 8 < b1) {
-            k0 = plan(b + 8);
-            issue(b + 8, k0, o0);
+        if (i + 8 < ne) {
+            k0 = plan(i + 8);
+            issue(k0, o0);
         }
         consume(k1, o1);
     }
@@ -1225,6 +1242,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
 // through uniform scalar loads.
 // ===========================================================================
+constexpr int KEYS_MAXE = 32;  // list entries per workgroup of the FP16-key pass
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
                                                 const double *qd) {
@@ -1232,28 +1251,48 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l = St.layer;
     if (skip_seq[n]) return;
-    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
-    const int N = len / 64;
-    const int b0 = sp * St.bps, b1 = min(N, b0 + St.bps);
     constexpr uint32_t ALL = (1u << G) - 1u;
-    __shared__ uint32_t sbits[MAX_BPS];
+    __shared__ uint32_t sbits[KEYS_MAXE], sblk[KEYS_MAXE];
+    __shared__ float sres[4][KEYS_MAXE / 4][G][64];
+    __shared__ float2 sml[4][KEYS_MAXE / 4][G];
     const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
-    for (int i = threadIdx.x; i < b1 - b0; i += 256) sbits[i] = St.sel[selbase + b0 + i];
+    // an equal share of the (seq, kv head)'s P blocks per workgroup
+    const size_t ng = (size_t)n * Ly.Hkv + g;
+    const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[WL_KEYS * (size_t)Ly.B * Ly.Hkv + ng]);
+    const int nsp = gridDim.x;
+    const int e0 = (int)((long long)sp * cnt / nsp);
+    // at most KEYS_MAXE entries (the launch has enough workgroups for that)
+    const int ne = min((int)((long long)(sp + 1) * cnt / nsp) - e0, KEYS_MAXE);
+    const uint32_t *lst = St.wl + (WL_KEYS * (size_t)Ly.B * Ly.Hkv + ng) * (size_t)(Ly.Nmax + 1);
+    for (int i = threadIdx.x; i < ne; i += 256) {
+        const uint32_t b = lst[e0 + i];
+        sblk[i] = b;
+        sbits[i] = St.sel[selbase + b];
+    }
     __syncthreads();
     // q as [D][G] FP64, read through the constant address space (qd is not
     // written during this kernel): the loads are scalar
     typedef const __attribute__((address_space(4))) double cdouble;
     const int qbase = __builtin_amdgcn_readfirstlane((n * Ly.Hkv + g) * D * G);
     const size_t NS64 = (size_t)St.NS * 64;
-    auto pmask = [&](int b) { return __builtin_amdgcn_readfirstlane(sbits[b - b0]) & ALL; };
-    auto issue = [&](int b, uint32_t pm, uint4 (&kr)[D / 8]) {
-        if (!pm) return;
-        const uint16_t *kb = St.stage_k + (selbase + b) * 64 * D;
+    auto pmask = [&](int i) { return __builtin_amdgcn_readfirstlane(sbits[i]) & ALL; };
+    auto blk = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sblk[i]); };
+    // the (seq, kv head)'s staging area as a buffer resource: entries past
+    // the list load zeros from nowhere, so every path requests the same
+    // loads and the waits before each use stay exact
+    constexpr uint32_t BLKB = 64 * D * 2;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(St.stage_k + selbase * 64 * D, (uint32_t)Ly.Nmax * BLKB);
+    auto issue = [&](int i, uint4 (&kr)[D / 8]) {
+        const int ic = i < ne ? i : 0;  // in-range list index on every path
+        const uint32_t off = (i < ne ? (uint32_t)blk(ic) * BLKB : RSRC_OOB) + lane * 16;
 #pragma unroll
-        for (int ch = 0; ch < D / 8; ++ch) kr[ch] = *reinterpret_cast<const uint4 *>(kb + ch * 512 + lane * 8);
+        for (int ch = 0; ch < D / 8; ++ch) kr[ch] = rsrc_load16(rs, off + ch * 1024);
     };
-    auto consume = [&](int b, uint32_t pm, const uint4 (&kr)[D / 8]) {
-        if (!pm) return;
+    struct Res {
+        float s[G];
+    };
+    // FP64 chain over the channels for the G heads of the block in kr
+    auto compute = [&](const uint4 (&kr)[D / 8]) {
         int qoff = 0;
         asm volatile("" : "+s"(qoff));  // opaque zero: keeps the q loads in the loop
         cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(qbase + qoff);
@@ -1290,38 +1329,115 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
 #pragma unroll
             for (int i = 0; i < QN; ++i) qc[i] = qn[i];
         }
+        Res r;
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) r.s[jj] = (float)(a[jj] * (double)St.sm);
+        return r;
+    };
+    // scores, block max and mass of the heads of P, kept in LDS until the
+    // loads are done: a global store between the loads would make every
+    // wait for a load drain all outstanding requests (stores and loads
+    // share one counter and stores may finish out of order)
+    auto store = [&](int i, int t, const Res &r) {
+        const uint32_t pm = pmask(i);
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) {
+            if (!(pm & (1u << jj))) continue;
+            const float s = r.s[jj];
+            sres[wave][t][jj][lane] = s;
+            const float mx = wave_max_dpp(s);
+            const float l_ = tree64_f32_dpp(exp_c(s - mx));
+            // every lane writes the same pair (no lane-divergent branch in
+            // the loop: its exec-mask skips would add paths that bypass the
+            // next requests, and the waits would have to assume them)
+            sml[wave][t][jj] = make_float2(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_), 0)));
+        }
+    };
+    // entries wave, wave + 4, ...; two blocks requested ahead of each use
+    uint4 k0[D / 8], k1[D / 8];
+    const int nw = ne > wave ? (ne - wave + 3) / 4 : 0;
+    auto ent = [&](int t) { return wave + 4 * t; };
+    if (nw > 0) {
+        issue(ent(0), k0);
+        // k0's requests stay ahead of k1's (the waits count on that order)
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ent(1), k1);
+        int t = 0;
+        for (; t + 1 < nw; t += 2) {
+            Res r = compute(k0);
+            issue(ent(t + 2), k0);
+            store(ent(t), t, r);
+            r = compute(k1);
+            issue(ent(t + 3), k1);
+            store(ent(t + 1), t + 1, r);
+        }
+        if (t < nw) store(ent(t), t, compute(k0));
+    }
+    // the wave's results to global memory
+    for (int t = 0; t < nw; ++t) {
+        const int i = ent(t), b = blk(i);
+        const uint32_t pm = pmask(i);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
             if (!(pm & (1u << jj))) continue;
             const int h = g * G + jj;
-            const float s = (float)(a[jj] * (double)St.sm);
-            St.score16[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane] = s;
-            const float mx = wave_max_dpp(s);
-            const float l_ = tree64_f32_dpp(exp_c(s - mx));
-            if (lane == 0) St.st16[((size_t)n * Ly.Hq + h) * Ly.Nmax + b] = make_float2(mx, l_);
+            St.score16[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane] = sres[wave][t][jj][lane];
+            if (lane == 0) St.st16[((size_t)n * Ly.Hq + h) * Ly.Nmax + b] = sml[wave][t][jj];
         }
-    };
-    // two blocks in flight per wave
-    uint4 k0[D / 8], k1[D / 8];
-    uint32_t p0 = 0, p1 = 0;
-    int b = b0 + wave;
-    if (b < b1) {
-        p0 = pmask(b);
-        issue(b, p0, k0);
     }
-    for (; b < b1; b += 8) {
-        const bool more = b + 4 < b1;
-        if (more) {
-            p1 = pmask(b + 4);
-            issue(b + 4, p1, k1);
+}
+
+// ===========================================================================
+// Block lists of the value and FP16-key passes, one workgroup per (kv head,
+// sequence): the blocks of the sequence in ascending order whose selection
+// bits put them in P of some head (FP16 keys), in P without FP16 values for
+// some head (INT4 values at FP16-key weights), give FP16 values to some head
+// (the unfinished block, when there is one, ends this list), or leave some
+// head's block outside P and VP (the tail).
+// ===========================================================================
+template <int G>
+__global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St) {
+    const int g = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int len = __builtin_amdgcn_readfirstlane(Ly.len[St.layer * Ly.B + n]);
+    const int N = len / 64;
+    constexpr uint32_t ALL = (1u << G) - 1u;
+    const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
+    const uint32_t *sel = St.sel + ng * Ly.Nmax;
+    uint32_t *lst[WL_KINDS];
+#pragma unroll
+    for (int k = 0; k < WL_KINDS; ++k) lst[k] = St.wl + (k * nk + ng) * (size_t)(Ly.Nmax + 1);
+    __shared__ int wc[WL_KINDS][4];
+    int base[WL_KINDS] = {};
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int r0 = 0; r0 < N; r0 += 256) {
+        const int b = r0 + tid;
+        const uint32_t bits = b < N ? sel[b] : 0u;
+        const uint32_t pm = bits & ALL, vm = (bits >> 8) & ALL;
+        const bool f[WL_KINDS] = {pm != 0, (pm & ~vm) != 0, vm != 0, b < N && (pm | vm) != ALL};
+        uint64_t bal[WL_KINDS];
+#pragma unroll
+        for (int k = 0; k < WL_KINDS; ++k) {
+            bal[k] = __ballot(f[k]);
+            if (lane == 0) wc[k][wave] = __popcll(bal[k]);
         }
-        consume(b, p0, k0);
-        if (!more) break;
-        if (b + 8 < b1) {
-            p0 = pmask(b + 8);
-            issue(b + 8, p0, k0);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < WL_KINDS; ++k) {
+            int off = base[k], tot = 0;
+            for (int w = 0; w < 4; ++w) {
+                off += w < wave ? wc[k][w] : 0;
+                tot += wc[k][w];
+            }
+            if (f[k]) lst[k][off + __popcll(bal[k] & below)] = (uint32_t)b;
+            base[k] += tot;
         }
-        consume(b + 4, p1, k1);
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (len % 64) lst[WL_FP16][base[WL_FP16]++] = (uint32_t)N;
+#pragma unroll
+        for (int k = 0; k < WL_KINDS; ++k) St.wcnt[k * nk + ng] = base[k];
     }
 }
 
@@ -1739,9 +1855,18 @@ hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
     });
 }
 
+hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        (void)D;
+        hipLaunchKernelGGL((k_worklist<decltype(G)::value>), dim3(Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
+        return hipGetLastError();
+    });
+}
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        const int nsp = (St.nb + St.bps - 1) / St.bps;
+        // enough workgroups that none gets more than KEYS_MAXE list entries
+        const int per = St.bps < KEYS_MAXE ? St.bps : KEYS_MAXE;
+        const int nsp = (St.nb + per - 1) / per;
         if (nsp == 0) return hipSuccess;
         hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>),
                            dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq,

@@ -41,7 +41,9 @@ __device__ __forceinline__ float ru32(double x) {
 __device__ __forceinline__ float exp_c(float x) {
     float y = x * 1.44269502f;           // log2(e) in binary32: 0x3FB8AA3B
     float k = rintf(y);
-    if (k < -125.0f) return 0.0f;
+    // below 2^-125 the result is 0; selected at the end rather than branched
+    // on, so that the caller's loop has no lane-divergent paths
+    const bool under = k < -125.0f;
     float r = fmaf(-k, 0.693145751953125f, x);   // 0x3F317200
     r = fmaf(-k, 1.42860677e-06f, r);            // 0x35BFBE8E
     float p = 1.98412701e-04f;                   // 1/7!  0x39500D01
@@ -52,7 +54,7 @@ __device__ __forceinline__ float exp_c(float x) {
     p = fmaf(p, r, 0.5f);
     p = fmaf(p, r, 1.0f);
     p = fmaf(p, r, 1.0f);
-    return ldexpf(p, (int)k);
+    return under ? 0.0f : ldexpf(p, (int)k);
 }
 
 // Upper bound of e^x, x >= 0: halve to r <= 1/16, Taylor to degree 12,
@@ -156,9 +158,28 @@ __device__ __forceinline__ int wave_or_i32(int v) {
     return v;
 }
 
+// ---- buffer-resource loads ---------------------------------------------------
+// A buffer resource covers [base, base + bytes); a load at an offset past
+// the range returns zeros and touches no memory, so a load instruction can be
+// issued on every path (as a placeholder where there is nothing to load).
+// Word 3 of the resource: 32-bit data format, no swizzle, no index stride.
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+constexpr uint32_t RSRC_OOB = 0x40000000u;  // an offset past every range used
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float rsrc_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- DPP row operations (16-lane rows of a wave64) --------------------------
-// row_shl:n gives lane i the value of lane i + n of its row; lanes past the
-// end of the row keep their own value.  quad_perm / mirrors permute inside
+// row_shl:n gives lane i the value of lane i + n of its row, row_shr:n the
+// value of lane i - n; lanes whose source lies outside the row keep the
+// `old` operand (their own value, or 0 in the zero-filling forms).  quad_perm / mirrors permute inside
 // a row.  These run on the VALU without going through LDS.
 enum : int {
     DPP_QP_1032 = 0xB1,        // quad_perm [1,0,3,2]
@@ -167,6 +188,10 @@ enum : int {
     DPP_ROW_SL2 = 0x102,
     DPP_ROW_SL4 = 0x104,
     DPP_ROW_SL8 = 0x108,
+    DPP_ROW_SR1 = 0x111,
+    DPP_ROW_SR2 = 0x112,
+    DPP_ROW_SR4 = 0x114,
+    DPP_ROW_SR8 = 0x118,
     DPP_ROW_MIRROR = 0x140,
     DPP_ROW_HALF_MIRROR = 0x141,
 };
@@ -252,6 +277,96 @@ __device__ __forceinline__ float tree64_f32_dpp(float v) {
     v = v + __shfl_down(v, 32, 64);
     v = v + __shfl_down(v, 16, 64);
     return row_tree_f32(v);
+}
+
+// ---- 64-bit DPP helpers and order-free wave reductions ---------------------
+// (max, min, sum, or: any combination order gives the same result)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(v >> 32), (int)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// shifted copy inside the row with zero fill (row_shl / row_shr)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64_z(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32_z(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)v, l), hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+template <class Op>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t v, Op op) {
+    v = op(v, dpp_u64<DPP_QP_1032>(v));
+    v = op(v, dpp_u64<DPP_QP_2301>(v));
+    v = op(v, dpp_u64<DPP_ROW_HALF_MIRROR>(v));
+    v = op(v, dpp_u64<DPP_ROW_MIRROR>(v));
+    return op(op(readlane_u64(v, 0), readlane_u64(v, 16)), op(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+__device__ __forceinline__ uint64_t wave_sum_u64_dpp(uint64_t v) {
+    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a + b; });
+}
+__device__ __forceinline__ uint64_t wave_or_u64_dpp(uint64_t v) {
+    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a | b; });
+}
+__device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t v) {
+    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ double wave_max_f64_dpp(double v) {
+    v = fmax(v, dpp_f64<DPP_QP_1032>(v));
+    v = fmax(v, dpp_f64<DPP_QP_2301>(v));
+    v = fmax(v, dpp_f64<DPP_ROW_HALF_MIRROR>(v));
+    v = fmax(v, dpp_f64<DPP_ROW_MIRROR>(v));
+    auto rl = [&](int l) { return __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(v), l)); };
+    return fmax(fmax(rl(0), rl(16)), fmax(rl(32), rl(48)));
+}
+__device__ __forceinline__ int wave_sum_i32_dpp(int v) {
+    v = row_sum_i32(v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// Inclusive suffix sums over the 64 lanes (lane i gets sum of lanes >= i)
+// and exclusive prefix sums (lane i gets sum of lanes < i), exact integers.
+__device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t v, int lane) {
+    v += dpp_u64_z<DPP_ROW_SL1>(v);
+    v += dpp_u64_z<DPP_ROW_SL2>(v);
+    v += dpp_u64_z<DPP_ROW_SL4>(v);
+    v += dpp_u64_z<DPP_ROW_SL8>(v);
+    const uint64_t t1 = readlane_u64(v, 16), t2 = readlane_u64(v, 32), t3 = readlane_u64(v, 48);
+    const int r = lane >> 4;
+    return v + (r < 1 ? t1 : 0) + (r < 2 ? t2 : 0) + (r < 3 ? t3 : 0);
+}
+__device__ __forceinline__ uint64_t wave_prefix_excl_u64(uint64_t v, int lane) {
+    const uint64_t x = v;
+    v += dpp_u64_z<DPP_ROW_SR1>(v);
+    v += dpp_u64_z<DPP_ROW_SR2>(v);
+    v += dpp_u64_z<DPP_ROW_SR4>(v);
+    v += dpp_u64_z<DPP_ROW_SR8>(v);
+    const uint64_t t0 = readlane_u64(v, 15), t1 = readlane_u64(v, 31), t2 = readlane_u64(v, 47);
+    const int r = lane >> 4;
+    return v - x + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
+}
+__device__ __forceinline__ uint32_t wave_prefix_excl_u32(uint32_t v, int lane) {
+    const uint32_t x = v;
+    v += dpp_u32_z<DPP_ROW_SR1>(v);
+    v += dpp_u32_z<DPP_ROW_SR2>(v);
+    v += dpp_u32_z<DPP_ROW_SR4>(v);
+    v += dpp_u32_z<DPP_ROW_SR8>(v);
+    const uint32_t t0 = __builtin_amdgcn_readlane((int)v, 15), t1 = __builtin_amdgcn_readlane((int)v, 31),
+                   t2 = __builtin_amdgcn_readlane((int)v, 47);
+    const int r = lane >> 4;
+    return v - x + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
 }
 
 }  // namespace ckv

@@ -91,8 +91,17 @@ struct Step {
     int nsplit_cap;
     const uint16_t *stage_k, *stage_v;  // [B][Hkv][Nmax][64*d]
     double *qd;             // [B][Hkv][d][G] q in FP64 (written by the scoring pass)
+    // Block lists per (seq, kv head), ascending block index, WL_KINDS kinds
+    // at a stride of B*Hkv*(Nmax+1) entries: WL_KEYS blocks in P of some head
+    // (FP16 keys), WL_INT4 blocks in P of some head without FP16 values,
+    // WL_FP16 blocks with FP16 values for some head, then the unfinished
+    // block (index N) when there is one, WL_TAIL blocks outside P and VP for
+    // some head.  wcnt[kind][B][Hkv] = lengths.
+    uint32_t *wl;
+    int *wcnt;
     float *out;             // [batch][Hq][d]
 };
+enum { WL_KEYS = 0, WL_INT4 = 1, WL_FP16 = 2, WL_TAIL = 3, WL_KINDS = 4 };
 
 // Source of an exact dense attention: FP16 blocks of (seq n, kv head g) at
 // k + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
@@ -131,6 +140,7 @@ hipError_t launch_vrange(const Layout &Ly, int l, int n, const uint16_t *vin, in
 hipError_t launch_score(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStream_t s);
 hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s);
+hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq,
                            hipStream_t s);
