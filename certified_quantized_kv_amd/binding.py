@@ -39,14 +39,14 @@ class Thresholds(ctypes.Structure):
 
 
 class Profile(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 9), ("counts", ctypes.c_int * 9), ("steps", ctypes.c_int),
+    _fields_ = [("ms", ctypes.c_double * 10), ("counts", ctypes.c_int * 10), ("steps", ctypes.c_int),
                 ("bytes_paged", ctypes.c_uint64), ("copies", ctypes.c_uint64),
                 ("q8_blocks", ctypes.c_uint64), ("tail_blocks", ctypes.c_uint64),
                 ("k16_blocks", ctypes.c_uint64), ("v16_blocks", ctypes.c_uint64),
                 ("int4p_blocks", ctypes.c_uint64), ("dense_blocks", ctypes.c_uint64)]
 
 
-PHASES = ["score", "select", "tail", "page", "promoted", "fallback", "step", "merge", "keys16"]
+PHASES = ["score", "select", "tail", "page", "promoted4", "fallback", "step", "merge", "keys16", "promoted16"]
 
 
 REPORT_DTYPE = np.dtype([("e_key", "<f4"), ("e_val", "<f4"), ("tv_bound", "<f4"),

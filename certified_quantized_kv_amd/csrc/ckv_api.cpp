@@ -46,7 +46,7 @@ ckv_status fail(ckv_status st, const char *fmt, ...) {
                         __FILE__, __LINE__);                                                \
     } while (0)
 
-enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO, PH_FALLBACK, PH_STEP, PH_MERGE, PH_KEYS, PH_N = 9 };
+enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO4, PH_FALLBACK, PH_STEP, PH_MERGE, PH_KEYS, PH_PROMO16, PH_N = 10 };
 
 }  // namespace
 
@@ -89,7 +89,7 @@ struct ckv_cache {
     hipStream_t side[NSIDE] = {};
     hipEvent_t ev_side[NSIDE] = {};
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
-    hipEvent_t pev[13] = {};
+    hipEvent_t pev[14] = {};
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
     std::vector<int> seq_flags;               // [B] of the last step
     bool have_step = false;
@@ -617,7 +617,9 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     if (prof) HIPCHK(hipEventRecord(E[7], s));
     HIPCHK(launch_keys16(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[12], s));
-    HIPCHK(launch_promoted(Ly, St, c->dskip, s));
+    HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
+    if (prof) HIPCHK(hipEventRecord(E[13], s));
+    HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[11], s));
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, s));
     if (prof) HIPCHK(hipEventRecord(E[8], s));
@@ -738,7 +740,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         if (St.nsplit > 0) TRY(acc(PH_TAIL, 3, 4));
         TRY(acc(PH_PAGE, 5, 6));
         TRY(acc(PH_KEYS, 7, 12));
-        TRY(acc(PH_PROMO, 12, 11));
+        TRY(acc(PH_PROMO4, 12, 13));
+        TRY(acc(PH_PROMO16, 13, 11));
         TRY(acc(PH_MERGE, 11, 8));
         if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
         c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();

@@ -1875,12 +1875,17 @@ hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, 
     });
 }
 
-hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
+hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         const int nsp4 = (St.nb + St.bps - 1) / St.bps;
         if (nsp4 > 0)
             hipLaunchKernelGGL((k_promoted4<decltype(D)::value, decltype(G)::value>),
                                dim3(nsp4, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
+        return hipGetLastError();
+    });
+}
+hipError_t launch_promoted16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         const int nsp = (St.nb + 1 + St.bps - 1) / St.bps;
         hipLaunchKernelGGL((k_promoted16<decltype(D)::value, decltype(G)::value>),
                            dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);

@@ -142,8 +142,8 @@ hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStre
 hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
-hipError_t launch_promoted(const Layout &Ly, const Step &St, const int *skip_seq,
-                           hipStream_t s);
+hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
+hipError_t launch_promoted16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, const int *skip_seq,
                              uint32_t *plist, uint64_t *keys, hipStream_t s);
 hipError_t launch_dense_src(int d, int G, const DenseSrc &S, int nsplit, int batch,

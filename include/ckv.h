@@ -187,15 +187,16 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
 /* Profile of the decode steps since profiling was enabled (enabling resets
  * it).  Phase times are measured with HIP events on the streams the work
  * runs on: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
- * 3 page-in (the host-to-device copies on the side stream), 4 promoted
- * value pass (K4a), 5 fallback (paging + dense recompute), 6 the whole step
- * on the host wall clock, 7 rank check + merge (K4b), 8 FP16-key scoring of
- * the promoted blocks (K4a keys).  Block counts are what the
- * passes read, summed over steps: a block is one (sequence, kv head, 64
- * tokens).  Profiling adds a few event records per step. */
+ * 3 page-in (the host-to-device copies on the paging streams), 4 promoted
+ * value pass over INT4 values (K4a), 5 fallback (paging + dense recompute),
+ * 6 the whole step on the host wall clock, 7 rank check + merge (K4b),
+ * 8 FP16-key scoring of the promoted blocks (K4a keys), 9 promoted value
+ * pass over FP16 values (K4a).  Block counts are what the passes read,
+ * summed over steps: a block is one (sequence, kv head, 64 tokens).
+ * Profiling adds a few event records per step. */
 typedef struct {
-    double ms[9];           /* accumulated milliseconds per phase            */
-    int counts[9];          /* timed occurrences per phase                   */
+    double ms[10];          /* accumulated milliseconds per phase            */
+    int counts[10];         /* timed occurrences per phase                   */
     int steps;              /* decode steps profiled                         */
     uint64_t bytes_paged;   /* tier 2 -> staging bytes (with filled gaps)    */
     uint64_t copies;        /* host-to-device copies issued                  */
