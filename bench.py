@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default="llama_32k,needle_128k",
                     help="comma-separated workloads; the first one is the reported value")
     ap.add_argument("--layers", type=int, default=0, help="layers to build (0: the workload's)")
+    ap.add_argument("--decode-steps", type=int, default=4,
+                    help="decode-loop steps after the timed region, first workload only: one token "
+                         "appended to every sequence of every layer, then that layer's certified step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -71,7 +74,7 @@ def counters_for(kernel, workload):
     return rec.get("traffic_bytes_per_dispatch")
 
 
-def run_workload(name, args, cpu_baseline):
+def run_workload(name, args, cpu_baseline, decode_steps=0):
     import numpy as np
     import torch
 
@@ -84,7 +87,8 @@ def run_workload(name, args, cpu_baseline):
     dev = torch.device("cuda:0")
     log(f"workload {name}: {L} layers, batch {B}, context {T}, {Hq}/{Hkv} heads, d {d}")
     t0 = time.time()
-    cache = ckv.Cache(L, B, Hq, Hkv, d, T, device=0)
+    # room for the decode loop's tokens (one more block)
+    cache = ckv.Cache(L, B, Hq, Hkv, d, T + (64 if decode_steps else 0), device=0)
     fp = cache.footprint()
     log(f"cache created in {time.time() - t0:.1f}s: device {fp['device'] / 2**30:.2f} GiB "
         f"(tier 1 {fp['tier1'] / 2**30:.2f} GiB), pinned host {fp['host'] / 2**30:.2f} GiB")
@@ -201,6 +205,15 @@ def run_workload(name, args, cpu_baseline):
                    "v_tol": th["v_tol"], "rank_tol": th["rank_tol"]},
     }
 
+    if decode_steps:
+        rec["decode_loop"] = decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, decode_steps)
+        # the same loop with paged FP16 blocks kept in device memory across
+        # steps (the first step of each layer pages, later ones only new blocks)
+        free, _ = torch.cuda.mem_get_info()
+        nl = cache.enable_fp16_cache(int(free * 0.8))
+        rec["decode_loop_fp16_cache"] = dict(decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, decode_steps),
+                                             layers_cached=nl)
+
     if n_dense:
         for i in range(2 * n_dense):
             kb, vb = dense_kv[i % n_dense]
@@ -235,6 +248,49 @@ def run_workload(name, args, cpu_baseline):
     return rec
 
 
+def decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, steps):
+    """Steady-state decode: per step, one new token (synthetic K, V of the
+    workload's distributions, from device memory) appended to every sequence
+    of every layer, each layer's certified step right after its appends, a
+    fresh q per layer-step.  Timed from the first append to the last step."""
+    import torch
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(4321)
+    toks = [(torch.randn((steps * L, 1, Hkv, d), generator=gen, device=dev).half(),
+             torch.randn((steps * L, 1, Hkv, d), generator=gen, device=dev).half()) for _ in range(B)]
+    qs = (torch.randn((steps * L, B, Hq, d), generator=gen, device=dev) * cfg["q_std"]).half()
+    T0 = cache.seq_length(0, 0)
+    torch.cuda.synchronize()
+    t_app = 0.0
+    cache.set_profiling(True)
+    per_step = []
+    for s in range(steps):
+        t0 = time.perf_counter()
+        for l in range(L):
+            i = s * L + l
+            ta = time.perf_counter()
+            for n in range(B):
+                cache.append_kv(l, n, toks[n][0][i], toks[n][1][i])
+            t_app += time.perf_counter() - ta
+            cache.certified_decode_attention(l, qs[i], th, out=out)
+        torch.cuda.synchronize()
+        per_step.append(time.perf_counter() - t0)
+    prof = cache.profile()
+    cache.set_profiling(False)
+    el = sum(per_step)
+    ls = steps * L
+    log(f"decode loop: {steps} steps x {L} layers: {1e3 * el / ls:.3f} ms per layer-step "
+        f"({1e3 * t_app / ls:.3f} ms of appends), {B * steps / el:.2f} tokens/s; "
+        f"per step {[round(1e3 * x / L, 3) for x in per_step]} ms per layer-step")
+    return {"steps": steps, "layer_steps": ls, "context_start": T0, "context_end": T0 + steps,
+            "ms_per_layer_step": round(1e3 * el / ls, 4),
+            "ms_per_layer_step_by_step": [round(1e3 * x / L, 4) for x in per_step],
+            "append_ms_per_layer_step": round(1e3 * t_app / ls, 4),
+            "paged_MiB_per_layer_step": round(prof["bytes_paged"] / ls / 2 ** 20, 2),
+            "generated_tokens_per_s": round(B * steps / el, 3),
+            "kv_tokens_per_s": round(B * (T0 + steps / 2) * ls / el, 1)}
+
+
 def h2d_probe():
     import torch
     x = torch.empty(256 * 2 ** 20, dtype=torch.uint8).pin_memory()
@@ -258,7 +314,8 @@ def main():
     import torch
 
     names = [w for w in args.workload.split(",") if w]
-    recs = [run_workload(w, args, cpu_baseline=(i == 0 and not args.no_cpu_baseline))
+    recs = [run_workload(w, args, cpu_baseline=(i == 0 and not args.no_cpu_baseline),
+                         decode_steps=(args.decode_steps if i == 0 else 0))
             for i, w in enumerate(names)]
     first = recs[0]
     copy_probe = None

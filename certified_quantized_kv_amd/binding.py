@@ -14,7 +14,7 @@ CKV_STATUS = {0: "CKV_OK", 1: "CKV_EINVAL", 2: "CKV_ENOMEM", 3: "CKV_EHIP", 4: "
 EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv",
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
-            "ckv_set_profiling", "ckv_get_profile"]
+            "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache"]
 
 
 class CkvError(RuntimeError):
@@ -89,6 +89,7 @@ def lib():
                                       vp, vp, vp]
         L.ckv_set_profiling.argtypes = [vp, i32]
         L.ckv_get_profile.argtypes = [vp, ctypes.POINTER(Profile)]
+        L.ckv_enable_fp16_cache.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
         for name in EXPORTED:
             if name not in ("ckv_destroy", "ckv_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -163,6 +164,13 @@ class Cache:
         _check(lib().ckv_append_kv(self._h, layer, seq, ctypes.c_void_p(k.data_ptr()),
                                    ctypes.c_void_p(v.data_ptr()), k.shape[0], int(k.is_cuda),
                                    _stream_ptr(stream)))
+
+    def enable_fp16_cache(self, max_bytes):
+        """Keep paged FP16 blocks in device memory across steps for as many
+        layers (from layer 0) as max_bytes allows; returns that layer count."""
+        n = ctypes.c_int()
+        _check(lib().ckv_enable_fp16_cache(self._h, ctypes.c_size_t(int(max_bytes)), ctypes.byref(n)))
+        return n.value
 
     def seq_length(self, layer, seq):
         n = ctypes.c_int()

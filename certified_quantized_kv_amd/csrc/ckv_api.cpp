@@ -91,6 +91,11 @@ struct ckv_cache {
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
     hipEvent_t pev[14] = {};
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
+    // persistent FP16 mirror of layers 0 .. pcache_layers-1: blocks paged in
+    // once stay in HBM across steps (complete blocks never change)
+    int pcache_layers = 0;
+    std::vector<uint16_t *> pstage_k, pstage_v;
+    std::vector<std::vector<uint8_t>> pstaged_k, pstaged_v;
     std::vector<int> seq_flags;               // [B] of the last step
     bool have_step = false;
     int last_batch = 0, last_np = 0, last_nb = 0;
@@ -314,8 +319,41 @@ ckv_status ckv_reset_sequence(ckv_cache *c, int seq) {
         c->len[(size_t)l * c->cfg.max_batch + seq] = 0;
         c->h_len[(size_t)l * c->cfg.max_batch + seq] = 0;
     }
+    // the sequence's mirrored blocks are stale from now on
+    const size_t per_seq = (size_t)c->Ly.Hkv * c->Ly.Nmax;
+    for (int l = 0; l < c->pcache_layers; ++l) {
+        std::fill(c->pstaged_k[l].begin() + seq * per_seq, c->pstaged_k[l].begin() + (seq + 1) * per_seq, 0);
+        std::fill(c->pstaged_v[l].begin() + seq * per_seq, c->pstaged_v[l].begin() + (seq + 1) * per_seq, 0);
+    }
     HIPCHK(hipMemcpy(c->Ly.len, c->h_len, sizeof(int) * c->cfg.n_layers * c->cfg.max_batch,
                      hipMemcpyHostToDevice));
+    return CKV_OK;
+}
+
+ckv_status ckv_enable_fp16_cache(ckv_cache *c, size_t max_bytes, int *layers) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    if (c->pcache_layers) return fail(CKV_ESTATE, "the FP16 cache is already enabled");
+    HIPCHK(hipSetDevice(c->cfg.device));
+    const size_t sblk = (size_t)c->Ly.B * c->Ly.Hkv * c->Ly.Nmax;
+    const size_t per_layer = 2 * sblk * 64 * c->d * sizeof(uint16_t);
+    const int m = (int)std::min<size_t>((size_t)c->cfg.n_layers, max_bytes / per_layer);
+    // on an allocation failure the layers mirrored so far stay in use
+    for (int l = 0; l < m; ++l) {
+        uint16_t *k = nullptr, *v = nullptr;
+        ckv_status st = dalloc(c, &k, sblk * 64 * c->d);
+        if (st == CKV_OK) st = dalloc(c, &v, sblk * 64 * c->d);
+        if (st != CKV_OK) {
+            c->pcache_layers = l;
+            if (layers) *layers = l;
+            return st;
+        }
+        c->pstage_k.push_back(k);
+        c->pstage_v.push_back(v);
+        c->pstaged_k.emplace_back(sblk, 0);
+        c->pstaged_v.emplace_back(sblk, 0);
+    }
+    c->pcache_layers = m;
+    if (layers) *layers = m;
     return CKV_OK;
 }
 
@@ -537,8 +575,14 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.part_tail = c->part_tail;
     St.part_blk = c->part_blk;
     St.part_blk16 = c->part_blk16;
-    St.stage_k = c->stage_k;
-    St.stage_v = c->stage_v;
+    // staging of this layer: its persistent mirror, or the shared area
+    const bool pers = layer < c->pcache_layers;
+    uint16_t *stage_k = pers ? c->pstage_k[layer] : c->stage_k;
+    uint16_t *stage_v = pers ? c->pstage_v[layer] : c->stage_v;
+    std::vector<uint8_t> &staged_k = pers ? c->pstaged_k[layer] : c->staged_k;
+    std::vector<uint8_t> &staged_v = pers ? c->pstaged_v[layer] : c->staged_v;
+    St.stage_k = stage_k;
+    St.stage_v = stage_v;
     St.qd = c->qd;
     St.wl = c->wl;
     St.wcnt = c->wcnt;
@@ -575,8 +619,10 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
 
     // rung 4 before paging: a cap exhausted on any head of the sequence
     std::vector<uint8_t> wantk(Ly.Nmax), wantv(Ly.Nmax);
-    std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
-    std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
+    if (!pers) {
+        std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
+        std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
+    }
     size_t paged = 0;
     CopyList cl;
     if (prof) HIPCHK(hipEventRecord(E[5], c->side[0]));
@@ -602,8 +648,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 }
             }
             if (prof) c->pf.q8_blocks += N;
-            page_runs(c, layer, n, g, N, wantk.data(), c->staged_k, c->t2k, c->stage_k, cl);
-            page_runs(c, layer, n, g, N, wantv.data(), c->staged_v, c->t2v, c->stage_v, cl);
+            page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, cl);
+            page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
         }
     }
     TRY(issue_copies(c, cl));
@@ -653,8 +699,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 for (int j = 0; j < G; ++j) m |= (uint32_t)dense[(size_t)n * Hq + g * G + j] << j;
                 c->h_mask[n * Hkv + g] = m;
                 if (m) {
-                    page_runs(c, layer, n, g, N, all.data(), c->staged_k, c->t2k, c->stage_k, cl);
-                    page_runs(c, layer, n, g, N, all.data(), c->staged_v, c->t2v, c->stage_v, cl);
+                    page_runs(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, cl);
+                    page_runs(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, cl);
                     if (prof) c->pf.dense_blocks += N;
                 }
             }
@@ -667,8 +713,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
         HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
         DenseSrc S{};
-        S.k = c->stage_k;
-        S.v = c->stage_v;
+        S.k = stage_k;
+        S.v = stage_v;
         S.kp = Ly.kpart + Ly.seqg(layer, 0, 0) * c->blk_fp16;
         S.vp = Ly.vpart + Ly.seqg(layer, 0, 0) * c->blk_fp16;
         S.len = Ly.len + (size_t)layer * cf.max_batch;

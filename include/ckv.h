@@ -184,6 +184,19 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
                            float *mref, uint64_t *mfx, uint32_t *sel, uint64_t *m16fx,
                            double *bounds, int *seq_flags);
 
+/* Device-resident FP16 block cache across steps (a "next" step beyond the
+ * page's design, which names host-to-device paging traffic as the main
+ * overhead): FP16 K and V blocks paged in for layer l stay in HBM for the
+ * following steps of layer l, so a block is copied from tier 2 at most once
+ * while it stays complete (blocks are immutable; ckv_reset_sequence drops a
+ * sequence's blocks).  Layers 0 .. m-1 get a persistent mirror of their
+ * staging area, m = min(n_layers, max_bytes / (2 * max_batch * n_kv_heads *
+ * ceil(max_context/64) * 64 * head_dim * 2 bytes)); the other layers page
+ * every step as before.  *layers receives m.  Results are identical with and
+ * without the cache.  Errors: EINVAL (null cache), ESTATE (already enabled),
+ * ENOMEM (device memory: the layers mirrored so far stay enabled). */
+ckv_status ckv_enable_fp16_cache(ckv_cache *c, size_t max_bytes, int *layers);
+
 /* Profile of the decode steps since profiling was enabled (enabling resets
  * it).  Phase times are measured with HIP events on the streams the work
  * runs on: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
