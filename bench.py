@@ -205,6 +205,29 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
                    "v_tol": th["v_tol"], "rank_tol": th["rank_tol"]},
     }
 
+    # the same layer-steps with device-initiated paging (a kernel reading
+    # pinned host memory instead of host-issued copies): a comparison line
+    cache.set_device_paging(True)
+    Kd = min(args.steps, L)
+    for i in range(min(args.warmup, 4)):
+        cache.certified_decode_attention(i % L, qs[i % L], th, out=out)
+    torch.cuda.synchronize()
+    cache.set_profiling(True)
+    t1 = time.perf_counter()
+    for i in range(Kd):
+        l = (args.warmup + i) % L
+        cache.certified_decode_attention(l, qs[l], th, out=out)
+    torch.cuda.synchronize()
+    eld = time.perf_counter() - t1
+    profd = cache.profile()
+    cache.set_profiling(False)
+    cache.set_device_paging(False)
+    rec["device_paging"] = {"steps": Kd, "ms_per_step": round(1e3 * eld / Kd, 4),
+                            "value": round(B * T * Kd / eld, 1),
+                            "paged_MiB_per_step": round(profd["bytes_paged"] / Kd / 2 ** 20, 2),
+                            "page_ms_per_step": round(profd["phases"]["page"][0] / Kd, 4)}
+    log(f"device paging: {1e3 * eld / Kd:.3f} ms/step")
+
     if decode_steps:
         rec["decode_loop"] = decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, decode_steps)
         # the same loop with paged FP16 blocks kept in device memory across

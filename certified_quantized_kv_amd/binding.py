@@ -14,7 +14,8 @@ CKV_STATUS = {0: "CKV_OK", 1: "CKV_EINVAL", 2: "CKV_ENOMEM", 3: "CKV_EHIP", 4: "
 EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv",
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
-            "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache"]
+            "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache",
+            "ckv_set_device_paging"]
 
 
 class CkvError(RuntimeError):
@@ -90,6 +91,7 @@ def lib():
         L.ckv_set_profiling.argtypes = [vp, i32]
         L.ckv_get_profile.argtypes = [vp, ctypes.POINTER(Profile)]
         L.ckv_enable_fp16_cache.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
+        L.ckv_set_device_paging.argtypes = [vp, i32]
         for name in EXPORTED:
             if name not in ("ckv_destroy", "ckv_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -164,6 +166,11 @@ class Cache:
         _check(lib().ckv_append_kv(self._h, layer, seq, ctypes.c_void_p(k.data_ptr()),
                                    ctypes.c_void_p(v.data_ptr()), k.shape[0], int(k.is_cuda),
                                    _stream_ptr(stream)))
+
+    def set_device_paging(self, enable=True):
+        """Page FP16 blocks with a device kernel reading pinned host memory
+        (True) or with host-issued copies (False, the default)."""
+        _check(lib().ckv_set_device_paging(self._h, int(bool(enable))))
 
     def enable_fp16_cache(self, max_bytes):
         """Keep paged FP16 blocks in device memory across steps for as many

@@ -94,6 +94,11 @@ struct ckv_cache {
     // persistent FP16 mirror of layers 0 .. pcache_layers-1: blocks paged in
     // once stay in HBM across steps (complete blocks never change)
     int pcache_layers = 0;
+    // paging by the device (a kernel reading tier 2 over the host link)
+    // instead of host-issued copies; the device addresses of tier 2
+    bool device_gather = false;
+    const uint16_t *t2k_dev = nullptr, *t2v_dev = nullptr;
+    hipEvent_t ev_wl = nullptr;
     std::vector<uint16_t *> pstage_k, pstage_v;
     std::vector<std::vector<uint8_t>> pstaged_k, pstaged_v;
     std::vector<int> seq_flags;               // [B] of the last step
@@ -121,7 +126,9 @@ template <class T>
 ckv_status halloc(ckv_cache *c, T **p, size_t count, bool tier2 = false) {
     void *ptr = nullptr;
     size_t bytes = std::max<size_t>(count * sizeof(T), 64);
-    hipError_t e = hipHostMalloc(&ptr, bytes, hipHostMallocDefault);
+    // tier 2 is also mapped into the device's address space (read by the
+    // device-initiated paging kernel)
+    hipError_t e = hipHostMalloc(&ptr, bytes, tier2 ? hipHostMallocMapped : hipHostMallocDefault);
     if (e != hipSuccess)
         return fail(CKV_ENOMEM, "hipHostMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
     if (tier2) c->host_bytes += bytes;
@@ -200,7 +207,7 @@ void ckv_destroy(ckv_cache *c) {
         if (st) (void)hipStreamDestroy(st);
     for (hipEvent_t e : c->ev_side)
         if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done})
+    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl})
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->pev)
         if (e) (void)hipEventDestroy(e);
@@ -304,6 +311,14 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         HIPCHK(hipEventCreateWithFlags(&c->ev_side[k], hipEventDisableTiming));
     }
     HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_wl, hipEventDisableTiming));
+    {
+        void *pk = nullptr, *pv = nullptr;
+        HIPCHK(hipHostGetDevicePointer(&pk, c->t2k, 0));
+        HIPCHK(hipHostGetDevicePointer(&pv, c->t2v, 0));
+        c->t2k_dev = static_cast<const uint16_t *>(pk);
+        c->t2v_dev = static_cast<const uint16_t *>(pv);
+    }
     HIPCHK(hipEventCreateWithFlags(&c->ev_paged, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming));
     for (auto &e : c->pev) HIPCHK(hipEventCreate(&e));
@@ -354,6 +369,12 @@ ckv_status ckv_enable_fp16_cache(ckv_cache *c, size_t max_bytes, int *layers) {
     }
     c->pcache_layers = m;
     if (layers) *layers = m;
+    return CKV_OK;
+}
+
+ckv_status ckv_set_device_paging(ckv_cache *c, int enable) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    c->device_gather = enable != 0;
     return CKV_OK;
 }
 
@@ -581,6 +602,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     uint16_t *stage_v = pers ? c->pstage_v[layer] : c->stage_v;
     std::vector<uint8_t> &staged_k = pers ? c->pstaged_k[layer] : c->staged_k;
     std::vector<uint8_t> &staged_v = pers ? c->pstaged_v[layer] : c->staged_v;
+    const bool gather = c->device_gather && !pers;
     St.stage_k = stage_k;
     St.stage_v = stage_v;
     St.qd = c->qd;
@@ -612,6 +634,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     // block lists of the value passes; K3: tail blocks; both overlap the
     // host's page lists and the paging below
     HIPCHK(launch_worklist(Ly, St, s));
+    HIPCHK(hipEventRecord(c->ev_wl, s));
     if (prof) HIPCHK(hipEventRecord(E[3], s));
     if (St.nsplit > 0) HIPCHK(launch_tail(Ly, St, s));
     if (prof) HIPCHK(hipEventRecord(E[4], s));
@@ -648,14 +671,27 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 }
             }
             if (prof) c->pf.q8_blocks += N;
+            if (gather && !skip) {
+                // the device copies this (seq, kv head)'s listed blocks itself
+                for (int b = 0; b < N; ++b) paged += (size_t)(wantk[b] + wantv[b]) * c->blk_fp16 * 2;
+                continue;
+            }
             page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, cl);
             page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
         }
     }
+    if (gather) {
+        // the skip flags first (the kernel leaves skipped sequences to the
+        // copies), the block lists from the worklist kernel
+        HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
+        HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_wl, 0));
+        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, c->side[0]));
+    }
     TRY(issue_copies(c, cl));
     paged += cl.bytes;
     if (prof) c->pf.copies += cl.size.size();
-    HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
+    if (!gather)
+        HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
     if (prof) HIPCHK(hipEventRecord(E[6], c->side[0]));
     HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));

@@ -1388,6 +1388,53 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
 }
 
 // ===========================================================================
+// Device-initiated paging (a measured alternative to host-issued copies):
+// the FP16 K blocks of the P lists and the FP16 V blocks of the VP lists,
+// read from tier 2 (pinned host memory mapped into the device's address
+// space) over the host link and written to the staging area, only the
+// listed blocks (no gap fill) and no per-copy overhead.  One workgroup per
+// (slice, kv head, sequence); wave w of slice x takes list entries
+// 4x + w, 4x + w + 4*GATHER_X, ...; a wave moves a 64-token block as D/8
+// 16-byte loads per lane.  Skipped sequences (rung 4 before paging) are left
+// to the host's copies.
+// ===========================================================================
+constexpr int GATHER_X = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *skip_seq, const uint16_t *t2k,
+                                                const uint16_t *t2v, uint16_t *stk, uint16_t *stv) {
+    const int x = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (skip_seq[n]) return;
+    const int l = St.layer;
+    const int N = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]) / 64;
+    const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
+    const int W = GATHER_X * 4;
+    constexpr int NL = D / 8;  // 16-byte loads per lane per block
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {
+        const int lk = kind == 0 ? WL_KEYS : WL_FP16;
+        const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[lk * nk + ng]);
+        const uint32_t *lst = St.wl + (lk * nk + ng) * (size_t)(Ly.Nmax + 1);
+        const uint16_t *src = kind == 0 ? t2k : t2v;
+        uint16_t *dst = kind == 0 ? stk : stv;
+        for (int i = x * 4 + wave; i < cnt; i += W) {
+            const int b = __builtin_amdgcn_readfirstlane(lst[i]);
+            if (b >= N) continue;  // the unfinished block stays on the device
+            const uint4 *sp = reinterpret_cast<const uint4 *>(src + Ly.blk(l, n, g, b) * 64 * D);
+            uint4 *dp = reinterpret_cast<uint4 *>(dst + (ng * Ly.Nmax + b) * 64 * D);
+            // streaming loads (not kept in the caches: a reset sequence's
+            // tier-2 blocks get new contents later)
+            v4u32 r[NL];
+#pragma unroll
+            for (int c = 0; c < NL; ++c) r[c] = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(sp) + c * 64 + lane);
+#pragma unroll
+            for (int c = 0; c < NL; ++c) dp[c * 64 + lane] = make_uint4(r[c].x, r[c].y, r[c].z, r[c].w);
+        }
+    }
+}
+
+// ===========================================================================
 // Block lists of the value and FP16-key passes, one workgroup per (kv head,
 // sequence): the blocks of the sequence in ascending order whose selection
 // bits put them in P of some head (FP16 keys), in P without FP16 values for
@@ -1855,6 +1902,15 @@ hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
     });
 }
 
+hipError_t launch_gather(const Layout &Ly, const Step &St, const int *skip_seq, const uint16_t *t2k,
+                         const uint16_t *t2v, uint16_t *stk, uint16_t *stv, hipStream_t s) {
+    return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
+        (void)G;
+        hipLaunchKernelGGL((k_gather<decltype(D)::value>), dim3(GATHER_X, Ly.Hkv, St.batch), dim3(256), 0, s,
+                           Ly, St, skip_seq, t2k, t2v, stk, stv);
+        return hipGetLastError();
+    });
+}
 hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         (void)D;

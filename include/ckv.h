@@ -197,6 +197,17 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
  * ENOMEM (device memory: the layers mirrored so far stay enabled). */
 ckv_status ckv_enable_fp16_cache(ckv_cache *c, size_t max_bytes, int *layers);
 
+/* Paging by the device instead of host-issued copies (a measured
+ * alternative to the design's hipMemcpyAsync paging): a kernel reads the
+ * listed FP16 blocks straight from tier 2 (pinned host memory mapped into
+ * the device's address space) into the staging area: only the needed
+ * blocks cross the host link (no gap fill) and there is no per-copy cost.
+ * Results are identical.  Layers with the FP16 cache enabled, sequences
+ * skipped by rung 4 before paging and the dense fallback keep using the
+ * copies.  enable: 0 host copies (default), 1 device paging.
+ * Errors: EINVAL (null cache). */
+ckv_status ckv_set_device_paging(ckv_cache *c, int enable);
+
 /* Profile of the decode steps since profiling was enabled (enabling resets
  * it).  Phase times are measured with HIP events on the streams the work
  * runs on: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
