@@ -228,6 +228,9 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
                             "page_ms_per_step": round(profd["phases"]["page"][0] / Kd, 4)}
     log(f"device paging: {1e3 * eld / Kd:.3f} ms/step")
 
+    if n_dense:
+        rec["variants"] = variants(cache, dense_kv, qs, th, T, sm, n_dense)
+
     if decode_steps:
         rec["decode_loop"] = decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, decode_steps)
         # the same loop with paged FP16 blocks kept in device memory across
@@ -269,6 +272,49 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
                       f"({T} tokens, {Hq} q heads), {cs:.1f} s single-threaded"}
         log(f"cpu baseline: {cs:.1f}s for the sample")
     return rec
+
+
+def variants(cache, dense_kv, qs, th, T, sm, n):
+    """The documented variants on the first n layers, each against exact dense
+    attention on the FP16 originals: the certified step; plain quantized
+    attention (tau_cov = 0, infinite tolerances: no FP16 blocks, its bounds
+    still reported); FP16 values for every promoted head (v_tol = 0); and a
+    v_tol sweep."""
+    import numpy as np
+    import torch
+    inf = float("inf")
+    cases = [("certified", dict(th)),
+             ("naive_int8_int4", dict(th, tau_cov=0.0, k_tol=inf, v_tol=inf)),
+             ("fp16_values", dict(th, v_tol=0.0)),
+             ("v_tol_0.1", dict(th, v_tol=0.1)),
+             ("v_tol_0.001", dict(th, v_tol=1e-3))]
+    dense = []
+    for l in range(n):
+        kb, vb = dense_kv[l]
+        dense.append(cache.dense_decode_attention(kb, vb, T, qs[l], sm).clone())
+    res = {}
+    for tag, thv in cases:
+        cache.set_profiling(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        outs = [cache.certified_decode_attention(l, qs[l], thv) for l in range(n)]
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t1
+        pr = cache.profile()
+        cache.set_profiling(False)
+        err = max(float((o - dense[l]).abs().max()) for l, (o, _) in enumerate(outs))
+        reps = [r for _, r in outs]
+        res[tag] = {"ms_per_step": round(1e3 * el / n, 4),
+                    "paged_MiB_per_step": round(pr["bytes_paged"] / n / 2 ** 20, 2),
+                    "max_abs_err_vs_dense": float(f"{err:.3g}"),
+                    "e_key_max": float(f"{max(float(r['e_key'].max()) for r in reps):.3g}"),
+                    "e_val_max": float(f"{max(float(r['e_val'].max()) for r in reps):.3g}"),
+                    "kstar_mean": round(float(np.mean([r["kstar"].mean() for r in reps])), 2),
+                    "v_promoted_mean": round(float(np.mean([r["n_v_promoted"].mean() for r in reps])), 2),
+                    "rungs_max_hist": np.bincount(np.concatenate([r["rung_max"].ravel() for r in reps]),
+                                                  minlength=5).tolist()}
+        log(f"variant {tag}: {res[tag]}")
+    return res
 
 
 def decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, steps):

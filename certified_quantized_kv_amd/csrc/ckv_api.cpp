@@ -558,7 +558,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     if (layer < 0 || layer >= cf.n_layers || batch < 1 || batch > cf.max_batch || !q || !th || !out ||
         !report)
         return fail(CKV_EINVAL, "bad layer, batch or null pointer");
-    if (!(th->tau_cov > 0.0f && th->tau_cov <= 1.0f) || !(th->sm_scale > 0.0f) ||
+    if (!(th->tau_cov >= 0.0f && th->tau_cov <= 1.0f) || !(th->sm_scale > 0.0f) ||
         !std::isfinite(th->sm_scale) || th->n_widen < 0 || std::isnan(th->k_tol) ||
         std::isnan(th->v_tol) || std::isnan(th->rank_tol) || std::isnan(th->f_layer))
         return fail(CKV_EINVAL, "bad thresholds");

@@ -59,7 +59,9 @@ typedef struct {
 
 /* Thresholds of the certified decode step [Meth-3, Results].
  * tau_cov: coverage of the estimated attention mass by the blocks whose
- *   FP16 keys are paged in (the page's example: 0.995).
+ *   FP16 keys are paged in (the page's example: 0.995), in [0, 1].  0 pages
+ *   no FP16 keys: with k_tol and v_tol infinite the step is plain quantized
+ *   attention (INT8 keys, INT4 values) and E_key, E_val bound its error.
  * k_tol / v_tol: tolerances on E_key / E_val, in output units.
  * rank_tol: the rank check fails when more than floor(rank_tol * K*(K*-1)/2)
  *   pairs of promoted blocks are ordered differently by INT8 and FP16 keys.

@@ -167,6 +167,7 @@ THRESHOLD_CASES = [
     dict(rank_tol=-1.0, f_layer=0.5),             # rung 4 after the rank check
     dict(k_tol=2e-4),                             # rung 1 widening
     dict(tau_cov=1.0, v_tol=0.0, k_tol=1.0),      # everything promoted
+    dict(tau_cov=0.0, k_tol=float("inf"), v_tol=float("inf")),   # plain INT8/INT4 attention
 ]
 
 

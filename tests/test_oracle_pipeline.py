@@ -78,6 +78,29 @@ def test_bounds_dominate_measured_errors(seed):
     assert np.all(r.report["e_key"] >= ek) and np.all(r.report["e_val"] >= ev)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_naive_quantized_mode_is_bounded(seed):
+    """tau_cov = 0 with infinite tolerances: no FP16 keys or values (only the
+    unfinished block stays exact), the output is plain INT8/INT4 attention,
+    and its distance to exact attention is still within E_key + E_val."""
+    kind = KINDS[seed % len(KINDS)]
+    T = [512, 1000, 130][seed % 3]
+    k, v, q, sm = micro(100 + seed, T=T, Hq=8, Hkv=2, kind=kind)
+    th = oracle.default_thresholds(sm, tau_cov=0.0, k_tol=float("inf"), v_tol=float("inf"), rank_tol=1.0)
+    r = oracle.certified_decode(k, v, q, th)
+    assert np.all(r.report["kstar"] == 0) and np.all(r.report["n_v_promoted"] == 0)
+    assert np.all(r.report["rung_max"] == 0)
+    tr = r.trace
+    N = T // 64
+    assert not np.any(tr["sel"][..., :N])          # no block of P or VP
+    ek, ev = tr["bounds"][..., 2], tr["bounds"][..., 3]
+    dist = np.abs(r.out - tr["o_dense"]).max(axis=2)
+    assert np.all(dist <= ek + ev + 1e-12)
+    # the certified step at the default thresholds is closer to exact
+    rc = oracle.certified_decode(k, v, q, oracle.default_thresholds(sm, rank_tol=1.0))
+    assert np.abs(rc.out - tr["o_dense"]).max() <= dist.max() + 1e-12
+
+
 def test_eta_mutation_breaks_value_dominance():
     """Mutation: with eta_b forced to 0 the value bound collapses to 0 while
     the measured INT4 error is not 0: the dominance test has teeth."""
