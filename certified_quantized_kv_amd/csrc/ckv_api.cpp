@@ -87,9 +87,9 @@ struct ckv_cache {
     // paging streams: host-issued copies spread over several streams so that
     // the per-copy latency of one stream overlaps the others'
     hipStream_t side[NSIDE] = {};
-    hipEvent_t ev_side[NSIDE] = {};
+    hipEvent_t ev_side[NSIDE] = {}, ev_kside[NSIDE] = {};
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
-    hipEvent_t pev[14] = {};
+    hipEvent_t pev[15] = {};
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
     // persistent FP16 mirror of layers 0 .. pcache_layers-1: blocks paged in
     // once stay in HBM across steps (complete blocks never change)
@@ -207,6 +207,8 @@ void ckv_destroy(ckv_cache *c) {
         if (st) (void)hipStreamDestroy(st);
     for (hipEvent_t e : c->ev_side)
         if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->ev_kside)
+        if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl})
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->pev)
@@ -309,6 +311,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     for (int k = 0; k < NSIDE; ++k) {
         HIPCHK(hipStreamCreateWithFlags(&c->side[k], hipStreamNonBlocking));
         HIPCHK(hipEventCreateWithFlags(&c->ev_side[k], hipEventDisableTiming));
+        HIPCHK(hipEventCreateWithFlags(&c->ev_kside[k], hipEventDisableTiming));
     }
     HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_wl, hipEventDisableTiming));
@@ -510,8 +513,9 @@ static batch_fn batch_copy() {
 
 // Issue a paging round over the paging streams (each run to the stream with
 // the fewest bytes so far; per stream one batched call when the runtime has
-// it, else one hipMemcpyAsync per run), then join them on side[0].
-static ckv_status issue_copies(ckv_cache *c, CopyList &cl) {
+// it, else one hipMemcpyAsync per run), then, if `join`, join them on
+// side[0].
+static ckv_status issue_copies(ckv_cache *c, CopyList &cl, bool join = true) {
     if (cl.size.empty()) return CKV_OK;
     CopyList per[NSIDE];
     size_t load[NSIDE] = {};
@@ -537,7 +541,7 @@ static ckv_status issue_copies(ckv_cache *c, CopyList &cl) {
             for (size_t i = 0; i < q.size.size(); ++i)
                 HIPCHK(hipMemcpyAsync(q.dst[i], q.src[i], q.size[i], hipMemcpyHostToDevice, c->side[k]));
         }
-        if (k > 0) {
+        if (k > 0 && join) {
             HIPCHK(hipEventRecord(c->ev_side[k], c->side[k]));
             HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_side[k], 0));
         }
@@ -647,7 +651,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
     }
     size_t paged = 0;
-    CopyList cl;
+    CopyList cl, clk;  // V runs (and the fallback's), K runs
     if (prof) HIPCHK(hipEventRecord(E[5], c->side[0]));
     const uint32_t allg = (1u << G) - 1u;
     for (int n = 0; n < batch; ++n) {
@@ -676,10 +680,12 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                 for (int b = 0; b < N; ++b) paged += (size_t)(wantk[b] + wantv[b]) * c->blk_fp16 * 2;
                 continue;
             }
-            page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, cl);
+            page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, clk);
             page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
         }
     }
+    if (!gather)
+        HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
     if (gather) {
         // the skip flags first (the kernel leaves skipped sequences to the
         // copies), the block lists from the worklist kernel
@@ -687,20 +693,26 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_wl, 0));
         HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, c->side[0]));
     }
+    // K runs first: the FP16-key pass and the INT4 promoted pass need only
+    // them and run while the V runs are copied
+    TRY(issue_copies(c, clk, false));
+    for (int k = 0; k < NSIDE; ++k) {
+        HIPCHK(hipEventRecord(c->ev_kside[k], c->side[k]));
+        HIPCHK(hipStreamWaitEvent(s, c->ev_kside[k], 0));
+    }
     TRY(issue_copies(c, cl));
-    paged += cl.bytes;
-    if (prof) c->pf.copies += cl.size.size();
-    if (!gather)
-        HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
+    paged += cl.bytes + clk.bytes;
+    if (prof) c->pf.copies += cl.size.size() + clk.size.size();
     if (prof) HIPCHK(hipEventRecord(E[6], c->side[0]));
     HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
-    HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
     // K4: promoted blocks, rank check, merge
     if (prof) HIPCHK(hipEventRecord(E[7], s));
     HIPCHK(launch_keys16(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[12], s));
     HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[13], s));
+    HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
+    if (prof) HIPCHK(hipEventRecord(E[14], s));
     HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[11], s));
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, s));
@@ -823,7 +835,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         TRY(acc(PH_PAGE, 5, 6));
         TRY(acc(PH_KEYS, 7, 12));
         TRY(acc(PH_PROMO4, 12, 13));
-        TRY(acc(PH_PROMO16, 13, 11));
+        TRY(acc(PH_PROMO16, 14, 11));
         TRY(acc(PH_MERGE, 11, 8));
         if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
         c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
 // K2: selection, bounds, rungs 1-2 [Meth-2, Meth-3, Contrib].
 // One SEL_T-thread workgroup per (q head, sequence).
 // ===========================================================================
-constexpr int SEL_T = 512;
+constexpr int SEL_T = 1024;
 constexpr int MAX_BPS = 64;
 constexpr int SEL_LDS = 2048;  // blocks per head whose selection keys stay in LDS  // blocks per split, at most (the host keeps bps in [4, 64])
 
@@ -426,6 +426,9 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
     uint64_t lo = kmin, hi = kmax;
     uint64_t outside = 0;  // TOP: sum above [lo, hi]; REST: sum below
     uint32_t sat_out = 0;
+    // the first pass buckets by value octave when the values span more than
+    // 64x (linear buckets would put nearly every key in the lowest bucket)
+    bool logp = ((kmax >> 16) >> 6) > (kmin >> 16);
     for (;;) {
         const uint64_t span = hi - lo;  // >= 0
         const int shift = span >> 6 ? 58 - __builtin_clzll(span) : 0;  // (span >> shift) < 64
@@ -437,15 +440,37 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
             sh.hcnt[tid] = 0;
         }
         __syncthreads();
-        for (int b = tid; b < N; b += SEL_T) {
-            const uint64_t v = val[b];
-            const uint64_t key = (v << 16) | (uint64_t)(0xFFFF - b);
-            if (key >= lo && key <= hi) {
-                const int dg = (int)((key - lo) >> shift);
+        for (int r0 = 0; r0 < N; r0 += SEL_T) {
+            const int b = r0 + tid;
+            uint64_t v = 0, key = 0;
+            bool act = false;
+            int dg = 0;
+            if (b < N) {
+                v = val[b];
+                key = (v << 16) | (uint64_t)(0xFFFF - b);
+                act = key >= lo && key <= hi;
+                dg = logp ? (v ? 64 - __builtin_clzll(v) : 0) : (int)((key - lo) >> shift);
+            }
+            const uint64_t am = __ballot(act);
+            if (!am) continue;
+            const int first = __builtin_ctzll(am);
+            const int d0 = __builtin_amdgcn_readlane(dg, first);
+            if (__ballot(act && dg != d0) == 0) {
+                // the wave's keys share one bucket: one update for the wave
+                // (same-address atomics from every lane would serialize)
+                const uint64_t sw = wave_sum_u64_dpp(act ? v : 0);
+                const uint32_t ns = (uint32_t)__popcll(__ballot(act && !TOP && v >= FXCAP));
+                if (lane == first) {
+                    atomicAdd((unsigned long long *)&sh.hsum[d0], (unsigned long long)sw);
+                    atomicAdd(&sh.hcnt[d0], (uint32_t)__popcll(am));
+                    if (ns) atomicAdd(&sh.hsat[d0], ns);
+                    sh.hkey[d0] = key;  // read only when the bucket holds one key
+                }
+            } else if (act) {
                 atomicAdd((unsigned long long *)&sh.hsum[dg], (unsigned long long)v);
-                atomicMax((unsigned long long *)&sh.hkey[dg], (unsigned long long)key);
                 atomicAdd(&sh.hcnt[dg], 1u);
                 if (!TOP && v >= FXCAP) atomicAdd(&sh.hsat[dg], 1u);
+                sh.hkey[dg] = key;
             }
         }
         __syncthreads();
@@ -488,7 +513,17 @@ __device__ __forceinline__ uint64_t radix_select(P val, int N, uint64_t need, do
         const uint64_t kk = sh.bc_u[2];
         // the threshold: a single key in the chosen bucket whose exclusion was
         // tested, or the key value itself once buckets are single values
-        if ((cnt == 1 && best < 63) || shift == 0) return shift == 0 ? lo + (uint64_t)best : kk;
+        if (cnt == 1 && best < 63) return kk;
+        if (logp) {
+            // octave `best` holds the values [2^(best-1), 2^best) (0: value 0)
+            const uint64_t olo = best ? (1ull << (best - 1)) << 16 : 0;
+            const uint64_t ohi = best ? ((1ull << best) << 16) - 1 : 0xFFFFull;
+            lo = olo > lo ? olo : lo;
+            hi = ohi < hi ? ohi : hi;
+            logp = false;
+            continue;
+        }
+        if (shift == 0) return lo + (uint64_t)best;
         const uint64_t nlo = lo + ((uint64_t)best << shift);
         const uint64_t nhi = nlo + ((1ull << shift) - 1);
         lo = nlo;
