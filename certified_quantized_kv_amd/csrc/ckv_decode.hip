@@ -1545,56 +1545,83 @@ __device__ __forceinline__ int count_greater(const uint64_t *r, int n, uint64_t 
 }
 
 // Kendall discordant pairs between two orders of the same K <= RANK_LDS items
-// given as unique keys (kI[i], k16[i]): sort by kI descending (bitonic, in
-// LDS), then merge-sort the k16 sequence descending, counting for every
-// element of a right run the elements of the left run smaller than it.
-// Exact integer result, independent of the thread count.  Uses and
-// overwrites kI, k16; tmp holds RANK_LDS entries.  All threads call it.
+// given as unique keys (kI[i], k16[i]) whose low 16 bits are 0xFFFF - i:
+// sort kI descending (bitonic, in LDS), gather the k16 keys in that order,
+// then merge-sort them descending, counting for every element of a right run
+// the elements of the left run smaller than it.  Exact integer result,
+// independent of the thread count.  Wave w owns elements [128w, 128w + 128):
+// sort stages with stride <= 64 and merge passes with runs <= 64 stay inside
+// a wave (no workgroup barrier).  Uses and overwrites kI, k16, tmp (RANK_LDS
+// entries each).  All threads call it.
 __device__ __forceinline__ long long discordant_sorted(uint64_t *kI, uint64_t *k16, uint64_t *tmp, int K) {
     const int tid = threadIdx.x;
-    int Kp = 1;
-    while (Kp < K) Kp <<= 1;
-    for (int i = K + tid; i < Kp; i += MERGE_T) {
-        kI[i] = 0;   // real keys are >= 1 after the shift below: padding sorts last
-        k16[i] = 0;
+    int Kp = 1, lgKp = 0;
+    while (Kp < K) {
+        Kp <<= 1;
+        ++lgKp;
     }
+    for (int i = K + tid; i < Kp; i += MERGE_T) kI[i] = 0;  // padding sorts last (real keys are > 0 after +1)
     for (int i = tid; i < K; i += MERGE_T) kI[i] += 1;
     __syncthreads();
-    for (int size = 2; size <= Kp; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < Kp / 2; t += MERGE_T) {
-                const int i = 2 * stride * (t / stride) + (t % stride);
-                const int jx = i + stride;
-                const bool desc = ((i & size) == 0);
-                const uint64_t a = kI[i], b = kI[jx];
-                if ((a < b) == desc) {
-                    kI[i] = b; kI[jx] = a;
-                    const uint64_t c = k16[i]; k16[i] = k16[jx]; k16[jx] = c;
-                }
+    // one compare-exchange per thread and stage (Kp / 2 <= MERGE_T)
+    auto stage = [&](int lgs, int size) {
+        const int t = tid;
+        if (t < (Kp >> 1)) {
+            const int stride = 1 << lgs;
+            const int i = ((t >> lgs) << (lgs + 1)) | (t & (stride - 1));
+            const int jx = i + stride;
+            const bool desc = (i & size) == 0;
+            const uint64_t a = kI[i], b = kI[jx];
+            if ((a < b) == desc) {
+                kI[i] = b;
+                kI[jx] = a;
             }
+        }
+    };
+    for (int lsz = 1; lsz <= lgKp; ++lsz) {
+        const int size = 1 << lsz;
+        int lgs = lsz - 1;
+        for (; lgs >= 7; --lgs) {  // stride >= 128: across waves
+            stage(lgs, size);
             __syncthreads();
         }
-    }
-    long long D = 0;
-    uint64_t *src = k16, *dst = tmp;
-    for (int w = 1; w < K; w <<= 1) {
-        for (int e = tid; e < K; e += MERGE_T) {
-            const int s0 = (e / (2 * w)) * (2 * w);
-            const int lw = min(w, K - s0);
-            const int rw = max(0, min(w, K - s0 - w));
-            const uint64_t x = src[e];
-            int pos;
-            if (e < s0 + lw) {
-                pos = (e - s0) + count_greater(src + s0 + lw, rw, x);
-            } else {
-                const int g = count_greater(src + s0, lw, x);
-                D += lw - g;   // left elements smaller than x: discordant
-                pos = (e - s0 - lw) + g;
-            }
-            dst[s0 + pos] = x;
+        for (; lgs >= 0; --lgs) {  // inside the wave's 128 elements
+            stage(lgs, size);
+            wave_sync();
         }
         __syncthreads();
-        uint64_t *t_ = src; src = dst; dst = t_;
+    }
+    // the FP16-side keys in INT8 order
+    for (int e = tid; e < K; e += MERGE_T) tmp[e] = k16[0xFFFF - (int)((kI[e] - 1) & 0xFFFF)];
+    __syncthreads();
+    long long D = 0;
+    uint64_t *src = tmp, *dst = k16;
+    const int wv = tid >> 6, lane = tid & 63;
+    for (int lw = 0; (1 << lw) < K; ++lw) {
+        const int w = 1 << lw;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int e = 128 * wv + 64 * half + lane;
+            if (e < K) {
+                const int s0 = (e >> (lw + 1)) << (lw + 1);
+                const int lw_ = min(w, K - s0);
+                const int rw = max(0, min(w, K - s0 - w));
+                const uint64_t x = src[e];
+                int pos;
+                if (e < s0 + lw_) {
+                    pos = (e - s0) + count_greater(src + s0 + lw_, rw, x);
+                } else {
+                    const int gg = count_greater(src + s0, lw_, x);
+                    D += lw_ - gg;  // left elements smaller than x: discordant
+                    pos = (e - s0 - lw_) + gg;
+                }
+                dst[s0 + pos] = x;
+            }
+        }
+        if (w >= 64) __syncthreads(); else wave_sync();
+        uint64_t *t_ = src;
+        src = dst;
+        dst = t_;
     }
     return D;
 }
@@ -1647,13 +1674,15 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     const uint64_t *M = St.mfx + hs * St.NS;
     // block b's fixed-point FP16 mass M16 (relative to the largest FP16 block
     // max mr over P) and the two keys (mass desc, index asc)
-    auto keys = [&](uint32_t b, float mr, uint64_t &ki, uint64_t &k16) {
+    // ties broken by `tie`, ascending: the block index, or its position in
+    // the (ascending) P list, which orders the same way
+    auto keys = [&](uint32_t b, uint32_t tie, float mr, uint64_t &ki, uint64_t &k16) {
         const float2 s = st16[b];
         const float m16 = s.y * exp_c(s.x - mr);
         const uint64_t M16 = (uint64_t)((double)m16 * 4294967296.0);
         St.m16[hs * Ly.Nmax + b] = M16;
-        ki = (M[b] << 16) | (uint64_t)(0xFFFF - b);
-        k16 = (M16 << 16) | (uint64_t)(0xFFFF - b);
+        ki = (M[b] << 16) | (uint64_t)(0xFFFF - tie);
+        k16 = (M16 << 16) | (uint64_t)(0xFFFF - tie);
     };
     auto block_max = [&](float v) {
         v = wave_max_f32(v);
@@ -1670,7 +1699,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         float mr = -INFINITY;
         for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[lds_list[i]].x);
         mr = block_max(mr);
-        for (int i = tid; i < K; i += MERGE_T) keys(lds_list[i], mr, lds_kI[i], lds_k16[i]);
+        for (int i = tid; i < K; i += MERGE_T) keys(lds_list[i], (uint32_t)i, mr, lds_kI[i], lds_k16[i]);
         __syncthreads();
         if (K <= RANK_PAIRS) {
             // all pairs (i, q > i) from LDS: RANK_SUB threads per row, rows
@@ -1697,7 +1726,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         float mr = -INFINITY;
         for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[plist[i]].x);
         mr = block_max(mr);
-        for (int i = tid; i < K; i += MERGE_T) keys(plist[i], mr, kI[i], k16[i]);
+        for (int i = tid; i < K; i += MERGE_T) keys(plist[i], plist[i], mr, kI[i], k16[i]);
         __syncthreads();
         // rows i and K-1-i go to the same thread (equal work per thread)
         for (int i = tid; i < (K + 1) / 2; i += MERGE_T) {

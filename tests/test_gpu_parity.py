@@ -201,6 +201,17 @@ def test_single_token_and_single_block():
         both(k, v, q, oracle.default_thresholds(sm))
 
 
+@pytest.mark.parametrize("nblk", [513, 700, 1024, 1500, 2048])
+def test_rank_check_large_promoted_sets(nblk):
+    """K* above the direct-pairs limit: the sorted rank check (bitonic sort of
+    the INT8 order, merge count of the FP16 order) against the oracle."""
+    k, v, q, sm = micro(900 + nblk, T=64 * nblk, Hq=4, Hkv=1, d=64, kind="flat")
+    th = oracle.default_thresholds(sm, tau_cov=1.0, rank_tol=1.0)
+    res, rep = both(k, v, q, th)
+    assert np.all(rep["kstar"] == nblk)
+    assert np.all(rep["n_discordant"] > 0)
+
+
 def test_mixed_lengths_in_a_batch():
     """Sequences of different lengths in one step (each compared alone)."""
     import certified_quantized_kv_amd as ckv
@@ -320,7 +331,7 @@ def test_error_paths():
         c.certified_decode_attention(5, q, th)
     assert e.value.name == "CKV_EINVAL"
     with pytest.raises(ckv.CkvError) as e:
-        c.certified_decode_attention(0, q, dict(th, tau_cov=0.0))
+        c.certified_decode_attention(0, q, dict(th, tau_cov=-0.5))
     assert e.value.name == "CKV_EINVAL"
     out, rep = c.certified_decode_attention(0, q, th)   # all-zero K, V, q: defined
     assert np.all(out.cpu().numpy() == 0)
