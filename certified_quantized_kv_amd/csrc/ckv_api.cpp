@@ -691,7 +691,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         // copies), the block lists from the worklist kernel
         HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
         HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_wl, 0));
-        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, c->side[0]));
+        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, 1, c->side[0]));
     }
     // K runs first: the FP16-key pass and the INT4 promoted pass need only
     // them and run while the V runs are copied
@@ -700,6 +700,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         HIPCHK(hipEventRecord(c->ev_kside[k], c->side[k]));
         HIPCHK(hipStreamWaitEvent(s, c->ev_kside[k], 0));
     }
+    if (gather)
+        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, 2, c->side[0]));
     TRY(issue_copies(c, cl));
     paged += cl.bytes + clk.bytes;
     if (prof) c->pf.copies += cl.size.size() + clk.size.size();

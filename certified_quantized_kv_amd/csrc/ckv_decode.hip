@@ -1427,7 +1427,8 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
 // the FP16 K blocks of the P lists and the FP16 V blocks of the VP lists,
 // read from tier 2 (pinned host memory mapped into the device's address
 // space) over the host link and written to the staging area, only the
-// listed blocks (no gap fill) and no per-copy overhead.  One workgroup per
+// listed blocks (no gap fill) and no per-copy overhead; `kinds`: bit 0 the
+// K blocks, bit 1 the V blocks.  One workgroup per
 // (slice, kv head, sequence); wave w of slice x takes list entries
 // 4x + w, 4x + w + 4*GATHER_X, ...; a wave moves a 64-token block as D/8
 // 16-byte loads per lane.  Skipped sequences (rung 4 before paging) are left
@@ -1437,7 +1438,7 @@ constexpr int GATHER_X = 32;
 
 template <int D>
 __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *skip_seq, const uint16_t *t2k,
-                                                const uint16_t *t2v, uint16_t *stk, uint16_t *stv) {
+                                                const uint16_t *t2v, uint16_t *stk, uint16_t *stv, int kinds) {
     const int x = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (skip_seq[n]) return;
@@ -1448,6 +1449,7 @@ __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *s
     constexpr int NL = D / 8;  // 16-byte loads per lane per block
 #pragma unroll
     for (int kind = 0; kind < 2; ++kind) {
+        if (!(kinds & (1 << kind))) continue;
         const int lk = kind == 0 ? WL_KEYS : WL_FP16;
         const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[lk * nk + ng]);
         const uint32_t *lst = St.wl + (lk * nk + ng) * (size_t)(Ly.Nmax + 1);
@@ -1967,11 +1969,11 @@ hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
 }
 
 hipError_t launch_gather(const Layout &Ly, const Step &St, const int *skip_seq, const uint16_t *t2k,
-                         const uint16_t *t2v, uint16_t *stk, uint16_t *stv, hipStream_t s) {
+                         const uint16_t *t2v, uint16_t *stk, uint16_t *stv, int kinds, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         (void)G;
         hipLaunchKernelGGL((k_gather<decltype(D)::value>), dim3(GATHER_X, Ly.Hkv, St.batch), dim3(256), 0, s,
-                           Ly, St, skip_seq, t2k, t2v, stk, stv);
+                           Ly, St, skip_seq, t2k, t2v, stk, stv, kinds);
         return hipGetLastError();
     });
 }

@@ -142,7 +142,7 @@ hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStre
 hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s);
 hipError_t launch_gather(const Layout &Ly, const Step &St, const int *skip_seq, const uint16_t *t2k,
-                         const uint16_t *t2v, uint16_t *stk, uint16_t *stv, hipStream_t s);
+                         const uint16_t *t2v, uint16_t *stk, uint16_t *stv, int kinds, hipStream_t s);
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_promoted16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
