@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=4,
                     help="decode-loop steps after the timed region, first workload only: one token "
                          "appended to every sequence of every layer, then that layer's certified step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline layer-steps (no device-paging, variant or decode-loop lines): "
+                         "for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -205,6 +208,32 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
                    "v_tol": th["v_tol"], "rank_tol": th["rank_tol"]},
     }
 
+    if not args.no_extras:
+        extra_lines(rec, args, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
+                    ms_step, decode_steps)
+    cache.close()
+    del dense_kv
+
+    if sample is not None:
+        import oracle
+        k1, v1, q1, sm1 = sample
+        t1 = time.perf_counter()
+        oracle.certified_decode(k1, v1, q1, oracle.default_thresholds(sm1), trace=False)
+        cs = time.perf_counter() - t1
+        rec["cpu_baseline"] = {
+            "value": round(T / cs, 1), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{name} layer 0, sequence 0 of {B}: one full layer-step of one sequence "
+                      f"({T} tokens, {Hq} q heads), {cs:.1f} s single-threaded"}
+        log(f"cpu baseline: {cs:.1f}s for the sample")
+    return rec
+
+
+def extra_lines(rec, args, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
+                ms_step, decode_steps):
+    """Comparison lines after the headline layer-steps: device-initiated
+    paging, the threshold variants against dense attention, the decode loop
+    (with and without the FP16 cache) and the dense comparator."""
+    import torch
     # the same layer-steps with device-initiated paging (a kernel reading
     # pinned host memory instead of host-issued copies): a comparison line
     cache.set_device_paging(True)
@@ -257,21 +286,6 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
                                    "certified_over_dense": round(ms_step / dms, 2),
                                    "layers_cycled": n_dense}
         log(f"dense comparator: {dms:.3f} ms/step")
-    cache.close()
-    del dense_kv
-
-    if sample is not None:
-        import oracle
-        k1, v1, q1, sm1 = sample
-        t1 = time.perf_counter()
-        oracle.certified_decode(k1, v1, q1, oracle.default_thresholds(sm1), trace=False)
-        cs = time.perf_counter() - t1
-        rec["cpu_baseline"] = {
-            "value": round(T / cs, 1), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{name} layer 0, sequence 0 of {B}: one full layer-step of one sequence "
-                      f"({T} tokens, {Hq} q heads), {cs:.1f} s single-threaded"}
-        log(f"cpu baseline: {cs:.1f}s for the sample")
-    return rec
 
 
 def variants(cache, dense_kv, qs, th, T, sm, n):
