@@ -1269,6 +1269,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     values_pass<D, G, VP_FP16>(Ly, St, skip_seq);
 }
 
+constexpr int KEYS_MAXE = 32;  // list entries per workgroup of the FP16-key pass
+
+// An equal share of one kind of block list over the whole step: the lists
+// of all (sequence, kv head) pairs of the batch concatenated in pair order
+// (pairs of a sequence flagged in skip_seq count as empty), entries
+// [sp*total/nsp, (sp+1)*total/nsp) to workgroup sp of nsp.  Entry i of the
+// share is entry sidx[i] of pair sng[i]'s list.  Returns the share's size,
+// at most CAP when nsp * CAP >= total.  256 threads; wtot: 4 ints of LDS.
+template <int CAP>
+__device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int kind, const int *skip_seq, int sp,
+                                          int nsp, int *sng, int *sidx, int *wtot) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Hkv = Ly.Hkv, BH = St.batch * Hkv;
+    const int *cnt = St.wcnt + (size_t)kind * Ly.B * Hkv;
+    auto count = [&](int ng) { return ng < BH && !(skip_seq && skip_seq[ng / Hkv]) ? cnt[ng] : 0; };
+    int t = 0;
+    for (int c0 = 0; c0 < BH; c0 += 256) t += count(c0 + tid);
+    t = wave_sum_i32_dpp(t);
+    if (lane == 0) wtot[wave] = t;
+    __syncthreads();
+    const long long total = (long long)wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    const int e0 = (int)((long long)sp * total / nsp);
+    const int ne = min((int)((long long)(sp + 1) * total / nsp) - e0, CAP);
+    __syncthreads();
+    // the pairs whose entries fall in [e0, e0 + ne), 256 pairs at a time
+    int base = 0;
+    for (int c0 = 0; c0 < BH && base < e0 + ne; c0 += 256) {
+        const int ng = c0 + tid, c = count(ng);
+        const int pw = (int)wave_prefix_excl_u32((uint32_t)c, lane);
+        if (lane == 63) wtot[wave] = pw + c;
+        __syncthreads();
+        int pre = base + pw, chunk = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            pre += w < wave ? wtot[w] : 0;
+            chunk += wtot[w];
+        }
+        const int lo = max(pre, e0), hi = min(pre + c, e0 + ne);
+        for (int e = lo; e < hi; ++e) {
+            sng[e - e0] = ng;
+            sidx[e - e0] = e - pre;
+        }
+        base += chunk;
+        __syncthreads();
+    }
+    return ne;
+}
+
 // ===========================================================================
 // K4a (keys): FP16-key scores of the P blocks from the staging area [Meth-3
 // rank-consistency check], one wave per block, lane = token: FP64 fma chain
@@ -1277,48 +1325,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
 // through uniform scalar loads.
 // ===========================================================================
-constexpr int KEYS_MAXE = 32;  // list entries per workgroup of the FP16-key pass
-
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
                                                 const double *qd) {
-    const int sp = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int l = St.layer;
-    if (skip_seq[n]) return;
     constexpr uint32_t ALL = (1u << G) - 1u;
     __shared__ uint32_t sbits[KEYS_MAXE], sblk[KEYS_MAXE];
+    __shared__ int sng[KEYS_MAXE], sidx[KEYS_MAXE], wtot[4];
     __shared__ float sres[4][KEYS_MAXE / 4][G][64];
     __shared__ float2 sml[4][KEYS_MAXE / 4][G];
-    const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
-    // an equal share of the (seq, kv head)'s P blocks per workgroup
-    const size_t ng = (size_t)n * Ly.Hkv + g;
-    const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[WL_KEYS * (size_t)Ly.B * Ly.Hkv + ng]);
-    const int nsp = gridDim.x;
-    const int e0 = (int)((long long)sp * cnt / nsp);
-    // at most KEYS_MAXE entries (the launch has enough workgroups for that)
-    const int ne = min((int)((long long)(sp + 1) * cnt / nsp) - e0, KEYS_MAXE);
-    const uint32_t *lst = St.wl + (WL_KEYS * (size_t)Ly.B * Ly.Hkv + ng) * (size_t)(Ly.Nmax + 1);
+    // an equal share of the step's P blocks (all sequences and kv heads)
+    // per workgroup, whatever their spread over the kv heads
+    const int ne = list_share<KEYS_MAXE>(Ly, St, WL_KEYS, skip_seq, blockIdx.x, gridDim.x, sng, sidx, wtot);
+    const size_t nk = (size_t)Ly.B * Ly.Hkv;
     for (int i = threadIdx.x; i < ne; i += 256) {
-        const uint32_t b = lst[e0 + i];
+        const size_t ng = (size_t)sng[i];
+        const uint32_t b = St.wl[(WL_KEYS * nk + ng) * (size_t)(Ly.Nmax + 1) + sidx[i]];
         sblk[i] = b;
-        sbits[i] = St.sel[selbase + b];
+        sbits[i] = St.sel[ng * Ly.Nmax + b];
     }
     __syncthreads();
     // q as [D][G] FP64, read through the constant address space (qd is not
     // written during this kernel): the loads are scalar
     typedef const __attribute__((address_space(4))) double cdouble;
-    const int qbase = __builtin_amdgcn_readfirstlane((n * Ly.Hkv + g) * D * G);
     const size_t NS64 = (size_t)St.NS * 64;
     auto pmask = [&](int i) { return __builtin_amdgcn_readfirstlane(sbits[i]) & ALL; };
     auto blk = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sblk[i]); };
-    // the (seq, kv head)'s staging area as a buffer resource: entries past
-    // the list load zeros from nowhere, so every path requests the same
-    // loads and the waits before each use stay exact
+    auto pair = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sng[i]); };
+    // each pair's staging area as a buffer resource: entries past the share
+    // load zeros from nowhere, so every path requests the same loads and the
+    // waits before each use stay exact
     constexpr uint32_t BLKB = 64 * D * 2;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(St.stage_k + selbase * 64 * D, (uint32_t)Ly.Nmax * BLKB);
     auto issue = [&](int i, uint4 (&kr)[D / 8]) {
-        const int ic = i < ne ? i : 0;  // in-range list index on every path
+        const int ic = i < ne ? i : 0;  // in-range share index on every path
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(St.stage_k + (size_t)pair(ic) * Ly.Nmax * 64 * D, (uint32_t)Ly.Nmax * BLKB);
         const uint32_t off = (i < ne ? (uint32_t)blk(ic) * BLKB : RSRC_OOB) + lane * 16;
 #pragma unroll
         for (int ch = 0; ch < D / 8; ++ch) kr[ch] = rsrc_load16(rs, off + ch * 1024);
@@ -1326,11 +1367,12 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     struct Res {
         float s[G];
     };
-    // FP64 chain over the channels for the G heads of the block in kr
-    auto compute = [&](const uint4 (&kr)[D / 8]) {
+    // FP64 chain over the channels for the G heads of the block in kr, q of
+    // pair ng
+    auto compute = [&](const uint4 (&kr)[D / 8], int ng) {
         int qoff = 0;
         asm volatile("" : "+s"(qoff));  // opaque zero: keeps the q loads in the loop
-        cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(qbase + qoff);
+        cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(ng * D * G + qoff);
         // q in groups of 16 doubles (CS channels x G heads, two scalar loads);
         // the next group is requested before the current one is used
         constexpr int QN = 16, CS = QN / G, NQ = D / CS;
@@ -1399,18 +1441,19 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
         issue(ent(1), k1);
         int t = 0;
         for (; t + 1 < nw; t += 2) {
-            Res r = compute(k0);
+            Res r = compute(k0, pair(ent(t)));
             issue(ent(t + 2), k0);
             store(ent(t), t, r);
-            r = compute(k1);
+            r = compute(k1, pair(ent(t + 1)));
             issue(ent(t + 3), k1);
             store(ent(t + 1), t + 1, r);
         }
-        if (t < nw) store(ent(t), t, compute(k0));
+        if (t < nw) store(ent(t), t, compute(k0, pair(ent(t))));
     }
     // the wave's results to global memory
     for (int t = 0; t < nw; ++t) {
-        const int i = ent(t), b = blk(i);
+        const int i = ent(t), b = blk(i), ng = pair(i);
+        const int n = ng / Ly.Hkv, g = ng - n * Ly.Hkv;
         const uint32_t pm = pmask(i);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
@@ -1987,12 +2030,13 @@ hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s) {
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         // enough workgroups that none gets more than KEYS_MAXE list entries
+        // (the lists hold at most nb blocks per sequence and kv head)
         const int per = St.bps < KEYS_MAXE ? St.bps : KEYS_MAXE;
-        const int nsp = (St.nb + per - 1) / per;
+        const long long bound = (long long)St.nb * Ly.Hkv * St.batch;
+        const int nsp = (int)((bound + per - 1) / per);
         if (nsp == 0) return hipSuccess;
-        hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>),
-                           dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq,
-                           (const double *)St.qd);
+        hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>), dim3(nsp), dim3(256), 0, s, Ly, St,
+                           skip_seq, (const double *)St.qd);
         return hipGetLastError();
     });
 }
