@@ -1269,17 +1269,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     values_pass<D, G, VP_FP16>(Ly, St, skip_seq);
 }
 
-constexpr int KEYS_MAXE = 32;  // list entries per workgroup of the FP16-key pass
+constexpr int KEYS_PW = 3;             // list entries per wave of the FP16-key pass
+constexpr int KEYS_MAXE = 4 * KEYS_PW;  // list entries per workgroup
 
-// An equal share of one kind of block list over the whole step: the lists
-// of all (sequence, kv head) pairs of the batch concatenated in pair order
-// (pairs of a sequence flagged in skip_seq count as empty), entries
-// [sp*total/nsp, (sp+1)*total/nsp) to workgroup sp of nsp.  Entry i of the
-// share is entry sidx[i] of pair sng[i]'s list.  Returns the share's size,
-// at most CAP when nsp * CAP >= total.  256 threads; wtot: 4 ints of LDS.
+// The share of workgroup sp in one kind of block list over the whole step:
+// the lists of all (sequence, kv head) pairs of the batch concatenated in
+// pair order (pairs of a sequence flagged in skip_seq count as empty),
+// entries [sp*CAP, sp*CAP + CAP).  Entry i of the share is entry sidx[i] of
+// pair sng[i]'s list.  Returns the share's size.  256 threads; wtot: 4 ints
+// of LDS.
 template <int CAP>
 __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int kind, const int *skip_seq, int sp,
-                                          int nsp, int *sng, int *sidx, int *wtot) {
+                                          int *sng, int *sidx, int *wtot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Hkv = Ly.Hkv, BH = St.batch * Hkv;
     const int *cnt = St.wcnt + (size_t)kind * Ly.B * Hkv;
@@ -1290,8 +1291,9 @@ __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int 
     if (lane == 0) wtot[wave] = t;
     __syncthreads();
     const long long total = (long long)wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    const int e0 = (int)((long long)sp * total / nsp);
-    const int ne = min((int)((long long)(sp + 1) * total / nsp) - e0, CAP);
+    const long long e0l = (long long)sp * CAP;
+    const int ne = e0l >= total ? 0 : (int)min((long long)CAP, total - e0l);
+    const int e0 = (int)min(e0l, total);
     __syncthreads();
     // the pairs whose entries fall in [e0, e0 + ne), 256 pairs at a time
     int base = 0;
@@ -1323,7 +1325,11 @@ __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int 
 // over c = 0 .. D-1 with one rounding to FP32 after the scale (the decision
 // arithmetic of the rank check), the block's FP16-side max and mass (64-leaf
 // tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
-// through uniform scalar loads.
+// through uniform scalar loads.  Workgroups take consecutive KEYS_MAXE
+// entries of the step's P list (all pairs), KEYS_PW per wave; a block is
+// loaded as two halves of D/2 channels, three halves in registers (two in
+// flight while the chain runs over the third), which keeps the registers at
+// four waves per SIMD.
 // ===========================================================================
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
@@ -1332,11 +1338,10 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     constexpr uint32_t ALL = (1u << G) - 1u;
     __shared__ uint32_t sbits[KEYS_MAXE], sblk[KEYS_MAXE];
     __shared__ int sng[KEYS_MAXE], sidx[KEYS_MAXE], wtot[4];
-    __shared__ float sres[4][KEYS_MAXE / 4][G][64];
-    __shared__ float2 sml[4][KEYS_MAXE / 4][G];
-    // an equal share of the step's P blocks (all sequences and kv heads)
-    // per workgroup, whatever their spread over the kv heads
-    const int ne = list_share<KEYS_MAXE>(Ly, St, WL_KEYS, skip_seq, blockIdx.x, gridDim.x, sng, sidx, wtot);
+    __shared__ float sres[4][KEYS_PW][G][64];
+    __shared__ float2 sml[4][KEYS_PW][G];
+    const int ne = list_share<KEYS_MAXE>(Ly, St, WL_KEYS, skip_seq, blockIdx.x, sng, sidx, wtot);
+    if (ne == 0) return;
     const size_t nk = (size_t)Ly.B * Ly.Hkv;
     for (int i = threadIdx.x; i < ne; i += 256) {
         const size_t ng = (size_t)sng[i];
@@ -1351,37 +1356,32 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     const size_t NS64 = (size_t)St.NS * 64;
     auto pmask = [&](int i) { return __builtin_amdgcn_readfirstlane(sbits[i]) & ALL; };
     auto blk = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sblk[i]); };
-    auto pair = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sng[i]); };
+    auto pair = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sng[i < ne ? i : 0]); };
     // each pair's staging area as a buffer resource: entries past the share
     // load zeros from nowhere, so every path requests the same loads and the
     // waits before each use stay exact
     constexpr uint32_t BLKB = 64 * D * 2;
-    auto issue = [&](int i, uint4 (&kr)[D / 8]) {
+    constexpr int HC = D / 16;  // 16-byte chunks per lane in half a block
+    using Half = uint4[HC];
+    auto issue = [&](int i, int h, Half &kr) {
         const int ic = i < ne ? i : 0;  // in-range share index on every path
         const __amdgpu_buffer_rsrc_t rs =
             make_rsrc(St.stage_k + (size_t)pair(ic) * Ly.Nmax * 64 * D, (uint32_t)Ly.Nmax * BLKB);
-        const uint32_t off = (i < ne ? (uint32_t)blk(ic) * BLKB : RSRC_OOB) + lane * 16;
+        const uint32_t off = (i < ne ? (uint32_t)blk(ic) * BLKB : RSRC_OOB) + lane * 16 + h * HC * 1024;
 #pragma unroll
-        for (int ch = 0; ch < D / 8; ++ch) kr[ch] = rsrc_load16(rs, off + ch * 1024);
+        for (int ch = 0; ch < HC; ++ch) kr[ch] = rsrc_load16(rs, off + ch * 1024);
     };
-    struct Res {
-        float s[G];
-    };
-    // FP64 chain over the channels for the G heads of the block in kr, q of
-    // pair ng
-    auto compute = [&](const uint4 (&kr)[D / 8], int ng) {
+    // FP64 chain over the channels of half h for the G heads, q of pair ng
+    auto chain = [&](const Half &kr, int h, int ng, double (&a)[G]) {
         int qoff = 0;
         asm volatile("" : "+s"(qoff));  // opaque zero: keeps the q loads in the loop
-        cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(ng * D * G + qoff);
         // q in groups of 16 doubles (CS channels x G heads, two scalar loads);
         // the next group is requested before the current one is used
-        constexpr int QN = 16, CS = QN / G, NQ = D / CS;
+        constexpr int QN = 16, CS = QN / G, NQ = D / 2 / CS;
+        cdouble *qb = (cdouble *)qd + __builtin_amdgcn_readfirstlane(ng * D * G + h * (D / 2) * G + qoff);
         double qc[QN], qn[QN];
 #pragma unroll
         for (int i = 0; i < QN; ++i) qc[i] = qb[i];
-        double a[G];
-#pragma unroll
-        for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
         float kf[8];
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
@@ -1393,7 +1393,7 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
             for (int jj = 0; jj < G; ++jj) asm volatile("" : "+v"(a[jj])::"memory");
 #pragma unroll
             for (int cc = 0; cc < CS; ++cc) {
-                const int c = qi * CS + cc;
+                const int c = qi * CS + cc;  // channel within the half
                 if (c % 8 == 0) unpack_fp16x8(kr[c / 8], kf);
                 const double kc = (double)kf[c % 8];
 #pragma unroll
@@ -1406,53 +1406,64 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
 #pragma unroll
             for (int i = 0; i < QN; ++i) qc[i] = qn[i];
         }
-        Res r;
-#pragma unroll
-        for (int jj = 0; jj < G; ++jj) r.s[jj] = (float)(a[jj] * (double)St.sm);
-        return r;
     };
     // scores, block max and mass of the heads of P, kept in LDS until the
     // loads are done: a global store between the loads would make every
     // wait for a load drain all outstanding requests (stores and loads
     // share one counter and stores may finish out of order)
-    auto store = [&](int i, int t, const Res &r) {
+    auto store = [&](int i, int t, const double (&a)[G]) {
         const uint32_t pm = pmask(i);
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
             if (!(pm & (1u << jj))) continue;
-            const float s = r.s[jj];
+            const float s = (float)(a[jj] * (double)St.sm);
             sres[wave][t][jj][lane] = s;
             const float mx = wave_max_dpp(s);
             const float l_ = tree64_f32_dpp(exp_c(s - mx));
-            // every lane writes the same pair (no lane-divergent branch in
-            // the loop: its exec-mask skips would add paths that bypass the
-            // next requests, and the waits would have to assume them)
+            // every lane writes the same pair (no lane-divergent branch
+            // between the loads: its exec-mask skips would add paths that
+            // bypass the next requests, and the waits would have to assume
+            // them)
             sml[wave][t][jj] = make_float2(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_), 0)));
         }
     };
-    // entries wave, wave + 4, ...; two blocks requested ahead of each use
-    uint4 k0[D / 8], k1[D / 8];
-    const int nw = ne > wave ? (ne - wave + 3) / 4 : 0;
-    auto ent = [&](int t) { return wave + 4 * t; };
-    if (nw > 0) {
-        issue(ent(0), k0);
-        // k0's requests stay ahead of k1's (the waits count on that order)
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ent(1), k1);
-        int t = 0;
-        for (; t + 1 < nw; t += 2) {
-            Res r = compute(k0, pair(ent(t)));
-            issue(ent(t + 2), k0);
-            store(ent(t), t, r);
-            r = compute(k1, pair(ent(t + 1)));
-            issue(ent(t + 3), k1);
-            store(ent(t + 1), t + 1, r);
-        }
-        if (t < nw) store(ent(t), t, compute(k0, pair(ent(t))));
+    // the wave's entries wave, wave + 4, wave + 8 (past the share: zeros,
+    // results not kept); halves in X, Y, Z in the order E0h0 E0h1 E1h0 E1h1
+    // E2h0 E2h1, each buffer refilled as soon as its half is used
+    static_assert(KEYS_PW == 3, "the schedule below is written for three entries per wave");
+    const int nw = ne > wave ? min((ne - wave + 3) / 4, KEYS_PW) : 0;
+    const int E0 = wave, E1 = wave + 4, E2 = wave + 8;
+    Half X, Y, Z;
+    double a[G];
+    auto zero = [&]() {
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
+    };
+    issue(E0, 0, X);
+    __builtin_amdgcn_sched_barrier(0);  // requests in this order (the waits count on it)
+    issue(E0, 1, Y);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(E1, 0, Z);
+    zero();
+    chain(X, 0, pair(E0), a);
+    issue(E1, 1, X);
+    chain(Y, 1, pair(E0), a);
+    issue(E2, 0, Y);
+    if (nw > 0) store(E0, 0, a);
+    zero();
+    chain(Z, 0, pair(E1), a);
+    issue(E2, 1, Z);
+    chain(X, 1, pair(E1), a);
+    if (nw > 1) store(E1, 1, a);
+    if (nw > 2) {
+        zero();
+        chain(Y, 0, pair(E2), a);
+        chain(Z, 1, pair(E2), a);
+        store(E2, 2, a);
     }
     // the wave's results to global memory
     for (int t = 0; t < nw; ++t) {
-        const int i = ent(t), b = blk(i), ng = pair(i);
+        const int i = wave + 4 * t, b = blk(i), ng = pair(i);
         const int n = ng / Ly.Hkv, g = ng - n * Ly.Hkv;
         const uint32_t pm = pmask(i);
 #pragma unroll
@@ -2029,11 +2040,10 @@ hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s) {
 }
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        // enough workgroups that none gets more than KEYS_MAXE list entries
-        // (the lists hold at most nb blocks per sequence and kv head)
-        const int per = St.bps < KEYS_MAXE ? St.bps : KEYS_MAXE;
+        // KEYS_MAXE entries per workgroup over the step's P list (at most nb
+        // blocks per sequence and kv head); workgroups past its end exit
         const long long bound = (long long)St.nb * Ly.Hkv * St.batch;
-        const int nsp = (int)((bound + per - 1) / per);
+        const int nsp = (int)((bound + KEYS_MAXE - 1) / KEYS_MAXE);
         if (nsp == 0) return hipSuccess;
         hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>), dim3(nsp), dim3(256), 0, s, Ly, St,
                            skip_seq, (const double *)St.qd);
