@@ -60,6 +60,7 @@ struct ckv_cache {
     ckv_config cfg{};
     Layout Ly{};
     int G = 0, d = 0, Nmax = 0, NS = 0, nsplit_cap = 0;
+    int ncu = 0;  // compute units of the device
     size_t blk_fp16 = 0;  // elements of one FP16 block
     std::vector<void *> dev_allocs;
     size_t dev_bytes = 0, host_bytes = 0, tier1_bytes = 0;
@@ -233,6 +234,8 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         return fail(CKV_EINVAL, "max_context %d too large for head_dim %d", k.max_context, k.head_dim);
     if (Nmax > 65536) return fail(CKV_EINVAL, "max_context above 4M tokens");
     HIPCHK(hipSetDevice(k.device));
+    int ncu = 0;
+    HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, k.device));
     ckv_cache *c = new ckv_cache();
     c->cfg = k;
     c->G = G;
@@ -241,6 +244,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     c->NS = Nmax + 1;
     c->nsplit_cap = c->NS;
     c->blk_fp16 = (size_t)64 * k.head_dim;
+    c->ncu = ncu;
     const int L = k.n_layers, B = k.max_batch, Hq = k.n_q_heads, Hkv = k.n_kv_heads, d = k.head_dim;
     const size_t nblk = (size_t)L * B * Hkv * Nmax;
     auto cleanup = [&](ckv_status s) {
@@ -584,6 +588,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     St.NS = c->NS;
     St.bps = split_blocks(nb, Hkv, batch);
     St.spw = score_slots(nb, Hkv, batch);
+    St.ncu = c->ncu;
     St.nsplit = (nb + St.bps - 1) / St.bps;
     St.nsplit_cap = c->nsplit_cap;
     St.sm = th->sm_scale;

@@ -1269,18 +1269,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     values_pass<D, G, VP_FP16>(Ly, St, skip_seq);
 }
 
-constexpr int KEYS_PW = 3;             // list entries per wave of the FP16-key pass
-constexpr int KEYS_MAXE = 4 * KEYS_PW;  // list entries per workgroup
+constexpr int KEYS_PW = 4;             // list entries per wave of the FP16-key pass, at most
+constexpr int KEYS_MAXE = 4 * KEYS_PW;  // list entries per workgroup, at most
 
-// The share of workgroup sp in one kind of block list over the whole step:
-// the lists of all (sequence, kv head) pairs of the batch concatenated in
-// pair order (pairs of a sequence flagged in skip_seq count as empty),
-// entries [sp*CAP, sp*CAP + CAP).  Entry i of the share is entry sidx[i] of
-// pair sng[i]'s list.  Returns the share's size.  256 threads; wtot: 4 ints
-// of LDS.
+// An equal share of one kind of block list over the whole step: the lists
+// of all (sequence, kv head) pairs of the batch concatenated in pair order
+// (pairs of a sequence flagged in skip_seq count as empty), entries
+// [sp*total/nsp, (sp+1)*total/nsp) to workgroup sp of nsp.  Entry i of the
+// share is entry sidx[i] of pair sng[i]'s list.  Returns the share's size,
+// at most CAP when nsp * CAP >= total.  256 threads; wtot: 4 ints of LDS.
 template <int CAP>
 __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int kind, const int *skip_seq, int sp,
-                                          int *sng, int *sidx, int *wtot) {
+                                          int nsp, int *sng, int *sidx, int *wtot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Hkv = Ly.Hkv, BH = St.batch * Hkv;
     const int *cnt = St.wcnt + (size_t)kind * Ly.B * Hkv;
@@ -1291,9 +1291,8 @@ __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int 
     if (lane == 0) wtot[wave] = t;
     __syncthreads();
     const long long total = (long long)wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    const long long e0l = (long long)sp * CAP;
-    const int ne = e0l >= total ? 0 : (int)min((long long)CAP, total - e0l);
-    const int e0 = (int)min(e0l, total);
+    const int e0 = (int)((long long)sp * total / nsp);
+    const int ne = min((int)((long long)(sp + 1) * total / nsp) - e0, CAP);
     __syncthreads();
     // the pairs whose entries fall in [e0, e0 + ne), 256 pairs at a time
     int base = 0;
@@ -1325,9 +1324,10 @@ __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int 
 // over c = 0 .. D-1 with one rounding to FP32 after the scale (the decision
 // arithmetic of the rank check), the block's FP16-side max and mass (64-leaf
 // tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
-// through uniform scalar loads.  Workgroups take consecutive KEYS_MAXE
-// entries of the step's P list (all pairs), KEYS_PW per wave; a block is
-// loaded as two halves of D/2 channels, three halves in registers (two in
+// through uniform scalar loads.  The step's P list (all pairs) is split
+// evenly over the workgroups (one round of resident workgroups when it has
+// at most KEYS_MAXE entries each), at most KEYS_PW entries per wave; a block
+// is loaded as two halves of D/2 channels, three halves in registers (two in
 // flight while the chain runs over the third), which keeps the registers at
 // four waves per SIMD.
 // ===========================================================================
@@ -1340,7 +1340,7 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     __shared__ int sng[KEYS_MAXE], sidx[KEYS_MAXE], wtot[4];
     __shared__ float sres[4][KEYS_PW][G][64];
     __shared__ float2 sml[4][KEYS_PW][G];
-    const int ne = list_share<KEYS_MAXE>(Ly, St, WL_KEYS, skip_seq, blockIdx.x, sng, sidx, wtot);
+    const int ne = list_share<KEYS_MAXE>(Ly, St, WL_KEYS, skip_seq, blockIdx.x, gridDim.x, sng, sidx, wtot);
     if (ne == 0) return;
     const size_t nk = (size_t)Ly.B * Ly.Hkv;
     for (int i = threadIdx.x; i < ne; i += 256) {
@@ -1427,12 +1427,14 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
             sml[wave][t][jj] = make_float2(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_), 0)));
         }
     };
-    // the wave's entries wave, wave + 4, wave + 8 (past the share: zeros,
-    // results not kept); halves in X, Y, Z in the order E0h0 E0h1 E1h0 E1h1
-    // E2h0 E2h1, each buffer refilled as soon as its half is used
-    static_assert(KEYS_PW == 3, "the schedule below is written for three entries per wave");
+    // the wave's entries wave + 4t, t < KEYS_PW (past the share: zeros from
+    // nowhere, no FMAs, results not kept); halves in X, Y, Z in the order
+    // E0h0 E0h1 E1h0 E1h1 E2h0 E2h1 E3h0 E3h1, each buffer refilled as soon
+    // as its half is used, every request on every path
+    static_assert(KEYS_PW == 4, "the schedule below is written for four entries per wave");
     const int nw = ne > wave ? min((ne - wave + 3) / 4, KEYS_PW) : 0;
-    const int E0 = wave, E1 = wave + 4, E2 = wave + 8;
+    const int E0 = wave, E1 = wave + 4, E2 = wave + 8, E3 = wave + 12;
+    if (nw == 0) return;  // no barrier follows
     Half X, Y, Z;
     double a[G];
     auto zero = [&]() {
@@ -1449,17 +1451,31 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     issue(E1, 1, X);
     chain(Y, 1, pair(E0), a);
     issue(E2, 0, Y);
-    if (nw > 0) store(E0, 0, a);
-    zero();
-    chain(Z, 0, pair(E1), a);
+    store(E0, 0, a);
+    if (nw > 1) {
+        zero();
+        chain(Z, 0, pair(E1), a);
+    }
     issue(E2, 1, Z);
-    chain(X, 1, pair(E1), a);
-    if (nw > 1) store(E1, 1, a);
+    if (nw > 1) {
+        chain(X, 1, pair(E1), a);
+        store(E1, 1, a);
+    }
+    issue(E3, 0, X);
     if (nw > 2) {
         zero();
         chain(Y, 0, pair(E2), a);
+    }
+    issue(E3, 1, Y);
+    if (nw > 2) {
         chain(Z, 1, pair(E2), a);
         store(E2, 2, a);
+    }
+    if (nw > 3) {
+        zero();
+        chain(X, 0, pair(E3), a);
+        chain(Y, 1, pair(E3), a);
+        store(E3, 3, a);
     }
     // the wave's results to global memory
     for (int t = 0; t < nw; ++t) {
@@ -2040,11 +2056,12 @@ hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s) {
 }
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        // KEYS_MAXE entries per workgroup over the step's P list (at most nb
-        // blocks per sequence and kv head); workgroups past its end exit
+        // one round of resident workgroups (four per compute unit at this
+        // kernel's registers), more when the list may exceed KEYS_MAXE
+        // entries per workgroup (at most nb blocks per sequence and kv head)
         const long long bound = (long long)St.nb * Ly.Hkv * St.batch;
-        const int nsp = (int)((bound + KEYS_MAXE - 1) / KEYS_MAXE);
-        if (nsp == 0) return hipSuccess;
+        if (bound == 0) return hipSuccess;
+        const int nsp = (int)std::max<long long>(4LL * St.ncu, (bound + KEYS_MAXE - 1) / KEYS_MAXE);
         hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>), dim3(nsp), dim3(256), 0, s, Ly, St,
                            skip_seq, (const double *)St.qd);
         return hipGetLastError();

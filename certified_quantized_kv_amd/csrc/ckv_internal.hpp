@@ -74,6 +74,7 @@ struct Step {
     int NS;                 // slot stride
     int nsplit, bps;        // tail splits per (seq, kv head), blocks per split
     int spw;                // block slots per wave of the scoring pass
+    int ncu;                // compute units of the device
     float sm;
     const uint16_t *q;      // [batch][Hq][d]
     float *score;           // [B][Hq][NS*64]  INT8 scores (unfinished block: FP16)
