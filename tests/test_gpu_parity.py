@@ -212,6 +212,27 @@ def test_rank_check_large_promoted_sets(nblk):
     assert np.all(rep["n_discordant"] > 0)
 
 
+def test_batch_with_some_sequences_at_rung4_before_paging():
+    """A batch whose sequences differ in how many FP16 value blocks they ask
+    for: with a small cap, sequences 1 and 3 (values of unit range, flat
+    attention) go to rung 4 before paging, so their lists count as empty in
+    the passes that split the whole step's lists, while sequences 0 and 2
+    (values of small range) are certified; every intermediate against the
+    oracle."""
+    rng = np.random.default_rng(77)
+    B, T, Hq, Hkv, d = 4, 1280, 8, 4, 64
+    k = rng.standard_normal((B, T, Hkv, d))
+    v = rng.standard_normal((B, T, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    v[0] *= 0.01
+    v[2] *= 0.01
+    q[1] *= 0.02
+    q[3] *= 0.02
+    th = oracle.default_thresholds(1 / np.sqrt(d), v_cap_blocks=2)
+    res, rep = both(f16(k), f16(v), f16(q), th)
+    assert list(res.trace["seq_flags"] & 1) == [0, 1, 0, 1]
+
+
 def test_mixed_lengths_in_a_batch():
     """Sequences of different lengths in one step (each compared alone)."""
     import certified_quantized_kv_amd as ckv
