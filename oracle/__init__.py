@@ -64,6 +64,7 @@ def lib():
         L.orc_fx.argtypes, L.orc_fx.restype = [f64], ctypes.c_uint64
         L.orc_quant_k_block.argtypes = [i32, vp, vp, vp, vp]
         L.orc_quant_v_block.argtypes = [i32, vp, vp, vp, vp, vp]
+        L.orc_quant_v_block_bits.argtypes = [i32, i32, vp, vp, vp, vp, vp]
         L.orc_score_q8.argtypes = [i32, vp, vp, vp, vp, f32, vp]
         L.orc_score_f16.argtypes = [i32, vp, vp, i32, f32, vp]
         L.orc_delta_rho.argtypes = [i32, vp, vp, vp, f32, vp, vp]
@@ -74,6 +75,10 @@ def lib():
                                            ctypes.POINTER(Thresholds), vp, vp,
                                            ctypes.POINTER(_Trace)]
         L.orc_certified_decode.restype = i32
+        L.orc_certified_decode_vb.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                           ctypes.POINTER(Thresholds), vp, vp,
+                                           ctypes.POINTER(_Trace)]
+        L.orc_certified_decode_vb.restype = i32
         L.orc_dense_head.argtypes = [i32, i32, i32, i32, vp, vp, vp, f64, vp]
         _lib = L
     return _lib
@@ -101,13 +106,14 @@ class Result:
     trace: dict
 
 
-def certified_decode(k, v, q, thresholds, trace=True):
+def certified_decode(k, v, q, thresholds, trace=True, v_bits=4):
     """Run the oracle's decode step.
 
     k, v: uint16 FP16 bit patterns [B][T][Hkv][d]; q: uint16 [B][Hq][d].
     thresholds: dict of Thresholds fields.  Returns outputs [B][Hq][d] (FP64),
     the per-head report and (if ``trace``) every intermediate named in
-    ckv_oracle.h.
+    ckv_oracle.h.  v_bits: 4 (INT4 values, the design) or 8 (the symmetric
+    cache configuration, values at the keys' width).
     """
     k = np.ascontiguousarray(k, np.uint16)
     v = np.ascontiguousarray(v, np.uint16)
@@ -125,7 +131,7 @@ def certified_decode(k, v, q, thresholds, trace=True):
     if trace:
         shapes = dict(
             k_code=((B, Hkv, N, 64, d), np.uint8), k_s=((B, Hkv, N, d), np.uint16),
-            k_z=((B, Hkv, N, d), np.uint16), v_code=((B, Hkv, N, 64, d // 2), np.uint8),
+            k_z=((B, Hkv, N, d), np.uint16), v_code=((B, Hkv, N, 64, d * v_bits // 8), np.uint8),
             v_s=((B, Hkv, N, 64, ng), np.uint16), v_z=((B, Hkv, N, 64, ng), np.uint16),
             eta=((B, Hkv, N), np.float32), vrange=((B, Hkv), np.float32),
             score=((B, Hq, Np * 64), np.float32), bmax=((B, Hq, Np), np.float32),
@@ -140,7 +146,7 @@ def certified_decode(k, v, q, thresholds, trace=True):
             tr[f] = np.zeros(shp, dt)
             setattr(ctr, f, tr[f].ctypes.data if tr[f].size else None)
     th = Thresholds(**thresholds)
-    rc = lib().orc_certified_decode(B, T, Hq, Hkv, d, _p(k), _p(v), _p(q), ctypes.byref(th),
+    rc = lib().orc_certified_decode_vb(B, T, Hq, Hkv, d, v_bits, _p(k), _p(v), _p(q), ctypes.byref(th),
                                     _p(out), _p(rep), ctypes.byref(ctr))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
@@ -163,14 +169,14 @@ def quant_k_block(kblk):
     return code, s, z
 
 
-def quant_v_block(vblk):
+def quant_v_block(vblk, bits=4):
     vblk = np.ascontiguousarray(vblk, np.uint16)
     d = vblk.shape[1]
-    code = np.zeros((64, d // 2), np.uint8)
+    code = np.zeros((64, d * bits // 8), np.uint8)
     s = np.zeros((64, d // 32), np.uint16)
     z = np.zeros((64, d // 32), np.uint16)
     eta = np.zeros(1, np.float32)
-    lib().orc_quant_v_block(d, _p(vblk), _p(code), _p(s), _p(z), _p(eta))
+    lib().orc_quant_v_block_bits(d, bits, _p(vblk), _p(code), _p(s), _p(z), _p(eta))
     return code, s, z, float(eta[0])
 
 

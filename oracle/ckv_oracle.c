@@ -254,12 +254,18 @@ void orc_quant_k_block(int d, const uint16_t *k, uint8_t *code, uint16_t *s, uin
 }
 
 /* v: [64][d] FP16.  eta = max |v - (z + s*code)| over the block, exact in
- * FP64 and rounded up to FP32 (reading of the per-block annotation). */
-void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z, float *eta)
+ * FP64 and rounded up to FP32 (reading of the per-block annotation).
+ * bits = 4: the design's INT4 values, two codes per byte (low nibble = even
+ * channel), [64][d/2]; bits = 8: the symmetric cache configuration of
+ * [Signif] (values at the keys' width; reading: the same per-token groups
+ * of 32 channels, 255 levels), one code per byte, [64][d]. */
+void orc_quant_v_block_bits(int d, int bits, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z,
+                            float *eta)
 {
     int ng = d / ORC_VG;
+    const int levels = bits == 8 ? 255 : 15;
     double emax = 0.0;
-    memset(code, 0, (size_t)ORC_BT * d / 2);
+    memset(code, 0, (size_t)ORC_BT * d * bits / 8);
     for (int t = 0; t < ORC_BT; t++) {
         for (int g = 0; g < ng; g++) {
             const uint16_t *row = v + (size_t)t * d + g * ORC_VG;
@@ -276,15 +282,18 @@ void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uin
             }
             if (lo == 0.0f)
                 zh = 0;
-            uint16_t sh = scale_for(lo, hi, 15.0f);
+            uint16_t sh = scale_for(lo, hi, (float)levels);
             s[t * ng + g] = sh;
             z[t * ng + g] = zh;
             float sf = orc_h2f(sh);
             for (int c = 0; c < ORC_VG; c++) {
                 float x = orc_h2f(row[c]);
-                int q = code_for(x, lo, sf, 15);
+                int q = code_for(x, lo, sf, levels);
                 int ch = g * ORC_VG + c;
-                code[(size_t)t * (d / 2) + ch / 2] |= (uint8_t)((ch & 1) ? (q << 4) : q);
+                if (bits == 8)
+                    code[(size_t)t * d + ch] = (uint8_t)q;
+                else
+                    code[(size_t)t * (d / 2) + ch / 2] |= (uint8_t)((ch & 1) ? (q << 4) : q);
                 double rec = (double)lo + (double)sf * (double)q;
                 double e = fabs((double)x - rec);
                 if (e > emax)
@@ -293,6 +302,11 @@ void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uin
         }
     }
     *eta = orc_ru32(emax);
+}
+
+void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z, float *eta)
+{
+    orc_quant_v_block_bits(d, 4, v, code, s, z, eta);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -701,8 +715,18 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
                          const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
                          double *out, orc_report *rep, orc_trace *tr)
 {
-    if (B < 1 || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || (d != 64 && d != 128))
+    return orc_certified_decode_vb(B, T, Hq, Hkv, d, 4, K, V, q, th, out, rep, tr);
+}
+
+int orc_certified_decode_vb(int B, int T, int Hq, int Hkv, int d, int v_bits, const uint16_t *K,
+                            const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
+                            double *out, orc_report *rep, orc_trace *tr)
+{
+    if (B < 1 || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || (d != 64 && d != 128) ||
+        (v_bits != 4 && v_bits != 8))
         return -1;
+    /* bytes of value codes per token */
+    const size_t vcb = (size_t)d * v_bits / 8;
     const int G = Hq / Hkv, N = T / ORC_BT, np = T % ORC_BT, has_part = np > 0,
               Np = N + has_part, ng = d / ORC_VG;
     const double sm = (double)th->sm_scale;
@@ -715,7 +739,7 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
     size_t nb = (size_t)(N > 0 ? N : 1);
     uint8_t *kc = (uint8_t *)malloc(nb * ORC_BT * d);
     uint16_t *ks = (uint16_t *)malloc(nb * d * 2), *kz = (uint16_t *)malloc(nb * d * 2);
-    uint8_t *vc = (uint8_t *)malloc(nb * ORC_BT * d / 2);
+    uint8_t *vc = (uint8_t *)malloc(nb * ORC_BT * vcb);
     uint16_t *vs = (uint16_t *)malloc(nb * ORC_BT * ng * 2), *vz = (uint16_t *)malloc(nb * ORC_BT * ng * 2);
     float *eta = (float *)malloc(nb * sizeof(float));
     uint16_t *blk = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
@@ -745,7 +769,7 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
     float *smix = (float *)malloc((size_t)Np * ORC_BT * sizeof(float));
     float *allsmix = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
     /* quantized tier 1 of all kv heads of the sequence (needed for outputs) */
-    uint8_t *all_vc = (uint8_t *)malloc((size_t)Hkv * nb * ORC_BT * d / 2);
+    uint8_t *all_vc = (uint8_t *)malloc((size_t)Hkv * nb * ORC_BT * vcb);
     uint16_t *all_vs = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * ng * 2);
     uint16_t *all_vz = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * ng * 2);
 
@@ -763,8 +787,8 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
                         blv[t * d + c] = Vn[src];
                     }
                 orc_quant_k_block(d, blk, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d);
-                orc_quant_v_block(d, blv, vc + (size_t)b * ORC_BT * d / 2, vs + (size_t)b * ORC_BT * ng,
-                                  vz + (size_t)b * ORC_BT * ng, &eta[b]);
+                orc_quant_v_block_bits(d, v_bits, blv, vc + (size_t)b * ORC_BT * vcb, vs + (size_t)b * ORC_BT * ng,
+                                       vz + (size_t)b * ORC_BT * ng, &eta[b]);
             }
             size_t gofs = ((size_t)n * Hkv + g) * N;
             if (tr->k_code)
@@ -774,14 +798,14 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
             if (tr->k_z)
                 memcpy(tr->k_z + gofs * d, kz, (size_t)N * d * 2);
             if (tr->v_code)
-                memcpy(tr->v_code + gofs * ORC_BT * d / 2, vc, (size_t)N * ORC_BT * d / 2);
+                memcpy(tr->v_code + gofs * ORC_BT * vcb, vc, (size_t)N * ORC_BT * vcb);
             if (tr->v_s)
                 memcpy(tr->v_s + gofs * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
             if (tr->v_z)
                 memcpy(tr->v_z + gofs * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
             if (tr->eta)
                 memcpy(tr->eta + gofs, eta, (size_t)N * sizeof(float));
-            memcpy(all_vc + (size_t)g * nb * ORC_BT * d / 2, vc, (size_t)N * ORC_BT * d / 2);
+            memcpy(all_vc + (size_t)g * nb * ORC_BT * vcb, vc, (size_t)N * ORC_BT * vcb);
             memcpy(all_vs + (size_t)g * nb * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
             memcpy(all_vz + (size_t)g * nb * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
 
@@ -939,7 +963,7 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
             int g = h / G;
             const uint16_t *Vg = Vn;
             const float *smh = allsmix + (size_t)h * Np * ORC_BT;
-            const uint8_t *vcg = all_vc + (size_t)g * nb * ORC_BT * d / 2;
+            const uint8_t *vcg = all_vc + (size_t)g * nb * ORC_BT * vcb;
             const uint16_t *vsg = all_vs + (size_t)g * nb * ORC_BT * ng;
             const uint16_t *vzg = all_vz + (size_t)g * nb * ORC_BT * ng;
             double *oc = ocert + (size_t)h * d;
@@ -985,8 +1009,13 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
                     double v = (double)orc_h2f(Vg[((size_t)t * Hkv + g) * d + c]);
                     double vu = v;
                     if (b < N && !p->inVP[b]) {
-                        uint8_t byte = vcg[((size_t)b * ORC_BT + tt) * (d / 2) + c / 2];
-                        int code = (c & 1) ? (byte >> 4) : (byte & 15);
+                        int code;
+                        if (v_bits == 8) {
+                            code = vcg[((size_t)b * ORC_BT + tt) * d + c];
+                        } else {
+                            uint8_t byte = vcg[((size_t)b * ORC_BT + tt) * (d / 2) + c / 2];
+                            code = (c & 1) ? (byte >> 4) : (byte & 15);
+                        }
                         size_t mi = ((size_t)b * ORC_BT + tt) * ng + c / ORC_VG;
                         vu = (double)orc_h2f(vzg[mi]) + (double)orc_h2f(vsg[mi]) * (double)code;
                     }

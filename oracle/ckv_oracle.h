@@ -54,7 +54,7 @@ typedef struct {
     uint8_t *k_code;   /* [B][Hkv][N][64][d]    INT8 key codes, token-major   */
     uint16_t *k_s;     /* [B][Hkv][N][d]        FP16 key scale per channel    */
     uint16_t *k_z;     /* [B][Hkv][N][d]        FP16 key offset per channel   */
-    uint8_t *v_code;   /* [B][Hkv][N][64][d/2]  INT4 pairs, low nibble = even */
+    uint8_t *v_code;   /* [B][Hkv][N][64][d*v_bits/8]  INT4 pairs (low nibble = even) or INT8 */
     uint16_t *v_s;     /* [B][Hkv][N][64][d/32] FP16 value scale per group    */
     uint16_t *v_z;     /* [B][Hkv][N][64][d/32] FP16 value offset per group   */
     float *eta;        /* [B][Hkv][N]           per-block value error eta_b   */
@@ -93,6 +93,8 @@ uint64_t orc_fx(double t);
 
 void orc_quant_k_block(int d, const uint16_t *k, uint8_t *code, uint16_t *s, uint16_t *z);
 void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z, float *eta);
+void orc_quant_v_block_bits(int d, int bits, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z,
+                            float *eta);
 void orc_score_q8(int d, const uint16_t *q, const uint8_t *code, const uint16_t *s,
                   const uint16_t *z, float sm, float *out);
 void orc_score_f16(int d, const uint16_t *q, const uint16_t *k, int n, float sm, float *out);
@@ -114,6 +116,11 @@ int64_t orc_discordant(int n, const uint64_t *key_a, const uint64_t *key_b);
 int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K,
                          const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
                          double *out, orc_report *rep, orc_trace *tr);
+/* The same with the values at v_bits = 4 (the design) or 8 (the symmetric
+ * cache configuration of [Signif]). */
+int orc_certified_decode_vb(int B, int T, int Hq, int Hkv, int d, int v_bits, const uint16_t *K,
+                            const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
+                            double *out, orc_report *rep, orc_trace *tr);
 
 /* Exact softmax attention in FP64 for one (sequence, q head); the "FP16
  * reference" of [Signif].  k, v: [T][Hkv][d] of one sequence. */

@@ -200,6 +200,40 @@ def test_int4_value_quantizer_invariants(d):
         assert eta == float(ru)                                   # eta_b = max error, rounded up
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_value_quantizer_invariants(d):
+    """The symmetric configuration's values: one byte per value, 255 levels
+    per (token, 32-channel group); the same invariants as INT4 and a brute
+    force nearest-level check; the INT4 codes of the same block are the
+    8-bit quantizer's structure at 15 levels (cross-check of the shared
+    scale / offset rule)."""
+    rng = np.random.default_rng(5)
+    for vb in _k_blocks(rng, d):
+        code, s, z, eta = oracle.quant_v_block(vb, bits=8)
+        assert code.shape == (64, d)
+        vf = h2f(vb)
+        sf = np.repeat(h2f(s), 32, axis=1)
+        zf = np.repeat(h2f(z), 32, axis=1)
+        grp = vf.reshape(64, d // 32, 32)
+        assert np.array_equal(h2f(z), grp.min(axis=2))
+        assert np.all(h2f(s) * 255.0 >= grp.max(axis=2) - grp.min(axis=2))
+        rec = zf + sf * code.astype(np.int64)
+        err = np.abs(vf - rec)
+        assert np.all(err <= sf * (0.5 + 2.0 ** -14))
+        lv = zf[None] + sf[None] * np.arange(256)[:, None, None]
+        best = np.abs(vf[None] - lv).min(axis=0)
+        assert np.all(err <= best + sf * 2.0 ** -14)
+        emax = err.max()
+        ru = np.float32(emax)
+        if float(ru) < emax:
+            ru = np.nextafter(ru, np.float32(np.inf))
+        assert eta == float(ru)
+        # 8-bit steps are (at least) 17x finer than the 4-bit ones
+        _, s4, z4, eta4 = oracle.quant_v_block(vb)
+        assert np.array_equal(z4, z)
+        assert eta <= eta4
+
+
 # -- scores and the perturbation bound [Meth-2] --------------------------------
 
 def _adversarial_block(rng, d, q):

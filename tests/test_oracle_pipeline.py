@@ -57,15 +57,16 @@ def certified_heads(res):
     return res.report["rung_max"] < 3
 
 
+@pytest.mark.parametrize("v_bits", [4, 8])
 @pytest.mark.parametrize("seed", range(12))
-def test_bounds_dominate_measured_errors(seed):
+def test_bounds_dominate_measured_errors(seed, v_bits):
     kind = KINDS[seed % len(KINDS)]
     T = [512, 640, 1000, 200, 64, 130][seed % 6]
     Hq, Hkv = [(4, 1), (8, 2), (2, 2)][seed % 3]
     k, v, q, sm = micro(seed, T=T, Hq=Hq, Hkv=Hkv, kind=kind)
     # tolerances and rank_tol out of reach: every head stays certified
     th = oracle.default_thresholds(sm, k_tol=1e30, v_tol=1e30, rank_tol=1.0)
-    r = oracle.certified_decode(k, v, q, th)
+    r = oracle.certified_decode(k, v, q, th, v_bits=v_bits)
     tr = r.trace
     ok = certified_heads(r)
     assert ok.all()
@@ -76,6 +77,33 @@ def test_bounds_dominate_measured_errors(seed):
     assert np.all(dist <= ek + ev + 1e-12)
     # reported bounds are the plan's bounds rounded up to FP32
     assert np.all(r.report["e_key"] >= ek) and np.all(r.report["e_val"] >= ev)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_symmetric_values_only_change_the_value_term(seed):
+    """INT8 values (the symmetric configuration) against INT4 values on the
+    same layer: keys, scores, selection, K* and E_key are identical (the
+    value width enters nothing on the key side), eta_b and E_val shrink,
+    and the output is closer to exact attention in the plain quantized mode."""
+    kind = KINDS[seed % len(KINDS)]
+    k, v, q, sm = micro(200 + seed, T=[512, 1000, 130][seed % 3], Hq=8, Hkv=2, kind=kind)
+    th = oracle.default_thresholds(sm, v_tol=1e30, k_tol=1e30, rank_tol=1.0)
+    r4 = oracle.certified_decode(k, v, q, th)
+    r8 = oracle.certified_decode(k, v, q, th, v_bits=8)
+    for f in ("k_code", "k_s", "k_z", "score", "mfx", "score16"):
+        assert np.array_equal(r4.trace[f], r8.trace[f]), f
+    assert np.array_equal(r4.trace["sel"] & 1, r8.trace["sel"] & 1)
+    assert np.array_equal(r4.report["kstar"], r8.report["kstar"])
+    assert np.array_equal(r4.trace["bounds"][..., 2], r8.trace["bounds"][..., 2])
+    assert np.all(r8.trace["eta"] <= r4.trace["eta"])
+    assert np.all(r8.trace["bounds"][..., 3] <= r4.trace["bounds"][..., 3])
+    thn = oracle.default_thresholds(sm, tau_cov=0.0, k_tol=float("inf"), v_tol=float("inf"), rank_tol=1.0)
+    n4 = oracle.certified_decode(k, v, q, thn)
+    n8 = oracle.certified_decode(k, v, q, thn, v_bits=8)
+    d4 = np.abs(n4.out - n4.trace["o_dense"]).max(axis=2)
+    d8 = np.abs(n8.out - n8.trace["o_dense"]).max(axis=2)
+    assert np.all(d8 <= n8.trace["bounds"][..., 2] + n8.trace["bounds"][..., 3] + 1e-12)
+    assert d8.max() <= d4.max()
 
 
 @pytest.mark.parametrize("seed", range(6))
