@@ -29,7 +29,7 @@ class Config(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int), ("max_batch", ctypes.c_int),
                 ("n_q_heads", ctypes.c_int), ("n_kv_heads", ctypes.c_int),
                 ("head_dim", ctypes.c_int), ("max_context", ctypes.c_int),
-                ("device", ctypes.c_int)]
+                ("device", ctypes.c_int), ("v_bits", ctypes.c_int)]
 
 
 class Thresholds(ctypes.Structure):
@@ -116,12 +116,14 @@ def _stream_ptr(stream):
 
 class Cache:
     """A tiered KV cache: tier 1 (INT8 K / INT4 V / metadata / annotations)
-    on the GPU, tier 2 (FP16 originals) in pinned host memory."""
+    on the GPU, tier 2 (FP16 originals) in pinned host memory.  v_bits = 8
+    stores the values at 8 bits (the symmetric cache configuration)."""
 
-    def __init__(self, n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_context, device=0):
-        self.cfg = Config(n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_context, device)
+    def __init__(self, n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_context, device=0, v_bits=4):
+        self.cfg = Config(n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_context, device, v_bits)
         self.n_layers, self.max_batch = n_layers, max_batch
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
+        self.v_bits = v_bits
         self.device = device
         h = ctypes.c_void_p()
         _check(lib().ckv_create(ctypes.byref(self.cfg), ctypes.byref(h)))
@@ -225,7 +227,7 @@ class Cache:
     def export_block(self, layer, seq, kv_head, block):
         d = self.d
         r = dict(k_code=np.zeros((64, d), np.uint8), k_s=np.zeros(d, np.uint16),
-                 k_z=np.zeros(d, np.uint16), v_code=np.zeros((64, d // 2), np.uint8),
+                 k_z=np.zeros(d, np.uint16), v_code=np.zeros((64, d * self.v_bits // 8), np.uint8),
                  v_s=np.zeros((64, d // 32), np.uint16), v_z=np.zeros((64, d // 32), np.uint16),
                  eta=np.zeros(1, np.float32))
         _check(lib().ckv_export_block(self._h, layer, seq, kv_head, block,

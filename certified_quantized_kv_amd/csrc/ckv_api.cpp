@@ -225,6 +225,8 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         k.n_q_heads % k.n_kv_heads || (k.head_dim != 64 && k.head_dim != 128) || k.max_context < 1)
         return fail(CKV_EINVAL, "bad cache shape");
     const int G = k.n_q_heads / k.n_kv_heads;
+    const int vbits = k.v_bits == 0 ? 4 : k.v_bits;
+    if (vbits != 4 && vbits != 8) return fail(CKV_EINVAL, "v_bits must be 4 or 8");
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(CKV_EINVAL, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
     const int Nmax = (k.max_context + 63) / 64;
@@ -260,11 +262,12 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     } while (0)
     Layout &Ly = c->Ly;
     Ly.L = L; Ly.B = B; Ly.Hq = Hq; Ly.Hkv = Hkv; Ly.d = d; Ly.G = G; Ly.Nmax = Nmax;
+    Ly.vb = vbits;
     // tier 1 [Meth-1]
     size_t before = c->dev_bytes;
     CTRY(dalloc(c, &Ly.kq, nblk * 64 * d));
     CTRY(dalloc(c, &Ly.kmeta, nblk * d));
-    CTRY(dalloc(c, &Ly.vq, nblk * 64 * (d / 2)));
+    CTRY(dalloc(c, &Ly.vq, nblk * 64 * d * vbits / 8));
     CTRY(dalloc(c, &Ly.vmeta, nblk * 64 * (d / 32)));
     CTRY(dalloc(c, &Ly.eta, nblk));
     c->tier1_bytes = c->dev_bytes - before;
@@ -907,7 +910,13 @@ ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int g, int b, uint
             if (k_z) k_z[ch] = (uint16_t)(m[ch] >> 16);
         }
     }
-    if (v_code) {
+    if (v_code && Ly.vb == 8) {
+        // stored channel-major (byte c * 64 + t)
+        std::vector<uint8_t> raw((size_t)64 * d);
+        HIPCHK(hipMemcpy(raw.data(), Ly.vq + bi * 64 * d, raw.size(), hipMemcpyDeviceToHost));
+        for (int t = 0; t < 64; ++t)
+            for (int ch = 0; ch < d; ++ch) v_code[t * d + ch] = raw[ch * 64 + t];
+    } else if (v_code) {
         // stored channel-major (byte c * 32 + t / 2, low nibble = even t)
         std::vector<uint8_t> raw((size_t)64 * (d / 2));
         HIPCHK(hipMemcpy(raw.data(), Ly.vq + bi * 64 * (d / 2), raw.size(), hipMemcpyDeviceToHost));

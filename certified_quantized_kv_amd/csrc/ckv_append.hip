@@ -80,9 +80,10 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
         // of the scoring pass's integer matrix product
         for (int t = 0; t < 64; ++t) kq[t * 16] = (uint8_t)(quant_code(h2f(col[t * 8]), lo, sf, 255.0f) ^ 0x80);
     }
-    // values: one thread per token; the codes are staged in LDS and packed
-    // channel-major, two tokens per byte
+    // values: one thread per token; the codes are staged in LDS and stored
+    // channel-major, two tokens per byte (INT4) or one (INT8)
     __shared__ uint8_t cq[D][64];
+    const float levels = Ly.vb == 8 ? 255.0f : 15.0f;
     double emax = 0.0;
     if (tid < 64) {
         const int t = tid;
@@ -96,13 +97,13 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
                 hi = fmaxf(hi, x);
             }
             const float r = hi - lo;
-            const uint16_t sb = r == 0.0f ? (uint16_t)0 : f2h_up(r / 15.0f);
+            const uint16_t sb = r == 0.0f ? (uint16_t)0 : f2h_up(r / levels);
             const uint16_t zb = lo == 0.0f ? (uint16_t)0 : __half_as_ushort(__float2half_rn(lo));
             const float sf = h2f(sb);
             vm[gr * 64 + t] = (uint32_t)sb | ((uint32_t)zb << 16);
             for (int c = 0; c < 32; ++c) {
                 const float x = h2f(col[c * 64]);
-                const int q = quant_code(x, lo, sf, 15.0f);
+                const int q = quant_code(x, lo, sf, levels);
                 cq[gr * 32 + c][t] = (uint8_t)q;
                 const double rec = (double)lo + (double)sf * (double)q;
                 emax = fmax(emax, fabs((double)x - rec));
@@ -111,10 +112,15 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
     }
     emax_s[tid] = emax;
     __syncthreads();
-    uint8_t *vq = Ly.vq + blk * 64 * (D / 2);
-    for (int e = tid; e < D * 32; e += 128) {
-        const int c = e / 32, j = e % 32;
-        vq[c * 32 + j] = (uint8_t)(cq[c][2 * j] | (cq[c][2 * j + 1] << 4));
+    if (Ly.vb == 8) {
+        uint8_t *vq = Ly.vq + blk * 64 * D;
+        for (int e = tid; e < D * 64; e += 128) vq[e] = cq[e / 64][e % 64];
+    } else {
+        uint8_t *vq = Ly.vq + blk * 64 * (D / 2);
+        for (int e = tid; e < D * 32; e += 128) {
+            const int c = e / 32, j = e % 32;
+            vq[c * 32 + j] = (uint8_t)(cq[c][2 * j] | (cq[c][2 * j + 1] << 4));
+        }
     }
     if (tid == 0) {
         double m = 0.0;
@@ -162,13 +168,14 @@ __global__ __launch_bounds__(128) void k_vrange(Layout Ly, int l, int n, const u
 }
 
 // K of a value group from its range R (largest max minus smallest min over
-// the group's channels): the smallest power of two P >= R / 15 (1 + 2^-8)
-// bounds every INT4 scale of the group (scale = range / 15 rounded up to
-// FP16, so scale <= R / 15 (1 + 2^-10)(1 + 2^-23)), and K = 2^14 / P, kept
-// in [1, 2^15].  The value passes weight INT4 codes by p s K and FP16 values
-// by p K, both below 2^15, before splitting the weights into FP16 parts.
-__device__ __forceinline__ float value_scale(double R) {
-    const double x = R / 15.0 * (1.0 + 0x1p-8);
+// the group's channels): the smallest power of two P >= R / lv (1 + 2^-8)
+// bounds every scale of the group (lv = 15 levels for INT4, 255 for INT8;
+// scale = range / lv rounded up to FP16, so scale <= R / lv (1 + 2^-10)
+// (1 + 2^-23)), and K = 2^14 / P, kept in [1, 2^15].  The value passes
+// weight the codes by p s K and FP16 values by p K, both below 2^15, before
+// splitting the weights into FP16 parts.
+__device__ __forceinline__ float value_scale(double R, double lv) {
+    const double x = R / lv * (1.0 + 0x1p-8);
     if (!(x > 0.0)) return 0x1p15f;
     int e;
     (void)frexp(x, &e);  // x < 2^e
@@ -187,7 +194,7 @@ __global__ void k_vscale(Layout Ly, int l, int n) {
         lo = fminf(lo, ord2f(Ly.vmin[base + c]));
         hi = fmaxf(hi, ord2f(Ly.vmax[base + c]));
     }
-    Ly.vscale[Ly.seqg(l, n, g) * ng + gr] = value_scale((double)hi - (double)lo);
+    Ly.vscale[Ly.seqg(l, n, g) * ng + gr] = value_scale((double)hi - (double)lo, Ly.vb == 8 ? 255.0 : 15.0);
 }
 
 hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,

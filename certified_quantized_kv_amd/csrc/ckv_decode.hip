@@ -778,6 +778,20 @@ __device__ __forceinline__ v8h int4_operand(uint32_t w) {
     return __builtin_bit_cast(v8h, r);
 }
 
+// Eight INT8 codes (tokens 0-3 in lo, 4-7 in hi, one byte each) as an FP16
+// operand of subnormals in the same token order as int4_operand: register r
+// holds tokens (r, r + 4), unscaled.
+__device__ __forceinline__ v8h int8_operand(uint32_t lo, uint32_t hi) {
+    const v4u r = {__builtin_amdgcn_perm(hi, lo, 0x0C040C00u), __builtin_amdgcn_perm(hi, lo, 0x0C050C01u),
+                   __builtin_amdgcn_perm(hi, lo, 0x0C060C02u), __builtin_amdgcn_perm(hi, lo, 0x0C070C03u)};
+    return __builtin_bit_cast(v8h, r);
+}
+
+// Value codes of one channel for a lane's 16 tokens: INT4 (8 bytes) or
+// INT8 (16 bytes).
+template <bool V8>
+using CodeWord = typename std::conditional<V8, uint4, uint2>::type;
+
 // x = hi + lo + err with FP16 hi, lo (round toward zero);
 // |err| <= max(2^-20 |x|, 2^-24).
 __device__ __forceinline__ void split_pair(float x, float y, uint32_t &hi, uint32_t &lo) {
@@ -877,11 +891,13 @@ struct VAcc {
             }
         }
     }
-    // INT4 values for the heads in `mask`.  p: weights (A layout); cw[nt]:
-    // the codes of channel 16 nt + lane % 16 for tokens 16 (lane / 16) + 0..15;
-    // mt[rt]: scale | offset words of the A row's group for the same tokens.
+    // INT4 (INT8 if V8) values for the heads in `mask`.  p: weights (A
+    // layout); cw[nt]: the codes of channel 16 nt + lane % 16 for tokens
+    // 16 (lane / 16) + 0..15; mt[rt]: scale | offset words of the A row's
+    // group for the same tokens.
+    template <bool V8>
     __device__ __forceinline__ void int4_block(uint32_t mask, const float (&p)[RT][16], const v4u (&mt)[RT][4],
-                                               const uint2 (&cw)[NT], const float *ksg, int lane) {
+                                               const CodeWord<V8> (&cw)[NT], const float *ksg, int lane) {
         v8h ahi[RT][2], alo[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -893,9 +909,9 @@ struct VAcc {
             for (int i = 0; i < 16; ++i) {
                 const uint32_t mw = mt[rt][i / 4][i % 4];
                 const float s = h2f((uint16_t)(mw & 0xFFFFu)), zz = h2f((uint16_t)(mw >> 16));
-                // odd registers of the operand (tokens 1, 3, 5, 7 of each
-                // 8) carry codes scaled by 16
-                a[i] = (p[rt][i] * s) * ((i & 1) ? K * 0.0625f : K);
+                // INT4: odd registers of the operand (tokens 1, 3, 5, 7 of
+                // each 8) carry codes scaled by 16
+                a[i] = (p[rt][i] * s) * ((!V8 && (i & 1)) ? K * 0.0625f : K);
                 z = fmaf(p[rt][i], zz, z);
             }
             zacc[rt] += on ? z : 0.0f;
@@ -915,7 +931,14 @@ struct VAcc {
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const v8h b0 = int4_operand(cw[nt].x), b1 = int4_operand(cw[nt].y);
+            v8h b0, b1;
+            if constexpr (V8) {
+                b0 = int8_operand(cw[nt].x, cw[nt].y);
+                b1 = int8_operand(cw[nt].z, cw[nt].w);
+            } else {
+                b0 = int4_operand(cw[nt].x);
+                b1 = int4_operand(cw[nt].y);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 v4f c = acc[rt][nt];
@@ -967,17 +990,20 @@ struct VAcc {
 };
 
 // Tier-1 value operands of block `bi` for this lane: INT4 codes (channel-
-// major, 32 bytes per channel) and the scale | offset words of the A rows'
-// groups (group-major, 64 words per group).
-template <int D, int G, bool F>
-__device__ __forceinline__ void load_int4(const Layout &Ly, size_t bi, int lane, uint2 (&cw)[D / 16],
+// major, 32 bytes per channel; INT8 if V8: 64 bytes per channel) and the
+// scale | offset words of the A rows' groups (group-major, 64 words per
+// group).
+template <int D, int G, bool F, bool V8>
+__device__ __forceinline__ void load_int4(const Layout &Ly, size_t bi, int lane, CodeWord<V8> (&cw)[D / 16],
                                           v4u (&mt)[VAcc<D, G, F>::RT][4]) {
     using VA = VAcc<D, G, F>;
-    const uint8_t *vq = Ly.vq + bi * 64 * (D / 2);
+    constexpr int CB = V8 ? 64 : 32;  // code bytes per channel
+    const uint8_t *vq = Ly.vq + bi * (size_t)(D * CB);
     const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
 #pragma unroll
     for (int nt = 0; nt < VA::NT; ++nt)
-        cw[nt] = *reinterpret_cast<const uint2 *>(vq + (16 * nt + (lane & 15)) * 32 + 8 * (lane >> 4));
+        cw[nt] = *reinterpret_cast<const CodeWord<V8> *>(vq + (16 * nt + (lane & 15)) * CB +
+                                                         (CB / 4) * (lane >> 4));
 #pragma unroll
     for (int rt = 0; rt < VA::RT; ++rt) {
         const v4u *src = reinterpret_cast<const v4u *>(vm + VA::agroup(rt, lane) * 64 + 16 * (lane >> 4));
@@ -1120,7 +1146,7 @@ __device__ __forceinline__ void write_partials(VAcc<D, G, F> &va, const float *k
 // ===========================================================================
 enum { VP_TAIL = 0, VP_INT4 = 1, VP_FP16 = 2 };
 
-template <int D, int G, int MODE>
+template <int D, int G, int MODE, bool V8>
 __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, const int *skip_seq) {
     constexpr bool F16 = MODE == VP_FP16;
     using VA = VAcc<D, G, false>;
@@ -1169,7 +1195,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     };
     struct Opd {
         uint4 vv[F16 ? VA::NT : 1][2];
-        uint2 cw[F16 ? 1 : VA::NT];
+        CodeWord<V8> cw[F16 ? 1 : VA::NT];
         v4u mt[F16 ? 1 : VA::RT][4];
         float s[G];  // scores, lane = token
     };
@@ -1200,7 +1226,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
             load_fp16v<D>(k.part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + (selbase + b) * 64 * D, lane,
                           o.vv);
         else
-            load_int4<D, G, false>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
+            load_int4<D, G, false, V8>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
         // scores of the group's heads: the FP16-key ones on P (promoted
         // passes), the INT8 ones elsewhere, zero for heads not served here
         // (an offset past the range: no memory access)
@@ -1224,7 +1250,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
         if constexpr (F16)
             va.fp16_block(k.use, sv, o.vv, lane);
         else
-            va.int4_block(k.use, sv, o.mt, o.cw, ksg, lane);
+            va.template int4_block<V8>(k.use, sv, o.mt, o.cw, ksg, lane);
     };
     // entries wave, wave + 4, ...: the next entry's operands in flight
     // while the current one is used
@@ -1253,20 +1279,20 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     write_partials<D, G, false>(va, ksg, part, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp, ALL, !F16);
 }
 
-// Three waves per SIMD where the registers allow.
-template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G * D <= 512 ? 3 : 2))) void k_tail(Layout Ly, Step St) {
-    values_pass<D, G, VP_TAIL>(Ly, St, nullptr);
+// Three waves per SIMD where the registers allow (INT4 codes, G d <= 512).
+template <int D, int G, bool V8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(!V8 && G * D <= 512 ? 3 : 2))) void k_tail(Layout Ly, Step St) {
+    values_pass<D, G, VP_TAIL, V8>(Ly, St, nullptr);
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G * D <= 512 ? 3 : 2))) void k_promoted4(Layout Ly, Step St, const int *skip_seq) {
-    values_pass<D, G, VP_INT4>(Ly, St, skip_seq);
+template <int D, int G, bool V8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(!V8 && G * D <= 512 ? 3 : 2))) void k_promoted4(Layout Ly, Step St, const int *skip_seq) {
+    values_pass<D, G, VP_INT4, V8>(Ly, St, skip_seq);
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_promoted16(Layout Ly, Step St, const int *skip_seq) {
-    values_pass<D, G, VP_FP16>(Ly, St, skip_seq);
+    values_pass<D, G, VP_FP16, false>(Ly, St, skip_seq);
 }
 
 constexpr int KEYS_PW = 4;             // list entries per wave of the FP16-key pass, at most
@@ -2032,8 +2058,12 @@ hipError_t launch_select(const Layout &Ly, const Step &St, const Th &th, hipStre
 
 hipError_t launch_tail(const Layout &Ly, const Step &St, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        hipLaunchKernelGGL((k_tail<decltype(D)::value, decltype(G)::value>),
-                           dim3(St.nsplit, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
+        if (Ly.vb == 8)
+            hipLaunchKernelGGL((k_tail<decltype(D)::value, decltype(G)::value, true>),
+                               dim3(St.nsplit, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
+        else
+            hipLaunchKernelGGL((k_tail<decltype(D)::value, decltype(G)::value, false>),
+                               dim3(St.nsplit, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
         return hipGetLastError();
     });
 }
@@ -2071,8 +2101,11 @@ hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, 
 hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         const int nsp4 = (St.nb + St.bps - 1) / St.bps;
-        if (nsp4 > 0)
-            hipLaunchKernelGGL((k_promoted4<decltype(D)::value, decltype(G)::value>),
+        if (nsp4 > 0 && Ly.vb == 8)
+            hipLaunchKernelGGL((k_promoted4<decltype(D)::value, decltype(G)::value, true>),
+                               dim3(nsp4, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
+        else if (nsp4 > 0)
+            hipLaunchKernelGGL((k_promoted4<decltype(D)::value, decltype(G)::value, false>),
                                dim3(nsp4, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
         return hipGetLastError();
     });

@@ -9,6 +9,7 @@
 //   kmeta u32 [d]              binary16 scale | binary16 offset << 16
 //   vq    u8  [d][32]          INT4 value codes, channel-major: byte
 //                              c * 32 + t / 2, low nibble = even token t
+//                              (vb = 8: u8 [d][64], byte c * 64 + t)
 //   vmeta u32 [d/32][64]       per (group, token): binary16 scale |
 //                              binary16 offset << 16
 //   eta   f32                  value-error annotation of the block
@@ -25,6 +26,7 @@ namespace ckv {
 
 struct Layout {
     int L, B, Hq, Hkv, d, G, Nmax;  // Nmax: full-block capacity per sequence
+    int vb;                         // value code width, 4 or 8
     uint8_t *kq;
     uint32_t *kmeta;
     uint8_t *vq;

@@ -55,6 +55,11 @@ typedef struct {
     int head_dim;
     int max_context;  /* tokens per sequence                               */
     int device;       /* HIP device ordinal                                */
+    int v_bits;       /* value code width: 4 (the design's asymmetric cache:
+                         INT8 keys, INT4 values; 0 also means 4) or 8 (the
+                         symmetric cache configuration of [Signif]: values
+                         at the keys' width, the same per-token 32-channel
+                         groups with 255 levels, one code per byte)       */
 } ckv_config;
 
 /* Thresholds of the certified decode step [Meth-3, Results].
@@ -104,8 +109,9 @@ ckv_status ckv_reset_sequence(ckv_cache *c, int seq);
  * k_fp16, v_fp16: [n_tokens][n_kv_heads][head_dim] binary16, in device
  *   memory if src_on_device, else in host memory; read before return.
  * Every completed 64-token block is quantized (INT8 keys with a per-channel
- * scale/offset per block, INT4 values with a scale/offset per token and
- * 32-channel group, the block's value-error annotation); tokens of an
+ * scale/offset per block, INT4 values (INT8 when v_bits = 8) with a
+ * scale/offset per token and 32-channel group, the block's value-error
+ * annotation); tokens of an
  * unfinished block stay FP16 on the device.  All tokens are copied to the
  * FP16 tier in host memory.  The call synchronizes `stream`.
  * Errors: EINVAL, ERANGE (would exceed max_context), EHIP. */
@@ -160,7 +166,8 @@ const char *ckv_last_error(void);
 
 /* Tier-1 contents of one block, in token-major layout:
  * k_code [64][d] u8, k_s, k_z [d] binary16, v_code [64][d/2] u8 (low nibble
- * = even channel), v_s, v_z [64][d/32] binary16, eta [1] FP32.  Host
+ * = even channel; [64][d] when v_bits = 8), v_s, v_z [64][d/32] binary16,
+ * eta [1] FP32.  Host
  * pointers; any may be NULL.  Errors: EINVAL (block not complete), EHIP. */
 ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int kv_head, int block,
                             uint8_t *k_code, uint16_t *k_s, uint16_t *k_z, uint8_t *v_code,

@@ -32,16 +32,16 @@ def f16(x):
     return np.asarray(x, np.float16).view(np.uint16)
 
 
-def make_cache(B, Hq, Hkv, d, T):
+def make_cache(B, Hq, Hkv, d, T, v_bits=4):
     import certified_quantized_kv_amd as ckv
-    return ckv.Cache(1, B, Hq, Hkv, d, T)
+    return ckv.Cache(1, B, Hq, Hkv, d, T, v_bits=v_bits)
 
 
-def gpu_run(k, v, q, th, chunks=None, cache=None):
+def gpu_run(k, v, q, th, chunks=None, cache=None, v_bits=4):
     """Append k, v ([B][T][Hkv][d] uint16) and run one decode step."""
     B, T, Hkv, d = k.shape
     Hq = q.shape[1]
-    c = cache or make_cache(B, Hq, Hkv, d, T)
+    c = cache or make_cache(B, Hq, Hkv, d, T, v_bits=v_bits)
     for n in range(B):
         if chunks is None:
             c.append_kv(0, n, k[n], v[n])
@@ -128,11 +128,11 @@ def check_parity(k, v, q, th, res, c, out, rep, step, seqs=None, kv_heads=None):
                 assert np.all(np.abs(out[n, h] - ref) <= ATOL + RTOL * np.abs(ref)), (n, h)
 
 
-def both(k, v, q, th, chunks=None):
+def both(k, v, q, th, chunks=None, v_bits=4):
     print(f"case B={k.shape[0]} T={k.shape[1]} Hkv={k.shape[2]} d={k.shape[3]} Hq={q.shape[1]} "
-          f"th={th}", flush=True)
-    res = oracle.certified_decode(k, v, q, th)
-    c, out, rep, step = gpu_run(k, v, q, th, chunks=chunks)
+          f"v_bits={v_bits} th={th}", flush=True)
+    res = oracle.certified_decode(k, v, q, th, v_bits=v_bits)
+    c, out, rep, step = gpu_run(k, v, q, th, chunks=chunks, v_bits=v_bits)
     check_parity(k, v, q, th, res, c, out, rep, step)
     c.close()
     return res, rep
@@ -193,6 +193,26 @@ def test_head_shapes_and_distributions(shape, kind):
     seed = zlib.crc32(repr((shape, kind)).encode()) % 1000
     k, v, q, sm = micro(seed, T=[640, 1000, 130][seed % 3], Hq=Hq, Hkv=Hkv, d=d, B=2, kind=kind)
     both(k, v, q, oracle.default_thresholds(sm))
+
+
+@pytest.mark.parametrize("case", range(len(THRESHOLD_CASES)))
+def test_symmetric_cache_tiny_config_all_rungs(case):
+    """INT8 values (the symmetric cache configuration): codes, eta_b and every
+    intermediate and output against the oracle run at 8-bit values."""
+    L = datagen.make_layer("tiny_1k", 0)
+    th = oracle.default_thresholds(L.sm, **THRESHOLD_CASES[case])
+    both(L.k, L.v, L.q, th, v_bits=8)
+
+
+@pytest.mark.parametrize("shape", [(4, 1, 64), (8, 2, 64), (16, 2, 128), (8, 1, 128)])
+@pytest.mark.parametrize("kind", ["normal", "heavy", "flat"])
+def test_symmetric_cache_head_shapes(shape, kind):
+    Hq, Hkv, d = shape
+    seed = zlib.crc32(repr((shape, kind, 8)).encode()) % 1000
+    k, v, q, sm = micro(seed, T=[640, 1000, 130][seed % 3], Hq=Hq, Hkv=Hkv, d=d, B=2, kind=kind)
+    both(k, v, q, oracle.default_thresholds(sm, tau_cov=0.0, k_tol=float("inf"), v_tol=float("inf")),
+         v_bits=8)
+    both(k, v, q, oracle.default_thresholds(sm), v_bits=8)
 
 
 def test_single_token_and_single_block():
