@@ -209,7 +209,7 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
     }
 
     if not args.no_extras:
-        extra_lines(rec, args, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
+        extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
                     ms_step, decode_steps)
     cache.close()
     del dense_kv
@@ -228,7 +228,7 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
     return rec
 
 
-def extra_lines(rec, args, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
+def extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
                 ms_step, decode_steps):
     """Comparison lines after the headline layer-steps: device-initiated
     paging, the threshold variants against dense attention, the decode loop
@@ -259,6 +259,7 @@ def extra_lines(rec, args, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, 
 
     if n_dense:
         rec["variants"] = variants(cache, dense_kv, qs, th, T, sm, n_dense)
+        rec["cache_configs"] = cache_configs(name, cfg, cache, dense_kv, qs, th, T, sm, n_dense)
 
     if decode_steps:
         rec["decode_loop"] = decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, decode_steps)
@@ -328,6 +329,48 @@ def variants(cache, dense_kv, qs, th, T, sm, n):
                     "rungs_max_hist": np.bincount(np.concatenate([r["rung_max"].ravel() for r in reps]),
                                                   minlength=5).tolist()}
         log(f"variant {tag}: {res[tag]}")
+    return res
+
+
+def cache_configs(name, cfg, cache, dense_kv, qs, th, T, sm, n):
+    """The design's asymmetric cache (INT8 keys, INT4 values) against the
+    symmetric one (values at the keys' 8 bits) on the first n layers, each in
+    a cache of its own: tier-1 bytes per token and kv head (and against the
+    2 d bytes of FP16 K + V), certified and plain quantized latency, and the
+    error against dense attention on the FP16 originals."""
+    import numpy as np
+    import torch
+
+    import certified_quantized_kv_amd as ckv
+    import datagen
+    B, Hq, Hkv, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    inf = float("inf")
+    dense = [cache.dense_decode_attention(kb, vb, T, qs[l], sm).clone() for l, (kb, vb) in enumerate(dense_kv[:n])]
+    res = {}
+    for vbits in (4, 8):
+        c = ckv.Cache(n, B, Hq, Hkv, d, T, device=0, v_bits=vbits)
+        for l in range(n):
+            lay = datagen.make_layer(name, l)
+            for s_ in range(B):
+                c.append_kv(l, s_, lay.k[s_], lay.v[s_])
+        per_tok = c.footprint()["tier1"] / (n * B * Hkv * T)
+        r = {"tier1_bytes_per_token_per_kv_head": round(per_tok, 2),
+             "tier1_vs_fp16_kv": round(per_tok / (4 * d), 4)}
+        for tag, thv in (("certified", dict(th)), ("plain_quantized", dict(th, tau_cov=0.0, k_tol=inf, v_tol=inf))):
+            for l in range(n):
+                c.certified_decode_attention(l, qs[l], thv)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            outs = [c.certified_decode_attention(l, qs[l], thv) for _ in range(2) for l in range(n)]
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t1
+            err = max(float((o - dense[i % n]).abs().max()) for i, (o, _) in enumerate(outs))
+            r[tag] = {"ms_per_step": round(1e3 * el / (2 * n), 4), "max_abs_err_vs_dense": float(f"{err:.3g}"),
+                      "e_val_max": float(f"{max(float(rp['e_val'].max()) for _, rp in outs):.3g}"),
+                      "v_promoted_mean": round(float(np.mean([rp["n_v_promoted"].mean() for _, rp in outs])), 2)}
+        c.close()
+        res["asymmetric_int8_int4" if vbits == 4 else "symmetric_int8_int8"] = r
+        log(f"cache config v_bits={vbits}: {r}")
     return res
 
 
