@@ -57,7 +57,7 @@ typedef struct {
     int device;       /* HIP device ordinal                                */
     int v_bits;       /* value code width: 4 (the design's asymmetric cache:
                          INT8 keys, INT4 values; 0 also means 4) or 8 (the
-                         symmetric cache configuration of [Signif]: values
+                         symmetric cache configuration of [Results]: values
                          at the keys' width, the same per-token 32-channel
                          groups with 255 levels, one code per byte)       */
 } ckv_config;

@@ -257,7 +257,7 @@ void orc_quant_k_block(int d, const uint16_t *k, uint8_t *code, uint16_t *s, uin
  * FP64 and rounded up to FP32 (reading of the per-block annotation).
  * bits = 4: the design's INT4 values, two codes per byte (low nibble = even
  * channel), [64][d/2]; bits = 8: the symmetric cache configuration of
- * [Signif] (values at the keys' width; reading: the same per-token groups
+ * [Results] (values at the keys' width; reading: the same per-token groups
  * of 32 channels, 255 levels), one code per byte, [64][d]. */
 void orc_quant_v_block_bits(int d, int bits, const uint16_t *v, uint8_t *code, uint16_t *s, uint16_t *z,
                             float *eta)

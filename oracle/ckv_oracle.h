@@ -12,6 +12,7 @@
  *   [Meth-2]  Methodology, pillar 2: two-term error decomposition
  *   [Meth-3]  Methodology, pillar 3: adaptive precision and fallback ladder
  *   [Contrib] Key contributions
+ *   [Results] Experimental results
  *   [Signif]  Significance and claims
  *
  * Values (outputs, the dense reference, measured errors) are computed in
@@ -117,7 +118,7 @@ int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K
                          const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
                          double *out, orc_report *rep, orc_trace *tr);
 /* The same with the values at v_bits = 4 (the design) or 8 (the symmetric
- * cache configuration of [Signif]). */
+ * cache configuration of [Results]). */
 int orc_certified_decode_vb(int B, int T, int Hq, int Hkv, int d, int v_bits, const uint16_t *K,
                             const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
                             double *out, orc_report *rep, orc_trace *tr);
