@@ -443,12 +443,14 @@ ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k, const 
     HIPCHK(launch_quant(Ly, layer, seq, b0, nfull, nblk, c->pk, c->pv, s));
     if (new_len % 64) HIPCHK(launch_set_partial(Ly, layer, seq, nblk - 1, nblk, c->pk, c->pv, s));
     HIPCHK(launch_vrange(Ly, layer, seq, vin, ntok, len0 == 0, s));
-    for (int g = 0; g < Hkv; ++g) {
+    // tier 2 receives the blocks this append completed; the unfinished block
+    // is read from its device copy until it completes
+    for (int g = 0; g < Hkv && nfull > 0; ++g) {
         const size_t dst = Ly.blk(layer, seq, g, b0) * c->blk_fp16;
         const size_t src = (size_t)g * nblk * c->blk_fp16;
-        HIPCHK(hipMemcpyAsync(c->t2k + dst, c->pk + src, (size_t)nblk * c->blk_fp16 * 2,
+        HIPCHK(hipMemcpyAsync(c->t2k + dst, c->pk + src, (size_t)nfull * c->blk_fp16 * 2,
                               hipMemcpyDeviceToHost, s));
-        HIPCHK(hipMemcpyAsync(c->t2v + dst, c->pv + src, (size_t)nblk * c->blk_fp16 * 2,
+        HIPCHK(hipMemcpyAsync(c->t2v + dst, c->pv + src, (size_t)nfull * c->blk_fp16 * 2,
                               hipMemcpyDeviceToHost, s));
     }
     c->h_len[li] = new_len;

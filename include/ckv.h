@@ -112,8 +112,9 @@ ckv_status ckv_reset_sequence(ckv_cache *c, int seq);
  * scale/offset per block, INT4 values (INT8 when v_bits = 8) with a
  * scale/offset per token and 32-channel group, the block's value-error
  * annotation); tokens of an
- * unfinished block stay FP16 on the device.  All tokens are copied to the
- * FP16 tier in host memory.  The call synchronizes `stream`.
+ * unfinished block stay FP16 on the device.  Completed blocks are copied to
+ * the FP16 tier in host memory (an unfinished block is read from its device
+ * copy until it completes).  The call synchronizes `stream`.
  * Errors: EINVAL, ERANGE (would exceed max_context), EHIP. */
 ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k_fp16,
                          const void *v_fp16, int n_tokens, int src_on_device, void *stream);
