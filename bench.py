@@ -377,13 +377,14 @@ def cache_configs(name, cfg, cache, dense_kv, qs, th, T, sm, n):
 def decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, steps):
     """Steady-state decode: per step, one new token (synthetic K, V of the
     workload's distributions, from device memory) appended to every sequence
-    of every layer, each layer's certified step right after its appends, a
-    fresh q per layer-step.  Timed from the first append to the last step."""
+    of every layer (one batched append per layer), each layer's certified
+    step right after its appends, a fresh q per layer-step.  Timed from the
+    first append to the last step."""
     import torch
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev).manual_seed(4321)
-    toks = [(torch.randn((steps * L, 1, Hkv, d), generator=gen, device=dev).half(),
-             torch.randn((steps * L, 1, Hkv, d), generator=gen, device=dev).half()) for _ in range(B)]
+    toks = (torch.randn((steps * L, B, Hkv, d), generator=gen, device=dev).half(),
+            torch.randn((steps * L, B, Hkv, d), generator=gen, device=dev).half())
     qs = (torch.randn((steps * L, B, Hq, d), generator=gen, device=dev) * cfg["q_std"]).half()
     T0 = cache.seq_length(0, 0)
     torch.cuda.synchronize()
@@ -395,8 +396,7 @@ def decode_loop(cache, L, B, Hq, Hkv, d, T, cfg, th, out, steps):
         for l in range(L):
             i = s * L + l
             ta = time.perf_counter()
-            for n in range(B):
-                cache.append_kv(l, n, toks[n][0][i], toks[n][1][i])
+            cache.append_token(l, toks[0][i], toks[1][i])   # the batch's tokens in one call
             t_app += time.perf_counter() - ta
             cache.certified_decode_attention(l, qs[i], th, out=out)
         torch.cuda.synchronize()

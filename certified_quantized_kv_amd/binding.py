@@ -11,7 +11,7 @@ _lib = None
 CKV_STATUS = {0: "CKV_OK", 1: "CKV_EINVAL", 2: "CKV_ENOMEM", 3: "CKV_EHIP", 4: "CKV_ERANGE",
               5: "CKV_ESTATE"}
 
-EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv",
+EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv", "ckv_append_token",
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
             "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache",
@@ -78,6 +78,7 @@ def lib():
         L.ckv_destroy.restype = None
         L.ckv_reset_sequence.argtypes = [vp, i32]
         L.ckv_append_kv.argtypes = [vp, i32, i32, vp, vp, i32, i32, vp]
+        L.ckv_append_token.argtypes = [vp, i32, i32, vp, vp, i32, vp]
         L.ckv_certified_decode_attention.argtypes = [vp, i32, vp, i32, ctypes.POINTER(Thresholds),
                                                      vp, vp, vp]
         L.ckv_dense_decode_attention.argtypes = [vp, vp, vp, i32, vp, i32, f32, vp, vp]
@@ -168,6 +169,25 @@ class Cache:
         _check(lib().ckv_append_kv(self._h, layer, seq, ctypes.c_void_p(k.data_ptr()),
                                    ctypes.c_void_p(v.data_ptr()), k.shape[0], int(k.is_cuda),
                                    _stream_ptr(stream)))
+
+    def append_token(self, layer, k, v, stream=None):
+        """One decode token for each of sequences 0 .. batch-1: k, v
+        [batch][n_kv_heads][head_dim] FP16 (torch tensors, device or host,
+        or numpy arrays)."""
+        if isinstance(k, np.ndarray):
+            k = np.ascontiguousarray(k).view(np.uint16)
+            v = np.ascontiguousarray(v).view(np.uint16)
+            assert k.shape == v.shape and k.shape[1:] == (self.Hkv, self.d)
+            _check(lib().ckv_append_token(self._h, layer, k.shape[0], _np_ptr(k), _np_ptr(v), 0,
+                                          _stream_ptr(stream) if _torch_cuda() else None))
+            return
+        import torch
+        assert k.dtype == torch.float16 and v.dtype == torch.float16 and k.shape == v.shape
+        assert tuple(k.shape[1:]) == (self.Hkv, self.d)
+        k = k.contiguous()
+        v = v.contiguous()
+        _check(lib().ckv_append_token(self._h, layer, k.shape[0], ctypes.c_void_p(k.data_ptr()),
+                                      ctypes.c_void_p(v.data_ptr()), int(k.is_cuda), _stream_ptr(stream)))
 
     def set_device_paging(self, enable=True):
         """Page FP16 blocks with a device kernel reading pinned host memory

@@ -460,6 +460,58 @@ ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k, const 
     return CKV_OK;
 }
 
+// Decode append [Meth-1]: one token for each of sequences 0 .. batch-1 of a
+// layer in one pass (the unfinished blocks' device copies, the value ranges
+// and weight scales), then the blocks this token completed: quantized, and
+// written to tier 2.
+ckv_status ckv_append_token(ckv_cache *c, int layer, int batch, const void *k, const void *v,
+                            int src_on_device, void *stream) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    const ckv_config &cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || batch < 0 || batch > cf.max_batch)
+        return fail(CKV_EINVAL, "bad layer or batch");
+    if (batch == 0) return CKV_OK;
+    if (!k || !v) return fail(CKV_EINVAL, "null K or V");
+    const size_t l0 = (size_t)layer * cf.max_batch;
+    for (int n = 0; n < batch; ++n)
+        if (c->len[l0 + n] + 1 > cf.max_context)
+            return fail(CKV_ERANGE, "append to sequence %d exceeds max_context %d", n, cf.max_context);
+    HIPCHK(hipSetDevice(cf.device));
+    hipStream_t s = (hipStream_t)stream;
+    const int d = c->d, Hkv = cf.n_kv_heads;
+    const size_t tokel = (size_t)Hkv * d;
+    const uint16_t *kin = (const uint16_t *)k, *vin = (const uint16_t *)v;
+    if (!src_on_device) {
+        TRY(grow(c, &c->ain_k, &c->ain_v, &c->ain_cap, (size_t)batch * tokel));
+        HIPCHK(hipMemcpyAsync(c->ain_k, k, (size_t)batch * tokel * 2, hipMemcpyHostToDevice, s));
+        HIPCHK(hipMemcpyAsync(c->ain_v, v, (size_t)batch * tokel * 2, hipMemcpyHostToDevice, s));
+        kin = c->ain_k;
+        vin = c->ain_v;
+    }
+    const Layout &Ly = c->Ly;
+    HIPCHK(launch_append_token(Ly, layer, batch, kin, vin, s));
+    const size_t bb = c->blk_fp16 * 2;  // bytes of one FP16 block
+    for (int n = 0; n < batch; ++n) {
+        const int nl = c->len[l0 + n] + 1;
+        if (nl % 64) continue;
+        // block b of (layer, n) is complete: quantize it from the device
+        // copy ([Hkv] consecutive blocks) and write it to tier 2
+        const int b = nl / 64 - 1;
+        const uint16_t *kp = Ly.kpart + Ly.seqg(layer, n, 0) * c->blk_fp16;
+        const uint16_t *vp = Ly.vpart + Ly.seqg(layer, n, 0) * c->blk_fp16;
+        HIPCHK(launch_quant(Ly, layer, n, b, 1, 1, kp, vp, s));
+        HIPCHK(hipMemcpy2DAsync(c->t2k + Ly.blk(layer, n, 0, b) * c->blk_fp16, (size_t)Ly.Nmax * bb, kp, bb, bb, Hkv,
+                                hipMemcpyDeviceToHost, s));
+        HIPCHK(hipMemcpy2DAsync(c->t2v + Ly.blk(layer, n, 0, b) * c->blk_fp16, (size_t)Ly.Nmax * bb, vp, bb, bb, Hkv,
+                                hipMemcpyDeviceToHost, s));
+    }
+    for (int n = 0; n < batch; ++n) c->h_len[l0 + n] = c->len[l0 + n] + 1;
+    HIPCHK(hipMemcpyAsync(c->Ly.len + l0, c->h_len + l0, sizeof(int) * batch, hipMemcpyHostToDevice, s));
+    HIPCHK(hipStreamSynchronize(s));
+    for (int n = 0; n < batch; ++n) c->len[l0 + n] += 1;
+    return CKV_OK;
+}
+
 namespace {
 
 // Copies of one paging round: tier 2 -> staging.

@@ -197,6 +197,55 @@ __global__ void k_vscale(Layout Ly, int l, int n) {
     Ly.vscale[Ly.seqg(l, n, g) * ng + gr] = value_scale((double)hi - (double)lo, Ly.vb == 8 ? 255.0 : 15.0);
 }
 
+// One decode token for each sequence n < batch of layer l (kin, vin:
+// [batch][Hkv][d]): written into the unfinished block's device copy at
+// position len % 64, the running value range updated (set, for a sequence's
+// first token) and the weight scales of the value groups recomputed; the
+// same state as an append of that token alone.  One workgroup per (kv head,
+// sequence), a thread per channel; len is read before the host updates it.
+__global__ __launch_bounds__(128) void k_append_token(Layout Ly, int l, const uint16_t *kin, const uint16_t *vin) {
+    const int g = blockIdx.x, n = blockIdx.y, c = threadIdx.x, d = Ly.d;
+    const int len = Ly.len[l * Ly.B + n];
+    const int t = len % 64;
+    const size_t sg = Ly.seqg(l, n, g);
+    __shared__ float lo_s[128], hi_s[128];
+    if (c < d) {
+        const size_t src = ((size_t)n * Ly.Hkv + g) * d + c;
+        const uint16_t kv = kin[src], vv = vin[src];
+        uint16_t *kp = Ly.kpart + sg * 64 * d, *vp = Ly.vpart + sg * 64 * d;
+        if (t == 0)  // a new block: the slots past the token hold 0 (as after a pack)
+            for (int u = 1; u < 64; ++u) {
+                kp[(c / 8) * 512 + u * 8 + (c % 8)] = 0;
+                vp[c * 64 + u] = 0;
+            }
+        kp[(c / 8) * 512 + t * 8 + (c % 8)] = kv;
+        vp[c * 64 + t] = vv;
+        // this workgroup alone touches the range of (l, n, g)
+        const uint32_t o = f2ord(h2f(vv));
+        uint32_t *mn = &Ly.vmin[sg * d + c], *mx = &Ly.vmax[sg * d + c];
+        const uint32_t nmn = len == 0 ? o : min(*mn, o), nmx = len == 0 ? o : max(*mx, o);
+        *mn = nmn;
+        *mx = nmx;
+        lo_s[c] = ord2f(nmn);
+        hi_s[c] = ord2f(nmx);
+    }
+    __syncthreads();
+    if (c < d / 32) {
+        float lo = INFINITY, hi = -INFINITY;
+        for (int i = 0; i < 32; ++i) {
+            lo = fminf(lo, lo_s[c * 32 + i]);
+            hi = fmaxf(hi, hi_s[c * 32 + i]);
+        }
+        Ly.vscale[sg * (d / 32) + c] = value_scale((double)hi - (double)lo, Ly.vb == 8 ? 255.0 : 15.0);
+    }
+}
+
+hipError_t launch_append_token(const Layout &Ly, int l, int batch, const uint16_t *kin, const uint16_t *vin,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(k_append_token, dim3(Ly.Hkv, batch), dim3(128), 0, s, Ly, l, kin, vin);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,
                        int len0, int ntok, int b0, int nblk, uint16_t *pk, uint16_t *pv,
                        hipStream_t s) {

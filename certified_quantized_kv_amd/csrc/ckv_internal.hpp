@@ -130,6 +130,8 @@ struct Th {
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------
+hipError_t launch_append_token(const Layout &Ly, int l, int batch, const uint16_t *kin, const uint16_t *vin,
+                               hipStream_t s);
 hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,
                        int len0, int ntok, int b0, int nblk, uint16_t *pk, uint16_t *pv,
                        hipStream_t s);

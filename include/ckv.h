@@ -119,6 +119,17 @@ ckv_status ckv_reset_sequence(ckv_cache *c, int seq);
 ckv_status ckv_append_kv(ckv_cache *c, int layer, int seq, const void *k_fp16,
                          const void *v_fp16, int n_tokens, int src_on_device, void *stream);
 
+/* Append one decode token to each of sequences 0..batch-1 of `layer`
+ * [Meth-1]: the same result as ckv_append_kv with n_tokens = 1 for each
+ * sequence in turn, in one pass over the batch (the decode step's append).
+ * k_fp16, v_fp16: [batch][n_kv_heads][head_dim] binary16, in device memory
+ * if src_on_device, else in host memory; read before return.  A block that
+ * the token completes is quantized and written to the FP16 tier.  The call
+ * synchronizes `stream`.  Errors: EINVAL, ERANGE (a sequence would exceed
+ * max_context; nothing is appended), EHIP. */
+ckv_status ckv_append_token(ckv_cache *c, int layer, int batch, const void *k_fp16,
+                            const void *v_fp16, int src_on_device, void *stream);
+
 /* Certified decode attention for sequences 0..batch-1 of `layer`
  * [Meth-2, Meth-3, Contrib].
  * q_fp16: device, [batch][n_q_heads][head_dim] binary16.

@@ -132,3 +132,65 @@ def test_fp16_cache_same_results_fewer_copies():
         assert np.array_equal(rep[1][f], ref.report[0][f]), f
     for c in caches:
         c.close()
+
+
+@pytest.mark.parametrize("v_bits", [4, 8])
+def test_append_token_matches_per_sequence_appends(v_bits):
+    """The batched one-token append against ckv_append_kv of the same tokens
+    one sequence at a time: identical tier 1 (codes, scales, eta of every
+    completed block), identical certified outputs and reports, and tier 2
+    read back through a dense-fallback step (rung 4 on every head) equal to
+    exact attention.  Sequences start empty, inside a block and at a block
+    end, and cross block ends."""
+    import certified_quantized_kv_amd as ckv
+    Hq, Hkv, d, B, steps = 8, 2, 128, 3, 140
+    T0 = [0, 37, 64]
+    Tmax = max(T0) + steps
+    rng = np.random.default_rng(77 + v_bits)
+    k = f16(rng.standard_normal((B, Tmax, Hkv, d)))
+    v = f16(rng.standard_normal((B, Tmax, Hkv, d)))
+    sm = float(1 / np.sqrt(d))
+    th = oracle.default_thresholds(sm)
+    a = ckv.Cache(1, B, Hq, Hkv, d, Tmax, v_bits=v_bits)
+    b = ckv.Cache(1, B, Hq, Hkv, d, Tmax, v_bits=v_bits)
+    for n in range(B):
+        if T0[n]:
+            a.append_kv(0, n, k[n, :T0[n]], v[n, :T0[n]])
+            b.append_kv(0, n, k[n, :T0[n]], v[n, :T0[n]])
+    for s in range(steps):
+        tk = np.stack([k[n, T0[n] + s] for n in range(B)])
+        tv = np.stack([v[n, T0[n] + s] for n in range(B)])
+        if s % 2:   # device and host sources alternate
+            a.append_token(0, torch.from_numpy(tk.view(np.float16)).cuda(),
+                           torch.from_numpy(tv.view(np.float16)).cuda())
+        else:
+            a.append_token(0, tk, tv)
+        for n in range(B):
+            b.append_kv(0, n, k[n, T0[n] + s:T0[n] + s + 1], v[n, T0[n] + s:T0[n] + s + 1])
+        if s % 35 == 34 or s == steps - 1:
+            for n in range(B):
+                assert a.seq_length(0, n) == b.seq_length(0, n) == T0[n] + s + 1
+                for g in range(Hkv):
+                    for blk in range((T0[n] + s + 1) // 64):
+                        ea, eb = a.export_block(0, n, g, blk), b.export_block(0, n, g, blk)
+                        for f in ea:
+                            assert np.array_equal(ea[f], eb[f]), (s, n, g, blk, f)
+            q = torch.from_numpy(f16(rng.standard_normal((B, Hq, d))).view(np.float16)).cuda()
+            oa, ra = a.certified_decode_attention(0, q, th)
+            ob, rb = b.certified_decode_attention(0, q, th)
+            assert torch.equal(oa, ob) and np.array_equal(ra, rb), s
+    # tier 2: every head falls back (rank_tol < 0, f_layer = 0): the output is
+    # exact attention over the FP16 blocks paged from tier 2 and the device
+    # copy of the unfinished block
+    thd = oracle.default_thresholds(sm, rank_tol=-1.0, f_layer=0.0)
+    q = f16(rng.standard_normal((B, Hq, d)))
+    out, rep = a.certified_decode_attention(0, torch.from_numpy(q.view(np.float16)).cuda(), thd)
+    out = out.cpu().numpy()
+    assert np.all(rep["rung_max"] == 4)
+    for n in range(B):
+        T = T0[n] + steps
+        res = oracle.certified_decode(k[n:n + 1, :T], v[n:n + 1, :T], q[n:n + 1], thd, v_bits=v_bits)
+        ref = res.trace["o_dense"][0]
+        assert np.all(np.abs(out[n] - ref) <= ATOL + RTOL * np.abs(ref)), n
+    a.close()
+    b.close()
