@@ -378,4 +378,19 @@ def test_error_paths():
     assert np.all(out.cpu().numpy() == 0)
     c.reset_sequence(0)
     assert c.seq_length(0, 0) == 0
+    # the batched one-token append: a full sequence rejects the whole call
+    tok = np.zeros((2, 2, 64), np.uint16)
+    c.append_kv(0, 1, np.zeros((256, 2, 64), np.uint16), np.zeros((256, 2, 64), np.uint16))
+    with pytest.raises(ckv.CkvError) as e:
+        c.append_token(0, tok, tok)
+    assert e.value.name == "CKV_ERANGE"
+    assert c.seq_length(0, 0) == 0 and c.seq_length(0, 1) == 256
+    with pytest.raises(ckv.CkvError) as e:
+        c.append_token(0, np.zeros((3, 2, 64), np.uint16), np.zeros((3, 2, 64), np.uint16))
+    assert e.value.name == "CKV_EINVAL"   # batch above max_batch
+    c.append_token(0, tok[:1], tok[:1])
+    assert c.seq_length(0, 0) == 1
     c.close()
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.Cache(1, 1, 8, 2, 64, 256, v_bits=5)
+    assert e.value.name == "CKV_EINVAL"
