@@ -316,6 +316,18 @@ def test_llama_32k_batch4_sampled_sequence():
     c.close()
 
 
+def test_needle_64k_sampled_kv_head():
+    """Full 64K layer (the needle workload's shorter context) on the GPU;
+    the oracle recomputes kv head 2's group."""
+    L = datagen.make_layer("needle_64k", 0)
+    th = oracle.default_thresholds(L.sm)
+    c, out, rep, step = gpu_run(L.k, L.v, L.q, th)
+    g = 2
+    res = oracle.certified_decode(L.k[:, :, g:g + 1], L.v[:, :, g:g + 1], L.q[:, 4 * g:4 * g + 4], th)
+    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step, kv_heads=[g])
+    c.close()
+
+
 def test_needle_128k_sampled_kv_head():
     """Full 128K layer on the GPU; the oracle recomputes kv head 5's group."""
     L = datagen.make_layer("needle_128k", 0)
