@@ -537,16 +537,28 @@ constexpr size_t COPY_COST_BYTES = (size_t)512 << 10;
 
 // Queue the FP16 blocks of (seq n, kv head g) whose flag is set (and not
 // already staged) as runs of consecutive blocks, small gaps filled.
+// First block at or after b that is wanted and not staged (N if none);
+// both flag arrays hold 0 / 1 bytes, scanned eight at a time.
+static int next_needed(const uint8_t *want, const uint8_t *staged, int b, int N) {
+    for (; b + 8 <= N; b += 8) {
+        uint64_t w, s;
+        std::memcpy(&w, want + b, 8);
+        std::memcpy(&s, staged + b, 8);
+        const uint64_t need = w & ~s;
+        if (need) return b + (__builtin_ctzll(need) >> 3);
+    }
+    while (b < N && (!want[b] || staged[b])) ++b;
+    return b;
+}
+
 static void page_runs(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
                std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage, CopyList &cl) {
     const Layout &Ly = c->Ly;
     const size_t sb = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
     int b = 0;
     while (b < N) {
-        if (!want[b] || staged[sb + b]) {
-            ++b;
-            continue;
-        }
+        b = next_needed(want, staged.data() + sb, b, N);
+        if (b >= N) break;
         int e = b + 1, last = b;
         while (e < N && !staged[sb + e] && e - last <= PAGE_GAP) {
             if (want[e]) last = e;
@@ -723,11 +735,15 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
         for (int g = 0; g < Hkv; ++g) {
             const uint32_t *sl = c->h_sel + ((size_t)n * Hkv + g) * Ly.Nmax;
+            const uint8_t sk = skip ? 1 : 0;
             for (int b = 0; b < N; ++b) {
-                const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
-                wantk[b] = skip || pm;
-                wantv[b] = skip || vm;
-                if (prof) {
+                const uint32_t w = sl[b];
+                wantk[b] = (uint8_t)(sk | ((w & allg) != 0));
+                wantv[b] = (uint8_t)(sk | (((w >> 8) & allg) != 0));
+            }
+            if (prof) {
+                for (int b = 0; b < N; ++b) {
+                    const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
                     c->pf.tail_blocks += ((pm | vm) != allg);
                     if (!skip) {
                         c->pf.k16_blocks += pm != 0;
@@ -735,8 +751,8 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                         c->pf.int4p_blocks += (pm & ~vm) != 0;
                     }
                 }
+                c->pf.q8_blocks += N;
             }
-            if (prof) c->pf.q8_blocks += N;
             if (gather && !skip) {
                 // the device copies this (seq, kv head)'s listed blocks itself
                 for (int b = 0; b < N; ++b) paged += (size_t)(wantk[b] + wantv[b]) * c->blk_fp16 * 2;

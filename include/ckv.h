@@ -196,6 +196,8 @@ ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int kv_head, int b
  *                                          group, bit 8+j: VP of head j
  *                                          (first N entries of each row)
  *   m16fx  [batch][n_q_heads][Np] u64      fixed-point FP16 masses on P
+ *                                          (not written for a sequence at
+ *                                          rung 4 before paging)
  *                                          (first N entries of each row)
  *   bounds [batch][n_q_heads][4] FP64      mu, TV, E_key, E_val
  *   seq_flags [batch] int                  bit0 rung 4 before paging,

@@ -48,6 +48,8 @@ def run_both(k, v, q, th, layers=1):
         B, Hq = r0.shape
         G = Hq // k.shape[2]
         for n in range(B):
+            if s0["seq_flags"][n] & 1:   # rung 4 before paging: no FP16-side masses
+                continue
             for h in range(Hq):
                 sel = s0["sel"][n, h // G, :k.shape[1] // 64]
                 inP = ((sel >> (h % G)) & 1).astype(bool)
