@@ -81,10 +81,13 @@ def test_decode_loop_one_token_per_step(Hq, Hkv, d):
     c.close()
 
 
-def test_fp16_cache_same_results_fewer_copies():
+@pytest.mark.parametrize("batched", [False, True])
+def test_fp16_cache_same_results_fewer_copies(batched):
     """The device FP16 block cache: the same outputs and reports as paging
     every step, fewer bytes copied from tier 2; a reset sequence's mirrored
-    blocks are not reused for its new contents."""
+    blocks are not reused for its new contents.  batched: the cached cache
+    takes its decode tokens through the one-token append (a block completes
+    at step 2 while its layer is mirrored)."""
     import certified_quantized_kv_amd as ckv
     L, B, Hq, Hkv, d, T0, steps = 2, 2, 8, 2, 128, 190, 6
     Tmax = T0 + steps + 200
@@ -103,10 +106,13 @@ def test_fp16_cache_same_results_fewer_copies():
         for l in range(L):
             q = torch.from_numpy(f16(rng.standard_normal((B, Hq, d))).view(np.float16)).cuda()
             res = []
-            for c in caches:
-                for n in range(B):
-                    t = T0 + s
-                    c.append_kv(l, n, k[l, n, t:t + 1], v[l, n, t:t + 1])
+            for ci, c in enumerate(caches):
+                t = T0 + s
+                if batched and ci == 1:
+                    c.append_token(l, k[l, :, t].copy(), v[l, :, t].copy())
+                else:
+                    for n in range(B):
+                        c.append_kv(l, n, k[l, n, t:t + 1], v[l, n, t:t + 1])
                 out, rep = c.certified_decode_attention(l, q, th)
                 res.append((out.cpu().numpy(), rep))
             assert np.array_equal(res[0][0], res[1][0]), (s, l)
