@@ -300,6 +300,12 @@ def test_llama_8k_layer():
     both(L.k, L.v, L.q, oracle.default_thresholds(L.sm))
 
 
+def test_llama_8k_layer_symmetric_cache():
+    """The full 8K layer with 8-bit values (the symmetric configuration)."""
+    L = datagen.make_layer("llama_8k", 1)
+    both(L.k, L.v, L.q, oracle.default_thresholds(L.sm), v_bits=8)
+
+
 @pytest.mark.parametrize("layer", [0, 1, 2, 3])
 def test_stress_32k_layers(layer):
     L = datagen.make_layer("stress_32k", layer)
