@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline layer-steps (no device-paging, variant or decode-loop lines): "
                          "for profiler runs")
+    ap.add_argument("--staged-threads", type=int, default=-1,
+                    help="host threads packing the paged blocks into pinned chunks "
+                         "(0: one copy per run of blocks; -1: the library's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -93,6 +96,8 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
     t0 = time.time()
     # room for the decode loop's tokens (one more block)
     cache = ckv.Cache(L, B, Hq, Hkv, d, T + (64 if decode_steps else 0), device=0)
+    if args.staged_threads >= 0:
+        cache.set_staged_paging(args.staged_threads)
     fp = cache.footprint()
     log(f"cache created in {time.time() - t0:.1f}s: device {fp['device'] / 2**30:.2f} GiB "
         f"(tier 1 {fp['tier1'] / 2**30:.2f} GiB), pinned host {fp['host'] / 2**30:.2f} GiB")
@@ -206,7 +211,9 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
         "v_promoted_mean": round(nvp, 2),
         "config": {"workload": name, "batch": B, "context": T, "layers": L, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": d, "tau_cov": th["tau_cov"], "k_tol": th["k_tol"],
-                   "v_tol": th["v_tol"], "rank_tol": th["rank_tol"]},
+                   "v_tol": th["v_tol"], "rank_tol": th["rank_tol"],
+                   "paging": "staged, %d host threads" % (args.staged_threads if args.staged_threads >= 0 else 4)
+                   if args.staged_threads != 0 else "runs"},
     }
 
     if not args.no_extras:
@@ -257,6 +264,30 @@ def extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B
                             "paged_MiB_per_step": round(profd["bytes_paged"] / Kd / 2 ** 20, 2),
                             "page_ms_per_step": round(profd["phases"]["page"][0] / Kd, 4)}
     log(f"device paging: {1e3 * eld / Kd:.3f} ms/step")
+
+    # the same layer-steps with the listed blocks copied as runs (one copy
+    # per run of blocks, small gaps filled) instead of host-packed chunks
+    staged = args.staged_threads if args.staged_threads >= 0 else 4
+    cache.set_staged_paging(0)
+    for i in range(min(args.warmup, 4)):
+        cache.certified_decode_attention(i % L, qs[i % L], th, out=out)
+    torch.cuda.synchronize()
+    cache.set_profiling(True)
+    t1 = time.perf_counter()
+    for i in range(Kd):
+        l = (args.warmup + i) % L
+        cache.certified_decode_attention(l, qs[l], th, out=out)
+    torch.cuda.synchronize()
+    elr = time.perf_counter() - t1
+    profr = cache.profile()
+    cache.set_profiling(False)
+    cache.set_staged_paging(staged)
+    rec["run_copies"] = {"steps": Kd, "ms_per_step": round(1e3 * elr / Kd, 4),
+                         "value": round(B * T * Kd / elr, 1),
+                         "paged_MiB_per_step": round(profr["bytes_paged"] / Kd / 2 ** 20, 2),
+                         "h2d_copies_per_step": round(profr["copies"] / Kd, 1),
+                         "page_ms_per_step": round(profr["phases"]["page"][0] / Kd, 4)}
+    log(f"run copies: {1e3 * elr / Kd:.3f} ms/step")
 
     if n_dense:
         rec["variants"] = variants(cache, dense_kv, qs, th, T, sm, n_dense)

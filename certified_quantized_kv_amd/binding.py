@@ -15,7 +15,7 @@ EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv", 
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
             "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache",
-            "ckv_set_device_paging"]
+            "ckv_set_device_paging", "ckv_set_staged_paging"]
 
 
 class CkvError(RuntimeError):
@@ -93,6 +93,7 @@ def lib():
         L.ckv_get_profile.argtypes = [vp, ctypes.POINTER(Profile)]
         L.ckv_enable_fp16_cache.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
         L.ckv_set_device_paging.argtypes = [vp, i32]
+        L.ckv_set_staged_paging.argtypes = [vp, i32]
         for name in EXPORTED:
             if name not in ("ckv_destroy", "ckv_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -193,6 +194,11 @@ class Cache:
         """Page FP16 blocks with a device kernel reading pinned host memory
         (True) or with host-issued copies (False, the default)."""
         _check(lib().ckv_set_device_paging(self._h, int(bool(enable))))
+
+    def set_staged_paging(self, threads):
+        """Copy the listed FP16 blocks packed into 4 MiB pinned chunks by
+        `threads` host threads (0: one copy per run of blocks)."""
+        _check(lib().ckv_set_staged_paging(self._h, int(threads)))
 
     def enable_fp16_cache(self, max_bytes):
         """Keep paged FP16 blocks in device memory across steps for as many

@@ -280,4 +280,22 @@ hipError_t launch_vrange(const Layout &Ly, int l, int n, const uint16_t *vin, in
     return hipGetLastError();
 }
 
+// Staged paging: a chunk is a header of destination addresses (one 64-bit
+// device address per block, PAGE_HDR bytes) followed by the blocks packed
+// back to back; workgroup i moves block i of the chunk to its staging slot.
+__global__ __launch_bounds__(256) void k_page_scatter(const uint8_t *__restrict__ chunk, int blk_bytes) {
+    const uint64_t dst = reinterpret_cast<const uint64_t *>(chunk)[blockIdx.x];
+    const uint4 *src = reinterpret_cast<const uint4 *>(chunk + PAGE_HDR + (size_t)blockIdx.x * blk_bytes);
+    uint4 *out = reinterpret_cast<uint4 *>(dst);
+    const int n = blk_bytes / 16;
+    for (int i = threadIdx.x; i < n; i += 256) out[i] = src[i];
+}
+
+hipError_t launch_page_scatter(const uint8_t *chunk, int nblk, int blk_bytes, hipStream_t s) {
+    if (nblk <= 0) return hipSuccess;
+    if (nblk > PAGE_HDR / 8 || blk_bytes % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_page_scatter, dim3(nblk), dim3(256), 0, s, chunk, blk_bytes);
+    return hipGetLastError();
+}
+
 }  // namespace ckv

@@ -130,6 +130,9 @@ struct Th {
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------
+// header bytes of a staged-paging chunk: up to 512 block addresses
+constexpr int PAGE_HDR = 4096;
+hipError_t launch_page_scatter(const uint8_t *chunk, int nblk, int blk_bytes, hipStream_t s);
 hipError_t launch_append_token(const Layout &Ly, int l, int batch, const uint16_t *kin, const uint16_t *vin,
                                hipStream_t s);
 hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,

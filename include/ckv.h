@@ -202,6 +202,8 @@ ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int kv_head, int b
  *   bounds [batch][n_q_heads][4] FP64      mu, TV, E_key, E_val
  *   seq_flags [batch] int                  bit0 rung 4 before paging,
  *                                          bit1 rung 4 after the rank check
+ * Entries past a shorter sequence's own tokens (score) or slots (the
+ * per-block arrays) are not defined.
  * np_out receives Np.  Errors: ESTATE (no step yet), EINVAL, EHIP. */
 ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, float *bstat,
                            float *mref, uint64_t *mfx, uint32_t *sel, uint64_t *m16fx,
@@ -230,6 +232,25 @@ ckv_status ckv_enable_fp16_cache(ckv_cache *c, size_t max_bytes, int *layers);
  * copies.  enable: 0 host copies (default), 1 device paging.
  * Errors: EINVAL (null cache). */
 ckv_status ckv_set_device_paging(ckv_cache *c, int enable);
+
+/* Staged paging (an implementation choice for the host-issued paging of
+ * [Meth-1]; the page issues one copy per block), on by default: host
+ * threads pack the listed FP16 blocks of a step, and only those, into 4 MiB
+ * chunks of a ring in pinned host memory (16 chunks); each chunk crosses the
+ * host link in one hipMemcpyAsync on a paging stream and a kernel moves its
+ * blocks to their staging slots.  Runs of consecutive listed blocks of at
+ * least a chunk's bytes are copied directly, one copy each.  Switched off,
+ * the blocks are copied as runs of consecutive blocks, small gaps filled, one
+ * copy per run.  The results
+ * are identical either way.  threads: 0 switches it off, 1 .. 64 the packing
+ * threads (held by the cache until it is destroyed or this is called again;
+ * ckv_create starts 4, fewer on a host with fewer CPUs).  The first switch
+ * on (in ckv_create) allocates the ring, about 64 MiB of pinned host and of
+ * device memory, kept until ckv_destroy, and reads every page of tier 2 once
+ * so that the packing takes no page faults.  Waits for the device to finish.
+ * CKV_EINVAL for threads outside 0 .. 64, CKV_ENOMEM when the ring or the
+ * threads cannot be had.  Device paging, when on, takes precedence. */
+ckv_status ckv_set_staged_paging(ckv_cache *c, int threads);
 
 /* Profile of the decode steps since profiling was enabled (enabling resets
  * it).  Phase times are measured with HIP events on the streams the work

@@ -81,13 +81,14 @@ def test_decode_loop_one_token_per_step(Hq, Hkv, d):
     c.close()
 
 
-@pytest.mark.parametrize("batched", [False, True])
-def test_fp16_cache_same_results_fewer_copies(batched):
+@pytest.mark.parametrize("batched,staged", [(False, 0), (True, 0), (True, 4)])
+def test_fp16_cache_same_results_fewer_copies(batched, staged):
     """The device FP16 block cache: the same outputs and reports as paging
     every step, fewer bytes copied from tier 2; a reset sequence's mirrored
     blocks are not reused for its new contents.  batched: the cached cache
     takes its decode tokens through the one-token append (a block completes
-    at step 2 while its layer is mirrored)."""
+    at step 2 while its layer is mirrored).  staged: both caches page with
+    staged paging on that many threads."""
     import certified_quantized_kv_amd as ckv
     L, B, Hq, Hkv, d, T0, steps = 2, 2, 8, 2, 128, 190, 6
     Tmax = T0 + steps + 200
@@ -98,6 +99,7 @@ def test_fp16_cache_same_results_fewer_copies(batched):
     caches = [ckv.Cache(L, B, Hq, Hkv, d, Tmax) for _ in range(2)]
     assert caches[1].enable_fp16_cache(1 << 34) == L
     for c in caches:
+        c.set_staged_paging(staged)
         for l in range(L):
             for n in range(B):
                 c.append_kv(l, n, k[l, n, :T0], v[l, n, :T0])
