@@ -1147,22 +1147,32 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         if (prof) HIPCHK(hipEventRecord(E[9], c->side[0]));
         std::vector<uint8_t> all(Ly.Nmax, 1);
         cl.clear();
+        CopyList clv;  // V runs (staged paging)
         for (int n = 0; n < batch; ++n) {
             const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
             for (int g = 0; g < Hkv; ++g) {
                 uint32_t m = 0;
                 for (int j = 0; j < G; ++j) m |= (uint32_t)dense[(size_t)n * Hq + g * G + j] << j;
                 c->h_mask[n * Hkv + g] = m;
-                if (m) {
+                if (m && staged) {
+                    // the blocks between those already staged: packed
+                    Stager &SG = *c->stager;
+                    list_blocks(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, SG.src, SG.dst, cl);
+                    list_blocks(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, SG.vsrc, SG.vdst, clv);
+                } else if (m) {
                     page_runs(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, cl);
                     page_runs(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, cl);
-                    if (prof) c->pf.dense_blocks += N;
                 }
+                if (m && prof) c->pf.dense_blocks += N;
             }
         }
-        TRY(issue_copies(c, cl));
-        paged += cl.bytes;
-        if (prof) c->pf.copies += cl.size.size();
+        if (staged) {
+            TRY(stage_and_copy(c, *c->stager, cl, clv, s, paged));
+        } else {
+            TRY(issue_copies(c, cl));
+            paged += cl.bytes;
+            if (prof) c->pf.copies += cl.size.size();
+        }
         HIPCHK(hipMemcpyAsync(c->dmask, c->h_mask, sizeof(uint32_t) * batch * Hkv, hipMemcpyHostToDevice,
                               c->side[0]));
         HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
