@@ -1118,11 +1118,14 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
     if (prof) HIPCHK(hipEventRecord(E[12], s));
     HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[13], s));
+    // the rank check needs only the FP16-key pass: it runs while the FP16
+    // values are still being paged
+    HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 1, s));
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
     if (prof) HIPCHK(hipEventRecord(E[14], s));
     HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
     if (prof) HIPCHK(hipEventRecord(E[11], s));
-    HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, s));
+    HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 2, s));
     if (prof) HIPCHK(hipEventRecord(E[8], s));
     HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(c->ev_done, s));

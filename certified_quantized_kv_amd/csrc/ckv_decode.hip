@@ -1725,8 +1725,10 @@ __device__ __forceinline__ long long discordant_sorted(uint64_t *kI, uint64_t *k
 }
 
 template <int D, int G>
+// part: bit 0 the rank check (needs the FP16-key pass only, so it can run
+// while the FP16 values are still being paged), bit 1 the merge.
 __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, const int *skip_seq,
-                                                   uint32_t *plist_g, uint64_t *keys_g) {
+                                                   uint32_t *plist_g, uint64_t *keys_g, int part) {
     constexpr int CPL = D / 64;
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1741,6 +1743,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     __shared__ long long red_ll[MERGE_T / 64];
     __shared__ float red_f[MERGE_T / 64];
     __shared__ float w_m[MERGE_T / 64], w_l[MERGE_T / 64], w_acc[MERGE_T / 64][D];
+    if (part & 1) {
 
     // compact list of P blocks (ascending index): one block per thread and
     // round, per-wave counts combined through LDS
@@ -1848,6 +1851,8 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         St.plan[hs].rank_ok = !((double)Dt > lim);
         St.plan[hs].ndisc = (int)Dt;
     }
+    }  // rank check
+    if (!(part & 2)) return;
 
     // merge: tail partials then promoted partials; each wave merges a
     // contiguous quarter (eight loads in flight), the quarters are combined
@@ -2120,10 +2125,11 @@ hipError_t launch_promoted16(const Layout &Ly, const Step &St, const int *skip_s
 }
 
 hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, const int *skip_seq,
-                             uint32_t *plist, uint64_t *keys, hipStream_t s) {
+                             uint32_t *plist, uint64_t *keys, int part, hipStream_t s) {
+    if (part < 1 || part > 3) return hipErrorInvalidValue;
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         hipLaunchKernelGGL((k_merge<decltype(D)::value, decltype(G)::value>),
-                           dim3(Ly.Hq, St.batch), dim3(MERGE_T), 0, s, Ly, St, th, skip_seq, plist, keys);
+                           dim3(Ly.Hq, St.batch), dim3(MERGE_T), 0, s, Ly, St, th, skip_seq, plist, keys, part);
         return hipGetLastError();
     });
 }

@@ -154,8 +154,9 @@ hipError_t launch_gather(const Layout &Ly, const Step &St, const int *skip_seq, 
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
 hipError_t launch_promoted16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s);
+// part: 1 the rank check, 2 the merge of the partials, 3 both
 hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, const int *skip_seq,
-                             uint32_t *plist, uint64_t *keys, hipStream_t s);
+                             uint32_t *plist, uint64_t *keys, int part, hipStream_t s);
 hipError_t launch_dense_src(int d, int G, const DenseSrc &S, int nsplit, int batch,
                             hipStream_t s);
 
