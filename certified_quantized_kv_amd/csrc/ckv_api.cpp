@@ -131,24 +131,28 @@ static void touch_pages(const void *p, size_t bytes, int threads) {
 // A worker: take chunks in order of a shared counter; wait until the copy
 // that last left the chunk's slot has finished, then pack the blocks behind
 // the header of their destination addresses.
+static void pack_chunk(Stager *S, int ci) {
+    const int slot = ci % PAGE_SLOTS;
+    while (S->issued.load(std::memory_order_acquire) <= ci - PAGE_SLOTS) std::this_thread::yield();
+    // polled: the wait is at most one chunk's copy
+    hipError_t qe;
+    while ((qe = hipEventQuery(S->ev[slot])) == hipErrorNotReady) std::this_thread::yield();
+    if (qe != hipSuccess) S->err.store(1);
+    uint8_t *hc = S->hring + (size_t)slot * S->stride;
+    uint64_t *hdr = reinterpret_cast<uint64_t *>(hc);
+    for (int i = S->cstart[ci], j = 0; i < S->cstart[ci + 1]; ++i, ++j) {
+        hdr[j] = S->dst[i];
+        pack_block(hc + PAGE_HDR + (size_t)j * S->blk_bytes, S->src[i], S->blk_bytes);
+    }
+    _mm_sfence();  // the streaming stores are globally visible before the flag
+    S->ready[ci].store(1, std::memory_order_release);
+}
+
 static void stager_work(Stager *S) {
     for (;;) {
         const int ci = S->next.fetch_add(1, std::memory_order_relaxed);
         if (ci >= S->nchunk) return;
-        const int slot = ci % PAGE_SLOTS;
-        while (S->issued.load(std::memory_order_acquire) <= ci - PAGE_SLOTS) std::this_thread::yield();
-        // polled: a blocking wait sleeps far longer than one chunk's copy
-        hipError_t qe;
-        while ((qe = hipEventQuery(S->ev[slot])) == hipErrorNotReady) std::this_thread::yield();
-        if (qe != hipSuccess) S->err.store(1);
-        uint8_t *hc = S->hring + (size_t)slot * S->stride;
-        uint64_t *hdr = reinterpret_cast<uint64_t *>(hc);
-        for (int i = S->cstart[ci], j = 0; i < S->cstart[ci + 1]; ++i, ++j) {
-            hdr[j] = S->dst[i];
-            pack_block(hc + PAGE_HDR + (size_t)j * S->blk_bytes, S->src[i], S->blk_bytes);
-        }
-        _mm_sfence();  // the streaming stores are globally visible before the flag
-        S->ready[ci].store(1, std::memory_order_release);
+        pack_chunk(S, ci);
     }
 }
 
@@ -853,7 +857,12 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
     S.vdst.clear();
     const size_t nblk = S.src.size();
     S.cstart.clear();
-    for (size_t i = 0; i < nk; i += S.per_chunk) S.cstart.push_back((int)i);
+    // the step's first chunks are 1/8, 1/4 and 1/2 of a full one: the first
+    // copy starts after a short packing time
+    for (size_t i = 0, k = 0; i < nk; ++k) {
+        S.cstart.push_back((int)i);
+        i += k < 3 ? std::max(1, S.per_chunk >> (3 - k)) : S.per_chunk;
+    }
     const int nkc = (int)S.cstart.size();
     for (size_t i = nk; i < nblk; i += S.per_chunk) S.cstart.push_back((int)i);
     S.nchunk = (int)S.cstart.size();
@@ -882,7 +891,7 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
             S.ready.reset(new std::atomic<int>[S.ready_cap]);
         }
         for (int i = 0; i < S.nchunk; ++i) S.ready[i].store(0, std::memory_order_relaxed);
-        S.next.store(0);
+        S.next.store(1);  // chunk 0 is packed here while the threads wake
         S.issued.store(0);
         S.err.store(0);
         S.busy.store(S.nthreads);
@@ -891,6 +900,7 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
             ++S.gen;
         }
         S.cv.notify_all();
+        pack_chunk(&S, 0);
         for (int ci = 0; ci < S.nchunk && e == hipSuccess; ++ci) {
             while (!S.ready[ci].load(std::memory_order_acquire)) std::this_thread::yield();
             if (S.err.load()) {
