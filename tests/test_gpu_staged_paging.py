@@ -113,13 +113,27 @@ def test_staged_paging_wraps_the_ring():
 
 
 def test_staged_paging_arguments():
+    """Bad thread counts are rejected; switching the thread count, or staged
+    paging off and on, between steps of one cache leaves every step's
+    results unchanged."""
     import certified_quantized_kv_amd as ckv
-    c = ckv.Cache(1, 1, 4, 1, 64, 256)
+    L = datagen.make_layer("tiny_1k", 0, T=1000)
+    th = oracle.default_thresholds(L.sm, tau_cov=1.0)
+    B, T, Hkv, d = L.k.shape
+    c = ckv.Cache(1, B, L.q.shape[1], Hkv, d, T)
     for bad in (-1, 65):
         with pytest.raises(ckv.CkvError) as e:
             c.set_staged_paging(bad)
         assert e.value.status == 1
-    c.set_staged_paging(4)
-    c.set_staged_paging(2)
-    c.set_staged_paging(0)
+    for n in range(B):
+        c.append_kv(0, n, L.k[n], L.v[n])
+    q = torch.from_numpy(L.q.view(np.float16)).cuda()
+    res = []
+    for nt in (4, 2, 0, 3, 0, 1):
+        c.set_staged_paging(nt)
+        out, rep = c.certified_decode_attention(0, q, th)
+        res.append((out.cpu().numpy(), rep))
+    for o, r in res[1:]:
+        assert np.array_equal(o, res[0][0])
+        assert np.array_equal(r, res[0][1])
     c.close()
