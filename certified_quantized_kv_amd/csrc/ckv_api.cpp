@@ -876,13 +876,15 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
         return hipSuccess;
     };
     hipError_t e = hipSuccess;
+    S.err.store(0);
+    ckv_status runs_st = CKV_OK;  // a failed run copy (its message already set)
     // the long runs go first: the copy engines work on them while the
     // threads pack the first chunks
-    if (issue_copies(c, kruns, false) != CKV_OK) e = hipErrorUnknown;
+    if ((runs_st = issue_copies(c, kruns, false)) != CKV_OK) e = hipErrorUnknown;
     bytes += kruns.bytes;
     if (nkc == 0 && e == hipSuccess) {
         e = kjoin();
-        if (e == hipSuccess && issue_copies(c, vruns, false) != CKV_OK) e = hipErrorUnknown;
+        if (e == hipSuccess && (runs_st = issue_copies(c, vruns, false)) != CKV_OK) e = hipErrorUnknown;
         bytes += vruns.bytes;
     }
     if (S.nchunk > 0 && e == hipSuccess) {
@@ -919,7 +921,7 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
             S.issued.store(ci + 1, std::memory_order_release);
             if (ci + 1 == nkc) {
                 e = kjoin();
-                if (e == hipSuccess && issue_copies(c, vruns, false) != CKV_OK) e = hipErrorUnknown;
+                if (e == hipSuccess && (runs_st = issue_copies(c, vruns, false)) != CKV_OK) e = hipErrorUnknown;
                 bytes += vruns.bytes;
             }
         }
@@ -937,6 +939,8 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
     if (c->prof) c->pf.copies += S.nchunk + kruns.size.size() + vruns.size.size();
     S.src.clear();
     S.dst.clear();
+    if (runs_st != CKV_OK) return runs_st;
+    if (S.err.load()) return fail(CKV_EHIP, "staged paging: a ring slot's event failed");
     if (e != hipSuccess) return fail(CKV_EHIP, "staged paging: %s", hipGetErrorString(e));
     return CKV_OK;
 }
