@@ -575,6 +575,7 @@ ckv_status ckv_set_staged_paging(ckv_cache *c, int threads) {
         for (int i = 0; i < threads; ++i) S->th.emplace_back(stager_thread, S);
     } catch (...) {
         stager_stop(S);
+        S->nthreads = 0;  // staged paging stays off: no thread would pack
         return fail(CKV_ENOMEM, "cannot start paging threads");
     }
     return CKV_OK;
