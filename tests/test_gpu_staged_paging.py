@@ -91,24 +91,30 @@ def test_staged_paging_llama_8k(v_bits):
         assert np.array_equal(rep[f], res.report[f]), f
 
 
-def test_staged_paging_wraps_the_ring():
-    """Every key block listed (tau_cov = 1) in sequences of 272, 125, 125
-    and 93 blocks: the 272-block runs (at least a chunk's bytes) go as direct
-    copies, the other 8 x 343 K blocks as 11 chunks of up to 256 blocks per
-    step, and as many V chunks, against a ring of 16, over two steps (the
-    second step's chunks reuse slots of the first's)."""
+@pytest.mark.parametrize("d", [128, 64])
+def test_staged_paging_wraps_the_ring(d):
+    """Every key block listed (tau_cov = 1).  d = 128: sequences of 272, 125,
+    125 and 93 blocks; the 272-block runs (at least a chunk's 4 MiB) go as
+    direct copies, the other 8 x 343 K blocks as chunks of up to 256 blocks.
+    d = 64: 125, 125, 125 and 93 blocks, all packed, in chunks of up to 512
+    blocks (a full header of block addresses).  Either way more chunks per
+    step than the ring's 16 slots, over two steps (the second step's chunks
+    reuse slots of the first's)."""
     rng = np.random.default_rng(23)
-    B, T, Hq, Hkv, d = 4, 17408, 32, 8, 128
-    lens = [17408, 8000, 8000, 5952]
+    B, Hq, Hkv = 4, 32, 8
+    lens = [17408, 8000, 8000, 5952] if d == 128 else [8000, 8000, 8000, 5952]
+    T = max(lens)
     k = np.asarray(rng.standard_normal((B, T, Hkv, d)), np.float16).view(np.uint16)
     v = np.asarray(rng.standard_normal((B, T, Hkv, d)), np.float16).view(np.uint16)
     q = np.asarray(rng.standard_normal((B, Hq, d)), np.float16).view(np.uint16)
     th = oracle.default_thresholds(float(1 / np.sqrt(d)), tau_cov=1.0, v_tol=0.0)
     _, prof = run_modes(k, v, q, th, threads=(2, 8), steps=2, lens=lens)
-    packed = Hkv * sum(t // 64 for t in lens[1:])
+    per_chunk = (4 << 20) // (64 * d * 2)
+    direct = lens[0] // 64 >= per_chunk
+    packed = Hkv * sum(t // 64 for t in (lens[1:] if direct else lens))
     nblk = Hkv * sum(t // 64 for t in lens)
     for p in prof:
-        assert p["copies"] >= 2 * (packed // 256 + Hkv), p["copies"]
+        assert p["copies"] >= 2 * (packed // per_chunk + (Hkv if direct else 0)), p["copies"]
         assert p["bytes_paged"] >= 2 * nblk * 64 * d * 2, p["bytes_paged"]
 
 
