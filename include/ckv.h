@@ -266,8 +266,11 @@ typedef struct {
     double ms[10];          /* accumulated milliseconds per phase            */
     int counts[10];         /* timed occurrences per phase                   */
     int steps;              /* decode steps profiled                         */
-    uint64_t bytes_paged;   /* tier 2 -> staging bytes (with filled gaps)    */
-    uint64_t copies;        /* host-to-device copies issued                  */
+    uint64_t bytes_paged;   /* tier 2 -> staging bytes (staged paging: with
+                               the chunk headers; run copies: with filled
+                               gaps)                                         */
+    uint64_t copies;        /* host-to-device copies issued (staged paging:
+                               chunks and direct runs)                       */
     uint64_t q8_blocks;     /* blocks read by the scoring pass               */
     uint64_t tail_blocks;   /* blocks read by the tail pass (INT4 values)    */
     uint64_t k16_blocks;    /* FP16 key blocks read by the promoted pass     */
