@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libckv_oracle.so")
 _lib = None
 
-CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared"]
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
 
 
 def build():
@@ -41,7 +41,7 @@ REPORT_DTYPE = np.dtype([("e_key", "<f4"), ("e_val", "<f4"), ("tv_bound", "<f4")
 
 _TRACE_FIELDS = ["k_code", "k_s", "k_z", "v_code", "v_s", "v_z", "eta", "vrange", "score",
                  "bmax", "bl", "delta", "rho", "mref", "mfx", "sel", "bounds", "seq_flags",
-                 "score16", "m16fx", "err_key", "err_val", "o_cert", "o_dense"]
+                 "score16", "m16fx", "err_key", "err_val", "o_cert", "o_dense", "cval"]
 
 
 class _Trace(ctypes.Structure):
@@ -80,12 +80,23 @@ def lib():
                                            ctypes.POINTER(_Trace)]
         L.orc_certified_decode_vb.restype = i32
         L.orc_dense_head.argtypes = [i32, i32, i32, i32, vp, vp, vp, f64, vp]
+        L.orc_set_threads.argtypes, L.orc_set_threads.restype = [i32], None
+        L.orc_get_threads.argtypes, L.orc_get_threads.restype = [], i32
         _lib = L
     return _lib
 
 
 def set_mutation(flags):
     ctypes.c_int.in_dll(lib(), "orc_mutation").value = int(flags)
+
+
+def set_threads(n):
+    """OpenMP threads of the decode step (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads():
+    return lib().orc_get_threads()
 
 
 def _p(a):
@@ -141,7 +152,8 @@ def certified_decode(k, v, q, thresholds, trace=True, v_bits=4):
             bounds=((B, Hq, 4), np.float64), seq_flags=((B,), np.int32),
             score16=((B, Hq, N * 64), np.float32), m16fx=((B, Hq, N), np.uint64),
             err_key=((B, Hq), np.float64), err_val=((B, Hq), np.float64),
-            o_cert=((B, Hq, d), np.float64), o_dense=((B, Hq, d), np.float64))
+            o_cert=((B, Hq, d), np.float64), o_dense=((B, Hq, d), np.float64),
+            cval=((B, Hq, N), np.uint64))
         for f, (shp, dt) in shapes.items():
             tr[f] = np.zeros(shp, dt)
             setattr(ctr, f, tr[f].ctypes.data if tr[f].size else None)

@@ -1,9 +1,10 @@
 /*
  * ckv_oracle.c -- CPU oracle for certified quantized-KV decode attention.
  *
- * TEST INFRASTRUCTURE ONLY (see ckv_oracle.h).  Plain, slow and sequential
- * on purpose: one head at a time, full sorts where the method says "order",
- * FP64 for every value.  Built with -O2 -fno-fast-math -ffp-contract=off so
+ * TEST INFRASTRUCTURE ONLY (see ckv_oracle.h).  Plain and slow on purpose:
+ * each head is computed on its own, with full sorts where the method says
+ * "order" and FP64 for every value; heads run on OpenMP threads, which
+ * changes no result.  Built with -O2 -fno-fast-math -ffp-contract=off so
  * that every FP32 operation is the single IEEE operation written here.
  *
  * Section tags ([Meth-1] ...) refer to the page "Runtime-Certified
@@ -16,6 +17,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 int orc_mutation = 0;
 
@@ -422,7 +426,7 @@ static float rho_partial(int d, const uint16_t *q, const uint16_t *k, int n, flo
     for (int c = 0; c < d; c++) {
         double m = 0.0;
         for (int t = 0; t < n; t++) {
-            double x = fabs((double)orc_h2f(k[t * d + c]));
+            double x = (orc_mutation & 128) ? (double)orc_h2f(k[t * d + c]) : fabs((double)orc_h2f(k[t * d + c]));
             if (x > m)
                 m = x;
         }
@@ -463,6 +467,15 @@ static int cmp_vb_desc(const void *x, const void *y)
     const vb_t *a = (const vb_t *)x, *b = (const vb_t *)y;
     if (a->v != b->v)
         return a->v > b->v ? -1 : 1;
+    return a->b < b->b ? -1 : (a->b > b->b);
+}
+
+/* value ascending, index ascending: only for the rung-2 order mutation */
+static int cmp_vb_asc(const void *x, const void *y)
+{
+    const vb_t *a = (const vb_t *)x, *b = (const vb_t *)y;
+    if (a->v != b->v)
+        return a->v < b->v ? -1 : 1;
     return a->b < b->b ? -1 : (a->b > b->b);
 }
 
@@ -511,6 +524,7 @@ typedef struct {
     uint64_t *M; /* [Np] */
     uint64_t S;
     uint8_t *inP, *inVP; /* [N] */
+    uint64_t *cval;      /* [N] E_val contribution of each block */
     int kstar, nvp, widened, cap_fail;
     double tau, mu, tv, ekey, eval;
 } plan_t;
@@ -628,7 +642,7 @@ static void plan_head(plan_t *p, const orc_thresholds *th)
             p->cap_fail = 1;
             break;
         }
-        tau = 1.0 - (1.0 - tau) * 0.5;
+        tau = 1.0 - (1.0 - tau) * ((orc_mutation & 64) ? 0.25 : 0.5);
         p->widened = 1;
     }
     p->tau = tau;
@@ -639,7 +653,7 @@ static void plan_head(plan_t *p, const orc_thresholds *th)
      * always pages less than a dense recompute); a caller-set cap that is
      * too small escalates to rung 4. */
     double F = factor_F(p);
-    uint64_t *cb = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(N > 0 ? N : 1));
+    uint64_t *cb = p->cval;
     for (int b = 0; b < N; b++)
         cb[b] = val_term(p, F, b);
     vb_t *o = (vb_t *)malloc(sizeof(vb_t) * (size_t)(N > 0 ? N : 1));
@@ -647,7 +661,7 @@ static void plan_head(plan_t *p, const orc_thresholds *th)
         o[b].v = cb[b];
         o[b].b = b;
     }
-    qsort(o, (size_t)N, sizeof(vb_t), cmp_vb_desc);
+    qsort(o, (size_t)N, sizeof(vb_t), (orc_mutation & 32) ? cmp_vb_asc : cmp_vb_desc);
     /* suffix sums: rest[k] = sum of o[k..N) */
     memset(p->inVP, 0, (size_t)N);
     int k = 0;
@@ -671,7 +685,6 @@ static void plan_head(plan_t *p, const orc_thresholds *th)
     if (k > vcap || p->eval > (double)th->v_tol)
         p->cap_fail = 1;
     free(o);
-    free(cb);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -708,14 +721,397 @@ void orc_dense_head(int T, int Hkv, int d, int g, const uint16_t *k, const uint1
 
 /* ------------------------------------------------------------------------ */
 /* The decode step                                                          */
+/* The work of one sequence runs in phases, each a loop over kv heads or q  */
+/* heads whose iterations touch disjoint outputs; with OpenMP the           */
+/* iterations run on threads.  The arithmetic of each head is the same      */
+/* sequence of operations whatever the thread count.                        */
 /* ------------------------------------------------------------------------ */
-#define TRP(ptr, idx) ((ptr) ? &(ptr)[idx] : NULL)
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 int orc_certified_decode(int B, int T, int Hq, int Hkv, int d, const uint16_t *K,
                          const uint16_t *V, const uint16_t *q, const orc_thresholds *th,
                          double *out, orc_report *rep, orc_trace *tr)
 {
     return orc_certified_decode_vb(B, T, Hq, Hkv, d, 4, K, V, q, th, out, rep, tr);
+}
+
+/* Sizes and per-sequence arrays shared by the phases of one sequence. */
+typedef struct {
+    int T, Hq, Hkv, d, G, N, np, has_part, Np, ng, v_bits;
+    size_t vcb, nb;
+    const uint16_t *Kn, *Vn; /* [T][Hkv][d] of the sequence */
+    const orc_thresholds *th;
+    /* tier 1 per kv head */
+    uint8_t *kc, *vc;        /* [Hkv][nb][64][d], [Hkv][nb][64][vcb] */
+    uint16_t *ks, *kz;       /* [Hkv][nb][d] */
+    uint16_t *vs, *vz;       /* [Hkv][nb][64][ng] */
+    float *eta, *vrange;     /* [Hkv][nb], [Hkv] */
+    /* per q head */
+    plan_t *plans;                        /* [Hq] */
+    float *bmax, *bl, *dl, *rh, *sc;      /* [Hq][Np] ([Hq][Np*64] for sc) */
+    uint64_t *M, *cval;                   /* [Hq][Np], [Hq][nb] */
+    uint8_t *inP, *inVP;                  /* [Hq][nb] */
+    float *smix;                          /* [Hq][Np*64] certified scores */
+    double *odense, *ocert;               /* [Hq][d] */
+    int64_t *D;                           /* [Hq] discordant pairs */
+    int *rank_ok;                         /* [Hq] */
+} seq_t;
+
+/* Phase 1, per kv head g: quantize every full block [Meth-1] and take the
+ * value range R_g over all tokens ("value ranges" of [Meth-2]). */
+static void kv_head_tier1(const seq_t *S, int n, int g, orc_trace *tr)
+{
+    const int d = S->d, Hkv = S->Hkv, N = S->N, T = S->T, ng = S->ng;
+    const size_t vcb = S->vcb, nb = S->nb;
+    uint8_t *kc = S->kc + (size_t)g * nb * ORC_BT * d;
+    uint16_t *ks = S->ks + (size_t)g * nb * d, *kz = S->kz + (size_t)g * nb * d;
+    uint8_t *vc = S->vc + (size_t)g * nb * ORC_BT * vcb;
+    uint16_t *vs = S->vs + (size_t)g * nb * ORC_BT * ng, *vz = S->vz + (size_t)g * nb * ORC_BT * ng;
+    float *eta = S->eta + (size_t)g * nb;
+    uint16_t *blk = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
+    uint16_t *blv = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
+    for (int b = 0; b < N; b++) {
+        for (int t = 0; t < ORC_BT; t++)
+            for (int c = 0; c < d; c++) {
+                size_t src = ((size_t)(b * ORC_BT + t) * Hkv + g) * d + c;
+                blk[t * d + c] = S->Kn[src];
+                blv[t * d + c] = S->Vn[src];
+            }
+        orc_quant_k_block(d, blk, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d);
+        orc_quant_v_block_bits(d, S->v_bits, blv, vc + (size_t)b * ORC_BT * vcb, vs + (size_t)b * ORC_BT * ng,
+                               vz + (size_t)b * ORC_BT * ng, &eta[b]);
+    }
+    free(blk);
+    free(blv);
+    size_t gofs = ((size_t)n * Hkv + g) * N;
+    if (tr->k_code)
+        memcpy(tr->k_code + gofs * ORC_BT * d, kc, (size_t)N * ORC_BT * d);
+    if (tr->k_s)
+        memcpy(tr->k_s + gofs * d, ks, (size_t)N * d * 2);
+    if (tr->k_z)
+        memcpy(tr->k_z + gofs * d, kz, (size_t)N * d * 2);
+    if (tr->v_code)
+        memcpy(tr->v_code + gofs * ORC_BT * vcb, vc, (size_t)N * ORC_BT * vcb);
+    if (tr->v_s)
+        memcpy(tr->v_s + gofs * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
+    if (tr->v_z)
+        memcpy(tr->v_z + gofs * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
+    if (tr->eta)
+        memcpy(tr->eta + gofs, eta, (size_t)N * sizeof(float));
+
+    double rmax = 0.0;
+    for (int c = 0; c < d; c++) {
+        double lo = INFINITY, hi = -INFINITY;
+        for (int t = 0; t < T; t++) {
+            double x = (double)orc_h2f(S->Vn[((size_t)t * Hkv + g) * d + c]);
+            if (x < lo)
+                lo = x;
+            if (x > hi)
+                hi = x;
+        }
+        if (hi - lo > rmax)
+            rmax = hi - lo;
+    }
+    S->vrange[g] = orc_ru32(rmax);
+    if (tr->vrange)
+        tr->vrange[(size_t)n * Hkv + g] = S->vrange[g];
+}
+
+/* Phase 2, per q head h: the scoring pass over tier 1 (the partial block
+ * from its FP16 keys), the plan (selection, bounds, rungs 1-2) from
+ * INT8-side quantities only [Contrib], the certified scores (FP16 keys on
+ * P, paged from tier 2 [Meth-3]) and exact dense attention.  Returns 1 when
+ * a cap of rung 1 or 2 was exhausted. */
+static int q_head_plan(const seq_t *S, int n, int h, const uint16_t *q, orc_trace *tr)
+{
+    const int d = S->d, Hkv = S->Hkv, N = S->N, np = S->np, Np = S->Np, G = S->G, g = h / G;
+    const size_t nb = S->nb;
+    const orc_thresholds *th = S->th;
+    const uint8_t *kc = S->kc + (size_t)g * nb * ORC_BT * d;
+    const uint16_t *ks = S->ks + (size_t)g * nb * d, *kz = S->kz + (size_t)g * nb * d;
+    const uint16_t *qh = q + ((size_t)n * S->Hq + h) * d;
+    float *sc = S->sc + (size_t)h * Np * ORC_BT;
+    float *bmax = S->bmax + (size_t)h * Np, *bl = S->bl + (size_t)h * Np;
+    float *dl = S->dl + (size_t)h * Np, *rh = S->rh + (size_t)h * Np;
+    uint16_t *blk = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
+
+    for (int b = 0; b < N; b++) {
+        orc_score_q8(d, qh, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d, th->sm_scale,
+                     sc + (size_t)b * ORC_BT);
+        orc_block_est(sc + (size_t)b * ORC_BT, ORC_BT, &bmax[b], &bl[b]);
+        orc_delta_rho(d, qh, ks + (size_t)b * d, kz + (size_t)b * d, th->sm_scale, &dl[b], &rh[b]);
+    }
+    if (S->has_part) {
+        for (int t = 0; t < np; t++)
+            for (int c = 0; c < d; c++)
+                blk[t * d + c] = S->Kn[((size_t)(N * ORC_BT + t) * Hkv + g) * d + c];
+        float *sp = sc + (size_t)N * ORC_BT;
+        orc_score_f16(d, qh, blk, np, th->sm_scale, sp);
+        for (int t = np; t < ORC_BT; t++)
+            sp[t] = 0.0f;
+        orc_block_est(sp, np, &bmax[N], &bl[N]);
+        rh[N] = rho_partial(d, qh, blk, np, th->sm_scale);
+        dl[N] = rh[N];
+    }
+    plan_t *p = &S->plans[h];
+    p->N = N;
+    p->has_part = S->has_part;
+    p->bmax = bmax;
+    p->bl = bl;
+    p->delta = dl;
+    p->rho = rh;
+    p->eta = S->eta + (size_t)g * nb;
+    p->R = (double)S->vrange[g];
+    p->M = S->M + (size_t)h * Np;
+    p->inP = S->inP + (size_t)h * nb;
+    p->inVP = S->inVP + (size_t)h * nb;
+    p->cval = S->cval + (size_t)h * nb;
+    plan_head(p, th);
+
+    size_t ho = (size_t)n * S->Hq + h;
+    if (tr->score)
+        memcpy(tr->score + ho * Np * ORC_BT, sc, (size_t)Np * ORC_BT * sizeof(float));
+    if (tr->bmax)
+        memcpy(tr->bmax + ho * Np, bmax, (size_t)Np * sizeof(float));
+    if (tr->bl)
+        memcpy(tr->bl + ho * Np, bl, (size_t)Np * sizeof(float));
+    if (tr->delta)
+        memcpy(tr->delta + ho * Np, dl, (size_t)Np * sizeof(float));
+    if (tr->rho)
+        memcpy(tr->rho + ho * Np, rh, (size_t)Np * sizeof(float));
+    if (tr->mref)
+        tr->mref[ho] = p->mref;
+    if (tr->mfx)
+        memcpy(tr->mfx + ho * Np, p->M, (size_t)Np * sizeof(uint64_t));
+    if (tr->cval)
+        memcpy(tr->cval + ho * N, p->cval, (size_t)N * sizeof(uint64_t));
+    if (tr->sel)
+        for (int b = 0; b < N; b++)
+            tr->sel[ho * N + b] = (uint8_t)(p->inP[b] | (p->inVP[b] << 1));
+    if (tr->bounds) {
+        tr->bounds[ho * 4 + 0] = p->mu;
+        tr->bounds[ho * 4 + 1] = p->tv;
+        tr->bounds[ho * 4 + 2] = p->ekey;
+        tr->bounds[ho * 4 + 3] = p->eval;
+    }
+
+    /* certified scores: FP16 keys on P (paged from tier 2) and on the
+     * partial block, INT8 scores on the tail [Meth-3] */
+    float *smix = S->smix + (size_t)h * Np * ORC_BT;
+    memcpy(smix, sc, (size_t)Np * ORC_BT * sizeof(float));
+    for (int b = 0; b < N; b++) {
+        if (!p->inP[b])
+            continue;
+        for (int t = 0; t < ORC_BT; t++)
+            for (int c = 0; c < d; c++)
+                blk[t * d + c] = S->Kn[((size_t)(b * ORC_BT + t) * Hkv + g) * d + c];
+        orc_score_f16(d, qh, blk, ORC_BT, th->sm_scale, smix + (size_t)b * ORC_BT);
+    }
+    orc_dense_head(S->T, Hkv, d, g, S->Kn, S->Vn, qh, (double)th->sm_scale, S->odense + (size_t)h * d);
+    free(blk);
+    return p->cap_fail;
+}
+
+/* Phase 3, per q head h: the rank-consistency check on the promoted blocks
+ * [Meth-3].  The INT8 order is (estimated mass M desc, index asc); the FP16
+ * order is (M16 desc, index asc), M16 the fixed-point FP16-key block mass
+ * relative to the largest FP16-key block max over P; D = Kendall discordant
+ * pairs between the two orders; inconsistent iff D > floor(rank_tol *
+ * K*(K*-1)/2). */
+static void q_head_rank(const seq_t *S, int n, int h, orc_trace *tr)
+{
+    const int N = S->N, Np = S->Np;
+    const plan_t *p = &S->plans[h];
+    const float *sm16 = S->smix + (size_t)h * Np * ORC_BT;
+    size_t nb = S->nb;
+    float *b16max = (float *)malloc(nb * sizeof(float)), *b16l = (float *)malloc(nb * sizeof(float));
+    uint64_t *keyI = (uint64_t *)malloc(nb * sizeof(uint64_t)), *key16 = (uint64_t *)malloc(nb * sizeof(uint64_t));
+    int *plist = (int *)malloc(nb * sizeof(int));
+    int kk = 0;
+    for (int b = 0; b < N; b++)
+        if (p->inP[b])
+            plist[kk++] = b;
+    float mr16 = -INFINITY;
+    for (int i = 0; i < kk; i++) {
+        int b = plist[i];
+        orc_block_est(sm16 + (size_t)b * ORC_BT, ORC_BT, &b16max[i], &b16l[i]);
+        if (b16max[i] > mr16)
+            mr16 = b16max[i];
+    }
+    if (orc_mutation & 8)
+        mr16 = p->mref;
+    size_t ho = (size_t)n * S->Hq + h;
+    if (tr->m16fx)
+        memset(tr->m16fx + ho * N, 0, (size_t)N * sizeof(uint64_t));
+    if (tr->score16) {
+        memset(tr->score16 + ho * N * ORC_BT, 0, (size_t)N * ORC_BT * sizeof(float));
+        for (int i = 0; i < kk; i++)
+            memcpy(tr->score16 + ho * N * ORC_BT + (size_t)plist[i] * ORC_BT, sm16 + (size_t)plist[i] * ORC_BT,
+                   ORC_BT * sizeof(float));
+    }
+    for (int i = 0; i < kk; i++) {
+        int b = plist[i];
+        float m = b16l[i] * orc_exp_c(b16max[i] - mr16);
+        uint64_t M16 = (uint64_t)((double)m * 4294967296.0);
+        if (tr->m16fx)
+            tr->m16fx[ho * N + b] = M16;
+        uint64_t tie = (orc_mutation & 4) ? (uint64_t)b : (uint64_t)(0xFFFF - b);
+        keyI[i] = (p->M[b] << 16) | tie;
+        key16[i] = (((orc_mutation & 16) ? p->M[b] : M16) << 16) | tie;
+    }
+    S->D[h] = orc_discordant(kk, keyI, key16);
+    double pairs = (double)kk * (double)(kk - 1) / 2.0;
+    double lim = floor((double)S->th->rank_tol * pairs);
+    S->rank_ok[h] = !((double)S->D[h] > lim);
+    free(b16max);
+    free(b16l);
+    free(keyI);
+    free(key16);
+    free(plist);
+}
+
+/* Phase 4, per q head h: the certified output, the measured key and value
+ * errors against exact attention, and the ladder outcome [Meth-3,
+ * four-rung fallback ladder]; heads at rung 3 or 4 return exact dense
+ * attention [Contrib, deterministic recovery]. */
+static void q_head_output(const seq_t *S, int n, int h, int rung4_pre, int rung4_post, const uint16_t *q,
+                          double *out, orc_report *rep, orc_trace *tr)
+{
+    const int d = S->d, Hkv = S->Hkv, N = S->N, T = S->T, G = S->G, g = h / G, ng = S->ng, Np = S->Np;
+    const size_t vcb = S->vcb, nb = S->nb;
+    const double sm = (double)S->th->sm_scale;
+    const plan_t *p = &S->plans[h];
+    const uint16_t *Vg = S->Vn;
+    const float *smh = S->smix + (size_t)h * Np * ORC_BT;
+    const uint8_t *vcg = S->vc + (size_t)g * nb * ORC_BT * vcb;
+    const uint16_t *vsg = S->vs + (size_t)g * nb * ORC_BT * ng;
+    const uint16_t *vzg = S->vz + (size_t)g * nb * ORC_BT * ng;
+    double *oc = S->ocert + (size_t)h * d;
+    const double *od = S->odense + (size_t)h * d;
+    double *ptil = (double *)malloc((size_t)T * sizeof(double));
+    double *pex = (double *)malloc((size_t)T * sizeof(double));
+    /* p~ over all T tokens */
+    double mx = -INFINITY;
+    for (int t = 0; t < T; t++)
+        if ((double)smh[t] > mx)
+            mx = (double)smh[t];
+    double den = 0.0;
+    for (int t = 0; t < T; t++) {
+        ptil[t] = exp((double)smh[t] - mx);
+        den += ptil[t];
+    }
+    for (int t = 0; t < T; t++)
+        ptil[t] /= den;
+    /* exact p */
+    {
+        const uint16_t *qh = q + ((size_t)n * S->Hq + h) * d;
+        double m2 = -INFINITY;
+        for (int t = 0; t < T; t++) {
+            const uint16_t *kt = S->Kn + ((size_t)t * Hkv + g) * d;
+            double a = 0.0;
+            for (int c = 0; c < d; c++)
+                a += (double)orc_h2f(qh[c]) * (double)orc_h2f(kt[c]);
+            pex[t] = sm * a;
+            if (pex[t] > m2)
+                m2 = pex[t];
+        }
+        double dd = 0.0;
+        for (int t = 0; t < T; t++) {
+            pex[t] = exp(pex[t] - m2);
+            dd += pex[t];
+        }
+        for (int t = 0; t < T; t++)
+            pex[t] /= dd;
+    }
+    double ek = 0.0, ev = 0.0;
+    for (int c = 0; c < d; c++) {
+        double acc = 0.0, akey = 0.0, aval = 0.0;
+        for (int t = 0; t < T; t++) {
+            int b = t / ORC_BT, tt = t % ORC_BT;
+            double v = (double)orc_h2f(Vg[((size_t)t * Hkv + g) * d + c]);
+            double vu = v;
+            if (b < N && !p->inVP[b]) {
+                int code;
+                if (S->v_bits == 8) {
+                    code = vcg[((size_t)b * ORC_BT + tt) * d + c];
+                } else {
+                    uint8_t byte = vcg[((size_t)b * ORC_BT + tt) * (d / 2) + c / 2];
+                    code = (c & 1) ? (byte >> 4) : (byte & 15);
+                }
+                size_t mi = ((size_t)b * ORC_BT + tt) * ng + c / ORC_VG;
+                vu = (double)orc_h2f(vzg[mi]) + (double)orc_h2f(vsg[mi]) * (double)code;
+            }
+            acc += ptil[t] * vu;
+            akey += (ptil[t] - pex[t]) * v;
+            aval += ptil[t] * (vu - v);
+        }
+        oc[c] = acc;
+        if (fabs(akey) > ek)
+            ek = fabs(akey);
+        if (fabs(aval) > ev)
+            ev = fabs(aval);
+    }
+    free(ptil);
+    free(pex);
+    size_t ho = (size_t)n * S->Hq + h;
+    if (tr->err_key)
+        tr->err_key[ho] = ek;
+    if (tr->err_val)
+        tr->err_val[ho] = ev;
+    if (tr->o_cert)
+        memcpy(tr->o_cert + ho * d, oc, (size_t)d * sizeof(double));
+    if (tr->o_dense)
+        memcpy(tr->o_dense + ho * d, od, (size_t)d * sizeof(double));
+
+    int mask = 0;
+    if (p->widened)
+        mask |= 2;
+    if (p->nvp > 0)
+        mask |= 4;
+    int is3 = !rung4_pre && !S->rank_ok[h];
+    if (is3)
+        mask |= 8;
+    int is4 = rung4_pre || rung4_post;
+    if (is4)
+        mask |= 16;
+    int dense = is3 || is4;
+    int rmax = 0;
+    for (int r = 1; r <= 4; r++)
+        if (mask & (1 << r))
+            rmax = r;
+    orc_report *R = &rep[ho];
+    R->kstar = p->kstar;
+    R->n_v_promoted = p->nvp;
+    R->tau_final = (float)p->tau;
+    R->rank_ok = rung4_pre ? -1 : S->rank_ok[h];
+    R->n_discordant = rung4_pre ? 0 : (int)S->D[h];
+    R->rung_mask = mask;
+    R->rung_max = rmax;
+    if (dense) {
+        R->e_key = R->e_val = R->tv_bound = 0.0f;
+        memcpy(out + ho * d, od, (size_t)d * sizeof(double));
+    } else {
+        R->e_key = orc_ru32(p->ekey);
+        R->e_val = orc_ru32(p->eval);
+        R->tv_bound = orc_ru32(p->tv);
+        memcpy(out + ho * d, oc, (size_t)d * sizeof(double));
+    }
 }
 
 int orc_certified_decode_vb(int B, int T, int Hq, int Hkv, int d, int v_bits, const uint16_t *K,
@@ -725,363 +1121,80 @@ int orc_certified_decode_vb(int B, int T, int Hq, int Hkv, int d, int v_bits, co
     if (B < 1 || T < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || (d != 64 && d != 128) ||
         (v_bits != 4 && v_bits != 8))
         return -1;
-    /* bytes of value codes per token */
-    const size_t vcb = (size_t)d * v_bits / 8;
-    const int G = Hq / Hkv, N = T / ORC_BT, np = T % ORC_BT, has_part = np > 0,
-              Np = N + has_part, ng = d / ORC_VG;
-    const double sm = (double)th->sm_scale;
     orc_trace empty;
     memset(&empty, 0, sizeof empty);
     if (!tr)
         tr = &empty;
-
-    /* per (sequence, kv head) tier-1 contents in the oracle's own layout */
-    size_t nb = (size_t)(N > 0 ? N : 1);
-    uint8_t *kc = (uint8_t *)malloc(nb * ORC_BT * d);
-    uint16_t *ks = (uint16_t *)malloc(nb * d * 2), *kz = (uint16_t *)malloc(nb * d * 2);
-    uint8_t *vc = (uint8_t *)malloc(nb * ORC_BT * vcb);
-    uint16_t *vs = (uint16_t *)malloc(nb * ORC_BT * ng * 2), *vz = (uint16_t *)malloc(nb * ORC_BT * ng * 2);
-    float *eta = (float *)malloc(nb * sizeof(float));
-    uint16_t *blk = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
-    uint16_t *blv = (uint16_t *)malloc((size_t)ORC_BT * d * 2);
-    /* per head work arrays */
-    float *sc = (float *)malloc((size_t)Np * ORC_BT * sizeof(float));
-    float *bmax = (float *)malloc((size_t)Np * sizeof(float)), *bl = (float *)malloc((size_t)Np * sizeof(float));
-    float *dl = (float *)malloc((size_t)Np * sizeof(float)), *rh = (float *)malloc((size_t)Np * sizeof(float));
-    uint64_t *M = (uint64_t *)malloc((size_t)Np * sizeof(uint64_t));
-    uint8_t *inP = (uint8_t *)malloc(nb), *inVP = (uint8_t *)malloc(nb);
-    double *odense = (double *)malloc((size_t)Hq * d * sizeof(double));
-    double *ocert = (double *)malloc((size_t)Hq * d * sizeof(double));
-    int *dense = (int *)malloc((size_t)Hq * sizeof(int));
-    /* per sequence: plans of all heads */
-    plan_t *plans = (plan_t *)calloc((size_t)Hq, sizeof(plan_t));
-    uint8_t *allP = (uint8_t *)malloc((size_t)Hq * nb), *allVP = (uint8_t *)malloc((size_t)Hq * nb);
-    uint64_t *allM = (uint64_t *)malloc((size_t)Hq * Np * sizeof(uint64_t));
-    float *allsc = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
-    double *ptil = (double *)malloc((size_t)Np * ORC_BT * sizeof(double));
-    double *pex = (double *)malloc((size_t)Np * ORC_BT * sizeof(double));
-    float *s16 = (float *)malloc((size_t)ORC_BT * sizeof(float));
-    float *b16max = (float *)malloc(nb * sizeof(float)), *b16l = (float *)malloc(nb * sizeof(float));
-    uint64_t *keyI = (uint64_t *)malloc(nb * sizeof(uint64_t)), *key16 = (uint64_t *)malloc(nb * sizeof(uint64_t));
-    int *plist = (int *)malloc(nb * sizeof(int));
-    float *vrange = (float *)malloc((size_t)Hkv * sizeof(float));
-    /* the certified scores of one head: FP16 on P and partial, INT8 on tail */
-    float *smix = (float *)malloc((size_t)Np * ORC_BT * sizeof(float));
-    float *allsmix = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
-    /* quantized tier 1 of all kv heads of the sequence (needed for outputs) */
-    uint8_t *all_vc = (uint8_t *)malloc((size_t)Hkv * nb * ORC_BT * vcb);
-    uint16_t *all_vs = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * ng * 2);
-    uint16_t *all_vz = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * ng * 2);
+    seq_t S;
+    memset(&S, 0, sizeof S);
+    S.T = T;
+    S.Hq = Hq;
+    S.Hkv = Hkv;
+    S.d = d;
+    S.G = Hq / Hkv;
+    S.N = T / ORC_BT;
+    S.np = T % ORC_BT;
+    S.has_part = S.np > 0;
+    S.Np = S.N + S.has_part;
+    S.ng = d / ORC_VG;
+    S.v_bits = v_bits;
+    S.vcb = (size_t)d * v_bits / 8; /* bytes of value codes per token */
+    S.nb = (size_t)(S.N > 0 ? S.N : 1);
+    S.th = th;
+    const size_t nb = S.nb, Np = (size_t)S.Np;
+    S.kc = (uint8_t *)malloc((size_t)Hkv * nb * ORC_BT * d);
+    S.ks = (uint16_t *)malloc((size_t)Hkv * nb * d * 2);
+    S.kz = (uint16_t *)malloc((size_t)Hkv * nb * d * 2);
+    S.vc = (uint8_t *)malloc((size_t)Hkv * nb * ORC_BT * S.vcb);
+    S.vs = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * S.ng * 2);
+    S.vz = (uint16_t *)malloc((size_t)Hkv * nb * ORC_BT * S.ng * 2);
+    S.eta = (float *)malloc((size_t)Hkv * nb * sizeof(float));
+    S.vrange = (float *)malloc((size_t)Hkv * sizeof(float));
+    S.plans = (plan_t *)calloc((size_t)Hq, sizeof(plan_t));
+    S.bmax = (float *)malloc((size_t)Hq * Np * sizeof(float));
+    S.bl = (float *)malloc((size_t)Hq * Np * sizeof(float));
+    S.dl = (float *)malloc((size_t)Hq * Np * sizeof(float));
+    S.rh = (float *)malloc((size_t)Hq * Np * sizeof(float));
+    S.sc = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
+    S.M = (uint64_t *)malloc((size_t)Hq * Np * sizeof(uint64_t));
+    S.cval = (uint64_t *)malloc((size_t)Hq * nb * sizeof(uint64_t));
+    S.inP = (uint8_t *)malloc((size_t)Hq * nb);
+    S.inVP = (uint8_t *)malloc((size_t)Hq * nb);
+    S.smix = (float *)malloc((size_t)Hq * Np * ORC_BT * sizeof(float));
+    S.odense = (double *)malloc((size_t)Hq * d * sizeof(double));
+    S.ocert = (double *)malloc((size_t)Hq * d * sizeof(double));
+    S.D = (int64_t *)calloc((size_t)Hq, sizeof(int64_t));
+    S.rank_ok = (int *)malloc((size_t)Hq * sizeof(int));
 
     for (int n = 0; n < B; n++) {
-        const uint16_t *Kn = K + (size_t)n * T * Hkv * d;
-        const uint16_t *Vn = V + (size_t)n * T * Hkv * d;
+        S.Kn = K + (size_t)n * T * Hkv * d;
+        S.Vn = V + (size_t)n * T * Hkv * d;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int g = 0; g < Hkv; g++)
+            kv_head_tier1(&S, n, g, tr);
+        /* rung 4 before paging: a cap exhausted on any head of (n, layer) */
         int rung4_pre = 0;
-        for (int g = 0; g < Hkv; g++) {
-            /* quantize every full block of this kv head [Meth-1] */
-            for (int b = 0; b < N; b++) {
-                for (int t = 0; t < ORC_BT; t++)
-                    for (int c = 0; c < d; c++) {
-                        size_t src = ((size_t)(b * ORC_BT + t) * Hkv + g) * d + c;
-                        blk[t * d + c] = Kn[src];
-                        blv[t * d + c] = Vn[src];
-                    }
-                orc_quant_k_block(d, blk, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d);
-                orc_quant_v_block_bits(d, v_bits, blv, vc + (size_t)b * ORC_BT * vcb, vs + (size_t)b * ORC_BT * ng,
-                                       vz + (size_t)b * ORC_BT * ng, &eta[b]);
-            }
-            size_t gofs = ((size_t)n * Hkv + g) * N;
-            if (tr->k_code)
-                memcpy(tr->k_code + gofs * ORC_BT * d, kc, (size_t)N * ORC_BT * d);
-            if (tr->k_s)
-                memcpy(tr->k_s + gofs * d, ks, (size_t)N * d * 2);
-            if (tr->k_z)
-                memcpy(tr->k_z + gofs * d, kz, (size_t)N * d * 2);
-            if (tr->v_code)
-                memcpy(tr->v_code + gofs * ORC_BT * vcb, vc, (size_t)N * ORC_BT * vcb);
-            if (tr->v_s)
-                memcpy(tr->v_s + gofs * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
-            if (tr->v_z)
-                memcpy(tr->v_z + gofs * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
-            if (tr->eta)
-                memcpy(tr->eta + gofs, eta, (size_t)N * sizeof(float));
-            memcpy(all_vc + (size_t)g * nb * ORC_BT * vcb, vc, (size_t)N * ORC_BT * vcb);
-            memcpy(all_vs + (size_t)g * nb * ORC_BT * ng, vs, (size_t)N * ORC_BT * ng * 2);
-            memcpy(all_vz + (size_t)g * nb * ORC_BT * ng, vz, (size_t)N * ORC_BT * ng * 2);
-
-            /* value range R_g over all tokens, "value ranges" of [Meth-2] */
-            double rmax = 0.0;
-            for (int c = 0; c < d; c++) {
-                double lo = INFINITY, hi = -INFINITY;
-                for (int t = 0; t < T; t++) {
-                    double x = (double)orc_h2f(Vn[((size_t)t * Hkv + g) * d + c]);
-                    if (x < lo)
-                        lo = x;
-                    if (x > hi)
-                        hi = x;
-                }
-                if (hi - lo > rmax)
-                    rmax = hi - lo;
-            }
-            vrange[g] = orc_ru32(rmax);
-            if (tr->vrange)
-                tr->vrange[(size_t)n * Hkv + g] = vrange[g];
-
-            for (int j = 0; j < G; j++) {
-                int h = g * G + j;
-                const uint16_t *qh = q + ((size_t)n * Hq + h) * d;
-                /* scoring pass over tier 1; the partial block is scored
-                 * from its FP16 keys */
-                for (int b = 0; b < N; b++) {
-                    orc_score_q8(d, qh, kc + (size_t)b * ORC_BT * d, ks + (size_t)b * d, kz + (size_t)b * d,
-                                 th->sm_scale, sc + (size_t)b * ORC_BT);
-                    orc_block_est(sc + (size_t)b * ORC_BT, ORC_BT, &bmax[b], &bl[b]);
-                    orc_delta_rho(d, qh, ks + (size_t)b * d, kz + (size_t)b * d, th->sm_scale, &dl[b], &rh[b]);
-                }
-                if (has_part) {
-                    for (int t = 0; t < np; t++)
-                        for (int c = 0; c < d; c++)
-                            blk[t * d + c] = Kn[((size_t)(N * ORC_BT + t) * Hkv + g) * d + c];
-                    float *sp = sc + (size_t)N * ORC_BT;
-                    orc_score_f16(d, qh, blk, np, th->sm_scale, sp);
-                    for (int t = np; t < ORC_BT; t++)
-                        sp[t] = 0.0f;
-                    orc_block_est(sp, np, &bmax[N], &bl[N]);
-                    rh[N] = rho_partial(d, qh, blk, np, th->sm_scale);
-                    dl[N] = rh[N];
-                }
-                plan_t *p = &plans[h];
-                p->N = N;
-                p->has_part = has_part;
-                p->bmax = bmax;
-                p->bl = bl;
-                p->delta = dl;
-                p->rho = rh;
-                p->eta = eta;
-                p->R = (double)vrange[g];
-                p->M = allM + (size_t)h * Np;
-                p->inP = allP + (size_t)h * nb;
-                p->inVP = allVP + (size_t)h * nb;
-                plan_head(p, th);
-                if (p->cap_fail)
-                    rung4_pre = 1;
-
-                size_t ho = (size_t)n * Hq + h;
-                if (tr->score)
-                    memcpy(tr->score + ho * Np * ORC_BT, sc, (size_t)Np * ORC_BT * sizeof(float));
-                if (tr->bmax)
-                    memcpy(tr->bmax + ho * Np, bmax, (size_t)Np * sizeof(float));
-                if (tr->bl)
-                    memcpy(tr->bl + ho * Np, bl, (size_t)Np * sizeof(float));
-                if (tr->delta)
-                    memcpy(tr->delta + ho * Np, dl, (size_t)Np * sizeof(float));
-                if (tr->rho)
-                    memcpy(tr->rho + ho * Np, rh, (size_t)Np * sizeof(float));
-                if (tr->mref)
-                    tr->mref[ho] = p->mref;
-                if (tr->mfx)
-                    memcpy(tr->mfx + ho * Np, p->M, (size_t)Np * sizeof(uint64_t));
-                if (tr->sel)
-                    for (int b = 0; b < N; b++)
-                        tr->sel[ho * N + b] = (uint8_t)(p->inP[b] | (p->inVP[b] << 1));
-                if (tr->bounds) {
-                    tr->bounds[ho * 4 + 0] = p->mu;
-                    tr->bounds[ho * 4 + 1] = p->tv;
-                    tr->bounds[ho * 4 + 2] = p->ekey;
-                    tr->bounds[ho * 4 + 3] = p->eval;
-                }
-
-                /* certified scores: FP16 keys on P (paged from tier 2) and
-                 * on the partial block, INT8 scores on the tail [Meth-3] */
-                memcpy(smix, sc, (size_t)Np * ORC_BT * sizeof(float));
-                for (int b = 0; b < N; b++) {
-                    if (!p->inP[b])
-                        continue;
-                    for (int t = 0; t < ORC_BT; t++)
-                        for (int c = 0; c < d; c++)
-                            blk[t * d + c] = Kn[((size_t)(b * ORC_BT + t) * Hkv + g) * d + c];
-                    orc_score_f16(d, qh, blk, ORC_BT, th->sm_scale, smix + (size_t)b * ORC_BT);
-                }
-                memcpy(allsmix + (size_t)h * Np * ORC_BT, smix, (size_t)Np * ORC_BT * sizeof(float));
-                memcpy(allsc + (size_t)h * Np * ORC_BT, sc, (size_t)Np * ORC_BT * sizeof(float));
-                orc_dense_head(T, Hkv, d, g, Kn, Vn, qh, sm, odense + (size_t)h * d);
-            }
-        }
-
-        /* rank-consistency check on the promoted blocks [Meth-3]: order by
-         * INT8-estimated mass vs order by FP16-key mass; Kendall discordant
-         * pairs D; inconsistent iff D > floor(rank_tol * K*(K*-1)/2). */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rung4_pre)
+        for (int h = 0; h < Hq; h++)
+            rung4_pre |= q_head_plan(&S, n, h, q, tr);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int h = 0; h < Hq; h++)
+            q_head_rank(&S, n, h, tr);
+        /* rung 4 after the rank check: more than f_layer of the q heads
+         * at rung 3 */
         int n_rung3 = 0;
-        int64_t *Dh = (int64_t *)calloc((size_t)Hq, sizeof(int64_t));
-        int *rank_ok = (int *)malloc((size_t)Hq * sizeof(int));
-        for (int h = 0; h < Hq; h++) {
-            plan_t *p = &plans[h];
-            const float *sm16 = allsmix + (size_t)h * Np * ORC_BT;
-            int kk = 0;
-            for (int b = 0; b < N; b++)
-                if (p->inP[b])
-                    plist[kk++] = b;
-            float mr16 = -INFINITY;
-            for (int i = 0; i < kk; i++) {
-                int b = plist[i];
-                orc_block_est(sm16 + (size_t)b * ORC_BT, ORC_BT, &b16max[i], &b16l[i]);
-                if (b16max[i] > mr16)
-                    mr16 = b16max[i];
-            }
-            size_t ho = (size_t)n * Hq + h;
-            if (tr->m16fx)
-                memset(tr->m16fx + ho * N, 0, (size_t)N * sizeof(uint64_t));
-            if (tr->score16) {
-                memset(tr->score16 + ho * N * ORC_BT, 0, (size_t)N * ORC_BT * sizeof(float));
-                for (int i = 0; i < kk; i++)
-                    memcpy(tr->score16 + ho * N * ORC_BT + (size_t)plist[i] * ORC_BT,
-                           sm16 + (size_t)plist[i] * ORC_BT, ORC_BT * sizeof(float));
-            }
-            for (int i = 0; i < kk; i++) {
-                int b = plist[i];
-                float m = b16l[i] * orc_exp_c(b16max[i] - mr16);
-                uint64_t M16 = (uint64_t)((double)m * 4294967296.0);
-                if (tr->m16fx)
-                    tr->m16fx[ho * N + b] = M16;
-                keyI[i] = (p->M[b] << 16) | (uint64_t)(0xFFFF - b);
-                key16[i] = (M16 << 16) | (uint64_t)(0xFFFF - b);
-            }
-            Dh[h] = orc_discordant(kk, keyI, key16);
-            double pairs = (double)kk * (double)(kk - 1) / 2.0;
-            double lim = floor((double)th->rank_tol * pairs);
-            rank_ok[h] = !((double)Dh[h] > lim);
-            if (!rank_ok[h])
-                n_rung3++;
-        }
+        for (int h = 0; h < Hq; h++)
+            n_rung3 += !S.rank_ok[h];
         int rung4_post = !rung4_pre && ((double)n_rung3 > (double)th->f_layer * (double)Hq);
         if (tr->seq_flags)
             tr->seq_flags[n] = rung4_pre | (rung4_post << 1);
-
-        /* outputs */
-        for (int h = 0; h < Hq; h++) {
-            plan_t *p = &plans[h];
-            int g = h / G;
-            const uint16_t *Vg = Vn;
-            const float *smh = allsmix + (size_t)h * Np * ORC_BT;
-            const uint8_t *vcg = all_vc + (size_t)g * nb * ORC_BT * vcb;
-            const uint16_t *vsg = all_vs + (size_t)g * nb * ORC_BT * ng;
-            const uint16_t *vzg = all_vz + (size_t)g * nb * ORC_BT * ng;
-            double *oc = ocert + (size_t)h * d;
-            double *od = odense + (size_t)h * d;
-            /* p~ over all T tokens */
-            double mx = -INFINITY;
-            for (int t = 0; t < T; t++)
-                if ((double)smh[t] > mx)
-                    mx = (double)smh[t];
-            double den = 0.0;
-            for (int t = 0; t < T; t++) {
-                ptil[t] = exp((double)smh[t] - mx);
-                den += ptil[t];
-            }
-            for (int t = 0; t < T; t++)
-                ptil[t] /= den;
-            /* exact p */
-            {
-                const uint16_t *qh = q + ((size_t)n * Hq + h) * d;
-                double m2 = -INFINITY;
-                for (int t = 0; t < T; t++) {
-                    const uint16_t *kt = Kn + ((size_t)t * Hkv + g) * d;
-                    double a = 0.0;
-                    for (int c = 0; c < d; c++)
-                        a += (double)orc_h2f(qh[c]) * (double)orc_h2f(kt[c]);
-                    pex[t] = sm * a;
-                    if (pex[t] > m2)
-                        m2 = pex[t];
-                }
-                double dd = 0.0;
-                for (int t = 0; t < T; t++) {
-                    pex[t] = exp(pex[t] - m2);
-                    dd += pex[t];
-                }
-                for (int t = 0; t < T; t++)
-                    pex[t] /= dd;
-            }
-            double ek = 0.0, ev = 0.0;
-            for (int c = 0; c < d; c++) {
-                double acc = 0.0, akey = 0.0, aval = 0.0;
-                for (int t = 0; t < T; t++) {
-                    int b = t / ORC_BT, tt = t % ORC_BT;
-                    double v = (double)orc_h2f(Vg[((size_t)t * Hkv + g) * d + c]);
-                    double vu = v;
-                    if (b < N && !p->inVP[b]) {
-                        int code;
-                        if (v_bits == 8) {
-                            code = vcg[((size_t)b * ORC_BT + tt) * d + c];
-                        } else {
-                            uint8_t byte = vcg[((size_t)b * ORC_BT + tt) * (d / 2) + c / 2];
-                            code = (c & 1) ? (byte >> 4) : (byte & 15);
-                        }
-                        size_t mi = ((size_t)b * ORC_BT + tt) * ng + c / ORC_VG;
-                        vu = (double)orc_h2f(vzg[mi]) + (double)orc_h2f(vsg[mi]) * (double)code;
-                    }
-                    acc += ptil[t] * vu;
-                    akey += (ptil[t] - pex[t]) * v;
-                    aval += ptil[t] * (vu - v);
-                }
-                oc[c] = acc;
-                if (fabs(akey) > ek)
-                    ek = fabs(akey);
-                if (fabs(aval) > ev)
-                    ev = fabs(aval);
-            }
-            size_t ho = (size_t)n * Hq + h;
-            if (tr->err_key)
-                tr->err_key[ho] = ek;
-            if (tr->err_val)
-                tr->err_val[ho] = ev;
-            if (tr->o_cert)
-                memcpy(tr->o_cert + ho * d, oc, (size_t)d * sizeof(double));
-            if (tr->o_dense)
-                memcpy(tr->o_dense + ho * d, od, (size_t)d * sizeof(double));
-
-            /* ladder outcome [Meth-3, four-rung fallback ladder] */
-            int mask = 0;
-            if (p->widened)
-                mask |= 2;
-            if (p->nvp > 0)
-                mask |= 4;
-            int is3 = !rung4_pre && !rank_ok[h];
-            if (is3)
-                mask |= 8;
-            int is4 = rung4_pre || rung4_post;
-            if (is4)
-                mask |= 16;
-            dense[h] = is3 || is4;
-            int rmax = 0;
-            for (int r = 1; r <= 4; r++)
-                if (mask & (1 << r))
-                    rmax = r;
-            orc_report *R = &rep[ho];
-            R->kstar = p->kstar;
-            R->n_v_promoted = p->nvp;
-            R->tau_final = (float)p->tau;
-            R->rank_ok = rung4_pre ? -1 : rank_ok[h];
-            R->n_discordant = rung4_pre ? 0 : (int)Dh[h];
-            R->rung_mask = mask;
-            R->rung_max = rmax;
-            if (dense[h]) {
-                R->e_key = R->e_val = R->tv_bound = 0.0f;
-                memcpy(out + ho * d, od, (size_t)d * sizeof(double));
-            } else {
-                R->e_key = orc_ru32(p->ekey);
-                R->e_val = orc_ru32(p->eval);
-                R->tv_bound = orc_ru32(p->tv);
-                memcpy(out + ho * d, oc, (size_t)d * sizeof(double));
-            }
-        }
-        free(Dh);
-        free(rank_ok);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int h = 0; h < Hq; h++)
+            q_head_output(&S, n, h, rung4_pre, rung4_post, q, out, rep, tr);
     }
 
-    free(kc); free(ks); free(kz); free(vc); free(vs); free(vz); free(eta); free(blk); free(blv);
-    free(sc); free(bmax); free(bl); free(dl); free(rh); free(M); free(inP); free(inVP);
-    free(odense); free(ocert); free(dense); free(plans); free(allP); free(allVP); free(allM);
-    free(allsc); free(ptil); free(pex); free(s16); free(b16max); free(b16l); free(keyI); free(key16);
-    free(plist); free(vrange); free(smix); free(allsmix); free(all_vc); free(all_vs); free(all_vz);
+    free(S.kc); free(S.ks); free(S.kz); free(S.vc); free(S.vs); free(S.vz); free(S.eta); free(S.vrange);
+    free(S.plans); free(S.bmax); free(S.bl); free(S.dl); free(S.rh); free(S.sc); free(S.M); free(S.cval);
+    free(S.inP); free(S.inVP); free(S.smix); free(S.odense); free(S.ocert); free(S.D); free(S.rank_ok);
     return 0;
 }

@@ -76,11 +76,23 @@ typedef struct {
     double *err_val;   /* [B][Hq] measured |sum p~ (v_used - v)|_inf          */
     double *o_cert;    /* [B][Hq][d] certified output before any fallback     */
     double *o_dense;   /* [B][Hq][d] exact dense attention                    */
+    uint64_t *cval;    /* [B][Hq][N] fixed-point E_val contribution per block */
 } orc_trace;
 
-/* Deliberate mistakes, used only by tests that check that the dominance
- * tests can fail (bit0: eta_b forced to 0, bit1: Delta halved). */
+/* Deliberate mistakes, used only by tests that check that the pins can
+ * fail: bit0 eta_b forced to 0; bit1 Delta halved; bit2 the rank keys'
+ * tie-break reversed (index desc); bit3 the FP16-side masses of the rank
+ * check taken relative to the INT8 reference max instead of the largest
+ * FP16-key block max over P; bit4 the FP16-side rank key built from the
+ * INT8 mass; bit5 rung-2 blocks taken in ascending contribution order;
+ * bit6 rung-1 widening by 1 - tau <- (1 - tau) / 4; bit7 rho of the
+ * unfinished block from the signed key maximum. */
 extern int orc_mutation;
+
+/* OpenMP threads of the decode step (heads run in parallel; the results
+ * do not depend on it).  Without OpenMP both are no-ops returning 1. */
+void orc_set_threads(int n);
+int orc_get_threads(void);
 
 /* Conversions and elementary pieces (exported for the oracle's own pins). */
 float orc_h2f(uint16_t h);
