@@ -642,7 +642,7 @@ static void plan_head(plan_t *p, const orc_thresholds *th)
             p->cap_fail = 1;
             break;
         }
-        tau = 1.0 - (1.0 - tau) * ((orc_mutation & 64) ? 0.25 : 0.5);
+        tau = 1.0 - (1.0 - tau) * ((orc_mutation & 64) ? (1.0 / 3.0) : 0.5);
         p->widened = 1;
     }
     p->tau = tau;

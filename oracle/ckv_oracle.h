@@ -85,7 +85,7 @@ typedef struct {
  * check taken relative to the INT8 reference max instead of the largest
  * FP16-key block max over P; bit4 the FP16-side rank key built from the
  * INT8 mass; bit5 rung-2 blocks taken in ascending contribution order;
- * bit6 rung-1 widening by 1 - tau <- (1 - tau) / 4; bit7 rho of the
+ * bit6 rung-1 widening by 1 - tau <- (1 - tau) / 3; bit7 rho of the
  * unfinished block from the signed key maximum. */
 extern int orc_mutation;
 
