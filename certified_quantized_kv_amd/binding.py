@@ -15,7 +15,7 @@ EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv", 
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
             "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache",
-            "ckv_set_device_paging", "ckv_set_staged_paging"]
+            "ckv_set_device_paging", "ckv_set_staged_paging", "ckv_inject_paging_fault"]
 
 
 class CkvError(RuntimeError):
@@ -94,6 +94,7 @@ def lib():
         L.ckv_enable_fp16_cache.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
         L.ckv_set_device_paging.argtypes = [vp, i32]
         L.ckv_set_staged_paging.argtypes = [vp, i32]
+        L.ckv_inject_paging_fault.argtypes = [vp, i32]
         for name in EXPORTED:
             if name not in ("ckv_destroy", "ckv_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -229,10 +230,19 @@ class Cache:
             out = torch.empty((B, self.Hq, self.d), dtype=torch.float32, device=q.device)
         rep = np.zeros((B, self.Hq), REPORT_DTYPE)
         th = thresholds if isinstance(thresholds, Thresholds) else Thresholds(**thresholds)
-        _check(lib().ckv_certified_decode_attention(
+        st = lib().ckv_certified_decode_attention(
             self._h, layer, ctypes.c_void_p(q.data_ptr()), B, ctypes.byref(th),
-            ctypes.c_void_p(out.data_ptr()), _np_ptr(rep), _stream_ptr(stream)))
+            ctypes.c_void_p(out.data_ptr()), _np_ptr(rep), _stream_ptr(stream))
+        if st != 0:
+            err = CkvError(st, lib().ckv_last_error().decode())
+            err.report = rep   # every head at rung_max = -1
+            raise err
         return out, rep
+
+    def inject_paging_fault(self, after_copies=0):
+        """Make the paging copy after `after_copies` further copies report
+        failure (tests of the error path); < 0 clears the injection."""
+        _check(lib().ckv_inject_paging_fault(self._h, int(after_copies)))
 
     def dense_decode_attention(self, k_blocks, v_blocks, n_tokens, q, sm_scale, out=None,
                                stream=None):

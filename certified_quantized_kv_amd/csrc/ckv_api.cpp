@@ -7,7 +7,6 @@
 // Section tags refer to the page "Runtime-Certified Bounded-Error Quantized
 // Attention" (technical summary): [Meth-1] tiered storage, [Meth-3] the
 // adaptive selection and the fallback ladder.
-#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 #include <immintrin.h>
 
@@ -156,9 +155,11 @@ static void stager_work(Stager *S) {
     }
 }
 
-static void stager_thread(Stager *S) {
+// `seen`: the generation current when the thread was started; the thread
+// works only for later ones (a generation issued before it started belongs
+// to the threads that were running then).
+static void stager_thread(Stager *S, uint64_t seen) {
     (void)hipSetDevice(S->device);
-    uint64_t seen = 0;
     for (;;) {
         {
             std::unique_lock<std::mutex> lk(S->m);
@@ -234,6 +235,9 @@ struct ckv_cache {
     bool prof = false;
     ckv_profile pf{};
     Stager *stager = nullptr;  // staged paging when set
+    // ckv_inject_paging_fault: paging copies still to issue before the one
+    // that reports failure (-1: none)
+    long fault_after = -1;
 };
 
 namespace {
@@ -571,8 +575,13 @@ ckv_status ckv_set_staged_paging(ckv_cache *c, int threads) {
     Stager *S = c->stager;
     S->quit = false;
     S->nthreads = threads;
+    uint64_t gen0;
+    {
+        std::lock_guard<std::mutex> lk(S->m);
+        gen0 = S->gen;
+    }
     try {
-        for (int i = 0; i < threads; ++i) S->th.emplace_back(stager_thread, S);
+        for (int i = 0; i < threads; ++i) S->th.emplace_back(stager_thread, S, gen0);
     } catch (...) {
         stager_stop(S);
         S->nthreads = 0;  // staged paging stays off: no thread would pack
@@ -768,19 +777,23 @@ static void page_runs(ckv_cache *c, int layer, int n, int g, int N, const uint8_
     }
 }
 
-// hipMemcpyBatchAsync exists from HIP 7.1 on; the HIP runtime loaded in the
-// process may be older, so it is looked up at run time.
-using batch_fn = hipError_t (*)(void **, void **, size_t *, size_t, hipMemcpyAttributes *, size_t *,
-                                size_t, size_t *, hipStream_t);
-static batch_fn batch_copy() {
-    static batch_fn f = (batch_fn)dlsym(RTLD_DEFAULT, "hipMemcpyBatchAsync");
-    return f;
+// One host-to-device paging copy on stream `st`.  With a fault injected by
+// ckv_inject_paging_fault, the chosen copy is not issued and reports
+// failure, as a failed hipMemcpyAsync would.
+static hipError_t page_copy(ckv_cache *c, void *dst, const void *src, size_t bytes, hipStream_t st) {
+    if (c->fault_after >= 0) {
+        if (c->fault_after == 0) {
+            c->fault_after = -1;
+            return hipErrorUnknown;
+        }
+        --c->fault_after;
+    }
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st);
 }
 
 // Issue a paging round over the paging streams (each run to the stream with
-// the fewest bytes so far; per stream one batched call when the runtime has
-// it, else one hipMemcpyAsync per run), then, if `join`, join them on
-// side[0].
+// the fewest bytes so far, one hipMemcpyAsync per run), then, if `join`,
+// join them on side[0].
 static ckv_status issue_copies(ckv_cache *c, CopyList &cl, bool join = true) {
     if (cl.size.empty()) return CKV_OK;
     CopyList per[NSIDE];
@@ -797,16 +810,7 @@ static ckv_status issue_copies(ckv_cache *c, CopyList &cl, bool join = true) {
     for (int k = 0; k < NSIDE; ++k) {
         CopyList &q = per[k];
         if (q.size.empty()) continue;
-        size_t fail_idx = 0;
-        hipError_t e = hipErrorNotSupported;
-        if (batch_fn f = batch_copy())
-            e = f(q.dst.data(), q.src.data(), q.size.data(), q.size.size(), nullptr, nullptr, 0,
-                  &fail_idx, c->side[k]);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            for (size_t i = 0; i < q.size.size(); ++i)
-                HIPCHK(hipMemcpyAsync(q.dst[i], q.src[i], q.size[i], hipMemcpyHostToDevice, c->side[k]));
-        }
+        for (size_t i = 0; i < q.size.size(); ++i) HIPCHK(page_copy(c, q.dst[i], q.src[i], q.size[i], c->side[k]));
         if (k > 0 && join) {
             HIPCHK(hipEventRecord(c->ev_side[k], c->side[k]));
             HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_side[k], 0));
@@ -914,7 +918,7 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
             hipStream_t st = c->side[slot % NSIDE];
             uint8_t *dc = S.dring + (size_t)slot * S.stride;
             const size_t cb = PAGE_HDR + (size_t)nb * S.blk_bytes;
-            e = hipMemcpyAsync(dc, S.hring + (size_t)slot * S.stride, cb, hipMemcpyHostToDevice, st);
+            e = page_copy(c, dc, S.hring + (size_t)slot * S.stride, cb, st);
             if (e == hipSuccess) e = launch_page_scatter(dc, nb, S.blk_bytes, st);
             if (e == hipSuccess) e = hipEventRecord(S.ev[slot], st);
             if (e != hipSuccess) break;
@@ -948,9 +952,10 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
 
 }  // namespace
 
-ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q, int batch,
-                                          const ckv_thresholds *th, float *out,
-                                          ckv_head_report *report, void *stream) {
+namespace {
+
+ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, const ckv_thresholds *th,
+                          float *out, ckv_head_report *report, void *stream) {
     auto t_start = std::chrono::steady_clock::now();
     if (!c) return fail(CKV_EINVAL, "null cache");
     const ckv_config &cf = c->cfg;
@@ -1276,6 +1281,32 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
         c->pf.counts[PH_STEP] += 1;
     }
+    return CKV_OK;
+}
+
+}  // namespace
+
+ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q, int batch,
+                                          const ckv_thresholds *th, float *out,
+                                          ckv_head_report *report, void *stream) {
+    const ckv_status st = certified_step(c, layer, q, batch, th, out, report, stream);
+    if (st != CKV_OK && c && layer >= 0 && layer < c->cfg.n_layers) {
+        // blocks listed for paging are marked staged before their copies
+        // are issued; after a failed step none of them can be trusted, so
+        // the layer's next step pages them again
+        std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
+        std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
+        if (layer < c->pcache_layers) {
+            std::fill(c->pstaged_k[layer].begin(), c->pstaged_k[layer].end(), 0);
+            std::fill(c->pstaged_v[layer].begin(), c->pstaged_v[layer].end(), 0);
+        }
+    }
+    return st;
+}
+
+ckv_status ckv_inject_paging_fault(ckv_cache *c, int after_copies) {
+    if (!c) return fail(CKV_EINVAL, "null cache");
+    c->fault_after = after_copies < 0 ? -1 : after_copies;
     return CKV_OK;
 }
 

@@ -38,9 +38,9 @@ static hipError_t dispatch(int d, int G, F f) {
 }
 
 // ===========================================================================
-// K1: INT8 scoring pass [Meth-3 "lightweight scoring pass using INT8 keys to
-// estimate per-block attention masses"] and the per-token score
-// perturbation bound [Meth-2 "bounded by the per-token score perturbation"].
+// K1: INT8 scoring pass [Meth-3: scores from the INT8 keys give an estimate
+// of each block's attention mass] and the per-token bound on the score
+// error from quantization [Meth-2: E_key follows from it].
 //
 // Score of token t for q head h in block b, as an exact integer dot product:
 //   w_c = q_c s_c (exact in FP32), e = floor(log2 max_c |w_c|),
@@ -1135,8 +1135,8 @@ __device__ __forceinline__ void write_partials(VAcc<D, G, F> &va, const float *k
 // K3 (k_tail) / K4a values (k_promoted4, k_promoted16): split-K flash
 // decoding over one split of blocks of a (kv head, sequence); 256 threads,
 // one wave per block, two blocks in flight per wave.
-//   VP_TAIL   heads outside P and VP [Meth-3: "remaining tail blocks stay
-//             INT8"]: INT8 scores, INT4 values.
+//   VP_TAIL   heads outside P and VP [Meth-3: the blocks not promoted keep
+//             their INT8 keys]: INT8 scores, INT4 values.
 //   VP_INT4   heads of P without FP16 values: FP16-key scores (k_keys16),
 //             INT4 values.
 //   VP_FP16   heads of VP (FP16-key scores on P, else INT8 scores) and every

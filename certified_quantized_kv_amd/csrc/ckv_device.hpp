@@ -111,20 +111,10 @@ __device__ __forceinline__ double fx_bound(uint64_t sum, bool sat) {
     return (double)sum * 0x1p-32 * (1.0 + 0x1p-50);
 }
 
-__device__ __forceinline__ double gamma_n(int n) {
-    double nu = (double)n * 0x1p-24;
-    return nu / (1.0 - nu);
-}
-
 // ---- wave reductions (wave64) ---------------------------------------------
 
 // Halving-tree sum: lane i adds lane i + stride for stride 32..1; the result
 // is in lane 0 (other lanes hold partial sums).
-__device__ __forceinline__ float tree64_f32(float v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
-    return v;
-}
 __device__ __forceinline__ double tree64_f64(double v) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
@@ -140,11 +130,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 __device__ __forceinline__ double wave_max_f64(double v) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) v = fmax(v, __shfl_xor(v, s, 64));
-    return v;
-}
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
     return v;
 }
 __device__ __forceinline__ int wave_sum_i32(int v) {
@@ -272,7 +257,7 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 }
 
 // The halving tree over 64 lanes (strides 32, 16 across rows, then 8..1
-// inside row 0); the result is in lane 0.  Same pairing as tree64_f32.
+// inside row 0); the result is in lane 0.  Same pairing as tree64_f64.
 __device__ __forceinline__ float tree64_f32_dpp(float v) {
     v = v + __shfl_down(v, 32, 64);
     v = v + __shfl_down(v, 16, 64);

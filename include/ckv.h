@@ -282,6 +282,17 @@ typedef struct {
 ckv_status ckv_set_profiling(ckv_cache *c, int enable);
 ckv_status ckv_get_profile(const ckv_cache *c, ckv_profile *p);
 
+/* Fault injection for tests of the error path of a decode step: the host-to-
+ * device paging copy issued after `after_copies` further copies (0: the
+ * next one) is not issued and reports failure, as a failed hipMemcpyAsync
+ * would; the injection then clears itself.  < 0 clears it.  The step that
+ * meets it returns CKV_EHIP with every report at rung_max = -1 and forgets
+ * which blocks of the layer are staged, so the next step pages them again
+ * and is computed as if the failed step had not happened.  Device paging
+ * (ckv_set_device_paging) issues no copies for the listed blocks.
+ * Errors: EINVAL (null cache). */
+ckv_status ckv_inject_paging_fault(ckv_cache *c, int after_copies);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,20 +64,18 @@ def gpu_run(k, v, q, th, chunks=None, cache=None, v_bits=4):
     return c, out.cpu().numpy().astype(np.float64), rep, step
 
 
-def check_parity(k, v, q, th, res, c, out, rep, step, seqs=None, kv_heads=None):
-    """Compare the GPU step with the oracle result `res` (computed on the
-    sequences `seqs` and kv heads `kv_heads` of the GPU batch)."""
+def check_parity(k, v, q, th, res, c, out, rep, step):
+    """Compare the GPU step with the oracle result `res` on every sequence
+    and head of the batch."""
     B, T, Hkv, d = k.shape
     Hq = q.shape[1]
     G = Hq // Hkv
     N = T // 64
     tr = res.trace
-    seqs = list(range(B)) if seqs is None else list(seqs)
-    kvh = list(range(Hkv)) if kv_heads is None else list(kv_heads)
-    heads = [g * G + j for g in kvh for j in range(G)]
-    for oi, n in enumerate(seqs):
+    for n in range(B):
+        oi = n
         # tier 1, bit-exact
-        for og, g in enumerate(kvh):
+        for og, g in enumerate(range(Hkv)):
             for b in sorted({0, N // 2, N - 1} if N else set()):
                 e = c.export_block(0, n, g, b)
                 assert np.array_equal(e["k_code"], tr["k_code"][oi, og, b]), (n, g, b)
@@ -88,7 +86,7 @@ def check_parity(k, v, q, th, res, c, out, rep, step, seqs=None, kv_heads=None):
                 assert np.array_equal(e["v_z"], tr["v_z"][oi, og, b])
                 assert e["eta"][0] == tr["eta"][oi, og, b]
         Np = tr["score"].shape[-1] // 64
-        for oh, h in enumerate(heads):
+        for oh, h in enumerate(range(Hq)):
             g, j = h // G, h % G
             ctx = (n, h)
             assert np.array_equal(step["score"][n, h, :Np * 64], tr["score"][oi, oh]), ctx
@@ -106,26 +104,19 @@ def check_parity(k, v, q, th, res, c, out, rep, step, seqs=None, kv_heads=None):
             ro, rg = res.report[oi, oh], rep[n, h]
             for f in ("kstar", "n_v_promoted", "tau_final"):
                 assert ro[f] == rg[f], (ctx, f, ro[f], rg[f])
-        if kv_heads is None:
-            # ladder outcomes are per (sequence, layer): whole sequence needed
-            assert step["seq_flags"][n] == tr["seq_flags"][oi], n
-            for h in range(Hq):
-                ro, rg = res.report[oi, h], rep[n, h]
-                for f in ("rank_ok", "n_discordant", "rung_max", "rung_mask", "e_key", "e_val",
-                          "tv_bound"):
-                    assert ro[f] == rg[f], ((n, h), f, ro[f], rg[f])
-                if not (tr["seq_flags"][oi] & 1):
-                    inP = (tr["sel"][oi, h] & 1).astype(bool)
-                    assert np.array_equal(step["m16fx"][n, h, :N][inP], tr["m16fx"][oi, h][inP]), (n, h)
-            ref = res.out[oi]
-            assert np.all(np.abs(out[n] - ref) <= ATOL + RTOL * np.abs(ref)), \
-                (n, np.abs(out[n] - ref).max())
-        else:
-            # sampled kv heads: certified heads against the oracle's certified
-            # output, fallen-back heads against exact dense attention
-            for oh, h in enumerate(heads):
-                ref = tr["o_cert"][oi, oh] if rep[n, h]["rung_max"] < 3 else tr["o_dense"][oi, oh]
-                assert np.all(np.abs(out[n, h] - ref) <= ATOL + RTOL * np.abs(ref)), (n, h)
+        # the ladder outcome (per sequence and layer)
+        assert step["seq_flags"][n] == tr["seq_flags"][oi], n
+        for h in range(Hq):
+            ro, rg = res.report[oi, h], rep[n, h]
+            for f in ("rank_ok", "n_discordant", "rung_max", "rung_mask", "e_key", "e_val",
+                      "tv_bound"):
+                assert ro[f] == rg[f], ((n, h), f, ro[f], rg[f])
+            if not (tr["seq_flags"][oi] & 1):
+                inP = (tr["sel"][oi, h] & 1).astype(bool)
+                assert np.array_equal(step["m16fx"][n, h, :N][inP], tr["m16fx"][oi, h][inP]), (n, h)
+        ref = res.out[oi]
+        assert np.all(np.abs(out[n] - ref) <= ATOL + RTOL * np.abs(ref)), \
+            (n, np.abs(out[n] - ref).max())
 
 
 def both(k, v, q, th, chunks=None, v_bits=4):
@@ -306,43 +297,80 @@ def test_llama_8k_layer_symmetric_cache():
     both(L.k, L.v, L.q, oracle.default_thresholds(L.sm), v_bits=8)
 
 
+# The rungs each stress layer is built to reach (the workload's layer
+# variants): the oracle and the GPU must both reach them, so a drift of the
+# generator cannot silently drop rung-3/4 coverage at full size.
+STRESS_RUNGS = {
+    0: dict(mask_all=0b1110, seq_flags=0, min_rung3=1),    # rungs 1, 2 and 3 on flipped pairs
+    1: dict(mask_all=0b11110, seq_flags=2, min_rung3=17),  # > half the heads at rung 3 -> rung 4
+    2: dict(mask_all=0b1110, seq_flags=0, min_rung3=1),    # rung 3 on the flat-copy group
+    3: dict(mask_all=0b0100, seq_flags=0, min_rung3=0),    # certifies with rung 2
+}
+
+
 @pytest.mark.parametrize("layer", [0, 1, 2, 3])
 def test_stress_32k_layers(layer):
     L = datagen.make_layer("stress_32k", layer)
     res, rep = both(L.k, L.v, L.q, oracle.default_thresholds(L.sm))
+    want = STRESS_RUNGS[layer]
+    for r in (res.report[0], rep[0]):
+        assert np.bitwise_or.reduce(r["rung_mask"]) == want["mask_all"], layer
+        assert int(np.sum(r["rank_ok"] == 0)) >= want["min_rung3"], layer
+    assert res.trace["seq_flags"][0] == want["seq_flags"]
+    if want["seq_flags"] & 2:
+        assert np.all(rep[0]["rung_max"] == 4)
 
 
-def test_llama_32k_batch4_sampled_sequence():
-    """Full 4 x 32K layer on the GPU; the oracle recomputes sequence 2."""
-    L = datagen.make_layer("llama_32k", 0)
+def full_layer(name, layer):
+    """A full layer of a workload on the GPU against the oracle on every
+    sequence and head: tier 1, every intermediate, the ladder outcome
+    (rank verdicts, discordant counts, rungs, reported bounds, FP16-side
+    masses) and the outputs."""
+    L = datagen.make_layer(name, layer)
     th = oracle.default_thresholds(L.sm)
+    print(f"case {name} layer {layer}", flush=True)
+    res = oracle.certified_decode(L.k, L.v, L.q, th)
     c, out, rep, step = gpu_run(L.k, L.v, L.q, th)
-    res = oracle.certified_decode(L.k[2:3], L.v[2:3], L.q[2:3], th)
-    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step, seqs=[2])
+    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step)
     c.close()
+    return res, rep
 
 
-def test_needle_64k_sampled_kv_head():
-    """Full 64K layer (the needle workload's shorter context) on the GPU;
-    the oracle recomputes kv head 2's group."""
-    L = datagen.make_layer("needle_64k", 0)
-    th = oracle.default_thresholds(L.sm)
-    c, out, rep, step = gpu_run(L.k, L.v, L.q, th)
-    g = 2
-    res = oracle.certified_decode(L.k[:, :, g:g + 1], L.v[:, :, g:g + 1], L.q[:, 4 * g:4 * g + 4], th)
-    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step, kv_heads=[g])
-    c.close()
+def test_llama_32k_batch4_layer0():
+    """Full 4 x 32K layer, all four sequences."""
+    full_layer("llama_32k", 0)
 
 
-def test_needle_128k_sampled_kv_head():
-    """Full 128K layer on the GPU; the oracle recomputes kv head 5's group."""
-    L = datagen.make_layer("needle_128k", 0)
-    th = oracle.default_thresholds(L.sm)
-    c, out, rep, step = gpu_run(L.k, L.v, L.q, th)
-    g = 5
-    res = oracle.certified_decode(L.k[:, :, g:g + 1], L.v[:, :, g:g + 1], L.q[:, 4 * g:4 * g + 4], th)
-    check_parity(L.k, L.v, L.q, th, res, c, out, rep, step, kv_heads=[g])
-    c.close()
+def test_needle_64k_layer0():
+    full_layer("needle_64k", 0)
+
+
+def test_needle_128k_layer0():
+    """128K: K* of about 400 blocks per head, so the rank check sorts."""
+    res, rep = full_layer("needle_128k", 0)
+    assert rep["kstar"].max() > 512
+
+
+@pytest.mark.parametrize("name", ["llama_8k", "llama_32k", "needle_64k", "needle_128k"])
+def test_last_layer(name):
+    """Layer 31 of each LLaMA-shaped workload (other seeds, positions and
+    outlier channels than layer 0)."""
+    full_layer(name, 31)
+
+
+@pytest.mark.parametrize("case", ["all", "default"])
+def test_context_above_2048_blocks(case):
+    """2100 full blocks and an unfinished one: the selection keeps its
+    per-block arrays in global memory (above 2048 blocks) and, with every
+    block promoted, the rank check counts pairs in global memory (K* above
+    2048)."""
+    k, v, q, sm = micro(2100, T=2100 * 64 + 17, Hq=4, Hkv=1, d=64,
+                        kind="flat" if case == "all" else "peaked")
+    th = oracle.default_thresholds(sm, **(dict(tau_cov=1.0, rank_tol=1.0) if case == "all" else {}))
+    res, rep = both(k, v, q, th)
+    if case == "all":
+        assert np.all(rep["kstar"] == 2100)
+        assert np.all(rep["n_discordant"] > 0)
 
 
 # -- the dense comparator and error paths ---------------------------------------
