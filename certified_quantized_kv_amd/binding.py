@@ -15,7 +15,8 @@ EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv", 
             "ckv_certified_decode_attention", "ckv_dense_decode_attention", "ckv_footprint",
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
             "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache",
-            "ckv_set_device_paging", "ckv_set_staged_paging", "ckv_inject_paging_fault"]
+            "ckv_set_device_paging", "ckv_set_staged_paging", "ckv_inject_paging_fault",
+            "ckv_dense_decode_attention_noalloc"]
 
 
 class CkvError(RuntimeError):
@@ -82,6 +83,8 @@ def lib():
         L.ckv_certified_decode_attention.argtypes = [vp, i32, vp, i32, ctypes.POINTER(Thresholds),
                                                      vp, vp, vp]
         L.ckv_dense_decode_attention.argtypes = [vp, vp, vp, i32, vp, i32, f32, vp, vp]
+        L.ckv_dense_decode_attention_noalloc.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, f32,
+                                                         vp, vp]
         L.ckv_footprint.argtypes = [vp, szp, szp, szp]
         L.ckv_seq_length.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int)]
         L.ckv_last_error.argtypes = []
@@ -305,6 +308,20 @@ class Cache:
         r = {f: getattr(p, f) for f, _ in Profile._fields_ if f not in ("ms", "counts")}
         r["phases"] = {nm: (float(p.ms[i]), int(p.counts[i])) for i, nm in enumerate(PHASES)}
         return r
+
+
+def dense_decode_attention_noalloc(k_blocks, v_blocks, n_tokens, q, sm_scale, n_kv_heads, out,
+                                   stream=None):
+    """ckv_dense_decode_attention_noalloc: exact dense attention without a
+    cache and without allocating (the caller passes `out`, a float32 CUDA
+    tensor [batch][n_q_heads][head_dim]); k_blocks, v_blocks in the block
+    layout of Cache.dense_decode_attention."""
+    B, Hq, d = q.shape
+    _check(lib().ckv_dense_decode_attention_noalloc(
+        ctypes.c_void_p(k_blocks.data_ptr()), ctypes.c_void_p(v_blocks.data_ptr()), int(n_tokens),
+        ctypes.c_void_p(q.data_ptr()), B, Hq, int(n_kv_heads), d, float(sm_scale),
+        ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+    return out
 
 
 def _torch_cuda():

@@ -44,6 +44,17 @@ ckv_status fail(ckv_status st, const char *fmt, ...) {
     return st;
 }
 
+}  // namespace
+
+// Sets the calling thread's last-error message (for the other translation
+// units of the library) and returns `st`.
+int ckv::set_error(int st, const char *msg) {
+    g_err = msg;
+    return st;
+}
+
+namespace {
+
 #define HIPCHK(expr)                                                                        \
     do {                                                                                    \
         hipError_t e_ = (expr);                                                             \
@@ -203,11 +214,11 @@ struct ckv_cache {
     int *wcnt = nullptr;
     HeadPlan *plan = nullptr;
     float2 *st16 = nullptr;
-    int *dskip = nullptr, *dtmp_len = nullptr;
+    int *dskip = nullptr;
     // pinned host mirrors
     uint32_t *h_sel = nullptr, *h_mask = nullptr;
     HeadPlan *h_plan = nullptr;
-    int *h_skip = nullptr, *h_len = nullptr, *h_tmp_len = nullptr;
+    int *h_skip = nullptr, *h_len = nullptr;
     std::vector<int> len;  // [L][B]
     // append staging (device, grown on demand)
     uint16_t *ain_k = nullptr, *ain_v = nullptr, *pk = nullptr, *pv = nullptr;
@@ -294,17 +305,19 @@ void fill_failed_reports(ckv_head_report *r, int n) {
     }
 }
 
-// Blocks per split of the value passes: a multiple of 4 (one block per wave
-// of a 256-thread workgroup), about 1024 workgroups per launch.
+}  // namespace
+
 // Blocks per split of the value passes: about 704 four-wave workgroups, so
 // that the grid is resident in one round at three waves per SIMD (256 CUs x
 // 4 SIMDs x 3 = 3072 waves); a multiple of 4 in [4, 64].
-int split_blocks(int nb, int Hkv, int batch) {
+int ckv::split_blocks(int nb, int Hkv, int batch) {
     const long units = (long)nb * Hkv * batch;
     int bps = (int)((units + 703) / 704);
     bps = std::max(4, std::min(64, (bps + 3) / 4 * 4));
     return bps;
 }
+
+namespace {
 
 // Block slots per wave of the scoring pass (one-wave workgroups): about
 // 2816 waves, at least 2 slots so that one block's loads overlap the other.
@@ -333,7 +346,7 @@ void ckv_destroy(ckv_cache *c) {
     for (void *p : {(void *)c->ain_k, (void *)c->ain_v, (void *)c->pk, (void *)c->pv})
         if (p) (void)hipFree(p);
     for (void *p : {(void *)c->t2k, (void *)c->t2v, (void *)c->h_sel, (void *)c->h_mask,
-                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_tmp_len})
+                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len})
         if (p) (void)hipHostFree(p);
     for (hipStream_t st : c->side)
         if (st) (void)hipStreamDestroy(st);
@@ -443,14 +456,12 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->wcnt, (size_t)WL_KINDS * B * Hkv));
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
     CTRY(dalloc(c, &c->dskip, (size_t)B));
-    CTRY(dalloc(c, &c->dtmp_len, (size_t)B));
     CTRY(dalloc(c, &c->dmask, (size_t)B * Hkv));
     CTRY(halloc(c, &c->h_sel, sblk));
     CTRY(halloc(c, &c->h_mask, (size_t)B * Hkv));
     CTRY(halloc(c, &c->h_plan, (size_t)B * Hq));
     CTRY(halloc(c, &c->h_skip, (size_t)B));
     CTRY(halloc(c, &c->h_len, (size_t)L * B));
-    CTRY(halloc(c, &c->h_tmp_len, (size_t)B));
     c->len.assign((size_t)L * B, 0);
     c->staged_k.assign(sblk, 0);
     c->staged_v.assign(sblk, 0);
@@ -1318,13 +1329,12 @@ ckv_status ckv_dense_decode_attention(ckv_cache *c, const void *k, const void *v
         return fail(CKV_EINVAL, "bad batch, token count (multiple of 64) or scale");
     HIPCHK(hipSetDevice(cf.device));
     hipStream_t s = (hipStream_t)stream;
-    for (int n = 0; n < batch; ++n) c->h_tmp_len[n] = ntok;
-    HIPCHK(hipMemcpyAsync(c->dtmp_len, c->h_tmp_len, sizeof(int) * batch, hipMemcpyHostToDevice, s));
     DenseSrc S{};
     S.k = (const uint16_t *)k;
     S.v = (const uint16_t *)v;
     S.kp = S.vp = nullptr;
-    S.len = c->dtmp_len;
+    S.len = nullptr;  // every sequence holds ntok tokens
+    S.len_all = ntok;
     S.nstride = (size_t)ntok / 64;
     S.mask = nullptr;
     S.q = (const uint16_t *)q;

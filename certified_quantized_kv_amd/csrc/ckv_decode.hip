@@ -1945,7 +1945,7 @@ __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
     if (!mask) return;
-    const int len = __builtin_amdgcn_readfirstlane(S.len[n]);
+    const int len = S.len ? __builtin_amdgcn_readfirstlane(S.len[n]) : S.len_all;
     const int N = len / 64, np = len % 64;
     const int nslot = N + (np ? 1 : 0);
     const int b0 = sp * S.bps, b1 = min(nslot, b0 + S.bps);
@@ -2022,7 +2022,7 @@ __global__ __launch_bounds__(64) void k_merge_dense(DenseSrc S) {
     const int g = h / G, j = h % G;
     const uint32_t mask = S.mask ? S.mask[n * S.Hkv + g] : ((1u << G) - 1u);
     if (!(mask & (1u << j))) return;
-    const int len = __builtin_amdgcn_readfirstlane(S.len[n]);
+    const int len = S.len ? __builtin_amdgcn_readfirstlane(S.len[n]) : S.len_all;
     const int nslot = len / 64 + ((len % 64) ? 1 : 0);
     const int nsp = (nslot + S.bps - 1) / S.bps;
     const float *pt = S.part + (size_t)(n * S.Hq + h) * S.nsplit_cap * (D + 2);

@@ -108,12 +108,13 @@ enum { WL_KEYS = 0, WL_INT4 = 1, WL_FP16 = 2, WL_TAIL = 3, WL_KINDS = 4 };
 
 // Source of an exact dense attention: FP16 blocks of (seq n, kv head g) at
 // k + ((n * Hkv + g) * nstride + b) * 64 * D (K chunk-interleaved, V
-// channel-major), len[n] tokens, the unfinished block (if any) at
-// kp / vp + (n * Hkv + g) * 64 * D.
+// channel-major), len[n] tokens (len_all for every sequence when len is
+// null), the unfinished block (if any) at kp / vp + (n * Hkv + g) * 64 * D.
 struct DenseSrc {
     const uint16_t *k, *v;
     const uint16_t *kp, *vp;
     const int *len;
+    int len_all;
     size_t nstride;
     const uint32_t *mask;       // [B][Hkv] q heads of the group to compute (null: all)
     const uint16_t *q;
@@ -128,6 +129,11 @@ struct Th {
     float tau, k_tol, v_tol, rank_tol, f_layer;
     int n_widen, vcap;  // vcap <= 0: no cap
 };
+
+// Blocks per split of the value passes and the dense pass (ckv_api.cpp).
+int split_blocks(int nb, int Hkv, int batch);
+// The calling thread's last-error message (ckv_api.cpp); returns st.
+int set_error(int st, const char *msg);
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 // header bytes of a staged-paging chunk: up to 512 block addresses

@@ -163,6 +163,29 @@ ckv_status ckv_dense_decode_attention(ckv_cache *c, const void *k, const void *v
                                       const void *q_fp16, int batch, float sm_scale, float *out,
                                       void *stream);
 
+/* The same exact dense decode attention as ckv_dense_decode_attention,
+ * without a cache and without allocating anything: for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  No hipMalloc, hipFree or other
+ * allocating call is made.
+ * k, v, n_tokens, q_fp16, batch, sm_scale, out: as for
+ *   ckv_dense_decode_attention (device pointers, the same block layout).
+ * n_q_heads, n_kv_heads, head_dim: the head shape (head_dim 64 or 128,
+ *   n_q_heads / n_kv_heads in {1, 2, 4, 8}).
+ * Runs on the calling thread's current device; `stream` must belong to it.
+ * The split partials live in a static 4 MiB device array per GPU, held
+ * until the process ends: batch * n_q_heads * (head_dim + 2) * 4 bytes must
+ * not exceed it (batch * n_q_heads <= 7710 at head_dim 128), otherwise
+ * CKV_EINVAL; longer contexts use longer splits.  Every call on one GPU
+ * shares that array, and each call writes every partial it reads, so no
+ * state carries over; calls that overlap on one GPU (other streams or
+ * threads) race.  Stream-ordered, returns without synchronizing.
+ * Errors: EINVAL, EHIP. */
+ckv_status ckv_dense_decode_attention_noalloc(const void *k, const void *v, int n_tokens,
+                                              const void *q_fp16, int batch, int n_q_heads,
+                                              int n_kv_heads, int head_dim, float sm_scale,
+                                              float *out, void *stream);
+
 /* Bytes held: tier 1 + partial blocks + staging + scratch on the device,
  * tier 2 in pinned host memory. */
 ckv_status ckv_footprint(const ckv_cache *c, size_t *dev_bytes, size_t *host_bytes,
