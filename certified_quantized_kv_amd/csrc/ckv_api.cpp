@@ -319,13 +319,6 @@ int ckv::split_blocks(int nb, int Hkv, int batch) {
 
 namespace {
 
-// Block slots per wave of the scoring pass (one-wave workgroups): about
-// 2816 waves, at least 2 slots so that one block's loads overlap the other.
-int score_slots(int nb, int Hkv, int batch) {
-    const long units = (long)(nb + 1) * Hkv * batch;
-    return (int)std::max(2L, std::min(64L, (units + 2815) / 2816));
-}
-
 float ru32h(double x) {
     float f = (float)x;
     if ((double)f < x) f = std::nextafter(f, INFINITY);
@@ -996,7 +989,6 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     St.nb = nb;
     St.NS = c->NS;
     St.bps = split_blocks(nb, Hkv, batch);
-    St.spw = score_slots(nb, Hkv, batch);
     St.ncu = c->ncu;
     St.nsplit = (nb + St.bps - 1) / St.bps;
     St.nsplit_cap = c->nsplit_cap;

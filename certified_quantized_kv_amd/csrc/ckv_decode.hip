@@ -54,58 +54,79 @@ static hipError_t dispatch(int d, int G, F f) {
 //   Delta = sm (kappa H + E_w + (2^-20 + 2^-23) A + 2^-23 E_w) (1 + 2^-20),
 //   rho = sm 2^-23 A (1 + 2^-20), E_w = 2^(e-21) 255 d,
 // with H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c) as FP64 trees.
-// One wave per St.spw consecutive block slots of a (kv head, sequence).
-// ===========================================================================
+// A workgroup holds SCORE_W waves on consecutive block slots of a (kv head,
+// sequence), SCORE_BPW slots per wave, and shares q through LDS.  Each wave
+// requests the codes and scales of all its slots when it starts, then scores
+// them in turn: the later slots' data arrive while the first is computed,
+// and many short waves keep the memory system full.  Nothing waits on a
+// workgroup barrier after the q set-up.
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+constexpr int SCORE_W = 4;  // waves per workgroup of the scoring pass
+#ifndef SCORE_BPW
+#define SCORE_BPW 1
+#endif
+constexpr int SCORE_BPW_ = SCORE_BPW;  // block slots per wave
+
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
+__global__ __launch_bounds__(64 * SCORE_W) void k_score(Layout Ly, Step St) {
     constexpr int CPL = D / 64;           // channels per lane (meta, trees)
     constexpr int KS = D / 64;            // MFMA k-steps of 64 channels
     constexpr int RT = (4 * G + 15) / 16; // MFMA row tiles of 4 heads x 4 digits
     constexpr int CPR = D / 16;           // channels per lane in the set-up rows
-    const int g = blockIdx.y, n = blockIdx.z, lane = threadIdx.x;
+    constexpr int BPW = SCORE_BPW_;
+    const int g = blockIdx.y, n = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l = St.layer;
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
     const int N = len / 64, np = len % 64;
     const int nslot = N + (np ? 1 : 0);
-    const int s0 = blockIdx.x * St.spw, s1 = min(nslot, s0 + St.spw);
-    if (s0 >= s1) return;
+    const int slot0 = (blockIdx.x * SCORE_W + wave) * BPW;
     __shared__ float qs[G][D];
-    __shared__ __attribute__((aligned(16))) int8_t dig[G][4][D];
-    __shared__ double hd_C[G];
-    __shared__ int hd_e[G], hd_W[G];
-    __shared__ float hd_dl[G], hd_rh[G];
+    __shared__ __attribute__((aligned(16))) int8_t dig[SCORE_W][G][4][D];
+    __shared__ uint32_t kms[SCORE_W][D];
+    __shared__ double hd_C[SCORE_W][G];
+    __shared__ int hd_e[SCORE_W][G], hd_W[SCORE_W][G];
+    __shared__ float hd_dl[SCORE_W][G], hd_rh[SCORE_W][G];
     const int i16 = lane % 16;
-    // operands of a full block: codes (MFMA B operands) and this lane's
-    // scale / offset words; requested one block ahead
-    auto issue = [&](int slot, v4i (&bq)[4][KS], uint32_t (&km)[CPR]) {
-        const size_t bi = Ly.blk(l, n, g, slot);
-        const uint8_t *kb = Ly.kq + bi * 64 * D;
+    // the operands of the wave's full blocks, requested first: codes (MFMA B
+    // operands) and the scale | offset words (D / 64 per lane, spread
+    // through LDS below); slots past the full blocks load nothing
+    v4i bq[BPW][4][KS];
+    uint32_t kmw[BPW][CPL];
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile)
+    for (int u = 0; u < BPW; ++u) {
+        const int slot = slot0 + u;
+        if (slot < N) {
+            const size_t bi = Ly.blk(l, n, g, slot);
+            const uint8_t *kb = Ly.kq + bi * 64 * D;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                bq[tile][ks] = *reinterpret_cast<const v4i *>(kb + (ks * 4 + lane / 16) * 1024 +
-                                                              (tile * 16 + lane % 16) * 16);
+            for (int tile = 0; tile < 4; ++tile)
 #pragma unroll
-        for (int k = 0; k < CPR; ++k) km[k] = Ly.kmeta[bi * D + i16 + 16 * k];
-    };
-    v4i bq0[4][KS], bq1[4][KS];
-    uint32_t km0[CPR], km1[CPR];
-    if (s0 < N) issue(s0, bq0, km0);
-    for (int i = lane; i < G * D; i += 64) dig[i / D][3][i % D] = 0;  // the unused digit row
-    for (int i = lane; i < G * D; i += 64)
+                for (int ks = 0; ks < KS; ++ks)
+                    bq[u][tile][ks] = *reinterpret_cast<const v4i *>(kb + (ks * 4 + lane / 16) * 1024 +
+                                                                     (tile * 16 + lane % 16) * 16);
+            if constexpr (CPL == 2) {
+                const uint2 w = reinterpret_cast<const uint2 *>(Ly.kmeta + bi * D)[lane];
+                kmw[u][0] = w.x;
+                kmw[u][CPL - 1] = w.y;
+            } else {
+                kmw[u][0] = Ly.kmeta[bi * D + lane];
+            }
+        }
+    }
+    for (int i = threadIdx.x; i < G * D; i += 64 * SCORE_W)
         qs[i / D][i % D] = h2f(St.q[((size_t)n * Ly.Hq + g * G + i / D) * D + (i % D)]);
     __syncthreads();
-    if (s0 == 0)  // q in FP64, [D][G] per (seq, kv head), for the FP16-key pass
+    if (blockIdx.x == 0 && wave == 0)  // q in FP64, [D][G] per (seq, kv head), for the FP16-key pass
         for (int i = lane; i < G * D; i += 64)
             St.qd[((size_t)n * Ly.Hkv + g) * D * G + i] = (double)qs[i % G][i / G];
+    if (slot0 >= nslot) return;  // no workgroup barrier follows
     const float sm = St.sm;
     const size_t NS64 = (size_t)St.NS * 64;
 
+    // unfinished block: FP16 keys on the device, FP64 chain, one rounding
     auto partial = [&](int slot) {
-        // unfinished block: FP16 keys on the device, FP64 chain, one rounding
         const uint16_t *kp = Ly.kpart + Ly.seqg(l, n, g) * 64 * D;
         const bool valid = lane < np;
         double a[G];
@@ -153,30 +174,44 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
         }
     };
 
-    auto full = [&](int slot, const v4i (&bq)[4][KS], const uint32_t (&km)[CPR]) {
-        // the previous block's reads of dig / hd_* are complete
-        __syncthreads();
+    // a full block: per-head weights, digits and bounds, then the exact
+    // integer dot products on the matrix cores and the block estimate
+    auto full = [&](int slot, const v4i (&bqu)[4][KS], const uint32_t (&kmwu)[CPL]) {
+        // the scale | offset words of channels i16 + 16 k, k < D / 16; the
+        // wave's previous block has finished reading kms, dig and hd_*
+        wave_sync();
+        if constexpr (CPL == 2) {
+            kms[wave][2 * lane] = kmwu[0];
+            kms[wave][2 * lane + 1] = kmwu[CPL - 1];
+        } else {
+            kms[wave][lane] = kmwu[0];
+        }
+        for (int i = lane; i < G * D; i += 64) dig[wave][i / D][3][i % D] = 0;  // the unused digit row
+        wave_sync();
+        uint32_t km[CPR];
+#pragma unroll
+        for (int k = 0; k < CPR; ++k) km[k] = kms[wave][i16 + 16 * k];
         if (lane == 0) St.sel[((size_t)n * Ly.Hkv + g) * Ly.Nmax + slot] = 0u;
-        // set-up per head: row r of the wave takes head r (+4 on a second pass);
-        // lane i of the row holds channels c = i + 16 k, k < D/16, so the
-        // halving tree over the channels runs in-lane for strides >= 16 and
-        // across the row (DPP) for strides 8..1.
+        // set-up per head: row r of the wave takes head r (+4 on a second
+        // pass); lane i of the row holds channels c = i + 16 k, k < D/16, so
+        // the halving tree over the channels runs in-lane for strides >= 16
+        // and across the row (DPP) for strides 8..1.
         const int r = lane / 16;
         float sc[CPR], zc[CPR];
-    #pragma unroll
+#pragma unroll
         for (int k = 0; k < CPR; ++k) {
             sc[k] = h2f((uint16_t)(km[k] & 0xFFFFu));
             zc[k] = h2f((uint16_t)(km[k] >> 16));
         }
         const double kappa = 0.5 + 0x1p-14;
-    #pragma unroll
+#pragma unroll
         for (int pass = 0; pass < (G + 3) / 4; ++pass) {
             const int j = pass * 4 + r;
             if (j < G) {
                 float w[CPR], cz[CPR];
                 double hv[CPR], av[CPR];
                 float wm = 0.0f;
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < CPR; ++k) {
                     const float q = qs[j][i16 + 16 * k];
                     w[k] = q * sc[k];
@@ -186,9 +221,9 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                     wm = fmaxf(wm, fabsf(w[k]));
                 }
                 // in-lane tree levels (channel strides D/2 .. 16)
-    #pragma unroll
+#pragma unroll
                 for (int st = CPR / 2; st >= 1; st >>= 1)
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < st; ++k) {
                         cz[k] = cz[k] + cz[k + st];
                         hv[k] = hv[k] + hv[k + st];
@@ -201,7 +236,7 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                 const bool nz = wm > 0.0f;
                 const int e = nz ? (int)((__float_as_uint(wm) >> 23) & 0xFFu) - 127 : 0;
                 int wsum = 0;
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < CPR; ++k) {
                     const int wt = nz ? (int)rintf(ldexpf(w[k], 20 - e)) : 0;
                     wsum += wt;
@@ -210,9 +245,9 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                     const int d1 = (int8_t)r1;
                     const int d2 = (r1 - d1) >> 8;
                     const int c = i16 + 16 * k;
-                    dig[j][0][c] = (int8_t)d0;
-                    dig[j][1][c] = (int8_t)d1;
-                    dig[j][2][c] = (int8_t)d2;
+                    dig[wave][j][0][c] = (int8_t)d0;
+                    dig[wave][j][1][c] = (int8_t)d1;
+                    dig[wave][j][2][c] = (int8_t)d2;
                 }
                 wsum = row_sum_i32(wsum);
                 if (i16 == 0) {
@@ -225,45 +260,44 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
                     double rh = A * 0x1p-23;
                     rh = rh * (double)sm;
                     rh = rh * (1.0 + 0x1p-20);
-                    hd_C[j] = (double)C;
-                    hd_e[j] = e;
-                    hd_W[j] = wsum;
-                    hd_dl[j] = ru32(dl);
-                    hd_rh[j] = ru32(rh);
+                    hd_C[wave][j] = (double)C;
+                    hd_e[wave][j] = e;
+                    hd_W[wave][j] = wsum;
+                    hd_dl[wave][j] = ru32(dl);
+                    hd_rh[wave][j] = ru32(rh);
                 }
             }
         }
-        __syncthreads();
+        wave_sync();
 
         // matrix cores: rows = (head, digit), columns = tokens, k = channels
         const int row = lane % 16, hrow = row / 4, drow = row % 4;
-    #pragma unroll
+#pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int ha = rt * 4 + hrow;  // head of this lane's A row
             v4i a[KS];
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (ha < G)
-                    a[ks] = *reinterpret_cast<const v4i *>(&dig[ha][drow][ks * 64 + (lane / 16) * 16]);
+                    a[ks] = *reinterpret_cast<const v4i *>(&dig[wave][ha][drow][ks * 64 + (lane / 16) * 16]);
                 else
                     a[ks] = v4i{0, 0, 0, 0};
             }
             const int hh = rt * 4 + lane / 16;  // head of this lane's output rows
             float sv[4];
-    #pragma unroll
+#pragma unroll
             for (int tile = 0; tile < 4; ++tile) {
                 v4i acc = {0, 0, 0, 0};
-    #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], bq[tile][ks], acc, 0, 0, 0);
-                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks], bqu[tile][ks], acc, 0, 0, 0);
                 sv[tile] = 0.0f;
                 if (hh < G) {
-                    // S = 2^16 acc2 + 2^8 acc1 + acc0 + 128 W: an integer below 2^53
-                    // in magnitude, formed exactly in FP64
+                    // S = 2^16 acc2 + 2^8 acc1 + acc0 + 128 W: an integer below
+                    // 2^53 in magnitude, formed exactly in FP64
                     const double S = fma((double)acc[2], 65536.0,
-                                         fma((double)acc[1], 256.0, (double)acc[0] + 128.0 * (double)hd_W[hh]));
-                    const double x = hd_C[hh] + ldexp(S, hd_e[hh] - 20);
+                                         fma((double)acc[1], 256.0, (double)acc[0] + 128.0 * (double)hd_W[wave][hh]));
+                    const double x = hd_C[wave][hh] + ldexp(S, hd_e[wave][hh] - 20);
                     sv[tile] = (float)(x * (double)sm);
                     St.score[(size_t)(n * Ly.Hq + g * G + hh) * NS64 + (size_t)slot * 64 + tile * 16 + row] =
                         sv[tile];
@@ -275,36 +309,24 @@ __global__ __launch_bounds__(64) void k_score(Layout Ly, Step St) {
             float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
             mx = row_max_f32(mx);
             float e4[4];
-    #pragma unroll
+#pragma unroll
             for (int tile = 0; tile < 4; ++tile) e4[tile] = exp_c(sv[tile] - mx);
             const float u0 = e4[0] + e4[2], u1 = e4[1] + e4[3];
             const float v = row_tree_f32(u0 + u1);
             if (hh < G && row == 0)
-                St.bstat[(size_t)(n * Ly.Hq + g * G + hh) * St.NS + slot] = make_float4(mx, v, hd_dl[hh], hd_rh[hh]);
+                St.bstat[(size_t)(n * Ly.Hq + g * G + hh) * St.NS + slot] =
+                    make_float4(mx, v, hd_dl[wave][hh], hd_rh[wave][hh]);
         }
     };
-    // full blocks s0 .. f1-1, the next block's operands requested before the
-    // current block is used, on every path (a request made on some paths
-    // only would make the waits before each use drain it); then the
-    // unfinished block, if it is in this range
-    const int f1 = min(s1, N);
-    if (s0 < f1) {
-        int slot = s0;
-        for (; slot + 2 < f1; slot += 2) {
-            issue(slot + 1, bq1, km1);
-            full(slot, bq0, km0);
-            issue(slot + 2, bq0, km0);
-            full(slot + 1, bq1, km1);
-        }
-        if (slot + 1 < f1) {
-            issue(slot + 1, bq1, km1);
-            full(slot, bq0, km0);
-            full(slot + 1, bq1, km1);
-        } else {
-            full(slot, bq0, km0);
-        }
+
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) {
+        const int slot = slot0 + u;
+        if (slot < N)
+            full(slot, bq[u], kmw[u]);
+        else if (slot == N && np)
+            partial(slot);
     }
-    if (s1 > N) partial(N);
 }
 
 // ===========================================================================
@@ -801,12 +823,6 @@ __device__ __forceinline__ void split_pair(float x, float y, uint32_t &hi, uint3
     lo = __builtin_bit_cast(uint32_t, w);
 }
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 constexpr float K16 = 0x1p14f;  // weight scale of FP16 values
 
 template <int D, int G, bool F16ACC>
@@ -989,24 +1005,47 @@ struct VAcc {
     }
 };
 
-// Tier-1 value operands of block `bi` for this lane: INT4 codes (channel-
-// major, 32 bytes per channel; INT8 if V8: 64 bytes per channel) and the
-// scale | offset words of the A rows' groups (group-major, 64 words per
-// group).
+// A lane's share of a block's value scale | offset words: D / 32 words
+// (the block holds 2 D words).
+template <int D>
+using MetaWord = typename std::conditional<D == 128, v4u, uint2>::type;
+
+// Tier-1 value operands of one block for this lane, through buffer
+// resources over the (sequence, kv head)'s blocks (rq: codes, rm: scale |
+// offset words) at block offsets cb, mb (RSRC_OOB: loads zeros from
+// nowhere): INT4 codes (channel-major, 32 bytes per channel; INT8 if V8: 64
+// bytes per channel) and this lane's share of the scale | offset words
+// (group-major, 64 words per group), one load per lane; the words reach the
+// lanes that use them through LDS (vmeta_rows).
 template <int D, int G, bool F, bool V8>
-__device__ __forceinline__ void load_int4(const Layout &Ly, size_t bi, int lane, CodeWord<V8> (&cw)[D / 16],
-                                          v4u (&mt)[VAcc<D, G, F>::RT][4]) {
+__device__ __forceinline__ void load_int4(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rm, uint32_t cb,
+                                          uint32_t mb, int lane, CodeWord<V8> (&cw)[D / 16], MetaWord<D> &mw) {
     using VA = VAcc<D, G, F>;
     constexpr int CB = V8 ? 64 : 32;  // code bytes per channel
-    const uint8_t *vq = Ly.vq + bi * (size_t)(D * CB);
-    const uint32_t *vm = Ly.vmeta + bi * 64 * (D / 32);
 #pragma unroll
-    for (int nt = 0; nt < VA::NT; ++nt)
-        cw[nt] = *reinterpret_cast<const CodeWord<V8> *>(vq + (16 * nt + (lane & 15)) * CB +
-                                                         (CB / 4) * (lane >> 4));
+    for (int nt = 0; nt < VA::NT; ++nt) {
+        const uint32_t off = cb + (uint32_t)((16 * nt + (lane & 15)) * CB + (CB / 4) * (lane >> 4));
+        if constexpr (V8)
+            cw[nt] = rsrc_load16(rq, off);
+        else
+            cw[nt] = rsrc_load8(rq, off);
+    }
+    if constexpr (D == 128) {
+        const uint4 w = rsrc_load16(rm, mb + lane * 16);
+        mw = v4u{w.x, w.y, w.z, w.w};
+    } else {
+        mw = rsrc_load8(rm, mb + lane * 8);
+    }
+}
+
+// The scale | offset words of the A rows' groups for this lane's 16 tokens,
+// from the block's words in LDS (vms: 2 D words).
+template <int D, int G, bool F>
+__device__ __forceinline__ void vmeta_rows(const uint32_t *vms, int lane, v4u (&mt)[VAcc<D, G, F>::RT][4]) {
+    using VA = VAcc<D, G, F>;
 #pragma unroll
     for (int rt = 0; rt < VA::RT; ++rt) {
-        const v4u *src = reinterpret_cast<const v4u *>(vm + VA::agroup(rt, lane) * 64 + 16 * (lane >> 4));
+        const v4u *src = reinterpret_cast<const v4u *>(vms + VA::agroup(rt, lane) * 64 + 16 * (lane >> 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) mt[rt][i] = src[i];
     }
@@ -1021,6 +1060,15 @@ __device__ __forceinline__ void load_fp16v(const uint16_t *vb, int lane, uint4 (
         for (int ks = 0; ks < 2; ++ks)
             vv[nt][ks] = *reinterpret_cast<const uint4 *>(vb + (16 * nt + (lane & 15)) * 64 +
                                                           16 * (lane >> 4) + 8 * ks);
+}
+// The same through a buffer resource at byte offset vb (RSRC_OOB: zeros).
+template <int D>
+__device__ __forceinline__ void load_fp16v(__amdgpu_buffer_rsrc_t r, uint32_t vb, int lane, uint4 (&vv)[D / 16][2]) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            vv[nt][ks] = rsrc_load16(r, vb + (uint32_t)(((16 * nt + (lane & 15)) * 64 + 16 * (lane >> 4) + 8 * ks) * 2));
 }
 
 // Scores of the A rows' heads for this lane's 16 tokens (four 16-byte reads
@@ -1162,6 +1210,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     __shared__ float ksg[VA::NG];
     __shared__ uint32_t sbits[MAX_BPS], sblk[MAX_BPS];
     __shared__ __attribute__((aligned(16))) float st[4][G][64];
+    __shared__ __attribute__((aligned(16))) uint32_t vms[F16 ? 1 : 4][F16 ? 4 : 2 * D];
     const size_t selbase = ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
     // The blocks of this split: an equal share of the pass's block list, over
     // as many splits as the block range [0, nslot) has of bps blocks (the
@@ -1191,22 +1240,24 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     struct Blk {
         uint32_t pm, use;
         int b;
-        bool part;
+        bool part, valid;
     };
     struct Opd {
         uint4 vv[F16 ? VA::NT : 1][2];
         CodeWord<V8> cw[F16 ? 1 : VA::NT];
-        v4u mt[F16 ? 1 : VA::RT][4];
+        MetaWord<D> mw;
         float s[G];  // scores, lane = token
     };
-    // entry i of the split: block, heads of P, heads whose values it serves
+    // entry i of the split: block, heads of P, heads whose values it serves;
+    // past the split's entries: no block (its loads read nothing)
     auto plan = [&](int i) {
         Blk k;
-        k.b = (int)__builtin_amdgcn_readfirstlane(sblk[i]);
-        k.part = F16 && k.b == N;
+        k.valid = i < ne;
+        k.b = k.valid ? (int)__builtin_amdgcn_readfirstlane(sblk[i]) : 0;
+        k.part = F16 && k.valid && k.b == N;
         k.pm = 0;
-        k.use = ALL;
-        if (!k.part) {
+        k.use = k.valid ? ALL : 0u;
+        if (k.valid && !k.part) {
             const uint32_t bits = __builtin_amdgcn_readfirstlane(sbits[i]);
             k.pm = bits & ALL;
             const uint32_t vm = (bits >> 8) & ALL;
@@ -1220,13 +1271,19 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     const uint32_t sbytes = (uint32_t)(G * NS64 * 4);
     const __amdgpu_buffer_rsrc_t rs8 = make_rsrc(St.score + srow, sbytes);
     const __amdgpu_buffer_rsrc_t rs16 = make_rsrc(St.score16 + srow, sbytes);
+    // the block operands of the (sequence, kv head) as buffer resources
+    constexpr uint32_t CBLK = D * (V8 ? 64 : 32), MBLK = 64 * (D / 32) * 4, FBLK = 64 * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Ly.vq + Ly.blk(l, n, g, 0) * CBLK, (uint32_t)Ly.Nmax * CBLK);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(Ly.vmeta + Ly.blk(l, n, g, 0) * (MBLK / 4), (uint32_t)Ly.Nmax * MBLK);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(St.stage_v + selbase * 64 * D, (uint32_t)Ly.Nmax * FBLK);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(Ly.vpart + Ly.seqg(l, n, g) * 64 * D, FBLK);
     auto issue = [&](const Blk &k, Opd &o) {
         const int b = k.b;
         if constexpr (F16)
-            load_fp16v<D>(k.part ? Ly.vpart + Ly.seqg(l, n, g) * 64 * D : St.stage_v + (selbase + b) * 64 * D, lane,
-                          o.vv);
+            load_fp16v<D>(k.part ? rp : rv, !k.valid ? RSRC_OOB : k.part ? 0u : (uint32_t)b * FBLK, lane, o.vv);
         else
-            load_int4<D, G, false, V8>(Ly, Ly.blk(l, n, g, b), lane, o.cw, o.mt);
+            load_int4<D, G, false, V8>(rq, rm, k.valid ? (uint32_t)b * CBLK : RSRC_OOB,
+                                       k.valid ? (uint32_t)b * MBLK : RSRC_OOB, lane, o.cw, o.mw);
         // scores of the group's heads: the FP16-key ones on P (promoted
         // passes), the INT8 ones elsewhere, zero for heads not served here
         // (an offset past the range: no memory access)
@@ -1237,43 +1294,78 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
             o.s[j] = rsrc_load_f32(f16 ? rs16 : rs8, off + lane * 4);
         }
     };
-    auto consume = [&](const Blk &k, Opd &o) {
-        // scores to the A layout through LDS
+    // Softmax weights against a fixed reference per head: the largest INT8
+    // block estimate M^ of the head (the selection's reference).  INT8 scores
+    // are <= M^, FP16-key scores exceed it by at most Delta + rho, so
+    // p = e^(s - M^) neither overflows nor needs rescaling, and the partials
+    // of all splits share the same max.  The sum of the weights accumulates
+    // per lane (token) and is reduced once at the end.
+    float mh[G], lt[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) st[wave][j][lane] = o.s[j];
+    for (int j = 0; j < G; ++j) {
+        mh[j] = St.plan[(size_t)n * Ly.Hq + g * G + j].mref;
+        lt[j] = 0.0f;
+    }
+    auto consume = [&](const Blk &k, Opd &o) {
+        // weights (lane = token) of the heads this block serves, 0 for the
+        // others and past an unfinished block's end; to the A layout
+        // through LDS, with the block's value scales and offsets
+        const bool tok = !k.part || lane < np;
+        wave_sync();  // the wave's previous block has read st and vms
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float e = __builtin_amdgcn_exp2f((o.s[j] - mh[j]) * 1.44269504088896341f);
+            const float w = tok && ((k.use >> j) & 1u) ? e : 0.0f;
+            lt[j] += w;
+            st[wave][j][lane] = w;
+        }
+        if constexpr (!F16) *reinterpret_cast<MetaWord<D> *>(&vms[wave][lane * (D / 32)]) = o.mw;
         wave_sync();
         float sv[VA::RT][16];
         load_scores<D, G, false>(&st[wave][0][0], &st[wave][0][0], 0u, 64, lane, sv);
-        wave_sync();
-        mask_scores<D, G, false>(k.use, k.part ? np : 64, lane, sv);
-        va.softmax(sv, lane);
         if constexpr (F16)
             va.fp16_block(k.use, sv, o.vv, lane);
         else
-            va.template int4_block<V8>(k.use, sv, o.mt, o.cw, ksg, lane);
+        {
+            v4u mt[VA::RT][4];
+            vmeta_rows<D, G, false>(&vms[wave][0], lane, mt);
+            va.template int4_block<V8>(k.use, sv, mt, o.cw, ksg, lane);
+        }
     };
     // entries wave, wave + 4, ...: the next entry's operands in flight
-    // while the current one is used
+    // while the current one is used.  Every path makes the same requests
+    // (entries past the wave's share load zeros from nowhere) and consume
+    // makes none, so the wait before each use covers exactly its block.
+    const int nw = ne > wave ? (ne - wave + 3) / 4 : 0;
     Opd o0, o1;
-    Blk k0{}, k1{};
-    int i = wave;
-    if (i < ne) {
-        k0 = plan(i);
-        issue(k0, o0);
-    }
-    for (; i < ne; i += 8) {
-        const bool more = i + 4 < ne;
-        if (more) {
-            k1 = plan(i + 4);
-            issue(k1, o1);
-        }
+    Blk k0 = plan(wave), k1;
+    issue(k0, o0);
+    for (int t = 0; t < nw; t += 2) {
+        k1 = plan(wave + 4 * (t + 1));
+        issue(k1, o1);
         consume(k0, o0);
-        if (!more) break;
-        if (i + 8 < ne) {
-            k0 = plan(i + 8);
-            issue(k0, o0);
+        k0 = plan(wave + 4 * (t + 2));
+        issue(k0, o0);
+        if (t + 1 < nw) consume(k1, o1);
+    }
+    // the fixed max and the weight sums of the A rows' heads, for the
+    // partials (row h of the first tile lies in lane h)
+    {
+        float L[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) L[j] = wave_sum_dpp(lt[j]);
+#pragma unroll
+        for (int rt = 0; rt < VA::RT; ++rt) {
+            const int h = VA::ahead(rt, lane);
+            float m = mh[0], l_ = L[0];
+#pragma unroll
+            for (int j = 1; j < G; ++j) {
+                m = h == j ? mh[j] : m;
+                l_ = h == j ? L[j] : l_;
+            }
+            va.mrow[rt] = m;
+            va.lrow[rt] = l_;
         }
-        consume(k1, o1);
     }
     float *part = MODE == VP_TAIL ? St.part_tail : MODE == VP_INT4 ? St.part_blk : St.part_blk16;
     write_partials<D, G, false>(va, ksg, part, (size_t)n * Ly.Hq + g * G, St.nsplit_cap, sp, ALL, !F16);
@@ -2048,7 +2140,9 @@ __global__ __launch_bounds__(64) void k_merge_dense(DenseSrc S) {
 hipError_t launch_score(const Layout &Ly, const Step &St, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         hipLaunchKernelGGL((k_score<decltype(D)::value, decltype(G)::value>),
-                           dim3((St.nb + 1 + St.spw - 1) / St.spw, Ly.Hkv, St.batch), dim3(64), 0, s, Ly, St);
+                           dim3((St.nb + 1 + SCORE_W * SCORE_BPW_ - 1) / (SCORE_W * SCORE_BPW_), Ly.Hkv, St.batch),
+                           dim3(64 * SCORE_W), 0, s,
+                           Ly, St);
         return hipGetLastError();
     });
 }

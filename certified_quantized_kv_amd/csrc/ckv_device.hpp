@@ -111,6 +111,13 @@ __device__ __forceinline__ double fx_bound(uint64_t sum, bool sat) {
     return (double)sum * 0x1p-32 * (1.0 + 0x1p-50);
 }
 
+// LDS writes of the wave's lanes visible to the wave's other lanes.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---- wave reductions (wave64) ---------------------------------------------
 
 // Halving-tree sum: lane i adds lane i + stride for stride 32..1; the result
@@ -159,6 +166,11 @@ __device__ __forceinline__ float rsrc_load_f32(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 rsrc_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef uint32_t v2u32_ __attribute__((ext_vector_type(2)));
+    const v2u32_ v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v.x, v.y);
 }
 
 // ---- DPP row operations (16-lane rows of a wave64) --------------------------

@@ -75,7 +75,6 @@ struct Step {
     int layer, batch, nb;   // nb: max full blocks over the batch
     int NS;                 // slot stride
     int nsplit, bps;        // tail splits per (seq, kv head), blocks per split
-    int spw;                // block slots per wave of the scoring pass
     int ncu;                // compute units of the device
     float sm;
     const uint16_t *q;      // [batch][Hq][d]
