@@ -13,8 +13,9 @@ Prints one JSON line.  `value` = KV tokens (batch x context) per second per
 layer-step of the first workload (the 32K x 4 LLaMA-3.1-8B-shaped layer by
 default); the 128K workload's figures are in `other_workloads`.  `roofline`
 is measured for the dominant kernel (largest time per step among the passes
-whose algorithmic bytes are defined) with HIP events recorded by the library
-on the stream that kernel runs on.
+whose algorithmic bytes are defined); each kernel's launch duration is its
+own execution span (first wave's start to last wave's end), stamped by the
+kernel on the device's constant-rate wall clock while the timed steps run.
 """
 import argparse
 import json
@@ -38,8 +39,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", default="llama_32k,needle_128k",
-                    help="comma-separated workloads; the first one is the reported value")
+    ap.add_argument("--workload", default="llama_32k,needle_128k,llama_8k,needle_64k,stress_32k",
+                    help="comma-separated workloads; the first one is the reported value, the "
+                         "comparison lines (--no-extras) run on the first two")
     ap.add_argument("--layers", type=int, default=0, help="layers to build (0: the workload's)")
     ap.add_argument("--decode-steps", type=int, default=4,
                     help="decode-loop steps after the timed region, first workload only: one token "
@@ -81,7 +83,24 @@ def counters_for(kernel, workload):
     return rec.get("traffic_bytes_per_dispatch")
 
 
-def run_workload(name, args, cpu_baseline, decode_steps=0):
+def cpu_info():
+    """Host CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def run_workload(name, args, cpu_baseline, decode_steps=0, extras=False):
     import numpy as np
     import torch
 
@@ -102,7 +121,7 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
     log(f"cache created in {time.time() - t0:.1f}s: device {fp['device'] / 2**30:.2f} GiB "
         f"(tier 1 {fp['tier1'] / 2**30:.2f} GiB), pinned host {fp['host'] / 2**30:.2f} GiB")
     qs = []
-    n_dense = 0 if args.no_dense else min(L, 4)
+    n_dense = 0 if (args.no_dense or not extras) else min(L, 4)
     dense_kv = []
     sample = None
     for l in range(L):
@@ -128,14 +147,19 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # timed region: K layer-steps; the library records HIP events per pass
+    # timed region: K layer-steps; with profiling on, each timed kernel
+    # stamps its execution span on the device clock; every call returns
+    # after its report is on the host, so the host clock times each step
     cache.set_profiling(True)
     reps = []
+    step_s = []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         l = (args.warmup + i) % L
+        t_i = time.perf_counter()
         _, rep = cache.certified_decode_attention(l, qs[l], th, out=out)
+        step_s.append(time.perf_counter() - t_i)
         reps.append(rep)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
@@ -197,8 +221,10 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
         k13_rec = None
     tier1_step = prof["q8_blocks"] * q8_blk / K + B * T * Hkv * (d / 2 + 4 * d / 32 + 4 / 64)
     paged_step = prof["bytes_paged"] / K
+    st_ms = np.sort(np.array(step_s)) * 1e3
     rec = {
         "ms_per_step": round(ms_step, 4), "value": round(value, 1),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(st_ms, q)), 4) for q in (10, 50, 90)],
         "roofline": roofline, "kernels": table, "score_and_tail_hbm": k13_rec,
         "hbm_algorithmic_GBps_end_to_end": round((tier1_step + paged_step) / (elapsed / K) / 1e9, 1),
         "paged_MiB_per_step": round(paged_step / 2 ** 20, 2),
@@ -216,23 +242,34 @@ def run_workload(name, args, cpu_baseline, decode_steps=0):
                    if args.staged_threads != 0 else "runs"},
     }
 
-    if not args.no_extras:
+    if extras:
         extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
                     ms_step, decode_steps)
     cache.close()
     del dense_kv
 
     if sample is not None:
+        # the CPU oracle on one sequence of layer 0 (a full layer-step of that
+        # sequence: every head, scoring through outputs), on one thread and on
+        # every core this process may use (its heads run on OpenMP threads)
         import oracle
         k1, v1, q1, sm1 = sample
-        t1 = time.perf_counter()
-        oracle.certified_decode(k1, v1, q1, oracle.default_thresholds(sm1), trace=False)
-        cs = time.perf_counter() - t1
+        model, ncpu, usable = cpu_info()
+        runs = {}
+        for thr in (1, usable):
+            oracle.set_threads(thr)
+            t1 = time.perf_counter()
+            oracle.certified_decode(k1, v1, q1, oracle.default_thresholds(sm1), trace=False)
+            runs[thr] = time.perf_counter() - t1
+            log(f"cpu baseline: {runs[thr]:.2f}s for the sample on {thr} thread(s)")
+        oracle.set_threads(usable)
         rec["cpu_baseline"] = {
-            "value": round(T / cs, 1), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "value": round(T / runs[1], 1), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{name} layer 0, sequence 0 of {B}: one full layer-step of one sequence "
-                      f"({T} tokens, {Hq} q heads), {cs:.1f} s single-threaded"}
-        log(f"cpu baseline: {cs:.1f}s for the sample")
+                      f"({T} tokens, {Hq} q heads), {runs[1]:.1f} s on one thread",
+            "all_cores": {"value": round(T / runs[usable], 1), "cores": usable,
+                          "seconds": round(runs[usable], 2)},
+            "cpu_model": model, "nproc": ncpu, "usable_cores": usable}
     return rec
 
 
@@ -493,7 +530,8 @@ def main():
 
     names = [w for w in args.workload.split(",") if w]
     recs = [run_workload(w, args, cpu_baseline=(i == 0 and not args.no_cpu_baseline),
-                         decode_steps=(args.decode_steps if i == 0 else 0))
+                         decode_steps=(args.decode_steps if i == 0 and not args.no_extras else 0),
+                         extras=(i < 2 and not args.no_extras))
             for i, w in enumerate(names)]
     first = recs[0]
     # achievable HBM rate of a plain streaming kernel (torch's elementwise
@@ -512,11 +550,27 @@ def main():
     cms = 1e3 * (time.perf_counter() - t1) / 10
     copy_probe = {"bytes_read": 2 ** 30, "bytes_written": 2 ** 30, "ms": round(cms, 4),
                   "GBps": round(2 * 2 ** 30 / (cms * 1e-3) / 1e9, 1)}
+    # a read-only pass over the same 1 GiB (torch's sum: every byte read once,
+    # one value written): the calibration kernel of the FETCH_SIZE counter
+    # (its rate is that of torch's reduction, not a ceiling for reads)
+    for _ in range(3):
+        a.sum()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(10):
+        a.sum()
+    torch.cuda.synchronize()
+    rms = 1e3 * (time.perf_counter() - t1) / 10
+    read_probe = {"bytes_read": 2 ** 30, "ms": round(rms, 4), "GBps": round(2 ** 30 / (rms * 1e-3) / 1e9, 1)}
     del a, b
     line = {
         "metric": METRIC, "value": first["value"], "unit": "KV tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": first["ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        # the path's arithmetic: INT8 scores on the int8 matrix cores, FP16-key
+        # scores as FP64 chains, values on the f16 matrix cores, softmax and
+        # outputs in FP32, bounds in FP64
+        "dtype": "i8/f16/f32/f64",
         "data": "synthetic",
         "config": first["config"],
         "roofline": first["roofline"],
@@ -531,6 +585,7 @@ def main():
     line["pcie_h2d_GBps"] = h2d["GBps_256MiB"]
     line["pcie_h2d"] = h2d
     line["copy_probe"] = copy_probe
+    line["read_probe"] = read_probe
     print(json.dumps(line), flush=True)
 
 

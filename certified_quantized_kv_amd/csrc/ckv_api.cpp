@@ -64,6 +64,7 @@ namespace {
     } while (0)
 
 enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO4, PH_FALLBACK, PH_STEP, PH_MERGE, PH_KEYS, PH_PROMO16, PH_N = 10 };
+enum { KEV_SCORE, KEV_SELECT, KEV_TAIL, KEV_KEYS, KEV_PROMO4, KEV_PROMO16, KEV_RANK, KEV_MERGE, KEV_N };
 
 }  // namespace
 
@@ -229,6 +230,14 @@ struct ckv_cache {
     hipEvent_t ev_side[NSIDE] = {}, ev_kside[NSIDE] = {};
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
     hipEvent_t pev[15] = {};
+    // profiling: the execution span of each timed kernel (scoring,
+    // selection, tail, FP16 keys, INT4 promoted, FP16 promoted, rank check,
+    // merge) stamped by the kernel itself on the device's constant-rate
+    // clock: KEV_N x CLK_WORDS (CLK_SLOTS start slots, then CLK_SLOTS end
+    // slots, CLK_PAD words apart), reset from h_clk_init before each
+    // profiled step and read back into h_clk
+    unsigned long long *dclk = nullptr, *h_clk = nullptr, *h_clk_init = nullptr;
+    double clk_khz = 0.0;
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
     // persistent FP16 mirror of layers 0 .. pcache_layers-1: blocks paged in
     // once stay in HBM across steps (complete blocks never change)
@@ -339,7 +348,8 @@ void ckv_destroy(ckv_cache *c) {
     for (void *p : {(void *)c->ain_k, (void *)c->ain_v, (void *)c->pk, (void *)c->pv})
         if (p) (void)hipFree(p);
     for (void *p : {(void *)c->t2k, (void *)c->t2v, (void *)c->h_sel, (void *)c->h_mask,
-                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len})
+                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_clk,
+                    (void *)c->h_clk_init})
         if (p) (void)hipHostFree(p);
     for (hipStream_t st : c->side)
         if (st) (void)hipStreamDestroy(st);
@@ -475,6 +485,18 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     HIPCHK(hipEventCreateWithFlags(&c->ev_paged, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming));
     for (auto &e : c->pev) HIPCHK(hipEventCreate(&e));
+    {
+        const size_t nclk = (size_t)KEV_N * CLK_WORDS;
+        CTRY(dalloc(c, &c->dclk, nclk));
+        CTRY(halloc(c, &c->h_clk, nclk));
+        CTRY(halloc(c, &c->h_clk_init, nclk));
+        // start slots at the largest value, end slots (and the padding) at 0
+        for (size_t i = 0; i < nclk; ++i)
+            c->h_clk_init[i] = (i % CLK_WORDS) < (size_t)CLK_SLOTS * CLK_PAD ? ~0ull : 0ull;
+        int khz = 0;
+        HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device));
+        c->clk_khz = khz;
+    }
     {
         // staged paging on by default; four packing threads keep up with the
         // host link (each packs at ~25 GB/s)
@@ -1038,12 +1060,16 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
 
     hipEvent_t *E = c->pev;
     const bool prof = c->prof;
-    if (prof) HIPCHK(hipEventRecord(E[0], s));
+    const size_t clk_bytes = sizeof(unsigned long long) * KEV_N * CLK_WORDS;
+    if (prof) HIPCHK(hipMemcpyAsync(c->dclk, c->h_clk_init, clk_bytes, hipMemcpyHostToDevice, s));
+    // the next kernel launched with St stamps its span in slot k (profiling)
+    auto kev = [&](int k) { St.clk = prof ? c->dclk + (size_t)k * CLK_WORDS : nullptr; };
     // K1: INT8 scoring pass; K2: selection, bounds, rungs 1-2
+    kev(KEV_SCORE);
     HIPCHK(launch_score(Ly, St, s));
-    if (prof) HIPCHK(hipEventRecord(E[1], s));
+    kev(KEV_SELECT);
     HIPCHK(launch_select(Ly, St, T, s));
-    if (prof) HIPCHK(hipEventRecord(E[2], s));
+    St.clk = nullptr;
     // page lists and plans to the host (the round trip of the selection)
     const size_t selbytes = (size_t)batch * Hkv * Ly.Nmax * sizeof(uint32_t);
     HIPCHK(hipMemcpyAsync(c->h_sel, c->sel, selbytes, hipMemcpyDeviceToHost, s));
@@ -1053,9 +1079,9 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     // host's page lists and the paging below
     HIPCHK(launch_worklist(Ly, St, s));
     HIPCHK(hipEventRecord(c->ev_wl, s));
-    if (prof) HIPCHK(hipEventRecord(E[3], s));
+    kev(KEV_TAIL);
     if (St.nsplit > 0) HIPCHK(launch_tail(Ly, St, s));
-    if (prof) HIPCHK(hipEventRecord(E[4], s));
+    St.clk = nullptr;
     HIPCHK(hipEventSynchronize(c->ev_sel));
 
     // rung 4 before paging: a cap exhausted on any head of the sequence
@@ -1136,21 +1162,22 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     if (prof) HIPCHK(hipEventRecord(E[6], c->side[0]));
     HIPCHK(hipEventRecord(c->ev_paged, c->side[0]));
     // K4: promoted blocks, rank check, merge
-    if (prof) HIPCHK(hipEventRecord(E[7], s));
+    kev(KEV_KEYS);
     HIPCHK(launch_keys16(Ly, St, c->dskip, s));
-    if (prof) HIPCHK(hipEventRecord(E[12], s));
+    kev(KEV_PROMO4);
     HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
-    if (prof) HIPCHK(hipEventRecord(E[13], s));
     // the rank check needs only the FP16-key pass: it runs while the FP16
     // values are still being paged
+    kev(KEV_RANK);
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 1, s));
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
-    if (prof) HIPCHK(hipEventRecord(E[14], s));
+    kev(KEV_PROMO16);
     HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
-    if (prof) HIPCHK(hipEventRecord(E[11], s));
+    kev(KEV_MERGE);
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 2, s));
-    if (prof) HIPCHK(hipEventRecord(E[8], s));
+    St.clk = nullptr;
     HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
+    if (prof) HIPCHK(hipMemcpyAsync(c->h_clk, c->dclk, clk_bytes, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(c->ev_done, s));
     HIPCHK(hipEventSynchronize(c->ev_done));
 
@@ -1272,14 +1299,34 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
             c->pf.counts[ph] += 1;
             return CKV_OK;
         };
-        TRY(acc(PH_SCORE, 0, 1));
-        TRY(acc(PH_SELECT, 1, 2));
-        if (St.nsplit > 0) TRY(acc(PH_TAIL, 3, 4));
+        // kernel phases: each kernel's own execution span, first wave's
+        // start to last wave's end (the tail, FP16-key and INT4 promoted
+        // passes launch only when the batch has a full block)
+        auto kacc = [&](int ph, int k) -> ckv_status {
+            const unsigned long long *w = c->h_clk + (size_t)k * CLK_WORDS;
+            unsigned long long t0 = ~0ull, t1 = 0;
+            for (int i = 0; i < CLK_SLOTS; ++i) {
+                t0 = std::min(t0, w[(size_t)i * CLK_PAD]);
+                t1 = std::max(t1, w[(size_t)(CLK_SLOTS + i) * CLK_PAD]);
+            }
+            if (t0 == ~0ull || t1 < t0 || !(c->clk_khz > 0.0))
+                return fail(CKV_EHIP, "kernel clock of a profiled kernel not stamped");
+            c->pf.ms[ph] += (double)(t1 - t0) / c->clk_khz;
+            c->pf.counts[ph] += 1;
+            return CKV_OK;
+        };
+        TRY(kacc(PH_SCORE, KEV_SCORE));
+        TRY(kacc(PH_SELECT, KEV_SELECT));
+        if (nb > 0) {
+            TRY(kacc(PH_TAIL, KEV_TAIL));
+            TRY(kacc(PH_KEYS, KEV_KEYS));
+            TRY(kacc(PH_PROMO4, KEV_PROMO4));
+        }
         TRY(acc(PH_PAGE, 5, 6));
-        TRY(acc(PH_KEYS, 7, 12));
-        TRY(acc(PH_PROMO4, 12, 13));
-        TRY(acc(PH_PROMO16, 14, 11));
-        TRY(acc(PH_MERGE, 11, 8));
+        TRY(kacc(PH_PROMO16, KEV_PROMO16));
+        TRY(kacc(PH_MERGE, KEV_RANK));
+        TRY(kacc(PH_MERGE, KEV_MERGE));
+        c->pf.counts[PH_MERGE] -= 1;  // one merge phase per step, two launches
         if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
         c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
         c->pf.counts[PH_STEP] += 1;

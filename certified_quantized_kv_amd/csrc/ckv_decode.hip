@@ -70,6 +70,7 @@ constexpr int SCORE_BPW_ = SCORE_BPW;  // block slots per wave
 
 template <int D, int G>
 __global__ __launch_bounds__(64 * SCORE_W) void k_score(Layout Ly, Step St) {
+    KernelClock kc(St.clk);
     constexpr int CPL = D / 64;           // channels per lane (meta, trees)
     constexpr int KS = D / 64;            // MFMA k-steps of 64 channels
     constexpr int RT = (4 * G + 15) / 16; // MFMA row tiles of 4 heads x 4 digits
@@ -567,6 +568,7 @@ __device__ __forceinline__ bool in_set(P val, int b, uint64_t thr) {
 
 template <int D, int G>
 __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
+    KernelClock kc(St.clk);
     __shared__ SelShared sh;
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int g = h / G, j = h % G, l = St.layer;
@@ -1374,16 +1376,19 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
 // Three waves per SIMD where the registers allow (INT4 codes, G d <= 512).
 template <int D, int G, bool V8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(!V8 && G * D <= 512 ? 3 : 2))) void k_tail(Layout Ly, Step St) {
+    KernelClock kc(St.clk);
     values_pass<D, G, VP_TAIL, V8>(Ly, St, nullptr);
 }
 
 template <int D, int G, bool V8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(!V8 && G * D <= 512 ? 3 : 2))) void k_promoted4(Layout Ly, Step St, const int *skip_seq) {
+    KernelClock kc(St.clk);
     values_pass<D, G, VP_INT4, V8>(Ly, St, skip_seq);
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_promoted16(Layout Ly, Step St, const int *skip_seq) {
+    KernelClock kc(St.clk);
     values_pass<D, G, VP_FP16, false>(Ly, St, skip_seq);
 }
 
@@ -1452,6 +1457,7 @@ __device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int 
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
                                                 const double *qd) {
+    KernelClock kc(St.clk);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     constexpr uint32_t ALL = (1u << G) - 1u;
     __shared__ uint32_t sbits[KEYS_MAXE], sblk[KEYS_MAXE];
@@ -1821,6 +1827,7 @@ template <int D, int G>
 // while the FP16 values are still being paged), bit 1 the merge.
 __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, const int *skip_seq,
                                                    uint32_t *plist_g, uint64_t *keys_g, int part) {
+    KernelClock kc(St.clk);
     constexpr int CPL = D / 64;
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;

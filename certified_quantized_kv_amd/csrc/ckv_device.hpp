@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ckv_internal.hpp"
+
 namespace ckv {
 
 constexpr int BT = 64;       // tokens per block
@@ -117,6 +119,36 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Execution span of one kernel launch, for profiling.  With a non-null
+// clk, every wave reads the device's constant-rate wall clock when it starts
+// and again when it ends; wave 0 of each workgroup takes the minimum of its
+// start time into start slot w % CLK_SLOTS and every wave the maximum of its
+// end time into the matching end slot (w = the linear workgroup index), so
+// max(end) - min(start) over the slots is the span from the first wave's
+// start to the last wave's end.  Both atomics are issued at the end, after
+// the wave's last load: an atomic issued first would hold the wave's first
+// load wait until it completed (memory counters retire in order).  The end
+// is stamped when the object goes out of scope, so early returns are
+// covered.  Spreading over slots on separate lines keeps the atomics from
+// queueing on one line.
+struct KernelClock {
+    unsigned long long *clk;
+    unsigned long long t0;
+    __device__ __forceinline__ explicit KernelClock(unsigned long long *c) : clk(c), t0(0) {
+        if (clk) t0 = (unsigned long long)wall_clock64();
+    }
+    __device__ __forceinline__ ~KernelClock() {
+        if (clk && (threadIdx.x & 63) == 0) {
+            const unsigned long long t1 = (unsigned long long)wall_clock64();
+            const int slot = (int)((blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) % CLK_SLOTS);
+            if (threadIdx.x == 0) atomicMin(clk + slot * CLK_PAD, t0);
+            atomicMax(clk + (CLK_SLOTS + slot) * CLK_PAD, t1);
+        }
+    }
+    KernelClock(const KernelClock &) = delete;
+    KernelClock &operator=(const KernelClock &) = delete;
+};
 
 // ---- wave reductions (wave64) ---------------------------------------------
 

@@ -102,6 +102,10 @@ struct Step {
     uint32_t *wl;
     int *wcnt;
     float *out;             // [batch][Hq][d]
+    // profiling: when not null, the kernel launched with this step stamps
+    // its execution span here (KernelClock: CLK_SLOTS start slots, then
+    // CLK_SLOTS end slots, in ticks of the device's constant-rate clock)
+    unsigned long long *clk;
 };
 enum { WL_KEYS = 0, WL_INT4 = 1, WL_FP16 = 2, WL_TAIL = 3, WL_KINDS = 4 };
 
@@ -133,6 +137,13 @@ struct Th {
 int split_blocks(int nb, int Hkv, int batch);
 // The calling thread's last-error message (ckv_api.cpp); returns st.
 int set_error(int st, const char *msg);
+
+// Spread slots of the kernel clock: workgroup w stamps slot w % CLK_SLOTS;
+// a slot is one word at the start of its own 128-byte line (CLK_PAD words),
+// since atomics on one line are serialized where they are performed.
+constexpr int CLK_SLOTS = 64;
+constexpr int CLK_PAD = 16;
+constexpr int CLK_WORDS = 2 * CLK_SLOTS * CLK_PAD;  // per timed kernel: starts, then ends
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 // header bytes of a staged-paging chunk: up to 512 block addresses

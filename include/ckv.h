@@ -150,7 +150,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                                           ckv_head_report *report, void *stream);
 
 /* Exact dense decode attention over caller-provided device FP16 K/V, the
- * "fast dense path" the certified step is compared with [Results].
+ * fast dense baseline the certified step is measured against [Results].
  * k, v: device binary16 in the block layout
  *   [batch][n_kv_heads][n_tokens/64][64 * head_dim], where a K block is
  *   [head_dim/8][64 tokens][8 channels] and a V block [head_dim][64 tokens];
@@ -276,15 +276,18 @@ ckv_status ckv_set_device_paging(ckv_cache *c, int enable);
 ckv_status ckv_set_staged_paging(ckv_cache *c, int threads);
 
 /* Profile of the decode steps since profiling was enabled (enabling resets
- * it).  Phase times are measured with HIP events on the streams the work
- * runs on: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
+ * it).  Phases: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
  * 3 page-in (the host-to-device copies on the paging streams), 4 promoted
  * value pass over INT4 values (K4a), 5 fallback (paging + dense recompute),
- * 6 the whole step on the host wall clock, 7 rank check + merge (K4b),
- * 8 FP16-key scoring of the promoted blocks (K4a keys), 9 promoted value
- * pass over FP16 values (K4a).  Block counts are what the passes read,
- * summed over steps: a block is one (sequence, kv head, 64 tokens).
- * Profiling adds a few event records per step. */
+ * 6 the whole step on the host wall clock, 7 rank check + merge (K4b, two
+ * launches), 8 FP16-key scoring of the promoted blocks (K4a keys),
+ * 9 promoted value pass over FP16 values (K4a).  The kernel phases (0, 1,
+ * 2, 4, 7, 8, 9) are each kernel's own execution span, its first wave's
+ * start to its last wave's end on the device's constant-rate wall clock,
+ * stamped by the kernel (a few atomics per workgroup); phases 3 and 5 are
+ * timed with HIP events on the streams they run on.  Block counts are what
+ * the passes read, summed over steps: a block is one (sequence, kv head,
+ * 64 tokens).  Profiling adds two small copies per step. */
 typedef struct {
     double ms[10];          /* accumulated milliseconds per phase            */
     int counts[10];         /* timed occurrences per phase                   */
