@@ -1164,12 +1164,13 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     // K4: promoted blocks, rank check, merge
     kev(KEV_KEYS);
     HIPCHK(launch_keys16(Ly, St, c->dskip, s));
-    kev(KEV_PROMO4);
-    HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
     // the rank check needs only the FP16-key pass: it runs while the FP16
-    // values are still being paged
+    // values are still being paged, and sets the promoted passes' softmax
+    // reference
     kev(KEV_RANK);
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 1, s));
+    kev(KEV_PROMO4);
+    HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
     kev(KEV_PROMO16);
     HIPCHK(launch_promoted16(Ly, St, c->dskip, s));

@@ -742,6 +742,7 @@ __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
             P.eval = eval;
             P.tau = tau;
             P.mref = mref;
+            P.mref16 = mref;
             P.kstar = kst;
             P.nvp = nvp;
             P.flags = widened | (cap_fail << 1);
@@ -1296,16 +1297,20 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
             o.s[j] = rsrc_load_f32(f16 ? rs16 : rs8, off + lane * 4);
         }
     };
-    // Softmax weights against a fixed reference per head: the largest INT8
-    // block estimate M^ of the head (the selection's reference).  INT8 scores
-    // are <= M^, FP16-key scores exceed it by at most Delta + rho, so
-    // p = e^(s - M^) neither overflows nor needs rescaling, and the partials
-    // of all splits share the same max.  The sum of the weights accumulates
-    // per lane (token) and is reduced once at the end.
+    // Softmax weights against a fixed reference per head, at least every
+    // score the pass uses: the largest INT8 block estimate M^ (INT8 scores,
+    // and the unfinished block's FP16 scores, are <= M^) for the tail; for
+    // the promoted passes also the largest FP16-key block max over P (from
+    // the rank check).  So p = e^(s - m) <= 1: the weights never overflow
+    // (the weight scales of the matrix-core operands assume p <= 1) and
+    // need no rescaling.  The merge rescales partials of different m.  The
+    // sum of the weights accumulates per lane (token) and is reduced once
+    // at the end.
     float mh[G], lt[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        mh[j] = St.plan[(size_t)n * Ly.Hq + g * G + j].mref;
+        const HeadPlan &P = St.plan[(size_t)n * Ly.Hq + g * G + j];
+        mh[j] = MODE == VP_TAIL ? P.mref : P.mref16;
         lt[j] = 0.0f;
     }
     auto consume = [&](const Blk &k, Opd &o) {
@@ -1895,10 +1900,12 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     // Kendall discordant pairs; the LDS path names the shared arrays
     // directly (LDS instructions, not generic addresses)
     long long D_ = 0;
+    float mrP = -INFINITY;  // largest FP16-key block max over P
     if (use_lds) {
         float mr = -INFINITY;
         for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[lds_list[i]].x);
         mr = block_max(mr);
+        mrP = mr;
         for (int i = tid; i < K; i += MERGE_T) keys(lds_list[i], (uint32_t)i, mr, lds_kI[i], lds_k16[i]);
         __syncthreads();
         if (K <= RANK_PAIRS) {
@@ -1926,6 +1933,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         float mr = -INFINITY;
         for (int i = tid; i < K; i += MERGE_T) mr = fmaxf(mr, st16[plist[i]].x);
         mr = block_max(mr);
+        mrP = mr;
         for (int i = tid; i < K; i += MERGE_T) keys(plist[i], plist[i], mr, kI[i], k16[i]);
         __syncthreads();
         // rows i and K-1-i go to the same thread (equal work per thread)
@@ -1949,6 +1957,8 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
         const double lim = floor((double)th.rank_tol * pairs);
         St.plan[hs].rank_ok = !((double)Dt > lim);
         St.plan[hs].ndisc = (int)Dt;
+        // the softmax reference of the promoted value passes
+        St.plan[hs].mref16 = fmaxf(St.plan[hs].mref, mrP);
     }
     }  // rank check
     if (!(part & 2)) return;

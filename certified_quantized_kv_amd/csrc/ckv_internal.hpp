@@ -62,7 +62,8 @@ __host__ __device__ inline float ord2f(uint32_t u) {
 // completed by the rank-check kernel.
 struct HeadPlan {
     double mu, tv, ekey, eval, tau;
-    float mref;
+    float mref;    // largest INT8 block estimate M^ (the selection's reference)
+    float mref16;  // max(M^, largest FP16-key block max over P): rank check
     int kstar, nvp, flags;  // flags: bit0 widened, bit1 a cap was exhausted
     int rank_ok, ndisc;
     uint64_t S;

@@ -206,6 +206,47 @@ def test_symmetric_cache_head_shapes(shape, kind):
     both(k, v, q, oracle.default_thresholds(sm), v_bits=8)
 
 
+def planted_excess(seed, A=96.0, T=512 + 17, d=64, Hq=2):
+    """A layer where a P block's FP16-key scores exceed the largest INT8
+    block estimate M^ by more than ln 4: one token of block 3 has every
+    channel 0.4 of a quantization step past a rounding point, against the
+    sign of q_c, so its INT8 score is low by about 0.8 Delta (Delta ~ 2
+    with keys spanning [-A, A] in every channel of the block) while it is
+    the largest exact score.  Both q heads are equal."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, Hq, d))
+    q[0, 1:] = q[0, 0]
+    k = rng.uniform(-0.5, 0.5, (1, T, 1, d)) * A
+    v = rng.standard_normal((1, T, 1, d))
+    blk = k[0, 3 * 64:4 * 64, 0]
+    blk[0], blk[1] = -A, A
+    s = 2 * A / 255
+    sg = np.sign(q[0, 0])
+    blk[21] = -A + (np.where(sg > 0, 230, 25) + np.where(sg > 0, 0.4, -0.4)) * s
+    return f16(k), f16(v), f16(q), float(1 / np.sqrt(d))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("v_tol", [float("inf"), 0.0])
+def test_promoted_weights_when_fp16_key_scores_exceed_the_estimate(seed, v_tol):
+    """The promoted value passes weigh FP16-key scores, which may exceed
+    M^ by up to Delta + rho; their softmax reference must cover that
+    (weights above 4 would overflow the FP16 operands of the value
+    contraction).  INT4 values (v_tol = inf) and FP16 values (v_tol = 0);
+    the rank check never fails (rank_tol = 1), so the promoted passes give
+    the output."""
+    k, v, q, sm = planted_excess(seed)
+    th = oracle.default_thresholds(sm, k_tol=float("inf"), v_tol=v_tol, rank_tol=1.0)
+    res, rep = both(k, v, q, th)
+    tr = res.trace
+    N = k.shape[1] // 64
+    for h in range(q.shape[1]):
+        inP = (tr["sel"][0, h] & 1).astype(bool)
+        s16 = tr["score16"][0, h, :N * 64].reshape(N, 64)[inP]
+        assert s16.max() - tr["mref"][0, h] > np.log(4.0) + 0.05
+        assert rep[0, h]["rung_max"] == (2 if v_tol == 0.0 else 0)
+
+
 def test_single_token_and_single_block():
     for T in [1, 63, 64, 65]:
         k, v, q, sm = micro(T, T=T, Hq=8, Hkv=2, d=128)
