@@ -299,7 +299,12 @@ def extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B
     rec["device_paging"] = {"steps": Kd, "ms_per_step": round(1e3 * eld / Kd, 4),
                             "value": round(B * T * Kd / eld, 1),
                             "paged_MiB_per_step": round(profd["bytes_paged"] / Kd / 2 ** 20, 2),
-                            "page_ms_per_step": round(profd["phases"]["page"][0] / Kd, 4)}
+                            "page_ms_per_step": round(profd["phases"]["page"][0] / Kd, 4),
+                            # the K gather's first wave after the selection
+                            # kernel's last wave, on the device clock: the
+                            # paging starts without the host's round trip
+                            "gather_start_after_select_us": round(
+                                1e3 * profd["gather_lead_ms"] / max(profd["gather_steps"], 1), 2)}
     log(f"device paging: {1e3 * eld / Kd:.3f} ms/step")
 
     # the same layer-steps with the listed blocks copied as runs (one copy

@@ -45,7 +45,8 @@ class Profile(ctypes.Structure):
                 ("bytes_paged", ctypes.c_uint64), ("copies", ctypes.c_uint64),
                 ("q8_blocks", ctypes.c_uint64), ("tail_blocks", ctypes.c_uint64),
                 ("k16_blocks", ctypes.c_uint64), ("v16_blocks", ctypes.c_uint64),
-                ("int4p_blocks", ctypes.c_uint64), ("dense_blocks", ctypes.c_uint64)]
+                ("int4p_blocks", ctypes.c_uint64), ("dense_blocks", ctypes.c_uint64),
+                ("gather_lead_ms", ctypes.c_double), ("gather_steps", ctypes.c_int)]
 
 
 PHASES = ["score", "select", "tail", "page", "promoted4", "fallback", "step", "merge", "keys16", "promoted16"]

@@ -64,7 +64,7 @@ namespace {
     } while (0)
 
 enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO4, PH_FALLBACK, PH_STEP, PH_MERGE, PH_KEYS, PH_PROMO16, PH_N = 10 };
-enum { KEV_SCORE, KEV_SELECT, KEV_TAIL, KEV_KEYS, KEV_PROMO4, KEV_PROMO16, KEV_RANK, KEV_MERGE, KEV_N };
+enum { KEV_SCORE, KEV_SELECT, KEV_TAIL, KEV_KEYS, KEV_PROMO4, KEV_PROMO16, KEV_RANK, KEV_MERGE, KEV_GATHER, KEV_N };
 
 }  // namespace
 
@@ -228,11 +228,11 @@ struct ckv_cache {
     // the per-copy latency of one stream overlaps the others'
     hipStream_t side[NSIDE] = {};
     hipEvent_t ev_side[NSIDE] = {}, ev_kside[NSIDE] = {};
-    hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
+    hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr, ev_selk = nullptr;
     hipEvent_t pev[15] = {};
     // profiling: the execution span of each timed kernel (scoring,
     // selection, tail, FP16 keys, INT4 promoted, FP16 promoted, rank check,
-    // merge) stamped by the kernel itself on the device's constant-rate
+    // merge, the K gather of device paging) stamped by the kernel itself on the device's constant-rate
     // clock: KEV_N x CLK_WORDS (CLK_SLOTS start slots, then CLK_SLOTS end
     // slots, CLK_PAD words apart), reset from h_clk_init before each
     // profiled step and read back into h_clk
@@ -247,6 +247,10 @@ struct ckv_cache {
     bool device_gather = false;
     const uint16_t *t2k_dev = nullptr, *t2v_dev = nullptr;
     hipEvent_t ev_wl = nullptr;
+    // device paging: the gather kernels' stream, and the ends of its K and
+    // V gathers
+    hipStream_t gstream = nullptr;
+    hipEvent_t ev_gk = nullptr, ev_gv = nullptr;
     std::vector<uint16_t *> pstage_k, pstage_v;
     std::vector<std::vector<uint8_t>> pstaged_k, pstaged_v;
     std::vector<int> seq_flags;               // [B] of the last step
@@ -357,8 +361,9 @@ void ckv_destroy(ckv_cache *c) {
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->ev_kside)
         if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl})
+    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl, c->ev_gk, c->ev_gv, c->ev_selk})
         if (e) (void)hipEventDestroy(e);
+    if (c->gstream) (void)hipStreamDestroy(c->gstream);
     for (hipEvent_t e : c->pev)
         if (e) (void)hipEventDestroy(e);
     if (Stager *S = c->stager) {
@@ -474,7 +479,11 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         HIPCHK(hipEventCreateWithFlags(&c->ev_kside[k], hipEventDisableTiming));
     }
     HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_selk, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_wl, hipEventDisableTiming));
+    HIPCHK(hipStreamCreateWithFlags(&c->gstream, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_gk, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_gv, hipEventDisableTiming));
     {
         void *pk = nullptr, *pv = nullptr;
         HIPCHK(hipHostGetDevicePointer(&pk, c->t2k, 0));
@@ -1070,15 +1079,32 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     kev(KEV_SELECT);
     HIPCHK(launch_select(Ly, St, T, s));
     St.clk = nullptr;
-    // page lists and plans to the host (the round trip of the selection)
+    // page lists and plans to the host (the round trip of the selection), on
+    // a paging stream: the passes below do not wait for these copies
     const size_t selbytes = (size_t)batch * Hkv * Ly.Nmax * sizeof(uint32_t);
-    HIPCHK(hipMemcpyAsync(c->h_sel, c->sel, selbytes, hipMemcpyDeviceToHost, s));
-    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
-    HIPCHK(hipEventRecord(c->ev_sel, s));
-    // block lists of the value passes; K3: tail blocks; both overlap the
-    // host's page lists and the paging below
-    HIPCHK(launch_worklist(Ly, St, s));
+    HIPCHK(hipEventRecord(c->ev_selk, s));
+    HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_selk, 0));
+    HIPCHK(hipMemcpyAsync(c->h_sel, c->sel, selbytes, hipMemcpyDeviceToHost, c->side[0]));
+    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, c->side[0]));
+    HIPCHK(hipEventRecord(c->ev_sel, c->side[0]));
+    // block lists of the value passes and the sequences' skip flags; K3:
+    // tail blocks; both overlap the host's page lists and the paging below
+    HIPCHK(launch_worklist(Ly, St, c->dskip, s));
     HIPCHK(hipEventRecord(c->ev_wl, s));
+    if (gather) {
+        // device-initiated paging starts from the device's own block lists
+        // and skip flags, before the host has seen the selection: K blocks,
+        // then V blocks, on a stream of their own (skipped sequences are
+        // left to the host's copies below)
+        HIPCHK(hipStreamWaitEvent(c->gstream, c->ev_wl, 0));
+        if (prof) HIPCHK(hipEventRecord(E[5], c->gstream));
+        kev(KEV_GATHER);
+        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, 1, c->gstream));
+        St.clk = nullptr;
+        HIPCHK(hipEventRecord(c->ev_gk, c->gstream));
+        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, 2, c->gstream));
+        HIPCHK(hipEventRecord(c->ev_gv, c->gstream));
+    }
     kev(KEV_TAIL);
     if (St.nsplit > 0) HIPCHK(launch_tail(Ly, St, s));
     St.clk = nullptr;
@@ -1092,7 +1118,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     }
     size_t paged = 0;
     CopyList cl, clk;  // V runs (and the fallback's), K runs
-    if (prof) HIPCHK(hipEventRecord(E[5], c->side[0]));
+    if (prof && !gather) HIPCHK(hipEventRecord(E[5], c->side[0]));
     const uint32_t allg = (1u << G) - 1u;
     for (int n = 0; n < batch; ++n) {
         int skip = 0;
@@ -1134,15 +1160,6 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
             page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
         }
     }
-    if (!gather)
-        HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
-    if (gather) {
-        // the skip flags first (the kernel leaves skipped sequences to the
-        // copies), the block lists from the worklist kernel
-        HIPCHK(hipMemcpyAsync(c->dskip, c->h_skip, sizeof(int) * batch, hipMemcpyHostToDevice, c->side[0]));
-        HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_wl, 0));
-        HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, 1, c->side[0]));
-    }
     if (staged) {
         TRY(stage_and_copy(c, *c->stager, clk, cl, s, paged));
     } else {
@@ -1153,8 +1170,12 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
             HIPCHK(hipEventRecord(c->ev_kside[k], c->side[k]));
             HIPCHK(hipStreamWaitEvent(s, c->ev_kside[k], 0));
         }
-        if (gather)
-            HIPCHK(launch_gather(Ly, St, c->dskip, c->t2k_dev, c->t2v_dev, stage_k, stage_v, 2, c->side[0]));
+        if (gather) {
+            // the FP16-key pass also waits for the K gather; the end of the
+            // paging (below) for the V gather
+            HIPCHK(hipStreamWaitEvent(s, c->ev_gk, 0));
+            HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_gv, 0));
+        }
         TRY(issue_copies(c, cl));
         paged += cl.bytes + clk.bytes;
         if (prof) c->pf.copies += cl.size.size() + clk.size.size();
@@ -1328,6 +1349,20 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         TRY(kacc(PH_MERGE, KEV_RANK));
         TRY(kacc(PH_MERGE, KEV_MERGE));
         c->pf.counts[PH_MERGE] -= 1;  // one merge phase per step, two launches
+        if (gather) {
+            // when the device paging started, after the selection ended
+            const unsigned long long *ws = c->h_clk + (size_t)KEV_SELECT * CLK_WORDS;
+            const unsigned long long *wg = c->h_clk + (size_t)KEV_GATHER * CLK_WORDS;
+            unsigned long long sel_end = 0, g0 = ~0ull;
+            for (int i = 0; i < CLK_SLOTS; ++i) {
+                sel_end = std::max(sel_end, ws[(size_t)(CLK_SLOTS + i) * CLK_PAD]);
+                g0 = std::min(g0, wg[(size_t)i * CLK_PAD]);
+            }
+            if (g0 != ~0ull && sel_end != 0) {
+                c->pf.gather_lead_ms += ((double)g0 - (double)sel_end) / c->clk_khz;
+                c->pf.gather_steps += 1;
+            }
+        }
         if (any_dense) TRY(acc(PH_FALLBACK, 9, 10));
         c->pf.ms[PH_STEP] += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
         c->pf.counts[PH_STEP] += 1;
@@ -1342,6 +1377,11 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
                                           ckv_head_report *report, void *stream) {
     const ckv_status st = certified_step(c, layer, q, batch, th, out, report, stream);
     if (st != CKV_OK && c && layer >= 0 && layer < c->cfg.n_layers) {
+        // paging already issued by the failed step (copies, gathers) ends
+        // before the next step reuses the staging area
+        for (hipStream_t ps : c->side)
+            if (ps) (void)hipStreamSynchronize(ps);
+        if (c->gstream) (void)hipStreamSynchronize(c->gstream);
         // blocks listed for paging are marked staged before their copies
         // are issued; after a failed step none of them can be trusted, so
         // the layer's next step pages them again

@@ -1638,6 +1638,7 @@ constexpr int GATHER_X = 32;
 template <int D>
 __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *skip_seq, const uint16_t *t2k,
                                                 const uint16_t *t2v, uint16_t *stk, uint16_t *stv, int kinds) {
+    KernelClock kc(St.clk);
     const int x = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (skip_seq[n]) return;
@@ -1676,12 +1677,21 @@ __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *s
 // bits put them in P of some head (FP16 keys), in P without FP16 values for
 // some head (INT4 values at FP16-key weights), give FP16 values to some head
 // (the unfinished block, when there is one, ends this list), or leave some
-// head's block outside P and VP (the tail).
+// head's block outside P and VP (the tail).  The workgroup of kv head 0
+// also writes the sequence's skip flag (rung 4 before paging: a cap of
+// rung 1 or 2 exhausted on some head), which the later passes and the
+// device-initiated paging read without the host's round trip.
 // ===========================================================================
 template <int G>
-__global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St) {
+__global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_seq) {
     const int g = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    if (g == 0 && wave == 0) {
+        int sk = 0;
+        for (int h = lane; h < Ly.Hq; h += 64) sk |= (St.plan[(size_t)n * Ly.Hq + h].flags >> 1) & 1;
+        const bool any = __ballot(sk != 0) != 0;
+        if (lane == 0) skip_seq[n] = any ? 1 : 0;
+    }
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[St.layer * Ly.B + n]);
     const int N = len / 64;
     constexpr uint32_t ALL = (1u << G) - 1u;
@@ -2193,10 +2203,11 @@ hipError_t launch_gather(const Layout &Ly, const Step &St, const int *skip_seq, 
         return hipGetLastError();
     });
 }
-hipError_t launch_worklist(const Layout &Ly, const Step &St, hipStream_t s) {
+hipError_t launch_worklist(const Layout &Ly, const Step &St, int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         (void)D;
-        hipLaunchKernelGGL((k_worklist<decltype(G)::value>), dim3(Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St);
+        hipLaunchKernelGGL((k_worklist<decltype(G)::value>), dim3(Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St,
+                           skip_seq);
         return hipGetLastError();
     });
 }

@@ -303,6 +303,11 @@ typedef struct {
     uint64_t v16_blocks;    /* FP16 value blocks read by the promoted pass   */
     uint64_t int4p_blocks;  /* INT4 value blocks read by the promoted pass   */
     uint64_t dense_blocks;  /* FP16 K+V blocks read by the dense fallback    */
+    double gather_lead_ms;  /* device paging only: summed over its steps, the
+                               K gather's first wave start minus the
+                               selection kernel's last wave end (device
+                               clock; the host's round trip is not in it)  */
+    int gather_steps;       /* steps that paged by the device                */
 } ckv_profile;
 
 ckv_status ckv_set_profiling(ckv_cache *c, int enable);

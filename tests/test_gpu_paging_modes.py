@@ -91,3 +91,29 @@ def test_device_paging_llama_8k():
     assert np.all(np.abs(out - res.out) <= ATOL + RTOL * np.abs(res.out))
     for f in ("kstar", "n_v_promoted", "rung_mask", "e_key", "e_val"):
         assert np.array_equal(rep[f], res.report[f]), f
+
+
+def test_device_paging_batch_with_some_sequences_at_rung4_before_paging():
+    """The gather starts from the device's own skip flags (written by the
+    worklist kernel, before the host reads the selection): sequences 1 and 3
+    go to rung 4 before paging (left to the host's copies), sequences 0 and
+    2 are certified and paged by the device; identical to host copies and to
+    the oracle, two layers in a row."""
+    rng = np.random.default_rng(77)
+    B, T, Hq, Hkv, d = 4, 1280, 8, 4, 64
+    k = rng.standard_normal((B, T, Hkv, d))
+    v = rng.standard_normal((B, T, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    v[0] *= 0.01
+    v[2] *= 0.01
+    q[1] *= 0.02
+    q[3] *= 0.02
+    k, v, q = (np.asarray(x, np.float16).view(np.uint16) for x in (k, v, q))
+    th = oracle.default_thresholds(1 / np.sqrt(d), v_cap_blocks=2)
+    out, rep, step = run_both(k, v, q, th, layers=2)
+    res = oracle.certified_decode(k, v, q, th)
+    assert list(res.trace["seq_flags"] & 1) == [0, 1, 0, 1]
+    assert list(step["seq_flags"] & 1) == [0, 1, 0, 1]
+    for f in ("kstar", "n_v_promoted", "rung_max", "rung_mask", "e_key", "e_val", "n_discordant"):
+        assert np.array_equal(rep[f], res.report[f]), f
+    assert np.all(np.abs(out - res.out) <= ATOL + RTOL * np.abs(res.out))
