@@ -213,6 +213,8 @@ struct ckv_cache {
     uint64_t *mfx = nullptr, *cval = nullptr, *m16 = nullptr, *keys = nullptr;
     uint32_t *sel = nullptr, *plist = nullptr, *dmask = nullptr, *wl = nullptr;
     int *wcnt = nullptr;
+    uint2 *klist = nullptr;
+    int *kcount = nullptr;
     HeadPlan *plan = nullptr;
     float2 *st16 = nullptr;
     int *dskip = nullptr;
@@ -462,6 +464,8 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->plist, (size_t)B * Hq * Nmax));
     CTRY(dalloc(c, &c->wl, (size_t)WL_KINDS * B * Hkv * (Nmax + 1)));
     CTRY(dalloc(c, &c->wcnt, (size_t)WL_KINDS * B * Hkv));
+    CTRY(dalloc(c, &c->klist, (size_t)B * Hkv * Nmax));
+    CTRY(dalloc(c, &c->kcount, 1));
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
     CTRY(dalloc(c, &c->dskip, (size_t)B));
     CTRY(dalloc(c, &c->dmask, (size_t)B * Hkv));
@@ -1057,6 +1061,8 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     St.qd = c->qd;
     St.wl = c->wl;
     St.wcnt = c->wcnt;
+    St.klist = c->klist;
+    St.kcount = c->kcount;
     St.out = out;
     Th T{};
     T.tau = th->tau_cov;

@@ -569,6 +569,7 @@ __device__ __forceinline__ bool in_set(P val, int b, uint64_t thr) {
 template <int D, int G>
 __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
     KernelClock kc(St.clk);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *St.kcount = 0;  // the flat key list
     __shared__ SelShared sh;
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int g = h / G, j = h % G, l = St.layer;
@@ -1400,64 +1401,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 constexpr int KEYS_PW = 4;             // list entries per wave of the FP16-key pass, at most
 constexpr int KEYS_MAXE = 4 * KEYS_PW;  // list entries per workgroup, at most
 
-// An equal share of one kind of block list over the whole step: the lists
-// of all (sequence, kv head) pairs of the batch concatenated in pair order
-// (pairs of a sequence flagged in skip_seq count as empty), entries
-// [sp*total/nsp, (sp+1)*total/nsp) to workgroup sp of nsp.  Entry i of the
-// share is entry sidx[i] of pair sng[i]'s list.  Returns the share's size,
-// at most CAP when nsp * CAP >= total.  256 threads; wtot: 4 ints of LDS.
-template <int CAP>
-__device__ __forceinline__ int list_share(const Layout &Ly, const Step &St, int kind, const int *skip_seq, int sp,
-                                          int nsp, int *sng, int *sidx, int *wtot) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int Hkv = Ly.Hkv, BH = St.batch * Hkv;
-    const int *cnt = St.wcnt + (size_t)kind * Ly.B * Hkv;
-    auto count = [&](int ng) { return ng < BH && !(skip_seq && skip_seq[ng / Hkv]) ? cnt[ng] : 0; };
-    int t = 0;
-    for (int c0 = 0; c0 < BH; c0 += 256) t += count(c0 + tid);
-    t = wave_sum_i32_dpp(t);
-    if (lane == 0) wtot[wave] = t;
-    __syncthreads();
-    const long long total = (long long)wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    const int e0 = (int)((long long)sp * total / nsp);
-    const int ne = min((int)((long long)(sp + 1) * total / nsp) - e0, CAP);
-    __syncthreads();
-    // the pairs whose entries fall in [e0, e0 + ne), 256 pairs at a time
-    int base = 0;
-    for (int c0 = 0; c0 < BH && base < e0 + ne; c0 += 256) {
-        const int ng = c0 + tid, c = count(ng);
-        const int pw = (int)wave_prefix_excl_u32((uint32_t)c, lane);
-        if (lane == 63) wtot[wave] = pw + c;
-        __syncthreads();
-        int pre = base + pw, chunk = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            pre += w < wave ? wtot[w] : 0;
-            chunk += wtot[w];
-        }
-        const int lo = max(pre, e0), hi = min(pre + c, e0 + ne);
-        for (int e = lo; e < hi; ++e) {
-            sng[e - e0] = ng;
-            sidx[e - e0] = e - pre;
-        }
-        base += chunk;
-        __syncthreads();
-    }
-    return ne;
-}
-
 // ===========================================================================
 // K4a (keys): FP16-key scores of the P blocks from the staging area [Meth-3
 // rank-consistency check], one wave per block, lane = token: FP64 fma chain
 // over c = 0 .. D-1 with one rounding to FP32 after the scale (the decision
 // arithmetic of the rank check), the block's FP16-side max and mass (64-leaf
 // tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
-// through uniform scalar loads.  The step's P list (all pairs) is split
-// evenly over the workgroups (one round of resident workgroups when it has
-// at most KEYS_MAXE entries each), at most KEYS_PW entries per wave; a block
-// is loaded as two halves of D/2 channels, three halves in registers (two in
-// flight while the chain runs over the third), which keeps the registers at
-// four waves per SIMD.
+// through uniform scalar loads.  The step's flat P list (all pairs) is
+// split evenly over the workgroups (one round of resident workgroups when
+// it has at most KEYS_MAXE entries each), at most KEYS_PW entries per wave;
+// a block is loaded as two halves of D/2 channels, three halves in registers
+// (two in flight while the chain runs over the third), which keeps the
+// registers at four waves per SIMD.
 // ===========================================================================
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
@@ -1466,17 +1421,21 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     constexpr uint32_t ALL = (1u << G) - 1u;
     __shared__ uint32_t sbits[KEYS_MAXE], sblk[KEYS_MAXE];
-    __shared__ int sng[KEYS_MAXE], sidx[KEYS_MAXE], wtot[4];
+    __shared__ int sng[KEYS_MAXE];
     __shared__ float sres[4][KEYS_PW][G][64];
     __shared__ float2 sml[4][KEYS_PW][G];
-    const int ne = list_share<KEYS_MAXE>(Ly, St, WL_KEYS, skip_seq, blockIdx.x, gridDim.x, sng, sidx, wtot);
-    if (ne == 0) return;
-    const size_t nk = (size_t)Ly.B * Ly.Hkv;
+    (void)skip_seq;  // skipped sequences are not in the flat list
+    // this workgroup's share of the step's flat FP16-key list: one load for
+    // the count, one for the entries, before the first block request
+    const int total = __builtin_amdgcn_readfirstlane(*St.kcount);
+    const int e0 = (int)((long long)blockIdx.x * total / gridDim.x);
+    const int ne = min((int)((long long)(blockIdx.x + 1) * total / gridDim.x) - e0, KEYS_MAXE);
+    if (ne <= 0) return;
     for (int i = threadIdx.x; i < ne; i += 256) {
-        const size_t ng = (size_t)sng[i];
-        const uint32_t b = St.wl[(WL_KEYS * nk + ng) * (size_t)(Ly.Nmax + 1) + sidx[i]];
-        sblk[i] = b;
-        sbits[i] = St.sel[ng * Ly.Nmax + b];
+        const uint2 e = St.klist[e0 + i];
+        sng[i] = (int)e.x;
+        sblk[i] = e.y & 0xFFFFFFu;
+        sbits[i] = e.y >> 24;
     }
     __syncthreads();
     // q as [D][G] FP64, read through the constant address space (qd is not
@@ -1680,17 +1639,23 @@ __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *s
 // head's block outside P and VP (the tail).  The workgroup of kv head 0
 // also writes the sequence's skip flag (rung 4 before paging: a cap of
 // rung 1 or 2 exhausted on some head), which the later passes and the
-// device-initiated paging read without the host's round trip.
+// device-initiated paging read without the host's round trip.  Each
+// workgroup of a sequence not skipped also appends its P list to the
+// step's flat FP16-key list (one atomic reservation per pair).
 // ===========================================================================
 template <int G>
 __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_seq) {
     const int g = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    if (g == 0 && wave == 0) {
+    __shared__ int sh_skip, sh_kbase, kc[4];
+    if (wave == 0) {
         int sk = 0;
         for (int h = lane; h < Ly.Hq; h += 64) sk |= (St.plan[(size_t)n * Ly.Hq + h].flags >> 1) & 1;
         const bool any = __ballot(sk != 0) != 0;
-        if (lane == 0) skip_seq[n] = any ? 1 : 0;
+        if (lane == 0) {
+            sh_skip = any ? 1 : 0;
+            if (g == 0) skip_seq[n] = any ? 1 : 0;
+        }
     }
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[St.layer * Ly.B + n]);
     const int N = len / 64;
@@ -1703,6 +1668,23 @@ __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_
     __shared__ int wc[WL_KINDS][4];
     int base[WL_KINDS] = {};
     const uint64_t below = (1ull << lane) - 1ull;
+    // the pair's place in the flat FP16-key list
+    {
+        int cnt = 0;
+        for (int r0 = 0; r0 < N; r0 += 256) {
+            const int b = r0 + tid;
+            cnt += __popcll(__ballot(b < N && (sel[b] & ALL) != 0));
+        }
+        if (lane == 0) kc[wave] = cnt;
+        __syncthreads();
+        if (tid == 0) {
+            const int tot = kc[0] + kc[1] + kc[2] + kc[3];
+            sh_kbase = !sh_skip && tot > 0 ? atomicAdd(St.kcount, tot) : 0;
+        }
+        __syncthreads();
+    }
+    const bool kflat = !sh_skip;
+    const int kbase = sh_kbase;
     for (int r0 = 0; r0 < N; r0 += 256) {
         const int b = r0 + tid;
         const uint32_t bits = b < N ? sel[b] : 0u;
@@ -1723,6 +1705,8 @@ __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_
                 tot += wc[k][w];
             }
             if (f[k]) lst[k][off + __popcll(bal[k] & below)] = (uint32_t)b;
+            if (k == WL_KEYS && kflat && f[k])
+                St.klist[kbase + off + __popcll(bal[k] & below)] = make_uint2((uint32_t)ng, (uint32_t)b | (pm << 24));
             base[k] += tot;
         }
         __syncthreads();

@@ -102,6 +102,12 @@ struct Step {
     // some head.  wcnt[kind][B][Hkv] = lengths.
     uint32_t *wl;
     int *wcnt;
+    // The FP16-key pass's entries of the whole step as one list: (pair
+    // n * Hkv + g, block | P heads << 24), pairs appended by the worklist
+    // kernel in any order (a pair's entries ascending), kcount entries
+    // (zeroed by the selection kernel); skipped sequences are left out.
+    uint2 *klist;
+    int *kcount;
     float *out;             // [batch][Hq][d]
     // profiling: when not null, the kernel launched with this step stamps
     // its execution span here (KernelClock: CLK_SLOTS start slots, then
