@@ -215,6 +215,11 @@ struct ckv_cache {
     int *wcnt = nullptr;
     uint2 *klist = nullptr;
     int *kcount = nullptr;
+    int *pcnt = nullptr, *vpref = nullptr;
+    // packed staging (staged paging without the persistent FP16 cache): the
+    // packed K / V slot of each listed block, for the dense fallback, which
+    // reads every block of a pair (pinned host copy, device copy)
+    uint32_t *h_kmap = nullptr, *h_vmap = nullptr, *kmap = nullptr, *vmap = nullptr;
     HeadPlan *plan = nullptr;
     float2 *st16 = nullptr;
     int *dskip = nullptr;
@@ -355,7 +360,7 @@ void ckv_destroy(ckv_cache *c) {
         if (p) (void)hipFree(p);
     for (void *p : {(void *)c->t2k, (void *)c->t2v, (void *)c->h_sel, (void *)c->h_mask,
                     (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_clk,
-                    (void *)c->h_clk_init})
+                    (void *)c->h_clk_init, (void *)c->h_kmap, (void *)c->h_vmap})
         if (p) (void)hipHostFree(p);
     for (hipStream_t st : c->side)
         if (st) (void)hipStreamDestroy(st);
@@ -466,6 +471,12 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->wcnt, (size_t)WL_KINDS * B * Hkv));
     CTRY(dalloc(c, &c->klist, (size_t)B * Hkv * Nmax));
     CTRY(dalloc(c, &c->kcount, 1));
+    CTRY(dalloc(c, &c->pcnt, (size_t)2 * B * Hkv));
+    CTRY(dalloc(c, &c->vpref, (size_t)B * Hkv));
+    CTRY(dalloc(c, &c->kmap, sblk));
+    CTRY(dalloc(c, &c->vmap, sblk));
+    CTRY(halloc(c, &c->h_kmap, sblk));
+    CTRY(halloc(c, &c->h_vmap, sblk));
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
     CTRY(dalloc(c, &c->dskip, (size_t)B));
     CTRY(dalloc(c, &c->dmask, (size_t)B * Hkv));
@@ -862,9 +873,22 @@ static ckv_status issue_copies(ckv_cache *c, CopyList &cl, bool join = true) {
 // and that are not staged yet, no gaps filled: runs of consecutive blocks of
 // at least a chunk's bytes to `direct` (one copy each, as efficient as a
 // chunk), the other blocks to the packing list.
+// Next free slot of the packed K and V staging areas (the step's listed
+// blocks in listing order).
+struct Slots {
+    uint32_t k = 0, v = 0;
+};
+
+// List the blocks of (n, g) that `want` asks for and are not staged yet:
+// runs of at least a chunk's size as direct copies, the rest for packing.
+// Block-indexed staging (`slot` null): a block's destination is its (pair,
+// block) place, kept in `dst` as an address.  Packed staging: it is the
+// next slot of the area, kept in `dst` as the slot number (and in `map`),
+// so a run takes consecutive slots and packed blocks keep listing order.
 static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
                         std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage,
-                        std::vector<const void *> &src, std::vector<uint64_t> &dst, CopyList &direct) {
+                        std::vector<const void *> &src, std::vector<uint64_t> &dst, CopyList &direct,
+                        uint32_t *slot, uint32_t *map) {
     const Layout &Ly = c->Ly;
     const size_t sb = ((size_t)n * Ly.Hkv + g) * Ly.Nmax, bb = c->blk_fp16 * 2;
     const int min_run = (int)((PAGE_CHUNK + bb - 1) / bb);
@@ -872,14 +896,21 @@ static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint
         int e = b + 1;
         while (e < N && want[e] && !staged[sb + e]) ++e;
         if (e - b >= min_run) {
-            direct.dst.push_back(stage + (sb + b) * c->blk_fp16);
+            direct.dst.push_back(stage + (slot ? (size_t)*slot : sb + b) * c->blk_fp16);
             direct.src.push_back((void *)(t2 + Ly.blk(layer, n, g, b) * c->blk_fp16));
             direct.size.push_back((size_t)(e - b) * bb);
             direct.bytes += (size_t)(e - b) * bb;
+            if (slot)
+                for (int i = b; i < e; ++i) map[sb + i] = (*slot)++;
         } else {
             for (int i = b; i < e; ++i) {
                 src.push_back(t2 + Ly.blk(layer, n, g, i) * c->blk_fp16);
-                dst.push_back((uint64_t)(uintptr_t)(stage + (sb + i) * c->blk_fp16));
+                if (slot) {
+                    map[sb + i] = *slot;
+                    dst.push_back((*slot)++);
+                } else {
+                    dst.push_back((uint64_t)(uintptr_t)(stage + (sb + i) * c->blk_fp16));
+                }
             }
         }
         for (int i = b; i < e; ++i) staged[sb + i] = 1;
@@ -888,12 +919,14 @@ static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint
 }
 
 // Copy the listed blocks: the long K runs and chunks of packed K blocks, then
-// the long V runs and chunks of packed V blocks; a chunk is one copy and one
-// scatter on the paging stream of its slot.  Once the K side is issued, `s`
-// waits for it (the FP16-key pass needs only K); at the end the paging
-// streams are joined on side[0].
+// the long V runs and chunks of packed V blocks.  Block-indexed staging
+// (pk null): a chunk is one copy into its device ring slot and one scatter
+// to the blocks' places.  Packed staging (pk, pv: the K and V areas): a
+// chunk holds consecutive slots and is one copy straight to them.  Once the
+// K side is issued, `s` waits for it (the FP16-key pass needs only K); at
+// the end the paging streams are joined on side[0].
 static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyList &vruns, hipStream_t s,
-                                 size_t &bytes) {
+                                 size_t &bytes, uint16_t *pk, uint16_t *pv) {
     const size_t nk = S.src.size();
     S.src.insert(S.src.end(), S.vsrc.begin(), S.vsrc.end());
     S.dst.insert(S.dst.end(), S.vdst.begin(), S.vdst.end());
@@ -902,13 +935,29 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
     const size_t nblk = S.src.size();
     S.cstart.clear();
     // the step's first chunks are 1/8, 1/4 and 1/2 of a full one: the first
-    // copy starts after a short packing time
+    // copy starts after a short packing time; packed staging also starts a
+    // chunk wherever the slots stop being consecutive (around a direct run)
+    const bool packed = pk != nullptr;
+    auto cut = [&](size_t i0, size_t i1, size_t i, int cap) {
+        size_t e = std::min(i1, i + (size_t)cap);
+        if (packed)
+            for (size_t j = i + 1; j < e; ++j)
+                if (S.dst[j] != S.dst[j - 1] + 1) {
+                    e = j;
+                    break;
+                }
+        (void)i0;
+        return e;
+    };
     for (size_t i = 0, k = 0; i < nk; ++k) {
         S.cstart.push_back((int)i);
-        i += k < 3 ? std::max(1, S.per_chunk >> (3 - k)) : S.per_chunk;
+        i = cut(0, nk, i, k < 3 ? std::max(1, S.per_chunk >> (3 - k)) : S.per_chunk);
     }
     const int nkc = (int)S.cstart.size();
-    for (size_t i = nk; i < nblk; i += S.per_chunk) S.cstart.push_back((int)i);
+    for (size_t i = nk; i < nblk;) {
+        S.cstart.push_back((int)i);
+        i = cut(nk, nblk, i, S.per_chunk);
+    }
     S.nchunk = (int)S.cstart.size();
     S.cstart.push_back((int)nblk);
     auto kjoin = [&]() -> hipError_t {
@@ -955,10 +1004,20 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
             }
             const int slot = ci % PAGE_SLOTS, nb = S.cstart[ci + 1] - S.cstart[ci];
             hipStream_t st = c->side[slot % NSIDE];
-            uint8_t *dc = S.dring + (size_t)slot * S.stride;
-            const size_t cb = PAGE_HDR + (size_t)nb * S.blk_bytes;
-            e = page_copy(c, dc, S.hring + (size_t)slot * S.stride, cb, st);
-            if (e == hipSuccess) e = launch_page_scatter(dc, nb, S.blk_bytes, st);
+            uint8_t *hc = S.hring + (size_t)slot * S.stride;
+            size_t cb;
+            if (packed) {
+                // the blocks straight to their consecutive slots
+                uint16_t *area = ci < nkc ? pk : pv;
+                uint8_t *dst = reinterpret_cast<uint8_t *>(area) + (size_t)S.dst[S.cstart[ci]] * S.blk_bytes;
+                cb = (size_t)nb * S.blk_bytes;
+                e = page_copy(c, dst, hc + PAGE_HDR, cb, st);
+            } else {
+                uint8_t *dc = S.dring + (size_t)slot * S.stride;
+                cb = PAGE_HDR + (size_t)nb * S.blk_bytes;
+                e = page_copy(c, dc, hc, cb, st);
+                if (e == hipSuccess) e = launch_page_scatter(dc, nb, S.blk_bytes, st);
+            }
             if (e == hipSuccess) e = hipEventRecord(S.ev[slot], st);
             if (e != hipSuccess) break;
             bytes += cb;
@@ -1050,6 +1109,9 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     const bool gather = c->device_gather && !pers;
     // staged paging (host-packed chunks) for the host-issued copies
     const bool staged = !gather && c->stager && c->stager->nthreads > 0;
+    // staged paging into the packed areas (the persistent FP16 cache keeps
+    // block-indexed staging: its blocks stay across steps)
+    const bool packed = staged && !pers;
     if (staged) {
         c->stager->src.clear();
         c->stager->dst.clear();
@@ -1063,6 +1125,9 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     St.wcnt = c->wcnt;
     St.klist = c->klist;
     St.kcount = c->kcount;
+    St.pcnt = c->pcnt;
+    St.vpref = c->vpref;
+    St.packed = packed ? 1 : 0;
     St.out = out;
     Th T{};
     T.tau = th->tau_cov;
@@ -1130,44 +1195,54 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         int skip = 0;
         for (int h = 0; h < Hq; ++h) skip |= (c->h_plan[(size_t)n * Hq + h].flags >> 1) & 1;
         c->h_skip[n] = skip;
-        const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
-        for (int g = 0; g < Hkv; ++g) {
-            const uint32_t *sl = c->h_sel + ((size_t)n * Hkv + g) * Ly.Nmax;
-            const uint8_t sk = skip ? 1 : 0;
-            for (int b = 0; b < N; ++b) {
-                const uint32_t w = sl[b];
-                wantk[b] = (uint8_t)(sk | ((w & allg) != 0));
-                wantv[b] = (uint8_t)(sk | (((w >> 8) & allg) != 0));
-            }
-            if (prof) {
-                for (int b = 0; b < N; ++b) {
-                    const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
-                    c->pf.tail_blocks += ((pm | vm) != allg);
-                    if (!skip) {
-                        c->pf.k16_blocks += pm != 0;
-                        c->pf.v16_blocks += vm != 0;
-                        c->pf.int4p_blocks += (pm & ~vm) != 0;
-                    }
-                }
-                c->pf.q8_blocks += N;
-            }
-            if (gather && !skip) {
-                // the device copies this (seq, kv head)'s listed blocks itself
-                for (int b = 0; b < N; ++b) paged += (size_t)(wantk[b] + wantv[b]) * c->blk_fp16 * 2;
-                continue;
-            }
-            if (staged) {
-                Stager &S = *c->stager;
-                list_blocks(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, S.src, S.dst, clk);
-                list_blocks(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, S.vsrc, S.vdst, cl);
-                continue;
-            }
-            page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, clk);
-            page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
-        }
     }
+    // packed slots, in the order the worklist kernel assumes: the pairs not
+    // skipped, pair by pair, then the skipped ones (all their blocks)
+    Slots slots;
+    for (int pass = 0; pass < 2; ++pass)
+        for (int n = 0; n < batch; ++n) {
+            const int skip = c->h_skip[n];
+            if (skip != pass) continue;
+            const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
+            for (int g = 0; g < Hkv; ++g) {
+                const uint32_t *sl = c->h_sel + ((size_t)n * Hkv + g) * Ly.Nmax;
+                const uint8_t sk = skip ? 1 : 0;
+                for (int b = 0; b < N; ++b) {
+                    const uint32_t w = sl[b];
+                    wantk[b] = (uint8_t)(sk | ((w & allg) != 0));
+                    wantv[b] = (uint8_t)(sk | (((w >> 8) & allg) != 0));
+                }
+                if (prof) {
+                    for (int b = 0; b < N; ++b) {
+                        const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
+                        c->pf.tail_blocks += ((pm | vm) != allg);
+                        if (!skip) {
+                            c->pf.k16_blocks += pm != 0;
+                            c->pf.v16_blocks += vm != 0;
+                            c->pf.int4p_blocks += (pm & ~vm) != 0;
+                        }
+                    }
+                    c->pf.q8_blocks += N;
+                }
+                if (gather && !skip) {
+                    // the device copies this (seq, kv head)'s listed blocks itself
+                    for (int b = 0; b < N; ++b) paged += (size_t)(wantk[b] + wantv[b]) * c->blk_fp16 * 2;
+                    continue;
+                }
+                if (staged) {
+                    Stager &S = *c->stager;
+                    list_blocks(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, S.src, S.dst, clk,
+                                packed ? &slots.k : nullptr, c->h_kmap);
+                    list_blocks(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, S.vsrc, S.vdst, cl,
+                                packed ? &slots.v : nullptr, c->h_vmap);
+                    continue;
+                }
+                page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, clk);
+                page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
+            }
+        }
     if (staged) {
-        TRY(stage_and_copy(c, *c->stager, clk, cl, s, paged));
+        TRY(stage_and_copy(c, *c->stager, clk, cl, s, paged, packed ? stage_k : nullptr, stage_v));
     } else {
         // K runs first: the FP16-key pass and the INT4 promoted pass need
         // only them and run while the V runs are copied
@@ -1238,8 +1313,10 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                 if (m && staged) {
                     // the blocks between those already staged: packed
                     Stager &SG = *c->stager;
-                    list_blocks(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, SG.src, SG.dst, cl);
-                    list_blocks(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, SG.vsrc, SG.vdst, clv);
+                    list_blocks(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, SG.src, SG.dst, cl,
+                                packed ? &slots.k : nullptr, c->h_kmap);
+                    list_blocks(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, SG.vsrc, SG.vdst, clv,
+                                packed ? &slots.v : nullptr, c->h_vmap);
                 } else if (m) {
                     page_runs(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, cl);
                     page_runs(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, cl);
@@ -1248,7 +1325,13 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
             }
         }
         if (staged) {
-            TRY(stage_and_copy(c, *c->stager, cl, clv, s, paged));
+            TRY(stage_and_copy(c, *c->stager, cl, clv, s, paged, packed ? stage_k : nullptr, stage_v));
+            if (packed) {
+                // where the dense pass finds each block of its pairs
+                const size_t mb = (size_t)batch * Hkv * Ly.Nmax * sizeof(uint32_t);
+                HIPCHK(hipMemcpyAsync(c->kmap, c->h_kmap, mb, hipMemcpyHostToDevice, c->side[0]));
+                HIPCHK(hipMemcpyAsync(c->vmap, c->h_vmap, mb, hipMemcpyHostToDevice, c->side[0]));
+            }
         } else {
             TRY(issue_copies(c, cl));
             paged += cl.bytes;
@@ -1261,6 +1344,8 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         DenseSrc S{};
         S.k = stage_k;
         S.v = stage_v;
+        S.kmap = packed ? c->kmap : nullptr;
+        S.vmap = packed ? c->vmap : nullptr;
         S.kp = Ly.kpart + Ly.seqg(layer, 0, 0) * c->blk_fp16;
         S.vp = Ly.vpart + Ly.seqg(layer, 0, 0) * c->blk_fp16;
         S.len = Ly.len + (size_t)layer * cf.max_batch;

@@ -569,7 +569,6 @@ __device__ __forceinline__ bool in_set(P val, int b, uint64_t thr) {
 template <int D, int G>
 __global__ __launch_bounds__(SEL_T) void k_select(Layout Ly, Step St, Th th) {
     KernelClock kc(St.clk);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *St.kcount = 0;  // the flat key list
     __shared__ SelShared sh;
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int g = h / G, j = h % G, l = St.layer;
@@ -1219,13 +1218,13 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     // The blocks of this split: an equal share of the pass's block list, over
     // as many splits as the block range [0, nslot) has of bps blocks (the
     // partials the merge reads); every listed block serves some head here.
-    int ne;
+    int ne, e0;
     {
         const int nsp = (nslot + St.bps - 1) / St.bps;
         const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
         const int kind = MODE == VP_TAIL ? WL_TAIL : F16 ? WL_FP16 : WL_INT4;
         const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[kind * nk + ng]);
-        const int e0 = sp < nsp ? (int)((long long)sp * cnt / nsp) : cnt;
+        e0 = sp < nsp ? (int)((long long)sp * cnt / nsp) : cnt;
         const int e1 = sp < nsp ? (int)((long long)(sp + 1) * cnt / nsp) : cnt;
         ne = min(e1 - e0, MAX_BPS);
         const uint32_t *lst = St.wl + (kind * nk + ng) * (size_t)(Ly.Nmax + 1);
@@ -1243,7 +1242,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     va.init();
     struct Blk {
         uint32_t pm, use;
-        int b;
+        int b, li;  // block, index in the pass's list of the pair
         bool part, valid;
     };
     struct Opd {
@@ -1258,6 +1257,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
         Blk k;
         k.valid = i < ne;
         k.b = k.valid ? (int)__builtin_amdgcn_readfirstlane(sblk[i]) : 0;
+        k.li = e0 + (k.valid ? i : 0);
         k.part = F16 && k.valid && k.b == N;
         k.pm = 0;
         k.use = k.valid ? ALL : 0u;
@@ -1279,12 +1279,16 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     constexpr uint32_t CBLK = D * (V8 ? 64 : 32), MBLK = 64 * (D / 32) * 4, FBLK = 64 * D * 2;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Ly.vq + Ly.blk(l, n, g, 0) * CBLK, (uint32_t)Ly.Nmax * CBLK);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(Ly.vmeta + Ly.blk(l, n, g, 0) * (MBLK / 4), (uint32_t)Ly.Nmax * MBLK);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(St.stage_v + selbase * 64 * D, (uint32_t)Ly.Nmax * FBLK);
+    // FP16 values: packed slot vpref + list index, or (pair, block)
+    const size_t vbase = St.packed && F16 ? (size_t)__builtin_amdgcn_readfirstlane(St.vpref[selbase / Ly.Nmax]) : 0;
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(Ly.vpart + Ly.seqg(l, n, g) * 64 * D, FBLK);
     auto issue = [&](const Blk &k, Opd &o) {
         const int b = k.b;
-        if constexpr (F16)
-            load_fp16v<D>(k.part ? rp : rv, !k.valid ? RSRC_OOB : k.part ? 0u : (uint32_t)b * FBLK, lane, o.vv);
+        if constexpr (F16) {
+            const size_t slot = St.packed ? vbase + (size_t)k.li : selbase + (size_t)b;
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(St.stage_v + slot * 64 * D, FBLK);
+            load_fp16v<D>(k.part ? rp : rv, !k.valid ? RSRC_OOB : 0u, lane, o.vv);
+        }
         else
             load_int4<D, G, false, V8>(rq, rm, k.valid ? (uint32_t)b * CBLK : RSRC_OOB,
                                        k.valid ? (uint32_t)b * MBLK : RSRC_OOB, lane, o.cw, o.mw);
@@ -1453,9 +1457,11 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
     using Half = uint4[HC];
     auto issue = [&](int i, int h, Half &kr) {
         const int ic = i < ne ? i : 0;  // in-range share index on every path
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(St.stage_k + (size_t)pair(ic) * Ly.Nmax * 64 * D, (uint32_t)Ly.Nmax * BLKB);
-        const uint32_t off = (i < ne ? (uint32_t)blk(ic) * BLKB : RSRC_OOB) + lane * 16 + h * HC * 1024;
+        // the block's K: packed slot e0 + ic (the list is in packed order), or
+        // (pair, block) in the staging area
+        const size_t slot = St.packed ? (size_t)(e0 + ic) : (size_t)pair(ic) * Ly.Nmax + (size_t)blk(ic);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(St.stage_k + slot * 64 * D, BLKB);
+        const uint32_t off = (i < ne ? 0u : RSRC_OOB) + lane * 16 + h * HC * 1024;
 #pragma unroll
         for (int ch = 0; ch < HC; ++ch) kr[ch] = rsrc_load16(rs, off + ch * 1024);
     };
@@ -1631,23 +1637,33 @@ __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *s
 }
 
 // ===========================================================================
-// Block lists of the value and FP16-key passes, one workgroup per (kv head,
-// sequence): the blocks of the sequence in ascending order whose selection
+// Block lists of the value and FP16-key passes, two kernels of one
+// workgroup per (kv head, sequence).
+//
+// k_wlcount: the sequence's skip flag (rung 4 before paging: a cap of rung
+// 1 or 2 exhausted on some head; written by the workgroup of kv head 0), and
+// the pair's counts of blocks in P of some head and of blocks with FP16
+// values for some head (0 for a skipped sequence).  These counts order the
+// packed staging areas of staged paging: the K (V) blocks of the pairs not
+// skipped, pair by pair and ascending, then those of the skipped pairs.
+//
+// k_worklist: the blocks of the sequence in ascending order whose selection
 // bits put them in P of some head (FP16 keys), in P without FP16 values for
 // some head (INT4 values at FP16-key weights), give FP16 values to some head
 // (the unfinished block, when there is one, ends this list), or leave some
-// head's block outside P and VP (the tail).  The workgroup of kv head 0
-// also writes the sequence's skip flag (rung 4 before paging: a cap of
-// rung 1 or 2 exhausted on some head), which the later passes and the
-// device-initiated paging read without the host's round trip.  Each
-// workgroup of a sequence not skipped also appends its P list to the
-// step's flat FP16-key list (one atomic reservation per pair).
+// head's block outside P and VP (the tail); the prefix of the earlier
+// pairs' counts (the pair's first packed V slot, kept for the FP16 value
+// pass); and the pair's P blocks in the step's flat FP16-key list at the
+// prefix of the earlier pairs' P counts, so that the list is in the packed
+// K order and an entry's index is its block's packed K slot.  Skipped
+// sequences are left out of the flat list; the passes and the
+// device-initiated paging read the skip flags without the host's round trip.
 // ===========================================================================
 template <int G>
-__global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_seq) {
+__global__ __launch_bounds__(256) void k_wlcount(Layout Ly, Step St, int *skip_seq) {
     const int g = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    __shared__ int sh_skip, sh_kbase, kc[4];
+    __shared__ int sh_skip, kc[4], vc[4];
     if (wave == 0) {
         int sk = 0;
         for (int h = lane; h < Ly.Hq; h += 64) sk |= (St.plan[(size_t)n * Ly.Hq + h].flags >> 1) & 1;
@@ -1657,34 +1673,72 @@ __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_
             if (g == 0) skip_seq[n] = any ? 1 : 0;
         }
     }
+    const int N = __builtin_amdgcn_readfirstlane(Ly.len[St.layer * Ly.B + n]) / 64;
+    constexpr uint32_t ALL = (1u << G) - 1u;
+    const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
+    const uint32_t *sel = St.sel + ng * Ly.Nmax;
+    int ck = 0, cv = 0;
+    for (int r0 = 0; r0 < N; r0 += 256) {
+        const int b = r0 + tid;
+        const uint32_t bits = b < N ? sel[b] : 0u;
+        ck += __popcll(__ballot((bits & ALL) != 0));
+        cv += __popcll(__ballot(((bits >> 8) & ALL) != 0));
+    }
+    if (lane == 0) {
+        kc[wave] = ck;
+        vc[wave] = cv;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        St.pcnt[ng] = sh_skip ? 0 : kc[0] + kc[1] + kc[2] + kc[3];
+        St.pcnt[nk + ng] = sh_skip ? 0 : vc[0] + vc[1] + vc[2] + vc[3];
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, const int *skip_seq) {
+    const int g = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int len = __builtin_amdgcn_readfirstlane(Ly.len[St.layer * Ly.B + n]);
     const int N = len / 64;
     constexpr uint32_t ALL = (1u << G) - 1u;
     const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
+    const int npair = St.batch * Ly.Hkv;
     const uint32_t *sel = St.sel + ng * Ly.Nmax;
     uint32_t *lst[WL_KINDS];
 #pragma unroll
     for (int k = 0; k < WL_KINDS; ++k) lst[k] = St.wl + (k * nk + ng) * (size_t)(Ly.Nmax + 1);
     __shared__ int wc[WL_KINDS][4];
-    int base[WL_KINDS] = {};
-    const uint64_t below = (1ull << lane) - 1ull;
-    // the pair's place in the flat FP16-key list
+    __shared__ int pk[4], pv[4], tk[4];
+    // prefixes of the earlier pairs' counts, and the total of P blocks
     {
-        int cnt = 0;
-        for (int r0 = 0; r0 < N; r0 += 256) {
-            const int b = r0 + tid;
-            cnt += __popcll(__ballot(b < N && (sel[b] & ALL) != 0));
+        int ak = 0, av = 0, at = 0;
+        for (int i = tid; i < npair; i += 256) {
+            const int c = St.pcnt[i];
+            at += c;
+            if (i < (int)ng) {
+                ak += c;
+                av += St.pcnt[nk + i];
+            }
         }
-        if (lane == 0) kc[wave] = cnt;
-        __syncthreads();
-        if (tid == 0) {
-            const int tot = kc[0] + kc[1] + kc[2] + kc[3];
-            sh_kbase = !sh_skip && tot > 0 ? atomicAdd(St.kcount, tot) : 0;
+        ak = wave_sum_i32_dpp(ak);
+        av = wave_sum_i32_dpp(av);
+        at = wave_sum_i32_dpp(at);
+        if (lane == 0) {
+            pk[wave] = ak;
+            pv[wave] = av;
+            tk[wave] = at;
         }
         __syncthreads();
     }
-    const bool kflat = !sh_skip;
-    const int kbase = sh_kbase;
+    const int kpref = pk[0] + pk[1] + pk[2] + pk[3];
+    if (tid == 0) {
+        St.vpref[ng] = pv[0] + pv[1] + pv[2] + pv[3];
+        if (ng == 0) *St.kcount = tk[0] + tk[1] + tk[2] + tk[3];
+    }
+    const bool kflat = skip_seq[n] == 0;
+    int base[WL_KINDS] = {};
+    const uint64_t below = (1ull << lane) - 1ull;
     for (int r0 = 0; r0 < N; r0 += 256) {
         const int b = r0 + tid;
         const uint32_t bits = b < N ? sel[b] : 0u;
@@ -1704,9 +1758,10 @@ __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, int *skip_
                 off += w < wave ? wc[k][w] : 0;
                 tot += wc[k][w];
             }
-            if (f[k]) lst[k][off + __popcll(bal[k] & below)] = (uint32_t)b;
+            const int pos = off + __popcll(bal[k] & below);
+            if (f[k]) lst[k][pos] = (uint32_t)b;
             if (k == WL_KEYS && kflat && f[k])
-                St.klist[kbase + off + __popcll(bal[k] & below)] = make_uint2((uint32_t)ng, (uint32_t)b | (pm << 24));
+                St.klist[kpref + pos] = make_uint2((uint32_t)ng, (uint32_t)b | (pm << 24));
             base[k] += tot;
         }
         __syncthreads();
@@ -2068,8 +2123,9 @@ __global__ __launch_bounds__(256) void k_dense(DenseSrc S) {
             kb = S.kp + ((size_t)n * S.Hkv + g) * 64 * D;
             vb = S.vp + ((size_t)n * S.Hkv + g) * 64 * D;
         } else {
-            kb = S.k + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
-            vb = S.v + (((size_t)n * S.Hkv + g) * S.nstride + b) * 64 * D;
+            const size_t ix = ((size_t)n * S.Hkv + g) * S.nstride + b;
+            kb = S.k + (S.kmap ? (size_t)S.kmap[ix] : ix) * 64 * D;
+            vb = S.v + (S.vmap ? (size_t)S.vmap[ix] : ix) * 64 * D;
         }
         uint4 kv[D / 8];
 #pragma unroll
@@ -2190,8 +2246,12 @@ hipError_t launch_gather(const Layout &Ly, const Step &St, const int *skip_seq, 
 hipError_t launch_worklist(const Layout &Ly, const Step &St, int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
         (void)D;
-        hipLaunchKernelGGL((k_worklist<decltype(G)::value>), dim3(Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St,
+        hipLaunchKernelGGL((k_wlcount<decltype(G)::value>), dim3(Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St,
                            skip_seq);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_worklist<decltype(G)::value>), dim3(Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St,
+                           (const int *)skip_seq);
         return hipGetLastError();
     });
 }

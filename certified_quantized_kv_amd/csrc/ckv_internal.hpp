@@ -103,11 +103,19 @@ struct Step {
     uint32_t *wl;
     int *wcnt;
     // The FP16-key pass's entries of the whole step as one list: (pair
-    // n * Hkv + g, block | P heads << 24), pairs appended by the worklist
-    // kernel in any order (a pair's entries ascending), kcount entries
-    // (zeroed by the selection kernel); skipped sequences are left out.
+    // n * Hkv + g, block | P heads << 24), pair by pair, a pair's entries
+    // ascending (the packed K order), kcount entries; skipped sequences are
+    // left out.  pcnt: [2][B * Hkv] the pairs' P and FP16-value block counts
+    // (0 when skipped); vpref: [B * Hkv] a pair's first packed V slot.
     uint2 *klist;
     int *kcount;
+    int *pcnt, *vpref;
+    // 1: the step's FP16 blocks are in the packed staging areas (staged
+    // paging of a layer without the persistent FP16 cache): a P block's K
+    // is at packed slot = its index in klist, a VP block's V at vpref of
+    // its pair + its index in the pair's FP16-value list.  0: the staging
+    // areas are indexed by (pair, block).
+    int packed;
     float *out;             // [batch][Hq][d]
     // profiling: when not null, the kernel launched with this step stamps
     // its execution span here (KernelClock: CLK_SLOTS start slots, then
@@ -126,6 +134,9 @@ struct DenseSrc {
     const int *len;
     int len_all;
     size_t nstride;
+    // packed staging: block (pair, b) at slot kmap / vmap[pair * nstride + b]
+    // of k / v (null: at pair * nstride + b)
+    const uint32_t *kmap, *vmap;
     const uint32_t *mask;       // [B][Hkv] q heads of the group to compute (null: all)
     const uint16_t *q;
     float sm;
