@@ -1402,71 +1402,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     values_pass<D, G, VP_FP16, false>(Ly, St, skip_seq);
 }
 
-constexpr int KEYS_PW = 4;             // list entries per wave of the FP16-key pass, at most
-constexpr int KEYS_MAXE = 4 * KEYS_PW;  // list entries per workgroup, at most
-
 // ===========================================================================
 // K4a (keys): FP16-key scores of the P blocks from the staging area [Meth-3
 // rank-consistency check], one wave per block, lane = token: FP64 fma chain
 // over c = 0 .. D-1 with one rounding to FP32 after the scale (the decision
 // arithmetic of the rank check), the block's FP16-side max and mass (64-leaf
 // tree of exp_c), and the scores for the value pass.  q in FP64 comes from qd
-// through uniform scalar loads.  The step's flat P list (all pairs) is
-// split evenly over the workgroups (one round of resident workgroups when
-// it has at most KEYS_MAXE entries each), at most KEYS_PW entries per wave;
-// a block is loaded as two halves of D/2 channels, three halves in registers
-// (two in flight while the chain runs over the third), which keeps the
-// registers at four waves per SIMD.
+// through uniform scalar loads.  Wave w of workgroup x takes entry 4x + w of
+// the step's flat P list; it requests the entry and the list's count
+// together (the entry through a buffer resource, so an index past the list
+// reads zeros), then both halves of its block (D/2 channels each) before
+// any arithmetic: many short waves that ask for all their data at once keep
+// the memory system full, and the registers (two halves) allow five waves
+// per SIMD.  The results are stored after the last load.
 // ===========================================================================
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *skip_seq,
                                                 const double *qd) {
     KernelClock kc(St.clk);
+    (void)skip_seq;  // skipped sequences are not in the flat list
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     constexpr uint32_t ALL = (1u << G) - 1u;
-    __shared__ uint32_t sbits[KEYS_MAXE], sblk[KEYS_MAXE];
-    __shared__ int sng[KEYS_MAXE];
-    __shared__ float sres[4][KEYS_PW][G][64];
-    __shared__ float2 sml[4][KEYS_PW][G];
-    (void)skip_seq;  // skipped sequences are not in the flat list
-    // this workgroup's share of the step's flat FP16-key list: one load for
-    // the count, one for the entries, before the first block request
+    const int e = blockIdx.x * 4 + wave;
+    const size_t cap = (size_t)Ly.B * Ly.Hkv * Ly.Nmax;  // entries the list can hold
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(St.klist, (uint32_t)min(cap * 8, (size_t)0xFFFFFFF0u));
+    const uint2 ent = rsrc_load8(rl, (uint32_t)e * 8u);
     const int total = __builtin_amdgcn_readfirstlane(*St.kcount);
-    const int e0 = (int)((long long)blockIdx.x * total / gridDim.x);
-    const int ne = min((int)((long long)(blockIdx.x + 1) * total / gridDim.x) - e0, KEYS_MAXE);
-    if (ne <= 0) return;
-    for (int i = threadIdx.x; i < ne; i += 256) {
-        const uint2 e = St.klist[e0 + i];
-        sng[i] = (int)e.x;
-        sblk[i] = e.y & 0xFFFFFFu;
-        sbits[i] = e.y >> 24;
-    }
-    __syncthreads();
+    if (e >= total) return;  // no barrier follows
+    const int ng = (int)__builtin_amdgcn_readfirstlane(ent.x);
+    const int b = (int)(__builtin_amdgcn_readfirstlane(ent.y) & 0xFFFFFFu);
+    const uint32_t pm = (__builtin_amdgcn_readfirstlane(ent.y) >> 24) & ALL;
     // q as [D][G] FP64, read through the constant address space (qd is not
     // written during this kernel): the loads are scalar
     typedef const __attribute__((address_space(4))) double cdouble;
     const size_t NS64 = (size_t)St.NS * 64;
-    auto pmask = [&](int i) { return __builtin_amdgcn_readfirstlane(sbits[i]) & ALL; };
-    auto blk = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sblk[i]); };
-    auto pair = [&](int i) { return (int)__builtin_amdgcn_readfirstlane(sng[i < ne ? i : 0]); };
-    // each pair's staging area as a buffer resource: entries past the share
-    // load zeros from nowhere, so every path requests the same loads and the
-    // waits before each use stay exact
     constexpr uint32_t BLKB = 64 * D * 2;
     constexpr int HC = D / 16;  // 16-byte chunks per lane in half a block
     using Half = uint4[HC];
-    auto issue = [&](int i, int h, Half &kr) {
-        const int ic = i < ne ? i : 0;  // in-range share index on every path
-        // the block's K: packed slot e0 + ic (the list is in packed order), or
-        // (pair, block) in the staging area
-        const size_t slot = St.packed ? (size_t)(e0 + ic) : (size_t)pair(ic) * Ly.Nmax + (size_t)blk(ic);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(St.stage_k + slot * 64 * D, BLKB);
-        const uint32_t off = (i < ne ? 0u : RSRC_OOB) + lane * 16 + h * HC * 1024;
+    // the block's K: packed slot e (the list is in packed order), or (pair,
+    // block) in the staging area
+    const size_t slot = St.packed ? (size_t)e : (size_t)ng * Ly.Nmax + (size_t)b;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(St.stage_k + slot * 64 * D, BLKB);
+    auto issue = [&](int h, Half &kr) {
 #pragma unroll
-        for (int ch = 0; ch < HC; ++ch) kr[ch] = rsrc_load16(rs, off + ch * 1024);
+        for (int ch = 0; ch < HC; ++ch) kr[ch] = rsrc_load16(rs, lane * 16 + h * HC * 1024 + ch * 1024);
     };
-    // FP64 chain over the channels of half h for the G heads, q of pair ng
-    auto chain = [&](const Half &kr, int h, int ng, double (&a)[G]) {
+    // FP64 chain over the channels of half h for the G heads
+    auto chain = [&](const Half &kr, int h, double (&a)[G]) {
         int qoff = 0;
         asm volatile("" : "+s"(qoff));  // opaque zero: keeps the q loads in the loop
         // q in groups of 16 doubles (CS channels x G heads, two scalar loads);
@@ -1501,88 +1483,27 @@ __global__ __launch_bounds__(256) void k_keys16(Layout Ly, Step St, const int *s
             for (int i = 0; i < QN; ++i) qc[i] = qn[i];
         }
     };
-    // scores, block max and mass of the heads of P, kept in LDS until the
-    // loads are done: a global store between the loads would make every
-    // wait for a load drain all outstanding requests (stores and loads
-    // share one counter and stores may finish out of order)
-    auto store = [&](int i, int t, const double (&a)[G]) {
-        const uint32_t pm = pmask(i);
-#pragma unroll
-        for (int jj = 0; jj < G; ++jj) {
-            if (!(pm & (1u << jj))) continue;
-            const float s = (float)(a[jj] * (double)St.sm);
-            sres[wave][t][jj][lane] = s;
-            const float mx = wave_max_dpp(s);
-            const float l_ = tree64_f32_dpp(exp_c(s - mx));
-            // every lane writes the same pair (no lane-divergent branch
-            // between the loads: its exec-mask skips would add paths that
-            // bypass the next requests, and the waits would have to assume
-            // them)
-            sml[wave][t][jj] = make_float2(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_), 0)));
-        }
-    };
-    // the wave's entries wave + 4t, t < KEYS_PW (past the share: zeros from
-    // nowhere, no FMAs, results not kept); halves in X, Y, Z in the order
-    // E0h0 E0h1 E1h0 E1h1 E2h0 E2h1 E3h0 E3h1, each buffer refilled as soon
-    // as its half is used, every request on every path
-    static_assert(KEYS_PW == 4, "the schedule below is written for four entries per wave");
-    const int nw = ne > wave ? min((ne - wave + 3) / 4, KEYS_PW) : 0;
-    const int E0 = wave, E1 = wave + 4, E2 = wave + 8, E3 = wave + 12;
-    if (nw == 0) return;  // no barrier follows
-    Half X, Y, Z;
-    double a[G];
-    auto zero = [&]() {
-#pragma unroll
-        for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
-    };
-    issue(E0, 0, X);
+    Half X, Y;
+    issue(0, X);
     __builtin_amdgcn_sched_barrier(0);  // requests in this order (the waits count on it)
-    issue(E0, 1, Y);
+    issue(1, Y);
     __builtin_amdgcn_sched_barrier(0);
-    issue(E1, 0, Z);
-    zero();
-    chain(X, 0, pair(E0), a);
-    issue(E1, 1, X);
-    chain(Y, 1, pair(E0), a);
-    issue(E2, 0, Y);
-    store(E0, 0, a);
-    if (nw > 1) {
-        zero();
-        chain(Z, 0, pair(E1), a);
-    }
-    issue(E2, 1, Z);
-    if (nw > 1) {
-        chain(X, 1, pair(E1), a);
-        store(E1, 1, a);
-    }
-    issue(E3, 0, X);
-    if (nw > 2) {
-        zero();
-        chain(Y, 0, pair(E2), a);
-    }
-    issue(E3, 1, Y);
-    if (nw > 2) {
-        chain(Z, 1, pair(E2), a);
-        store(E2, 2, a);
-    }
-    if (nw > 3) {
-        zero();
-        chain(X, 0, pair(E3), a);
-        chain(Y, 1, pair(E3), a);
-        store(E3, 3, a);
-    }
-    // the wave's results to global memory
-    for (int t = 0; t < nw; ++t) {
-        const int i = wave + 4 * t, b = blk(i), ng = pair(i);
-        const int n = ng / Ly.Hkv, g = ng - n * Ly.Hkv;
-        const uint32_t pm = pmask(i);
+    double a[G];
 #pragma unroll
-        for (int jj = 0; jj < G; ++jj) {
-            if (!(pm & (1u << jj))) continue;
-            const int h = g * G + jj;
-            St.score16[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane] = sres[wave][t][jj][lane];
-            if (lane == 0) St.st16[((size_t)n * Ly.Hq + h) * Ly.Nmax + b] = sml[wave][t][jj];
-        }
+    for (int jj = 0; jj < G; ++jj) a[jj] = 0.0;
+    chain(X, 0, a);
+    chain(Y, 1, a);
+    // scores, block max and mass of the heads of P
+    const int n = ng / Ly.Hkv, g = ng - n * Ly.Hkv;
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+        if (!(pm & (1u << jj))) continue;
+        const int h = g * G + jj;
+        const float sc = (float)(a[jj] * (double)St.sm);
+        St.score16[(size_t)(n * Ly.Hq + h) * NS64 + (size_t)b * 64 + lane] = sc;
+        const float mx = wave_max_dpp(sc);
+        const float l_ = tree64_f32_dpp(exp_c(sc - mx));
+        if (lane == 0) St.st16[((size_t)n * Ly.Hq + h) * Ly.Nmax + b] = make_float2(mx, l_);
     }
 }
 
@@ -2257,12 +2178,11 @@ hipError_t launch_worklist(const Layout &Ly, const Step &St, int *skip_seq, hipS
 }
 hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        // one round of resident workgroups (four per compute unit at this
-        // kernel's registers), more when the list may exceed KEYS_MAXE
-        // entries per workgroup (at most nb blocks per sequence and kv head)
+        // one wave per entry of the flat list, which holds at most nb
+        // blocks per sequence and kv head
         const long long bound = (long long)St.nb * Ly.Hkv * St.batch;
         if (bound == 0) return hipSuccess;
-        const int nsp = (int)std::max<long long>(4LL * St.ncu, (bound + KEYS_MAXE - 1) / KEYS_MAXE);
+        const int nsp = (int)((bound + 3) / 4);
         hipLaunchKernelGGL((k_keys16<decltype(D)::value, decltype(G)::value>), dim3(nsp), dim3(256), 0, s, Ly, St,
                            skip_seq, (const double *)St.qd);
         return hipGetLastError();
