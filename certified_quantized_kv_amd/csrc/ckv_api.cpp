@@ -1554,15 +1554,19 @@ ckv_status ckv_export_block(ckv_cache *c, int layer, int seq, int g, int b, uint
         for (int t = 0; t < 64; ++t)
             for (int ch = 0; ch < d; ++ch) v_code[t * d + ch] = raw[ch * 64 + t];
     } else if (v_code) {
-        // stored channel-major (byte c * 32 + t / 2, low nibble = even t)
+        // stored [d/32][64][16] (see the tier-1 layout): channel c, token t
+        // at byte (c/32)*1024 + ((t/16)*16 + c%16)*16 + ((c/16)%2)*8 +
+        // (t%16)/2, low nibble = even t
         std::vector<uint8_t> raw((size_t)64 * (d / 2));
         HIPCHK(hipMemcpy(raw.data(), Ly.vq + bi * 64 * (d / 2), raw.size(), hipMemcpyDeviceToHost));
+        auto code = [&](int ch, int t) {
+            const size_t at = (size_t)(ch / 32) * 1024 + (size_t)((t / 16) * 16 + ch % 16) * 16 +
+                              (size_t)((ch / 16) % 2) * 8 + (size_t)((t % 16) / 2);
+            return (raw[at] >> (4 * (t & 1))) & 15;
+        };
         for (int t = 0; t < 64; ++t)
-            for (int ch = 0; ch < d; ch += 2) {
-                const int c0 = (raw[ch * 32 + t / 2] >> (4 * (t & 1))) & 15;
-                const int c1 = (raw[(ch + 1) * 32 + t / 2] >> (4 * (t & 1))) & 15;
-                v_code[t * (d / 2) + ch / 2] = (uint8_t)(c0 | (c1 << 4));
-            }
+            for (int ch = 0; ch < d; ch += 2)
+                v_code[t * (d / 2) + ch / 2] = (uint8_t)(code(ch, t) | (code(ch + 1, t) << 4));
     }
     if (v_s || v_z) {
         // stored group-major [d/32][64]

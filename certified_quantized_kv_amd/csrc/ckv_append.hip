@@ -116,10 +116,14 @@ __global__ __launch_bounds__(128) void k_quant(Layout Ly, int l, int n, int b0, 
         uint8_t *vq = Ly.vq + blk * 64 * D;
         for (int e = tid; e < D * 64; e += 128) vq[e] = cq[e / 64][e % 64];
     } else {
+        // [d/32][64][16]: lane l = 16 tg + i of a channel pair p holds the 8
+        // bytes of channel 32 p + i, then of channel 32 p + 16 + i, for
+        // tokens 16 tg .. 16 tg + 15 (byte j: tokens 2 j, 2 j + 1)
         uint8_t *vq = Ly.vq + blk * 64 * (D / 2);
         for (int e = tid; e < D * 32; e += 128) {
             const int c = e / 32, j = e % 32;
-            vq[c * 32 + j] = (uint8_t)(cq[c][2 * j] | (cq[c][2 * j + 1] << 4));
+            const int pr = c >> 5, hf = (c >> 4) & 1, i = c & 15, tg = j >> 3, jj = j & 7;
+            vq[pr * 1024 + (tg * 16 + i) * 16 + hf * 8 + jj] = (uint8_t)(cq[c][2 * j] | (cq[c][2 * j + 1] << 4));
         }
     }
     if (tid == 0) {

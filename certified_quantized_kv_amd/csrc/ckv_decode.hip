@@ -1024,14 +1024,20 @@ template <int D, int G, bool F, bool V8>
 __device__ __forceinline__ void load_int4(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rm, uint32_t cb,
                                           uint32_t mb, int lane, CodeWord<V8> (&cw)[D / 16], MetaWord<D> &mw) {
     using VA = VAcc<D, G, F>;
-    constexpr int CB = V8 ? 64 : 32;  // code bytes per channel
+    if constexpr (V8) {
+        // [d][64]: channel 16 nt + lane % 16, tokens 16 (lane / 16) .. + 15
 #pragma unroll
-    for (int nt = 0; nt < VA::NT; ++nt) {
-        const uint32_t off = cb + (uint32_t)((16 * nt + (lane & 15)) * CB + (CB / 4) * (lane >> 4));
-        if constexpr (V8)
-            cw[nt] = rsrc_load16(rq, off);
-        else
-            cw[nt] = rsrc_load8(rq, off);
+        for (int nt = 0; nt < VA::NT; ++nt)
+            cw[nt] = rsrc_load16(rq, cb + (uint32_t)((16 * nt + (lane & 15)) * 64 + 16 * (lane >> 4)));
+    } else {
+        // [d/32][64][16]: one 16-byte load per lane and channel pair gives
+        // the codes of column tiles 2 p and 2 p + 1 for the lane's tokens
+#pragma unroll
+        for (int p = 0; p < VA::NT / 2; ++p) {
+            const uint4 w = rsrc_load16(rq, cb + (uint32_t)(p * 1024 + lane * 16));
+            cw[2 * p] = make_uint2(w.x, w.y);
+            cw[2 * p + 1] = make_uint2(w.z, w.w);
+        }
     }
     if constexpr (D == 128) {
         const uint4 w = rsrc_load16(rm, mb + lane * 16);

@@ -7,9 +7,14 @@
 //                              load per lane covers 16 channels of one token
 //                              and a wave's load covers 1 KiB contiguous
 //   kmeta u32 [d]              binary16 scale | binary16 offset << 16
-//   vq    u8  [d][32]          INT4 value codes, channel-major: byte
-//                              c * 32 + t / 2, low nibble = even token t
-//                              (vb = 8: u8 [d][64], byte c * 64 + t)
+//   vq    u8  [d/32][64][16]   INT4 value codes by channel pair p = c / 32
+//                              and lane l = 16 (t / 16) + c % 16: 8 bytes of
+//                              channel 32 p + c % 16, then 8 of channel
+//                              32 p + 16 + c % 16, for tokens 16 (t / 16) ..
+//                              + 15 (byte j: tokens 2 j, 2 j + 1, low nibble
+//                              = even); one 16-byte load per lane and pair,
+//                              1 KiB per wave (vb = 8: u8 [d][64], byte
+//                              c * 64 + t)
 //   vmeta u32 [d/32][64]       per (group, token): binary16 scale |
 //                              binary16 offset << 16
 //   eta   f32                  value-error annotation of the block
