@@ -378,15 +378,6 @@ __device__ __forceinline__ uint64_t block_sum_u(uint64_t v, SelShared &sh) {
     for (int i = 0; i < SEL_T / 64; ++i) r += sh.red_u[i];
     return r;
 }
-__device__ __forceinline__ uint64_t block_or_u(uint64_t v, SelShared &sh) {
-    v = wave_or_u64_dpp(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh.red_u[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint64_t r = 0;
-    for (int i = 0; i < SEL_T / 64; ++i) r |= sh.red_u[i];
-    return r;
-}
 __device__ __forceinline__ int block_sum_i(int v, SelShared &sh) {
     v = wave_sum_i32_dpp(v);
     __syncthreads();

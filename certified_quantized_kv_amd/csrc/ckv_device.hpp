@@ -166,21 +166,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
     for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, 64));
     return v;
 }
-__device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v = fmax(v, __shfl_xor(v, s, 64));
-    return v;
-}
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
-    return v;
-}
-__device__ __forceinline__ int wave_or_i32(int v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v |= __shfl_xor(v, s, 64);
-    return v;
-}
 
 // ---- buffer-resource loads ---------------------------------------------------
 // A buffer resource covers [base, base + bytes); a load at an offset past
@@ -341,9 +326,6 @@ __device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t v, Op op) {
 }
 __device__ __forceinline__ uint64_t wave_sum_u64_dpp(uint64_t v) {
     return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a + b; });
-}
-__device__ __forceinline__ uint64_t wave_or_u64_dpp(uint64_t v) {
-    return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a | b; });
 }
 __device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t v) {
     return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
