@@ -1199,6 +1199,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     // packed slots, in the order the worklist kernel assumes: the pairs not
     // skipped, pair by pair, then the skipped ones (all their blocks)
     Slots slots;
+    std::vector<int> pc4, pc16;  // the promoted passes' list lengths per pair
     for (int pass = 0; pass < 2; ++pass)
         for (int n = 0; n < batch; ++n) {
             const int skip = c->h_skip[n];
@@ -1211,6 +1212,18 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                     const uint32_t w = sl[b];
                     wantk[b] = (uint8_t)(sk | ((w & allg) != 0));
                     wantv[b] = (uint8_t)(sk | (((w >> 8) & allg) != 0));
+                }
+                if (!skip) {
+                    // this pair's entries in the worklist kernel's
+                    // INT4-promoted and FP16-value lists
+                    int c4 = 0, c16 = (c->len[(size_t)layer * cf.max_batch + n] % 64) ? 1 : 0;
+                    for (int b = 0; b < N; ++b) {
+                        const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
+                        c4 += (pm & ~vm) != 0;
+                        c16 += vm != 0;
+                    }
+                    pc4.push_back(c4);
+                    pc16.push_back(c16);
                 }
                 if (prof) {
                     for (int b = 0; b < N; ++b) {
@@ -1241,6 +1254,17 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                 page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
             }
         }
+    {
+        // the promoted passes' entries per split and grid widths
+        long long t4 = 0, t16 = 0;
+        for (int x : pc4) t4 += x;
+        for (int x : pc16) t16 += x;
+        St.t4 = (int)std::min<long long>(VP_TMAX, std::max<long long>(VP_TMIN, (t4 + VP_WG4 - 1) / VP_WG4));
+        St.t16 = (int)std::min<long long>(VP_TMAX, std::max<long long>(VP_TMIN, (t16 + VP_WG16 - 1) / VP_WG16));
+        St.nsp4 = St.nsp16 = 0;
+        for (int x : pc4) St.nsp4 = std::max(St.nsp4, (x + St.t4 - 1) / St.t4);
+        for (int x : pc16) St.nsp16 = std::max(St.nsp16, (x + St.t16 - 1) / St.t16);
+    }
     if (staged) {
         TRY(stage_and_copy(c, *c->stager, clk, cl, s, paged, packed ? stage_k : nullptr, stage_v));
     } else {
@@ -1422,8 +1446,9 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                 t0 = std::min(t0, w[(size_t)i * CLK_PAD]);
                 t1 = std::max(t1, w[(size_t)(CLK_SLOTS + i) * CLK_PAD]);
             }
+            if (t0 == ~0ull && t1 == 0) return CKV_OK;  // not launched this step (nothing to do)
             if (t0 == ~0ull || t1 < t0 || !(c->clk_khz > 0.0))
-                return fail(CKV_EHIP, "kernel clock of a profiled kernel not stamped");
+                return fail(CKV_EHIP, "kernel clock of a profiled kernel stamped incompletely");
             c->pf.ms[ph] += (double)(t1 - t0) / c->clk_khz;
             c->pf.counts[ph] += 1;
             return CKV_OK;

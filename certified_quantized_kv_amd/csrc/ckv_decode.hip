@@ -1217,10 +1217,14 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     // partials the merge reads); every listed block serves some head here.
     int ne, e0;
     {
-        const int nsp = (nslot + St.bps - 1) / St.bps;
         const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
         const int kind = MODE == VP_TAIL ? WL_TAIL : F16 ? WL_FP16 : WL_INT4;
         const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[kind * nk + ng]);
+        // the tail: splits of bps blocks of the context; the promoted passes:
+        // splits by the length of the pair's list (the merge reads as many)
+        const int tpe = F16 ? St.t16 : St.t4;
+        const int nsp = MODE == VP_TAIL ? (nslot + St.bps - 1) / St.bps : (cnt + tpe - 1) / tpe;
+        if (MODE != VP_TAIL && sp >= nsp) return;  // the whole workgroup; no partial is read for it
         e0 = sp < nsp ? (int)((long long)sp * cnt / nsp) : cnt;
         const int e1 = sp < nsp ? (int)((long long)(sp + 1) * cnt / nsp) : cnt;
         ne = min(e1 - e0, MAX_BPS);
@@ -1933,16 +1937,20 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     // merge: tail partials then promoted partials; each wave merges a
     // contiguous quarter (eight loads in flight), the quarters are combined
     // in wave order
-    const int nsp_t = (N + St.bps - 1) / St.bps;            // tail, and promoted INT4 values
-    const int nsp_f = (N + (np ? 1 : 0) + St.bps - 1) / St.bps;  // promoted FP16 values
+    // the splits each pass wrote for this pair: the tail's by context, the
+    // promoted passes' by the length of their lists
+    const size_t ngp = (size_t)n * Ly.Hkv + g, nkp = (size_t)Ly.B * Ly.Hkv;
+    const int nsp_t = (N + St.bps - 1) / St.bps;
+    const int nsp_4 = (St.wcnt[WL_INT4 * nkp + ngp] + St.t4 - 1) / St.t4;
+    const int nsp_f = (St.wcnt[WL_FP16 * nkp + ngp] + St.t16 - 1) / St.t16;
     const float *pt = St.part_tail + hs * St.nsplit_cap * (D + 2);
     const float *p4 = St.part_blk + hs * St.nsplit_cap * (D + 2);
     const float *pf = St.part_blk16 + hs * St.nsplit_cap * (D + 2);
     auto part_ptr = [&](int i) {
         return i < nsp_t ? pt + (size_t)i * (D + 2)
-             : i < 2 * nsp_t ? p4 + (size_t)(i - nsp_t) * (D + 2) : pf + (size_t)(i - 2 * nsp_t) * (D + 2);
+             : i < nsp_t + nsp_4 ? p4 + (size_t)(i - nsp_t) * (D + 2) : pf + (size_t)(i - nsp_t - nsp_4) * (D + 2);
     };
-    const int ntot = 2 * nsp_t + nsp_f;
+    const int ntot = nsp_t + nsp_4 + nsp_f;
     const int per = (ntot + MERGE_T / 64 - 1) / (MERGE_T / 64);
     const int i_lo = wave * per, i_hi = min(ntot, i_lo + per);
     constexpr int BATCH = 8;
@@ -2188,7 +2196,7 @@ hipError_t launch_keys16(const Layout &Ly, const Step &St, const int *skip_seq, 
 
 hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        const int nsp4 = (St.nb + St.bps - 1) / St.bps;
+        const int nsp4 = St.nsp4;
         if (nsp4 > 0 && Ly.vb == 8)
             hipLaunchKernelGGL((k_promoted4<decltype(D)::value, decltype(G)::value, true>),
                                dim3(nsp4, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
@@ -2200,7 +2208,8 @@ hipError_t launch_promoted4(const Layout &Ly, const Step &St, const int *skip_se
 }
 hipError_t launch_promoted16(const Layout &Ly, const Step &St, const int *skip_seq, hipStream_t s) {
     return dispatch(Ly.d, Ly.G, [&](auto D, auto G) {
-        const int nsp = (St.nb + 1 + St.bps - 1) / St.bps;
+        const int nsp = St.nsp16;
+        if (nsp <= 0) return hipSuccess;
         hipLaunchKernelGGL((k_promoted16<decltype(D)::value, decltype(G)::value>),
                            dim3(nsp, Ly.Hkv, St.batch), dim3(256), 0, s, Ly, St, skip_seq);
         return hipGetLastError();

@@ -121,6 +121,10 @@ struct Step {
     // its pair + its index in the pair's FP16-value list.  0: the staging
     // areas are indexed by (pair, block).
     int packed;
+    // the promoted passes' entries per split (t4: INT4 values, t16: FP16
+    // values) and grid widths (the largest split count over the pairs not
+    // skipped), host-computed from the selection
+    int t4, t16, nsp4, nsp16;
     float *out;             // [batch][Hq][d]
     // profiling: when not null, the kernel launched with this step stamps
     // its execution span here (KernelClock: CLK_SLOTS start slots, then
@@ -160,6 +164,14 @@ struct Th {
 int split_blocks(int nb, int Hkv, int batch);
 // The calling thread's last-error message (ckv_api.cpp); returns st.
 int set_error(int st, const char *msg);
+
+// Promoted value passes: a (sequence, kv head) pair with c entries in the
+// pass's list takes ceil(c / t) splits, so a pair's split count follows its
+// list, not its context (the partial buffers hold one split per block).
+// The host picks t per step so that a pass has about VP_WG4 (INT4 values)
+// or VP_WG16 (FP16 values) workgroups over the whole batch (measured best on
+// the 32K x 4 and 128K x 1 layers), t in [VP_TMIN, VP_TMAX].
+constexpr int VP_WG4 = 352, VP_WG16 = 384, VP_TMIN = 4, VP_TMAX = 64;
 
 // Spread slots of the kernel clock: workgroup w stamps slot w % CLK_SLOTS;
 // a slot is one word at the start of its own 128-byte line (CLK_PAD words),
