@@ -1202,8 +1202,11 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     // wave index as a uniform value: the block loop below branches uniformly
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l = St.layer;
-    if (MODE != VP_TAIL && skip_seq[n]) return;
-    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
+    // uniform words through the constant address space (scalar loads,
+    // requested together; none is written during this kernel)
+    typedef const __attribute__((address_space(4))) int cint;
+    if (MODE != VP_TAIL && ((cint *)skip_seq)[n]) return;
+    const int len = ((cint *)Ly.len)[l * Ly.B + n];
     const int N = len / 64, np = len % 64;
     const int nslot = F16 ? N + (np ? 1 : 0) : N;
     constexpr uint32_t ALL = (1u << G) - 1u;
@@ -1219,7 +1222,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     {
         const size_t ng = (size_t)n * Ly.Hkv + g, nk = (size_t)Ly.B * Ly.Hkv;
         const int kind = MODE == VP_TAIL ? WL_TAIL : F16 ? WL_FP16 : WL_INT4;
-        const int cnt = __builtin_amdgcn_readfirstlane(St.wcnt[kind * nk + ng]);
+        const int cnt = ((cint *)St.wcnt)[kind * nk + ng];
         // the tail: splits of bps blocks of the context; the promoted passes:
         // splits by the length of the pair's list (the merge reads as many)
         const int tpe = F16 ? St.t16 : St.t4;
@@ -1229,11 +1232,11 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
         const int e1 = sp < nsp ? (int)((long long)(sp + 1) * cnt / nsp) : cnt;
         ne = min(e1 - e0, MAX_BPS);
         const uint32_t *lst = St.wl + (kind * nk + ng) * (size_t)(Ly.Nmax + 1);
-        // block indices and selection bits of the split: one round trip
+        // block indices and selection bits of the split, one load each
         for (int i = threadIdx.x; i < ne; i += 256) {
-            const uint32_t b = lst[e0 + i];
-            sblk[i] = b;
-            sbits[i] = (int)b < N ? St.sel[selbase + b] : 0u;
+            const uint32_t e = lst[e0 + i];
+            sblk[i] = e & 0xFFFFu;
+            sbits[i] = e >> 16;
         }
     }
     if (threadIdx.x < VA::NG) ksg[threadIdx.x] = F16 ? K16 : Ly.vscale[Ly.seqg(l, n, g) * VA::NG + threadIdx.x];
@@ -1281,7 +1284,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Ly.vq + Ly.blk(l, n, g, 0) * CBLK, (uint32_t)Ly.Nmax * CBLK);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(Ly.vmeta + Ly.blk(l, n, g, 0) * (MBLK / 4), (uint32_t)Ly.Nmax * MBLK);
     // FP16 values: packed slot vpref + list index, or (pair, block)
-    const size_t vbase = St.packed && F16 ? (size_t)__builtin_amdgcn_readfirstlane(St.vpref[selbase / Ly.Nmax]) : 0;
+    const size_t vbase = St.packed && F16 ? (size_t)((cint *)St.vpref)[selbase / Ly.Nmax] : 0;
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(Ly.vpart + Ly.seqg(l, n, g) * 64 * D, FBLK);
     auto issue = [&](const Blk &k, Opd &o) {
         const int b = k.b;
@@ -1543,7 +1546,7 @@ __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *s
         const uint16_t *src = kind == 0 ? t2k : t2v;
         uint16_t *dst = kind == 0 ? stk : stv;
         for (int i = x * 4 + wave; i < cnt; i += W) {
-            const int b = __builtin_amdgcn_readfirstlane(lst[i]);
+            const int b = __builtin_amdgcn_readfirstlane(lst[i]) & 0xFFFF;
             if (b >= N) continue;  // the unfinished block stays on the device
             const uint4 *sp = reinterpret_cast<const uint4 *>(src + Ly.blk(l, n, g, b) * 64 * D);
             uint4 *dp = reinterpret_cast<uint4 *>(dst + (ng * Ly.Nmax + b) * 64 * D);
@@ -1569,7 +1572,8 @@ __global__ __launch_bounds__(256) void k_gather(Layout Ly, Step St, const int *s
 // packed staging areas of staged paging: the K (V) blocks of the pairs not
 // skipped, pair by pair and ascending, then those of the skipped pairs.
 //
-// k_worklist: the blocks of the sequence in ascending order whose selection
+// k_worklist: the blocks of the sequence in ascending order (an entry is
+// the block index | its selection bits << 16) whose selection
 // bits put them in P of some head (FP16 keys), in P without FP16 values for
 // some head (INT4 values at FP16-key weights), give FP16 values to some head
 // (the unfinished block, when there is one, ends this list), or leave some
@@ -1681,7 +1685,8 @@ __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, const int 
                 tot += wc[k][w];
             }
             const int pos = off + __popcll(bal[k] & below);
-            if (f[k]) lst[k][pos] = (uint32_t)b;
+            // entry: block | selection bits << 16 (P heads, then VP heads)
+            if (f[k]) lst[k][pos] = (uint32_t)b | ((pm | (vm << 8)) << 16);
             if (k == WL_KEYS && kflat && f[k])
                 St.klist[kpref + pos] = make_uint2((uint32_t)ng, (uint32_t)b | (pm << 24));
             base[k] += tot;
@@ -1689,7 +1694,7 @@ __global__ __launch_bounds__(256) void k_worklist(Layout Ly, Step St, const int 
         __syncthreads();
     }
     if (tid == 0) {
-        if (len % 64) lst[WL_FP16][base[WL_FP16]++] = (uint32_t)N;
+        if (len % 64) lst[WL_FP16][base[WL_FP16]++] = (uint32_t)N;  // the unfinished block, no bits
 #pragma unroll
         for (int k = 0; k < WL_KINDS; ++k) St.wcnt[k * nk + ng] = base[k];
     }
