@@ -9,6 +9,12 @@ own tier 1 (227 MB at 32K x 4 and at 128K: the 256 MB Infinity Cache cannot
 serve it from a previous step).  Inputs are synthetic (datagen) and resident
 (tier 1 in HBM, tier 2 in pinned host memory) before the timed region.
 
+Order: the headline layer-steps of every workload (each in a cache of its
+own), then the comparison lines of the first two workloads (device paging,
+run copies, threshold variants, cache configurations, decode loops, the
+dense comparator; fresh caches), then the CPU oracle baseline, so that no
+comparison line's allocations or the oracle's threads perturb a headline.
+
 Prints one JSON line.  `value` = KV tokens (batch x context) per second per
 layer-step of the first workload (the 32K x 4 LLaMA-3.1-8B-shaped layer by
 default); the 128K workload's figures are in `other_workloads`.  `roofline`
@@ -100,7 +106,7 @@ def cpu_info():
     return model, os.cpu_count(), usable
 
 
-def run_workload(name, args, cpu_baseline, decode_steps=0, extras=False):
+def run_workload(name, args, decode_steps=0, extras=False):
     import numpy as np
     import torch
 
@@ -123,7 +129,6 @@ def run_workload(name, args, cpu_baseline, decode_steps=0, extras=False):
     qs = []
     n_dense = 0 if (args.no_dense or not extras) else min(L, 4)
     dense_kv = []
-    sample = None
     for l in range(L):
         t1 = time.time()
         lay = datagen.make_layer(name, l)
@@ -134,8 +139,6 @@ def run_workload(name, args, cpu_baseline, decode_steps=0, extras=False):
             kb, vb = block_layout(lay.k, lay.v)
             dense_kv.append((torch.from_numpy(kb.view(np.float16)).to(dev),
                              torch.from_numpy(vb.view(np.float16)).to(dev)))
-        if l == 0 and cpu_baseline:
-            sample = (lay.k[:1].copy(), lay.v[:1].copy(), lay.q[:1].copy(), lay.sm)
         if l % 8 == 0 or l == L - 1:
             log(f"layer {l} generated and appended in {time.time() - t1:.1f}s")
     sm = cfg["sm"]
@@ -238,8 +241,8 @@ def run_workload(name, args, cpu_baseline, decode_steps=0, extras=False):
         "config": {"workload": name, "batch": B, "context": T, "layers": L, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": d, "tau_cov": th["tau_cov"], "k_tol": th["k_tol"],
                    "v_tol": th["v_tol"], "rank_tol": th["rank_tol"],
-                   "paging": "staged, %d host threads" % (args.staged_threads if args.staged_threads >= 0 else 4)
-                   if args.staged_threads != 0 else "runs"},
+                   "paging": "staged, %d host threads" % prof["staged_threads"]
+                   if prof["staged_threads"] > 0 else "runs"},
     }
 
     if extras:
@@ -248,29 +251,38 @@ def run_workload(name, args, cpu_baseline, decode_steps=0, extras=False):
     cache.close()
     del dense_kv
 
-    if sample is not None:
-        # the CPU oracle on one sequence of layer 0 (a full layer-step of that
-        # sequence: every head, scoring through outputs), on one thread and on
-        # every core this process may use (its heads run on OpenMP threads)
-        import oracle
-        k1, v1, q1, sm1 = sample
-        model, ncpu, usable = cpu_info()
-        runs = {}
-        for thr in (1, usable):
-            oracle.set_threads(thr)
-            t1 = time.perf_counter()
-            oracle.certified_decode(k1, v1, q1, oracle.default_thresholds(sm1), trace=False)
-            runs[thr] = time.perf_counter() - t1
-            log(f"cpu baseline: {runs[thr]:.2f}s for the sample on {thr} thread(s)")
-        oracle.set_threads(usable)
-        rec["cpu_baseline"] = {
-            "value": round(T / runs[1], 1), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{name} layer 0, sequence 0 of {B}: one full layer-step of one sequence "
-                      f"({T} tokens, {Hq} q heads), {runs[1]:.1f} s on one thread",
-            "all_cores": {"value": round(T / runs[usable], 1), "cores": usable,
-                          "seconds": round(runs[usable], 2)},
-            "cpu_model": model, "nproc": ncpu, "usable_cores": usable}
     return rec
+
+
+def cpu_baseline(name):
+    """The CPU oracle on one sequence of layer 0 of workload `name` (a full
+    layer-step of that sequence: every head, scoring through outputs), on one
+    thread and on every core this process may use (its heads run on OpenMP
+    threads).  Run after every GPU measurement: the oracle's threads must not
+    compete with the paging threads."""
+    import datagen
+    import oracle
+    cfg = datagen.CONFIGS[name]
+    B, T, Hq = cfg["B"], cfg["T"], cfg["Hq"]
+    lay = datagen.make_layer(name, 0)
+    k1, v1, q1, sm1 = lay.k[:1].copy(), lay.v[:1].copy(), lay.q[:1].copy(), lay.sm
+    del lay
+    model, ncpu, usable = cpu_info()
+    runs = {}
+    for thr in (1, usable):
+        oracle.set_threads(thr)
+        t1 = time.perf_counter()
+        oracle.certified_decode(k1, v1, q1, oracle.default_thresholds(sm1), trace=False)
+        runs[thr] = time.perf_counter() - t1
+        log(f"cpu baseline: {runs[thr]:.2f}s for the sample on {thr} thread(s)")
+    oracle.set_threads(usable)
+    return {
+        "value": round(T / runs[1], 1), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"{name} layer 0, sequence 0 of {B}: one full layer-step of one sequence "
+                  f"({T} tokens, {Hq} q heads), {runs[1]:.1f} s on one thread",
+        "all_cores": {"value": round(T / runs[usable], 1), "cores": usable,
+                      "seconds": round(runs[usable], 2)},
+        "cpu_model": model, "nproc": ncpu, "usable_cores": usable}
 
 
 def extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B, Hq, Hkv, d, L, cfg,
@@ -309,7 +321,8 @@ def extra_lines(rec, args, name, cache, dense_kv, n_dense, qs, th, out, T, sm, B
 
     # the same layer-steps with the listed blocks copied as runs (one copy
     # per run of blocks, small gaps filled) instead of host-packed chunks
-    staged = args.staged_threads if args.staged_threads >= 0 else 4
+    staged = rec["config"]["paging"]
+    staged = int(staged.split()[1]) if staged.startswith("staged") else 0
     cache.set_staged_paging(0)
     for i in range(min(args.warmup, 4)):
         cache.certified_decode_attention(i % L, qs[i % L], th, out=out)
@@ -534,10 +547,18 @@ def main():
     import torch
 
     names = [w for w in args.workload.split(",") if w]
-    recs = [run_workload(w, args, cpu_baseline=(i == 0 and not args.no_cpu_baseline),
-                         decode_steps=(args.decode_steps if i == 0 and not args.no_extras else 0),
-                         extras=(i < 2 and not args.no_extras))
-            for i, w in enumerate(names)]
+    # the headline layer-steps of every workload first, each in a cache of
+    # its own, then the comparison lines of the first two (another cache
+    # each: they leave large allocations behind), then the CPU oracle
+    recs = [run_workload(w, args) for w in names]
+    if not args.no_extras:
+        for i, w in enumerate(names[:2]):
+            ex = run_workload(w, args, decode_steps=(args.decode_steps if i == 0 else 0), extras=True)
+            for k, v in ex.items():
+                if k not in recs[i]:
+                    recs[i][k] = v
+    if not args.no_cpu_baseline:
+        recs[0]["cpu_baseline"] = cpu_baseline(names[0])
     first = recs[0]
     # achievable HBM rate of a plain streaming kernel (torch's elementwise
     # multiply over 1 GiB: one read and one write of every byte); also the

@@ -46,7 +46,8 @@ class Profile(ctypes.Structure):
                 ("q8_blocks", ctypes.c_uint64), ("tail_blocks", ctypes.c_uint64),
                 ("k16_blocks", ctypes.c_uint64), ("v16_blocks", ctypes.c_uint64),
                 ("int4p_blocks", ctypes.c_uint64), ("dense_blocks", ctypes.c_uint64),
-                ("gather_lead_ms", ctypes.c_double), ("gather_steps", ctypes.c_int)]
+                ("gather_lead_ms", ctypes.c_double), ("gather_steps", ctypes.c_int),
+                ("staged_threads", ctypes.c_int)]
 
 
 PHASES = ["score", "select", "tail", "page", "promoted4", "fallback", "step", "merge", "keys16", "promoted16"]

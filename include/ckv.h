@@ -260,14 +260,16 @@ ckv_status ckv_set_device_paging(ckv_cache *c, int enable);
  * [Meth-1]; the page issues one copy per block), on by default: host
  * threads pack the listed FP16 blocks of a step, and only those, into 4 MiB
  * chunks of a ring in pinned host memory (16 chunks); each chunk crosses the
- * host link in one hipMemcpyAsync on a paging stream and a kernel moves its
- * blocks to their staging slots.  Runs of consecutive listed blocks of at
+ * host link in one hipMemcpyAsync on a paging stream, straight into packed
+ * staging areas in listing order (for a layer with the persistent FP16 cache:
+ * into a device ring slot, and a kernel moves its blocks to their
+ * block-indexed staging slots).  Runs of consecutive listed blocks of at
  * least a chunk's bytes are copied directly, one copy each.  Switched off,
  * the blocks are copied as runs of consecutive blocks, small gaps filled, one
  * copy per run.  The results
  * are identical either way.  threads: 0 switches it off, 1 .. 64 the packing
  * threads (held by the cache until it is destroyed or this is called again;
- * ckv_create starts 4, fewer on a host with fewer CPUs).  The first switch
+ * ckv_create starts min(8, half the host's CPUs), at least 1).  The first switch
  * on (in ckv_create) allocates the ring, about 64 MiB of pinned host and of
  * device memory, kept until ckv_destroy, and reads every page of tier 2 once
  * so that the packing takes no page faults.  Waits for the device to finish.
@@ -308,6 +310,8 @@ typedef struct {
                                selection kernel's last wave end (device
                                clock; the host's round trip is not in it)  */
     int gather_steps;       /* steps that paged by the device                */
+    int staged_threads;     /* the cache's packing threads now (0: staged
+                               paging off)                                   */
 } ckv_profile;
 
 ckv_status ckv_set_profiling(ckv_cache *c, int enable);
