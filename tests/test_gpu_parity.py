@@ -285,6 +285,48 @@ def test_batch_with_some_sequences_at_rung4_before_paging():
     assert list(res.trace["seq_flags"] & 1) == [0, 1, 0, 1]
 
 
+@pytest.mark.parametrize("staged", [True, False])
+def test_batch_with_skipped_sequences_and_rung3_heads(staged):
+    """Rung 4 before paging on sequences 1 and 3 (a small cap) and rung 3 on
+    every head of sequences 0 and 2 (rank_tol < 0, f_layer = 1) in one step:
+    the dense pass then reads the skipped sequences' blocks (all listed at
+    the end of the packed staging areas) and the rung-3 pairs' blocks (those
+    of the first listing and the ones the fallback adds), through the slot
+    maps with staged paging, by (pair, block) with run copies; every
+    intermediate and output against the oracle, two layers in a row."""
+    import certified_quantized_kv_amd as ckv
+    rng = np.random.default_rng(78)
+    B, T, Hq, Hkv, d = 4, 1280 + 37, 8, 4, 64
+    k = rng.standard_normal((B, T, Hkv, d))
+    v = rng.standard_normal((B, T, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    v[0] *= 0.01
+    v[2] *= 0.01
+    q[1] *= 0.02
+    q[3] *= 0.02
+    k, v, q = f16(k), f16(v), f16(q)
+    th = oracle.default_thresholds(1 / np.sqrt(d), v_cap_blocks=2, rank_tol=-1.0, f_layer=1.0)
+    res = oracle.certified_decode(k, v, q, th)
+    assert list(res.trace["seq_flags"] & 1) == [0, 1, 0, 1]
+    assert np.all(res.report["rung_max"][[0, 2]] == 3) and np.all(res.report["rung_max"][[1, 3]] == 4)
+    c = ckv.Cache(2, B, Hq, Hkv, d, T)
+    if not staged:
+        c.set_staged_paging(0)
+    for l in range(2):
+        for n in range(B):
+            c.append_kv(l, n, k[n], v[n])
+    qd = torch.from_numpy(q.view(np.float16)).cuda()
+    for l in range(2):
+        out, rep = c.certified_decode_attention(l, qd, th)
+        torch.cuda.synchronize()
+        for f in ("kstar", "n_v_promoted", "rank_ok", "n_discordant", "rung_max", "rung_mask", "e_key",
+                  "e_val", "tv_bound", "tau_final"):
+            assert np.array_equal(res.report[f], rep[f]), (l, f)
+        o = out.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(o - res.out) <= ATOL + RTOL * np.abs(res.out)), (l, np.abs(o - res.out).max())
+    c.close()
+
+
 def test_mixed_lengths_in_a_batch():
     """Sequences of different lengths in one step (each compared alone)."""
     import certified_quantized_kv_amd as ckv
