@@ -881,22 +881,72 @@ struct Slots {
     uint32_t k = 0, v = 0;
 };
 
+// 16 flag bytes (0 or 1 each) as 16 bits.
+static inline uint32_t flag_bits16(const uint8_t *p) {
+    const __m128i v = _mm_loadu_si128(reinterpret_cast<const __m128i *>(p));
+    return (uint32_t)_mm_movemask_epi8(_mm_sub_epi8(_mm_setzero_si128(), v));
+}
+
 // List the blocks of (n, g) that `want` asks for and are not staged yet:
 // runs of at least a chunk's size as direct copies, the rest for packing.
 // Block-indexed staging (`slot` null): a block's destination is its (pair,
 // block) place, kept in `dst` as an address.  Packed staging: it is the
 // next slot of the area, kept in `dst` as the slot number (and in `map`),
 // so a run takes consecutive slots and packed blocks keep listing order.
+// `need`: scratch of at least (N + 63) / 64 words.
 static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
                         std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage,
                         std::vector<const void *> &src, std::vector<uint64_t> &dst, CopyList &direct,
-                        uint32_t *slot, uint32_t *map) {
+                        uint32_t *slot, uint32_t *map, uint64_t *need) {
     const Layout &Ly = c->Ly;
     const size_t sb = ((size_t)n * Ly.Hkv + g) * Ly.Nmax, bb = c->blk_fp16 * 2;
     const int min_run = (int)((PAGE_CHUNK + bb - 1) / bb);
-    for (int b = next_needed(want, staged.data() + sb, 0, N); b < N;) {
+    uint8_t *st = staged.data() + sb;
+    // the blocks to list as bit masks, 64 blocks a word; a run of min_run
+    // >= 128 blocks covers a whole word, so without a full word every block
+    // goes to the packing list and the runs need not be traced
+    const int nw = (N + 63) / 64;
+    bool full = false;
+    int cnt = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int b0 = 64 * w;
+        uint64_t m = 0;
+        if (b0 + 64 <= N) {
+            for (int k = 0; k < 4; ++k)
+                m |= (uint64_t)(flag_bits16(want + b0 + 16 * k) & ~flag_bits16(st + b0 + 16 * k)) << (16 * k);
+        } else {
+            for (int b = b0; b < N; ++b) m |= (uint64_t)(want[b] && !st[b]) << (b - b0);
+        }
+        need[w] = m;
+        full |= m == ~0ull;
+        cnt += __builtin_popcountll(m);
+    }
+    if (min_run >= 128 && !full) {
+        const size_t k0 = src.size();
+        src.resize(k0 + cnt);
+        dst.resize(k0 + cnt);
+        const void **ps = src.data() + k0;
+        uint64_t *pd = dst.data() + k0;
+        const uint16_t *from = t2 + Ly.blk(layer, n, g, 0) * c->blk_fp16;
+        uint32_t sl = slot ? *slot : 0;
+        for (int w = 0; w < nw; ++w)
+            for (uint64_t m = need[w]; m; m &= m - 1) {
+                const int i = 64 * w + __builtin_ctzll(m);
+                *ps++ = from + (size_t)i * c->blk_fp16;
+                if (slot) {
+                    map[sb + i] = sl;
+                    *pd++ = sl++;
+                } else {
+                    *pd++ = (uint64_t)(uintptr_t)(stage + (sb + i) * c->blk_fp16);
+                }
+                st[i] = 1;
+            }
+        if (slot) *slot = sl;
+        return;
+    }
+    for (int b = next_needed(want, st, 0, N); b < N;) {
         int e = b + 1;
-        while (e < N && want[e] && !staged[sb + e]) ++e;
+        while (e < N && want[e] && !st[e]) ++e;
         if (e - b >= min_run) {
             direct.dst.push_back(stage + (slot ? (size_t)*slot : sb + b) * c->blk_fp16);
             direct.src.push_back((void *)(t2 + Ly.blk(layer, n, g, b) * c->blk_fp16));
@@ -915,8 +965,8 @@ static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint
                 }
             }
         }
-        for (int i = b; i < e; ++i) staged[sb + i] = 1;
-        b = next_needed(want, staged.data() + sb, e, N);
+        for (int i = b; i < e; ++i) st[i] = 1;
+        b = next_needed(want, st, e, N);
     }
 }
 
@@ -1185,6 +1235,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
 
     // rung 4 before paging: a cap exhausted on any head of the sequence
     std::vector<uint8_t> wantk(Ly.Nmax), wantv(Ly.Nmax);
+    std::vector<uint64_t> needw((Ly.Nmax + 63) / 64);
     if (!pers) {
         std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
         std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
@@ -1247,9 +1298,9 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                 if (staged) {
                     Stager &S = *c->stager;
                     list_blocks(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, S.src, S.dst, clk,
-                                packed ? &slots.k : nullptr, c->h_kmap);
+                                packed ? &slots.k : nullptr, c->h_kmap, needw.data());
                     list_blocks(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, S.vsrc, S.vdst, cl,
-                                packed ? &slots.v : nullptr, c->h_vmap);
+                                packed ? &slots.v : nullptr, c->h_vmap, needw.data());
                     continue;
                 }
                 page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, clk);
@@ -1340,9 +1391,9 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                     // the blocks between those already staged: packed
                     Stager &SG = *c->stager;
                     list_blocks(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, SG.src, SG.dst, cl,
-                                packed ? &slots.k : nullptr, c->h_kmap);
+                                packed ? &slots.k : nullptr, c->h_kmap, needw.data());
                     list_blocks(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, SG.vsrc, SG.vdst, clv,
-                                packed ? &slots.v : nullptr, c->h_vmap);
+                                packed ? &slots.v : nullptr, c->h_vmap, needw.data());
                 } else if (m) {
                     page_runs(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, cl);
                     page_runs(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, cl);
