@@ -258,6 +258,10 @@ struct ckv_cache {
     // V gathers
     hipStream_t gstream = nullptr;
     hipEvent_t ev_gk = nullptr, ev_gv = nullptr;
+    // the plans to the host right after the rank check (the fallback's
+    // decisions), on a stream of their own: the paging streams are busy
+    hipStream_t pstream = nullptr;
+    hipEvent_t ev_rank = nullptr, ev_plan = nullptr;
     std::vector<uint16_t *> pstage_k, pstage_v;
     std::vector<std::vector<uint8_t>> pstaged_k, pstaged_v;
     std::vector<int> seq_flags;               // [B] of the last step
@@ -368,9 +372,11 @@ void ckv_destroy(ckv_cache *c) {
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->ev_kside)
         if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl, c->ev_gk, c->ev_gv, c->ev_selk})
+    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl, c->ev_gk, c->ev_gv, c->ev_selk, c->ev_rank,
+                         c->ev_plan})
         if (e) (void)hipEventDestroy(e);
     if (c->gstream) (void)hipStreamDestroy(c->gstream);
+    if (c->pstream) (void)hipStreamDestroy(c->pstream);
     for (hipEvent_t e : c->pev)
         if (e) (void)hipEventDestroy(e);
     if (Stager *S = c->stager) {
@@ -497,6 +503,9 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     HIPCHK(hipEventCreateWithFlags(&c->ev_selk, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_wl, hipEventDisableTiming));
     HIPCHK(hipStreamCreateWithFlags(&c->gstream, hipStreamNonBlocking));
+    HIPCHK(hipStreamCreateWithFlags(&c->pstream, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_rank, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&c->ev_plan, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_gk, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_gv, hipEventDisableTiming));
     {
@@ -986,9 +995,13 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
     S.vdst.clear();
     const size_t nblk = S.src.size();
     S.cstart.clear();
-    // the step's first chunks are 1/8, 1/4 and 1/2 of a full one: the first
-    // copy starts after a short packing time; packed staging also starts a
-    // chunk wherever the slots stop being consecutive (around a direct run)
+    // the step's first chunk is 1/8 of a full one and each next one 1.25x
+    // the last, up to full size: the first copy starts after a short packing
+    // time, and the chunks that the threads start on together become ready
+    // one after another rather than all at once (measured: 2% off the
+    // 128K-token step against 1/8, 1/4, 1/2, then full chunks); packed
+    // staging also starts a chunk wherever the slots stop being consecutive
+    // (around a direct run)
     const bool packed = pk != nullptr;
     auto cut = [&](size_t i0, size_t i1, size_t i, int cap) {
         size_t e = std::min(i1, i + (size_t)cap);
@@ -1001,9 +1014,10 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
         (void)i0;
         return e;
     };
-    for (size_t i = 0, k = 0; i < nk; ++k) {
+    double frac = 0.125;
+    for (size_t i = 0; i < nk; frac *= 1.25) {
         S.cstart.push_back((int)i);
-        i = cut(0, nk, i, k < 3 ? std::max(1, S.per_chunk >> (3 - k)) : S.per_chunk);
+        i = cut(0, nk, i, std::max(1, (int)(S.per_chunk * std::min(1.0, frac))));
     }
     const int nkc = (int)S.cstart.size();
     for (size_t i = nk; i < nblk;) {
@@ -1348,6 +1362,12 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     // reference
     kev(KEV_RANK);
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 1, s));
+    // the plans (the rank check's verdicts) to the host now: the fallback
+    // below pages its blocks while the promoted passes and the merge run
+    HIPCHK(hipEventRecord(c->ev_rank, s));
+    HIPCHK(hipStreamWaitEvent(c->pstream, c->ev_rank, 0));
+    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, c->pstream));
+    HIPCHK(hipEventRecord(c->ev_plan, c->pstream));
     kev(KEV_PROMO4);
     HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
@@ -1356,14 +1376,14 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     kev(KEV_MERGE);
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 2, s));
     St.clk = nullptr;
-    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, s));
-    if (prof) HIPCHK(hipMemcpyAsync(c->h_clk, c->dclk, clk_bytes, hipMemcpyDeviceToHost, s));
-    HIPCHK(hipEventRecord(c->ev_done, s));
-    HIPCHK(hipEventSynchronize(c->ev_done));
+    HIPCHK(hipEventSynchronize(c->ev_plan));
 
     // rungs 3 and 4 [Meth-3]: per-head dense on an inconsistent ranking;
     // the whole layer (per sequence) when more than f_layer of the heads
-    // fell back, or when a cap was exhausted before paging.
+    // fell back, or when a cap was exhausted before paging.  The missing
+    // blocks of the groups concerned are paged behind the step's own (the
+    // link stays busy) and the dense pass runs after the merge, whose
+    // outputs it replaces for those heads.
     std::vector<int> dense((size_t)batch * Hq, 0), r4post(batch, 0);
     bool any_dense = false;
     for (int n = 0; n < batch; ++n) {
@@ -1377,6 +1397,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         }
     }
     if (any_dense) {
+        // timed from where the step's own paging ends on side[0]
         if (prof) HIPCHK(hipEventRecord(E[9], c->side[0]));
         std::vector<uint8_t> all(Ly.Nmax, 1);
         cl.clear();
@@ -1400,6 +1421,11 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                 }
                 if (m && prof) c->pf.dense_blocks += N;
             }
+        }
+        if (gather) {
+            // the device's gathers write the staging area too: these copies
+            // (of the same blocks or others) start after them
+            for (int k = 0; k < NSIDE; ++k) HIPCHK(hipStreamWaitEvent(c->side[k], c->ev_gv, 0));
         }
         if (staged) {
             TRY(stage_and_copy(c, *c->stager, cl, clv, s, paged, packed ? stage_k : nullptr, stage_v));
@@ -1439,9 +1465,10 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         const int nsl = nb + np_any;
         HIPCHK(launch_dense_src(d, G, S, (nsl + S.bps - 1) / S.bps, batch, s));
         if (prof) HIPCHK(hipEventRecord(E[10], s));
-        HIPCHK(hipEventRecord(c->ev_done, s));
-        HIPCHK(hipEventSynchronize(c->ev_done));
     }
+    if (prof) HIPCHK(hipMemcpyAsync(c->h_clk, c->dclk, clk_bytes, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipEventRecord(c->ev_done, s));
+    HIPCHK(hipEventSynchronize(c->ev_done));
 
     // report [Meth-2 bounds per head and step; Meth-3 ladder]
     for (int n = 0; n < batch; ++n)
@@ -1551,6 +1578,7 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
         for (hipStream_t ps : c->side)
             if (ps) (void)hipStreamSynchronize(ps);
         if (c->gstream) (void)hipStreamSynchronize(c->gstream);
+        if (c->pstream) (void)hipStreamSynchronize(c->pstream);
         // blocks listed for paging are marked staged before their copies
         // are issued; after a failed step none of them can be trusted, so
         // the layer's next step pages them again

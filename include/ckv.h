@@ -280,7 +280,10 @@ ckv_status ckv_set_staged_paging(ckv_cache *c, int threads);
 /* Profile of the decode steps since profiling was enabled (enabling resets
  * it).  Phases: 0 scoring pass (K1), 1 selection (K2), 2 tail pass (K3),
  * 3 page-in (the host-to-device copies on the paging streams), 4 promoted
- * value pass over INT4 values (K4a), 5 fallback (paging + dense recompute),
+ * value pass over INT4 values (K4a), 5 fallback (the time it adds: from the
+ * end of the step's own paging on the first paging stream to the end of the
+ * dense recompute; its blocks are paged right behind the step's own, as soon
+ * as the rank check's verdicts reach the host),
  * 6 the whole step on the host wall clock, 7 rank check + merge (K4b, two
  * launches), 8 FP16-key scoring of the promoted blocks (K4a keys),
  * 9 promoted value pass over FP16 values (K4a).  The kernel phases (0, 1,
