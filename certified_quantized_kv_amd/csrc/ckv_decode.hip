@@ -1816,8 +1816,15 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int g = h / G, j = h % G, l = St.layer;
-    if (skip_seq[n]) return;
-    const int len = __builtin_amdgcn_readfirstlane(Ly.len[l * Ly.B + n]);
+    // the uniform words through the constant address space, requested
+    // together (scalar loads; none is written during this kernel): the
+    // skip flag, the length and the promoted passes' list lengths
+    typedef const __attribute__((address_space(4))) int cint;
+    const size_t ngp = (size_t)n * Ly.Hkv + g, nkp = (size_t)Ly.B * Ly.Hkv;
+    const int skip = ((cint *)skip_seq)[n];
+    const int len = ((cint *)Ly.len)[l * Ly.B + n];
+    const int cnt4 = ((cint *)St.wcnt)[WL_INT4 * nkp + ngp], cnt16 = ((cint *)St.wcnt)[WL_FP16 * nkp + ngp];
+    if (skip) return;
     const int N = len / 64, np = len % 64;
     const size_t hs = (size_t)n * Ly.Hq + h;
     const uint32_t *sel = St.sel + ((size_t)n * Ly.Hkv + g) * Ly.Nmax;
@@ -1943,14 +1950,14 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     if (!(part & 2)) return;
 
     // merge: tail partials then promoted partials; each wave merges a
-    // contiguous quarter (eight loads in flight), the quarters are combined
-    // in wave order
+    // contiguous share in one pass (eight partials in flight, the running
+    // maximum raised batch by batch and the sums rescaled to it), the
+    // shares are combined in wave order
     // the splits each pass wrote for this pair: the tail's by context, the
     // promoted passes' by the length of their lists
-    const size_t ngp = (size_t)n * Ly.Hkv + g, nkp = (size_t)Ly.B * Ly.Hkv;
     const int nsp_t = (N + St.bps - 1) / St.bps;
-    const int nsp_4 = (St.wcnt[WL_INT4 * nkp + ngp] + St.t4 - 1) / St.t4;
-    const int nsp_f = (St.wcnt[WL_FP16 * nkp + ngp] + St.t16 - 1) / St.t16;
+    const int nsp_4 = (cnt4 + St.t4 - 1) / St.t4;
+    const int nsp_f = (cnt16 + St.t16 - 1) / St.t16;
     const float *pt = St.part_tail + hs * St.nsplit_cap * (D + 2);
     const float *p4 = St.part_blk + hs * St.nsplit_cap * (D + 2);
     const float *pf = St.part_blk16 + hs * St.nsplit_cap * (D + 2);
@@ -1962,15 +1969,7 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
     const int per = (ntot + MERGE_T / 64 - 1) / (MERGE_T / 64);
     const int i_lo = wave * per, i_hi = min(ntot, i_lo + per);
     constexpr int BATCH = 8;
-    float mx = -INFINITY;
-    for (int i0 = i_lo; i0 < i_hi; i0 += BATCH) {
-        float m[BATCH];
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) m[i] = i0 + i < i_hi ? part_ptr(i0 + i)[0] : -INFINITY;
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) mx = fmaxf(mx, m[i]);
-    }
-    float den = 0.0f, num[CPL];
+    float mx = -INFINITY, den = 0.0f, num[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) num[k] = 0.0f;
     for (int i0 = i_lo; i0 < i_hi; i0 += BATCH) {
@@ -1985,6 +1984,18 @@ __global__ __launch_bounds__(MERGE_T) void k_merge(Layout Ly, Step St, Th th, co
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) a[i][k] = p[2 + lane + 64 * k];
             }
+        }
+        float bm = mx;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) bm = fmaxf(bm, m[i]);
+        if (bm == -INFINITY) continue;  // nothing yet (empty partials)
+        if (bm != mx) {
+            // a larger maximum: the sums so far to its scale (0 before any)
+            const float sc = __expf(mx - bm);
+            den *= sc;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) num[k] *= sc;
+            mx = bm;
         }
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
