@@ -902,8 +902,11 @@ static inline uint32_t flag_bits16(const uint8_t *p) {
 // block) place, kept in `dst` as an address.  Packed staging: it is the
 // next slot of the area, kept in `dst` as the slot number (and in `map`),
 // so a run takes consecutive slots and packed blocks keep listing order.
-// `need`: scratch of at least (N + 63) / 64 words.
-static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint8_t *want,
+// `want`: bit masks, 64 blocks a word, (N + 63) / 64 words, no bit at or
+// past N; `need`: scratch of as many words.  The runs are found with bit
+// operations (first set bit, then the first clear one after it), so the
+// cost is a few operations per run plus the stores of each listed block.
+static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint64_t *want,
                         std::vector<uint8_t> &staged, const uint16_t *t2, uint16_t *stage,
                         std::vector<const void *> &src, std::vector<uint64_t> &dst, CopyList &direct,
                         uint32_t *slot, uint32_t *map, uint64_t *need) {
@@ -911,36 +914,49 @@ static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint
     const size_t sb = ((size_t)n * Ly.Hkv + g) * Ly.Nmax, bb = c->blk_fp16 * 2;
     const int min_run = (int)((PAGE_CHUNK + bb - 1) / bb);
     uint8_t *st = staged.data() + sb;
-    // the blocks to list as bit masks, 64 blocks a word; a run of min_run
-    // >= 128 blocks covers a whole word, so without a full word every block
-    // goes to the packing list and the runs need not be traced
     const int nw = (N + 63) / 64;
-    bool full = false;
     int cnt = 0;
     for (int w = 0; w < nw; ++w) {
         const int b0 = 64 * w;
-        uint64_t m = 0;
+        uint64_t sm = 0;
         if (b0 + 64 <= N) {
-            for (int k = 0; k < 4; ++k)
-                m |= (uint64_t)(flag_bits16(want + b0 + 16 * k) & ~flag_bits16(st + b0 + 16 * k)) << (16 * k);
+            for (int k = 0; k < 4; ++k) sm |= (uint64_t)flag_bits16(st + b0 + 16 * k) << (16 * k);
         } else {
-            for (int b = b0; b < N; ++b) m |= (uint64_t)(want[b] && !st[b]) << (b - b0);
+            for (int b = b0; b < N; ++b) sm |= (uint64_t)(st[b] != 0) << (b - b0);
         }
-        need[w] = m;
-        full |= m == ~0ull;
-        cnt += __builtin_popcountll(m);
+        need[w] = want[w] & ~sm;
+        cnt += __builtin_popcountll(need[w]);
     }
-    if (min_run >= 128 && !full) {
-        const size_t k0 = src.size();
-        src.resize(k0 + cnt);
-        dst.resize(k0 + cnt);
-        const void **ps = src.data() + k0;
-        uint64_t *pd = dst.data() + k0;
-        const uint16_t *from = t2 + Ly.blk(layer, n, g, 0) * c->blk_fp16;
-        uint32_t sl = slot ? *slot : 0;
-        for (int w = 0; w < nw; ++w)
-            for (uint64_t m = need[w]; m; m &= m - 1) {
-                const int i = 64 * w + __builtin_ctzll(m);
+    if (!cnt) return;
+    const size_t k0 = src.size();
+    src.resize(k0 + cnt);
+    dst.resize(k0 + cnt);
+    const void **ps = src.data() + k0;
+    uint64_t *pd = dst.data() + k0;
+    const uint16_t *from = t2 + Ly.blk(layer, n, g, 0) * c->blk_fp16;
+    uint32_t sl = slot ? *slot : 0;
+    int w = 0;
+    uint64_t m = need[0];
+    for (;;) {
+        while (!m && ++w < nw) m = need[w];
+        if (!m) break;
+        const int b = 64 * w + __builtin_ctzll(m);
+        // the run's end: the first block at or after b not needed
+        int we = w;
+        uint64_t x = ~need[w] & (~0ull << (b - 64 * w));
+        while (!x && ++we < nw) x = ~need[we];
+        const int e = x ? std::min(N, 64 * we + __builtin_ctzll(x)) : N;
+        if (e - b >= min_run) {
+            direct.dst.push_back(stage + (slot ? (size_t)sl : sb + b) * c->blk_fp16);
+            direct.src.push_back((void *)(from + (size_t)b * c->blk_fp16));
+            direct.size.push_back((size_t)(e - b) * bb);
+            direct.bytes += (size_t)(e - b) * bb;
+            for (int i = b; i < e; ++i) {
+                if (slot) map[sb + i] = sl++;
+                st[i] = 1;
+            }
+        } else {
+            for (int i = b; i < e; ++i) {
                 *ps++ = from + (size_t)i * c->blk_fp16;
                 if (slot) {
                     map[sb + i] = sl;
@@ -950,33 +966,64 @@ static void list_blocks(ckv_cache *c, int layer, int n, int g, int N, const uint
                 }
                 st[i] = 1;
             }
-        if (slot) *slot = sl;
-        return;
-    }
-    for (int b = next_needed(want, st, 0, N); b < N;) {
-        int e = b + 1;
-        while (e < N && want[e] && !st[e]) ++e;
-        if (e - b >= min_run) {
-            direct.dst.push_back(stage + (slot ? (size_t)*slot : sb + b) * c->blk_fp16);
-            direct.src.push_back((void *)(t2 + Ly.blk(layer, n, g, b) * c->blk_fp16));
-            direct.size.push_back((size_t)(e - b) * bb);
-            direct.bytes += (size_t)(e - b) * bb;
-            if (slot)
-                for (int i = b; i < e; ++i) map[sb + i] = (*slot)++;
-        } else {
-            for (int i = b; i < e; ++i) {
-                src.push_back(t2 + Ly.blk(layer, n, g, i) * c->blk_fp16);
-                if (slot) {
-                    map[sb + i] = *slot;
-                    dst.push_back((*slot)++);
-                } else {
-                    dst.push_back((uint64_t)(uintptr_t)(stage + (sb + i) * c->blk_fp16));
-                }
-            }
         }
-        for (int i = b; i < e; ++i) st[i] = 1;
-        b = next_needed(want, st, e, N);
+        if (e >= N) break;
+        w = e / 64;
+        m = need[w] & (~0ull << (e % 64));
     }
+    src.resize((size_t)(ps - src.data()));
+    dst.resize((size_t)(pd - dst.data()));
+    if (slot) *slot = sl;
+}
+
+// The selection words of one (sequence, kv head), sl[0 .. N), as bit masks
+// of (N + 63) / 64 words (no bit at or past N), four words per SSE step:
+// km blocks in P of some head, vm blocks with FP16 values for some head, im
+// blocks in P of some head that has no FP16 values there, tm blocks with
+// some head outside P and VP (the tail's).
+static void sel_masks(const uint32_t *sl, int N, uint32_t allg, uint64_t *km, uint64_t *vm, uint64_t *im,
+                      uint64_t *tm) {
+    const int nw = (N + 63) / 64;
+    for (int w = 0; w < nw; ++w) km[w] = vm[w] = im[w] = tm[w] = 0;
+    const __m128i A = _mm_set1_epi32((int)allg), Z = _mm_setzero_si128();
+    auto nz4 = [&](__m128i x) {  // lanes not equal to Z, as 4 bits
+        return (uint64_t)(~_mm_movemask_ps(_mm_castsi128_ps(_mm_cmpeq_epi32(x, Z))) & 0xF);
+    };
+    int b = 0;
+    for (; b + 4 <= N; b += 4) {
+        const __m128i x = _mm_loadu_si128(reinterpret_cast<const __m128i *>(sl + b));
+        const __m128i p = _mm_and_si128(x, A), v = _mm_and_si128(_mm_srli_epi32(x, 8), A);
+        const int w = b >> 6, sh = b & 63;
+        km[w] |= nz4(p) << sh;
+        vm[w] |= nz4(v) << sh;
+        im[w] |= nz4(_mm_andnot_si128(v, p)) << sh;
+        tm[w] |= (uint64_t)(~_mm_movemask_ps(_mm_castsi128_ps(_mm_cmpeq_epi32(_mm_or_si128(p, v), A))) & 0xF) << sh;
+    }
+    for (; b < N; ++b) {
+        const uint32_t p = sl[b] & allg, v = (sl[b] >> 8) & allg;
+        const int w = b >> 6, sh = b & 63;
+        km[w] |= (uint64_t)(p != 0) << sh;
+        vm[w] |= (uint64_t)(v != 0) << sh;
+        im[w] |= (uint64_t)((p & ~v) != 0) << sh;
+        tm[w] |= (uint64_t)((p | v) != allg) << sh;
+    }
+}
+
+// Blocks [0, N) as a bit mask.
+static void ones_mask(uint64_t *m, int N) {
+    const int nw = (N + 63) / 64;
+    for (int w = 0; w < nw; ++w) m[w] = 64 * (w + 1) <= N ? ~0ull : (1ull << (N - 64 * w)) - 1ull;
+}
+
+static int popcount_mask(const uint64_t *m, int N) {
+    int c = 0;
+    for (int w = 0; w < (N + 63) / 64; ++w) c += __builtin_popcountll(m[w]);
+    return c;
+}
+
+// A mask as 0 / 1 bytes (the run copies' lists take bytes).
+static void mask_bytes(const uint64_t *m, int N, uint8_t *out) {
+    for (int b = 0; b < N; ++b) out[b] = (uint8_t)((m[b >> 6] >> (b & 63)) & 1);
 }
 
 // Copy the listed blocks: the long K runs and chunks of packed K blocks, then
@@ -1047,6 +1094,8 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
         bytes += vruns.bytes;
     }
     if (S.nchunk > 0 && e == hipSuccess) {
+        // the threads start on chunks 1, 2, ... (waking them before the long
+        // runs are issued made the 32K-token step 1% slower)
         if ((size_t)S.nchunk > S.ready_cap) {
             S.ready_cap = std::max<size_t>(S.nchunk, 2 * S.ready_cap);
             S.ready.reset(new std::atomic<int>[S.ready_cap]);
@@ -1249,7 +1298,8 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
 
     // rung 4 before paging: a cap exhausted on any head of the sequence
     std::vector<uint8_t> wantk(Ly.Nmax), wantv(Ly.Nmax);
-    std::vector<uint64_t> needw((Ly.Nmax + 63) / 64);
+    const int mw = (Ly.Nmax + 63) / 64;
+    std::vector<uint64_t> needw(mw), kmask(mw), vmask(mw), imask(mw), tmask(mw);
     if (!pers) {
         std::fill(c->staged_k.begin(), c->staged_k.end(), 0);
         std::fill(c->staged_v.begin(), c->staged_v.end(), 0);
@@ -1274,49 +1324,44 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
             const int N = c->len[(size_t)layer * cf.max_batch + n] / 64;
             for (int g = 0; g < Hkv; ++g) {
                 const uint32_t *sl = c->h_sel + ((size_t)n * Hkv + g) * Ly.Nmax;
-                const uint8_t sk = skip ? 1 : 0;
-                for (int b = 0; b < N; ++b) {
-                    const uint32_t w = sl[b];
-                    wantk[b] = (uint8_t)(sk | ((w & allg) != 0));
-                    wantv[b] = (uint8_t)(sk | (((w >> 8) & allg) != 0));
-                }
+                sel_masks(sl, N, allg, kmask.data(), vmask.data(), imask.data(), tmask.data());
                 if (!skip) {
                     // this pair's entries in the worklist kernel's
                     // INT4-promoted and FP16-value lists
-                    int c4 = 0, c16 = (c->len[(size_t)layer * cf.max_batch + n] % 64) ? 1 : 0;
-                    for (int b = 0; b < N; ++b) {
-                        const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
-                        c4 += (pm & ~vm) != 0;
-                        c16 += vm != 0;
-                    }
-                    pc4.push_back(c4);
-                    pc16.push_back(c16);
+                    pc4.push_back(popcount_mask(imask.data(), N));
+                    pc16.push_back(popcount_mask(vmask.data(), N) +
+                                   ((c->len[(size_t)layer * cf.max_batch + n] % 64) ? 1 : 0));
                 }
                 if (prof) {
-                    for (int b = 0; b < N; ++b) {
-                        const uint32_t pm = sl[b] & allg, vm = (sl[b] >> 8) & allg;
-                        c->pf.tail_blocks += ((pm | vm) != allg);
-                        if (!skip) {
-                            c->pf.k16_blocks += pm != 0;
-                            c->pf.v16_blocks += vm != 0;
-                            c->pf.int4p_blocks += (pm & ~vm) != 0;
-                        }
+                    c->pf.tail_blocks += popcount_mask(tmask.data(), N);
+                    if (!skip) {
+                        c->pf.k16_blocks += popcount_mask(kmask.data(), N);
+                        c->pf.v16_blocks += popcount_mask(vmask.data(), N);
+                        c->pf.int4p_blocks += popcount_mask(imask.data(), N);
                     }
                     c->pf.q8_blocks += N;
                 }
+                if (skip) {
+                    // every block of a skipped sequence (the dense pass)
+                    ones_mask(kmask.data(), N);
+                    ones_mask(vmask.data(), N);
+                }
                 if (gather && !skip) {
                     // the device copies this (seq, kv head)'s listed blocks itself
-                    for (int b = 0; b < N; ++b) paged += (size_t)(wantk[b] + wantv[b]) * c->blk_fp16 * 2;
+                    paged += (size_t)(popcount_mask(kmask.data(), N) + popcount_mask(vmask.data(), N)) *
+                             c->blk_fp16 * 2;
                     continue;
                 }
                 if (staged) {
                     Stager &S = *c->stager;
-                    list_blocks(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, S.src, S.dst, clk,
+                    list_blocks(c, layer, n, g, N, kmask.data(), staged_k, c->t2k, stage_k, S.src, S.dst, clk,
                                 packed ? &slots.k : nullptr, c->h_kmap, needw.data());
-                    list_blocks(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, S.vsrc, S.vdst, cl,
+                    list_blocks(c, layer, n, g, N, vmask.data(), staged_v, c->t2v, stage_v, S.vsrc, S.vdst, cl,
                                 packed ? &slots.v : nullptr, c->h_vmap, needw.data());
                     continue;
                 }
+                mask_bytes(kmask.data(), N, wantk.data());
+                mask_bytes(vmask.data(), N, wantv.data());
                 page_runs(c, layer, n, g, N, wantk.data(), staged_k, c->t2k, stage_k, clk);
                 page_runs(c, layer, n, g, N, wantv.data(), staged_v, c->t2v, stage_v, cl);
             }
@@ -1411,9 +1456,10 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                 if (m && staged) {
                     // the blocks between those already staged: packed
                     Stager &SG = *c->stager;
-                    list_blocks(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, SG.src, SG.dst, cl,
+                    ones_mask(vmask.data(), N);
+                    list_blocks(c, layer, n, g, N, vmask.data(), staged_k, c->t2k, stage_k, SG.src, SG.dst, cl,
                                 packed ? &slots.k : nullptr, c->h_kmap, needw.data());
-                    list_blocks(c, layer, n, g, N, all.data(), staged_v, c->t2v, stage_v, SG.vsrc, SG.vdst, clv,
+                    list_blocks(c, layer, n, g, N, vmask.data(), staged_v, c->t2v, stage_v, SG.vsrc, SG.vdst, clv,
                                 packed ? &slots.v : nullptr, c->h_vmap, needw.data());
                 } else if (m) {
                     page_runs(c, layer, n, g, N, all.data(), staged_k, c->t2k, stage_k, cl);
