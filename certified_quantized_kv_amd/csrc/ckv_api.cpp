@@ -64,7 +64,8 @@ namespace {
     } while (0)
 
 enum { PH_SCORE, PH_SELECT, PH_TAIL, PH_PAGE, PH_PROMO4, PH_FALLBACK, PH_STEP, PH_MERGE, PH_KEYS, PH_PROMO16, PH_N = 10 };
-enum { KEV_SCORE, KEV_SELECT, KEV_TAIL, KEV_KEYS, KEV_PROMO4, KEV_PROMO16, KEV_RANK, KEV_MERGE, KEV_GATHER, KEV_N };
+enum { KEV_SCORE, KEV_SELECT, KEV_TAIL, KEV_KEYS, KEV_PROMO4, KEV_PROMO16, KEV_RANK, KEV_MERGE, KEV_GATHER, KEV_PROMO16B,
+       KEV_N };
 
 }  // namespace
 
@@ -235,6 +236,9 @@ struct ckv_cache {
     // the per-copy latency of one stream overlaps the others'
     hipStream_t side[NSIDE] = {};
     hipEvent_t ev_side[NSIDE] = {}, ev_kside[NSIDE] = {};
+    // packed staging: the paging streams after the step's second-to-last
+    // chunk (the FP16 value pass starts on the pairs complete by then)
+    hipEvent_t ev_vsplit[NSIDE] = {};
     hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr, ev_selk = nullptr;
     hipEvent_t pev[15] = {};
     // profiling: the execution span of each timed kernel (scoring,
@@ -372,6 +376,8 @@ void ckv_destroy(ckv_cache *c) {
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->ev_kside)
         if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->ev_vsplit)
+        if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl, c->ev_gk, c->ev_gv, c->ev_selk, c->ev_rank,
                          c->ev_plan})
         if (e) (void)hipEventDestroy(e);
@@ -498,6 +504,7 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         HIPCHK(hipStreamCreateWithFlags(&c->side[k], hipStreamNonBlocking));
         HIPCHK(hipEventCreateWithFlags(&c->ev_side[k], hipEventDisableTiming));
         HIPCHK(hipEventCreateWithFlags(&c->ev_kside[k], hipEventDisableTiming));
+        HIPCHK(hipEventCreateWithFlags(&c->ev_vsplit[k], hipEventDisableTiming));
     }
     HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_selk, hipEventDisableTiming));
@@ -1032,9 +1039,12 @@ static void mask_bytes(const uint64_t *m, int N, uint8_t *out) {
 // to the blocks' places.  Packed staging (pk, pv: the K and V areas): a
 // chunk holds consecutive slots and is one copy straight to them.  Once the
 // K side is issued, `s` waits for it (the FP16-key pass needs only K); at
-// the end the paging streams are joined on side[0].
+// the end the paging streams are joined on side[0].  `vsplit` (packed
+// staging, may be null): with two V chunks or more, ev_vsplit is recorded
+// on every paging stream after the second-to-last chunk and *vsplit set to
+// the V slot below which every slot is then issued (0: no such point).
 static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyList &vruns, hipStream_t s,
-                                 size_t &bytes, uint16_t *pk, uint16_t *pv) {
+                                 size_t &bytes, uint16_t *pk, uint16_t *pv, uint32_t *vsplit = nullptr) {
     const size_t nk = S.src.size();
     S.src.insert(S.src.end(), S.vsrc.begin(), S.vsrc.end());
     S.dst.insert(S.dst.end(), S.vdst.begin(), S.vdst.end());
@@ -1073,6 +1083,8 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
     }
     S.nchunk = (int)S.cstart.size();
     S.cstart.push_back((int)nblk);
+    const int csplit = vsplit && packed && S.nchunk - 2 >= nkc ? S.nchunk - 2 : -1;
+    if (vsplit) *vsplit = 0;
     auto kjoin = [&]() -> hipError_t {
         for (int k = 0; k < NSIDE; ++k) {
             hipError_t e = hipEventRecord(c->ev_kside[k], c->side[k]);
@@ -1137,6 +1149,11 @@ static ckv_status stage_and_copy(ckv_cache *c, Stager &S, CopyList &kruns, CopyL
             if (e != hipSuccess) break;
             bytes += cb;
             S.issued.store(ci + 1, std::memory_order_release);
+            if (ci == csplit) {
+                for (int k = 0; k < NSIDE && e == hipSuccess; ++k) e = hipEventRecord(c->ev_vsplit[k], c->side[k]);
+                if (e != hipSuccess) break;
+                *vsplit = (uint32_t)S.dst[S.cstart[ci + 1] - 1] + 1;
+            }
             if (ci + 1 == nkc) {
                 e = kjoin();
                 if (e == hipSuccess && (runs_st = issue_copies(c, vruns, false)) != CKV_OK) e = hipErrorUnknown;
@@ -1196,6 +1213,8 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     St.layer = layer;
     St.batch = batch;
     St.nb = nb;
+    St.p16_lo = 0;
+    St.p16_hi = INT_MAX;
     St.NS = c->NS;
     St.bps = split_blocks(nb, Hkv, batch);
     St.ncu = c->ncu;
@@ -1317,6 +1336,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     // skipped, pair by pair, then the skipped ones (all their blocks)
     Slots slots;
     std::vector<int> pc4, pc16;  // the promoted passes' list lengths per pair
+    std::vector<uint32_t> vend((size_t)batch * Hkv, 0);  // packed: a pair's V slots end here
     for (int pass = 0; pass < 2; ++pass)
         for (int n = 0; n < batch; ++n) {
             const int skip = c->h_skip[n];
@@ -1358,6 +1378,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
                                 packed ? &slots.k : nullptr, c->h_kmap, needw.data());
                     list_blocks(c, layer, n, g, N, vmask.data(), staged_v, c->t2v, stage_v, S.vsrc, S.vdst, cl,
                                 packed ? &slots.v : nullptr, c->h_vmap, needw.data());
+                    if (!skip) vend[(size_t)n * Hkv + g] = slots.v;
                     continue;
                 }
                 mask_bytes(kmask.data(), N, wantk.data());
@@ -1377,8 +1398,10 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         for (int x : pc4) St.nsp4 = std::max(St.nsp4, (x + St.t4 - 1) / St.t4);
         for (int x : pc16) St.nsp16 = std::max(St.nsp16, (x + St.t16 - 1) / St.t16);
     }
+    uint32_t vsplit = 0;
     if (staged) {
-        TRY(stage_and_copy(c, *c->stager, clk, cl, s, paged, packed ? stage_k : nullptr, stage_v));
+        TRY(stage_and_copy(c, *c->stager, clk, cl, s, paged, packed ? stage_k : nullptr, stage_v,
+                           packed ? &vsplit : nullptr));
     } else {
         // K runs first: the FP16-key pass and the INT4 promoted pass need
         // only them and run while the V runs are copied
@@ -1415,9 +1438,33 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     HIPCHK(hipEventRecord(c->ev_plan, c->pstream));
     kev(KEV_PROMO4);
     HIPCHK(launch_promoted4(Ly, St, c->dskip, s));
+    // the FP16 value pass: with packed staging, first the pairs (in listing
+    // order, a prefix of n * Hkv + g) whose V slots were all issued by the
+    // second-to-last chunk, as soon as it has landed; the rest after the
+    // paging (only the last chunk's pairs wait for it)
+    int p16_split = 0;
+    if (vsplit > 0) {
+        p16_split = batch * Hkv;
+        for (int pr = 0; pr < batch * Hkv; ++pr)
+            if (!c->h_skip[pr / Hkv] && vend[pr] > vsplit) {
+                p16_split = pr;
+                break;
+            }
+    }
+    if (p16_split > 0) {
+        for (int k = 0; k < NSIDE; ++k) HIPCHK(hipStreamWaitEvent(s, c->ev_vsplit[k], 0));
+        St.p16_lo = 0;
+        St.p16_hi = p16_split;
+        kev(KEV_PROMO16);
+        HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
+    }
     HIPCHK(hipStreamWaitEvent(s, c->ev_paged, 0));
-    kev(KEV_PROMO16);
-    HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
+    if (p16_split < batch * Hkv) {
+        St.p16_lo = p16_split;
+        St.p16_hi = INT_MAX;
+        kev(p16_split > 0 ? KEV_PROMO16B : KEV_PROMO16);
+        HIPCHK(launch_promoted16(Ly, St, c->dskip, s));
+    }
     kev(KEV_MERGE);
     HIPCHK(launch_merge_impl(Ly, St, T, c->dskip, c->plist, c->keys, 2, s));
     St.clk = nullptr;
@@ -1587,7 +1634,13 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
             TRY(kacc(PH_PROMO4, KEV_PROMO4));
         }
         TRY(acc(PH_PAGE, 5, 6));
-        TRY(kacc(PH_PROMO16, KEV_PROMO16));
+        {
+            // one phase per step, one or two launches (their spans added)
+            const int before = c->pf.counts[PH_PROMO16];
+            TRY(kacc(PH_PROMO16, KEV_PROMO16));
+            TRY(kacc(PH_PROMO16, KEV_PROMO16B));
+            if (c->pf.counts[PH_PROMO16] - before == 2) c->pf.counts[PH_PROMO16] -= 1;
+        }
         TRY(kacc(PH_MERGE, KEV_RANK));
         TRY(kacc(PH_MERGE, KEV_MERGE));
         c->pf.counts[PH_MERGE] -= 1;  // one merge phase per step, two launches

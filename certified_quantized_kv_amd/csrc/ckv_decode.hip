@@ -1209,6 +1209,7 @@ __device__ __forceinline__ void values_pass(const Layout &Ly, const Step &St, co
     // requested together; none is written during this kernel)
     typedef const __attribute__((address_space(4))) int cint;
     if (MODE != VP_TAIL && ((cint *)skip_seq)[n]) return;
+    if (F16 && (n * Ly.Hkv + g < St.p16_lo || n * Ly.Hkv + g >= St.p16_hi)) return;  // another launch's pair
     const int len = ((cint *)Ly.len)[l * Ly.B + n];
     const int N = len / 64, np = len % 64;
     const int nslot = F16 ? N + (np ? 1 : 0) : N;

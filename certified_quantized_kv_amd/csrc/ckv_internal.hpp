@@ -125,6 +125,10 @@ struct Step {
     // values) and grid widths (the largest split count over the pairs not
     // skipped), host-computed from the selection
     int t4, t16, nsp4, nsp16;
+    // the FP16 value pass serves the pairs n * Hkv + g in [p16_lo, p16_hi)
+    // (packed staging runs it in two launches: the pairs whose FP16 values
+    // have landed while the last chunk is still being copied, then the rest)
+    int p16_lo, p16_hi;
     float *out;             // [batch][Hq][d]
     // profiling: when not null, the kernel launched with this step stamps
     // its execution span here (KernelClock: CLK_SLOTS start slots, then

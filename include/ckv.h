@@ -286,7 +286,9 @@ ckv_status ckv_set_staged_paging(ckv_cache *c, int threads);
  * as the rank check's verdicts reach the host),
  * 6 the whole step on the host wall clock, 7 rank check + merge (K4b, two
  * launches), 8 FP16-key scoring of the promoted blocks (K4a keys),
- * 9 promoted value pass over FP16 values (K4a).  The kernel phases (0, 1,
+ * 9 promoted value pass over FP16 values (K4a; with packed staged paging
+ * two launches, the pairs whose FP16 values land before the last chunk and
+ * then the rest, their spans added).  The kernel phases (0, 1,
  * 2, 4, 7, 8, 9) are each kernel's own execution span, its first wave's
  * start to its last wave's end on the device's constant-rate wall clock,
  * stamped by the kernel (a few atomics per workgroup); phases 3 and 5 are
