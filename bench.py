@@ -76,8 +76,10 @@ def block_layout(k, v):
 
 
 def counters_for(kernel, workload):
-    """HBM traffic per dispatch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source (else None)."""
+    """HBM traffic per layer-step (the kernel's dispatches of one step summed,
+    like its algorithmic bytes and kernel-clock time) from a committed
+    rocprofv3 --pmc summary, if it was taken on the current kernel source
+    (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
@@ -86,7 +88,7 @@ def counters_for(kernel, workload):
     src = open(os.path.join(ROOT, "certified_quantized_kv_amd", "csrc", "ckv_decode.hip"), "rb").read()
     if rec.get("source_sha1") != hashlib.sha1(src).hexdigest():
         return None
-    return rec.get("traffic_bytes_per_dispatch")
+    return rec.get("traffic_bytes_per_step", rec.get("traffic_bytes_per_dispatch"))
 
 
 def cpu_info():
