@@ -245,9 +245,11 @@ struct ckv_cache {
     // selection, tail, FP16 keys, INT4 promoted, FP16 promoted, rank check,
     // merge, the K gather of device paging) stamped by the kernel itself on the device's constant-rate
     // clock: KEV_N x CLK_WORDS (CLK_SLOTS start slots, then CLK_SLOTS end
-    // slots, CLK_PAD words apart), reset from h_clk_init before each
-    // profiled step and read back into h_clk
-    unsigned long long *dclk = nullptr, *h_clk = nullptr, *h_clk_init = nullptr;
+    // slots, CLK_PAD words apart), armed from h_clk_init at creation, when
+    // profiling is switched on and after a failed step; a profiled step
+    // ends with a fold of each kernel's slots into its first start and last
+    // end (dclkf, 2 words a kernel, read back into h_clkf), which re-arms them
+    unsigned long long *dclk = nullptr, *h_clk_init = nullptr, *dclkf = nullptr, *h_clkf = nullptr;
     double clk_khz = 0.0;
     std::vector<uint8_t> staged_k, staged_v;  // [B][Hkv][Nmax] of the last step
     // persistent FP16 mirror of layers 0 .. pcache_layers-1: blocks paged in
@@ -367,7 +369,7 @@ void ckv_destroy(ckv_cache *c) {
     for (void *p : {(void *)c->ain_k, (void *)c->ain_v, (void *)c->pk, (void *)c->pv})
         if (p) (void)hipFree(p);
     for (void *p : {(void *)c->t2k, (void *)c->t2v, (void *)c->h_sel, (void *)c->h_mask,
-                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_clk,
+                    (void *)c->h_plan, (void *)c->h_skip, (void *)c->h_len, (void *)c->h_clkf,
                     (void *)c->h_clk_init, (void *)c->h_kmap, (void *)c->h_vmap})
         if (p) (void)hipHostFree(p);
     for (hipStream_t st : c->side)
@@ -528,11 +530,13 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     {
         const size_t nclk = (size_t)KEV_N * CLK_WORDS;
         CTRY(dalloc(c, &c->dclk, nclk));
-        CTRY(halloc(c, &c->h_clk, nclk));
+        CTRY(dalloc(c, &c->dclkf, (size_t)2 * KEV_N));
+        CTRY(halloc(c, &c->h_clkf, (size_t)2 * KEV_N));
         CTRY(halloc(c, &c->h_clk_init, nclk));
         // start slots at the largest value, end slots (and the padding) at 0
         for (size_t i = 0; i < nclk; ++i)
             c->h_clk_init[i] = (i % CLK_WORDS) < (size_t)CLK_SLOTS * CLK_PAD ? ~0ull : 0ull;
+        HIPCHK(hipMemcpy(c->dclk, c->h_clk_init, nclk * sizeof(unsigned long long), hipMemcpyHostToDevice));
         int khz = 0;
         HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device));
         c->clk_khz = khz;
@@ -1274,8 +1278,6 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
 
     hipEvent_t *E = c->pev;
     const bool prof = c->prof;
-    const size_t clk_bytes = sizeof(unsigned long long) * KEV_N * CLK_WORDS;
-    if (prof) HIPCHK(hipMemcpyAsync(c->dclk, c->h_clk_init, clk_bytes, hipMemcpyHostToDevice, s));
     // the next kernel launched with St stamps its span in slot k (profiling)
     auto kev = [&](int k) { St.clk = prof ? c->dclk + (size_t)k * CLK_WORDS : nullptr; };
     // K1: INT8 scoring pass; K2: selection, bounds, rungs 1-2
@@ -1559,7 +1561,11 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         HIPCHK(launch_dense_src(d, G, S, (nsl + S.bps - 1) / S.bps, batch, s));
         if (prof) HIPCHK(hipEventRecord(E[10], s));
     }
-    if (prof) HIPCHK(hipMemcpyAsync(c->h_clk, c->dclk, clk_bytes, hipMemcpyDeviceToHost, s));
+    if (prof) {
+        HIPCHK(launch_clock_fold(c->dclk, c->dclkf, KEV_N, s));
+        HIPCHK(hipMemcpyAsync(c->h_clkf, c->dclkf, sizeof(unsigned long long) * 2 * KEV_N, hipMemcpyDeviceToHost,
+                              s));
+    }
     HIPCHK(hipEventRecord(c->ev_done, s));
     HIPCHK(hipEventSynchronize(c->ev_done));
 
@@ -1613,12 +1619,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         // start to last wave's end (the tail, FP16-key and INT4 promoted
         // passes launch only when the batch has a full block)
         auto kacc = [&](int ph, int k) -> ckv_status {
-            const unsigned long long *w = c->h_clk + (size_t)k * CLK_WORDS;
-            unsigned long long t0 = ~0ull, t1 = 0;
-            for (int i = 0; i < CLK_SLOTS; ++i) {
-                t0 = std::min(t0, w[(size_t)i * CLK_PAD]);
-                t1 = std::max(t1, w[(size_t)(CLK_SLOTS + i) * CLK_PAD]);
-            }
+            const unsigned long long t0 = c->h_clkf[2 * k], t1 = c->h_clkf[2 * k + 1];
             if (t0 == ~0ull && t1 == 0) return CKV_OK;  // not launched this step (nothing to do)
             if (t0 == ~0ull || t1 < t0 || !(c->clk_khz > 0.0))
                 return fail(CKV_EHIP, "kernel clock of a profiled kernel stamped incompletely");
@@ -1646,13 +1647,7 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
         c->pf.counts[PH_MERGE] -= 1;  // one merge phase per step, two launches
         if (gather) {
             // when the device paging started, after the selection ended
-            const unsigned long long *ws = c->h_clk + (size_t)KEV_SELECT * CLK_WORDS;
-            const unsigned long long *wg = c->h_clk + (size_t)KEV_GATHER * CLK_WORDS;
-            unsigned long long sel_end = 0, g0 = ~0ull;
-            for (int i = 0; i < CLK_SLOTS; ++i) {
-                sel_end = std::max(sel_end, ws[(size_t)(CLK_SLOTS + i) * CLK_PAD]);
-                g0 = std::min(g0, wg[(size_t)i * CLK_PAD]);
-            }
+            const unsigned long long sel_end = c->h_clkf[2 * KEV_SELECT + 1], g0 = c->h_clkf[2 * KEV_GATHER];
             if (g0 != ~0ull && sel_end != 0) {
                 c->pf.gather_lead_ms += ((double)g0 - (double)sel_end) / c->clk_khz;
                 c->pf.gather_steps += 1;
@@ -1678,6 +1673,13 @@ ckv_status ckv_certified_decode_attention(ckv_cache *c, int layer, const void *q
             if (ps) (void)hipStreamSynchronize(ps);
         if (c->gstream) (void)hipStreamSynchronize(c->gstream);
         if (c->pstream) (void)hipStreamSynchronize(c->pstream);
+        if (c->prof) {
+            // the step's kernels may have stamped the clock slots without
+            // the fold that re-arms them
+            (void)hipStreamSynchronize((hipStream_t)stream);
+            (void)hipMemcpy(c->dclk, c->h_clk_init, sizeof(unsigned long long) * KEV_N * CLK_WORDS,
+                            hipMemcpyHostToDevice);
+        }
         // blocks listed for paging are marked staged before their copies
         // are issued; after a failed step none of them can be trusted, so
         // the layer's next step pages them again
@@ -1837,6 +1839,12 @@ ckv_status ckv_export_step(ckv_cache *c, int batch, int *np_out, float *score, f
 
 ckv_status ckv_set_profiling(ckv_cache *c, int enable) {
     if (!c) return fail(CKV_EINVAL, "null cache");
+    if (enable) {
+        // the clock slots armed (a failed step may have left stamps)
+        HIPCHK(hipSetDevice(c->cfg.device));
+        HIPCHK(hipMemcpy(c->dclk, c->h_clk_init, sizeof(unsigned long long) * KEV_N * CLK_WORDS,
+                         hipMemcpyHostToDevice));
+    }
     c->prof = enable != 0;
     c->pf = ckv_profile{};
     return CKV_OK;

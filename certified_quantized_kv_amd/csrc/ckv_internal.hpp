@@ -214,5 +214,8 @@ hipError_t launch_merge_impl(const Layout &Ly, const Step &St, const Th &th, con
                              uint32_t *plist, uint64_t *keys, int part, hipStream_t s);
 hipError_t launch_dense_src(int d, int G, const DenseSrc &S, int nsplit, int batch,
                             hipStream_t s);
+// profiling: folds the clock slots of nk timed kernels into 2 nk words and
+// re-arms the slots
+hipError_t launch_clock_fold(unsigned long long *clk, unsigned long long *out, int nk, hipStream_t s);
 
 }  // namespace ckv
