@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libckv.so")
 
-SOURCES = ["ckv_api.cpp", "ckv_append.hip", "ckv_decode.hip", "ckv_noalloc.hip"]
+SOURCES = ["ckv_api.cpp", "ckv_append.hip", "ckv_decode.hip", "ckv_noalloc.hip", "ckv_profile.hip"]
 
 # -ffp-contract=off: the decision arithmetic is a fixed sequence of single
 # IEEE operations (fma only where written).  Packed FP32 instructions are
