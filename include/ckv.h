@@ -294,7 +294,10 @@ ckv_status ckv_set_staged_paging(ckv_cache *c, int threads);
  * stamped by the kernel (a few atomics per workgroup); phases 3 and 5 are
  * timed with HIP events on the streams they run on.  Block counts are what
  * the passes read, summed over steps: a block is one (sequence, kv head,
- * 64 tokens).  Profiling adds two small copies per step. */
+ * 64 tokens).  Profiling adds per step a kernel that folds the clock slots
+ * into one start and one end per timed launch (and re-arms them), a 160-byte
+ * copy back, and a few events.  Enabling it arms the slots and waits for
+ * that copy; CKV_EHIP if it fails. */
 typedef struct {
     double ms[10];          /* accumulated milliseconds per phase            */
     int counts[10];         /* timed occurrences per phase                   */
