@@ -315,7 +315,7 @@ void orc_quant_v_block(int d, const uint16_t *v, uint8_t *code, uint16_t *s, uin
 
 /* ------------------------------------------------------------------------ */
 /* INT8 scoring pass [Meth-3, adaptive top-K selection]                     */
-/* Reading (the page fixes no arithmetic for the "lightweight" INT8 pass):  */
+/* Reading (the page gives no arithmetic for the cheap INT8 first pass):   */
 /* an exact integer dot product of rounded weights.  w_c = q_c s_c is exact */
 /* in FP32; with e = floor(log2 max_c |w_c|) the weights are rounded to     */
 /* integers w~_c = rint(w_c 2^(20-e)), |w~_c| <= 2^21; S_t = sum_c w~_c     */
@@ -372,7 +372,7 @@ void orc_score_f16(int d, const uint16_t *q, const uint16_t *k, int n, float sm,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Per-token score perturbation bound [Meth-2, E_key "bounded by Delta"]    */
+/* Bound Delta on each token's INT8 score error [Meth-2, the E_key term]   */
 /* from the query and the quantization scales (tracked quantities only).    */
 /* With H = sum |q_c| s_c, A = sum |q_c| (|z_c| + 255 s_c) and              */
 /* E_w = 2^(e-21) 255 d (the weight rounding: at most half a unit of         */
