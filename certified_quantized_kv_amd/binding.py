@@ -16,7 +16,7 @@ EXPORTED = ["ckv_create", "ckv_destroy", "ckv_reset_sequence", "ckv_append_kv", 
             "ckv_seq_length", "ckv_last_error", "ckv_export_block", "ckv_export_step",
             "ckv_set_profiling", "ckv_get_profile", "ckv_enable_fp16_cache",
             "ckv_set_device_paging", "ckv_set_staged_paging", "ckv_inject_paging_fault",
-            "ckv_dense_decode_attention_noalloc"]
+            "ckv_dense_decode_attention_noalloc", "ckv_read_probe"]
 
 
 class CkvError(RuntimeError):
@@ -100,6 +100,7 @@ def lib():
         L.ckv_set_device_paging.argtypes = [vp, i32]
         L.ckv_set_staged_paging.argtypes = [vp, i32]
         L.ckv_inject_paging_fault.argtypes = [vp, i32]
+        L.ckv_read_probe.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
         for name in EXPORTED:
             if name not in ("ckv_destroy", "ckv_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -324,6 +325,14 @@ def dense_decode_attention_noalloc(k_blocks, v_blocks, n_tokens, q, sm_scale, n_
         ctypes.c_void_p(q.data_ptr()), B, Hq, int(n_kv_heads), d, float(sm_scale),
         ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
     return out
+
+
+def read_probe(buf, wave_kib, sink, stream=None):
+    """ckv_read_probe: enqueue one streaming read of the CUDA tensor `buf`
+    (its whole storage) in waves of wave_kib KiB; `sink` is a one-word int32
+    CUDA tensor."""
+    _check(lib().ckv_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                int(wave_kib), ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
 
 
 def _torch_cuda():

@@ -325,6 +325,19 @@ typedef struct {
 ckv_status ckv_set_profiling(ckv_cache *c, int enable);
 ckv_status ckv_get_profile(const ckv_cache *c, ckv_profile *p);
 
+/* Measurement aid (not part of the decode step): a streaming read of
+ * `bytes` of device memory at dev_buf, enqueued on `stream` (a hipStream_t;
+ * NULL: the null stream).  Wave w reads wave_kib KiB (4, 8 or 16) at byte
+ * offset w * wave_kib KiB as 16-byte loads per lane, all requested before any
+ * is used: the load shape of the scoring pass (8 KiB of key codes per wave)
+ * and of the FP16-key pass (16 KiB per block).  Timing it over a buffer much
+ * larger than the device's last-level cache gives the read rate these passes
+ * are measured against.  dev_sink: one device word, written only if the fold
+ * of the loaded words takes one particular value (it keeps the loads).  The
+ * caller owns both buffers; bytes must be a positive multiple of wave_kib KiB.
+ * Errors: EINVAL (null pointer, wave_kib, bytes), EHIP (launch failure). */
+ckv_status ckv_read_probe(const void *dev_buf, size_t bytes, int wave_kib, unsigned *dev_sink, void *stream);
+
 /* Fault injection for tests of the error path of a decode step: the host-to-
  * device paging copy issued after `after_copies` further copies (0: the
  * next one) is not issued and reports failure, as a failed hipMemcpyAsync
