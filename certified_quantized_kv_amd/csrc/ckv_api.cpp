@@ -239,7 +239,10 @@ struct ckv_cache {
     // packed staging: the paging streams after the step's second-to-last
     // chunk (the FP16 value pass starts on the pairs complete by then)
     hipEvent_t ev_vsplit[NSIDE] = {};
-    hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr, ev_selk = nullptr;
+    hipEvent_t ev_sel = nullptr, ev_paged = nullptr, ev_done = nullptr;
+    // h_sel and h_plan as device addresses: the selection kernel's words and
+    // plans are stored there by the device (mapped, coherent pinned memory)
+    void *h_sel_dev = nullptr, *h_plan_dev = nullptr;
     hipEvent_t pev[15] = {};
     // profiling: the execution span of each timed kernel (scoring,
     // selection, tail, FP16 keys, INT4 promoted, FP16 promoted, rank check,
@@ -296,12 +299,16 @@ ckv_status dalloc(ckv_cache *c, T **p, size_t count) {
 }
 
 template <class T>
-ckv_status halloc(ckv_cache *c, T **p, size_t count, bool tier2 = false) {
+ckv_status halloc(ckv_cache *c, T **p, size_t count, bool tier2 = false, bool dev_written = false) {
     void *ptr = nullptr;
     size_t bytes = std::max<size_t>(count * sizeof(T), 64);
     // tier 2 is also mapped into the device's address space (read by the
-    // device-initiated paging kernel)
-    hipError_t e = hipHostMalloc(&ptr, bytes, tier2 ? hipHostMallocMapped : hipHostMallocDefault);
+    // device-initiated paging kernel); buffers the device writes for the
+    // host are mapped and coherent (the device's stores reach host memory)
+    const unsigned flags = dev_written ? (hipHostMallocMapped | hipHostMallocCoherent)
+                           : tier2     ? hipHostMallocMapped
+                                       : hipHostMallocDefault;
+    hipError_t e = hipHostMalloc(&ptr, bytes, flags);
     if (e != hipSuccess)
         return fail(CKV_ENOMEM, "hipHostMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
     if (tier2) c->host_bytes += bytes;
@@ -380,7 +387,7 @@ void ckv_destroy(ckv_cache *c) {
         if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->ev_vsplit)
         if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl, c->ev_gk, c->ev_gv, c->ev_selk, c->ev_rank,
+    for (hipEvent_t e : {c->ev_sel, c->ev_paged, c->ev_done, c->ev_wl, c->ev_gk, c->ev_gv, c->ev_rank,
                          c->ev_plan})
         if (e) (void)hipEventDestroy(e);
     if (c->gstream) (void)hipStreamDestroy(c->gstream);
@@ -494,9 +501,9 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
     CTRY(dalloc(c, &c->keys, (size_t)B * Hq * 2 * Nmax));
     CTRY(dalloc(c, &c->dskip, (size_t)B));
     CTRY(dalloc(c, &c->dmask, (size_t)B * Hkv));
-    CTRY(halloc(c, &c->h_sel, sblk));
+    CTRY(halloc(c, &c->h_sel, sblk, false, true));
     CTRY(halloc(c, &c->h_mask, (size_t)B * Hkv));
-    CTRY(halloc(c, &c->h_plan, (size_t)B * Hq));
+    CTRY(halloc(c, &c->h_plan, (size_t)B * Hq, false, true));
     CTRY(halloc(c, &c->h_skip, (size_t)B));
     CTRY(halloc(c, &c->h_len, (size_t)L * B));
     c->len.assign((size_t)L * B, 0);
@@ -509,7 +516,6 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         HIPCHK(hipEventCreateWithFlags(&c->ev_vsplit[k], hipEventDisableTiming));
     }
     HIPCHK(hipEventCreateWithFlags(&c->ev_sel, hipEventDisableTiming));
-    HIPCHK(hipEventCreateWithFlags(&c->ev_selk, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_wl, hipEventDisableTiming));
     HIPCHK(hipStreamCreateWithFlags(&c->gstream, hipStreamNonBlocking));
     HIPCHK(hipStreamCreateWithFlags(&c->pstream, hipStreamNonBlocking));
@@ -523,6 +529,8 @@ ckv_status ckv_create(const ckv_config *cfg, ckv_cache **out) {
         HIPCHK(hipHostGetDevicePointer(&pv, c->t2v, 0));
         c->t2k_dev = static_cast<const uint16_t *>(pk);
         c->t2v_dev = static_cast<const uint16_t *>(pv);
+        HIPCHK(hipHostGetDevicePointer(&c->h_sel_dev, c->h_sel, 0));
+        HIPCHK(hipHostGetDevicePointer(&c->h_plan_dev, c->h_plan, 0));
     }
     HIPCHK(hipEventCreateWithFlags(&c->ev_paged, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming));
@@ -1286,14 +1294,15 @@ ckv_status certified_step(ckv_cache *c, int layer, const void *q, int batch, con
     kev(KEV_SELECT);
     HIPCHK(launch_select(Ly, St, T, s));
     St.clk = nullptr;
-    // page lists and plans to the host (the round trip of the selection), on
-    // a paging stream: the passes below do not wait for these copies
+    // page lists and plans to the host (the round trip of the selection): a
+    // small kernel right behind the selection stores them into mapped host
+    // memory, so the host's wait has no copy on another stream to wait for
+    // (a cross-stream wait and two runtime copies had started ~17 us after
+    // the selection ended); the passes below follow it by a few us
     const size_t selbytes = (size_t)batch * Hkv * Ly.Nmax * sizeof(uint32_t);
-    HIPCHK(hipEventRecord(c->ev_selk, s));
-    HIPCHK(hipStreamWaitEvent(c->side[0], c->ev_selk, 0));
-    HIPCHK(hipMemcpyAsync(c->h_sel, c->sel, selbytes, hipMemcpyDeviceToHost, c->side[0]));
-    HIPCHK(hipMemcpyAsync(c->h_plan, c->plan, sizeof(HeadPlan) * batch * Hq, hipMemcpyDeviceToHost, c->side[0]));
-    HIPCHK(hipEventRecord(c->ev_sel, c->side[0]));
+    HIPCHK(launch_to_host(c->sel, c->h_sel_dev, selbytes, c->plan, c->h_plan_dev,
+                          sizeof(HeadPlan) * batch * Hq, s));
+    HIPCHK(hipEventRecord(c->ev_sel, s));
     // block lists of the value passes and the sequences' skip flags; K3:
     // tail blocks; both overlap the host's page lists and the paging below
     HIPCHK(launch_worklist(Ly, St, c->dskip, s));

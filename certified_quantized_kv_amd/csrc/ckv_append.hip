@@ -302,4 +302,31 @@ hipError_t launch_page_scatter(const uint8_t *chunk, int nblk, int blk_bytes, hi
     return hipGetLastError();
 }
 
+// The selection's words and plans to the host: device stores straight into
+// mapped, coherent pinned memory, on the stream of the kernel that wrote
+// them (the host waits on an event recorded right after this kernel).  One
+// 4-byte word per thread per pass over the two buffers.
+__global__ __launch_bounds__(256) void k_to_host(const uint32_t *__restrict__ a, uint32_t *ha, size_t na,
+                                                 const uint32_t *__restrict__ b, uint32_t *hb, size_t nb) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < na + nb; i += stride) {
+        if (i < na)
+            ha[i] = a[i];
+        else
+            hb[i - na] = b[i - na];
+    }
+}
+
+hipError_t launch_to_host(const void *a, void *ha, size_t abytes, const void *b, void *hb, size_t bbytes,
+                          hipStream_t s) {
+    if (abytes % 4 || bbytes % 4) return hipErrorInvalidValue;
+    const size_t na = abytes / 4, nb = bbytes / 4;
+    if (na + nb == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<size_t>(64, (na + nb + 255) / 256);
+    hipLaunchKernelGGL(k_to_host, dim3(grid), dim3(256), 0, s, static_cast<const uint32_t *>(a),
+                       static_cast<uint32_t *>(ha), na, static_cast<const uint32_t *>(b),
+                       static_cast<uint32_t *>(hb), nb);
+    return hipGetLastError();
+}
+
 }  // namespace ckv

@@ -73,6 +73,7 @@ struct HeadPlan {
     int rank_ok, ndisc;
     uint64_t S;
 };
+static_assert(sizeof(HeadPlan) % 4 == 0, "plans reach the host as 4-byte words");
 
 // Scratch of one decode step; strides use the cache capacity so that any
 // batch size fits.  NS = Nmax + 1 slots per head (the extra one is the
@@ -188,6 +189,10 @@ constexpr int CLK_WORDS = 2 * CLK_SLOTS * CLK_PAD;  // per timed kernel: starts,
 // header bytes of a staged-paging chunk: up to 512 block addresses
 constexpr int PAGE_HDR = 4096;
 hipError_t launch_page_scatter(const uint8_t *chunk, int nblk, int blk_bytes, hipStream_t s);
+// Copy two device buffers (sizes multiples of 4 bytes) into pinned host
+// memory mapped into the device's address space (device addresses ha, hb).
+hipError_t launch_to_host(const void *a, void *ha, size_t abytes, const void *b, void *hb, size_t bbytes,
+                          hipStream_t s);
 hipError_t launch_append_token(const Layout &Ly, int l, int batch, const uint16_t *kin, const uint16_t *vin,
                                hipStream_t s);
 hipError_t launch_pack(const Layout &Ly, int l, int n, const uint16_t *kin, const uint16_t *vin,
