@@ -69,7 +69,7 @@ constexpr int SCORE_W = 4;  // waves per workgroup of the scoring pass
 constexpr int SCORE_BPW_ = SCORE_BPW;  // block slots per wave
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * SCORE_W) __attribute__((amdgpu_waves_per_eu(5))) void k_score(Layout Ly, Step St) {
+__global__ __launch_bounds__(64 * SCORE_W) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 5 : 4))) void k_score(Layout Ly, Step St) {
     KernelClock kc(St.clk);
     constexpr int CPL = D / 64;           // channels per lane (meta, trees)
     constexpr int KS = D / 64;            // MFMA k-steps of 64 channels
