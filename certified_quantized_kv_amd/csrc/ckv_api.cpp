@@ -344,13 +344,15 @@ void fill_failed_reports(ckv_head_report *r, int n) {
 
 }  // namespace
 
-// Blocks per split of the value passes: about 704 four-wave workgroups, so
+// Blocks per split of the value passes: about 768 four-wave workgroups, so
 // that the grid is resident in one round at three waves per SIMD (256 CUs x
-// 4 SIMDs x 3 = 3072 waves); a multiple of 4 in [4, 64].
+// 4 SIMDs x 3 = 3072 waves) and every CU holds three of them (704, rounded to
+// a multiple of 4 blocks, left a quarter of the CUs with two: the tail took
+// 0.6 us longer at 32K x 4 and 128K); in [4, 64].
 int ckv::split_blocks(int nb, int Hkv, int batch) {
     const long units = (long)nb * Hkv * batch;
-    int bps = (int)((units + 703) / 704);
-    bps = std::max(4, std::min(64, (bps + 3) / 4 * 4));
+    int bps = (int)((units + 767) / 768);
+    bps = std::max(4, std::min(64, bps));
     return bps;
 }
 
