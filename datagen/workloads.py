@@ -50,7 +50,7 @@ CONFIGS = {
     #    0: q not flattened, one +6 sigma needle pair, V ~ 3 N(0,1)   -> rung 1
     #    1: kv groups 0-4 (20 of 32 q heads) flat copies, rest as 0   -> rung 3 -> 4
     #    2: kv group 0 (4 q heads) flat copies, rest as 0             -> rung 3
-    #    3: as specified                                               -> see the design doc
+    #    3: as specified: adjacent blocks flip (D ~ 300 of 130K pairs)  -> rung 2
     "stress_32k": dict(cid=5, L=4, B=1, Hq=32, Hkv=8, d=128, T=32768, n_out=6, out_scale=10.0,
                        q_std=1 / math.sqrt(128), sm=1.0, tie_eps=0.004, v_nu=3,
                        flat_heads="all",

@@ -10,7 +10,7 @@
  * Section tags ([Meth-1] ...) refer to the page "Runtime-Certified
  * Bounded-Error Quantized Attention", technical summary; they are listed in
  * ckv_oracle.h.  Where the page leaves a step open, the reading taken is
- * stated at the step; the full list is in the design doc.
+ * stated at the step.
  */
 #include "ckv_oracle.h"
 

@@ -18,8 +18,8 @@
  * Values (outputs, the dense reference, measured errors) are computed in
  * FP64.  Decisions (codes, scores, masses, selected sets, bounds compared
  * with thresholds, verdicts) use a fixed FP32 / FP64 / fixed-point operation
- * sequence; that sequence is spelled out in DESIGN.md ("canonical decision
- * arithmetic") and is the contract the GPU path must meet bit for bit.
+ * sequence, written out at each function below; it is the contract the
+ * GPU path must meet bit for bit.
  */
 #ifndef CKV_ORACLE_H
 #define CKV_ORACLE_H
