@@ -353,6 +353,30 @@ def test_mixed_lengths_in_a_batch():
     c.close()
 
 
+def test_steps_with_fewer_sequences_than_the_cache_holds():
+    """Steps over the first 2, then all 4, then the first 1 of a cache made
+    for 4 sequences: the selection and the plans reach the host for the
+    step's own batch only, and what a larger earlier step left there is
+    never read (every step compared with the oracle on each sequence)."""
+    import certified_quantized_kv_amd as ckv
+    Hq, Hkv, d, T = 8, 2, 128, 1000
+    k, v, q, sm = micro(61, T=T, Hq=Hq, Hkv=Hkv, d=d, B=4, kind="peaked")
+    th = oracle.default_thresholds(sm)
+    c = ckv.Cache(1, 4, Hq, Hkv, d, T)
+    for n in range(4):
+        c.append_kv(0, n, k[n], v[n])
+    for batch in (2, 4, 1):
+        print(f"case batch {batch} of 4", flush=True)
+        out, rep = c.certified_decode_attention(0, torch.from_numpy(q[:batch].view(np.float16)).cuda(), th)
+        out = out.cpu().numpy()
+        res = oracle.certified_decode(k[:batch], v[:batch], q[:batch], th)
+        for f in ("kstar", "n_v_promoted", "rank_ok", "n_discordant", "rung_max", "rung_mask", "e_key",
+                  "e_val", "tv_bound", "tau_final"):
+            assert np.array_equal(rep[f], res.report[f]), (batch, f)
+        assert np.all(np.abs(out - res.out) <= ATOL + RTOL * np.abs(res.out)), batch
+    c.close()
+
+
 def test_deterministic_across_runs():
     L = datagen.make_layer("tiny_1k", 0, T=1000)
     th = oracle.default_thresholds(L.sm)
