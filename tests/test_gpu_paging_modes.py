@@ -117,3 +117,20 @@ def test_device_paging_batch_with_some_sequences_at_rung4_before_paging():
     for f in ("kstar", "n_v_promoted", "rung_max", "rung_mask", "e_key", "e_val", "n_discordant"):
         assert np.array_equal(rep[f], res.report[f]), f
     assert np.all(np.abs(out - res.out) <= ATOL + RTOL * np.abs(res.out))
+
+
+@pytest.mark.parametrize("name,layer", [("stress_32k", 0), ("stress_32k", 1), ("stress_32k", 2),
+                                        ("stress_32k", 3), ("needle_128k", 0)])
+def test_device_paging_full_size(name, layer):
+    """Full-size layers, device paging against host copies, bit for bit
+    (outputs, reports, step intermediates): the stress layers bring every
+    rung (the dense fallback pages whole kv groups after the rank check,
+    layer 1 sends its sequence to rung 4), the 128K layer gathers lists of
+    up to ~2000 blocks per kv head.  The host-copy side is checked against
+    the oracle at full size in test_gpu_parity.py."""
+    print(f"case device paging {name} layer {layer}", flush=True)
+    L = datagen.make_layer(name, layer)
+    th = oracle.default_thresholds(L.sm)
+    out, rep, step = run_both(L.k, L.v, L.q, th)
+    assert np.isfinite(out).all()
+    assert (rep["rung_max"] >= 0).all()
