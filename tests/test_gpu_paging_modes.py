@@ -134,3 +134,35 @@ def test_device_paging_full_size(name, layer):
     out, rep, step = run_both(L.k, L.v, L.q, th)
     assert np.isfinite(out).all()
     assert (rep["rung_max"] >= 0).all()
+
+
+@pytest.mark.parametrize("name,layer", [("stress_32k", 0), ("stress_32k", 1), ("stress_32k", 2),
+                                        ("stress_32k", 3), ("needle_128k", 0)])
+def test_fp16_cache_full_size(name, layer):
+    """Full-size layers with the device-resident FP16 block cache against a
+    cache without it, bit for bit over two steps (the second query is the
+    first with its heads rotated, so it selects other blocks and finds part
+    of them mirrored already)."""
+    import certified_quantized_kv_amd as ckv
+    print(f"case fp16 cache {name} layer {layer}", flush=True)
+    L = datagen.make_layer(name, layer)
+    th = oracle.default_thresholds(L.sm)
+    B, T, Hkv, d = L.k.shape
+    Hq = L.q.shape[1]
+    qs = [L.q, np.roll(L.q, 1, axis=1).copy()]
+    res = []
+    for use_cache in (False, True):
+        c = ckv.Cache(1, B, Hq, Hkv, d, T)
+        if use_cache:
+            assert c.enable_fp16_cache(1 << 34) == 1
+        for n in range(B):
+            c.append_kv(0, n, L.k[n], L.v[n])
+        steps = []
+        for q in qs:
+            out, rep = c.certified_decode_attention(0, torch.from_numpy(q.view(np.float16)).cuda(), th)
+            steps.append((out.cpu().numpy(), rep))
+        res.append(steps)
+        c.close()
+    for s in range(2):
+        assert np.array_equal(res[0][s][0], res[1][s][0]), s
+        assert np.array_equal(res[0][s][1], res[1][s][1]), s
