@@ -331,6 +331,7 @@ def read_probe(buf, wave_kib, sink, stream=None):
     """ckv_read_probe: enqueue one streaming read of the CUDA tensor `buf`
     (its whole storage) in waves of wave_kib KiB; `sink` is a one-word int32
     CUDA tensor."""
+    assert buf.is_cuda and buf.is_contiguous() and sink.is_cuda and sink.numel() >= 1
     _check(lib().ckv_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
                                 int(wave_kib), ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
 
